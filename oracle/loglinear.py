@@ -1,0 +1,238 @@
+"""CPU oracle for the forward pass of log-linear Mamba-2 attention (fp64).
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module. The HIP library
+and its Python binding never import, call or link anything under ``oracle/``,
+and this module imports nothing from them; the only thing both sides share is
+the seeded input generator in ``lla_synth`` (random draws, no method
+arithmetic).
+
+What is computed (sources are the five web pages on "Log-Linear Attention",
+arXiv 2506.04761):
+
+* The output is a level-weighted sum of per-level state read-outs,
+  ``o_t = sum_l lambda_t^(l) q_t^T S_t^(l)`` with non-negative, input-dependent
+  ``lambda`` (study notes, dimensionstp.github.io, sections 2-2 and 3-3;
+  gist.science zh technical summary, section 2.2).
+* The levels come from a Fenwick-tree (binary indexed tree) partition of the
+  prefix into power-of-two buckets, fine for recent and coarse for distant
+  tokens (study notes, sections 2-2 and 3-2). The level of a pair is
+  ``l(t, s) = bit_length(t XOR s)`` on 0-based positions: 0 for s == t,
+  otherwise floor(log2(t XOR s)) + 1.
+* Parallel form ``O = (Q K^T * M) V`` with the hierarchical mask composed with
+  Mamba-2's semiseparable decay mask, ``M = M^S * M^H`` (study notes, sections
+  3-4 and 3-5), giving, per head,
+
+      o_t = sum_{s <= t} lambda[t, l(t,s)] * prod_{r=s+1..t} a_r * (q_t . k_s) * v_s
+
+  with ``a_r = exp(log_a[r])``, so the decay factor is ``exp(A_t - A_s)`` for
+  the inclusive prefix sum ``A_t = sum_{r<=t} log_a[r]``.
+
+Functions:
+
+* ``bruteforce``        the O(T^2) definition above, row-blocked, fp64.
+* ``bruteforce_rows``   the same definition for selected query rows of one head.
+* ``recurrent``         the O(log T)-state recurrent form: one state per level,
+  merged like a carry when a lower level fills (study notes, section 3-6; zh
+  lay summary, "drawer" merging). It shares no helper with ``bruteforce``.
+
+Readings taken where the pages are silent are listed in the design doc and repeated
+at the functions that depend on them: 0-based positions, the bucket of s == t is
+level 0 and is included (the sum runs over s <= t), ``a_s`` itself is not in
+the decay of k_s, no scale/normaliser/gate inside the operator.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bit_length", "level", "num_levels", "level_matrix", "as_f64",
+    "bruteforce", "bruteforce_rows", "recurrent",
+]
+
+
+# ----------------------------------------------------------------------------
+# Levels
+# ----------------------------------------------------------------------------
+
+def bit_length(x) -> np.ndarray:
+    """Elementwise bit length of non-negative integers, integer ops only."""
+    y = np.array(x, dtype=np.int64, copy=True)
+    if np.any(y < 0):
+        raise ValueError("bit_length of a negative integer")
+    out = np.zeros_like(y)
+    while np.any(y):
+        nz = y > 0
+        out += nz
+        y >>= 1
+    return out
+
+
+def level(t: int, s: int) -> int:
+    """Fenwick level of position s seen from query position t (s <= t)."""
+    return int(t ^ s).bit_length()
+
+
+def num_levels(T: int) -> int:
+    """Number of lambda levels for T tokens: the largest level of any pair in
+    [0, T) is bit_length(T-1), so there are bit_length(T-1) + 1 of them."""
+    if T < 1:
+        raise ValueError("T must be >= 1")
+    return int(T - 1).bit_length() + 1
+
+
+def _levels(ts: np.ndarray, ss: np.ndarray) -> np.ndarray:
+    """Level matrix block, rows ts (query positions), columns ss (key positions)."""
+    return bit_length(ts[:, None] ^ ss[None, :])
+
+
+def level_matrix(T: int) -> np.ndarray:
+    """T x T matrix of levels l(t, s) for s <= t, -1 above the diagonal."""
+    t = np.arange(T)
+    lv = _levels(t, t)
+    lv[t[:, None] < t[None, :]] = -1
+    return lv
+
+
+# ----------------------------------------------------------------------------
+# Helpers of the parallel (masked) form
+# ----------------------------------------------------------------------------
+
+def as_f64(x) -> np.ndarray:
+    """Exact float64 copy of a numpy array or a (CPU or device) torch tensor."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.float64)
+
+
+def _prefix_log_decay(log_a_row: np.ndarray) -> np.ndarray:
+    """A_t = sum_{r <= t} log_a[r] (inclusive), so A_t - A_s = log prod_{r=s+1..t} a_r."""
+    return np.cumsum(log_a_row)
+
+
+def _pair_log_decay(A: np.ndarray, ts: np.ndarray, ss: np.ndarray) -> np.ndarray:
+    """log of prod_{r=s+1..t} a_r for every (t, s) in the block."""
+    return A[ts][:, None] - A[ss][None, :]
+
+
+def _causal(ts: np.ndarray, ss: np.ndarray) -> np.ndarray:
+    """Keys visible to each query: s <= t (the bucket of s == t is included)."""
+    return ss[None, :] <= ts[:, None]
+
+
+def _scores(q: np.ndarray, k: np.ndarray, ts: np.ndarray, ss: np.ndarray) -> np.ndarray:
+    """q_t . k_s for the block."""
+    return q[ts] @ k[ss].T
+
+
+def _mask_block(lam: np.ndarray, A: np.ndarray, ts: np.ndarray, ss: np.ndarray) -> np.ndarray:
+    """M[t, s] = lambda[t, l(t,s)] * exp(A_t - A_s) where s <= t, else 0."""
+    vis = _causal(ts, ss)
+    lv = _levels(ts, ss)
+    lv = np.where(vis, lv, 0)              # index only; masked out below
+    lam_ts = lam[ts[:, None], lv]
+    logd = np.where(vis, _pair_log_decay(A, ts, ss), -np.inf)
+    return np.where(vis, lam_ts * np.exp(logd), 0.0)
+
+
+def _check_shapes(q, k, v, log_a, lam):
+    B, H, T, dk = q.shape
+    if k.shape != (B, H, T, dk):
+        raise ValueError(f"k shape {k.shape} != {(B, H, T, dk)}")
+    if v.shape[:3] != (B, H, T):
+        raise ValueError(f"v shape {v.shape} does not start with {(B, H, T)}")
+    if log_a.shape != (B, H, T):
+        raise ValueError(f"log_a shape {log_a.shape} != {(B, H, T)}")
+    if lam.shape[:3] != (B, H, T) or (T > 0 and lam.shape[3] < num_levels(T)):
+        raise ValueError(f"lambda shape {lam.shape} too small for T={T}")
+    return B, H, T, dk, v.shape[3]
+
+
+def bruteforce(q, k, v, log_a, lam, row_block: int = 512) -> np.ndarray:
+    """The O(T^2) definition, in fp64, for every (b, h, t).
+
+    ``q, k [B,H,T,dk]``, ``v [B,H,T,dv]``, ``log_a [B,H,T]``,
+    ``lam [B,H,T,L]``; returns ``[B,H,T,dv]`` float64. Row blocks of queries
+    only bound memory: each block builds its own mask and applies two library
+    matmuls, ``(scores * mask) @ V``.
+    """
+    q, k, v, log_a, lam = (as_f64(x) for x in (q, k, v, log_a, lam))
+    B, H, T, dk, dv = _check_shapes(q, k, v, log_a, lam)
+    out = np.zeros((B, H, T, dv), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            A = _prefix_log_decay(log_a[b, h])
+            for t0 in range(0, T, row_block):
+                ts = np.arange(t0, min(T, t0 + row_block))
+                ss = np.arange(0, ts[-1] + 1)
+                P = _scores(q[b, h], k[b, h], ts, ss) * _mask_block(lam[b, h], A, ts, ss)
+                out[b, h, ts] = P @ v[b, h][ss]
+    return out
+
+
+def bruteforce_rows(q, k, v, log_a, lam, b: int, h: int, rows) -> np.ndarray:
+    """The same definition for query rows ``rows`` of head (b, h) only.
+
+    Returns ``[len(rows), dv]`` float64. Lets large sequences be checked on a
+    sample of outputs at O(t d) cost per row.
+    """
+    qh, kh, vh = (as_f64(x[b, h]) for x in (q, k, v))
+    la, lm = as_f64(log_a[b, h]), as_f64(lam[b, h])
+    A = _prefix_log_decay(la)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((len(rows), vh.shape[1]), dtype=np.float64)
+    for i, t in enumerate(rows):
+        ts = np.array([t])
+        ss = np.arange(0, t + 1)
+        P = _scores(qh, kh, ts, ss) * _mask_block(lm, A, ts, ss)
+        out[i] = (P @ vh[ss])[0]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Recurrent form with O(log T) states
+# ----------------------------------------------------------------------------
+
+def _ctz(t: int) -> int:
+    """Number of trailing zero bits of t > 0."""
+    return (t & -t).bit_length() - 1
+
+
+def recurrent(q, k, v, log_a, lam) -> np.ndarray:
+    """The recurrent (decoding) form: one dk x dv state per level.
+
+    At step t the live states are level 0 = {t} and, for each set bit j of t,
+    level j+1 holding the aligned block of 2^j positions just before the
+    blocks of the lower set bits. Going from t-1 to t with c = ctz(t): levels
+    0..c of t-1 are merged into level c+1 (the lower drawers are full and spill
+    into the next one), levels 1..c empty, every state is multiplied by a_t,
+    and level 0 is reset to k_t v_t^T. Then o_t = sum_l lambda[t,l] S_l^T q_t.
+
+    Cost O(T L dk dv) per head: a second, independent algorithm for the same
+    operator, used to cross-check ``bruteforce``.
+    """
+    q, k, v, log_a, lam = (as_f64(x) for x in (q, k, v, log_a, lam))
+    B, H, T, dk, dv = _check_shapes(q, k, v, log_a, lam)
+    out = np.zeros((B, H, T, dv), dtype=np.float64)
+    if T == 0:
+        return out
+    L = num_levels(T)
+    for b in range(B):
+        for h in range(H):
+            S = np.zeros((L + 1, dk, dv), dtype=np.float64)
+            for t in range(T):
+                if t > 0:
+                    c = _ctz(t)
+                    merged = S[: c + 1].sum(axis=0)
+                    S[1: c + 1] = 0.0
+                    S[c + 1] = merged
+                    S *= np.exp(log_a[b, h, t])
+                S[0] = np.outer(k[b, h, t], v[b, h, t])
+                w = lam[b, h, t, :L]
+                out[b, h, t] = np.einsum("l,lkv,k->v", w, S[:L], q[b, h, t])
+    return out
