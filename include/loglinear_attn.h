@@ -1,0 +1,137 @@
+/*
+ * loglinear_attn.h — C ABI of the MI355X (gfx950) log-linear Mamba-2 forward pass.
+ *
+ * Operation (per batch b and head h, every position t in [0, T)):
+ *
+ *   o_t = sum_{s <= t} lambda[t, l(t,s)] * prod_{r=s+1..t} a_r * (q_t . k_s) * v_s
+ *   l(t, s) = bit_length(t XOR s)      (0-based positions; 0 when s == t)
+ *   a_r     = exp(log_a[r])
+ *
+ * Sources ("Log-Linear Attention", arXiv 2506.04761, as explained on the study-notes
+ * page dimensionstp.github.io/study-concept/log_linear_attention and the gist.science
+ * summaries): the output is a lambda-weighted sum over Fenwick-tree levels of
+ * per-level states (study notes, sections 2-2 and 3-3); the prefix is split into
+ * power-of-two buckets (section 3-2); the parallel form is (QK^T * M)V with
+ * M = M^S * M^H, the Mamba-2 decay mask times the hierarchical mask (sections 3-4,
+ * 3-5); it is evaluated chunkwise, a dense masked block inside each chunk and
+ * O(log(T/C)) state passes between chunks (gist.science zh technical summary,
+ * section 2.3).
+ *
+ * Layout: every tensor is a dense row-major array in [B, H, T, ...] order:
+ *   q, k   [B, H, T, dk]     v, out  [B, H, T, dv]
+ *   log_a  [B, H, T]         lambda  [B, H, T, L],  L = loglinear_attn_num_levels(T)
+ * q, k, v and out are bfloat16 in loglinear_attn_fwd and float32 in
+ * loglinear_attn_fwd_f32; log_a and lambda are always float32. All accumulation is
+ * float32. Pointers are device pointers (HIP device memory of the current device);
+ * the caller owns every buffer. Inputs are read only; out is fully overwritten.
+ *
+ * Preconditions that are documented but not checked: log_a finite and <= 0,
+ * lambda finite and >= 0 (the arithmetic does not depend on either sign, but
+ * decay factors above 1 can overflow), q/k/v finite.
+ *
+ * Supported: B, H, T >= 0 (any product that is 0 is a no-op); dk, dv in
+ * {16, 32, 64, 128}; chunk in {16, 32, 64, 128}; any T (a ragged last chunk is
+ * masked). Output is bitwise deterministic for identical inputs and arguments.
+ *
+ * Errors: every function validates its arguments on the host before it touches the
+ * device and returns a status code (LLA_OK or a negative LLA_ERR_*); nothing is
+ * printed, nothing aborts, no exception crosses the ABI. Launches are asynchronous
+ * on `stream`; faults during kernel execution surface at the caller's next
+ * synchronisation of that stream. Functions are thread safe; the library keeps no
+ * state between calls.
+ */
+#ifndef LOGLINEAR_ATTN_H
+#define LOGLINEAR_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t without pulling in the HIP headers. */
+typedef struct ihipStream_t* lla_stream_t;
+
+enum lla_status {
+  LLA_OK = 0,
+  LLA_ERR_INVALID_ARG = -1,   /* null pointer, negative size, aliasing out, bad struct */
+  LLA_ERR_UNSUPPORTED = -2,   /* dk/dv/chunk outside the supported set, L > 32 */
+  LLA_ERR_HIP = -3,           /* a HIP runtime call or a kernel launch failed */
+  LLA_ERR_NO_MEMORY = -4,     /* stream-ordered workspace allocation failed */
+  LLA_ERR_WORKSPACE = -5      /* caller workspace smaller than loglinear_attn_workspace_bytes */
+};
+
+enum lla_dtype {
+  LLA_DTYPE_BF16 = 0,         /* q, k, v, out bfloat16 */
+  LLA_DTYPE_F32 = 1           /* q, k, v, out float32 */
+};
+
+/*
+ * loglinear_attn_fwd — the forward pass with bfloat16 q, k, v, out.
+ * log_a [B,H,T] and lambda [B,H,T,L] are float32. Chunk size and the number of
+ * chunks one workgroup sweeps are chosen by the library. A workspace is taken
+ * stream-ordered on `stream` (hipMallocAsync / hipFreeAsync) when the sequence
+ * spans more than one sweep.
+ * Returns LLA_OK or a negative LLA_ERR_* (see enum lla_status).
+ */
+int loglinear_attn_fwd(const void* q, const void* k, const void* v,
+                       const float* log_a, const float* lambda, void* out,
+                       int B, int H, int T, int dk, int dv, lla_stream_t stream);
+
+/* loglinear_attn_fwd_f32 — the same operation with float32 q, k, v, out. */
+int loglinear_attn_fwd_f32(const float* q, const float* k, const float* v,
+                           const float* log_a, const float* lambda, float* out,
+                           int B, int H, int T, int dk, int dv, lla_stream_t stream);
+
+/*
+ * Extended entry: explicit dtype, chunk size, sweep length and workspace.
+ *   chunk : 0 = library default, else one of 16, 32, 64, 128.
+ *   sweep : 0 = library default, else the number of consecutive chunks one
+ *           workgroup walks (1, 2, 4 or 8; 8 only when dk <= 64).
+ *   workspace / workspace_bytes : caller-owned device memory of at least
+ *           loglinear_attn_workspace_bytes(...) bytes (256-byte aligned), or
+ *           NULL/0 to let the library allocate stream-ordered on `stream`.
+ * The result does not depend on chunk or sweep beyond float rounding.
+ */
+typedef struct lla_fwd_args {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_a;
+  const float* lambda;
+  void* out;
+  int B, H, T, dk, dv;
+  int dtype;                  /* enum lla_dtype */
+  int chunk;
+  int sweep;
+  void* workspace;
+  size_t workspace_bytes;
+} lla_fwd_args;
+
+int loglinear_attn_fwd_ex(const lla_fwd_args* args, lla_stream_t stream);
+
+/*
+ * Bytes of workspace loglinear_attn_fwd_ex needs for these arguments (0 when
+ * the sequence fits one sweep). chunk/sweep 0 mean the library defaults, as in
+ * loglinear_attn_fwd_ex. Returns 0 as well for invalid arguments; the entry
+ * point reports those.
+ */
+size_t loglinear_attn_workspace_bytes(int B, int H, int T, int dk, int dv,
+                                      int chunk, int sweep, int dtype);
+
+/* Number of lambda levels for T tokens: bit_length(T-1) + 1 (1 for T = 1, 0 for T <= 0). */
+int loglinear_attn_num_levels(int T);
+
+/* Chunk size and sweep length the library picks when both are left at 0. */
+int loglinear_attn_default_chunk(int dk, int dv, int T, int dtype);
+int loglinear_attn_default_sweep(int B, int H, int T, int dk, int dv, int chunk, int dtype);
+
+/* Static, NUL-terminated description of a status code. */
+const char* loglinear_attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOGLINEAR_ATTN_H */

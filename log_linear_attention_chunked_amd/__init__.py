@@ -1,0 +1,118 @@
+"""Log-linear Mamba-2 attention forward pass on MI355X (gfx950), behind a C ABI.
+
+    from log_linear_attention_chunked_amd import forward
+    out = forward(q, k, v, log_a, lam)          # device tensors, [B,H,T,d] layout
+
+Computes, per head, o_t = sum_{s<=t} lam[t, l(t,s)] * prod_{r=s+1..t} a_r * (q_t.k_s) v_s
+with l(t,s) = bit_length(t XOR s) (Fenwick level) and a_r = exp(log_a[r]).
+PyTorch supplies device memory and the current stream; every step of the computation
+runs in the library's HIP kernels (``libloglinear_attn.so``).
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+from . import _lib
+from ._lib import LibraryNotBuilt  # noqa: F401
+
+__all__ = ["forward", "num_levels", "workspace_bytes", "default_chunk", "default_sweep",
+           "LLAError", "LibraryNotBuilt"]
+
+
+class LLAError(RuntimeError):
+    def __init__(self, status: int, where: str = "loglinear_attn_fwd_ex"):
+        self.status = status
+        super().__init__(f"{where} returned {status}: {_lib.status_string(status)}")
+
+
+def num_levels(T: int) -> int:
+    """Number of lambda levels for T tokens (bit_length(T-1) + 1)."""
+    return _lib.lib().loglinear_attn_num_levels(int(T))
+
+
+def _dtype_code(dtype) -> int:
+    import torch
+    if dtype in (torch.bfloat16, "bf16"):
+        return _lib.LLA_DTYPE_BF16
+    if dtype in (torch.float32, "f32"):
+        return _lib.LLA_DTYPE_F32
+    raise TypeError(f"unsupported q/k/v dtype {dtype}")
+
+
+def workspace_bytes(B, H, T, dk, dv, chunk=0, sweep=0, dtype="bf16") -> int:
+    return int(_lib.lib().loglinear_attn_workspace_bytes(
+        int(B), int(H), int(T), int(dk), int(dv), int(chunk), int(sweep), _dtype_code(dtype)))
+
+
+def default_chunk(dk, dv, T=0, dtype="bf16") -> int:
+    return _lib.lib().loglinear_attn_default_chunk(int(dk), int(dv), int(T), _dtype_code(dtype))
+
+
+def default_sweep(B, H, T, dk, dv, chunk=0, dtype="bf16") -> int:
+    return _lib.lib().loglinear_attn_default_sweep(int(B), int(H), int(T), int(dk), int(dv),
+                                                   int(chunk), _dtype_code(dtype))
+
+
+def _check(t, name, dtype, shape):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def make_args(q, k, v, log_a, lam, out, *, chunk=0, sweep=0, workspace=None) -> _lib.FwdArgs:
+    """Validate tensors and fill the C argument struct (no device work)."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, dk]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = num_levels(T) if T > 0 else 0
+    _check(q, "q", q.dtype, (B, H, T, dk))
+    _check(k, "k", q.dtype, (B, H, T, dk))
+    _check(v, "v", q.dtype, (B, H, T, dv))
+    _check(log_a, "log_a", torch.float32, (B, H, T))
+    _check(lam, "lam", torch.float32, (B, H, T, L))
+    _check(out, "out", q.dtype, (B, H, T, dv))
+    a = _lib.FwdArgs()
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.log_a, a.lam, a.out = log_a.data_ptr(), lam.data_ptr(), out.data_ptr()
+    a.B, a.H, a.T, a.dk, a.dv = int(B), int(H), int(T), int(dk), int(dv)
+    a.dtype = _dtype_code(q.dtype)
+    a.chunk, a.sweep = int(chunk), int(sweep)
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8, (workspace.numel(),))
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    else:
+        a.workspace, a.workspace_bytes = None, 0
+    return a
+
+
+def forward(q, k, v, log_a, lam, out=None, *, chunk: int = 0, sweep: int = 0,
+            workspace=None, stream=None):
+    """Forward pass on the current device and stream (or ``stream``).
+
+    q, k: [B,H,T,dk]; v: [B,H,T,dv] (bfloat16 or float32, all the same);
+    log_a: [B,H,T] float32; lam: [B,H,T,L] float32 with L = num_levels(T).
+    Returns out [B,H,T,dv] in q's dtype. ``chunk``/``sweep`` 0 = library default;
+    ``workspace``: optional uint8 device tensor of >= workspace_bytes(...) bytes.
+    """
+    import torch
+    if out is None:
+        out = torch.empty(q.shape[:3] + (v.shape[-1],), dtype=q.dtype, device=q.device)
+    a = make_args(q, k, v, log_a, lam, out, chunk=chunk, sweep=sweep, workspace=workspace)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = _lib.lib().loglinear_attn_fwd_ex(ctypes.byref(a), ctypes.c_void_p(handle))
+    if st != _lib.LLA_OK:
+        raise LLAError(st)
+    return out

@@ -1,0 +1,253 @@
+// lla_api.hip — C ABI of the log-linear Mamba-2 forward pass: argument validation, plan
+// (chunk, sweep, workspace layout), and the stream-ordered launch sequence
+//   sweep totals -> Fenwick up-sweep over sweeps -> chunk walk with read-outs.
+// See include/loglinear_attn.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/loglinear_attn.h"
+#include "lla_dispatch.hpp"
+#include "lla_kernels.hpp"
+
+namespace {
+
+using lla::ChunkSmem;
+using lla::KernelSet;
+using lla::Params;
+
+inline bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+inline int bit_len(unsigned x) { int n = 0; while (x) { ++n; x >>= 1; } return n; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline int lmax_for(int dk) { return dk >= 128 ? 2 : 3; }
+inline int num_units(int nqb) { int n = 0; for (int qb = 0; qb < nqb; ++qb) n += qb / 2 + 1; return n; }
+
+constexpr long kTargetWorkgroups = 2048;   // ~8 per CU on 256 CUs
+
+struct Plan {
+  int C, R, m, nchunks, nsweep, L, esize, nw;
+  long BH;
+  bool alias;
+  size_t ws_bytes, off_h, off_g, off_nodes;
+  int smem_state, smem_query, smem_fenwick;
+};
+
+int default_chunk(int dk, int dv) { return (dk <= 16 && dv <= 16) ? 16 : 64; }
+
+int default_sweep(long BH, int T, int dk, int C) {
+  const int nchunks = (T + C - 1) / C;
+  const int rmax = 1 << lmax_for(dk);
+  int R = 1;
+  while (R * 2 <= rmax && BH * ((nchunks + 2 * R - 1) / (2 * R)) >= kTargetWorkgroups) R *= 2;
+  return R;
+}
+
+// Host-only part of the plan: sizes and layout; no device calls.
+int make_plan(int B, int H, int T, int dk, int dv, int chunk, int sweep, int dtype, Plan& pl) {
+  if (dtype != LLA_DTYPE_BF16 && dtype != LLA_DTYPE_F32) return LLA_ERR_INVALID_ARG;
+  if (B < 0 || H < 0 || T < 0) return LLA_ERR_INVALID_ARG;
+  if (!supported_dim(dk) || !supported_dim(dv)) return LLA_ERR_UNSUPPORTED;
+  if (chunk != 0 && !supported_dim(chunk)) return LLA_ERR_UNSUPPORTED;
+  const int C = chunk ? chunk : default_chunk(dk, dv);
+  if (sweep != 0 && (sweep < 1 || sweep > (1 << lmax_for(dk)) || (sweep & (sweep - 1))))
+    return LLA_ERR_UNSUPPORTED;
+  const long BH = (long)B * H;
+  if (BH > 65535) return LLA_ERR_UNSUPPORTED;       // grid y dimension of the state kernels
+  pl.C = C;
+  pl.BH = BH;
+  pl.L = T > 0 ? bit_len((unsigned)(T - 1)) + 1 : 0;
+  if (pl.L > 32) return LLA_ERR_UNSUPPORTED;
+  pl.esize = dtype == LLA_DTYPE_BF16 ? 2 : 4;
+  pl.nw = dv / 16;
+  pl.nchunks = (T + C - 1) / C;
+  pl.R = sweep ? sweep : default_sweep(BH, T, dk, C);
+  pl.m = bit_len((unsigned)pl.R) - 1;
+  pl.nsweep = pl.nchunks > 0 ? (pl.nchunks + pl.R - 1) / pl.R : 0;
+  const long ns = pl.nsweep > 1 ? pl.nsweep - 1 : 0;
+  size_t off = 0;
+  pl.off_h = off;     off = align256(off + (size_t)BH * ns * dk * dv * 4);
+  pl.off_g = off;     off = align256(off + (size_t)BH * ns * 4);
+  pl.off_nodes = off; off = align256(off + (size_t)BH * ns * (dv / 16) * ((dk + 31) / 32) * 512 * pl.esize);
+  pl.ws_bytes = ns > 0 ? off : 0;
+  const int Lmem = pl.L > 0 ? pl.L : 1;
+  ChunkSmem sq, ss;
+  if (dtype == LLA_DTYPE_BF16) {
+    sq = lla::chunk_smem<lla::bf16>(C, dk, dv, Lmem, true, false);
+    ss = lla::chunk_smem<lla::bf16>(C, dk, dv, Lmem, false, false);
+  } else {
+    sq = lla::chunk_smem<float>(C, dk, dv, Lmem, true, false);
+    ss = lla::chunk_smem<float>(C, dk, dv, Lmem, false, false);
+  }
+  pl.alias = false;                 // decided against the device limit in launch()
+  pl.smem_query = sq.total;
+  pl.smem_state = ss.total;
+  pl.smem_fenwick = (int)align256((size_t)ns * 4 + 16);
+  return LLA_OK;
+}
+
+int alias_smem(int C, int dk, int dv, int L, int dtype) {
+  const int Lmem = L > 0 ? L : 1;
+  return dtype == LLA_DTYPE_BF16 ? lla::chunk_smem<lla::bf16>(C, dk, dv, Lmem, true, true).total
+                                 : lla::chunk_smem<float>(C, dk, dv, Lmem, true, true).total;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+int validate_pointers(const lla_fwd_args& a, const Plan& pl) {
+  if (!a.q || !a.k || !a.v || !a.log_a || !a.lambda || !a.out) return LLA_ERR_INVALID_ARG;
+  const size_t es = (size_t)pl.esize;
+  const size_t nt = (size_t)pl.BH * a.T;
+  const size_t nq = nt * a.dk * es, nv = nt * a.dv * es, nla = nt * 4, nlam = nt * pl.L * 4;
+  if (((uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.out) & 15) return LLA_ERR_INVALID_ARG;
+  if (((uintptr_t)a.log_a | (uintptr_t)a.lambda) & 3) return LLA_ERR_INVALID_ARG;
+  if (overlaps(a.out, nv, a.q, nq) || overlaps(a.out, nv, a.k, nq) || overlaps(a.out, nv, a.v, nv) ||
+      overlaps(a.out, nv, a.log_a, nla) || overlaps(a.out, nv, a.lambda, nlam))
+    return LLA_ERR_INVALID_ARG;
+  return LLA_OK;
+}
+
+int launch(const lla_fwd_args& a, const Plan& pl, void* ws, hipStream_t stream) {
+  const KernelSet* ks = a.dtype == LLA_DTYPE_BF16 ? lla::kernels_bf16(pl.C, a.dk) : lla::kernels_f32(pl.C, a.dk);
+  if (!ks) return LLA_ERR_UNSUPPORTED;
+
+  int dev = 0, max_smem = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LLA_ERR_HIP;
+  if (hipDeviceGetAttribute(&max_smem, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+    return LLA_ERR_HIP;
+
+  const void* qfn = ks->query;
+  int smem_q = pl.smem_query;
+  if (smem_q > max_smem) {
+    const int sa = alias_smem(pl.C, a.dk, a.dv, pl.L, a.dtype);
+    const int hold = (num_units(pl.C / 16) + pl.nw - 1) / pl.nw;
+    if (!ks->query_alias || sa > max_smem || hold > 4) return LLA_ERR_UNSUPPORTED;
+    qfn = ks->query_alias;
+    smem_q = sa;
+  }
+  if (pl.smem_state > max_smem) return LLA_ERR_UNSUPPORTED;
+
+  Params p;
+  memset(&p, 0, sizeof(p));
+  p.q = a.q; p.k = a.k; p.v = a.v; p.log_a = a.log_a; p.lam = a.lambda; p.out = a.out;
+  p.BH = (int)pl.BH; p.T = a.T; p.DV = a.dv; p.L = pl.L;
+  p.nchunks = pl.nchunks; p.sweep = pl.R; p.m = pl.m; p.nsweep = pl.nsweep;
+  if (ws) {
+    p.hbuf = reinterpret_cast<float*>((char*)ws + pl.off_h);
+    p.gbuf = reinterpret_cast<float*>((char*)ws + pl.off_g);
+    p.nodes = (char*)ws + pl.off_nodes;
+  }
+  const long total = (long)pl.nsweep * pl.BH;
+  p.xcd_per = (int)((total + 7) / 8);
+  void* args[] = {&p};
+  const dim3 block(64 * pl.nw);
+
+  if (pl.nsweep > 1) {
+    if (pl.smem_state > 65536 &&
+        hipFuncSetAttribute(ks->state, hipFuncAttributeMaxDynamicSharedMemorySize, pl.smem_state) != hipSuccess)
+      return LLA_ERR_HIP;
+    if (hipLaunchKernel(ks->state, dim3(pl.nsweep - 1, (unsigned)pl.BH), block, args, pl.smem_state, stream) != hipSuccess)
+      return LLA_ERR_HIP;
+    const int fthreads = pl.nw * ((a.dk + 31) / 32) * 64;
+    if (hipLaunchKernel(ks->fenwick, dim3((fthreads + 255) / 256, (unsigned)pl.BH), dim3(256), args,
+                        pl.smem_fenwick, stream) != hipSuccess)
+      return LLA_ERR_HIP;
+  }
+  if (smem_q > 65536 &&
+      hipFuncSetAttribute(qfn, hipFuncAttributeMaxDynamicSharedMemorySize, smem_q) != hipSuccess)
+    return LLA_ERR_HIP;
+  if (hipLaunchKernel(qfn, dim3((unsigned)(8 * p.xcd_per)), block, args, smem_q, stream) != hipSuccess)
+    return LLA_ERR_HIP;
+  return LLA_OK;
+}
+
+int forward(const lla_fwd_args& a, hipStream_t stream) {
+  Plan pl;
+  int st = make_plan(a.B, a.H, a.T, a.dk, a.dv, a.chunk, a.sweep, a.dtype, pl);
+  if (st != LLA_OK) return st;
+  if (pl.BH == 0 || a.T == 0) return LLA_OK;
+  st = validate_pointers(a, pl);
+  if (st != LLA_OK) return st;
+  void* ws = a.workspace;
+  bool owned = false;
+  if (pl.ws_bytes > 0) {
+    if (ws) {
+      if (a.workspace_bytes < pl.ws_bytes) return LLA_ERR_WORKSPACE;
+      if ((uintptr_t)ws & 255) return LLA_ERR_INVALID_ARG;
+    } else {
+      if (hipMallocAsync(&ws, pl.ws_bytes, stream) != hipSuccess) return LLA_ERR_NO_MEMORY;
+      owned = true;
+    }
+  }
+  st = launch(a, pl, ws, stream);
+  if (owned && hipFreeAsync(ws, stream) != hipSuccess && st == LLA_OK) st = LLA_ERR_HIP;
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int loglinear_attn_fwd_ex(const lla_fwd_args* args, lla_stream_t stream) {
+  if (!args) return LLA_ERR_INVALID_ARG;
+  return forward(*args, reinterpret_cast<hipStream_t>(stream));
+}
+
+int loglinear_attn_fwd(const void* q, const void* k, const void* v, const float* log_a,
+                       const float* lambda, void* out, int B, int H, int T, int dk, int dv,
+                       lla_stream_t stream) {
+  lla_fwd_args a;
+  memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v; a.log_a = log_a; a.lambda = lambda; a.out = out;
+  a.B = B; a.H = H; a.T = T; a.dk = dk; a.dv = dv; a.dtype = LLA_DTYPE_BF16;
+  return forward(a, reinterpret_cast<hipStream_t>(stream));
+}
+
+int loglinear_attn_fwd_f32(const float* q, const float* k, const float* v, const float* log_a,
+                           const float* lambda, float* out, int B, int H, int T, int dk, int dv,
+                           lla_stream_t stream) {
+  lla_fwd_args a;
+  memset(&a, 0, sizeof(a));
+  a.q = q; a.k = k; a.v = v; a.log_a = log_a; a.lambda = lambda; a.out = out;
+  a.B = B; a.H = H; a.T = T; a.dk = dk; a.dv = dv; a.dtype = LLA_DTYPE_F32;
+  return forward(a, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t loglinear_attn_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int sweep,
+                                      int dtype) {
+  Plan pl;
+  if (make_plan(B, H, T, dk, dv, chunk, sweep, dtype, pl) != LLA_OK) return 0;
+  return pl.ws_bytes;
+}
+
+int loglinear_attn_num_levels(int T) { return T > 0 ? bit_len((unsigned)(T - 1)) + 1 : 0; }
+
+int loglinear_attn_default_chunk(int dk, int dv, int T, int dtype) {
+  (void)T; (void)dtype;
+  return default_chunk(dk, dv);
+}
+
+int loglinear_attn_default_sweep(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
+  (void)dtype;
+  if (B < 0 || H < 0 || T < 0) return 0;
+  const int C = chunk ? chunk : default_chunk(dk, dv);
+  if (!supported_dim(C)) return 0;
+  return default_sweep((long)B * H, T, dk, C);
+}
+
+const char* loglinear_attn_status_string(int status) {
+  switch (status) {
+    case LLA_OK: return "ok";
+    case LLA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, negative size, aliasing output)";
+    case LLA_ERR_UNSUPPORTED: return "unsupported shape (dk, dv or chunk outside {16,32,64,128}, sweep, or shared memory)";
+    case LLA_ERR_HIP: return "HIP runtime call or kernel launch failed";
+    case LLA_ERR_NO_MEMORY: return "workspace allocation failed";
+    case LLA_ERR_WORKSPACE: return "caller workspace too small";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

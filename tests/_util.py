@@ -1,0 +1,43 @@
+"""Shared test helpers: build-on-demand, device runs, error metrics."""
+
+from __future__ import annotations
+
+import os
+
+import numpy as np
+
+from log_linear_attention_chunked_amd import _lib
+
+
+def ensure_built():
+    """Load what is built; build only when nothing is."""
+    if not os.path.exists(_lib.LIB_PATH):
+        from log_linear_attention_chunked_amd.build import build
+        build()
+
+
+def rel_l2(got, want) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    den = np.linalg.norm(want)
+    return float(np.linalg.norm(got - want) / (den if den > 0 else 1.0))
+
+
+def tol_for(dtype: str) -> float:
+    """Relative-L2 bars: 1e-4 for float32 inputs, 2e-2 for bfloat16 inputs with float32
+    accumulation."""
+    return 1e-4 if dtype == "f32" else 2e-2
+
+
+def to_device(x: dict):
+    return {k: v.cuda() for k, v in x.items()}
+
+
+def run_gpu(x: dict, **kw) -> np.ndarray:
+    """Device forward pass on CPU inputs `x`; returns float64 numpy of the output."""
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    d = to_device(x)
+    out = lla.forward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], **kw)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy()

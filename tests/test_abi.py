@@ -1,0 +1,137 @@
+"""The C-ABI library: it loads, exports what include/loglinear_attn.h declares, and its
+host-side validation returns the documented codes without touching a device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from log_linear_attention_chunked_amd import _lib
+from tests._util import ensure_built
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "loglinear_attn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    ensure_built()
+    return _lib.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(loglinear_attn_\w+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_num_levels(L):
+    assert [L.loglinear_attn_num_levels(T) for T in (0, 1, 2, 3, 4, 5, 256, 2048, 8192, 32768, 65536)] == \
+        [0, 1, 2, 3, 3, 4, 9, 12, 14, 16, 17]
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, -5):
+        s = _lib.status_string(code)
+        assert s and s != "unknown status"
+    assert _lib.status_string(-99) == "unknown status"
+
+
+def test_defaults(L):
+    assert L.loglinear_attn_default_chunk(16, 16, 256, 1) == 16
+    assert L.loglinear_attn_default_chunk(64, 64, 8192, 0) == 64
+    # headline shape: 64 heads x 128 chunks -> sweeps of 4 chunks (2048 workgroups)
+    assert L.loglinear_attn_default_sweep(4, 16, 8192, 64, 64, 64, 0) == 4
+    assert L.loglinear_attn_default_sweep(1, 1, 64, 64, 64, 64, 0) == 1
+    assert L.loglinear_attn_default_sweep(64, 64, 65536, 128, 128, 64, 0) == 4   # capped for dk=128
+    assert L.loglinear_attn_default_sweep(64, 64, 65536, 64, 64, 64, 0) == 8
+
+
+def test_workspace_bytes(L):
+    ws = L.loglinear_attn_workspace_bytes
+    assert ws(1, 2, 256, 16, 16, 16, 16, 1) == 0           # one sweep covers T
+    assert ws(1, 1, 64, 64, 64, 64, 1, 0) == 0              # one chunk
+    n = ws(4, 16, 8192, 64, 64, 64, 4, 0)
+    ns = 8192 // 64 // 4 - 1
+    per = 64 * ns
+    expect = per * 64 * 64 * 4 + per * 4 + per * 4 * 2 * 512 * 2
+    assert expect <= n <= expect + 3 * 256
+    assert ws(4, 16, 8192, 48, 64, 64, 4, 0) == 0           # invalid -> 0
+    assert ws(1, 1, 1000, 64, 64, 64, 2, 0) > 0             # ragged T
+
+
+def _args(**kw):
+    a = _lib.FwdArgs()
+    base = 1 << 40                 # fake, well-separated, aligned addresses: never dereferenced
+    a.q, a.k, a.v = base, base + (1 << 32), base + (2 << 32)
+    a.log_a, a.lam, a.out = base + (3 << 32), base + (4 << 32), base + (5 << 32)
+    a.B, a.H, a.T, a.dk, a.dv = 1, 2, 4096, 64, 64
+    a.dtype, a.chunk, a.sweep = 0, 64, 1
+    a.workspace, a.workspace_bytes = None, 0
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+def _call(L, a):
+    return L.loglinear_attn_fwd_ex(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), _lib.LLA_ERR_INVALID_ARG),
+    (dict(B=-1), _lib.LLA_ERR_INVALID_ARG),
+    (dict(T=-5), _lib.LLA_ERR_INVALID_ARG),
+    (dict(dk=48), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(dv=256), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(chunk=24), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(sweep=3), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(sweep=16), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(dk=128, dv=128, sweep=8), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(B=70000), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(q=None), _lib.LLA_ERR_INVALID_ARG),
+    (dict(lam=None), _lib.LLA_ERR_INVALID_ARG),
+    (dict(out=None), _lib.LLA_ERR_INVALID_ARG),
+    (dict(q=(1 << 40) + 8), _lib.LLA_ERR_INVALID_ARG),           # misaligned
+    (dict(log_a=(1 << 40) + (3 << 32) + 2), _lib.LLA_ERR_INVALID_ARG),
+    (dict(out=(1 << 40) + 4096), _lib.LLA_ERR_INVALID_ARG),      # out overlaps q
+    (dict(out=(1 << 40) + (4 << 32) + 256), _lib.LLA_ERR_INVALID_ARG),  # out overlaps lambda
+    (dict(workspace=(1 << 44), workspace_bytes=1024), _lib.LLA_ERR_WORKSPACE),
+    (dict(workspace=(1 << 44) + 16, workspace_bytes=1 << 30), _lib.LLA_ERR_INVALID_ARG),
+])
+def test_validation_codes(L, kw, code):
+    assert _call(L, _args(**kw)) == code
+
+
+def test_null_struct(L):
+    assert L.loglinear_attn_fwd_ex(None, None) == _lib.LLA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(T=0), dict(T=0, q=None, out=None)])
+def test_empty_is_a_noop(L, kw):
+    assert _call(L, _args(**kw)) == _lib.LLA_OK
+
+
+def test_plain_entries_validate(L):
+    vp = ctypes.c_void_p
+    assert L.loglinear_attn_fwd(None, None, None, None, None, None, 1, 1, 8, 64, 64, None) == _lib.LLA_ERR_INVALID_ARG
+    assert L.loglinear_attn_fwd_f32(None, None, None, None, None, None, 1, 1, 8, 20, 64, None) == _lib.LLA_ERR_UNSUPPORTED
+    assert L.loglinear_attn_fwd(vp(16), vp(32), vp(48), vp(64), vp(80), vp(96), 0, 1, 8, 64, 64, None) == _lib.LLA_OK
+
+
+def test_python_binding_requires_device_tensors():
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    ensure_built()
+    x = torch.zeros(1, 1, 8, 16)
+    with pytest.raises(ValueError):
+        lla.forward(x, x, x, torch.zeros(1, 1, 8), torch.zeros(1, 1, 8, 4))

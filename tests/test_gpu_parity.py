@@ -1,0 +1,215 @@
+"""GPU parity: the HIP path against the fp64 CPU oracle on identical seeded inputs.
+
+Bars (relative L2 over all outputs): 1e-4 for float32 inputs, 2e-2 for bfloat16 inputs
+with float32 accumulation. Small shapes compare every element with the O(T^2) oracle;
+the full-size workloads (in the launch configuration the benchmark times) compare
+sampled rows with the per-row oracle.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.loglinear as O
+from lla_synth import WORKLOADS, custom, generate
+from tests._util import ensure_built, rel_l2, run_gpu, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    import torch
+    ensure_built()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def check_full(x, dtype, **kw):
+    got = run_gpu(x, **kw)
+    want = O.bruteforce(x["q"], x["k"], x["v"], x["log_a"], x["lam"])
+    err = rel_l2(got, want)
+    print(f"rel_l2={err:.3e} kw={kw}", flush=True)
+    assert np.all(np.isfinite(got))
+    assert err <= tol_for(dtype), err
+    return got, want
+
+
+# --------------------------------------------------------------------------------------
+# the small fp32 workload, every element
+# --------------------------------------------------------------------------------------
+
+def test_small_f32_workload_full():
+    w = WORKLOADS["b1h2_t256_d16_f32"]
+    x = generate(w, seed=0)
+    check_full(x, "f32", chunk=w.chunk)
+
+
+@pytest.mark.parametrize("chunk,sweep", [(16, 1), (16, 2), (16, 4), (16, 8), (32, 1), (32, 4), (64, 2), (128, 1)])
+def test_small_f32_chunk_and_sweep_invariance(chunk, sweep):
+    w = WORKLOADS["b1h2_t256_d16_f32"]
+    x = generate(w, seed=0, log_a_mode="lowdecay")
+    check_full(x, "f32", chunk=chunk, sweep=sweep)
+
+
+# --------------------------------------------------------------------------------------
+# shapes: head dims, ragged T, degenerate sizes, both dtypes
+# --------------------------------------------------------------------------------------
+
+SHAPES = [
+    # B, H, T, dk, dv, chunk, sweep
+    (1, 1, 1, 16, 16, 16, 1),        # single token
+    (1, 1, 16, 16, 16, 16, 1),       # T = C, one chunk
+    (1, 2, 32, 32, 32, 16, 1),       # two chunks
+    (2, 1, 100, 32, 64, 32, 2),      # ragged last chunk, dk != dv
+    (1, 2, 333, 64, 32, 64, 2),      # ragged, dk > dv
+    (1, 1, 1024, 64, 64, 64, 4),     # several sweeps
+    (1, 2, 1000, 128, 128, 64, 4),   # d = 128, ragged
+    (1, 1, 512, 128, 64, 128, 2),    # C = 128
+    (2, 2, 768, 16, 128, 32, 8),     # non power-of-two sweep count
+    (1, 1, 4160, 64, 64, 64, 8),     # 65 chunks: many sweeps + one extra chunk
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "b{}h{}t{}dk{}dv{}c{}r{}".format(*s))
+def test_shapes(shape, dtype):
+    B, H, T, dk, dv, C, R = shape
+    if dtype == "f32" and C == 128 and max(dk, dv) == 128:
+        pytest.skip("float32 with C=128 and d=128 exceeds shared memory")
+    x = generate(custom(B, H, T, dk, dv, dtype=dtype), seed=T + dk)
+    check_full(x, dtype, chunk=C, sweep=R)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_default_plan(dtype):
+    x = generate(custom(2, 3, 1500, 64, 64, dtype=dtype), seed=11)
+    check_full(x, dtype)
+
+
+# --------------------------------------------------------------------------------------
+# stress: no decay, so coarse Fenwick levels carry weight; one-hot levels isolate stages
+# --------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("lev", [0, 3, 6, 7, 8, 9, 10, 11, 12])
+def test_onehot_levels_no_decay(lev, dtype):
+    # T=4096 at C=64, sweep 4: levels 0..6 intra-chunk, 7..8 inside a sweep, 9..12 across sweeps
+    x = generate(custom(1, 2, 4096, 64, 64, dtype=dtype), seed=lev,
+                 log_a_mode="nodecay", lam_mode=f"onehot:{lev}")
+    check_full(x, dtype, chunk=64, sweep=4)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", ["nodecay", "lowdecay"])
+def test_low_decay_all_levels(mode, dtype):
+    x = generate(custom(2, 2, 2048, 64, 64, dtype=dtype), seed=5, log_a_mode=mode)
+    check_full(x, dtype, chunk=64, sweep=2)
+
+
+def test_equal_lambda_reduces_to_mamba2_on_gpu():
+    x = generate(custom(1, 2, 700, 32, 32, dtype="f32"), seed=9, lam_mode="equal")
+    got = run_gpu(x, chunk=32, sweep=2)
+    # c_t * (S_t^T q_t) with S_t = a_t S_{t-1} + k_t v_t^T, evaluated as the masked product
+    q, k, v, la = (O.as_f64(x[n]) for n in ("q", "k", "v", "log_a"))
+    c = O.as_f64(x["lam"])[..., 0]
+    want = np.zeros_like(got)
+    for h in range(2):
+        A = np.cumsum(la[0, h])
+        D = np.tril(np.exp(np.minimum(A[:, None] - A[None, :], 0.0)))
+        want[0, h] = c[0, h][:, None] * ((q[0, h] @ k[0, h].T) * D) @ v[0, h]
+    assert rel_l2(got, want) <= 1e-4
+
+
+def test_zero_lambda_gives_zero():
+    x = generate(custom(1, 2, 300, 64, 64), seed=1, lam_mode="zero")
+    got = run_gpu(x, chunk=64, sweep=2)
+    assert np.all(got == 0.0)
+
+
+def test_causality():
+    import torch
+    w = custom(1, 2, 640, 64, 64)
+    x = generate(w, seed=2)
+    y = {k: v.clone() for k, v in x.items()}
+    t0 = 300
+    g = torch.Generator().manual_seed(3)
+    for key in ("q", "k", "v"):
+        y[key][:, :, t0:] = torch.randn(y[key][:, :, t0:].shape, generator=g).to(y[key].dtype)
+    y["log_a"][:, :, t0:] = -torch.rand(y["log_a"][:, :, t0:].shape, generator=g)
+    y["lam"][:, :, t0:] = torch.rand(y["lam"][:, :, t0:].shape, generator=g)
+    a = run_gpu(x, chunk=64, sweep=2)
+    b = run_gpu(y, chunk=64, sweep=2)
+    assert np.array_equal(a[:, :, :t0], b[:, :, :t0])
+    assert not np.array_equal(a[:, :, t0:], b[:, :, t0:])
+
+
+def test_bitwise_deterministic():
+    x = generate(custom(2, 4, 2048, 64, 64), seed=4)
+    a = run_gpu(x, chunk=64, sweep=4)
+    b = run_gpu(x, chunk=64, sweep=4)
+    assert np.array_equal(a, b)
+
+
+def test_caller_workspace_matches_library_workspace():
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    x = generate(custom(1, 4, 2048, 64, 64), seed=6)
+    d = {k: v.cuda() for k, v in x.items()}
+    n = lla.workspace_bytes(1, 4, 2048, 64, 64, 64, 2, "bf16")
+    assert n > 0
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a = lla.forward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], chunk=64, sweep=2, workspace=ws)
+    b = lla.forward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], chunk=64, sweep=2)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_plain_entry_points():
+    import ctypes
+    import torch
+    from log_linear_attention_chunked_amd import _lib
+    lib = _lib.lib()
+    for dtype, fn in (("bf16", lib.loglinear_attn_fwd), ("f32", lib.loglinear_attn_fwd_f32)):
+        x = generate(custom(1, 2, 1000, 64, 64, dtype=dtype), seed=8)
+        d = {k: v.cuda() for k, v in x.items()}
+        out = torch.empty_like(d["v"])
+        st = fn(d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(), d["log_a"].data_ptr(),
+                d["lam"].data_ptr(), out.data_ptr(), 1, 2, 1000, 64, 64,
+                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == 0
+        torch.cuda.synchronize()
+        want = O.bruteforce(x["q"], x["k"], x["v"], x["log_a"], x["lam"])
+        assert rel_l2(out.double().cpu().numpy(), want) <= tol_for(dtype)
+
+
+# --------------------------------------------------------------------------------------
+# full-size workloads, sampled rows, launch configuration of the benchmark
+# --------------------------------------------------------------------------------------
+
+def sample_rows(T, C, seed=1, n_uniform=48):
+    rows = set(range(min(T, 2 * C))) | set(range(max(0, T - C), T))
+    k = 1
+    while k < T:
+        rows |= {k - 1, k, min(T - 1, k + 1)}
+        k <<= 1
+    rng = np.random.default_rng(seed)
+    rows |= set(int(r) for r in rng.integers(0, T, n_uniform))
+    return sorted(r for r in rows if 0 <= r < T)
+
+
+@pytest.mark.parametrize("name", [n for n in WORKLOADS if n != "b1h2_t256_d16_f32"])
+@pytest.mark.parametrize("variant", ["as_stated", "nodecay"])
+def test_full_size_workloads_sampled(name, variant):
+    w = WORKLOADS[name]
+    kw = {} if variant == "as_stated" else dict(log_a_mode="nodecay")
+    x = generate(w, seed=0, **kw)
+    got = run_gpu(x, chunk=w.chunk)
+    rows = sample_rows(w.T, w.chunk)
+    heads = [(0, 0), (w.B - 1, w.H - 1), (w.B // 2, w.H // 2)]
+    errs = []
+    for (b, h) in heads:
+        want = O.bruteforce_rows(x["q"], x["k"], x["v"], x["log_a"], x["lam"], b, h, rows)
+        errs.append(rel_l2(got[b, h, rows], want))
+    print(f"{name} {variant}: rel_l2 per sampled head {['%.2e' % e for e in errs]}", flush=True)
+    assert np.all(np.isfinite(got))
+    assert max(errs) <= tol_for(w.dtype)
