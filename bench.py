@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Forward-pass throughput of log-linear Mamba-2 attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME]
+
+One step = one call of the C-ABI forward entry (sweep totals, Fenwick pass over sweeps,
+output kernel) over one batch of synthetic inputs already resident in HBM. Prints ONE
+JSON line: tokens/s (B*T per call), the roofline of the dominant kernel (the output
+kernel, timed live with the HIP events the library records around each of its kernels),
+and the CPU oracle timed on a bounded sample of the same workload.
+
+Only one GPU is used; --gpus N with N > 1 exits with a message.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fwd tokens/sec, log-linear Mamba-2 T=8192 d=64 bf16; MFMA util % of peak"
+HEADLINE = "b4h16_t8192_d64_bf16"
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 matrix
+
+
+def algorithmic_per_token(w, chunk: int) -> tuple[float, float]:
+    """(FLOP, bytes) per head-token.
+
+    FLOP: dense masked intra-chunk block 2C(dk+dv), one decayed chunk state 2 dk dv, and
+    the read-out of popcount(chunk index) Fenwick nodes, log2(T/C)/2 of them on average,
+    2 dk dv each. Bytes: q, k, v, out once each in the element type, lambda (L levels)
+    and log_a in float32.
+    """
+    import math
+    e = 2 if w.dtype == "bf16" else 4
+    n = max(1, w.T // chunk)
+    pbar = math.log2(n) / 2 if n > 1 else 0.0
+    flop = 2 * chunk * (w.dk + w.dv) + 2 * w.dk * w.dv * (1 + pbar)
+    byts = (2 * w.dk + 2 * w.dv) * e + 4 * w.L + 4
+    return flop, byts
+
+
+def cpu_baseline(w, x, heads: int) -> dict:
+    """The fp64 oracle as it stands, on `heads` heads of the workload, scaled to tokens/s."""
+    import oracle.loglinear as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    heads = max(1, min(heads, w.H))
+    sl = slice(0, heads)
+    t = time.perf_counter()
+    O.bruteforce(x["q"][:1, sl], x["k"][:1, sl], x["v"][:1, sl], x["log_a"][:1, sl], x["lam"][:1, sl])
+    dt = time.perf_counter() - t
+    # every head costs the same: the whole call (B*H heads) takes dt * B*H / heads
+    full = dt * w.B * w.H / heads
+    cpu = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": w.B * w.T / full,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"O(T^2) fp64 brute force on {heads} of {w.B * w.H} heads (b=0, h<{heads}), "
+                   f"T={w.T}, {dt:.2f} s measured, scaled x{w.B * w.H / heads:g} to the full call"),
+        "cpu_model": cpu or platform.processor(),
+        "seconds_measured": dt,
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--chunk", type=int, default=0, help="0: the workload's stated chunk size")
+    ap.add_argument("--sweep", type=int, default=0, help="0: library default")
+    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="skip the cold-cache, copy-bandwidth and CPU legs (profiler runs)")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_query_kernel.json"),
+                    help="measured HBM traffic of the output kernel (from rocprofv3 counters)")
+    a = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}, WORLD_SIZE {world}); "
+              "the heads of this method shard across GPUs with no communication, so the "
+              "one-GPU figure is the per-GPU share.", file=sys.stderr)
+        return 2
+
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    from lla_synth import WORKLOADS, generate
+    from log_linear_attention_chunked_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        from log_linear_attention_chunked_amd.build import build
+        build()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+
+    w = WORKLOADS[a.workload]
+    chunk = a.chunk or w.chunk
+    dev = torch.device("cuda:0")
+    x = generate(w, seed=0)
+    d = {k: v.to(dev) for k, v in x.items()}
+    out = torch.empty_like(d["v"])
+    sweep = a.sweep or lla.default_sweep(w.B, w.H, w.T, w.dk, w.dv, chunk, w.dtype)
+    nws = lla.workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, chunk, sweep, w.dtype)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def new_events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for e in evs:
+            e.record(stream)        # creates the underlying hipEvent_t
+        return evs
+
+    def step(evs=None):
+        lla.forward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], out, chunk=chunk, sweep=sweep,
+                    workspace=ws, stream=stream, stage_events=evs)
+
+    evsets = [new_events() for _ in range(a.steps)]
+    torch.cuda.synchronize(dev)
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(evsets[i])
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+
+    stage = {"sweep_state": 0.0, "fenwick": 0.0, "output": 0.0}
+    for evs in evsets:
+        stage["sweep_state"] += evs[0].elapsed_time(evs[1])
+        stage["fenwick"] += evs[1].elapsed_time(evs[2])
+        stage["output"] += evs[2].elapsed_time(evs[3])
+    stage = {k: v / a.steps for k, v in stage.items()}
+
+    tokens = w.B * w.T
+    ht = w.B * w.H * w.T
+    flop_ht, byte_ht = algorithmic_per_token(w, chunk)
+    ms_per_step = elapsed / a.steps * 1e3
+    value = tokens * a.steps / elapsed
+
+    t_out = stage["output"] * 1e-3
+    achieved = byte_ht * ht / t_out / 1e9
+    traffic = None
+    if os.path.exists(a.traffic):
+        try:
+            rec = json.load(open(a.traffic))
+            if (rec.get("workload") == w.name and rec.get("chunk") == chunk and rec.get("sweep") == sweep
+                    and rec.get("kernel_source_sha") == _kernel_sha()):
+                traffic = rec.get("hbm_bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+    peak_flops = (BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS) * 1e12
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv,
+                   "L": w.L, "chunk": chunk, "sweep": sweep, "parallelism": "single-gpu"},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel": "lla_query_kernel",
+            "kernel_ms": stage["output"],
+            "algorithmic_bytes_per_launch": byte_ht * ht,
+        },
+        "stages_ms": stage,
+        "path_hbm_frac": byte_ht * ht / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "mfma_util_algorithmic": flop_ht * ht / (ms_per_step * 1e-3) / peak_flops,
+        "algorithmic_flop_per_step": flop_ht * ht,
+    }
+
+    if not a.kernel_only:
+        # cold caches: overwrite a 512 MiB buffer (outside the events) before each call
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(max(5, min(a.steps, 20))):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            cold.append(e0.elapsed_time(e1))
+        cold.sort()
+        res["cold_ms_per_step_median"] = cold[len(cold) // 2]
+        del flush
+        # achievable HBM reference: device-to-device copy of 1 GiB
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        res["copy_gbs"] = 2 * 5 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del src, dst
+
+    if not a.kernel_only and not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, x, a.cpu_heads)
+        res["gpu_over_cpu"] = value / res["cpu_baseline"]["value"]
+
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def _kernel_sha() -> str:
+    """Hash of the kernel sources, to tell whether recorded counters still apply."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "log_linear_attention_chunked_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -92,6 +92,11 @@ int loglinear_attn_fwd_f32(const float* q, const float* k, const float* v,
  *   workspace / workspace_bytes : caller-owned device memory of at least
  *           loglinear_attn_workspace_bytes(...) bytes (256-byte aligned), or
  *           NULL/0 to let the library allocate stream-ordered on `stream`.
+ *   stage_events : optional timing hooks; each non-NULL entry is a hipEvent_t the
+ *           library records on `stream`: [0] before the first kernel, [1] after the
+ *           sweep-total kernel, [2] after the Fenwick kernel, [3] after the output
+ *           kernel ([1] and [2] are still recorded when a single sweep covers T and
+ *           those kernels are skipped). The caller owns the events.
  * The result does not depend on chunk or sweep beyond float rounding.
  */
 typedef struct lla_fwd_args {
@@ -107,6 +112,7 @@ typedef struct lla_fwd_args {
   int sweep;
   void* workspace;
   size_t workspace_bytes;
+  void* stage_events[4];      /* hipEvent_t or NULL */
 } lla_fwd_args;
 
 int loglinear_attn_fwd_ex(const lla_fwd_args* args, lla_stream_t stream);

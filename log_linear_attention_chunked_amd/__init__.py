@@ -68,7 +68,8 @@ def _check(t, name, dtype, shape):
         raise ValueError(f"{name} must be contiguous")
 
 
-def make_args(q, k, v, log_a, lam, out, *, chunk=0, sweep=0, workspace=None) -> _lib.FwdArgs:
+def make_args(q, k, v, log_a, lam, out, *, chunk=0, sweep=0, workspace=None,
+              stage_events=None) -> _lib.FwdArgs:
     """Validate tensors and fill the C argument struct (no device work)."""
     import torch
     if q.dim() != 4:
@@ -93,22 +94,29 @@ def make_args(q, k, v, log_a, lam, out, *, chunk=0, sweep=0, workspace=None) -> 
         a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
     else:
         a.workspace, a.workspace_bytes = None, 0
+    if stage_events is not None:
+        for i, ev in enumerate(stage_events):
+            a.stage_events[i] = ev.cuda_event if ev is not None else None
     return a
 
 
 def forward(q, k, v, log_a, lam, out=None, *, chunk: int = 0, sweep: int = 0,
-            workspace=None, stream=None):
+            workspace=None, stream=None, stage_events=None):
     """Forward pass on the current device and stream (or ``stream``).
 
     q, k: [B,H,T,dk]; v: [B,H,T,dv] (bfloat16 or float32, all the same);
     log_a: [B,H,T] float32; lam: [B,H,T,L] float32 with L = num_levels(T).
     Returns out [B,H,T,dv] in q's dtype. ``chunk``/``sweep`` 0 = library default;
     ``workspace``: optional uint8 device tensor of >= workspace_bytes(...) bytes.
+    ``stage_events``: optional 4 recorded ``torch.cuda.Event`` objects (or None) the
+    library records around its kernels (before, after sweep totals, after the Fenwick
+    pass, after the output kernel).
     """
     import torch
     if out is None:
         out = torch.empty(q.shape[:3] + (v.shape[-1],), dtype=q.dtype, device=q.device)
-    a = make_args(q, k, v, log_a, lam, out, chunk=chunk, sweep=sweep, workspace=workspace)
+    a = make_args(q, k, v, log_a, lam, out, chunk=chunk, sweep=sweep, workspace=workspace,
+                  stage_events=stage_events)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)

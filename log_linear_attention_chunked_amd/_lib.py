@@ -61,6 +61,7 @@ class FwdArgs(ctypes.Structure):
         ("sweep", ctypes.c_int),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("stage_events", ctypes.c_void_p * 4),
     ]
 
 
@@ -94,6 +95,12 @@ def lib():
     if _lib is None:
         with _lock:
             if _lib is None:
+                try:
+                    # load torch's HIP runtime first so the library binds to the same one
+                    # (one runtime per process: shared streams, events and allocations)
+                    import torch  # noqa: F401
+                except ImportError:
+                    pass
                 if not os.path.exists(LIB_PATH):
                     raise LibraryNotBuilt(
                         f"{LIB_PATH} is missing: build it with "

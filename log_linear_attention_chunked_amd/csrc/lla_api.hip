@@ -144,23 +144,33 @@ int launch(const lla_fwd_args& a, const Plan& pl, void* ws, hipStream_t stream) 
   p.xcd_per = (int)((total + 7) / 8);
   void* args[] = {&p};
   const dim3 block(64 * pl.nw);
+  auto mark = [&](int i) {
+    return a.stage_events[i] ? hipEventRecord(reinterpret_cast<hipEvent_t>(a.stage_events[i]), stream)
+                             : hipSuccess;
+  };
 
+  if (mark(0) != hipSuccess) return LLA_ERR_HIP;
   if (pl.nsweep > 1) {
     if (pl.smem_state > 65536 &&
         hipFuncSetAttribute(ks->state, hipFuncAttributeMaxDynamicSharedMemorySize, pl.smem_state) != hipSuccess)
       return LLA_ERR_HIP;
     if (hipLaunchKernel(ks->state, dim3(pl.nsweep - 1, (unsigned)pl.BH), block, args, pl.smem_state, stream) != hipSuccess)
       return LLA_ERR_HIP;
+    if (mark(1) != hipSuccess) return LLA_ERR_HIP;
     const int fthreads = pl.nw * ((a.dk + 31) / 32) * 64;
     if (hipLaunchKernel(ks->fenwick, dim3((fthreads + 255) / 256, (unsigned)pl.BH), dim3(256), args,
                         pl.smem_fenwick, stream) != hipSuccess)
       return LLA_ERR_HIP;
+    if (mark(2) != hipSuccess) return LLA_ERR_HIP;
+  } else if (mark(1) != hipSuccess || mark(2) != hipSuccess) {
+    return LLA_ERR_HIP;
   }
   if (smem_q > 65536 &&
       hipFuncSetAttribute(qfn, hipFuncAttributeMaxDynamicSharedMemorySize, smem_q) != hipSuccess)
     return LLA_ERR_HIP;
   if (hipLaunchKernel(qfn, dim3((unsigned)(8 * p.xcd_per)), block, args, smem_q, stream) != hipSuccess)
     return LLA_ERR_HIP;
+  if (mark(3) != hipSuccess) return LLA_ERR_HIP;
   return LLA_OK;
 }
 
