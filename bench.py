@@ -97,6 +97,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-only", action="store_true",
                     help="skip the cold-cache, copy-bandwidth and CPU legs (profiler runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 device copies of MIB MiB (hardware-counter calibration)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_query_kernel.json"),
                     help="measured HBM traffic of the output kernel (from rocprofv3 counters)")
     a = ap.parse_args(argv)
@@ -109,6 +111,14 @@ def main(argv=None) -> int:
         return 2
 
     import torch
+    if a.copy_calibration:
+        src = torch.ones(a.copy_calibration << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel(), "copies": 5}))
+        return 0
     import log_linear_attention_chunked_amd as lla
     from lla_synth import WORKLOADS, generate
     from log_linear_attention_chunked_amd import _lib

@@ -1,7 +1,7 @@
 // lla_api.hip — C ABI of the log-linear Mamba-2 forward pass: argument validation, plan
 // (chunk, sweep, workspace layout), and the stream-ordered launch sequence
 //   sweep totals -> Fenwick up-sweep over sweeps -> chunk walk with read-outs.
-// See include/loglinear_attn.h for the contract.
+// The contract is documented in include/loglinear_attn.h.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -10,6 +10,29 @@
 #include "../../include/loglinear_attn.h"
 #include "lla_dispatch.hpp"
 #include "lla_kernels.hpp"
+
+namespace lla {
+
+const KernelSet* kernel_set(int dtype, int C, int DK, int DV) {
+  if (dtype == LLA_DTYPE_BF16) {
+    switch (C) {
+      case 16: return kernels_bf16_c16(DK, DV);
+      case 32: return kernels_bf16_c32(DK, DV);
+      case 64: return kernels_bf16_c64(DK, DV);
+      case 128: return kernels_bf16_c128(DK, DV);
+    }
+  } else if (dtype == LLA_DTYPE_F32) {
+    switch (C) {
+      case 16: return kernels_f32_c16(DK, DV);
+      case 32: return kernels_f32_c32(DK, DV);
+      case 64: return kernels_f32_c64(DK, DV);
+      case 128: return kernels_f32_c128(DK, DV);
+    }
+  }
+  return nullptr;
+}
+
+}  // namespace lla
 
 namespace {
 
@@ -20,27 +43,29 @@ using lla::Params;
 inline bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 inline int bit_len(unsigned x) { int n = 0; while (x) { ++n; x >>= 1; } return n; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-inline int lmax_for(int dk) { return dk >= 128 ? 2 : 3; }
-inline int num_units(int nqb) { int n = 0; for (int qb = 0; qb < nqb; ++qb) n += qb / 2 + 1; return n; }
 
 constexpr long kTargetWorkgroups = 2048;   // ~8 per CU on 256 CUs
+constexpr int kFenwickSmem = 64 * 1024;    // preferred shared memory of one Fenwick slice
 
 struct Plan {
-  int C, R, m, nchunks, nsweep, L, esize, nw;
+  int C, R, m, nchunks, nsweep, ns, L, esize, nw;
   long BH;
-  bool alias;
-  size_t ws_bytes, off_h, off_g, off_nodes;
-  int smem_state, smem_query, smem_fenwick;
+  size_t ws_bytes, off_h, off_g, off_gn, off_nodes;
+  int smem_state, smem_query, smem_query_alias, fen_lanes, smem_fenwick;
 };
 
 int default_chunk(int dk, int dv) { return (dk <= 16 && dv <= 16) ? 16 : 64; }
 
-int default_sweep(long BH, int T, int dk, int C) {
+int default_sweep(long BH, int T, int C) {
   const int nchunks = (T + C - 1) / C;
-  const int rmax = 1 << lmax_for(dk);
   int R = 1;
-  while (R * 2 <= rmax && BH * ((nchunks + 2 * R - 1) / (2 * R)) >= kTargetWorkgroups) R *= 2;
+  while (R * 2 <= lla::kSweepCap && BH * ((nchunks + 2 * R - 1) / (2 * R)) >= kTargetWorkgroups) R *= 2;
   return R;
+}
+
+int smem_bytes(int dtype, int C, int dk, int dv, int L, bool with_q, bool alias) {
+  return dtype == LLA_DTYPE_BF16 ? lla::chunk_smem<lla::bf16>(C, dk, dv, L, with_q, alias).total
+                                 : lla::chunk_smem<float>(C, dk, dv, L, with_q, alias).total;
 }
 
 // Host-only part of the plan: sizes and layout; no device calls.
@@ -49,47 +74,38 @@ int make_plan(int B, int H, int T, int dk, int dv, int chunk, int sweep, int dty
   if (B < 0 || H < 0 || T < 0) return LLA_ERR_INVALID_ARG;
   if (!supported_dim(dk) || !supported_dim(dv)) return LLA_ERR_UNSUPPORTED;
   if (chunk != 0 && !supported_dim(chunk)) return LLA_ERR_UNSUPPORTED;
-  const int C = chunk ? chunk : default_chunk(dk, dv);
-  if (sweep != 0 && (sweep < 1 || sweep > (1 << lmax_for(dk)) || (sweep & (sweep - 1))))
+  if (sweep != 0 && (sweep < 1 || sweep > lla::kSweepCap || (sweep & (sweep - 1))))
     return LLA_ERR_UNSUPPORTED;
+  const int C = chunk ? chunk : default_chunk(dk, dv);
   const long BH = (long)B * H;
-  if (BH > 65535) return LLA_ERR_UNSUPPORTED;       // grid y dimension of the state kernels
+  if (BH > 65535) return LLA_ERR_UNSUPPORTED;       // grid y dimension of the sweep kernels
   pl.C = C;
   pl.BH = BH;
   pl.L = T > 0 ? bit_len((unsigned)(T - 1)) + 1 : 0;
-  if (pl.L > 32) return LLA_ERR_UNSUPPORTED;
+  if (pl.L > lla::kLamCap) return LLA_ERR_UNSUPPORTED;
   pl.esize = dtype == LLA_DTYPE_BF16 ? 2 : 4;
   pl.nw = dv / 16;
   pl.nchunks = (T + C - 1) / C;
-  pl.R = sweep ? sweep : default_sweep(BH, T, dk, C);
+  pl.R = sweep ? sweep : default_sweep(BH, T, C);
   pl.m = bit_len((unsigned)pl.R) - 1;
   pl.nsweep = pl.nchunks > 0 ? (pl.nchunks + pl.R - 1) / pl.R : 0;
-  const long ns = pl.nsweep > 1 ? pl.nsweep - 1 : 0;
+  pl.ns = pl.nsweep > 1 ? pl.nsweep - 1 : 0;
+  const size_t ns = (size_t)pl.ns;
   size_t off = 0;
   pl.off_h = off;     off = align256(off + (size_t)BH * ns * dk * dv * 4);
   pl.off_g = off;     off = align256(off + (size_t)BH * ns * 4);
+  pl.off_gn = off;    off = align256(off + (size_t)BH * ns * 4);
   pl.off_nodes = off; off = align256(off + (size_t)BH * ns * (dv / 16) * ((dk + 31) / 32) * 512 * pl.esize);
   pl.ws_bytes = ns > 0 ? off : 0;
   const int Lmem = pl.L > 0 ? pl.L : 1;
-  ChunkSmem sq, ss;
-  if (dtype == LLA_DTYPE_BF16) {
-    sq = lla::chunk_smem<lla::bf16>(C, dk, dv, Lmem, true, false);
-    ss = lla::chunk_smem<lla::bf16>(C, dk, dv, Lmem, false, false);
-  } else {
-    sq = lla::chunk_smem<float>(C, dk, dv, Lmem, true, false);
-    ss = lla::chunk_smem<float>(C, dk, dv, Lmem, false, false);
-  }
-  pl.alias = false;                 // decided against the device limit in launch()
-  pl.smem_query = sq.total;
-  pl.smem_state = ss.total;
-  pl.smem_fenwick = (int)align256((size_t)ns * 4 + 16);
+  pl.smem_query = smem_bytes(dtype, C, dk, dv, Lmem, true, false);
+  pl.smem_query_alias = smem_bytes(dtype, C, dk, dv, Lmem, true, true);
+  pl.smem_state = smem_bytes(dtype, C, dk, dv, Lmem, false, false);
+  // Fenwick slice: the most fragment lanes whose nodes fit the preferred shared memory
+  pl.fen_lanes = 32;
+  while (pl.fen_lanes > 1 && ns * (2 * pl.fen_lanes * 16 + 4) > (size_t)kFenwickSmem) pl.fen_lanes /= 2;
+  pl.smem_fenwick = (int)align256(ns * (2 * pl.fen_lanes * 16 + 4) + 16);
   return LLA_OK;
-}
-
-int alias_smem(int C, int dk, int dv, int L, int dtype) {
-  const int Lmem = L > 0 ? L : 1;
-  return dtype == LLA_DTYPE_BF16 ? lla::chunk_smem<lla::bf16>(C, dk, dv, Lmem, true, true).total
-                                 : lla::chunk_smem<float>(C, dk, dv, Lmem, true, true).total;
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -110,8 +126,13 @@ int validate_pointers(const lla_fwd_args& a, const Plan& pl) {
   return LLA_OK;
 }
 
+hipError_t set_smem(const void* fn, int bytes) {
+  return bytes > 65536 ? hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)
+                       : hipSuccess;
+}
+
 int launch(const lla_fwd_args& a, const Plan& pl, void* ws, hipStream_t stream) {
-  const KernelSet* ks = a.dtype == LLA_DTYPE_BF16 ? lla::kernels_bf16(pl.C, a.dk) : lla::kernels_f32(pl.C, a.dk);
+  const KernelSet* ks = lla::kernel_set(a.dtype, pl.C, a.dk, a.dv);
   if (!ks) return LLA_ERR_UNSUPPORTED;
 
   int dev = 0, max_smem = 0;
@@ -122,26 +143,26 @@ int launch(const lla_fwd_args& a, const Plan& pl, void* ws, hipStream_t stream) 
   const void* qfn = ks->query;
   int smem_q = pl.smem_query;
   if (smem_q > max_smem) {
-    const int sa = alias_smem(pl.C, a.dk, a.dv, pl.L, a.dtype);
-    const int hold = (num_units(pl.C / 16) + pl.nw - 1) / pl.nw;
-    if (!ks->query_alias || sa > max_smem || hold > 4) return LLA_ERR_UNSUPPORTED;
+    if (!ks->query_alias || pl.smem_query_alias > max_smem) return LLA_ERR_UNSUPPORTED;
     qfn = ks->query_alias;
-    smem_q = sa;
+    smem_q = pl.smem_query_alias;
   }
-  if (pl.smem_state > max_smem) return LLA_ERR_UNSUPPORTED;
+  if (pl.ns > 0 && (pl.smem_state > max_smem || pl.smem_fenwick > max_smem)) return LLA_ERR_UNSUPPORTED;
 
   Params p;
   memset(&p, 0, sizeof(p));
   p.q = a.q; p.k = a.k; p.v = a.v; p.log_a = a.log_a; p.lam = a.lambda; p.out = a.out;
-  p.BH = (int)pl.BH; p.T = a.T; p.DV = a.dv; p.L = pl.L;
+  p.BH = (int)pl.BH; p.T = a.T; p.L = pl.L;
   p.nchunks = pl.nchunks; p.sweep = pl.R; p.m = pl.m; p.nsweep = pl.nsweep;
   if (ws) {
     p.hbuf = reinterpret_cast<float*>((char*)ws + pl.off_h);
     p.gbuf = reinterpret_cast<float*>((char*)ws + pl.off_g);
+    p.gnode = reinterpret_cast<float*>((char*)ws + pl.off_gn);
     p.nodes = (char*)ws + pl.off_nodes;
   }
   const long total = (long)pl.nsweep * pl.BH;
   p.xcd_per = (int)((total + 7) / 8);
+  p.fen_lanes = pl.fen_lanes;
   void* args[] = {&p};
   const dim3 block(64 * pl.nw);
   auto mark = [&](int i) {
@@ -150,24 +171,21 @@ int launch(const lla_fwd_args& a, const Plan& pl, void* ws, hipStream_t stream) 
   };
 
   if (mark(0) != hipSuccess) return LLA_ERR_HIP;
-  if (pl.nsweep > 1) {
-    if (pl.smem_state > 65536 &&
-        hipFuncSetAttribute(ks->state, hipFuncAttributeMaxDynamicSharedMemorySize, pl.smem_state) != hipSuccess)
-      return LLA_ERR_HIP;
-    if (hipLaunchKernel(ks->state, dim3(pl.nsweep - 1, (unsigned)pl.BH), block, args, pl.smem_state, stream) != hipSuccess)
+  if (pl.ns > 0) {
+    if (set_smem(ks->state, pl.smem_state) != hipSuccess) return LLA_ERR_HIP;
+    if (hipLaunchKernel(ks->state, dim3(pl.ns, (unsigned)pl.BH), block, args, pl.smem_state, stream) != hipSuccess)
       return LLA_ERR_HIP;
     if (mark(1) != hipSuccess) return LLA_ERR_HIP;
-    const int fthreads = pl.nw * ((a.dk + 31) / 32) * 64;
-    if (hipLaunchKernel(ks->fenwick, dim3((fthreads + 255) / 256, (unsigned)pl.BH), dim3(256), args,
-                        pl.smem_fenwick, stream) != hipSuccess)
+    const int slices = pl.nw * ((a.dk + 31) / 32) * (64 / pl.fen_lanes);
+    if (set_smem(ks->fenwick, pl.smem_fenwick) != hipSuccess) return LLA_ERR_HIP;
+    if (hipLaunchKernel(ks->fenwick, dim3(slices, (unsigned)pl.BH), dim3(256), args, pl.smem_fenwick,
+                        stream) != hipSuccess)
       return LLA_ERR_HIP;
     if (mark(2) != hipSuccess) return LLA_ERR_HIP;
   } else if (mark(1) != hipSuccess || mark(2) != hipSuccess) {
     return LLA_ERR_HIP;
   }
-  if (smem_q > 65536 &&
-      hipFuncSetAttribute(qfn, hipFuncAttributeMaxDynamicSharedMemorySize, smem_q) != hipSuccess)
-    return LLA_ERR_HIP;
+  if (set_smem(qfn, smem_q) != hipSuccess) return LLA_ERR_HIP;
   if (hipLaunchKernel(qfn, dim3((unsigned)(8 * p.xcd_per)), block, args, smem_q, stream) != hipSuccess)
     return LLA_ERR_HIP;
   if (mark(3) != hipSuccess) return LLA_ERR_HIP;
@@ -245,14 +263,14 @@ int loglinear_attn_default_sweep(int B, int H, int T, int dk, int dv, int chunk,
   if (B < 0 || H < 0 || T < 0) return 0;
   const int C = chunk ? chunk : default_chunk(dk, dv);
   if (!supported_dim(C)) return 0;
-  return default_sweep((long)B * H, T, dk, C);
+  return default_sweep((long)B * H, T, C);
 }
 
 const char* loglinear_attn_status_string(int status) {
   switch (status) {
     case LLA_OK: return "ok";
     case LLA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, negative size, aliasing output)";
-    case LLA_ERR_UNSUPPORTED: return "unsupported shape (dk, dv or chunk outside {16,32,64,128}, sweep, or shared memory)";
+    case LLA_ERR_UNSUPPORTED: return "unsupported shape (dk, dv or chunk outside {16,32,64,128}, sweep, level count or shared memory)";
     case LLA_ERR_HIP: return "HIP runtime call or kernel launch failed";
     case LLA_ERR_NO_MEMORY: return "workspace allocation failed";
     case LLA_ERR_WORKSPACE: return "caller workspace too small";

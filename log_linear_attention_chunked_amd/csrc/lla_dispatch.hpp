@@ -4,14 +4,25 @@
 namespace lla {
 
 struct KernelSet {
-  const void* state;         // lla_sweep_state_kernel<T, C, DK>
-  const void* fenwick;       // lla_fenwick_kernel<T, DK>
-  const void* query;         // lla_query_kernel<T, C, DK, false>
-  const void* query_alias;   // lla_query_kernel<T, C, DK, true>, or nullptr
+  const void* state;         // lla_sweep_state_kernel<T, C, DK, DV>
+  const void* fenwick;       // lla_fenwick_kernel<T, DK, DV>
+  const void* query;         // lla_query_kernel<T, C, DK, DV, false>
+  const void* query_alias;   // lla_query_kernel<T, C, DK, DV, true>, or nullptr
 };
 
-// C in {16, 32, 64, 128}, DK in {16, 32, 64, 128}; nullptr otherwise.
-const KernelSet* kernels_bf16(int C, int DK);
-const KernelSet* kernels_f32(int C, int DK);
+// dtype 0 = bf16, 1 = f32; C, DK, DV in {16, 32, 64, 128}; nullptr otherwise.
+const KernelSet* kernel_set(int dtype, int C, int DK, int DV);
+
+// per (dtype, C) tables, one instantiation unit each
+const KernelSet* kernels_bf16_c16(int DK, int DV);
+const KernelSet* kernels_bf16_c32(int DK, int DV);
+const KernelSet* kernels_bf16_c64(int DK, int DV);
+const KernelSet* kernels_bf16_c128(int DK, int DV);
+const KernelSet* kernels_f32_c16(int DK, int DV);
+const KernelSet* kernels_f32_c32(int DK, int DV);
+const KernelSet* kernels_f32_c64(int DK, int DV);
+const KernelSet* kernels_f32_c128(int DK, int DV);
+
+inline int dim_index(int x) { return x == 16 ? 0 : x == 32 ? 1 : x == 64 ? 2 : x == 128 ? 3 : -1; }
 
 }  // namespace lla

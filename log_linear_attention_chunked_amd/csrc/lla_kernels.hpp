@@ -98,53 +98,72 @@ template <> struct Quad<float> { typedef f32x4 type; };
 
 __device__ __forceinline__ int bit_length(unsigned x) { return 32 - __clz((int)x); }
 
-// ----------------------------------------------------------------------------------------
-// shared-memory layout of one chunk (byte offsets; host and device agree)
-// ----------------------------------------------------------------------------------------
 
-struct ChunkSmem {
-  int qf, kf, pf, ktf, vtf, lam, aloc, total;
+constexpr int kLamCap = 24;       // lambda levels held per position (T <= 2^23)
+constexpr int kSweepCap = 4;      // chunks per sweep: Fenwick nodes inside a sweep in registers
+
+// bf16 operands contracted over positions (v, decayed k) are read with the gfx950 transposing
+// LDS read from a row-major image; f32 ones are stored in fragment order instead.
+template <typename T> struct TrNative { static constexpr bool value = sizeof(T) == 2; };
+
+// ----------------------------------------------------------------------------------------
+// shared-memory images of one chunk
+// ----------------------------------------------------------------------------------------
+// A [C, DF] block is kept row-major in 4-element quads whose place inside a row is XOR-swizzled:
+//   TR = false: quad q of row r sits at q ^ (r mod 16). A fragment read takes one quad of
+//               16 consecutive rows per 16 lanes: 16 distinct bank groups.
+//   TR = true : quad q of row r sits at q ^ 4 (r mod 4). A transposing read takes 4 quads of
+//               4 consecutive rows per 16 lanes: 16 distinct bank groups.
+template <typename T, int DF, bool TR>
+struct Img {
+  static constexpr int NQ = DF / 4;                  // quads per row
+  static constexpr int QB = 4 * (int)sizeof(T);      // bytes per quad
+  static constexpr int ROWB = DF * (int)sizeof(T);   // bytes per row
+  __device__ __forceinline__ static int swz(int r) {
+    return TR ? ((4 * (r & 3)) & (NQ - 1)) : (r & (NQ - 1) & 15);
+  }
+  __device__ __forceinline__ static int off(int r, int q) { return r * ROWB + (q ^ swz(r)) * QB; }
 };
 
-// slots: one slot = one fragment for all 64 lanes (64 * 8 elements)
+struct ChunkSmem {
+  int qimg, kimg, pf, kt, vt, lam, aloc, ea, eb, flag, total;
+};
+
+// Byte offsets of one chunk's shared memory (host and device agree). A fragment slot is one
+// operand fragment for all 64 lanes (64 x 8 elements).
 template <typename T>
 __host__ __device__ inline ChunkSmem chunk_smem(int C, int DK, int DV, int L, bool with_q,
                                                 bool alias_p) {
-  const int slot = 64 * 8 * (int)sizeof(T);
-  const int nqb = C / 16, nks_c = (C + 31) / 32, nks_d = (DK + 31) / 32;
-  const int ndkb = DK / 16, ndvb = DV / 16;
+  const int es = (int)sizeof(T);
+  const int slot = 64 * 8 * es;
+  const int nqb = C / 16, nks_c = (C + 31) / 32;
+  const bool trn = es == 2;
   ChunkSmem s;
   int off = 0;
-  s.qf = off;  off += with_q ? nqb * nks_d * slot : 0;
-  s.kf = off;  int kbytes = with_q ? nqb * nks_d * slot : 0;
-  int pbytes = with_q ? nqb * nks_c * slot : 0;
+  s.qimg = off; off += with_q ? C * DK * es : 0;
+  s.kimg = off;
+  const int kbytes = with_q ? C * DK * es : 0;
+  const int pbytes = with_q ? nqb * nks_c * slot : 0;
   if (alias_p) { s.pf = off; off += (kbytes > pbytes ? kbytes : pbytes); }
   else { off += kbytes; s.pf = off; off += pbytes; }
-  s.ktf = off; off += ndkb * nks_c * slot;
-  s.vtf = off; off += ndvb * nks_c * slot;
-  s.lam = off; off += with_q ? C * L * 4 : 0;
-  s.aloc = off; off += C * 4 + 16;
+  s.kt = off; off += trn ? C * DK * es : (DK / 16) * nks_c * slot;
+  s.vt = off; off += trn ? C * DV * es : (DV / 16) * nks_c * slot;
+  s.lam = off; off += with_q ? ((C * L * 4 + 15) & ~15) : 0;
+  s.aloc = off; off += C * 4;
+  s.ea = off; off += C * 4;
+  s.eb = off; off += C * 4;
+  s.flag = off; off += 16;
   s.total = (off + 255) & ~255;
   return s;
 }
 
 // ----------------------------------------------------------------------------------------
-// loading one chunk into operand fragments
+// global -> registers -> shared memory staging of one chunk
 // ----------------------------------------------------------------------------------------
 
-// Writes 4 consecutive contraction elements (k = k0..k0+3, k0 % 4 == 0, k0 < 32) of the
-// fragment row/column `rc` (0..15) of fragment slot `slot`.
-template <typename T>
-__device__ __forceinline__ void put_quad(T* base, int slot, int rc, int k0,
-                                         const typename Quad<T>::type& q4) {
-  const int hidx = k0 >> 2;
-  const int g = hidx & 3, e0 = (hidx >> 2) * 4;
-  T* p = base + ((size_t)slot * 64 + rc + 16 * g) * 8 + e0;
-  *reinterpret_cast<typename Quad<T>::type*>(p) = q4;
-}
-
-// 16-byte global piece: 8 bf16 or 4 f32
-template <typename T> struct Piece { static constexpr int n = 16 / sizeof(T); };
+template <typename T> struct Pair;
+template <> struct Pair<bf16> { typedef bf16 __attribute__((ext_vector_type(2))) type; };
+template <> struct Pair<float> { typedef float __attribute__((ext_vector_type(2))) type; };
 
 template <typename T>
 __device__ __forceinline__ uint4 load_piece(const T* p, bool valid) {
@@ -152,104 +171,219 @@ __device__ __forceinline__ uint4 load_piece(const T* p, bool valid) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+__device__ __forceinline__ unsigned word_of(const uint4& u, int i) {
+  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
+}
+
+// element i of a 16-byte piece, as float
+template <typename T> __device__ __forceinline__ float elemf(const uint4& u, int i);
+template <> __device__ __forceinline__ float elemf<bf16>(const uint4& u, int i) {
+  const unsigned w = word_of(u, i >> 1);
+  return __builtin_bit_cast(float, (i & 1) ? (w & 0xffff0000u) : (w << 16));
+}
+template <> __device__ __forceinline__ float elemf<float>(const uint4& u, int i) {
+  return __builtin_bit_cast(float, word_of(u, i));
+}
+
+// a 16-byte piece with every element multiplied by w (rounded back to T)
+template <typename T> __device__ __forceinline__ uint4 scale_piece(const uint4& u, float w);
+template <> __device__ __forceinline__ uint4 scale_piece<bf16>(const uint4& u, float w) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)(elemf<bf16>(u, i) * w);
+  const u32x4 x = __builtin_bit_cast(u32x4, r);
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+template <> __device__ __forceinline__ uint4 scale_piece<float>(const uint4& u, float w) {
+  return make_uint4(__builtin_bit_cast(unsigned, elemf<float>(u, 0) * w),
+                    __builtin_bit_cast(unsigned, elemf<float>(u, 1) * w),
+                    __builtin_bit_cast(unsigned, elemf<float>(u, 2) * w),
+                    __builtin_bit_cast(unsigned, elemf<float>(u, 3) * w));
+}
+
+// Writes one 16-byte piece (features f0..f0+EPP-1 of row r) into a swizzled image.
+template <typename T, int DF, bool TR>
+__device__ __forceinline__ void put_piece(unsigned char* img, int r, int f0, const uint4& x) {
+  typedef Img<T, DF, TR> I;
+  if (sizeof(T) == 2) {
+    // two quads 2p, 2p+1 land on an aligned pair, swapped when the swizzle flips bit 0
+    const int q = f0 / 4;
+    const int phys = q ^ I::swz(r);
+    uint4 y = (phys & 1) ? make_uint4(x.z, x.w, x.x, x.y) : x;
+    *reinterpret_cast<uint4*>(img + r * I::ROWB + (phys & ~1) * I::QB) = y;
+  } else {
+    *reinterpret_cast<uint4*>(img + I::off(r, f0 / 4)) = x;
+  }
+}
+
+// Writes 2 consecutive contraction elements k0, k0+1 (k0 even) of fragment row/column rc of
+// fragment slot `slot` (fragment-order storage, f32 position-contracted operands).
 template <typename T>
-__device__ __forceinline__ typename Quad<T>::type quad_of(const uint4& u, int h);
-template <>
-__device__ __forceinline__ bf16x4 quad_of<bf16>(const uint4& u, int h) {
-  uint2 w = h ? make_uint2(u.z, u.w) : make_uint2(u.x, u.y);
-  return *reinterpret_cast<bf16x4*>(&w);
-}
-template <>
-__device__ __forceinline__ f32x4 quad_of<float>(const uint4& u, int) {
-  return *reinterpret_cast<const f32x4*>(&u);
+__device__ __forceinline__ void put_pair(T* base, int slot, int rc, int k0,
+                                         const typename Pair<T>::type& p2) {
+  const int hidx = k0 >> 2;
+  const int g = hidx & 3, e = (hidx >> 2) * 4 + (k0 & 3);
+  *reinterpret_cast<typename Pair<T>::type*>(base + ((size_t)slot * 64 + rc + 16 * g) * 8 + e) = p2;
 }
 
-template <typename T>
-__device__ __forceinline__ T elem_of(const uint4& u, int i) {
-  return reinterpret_cast<const T*>(&u)[i];
-}
+// One [C, DF] block (row stride DF; rows past `valid` read as 0) in registers: units of 2
+// consecutive rows x one 16-byte piece, dealt round-robin to the NT threads.
+template <typename T, int C, int DF, int NT>
+struct BlockRegs {
+  static constexpr int EPP = 16 / (int)sizeof(T);
+  static constexpr int PPR = DF / EPP;
+  static constexpr int UNITS = (C / 2) * PPR;
+  static constexpr int ITERS = (UNITS + NT - 1) / NT;
+  uint4 x[ITERS][2];
 
+  __device__ __forceinline__ static int row0(int tid, int it) {
+    const int u = tid + it * NT;
+    return u < UNITS ? 2 * (u / PPR) : 0;
+  }
 
-// Loads rows [0, valid) of a [C, df] block (row stride df, rows past `valid` read as 0) and
-// writes them as
-//   rowf: row-major operand fragments, slot = (row / 16) * ceil(df/32) + col / 32
-//         (rows = positions, contraction = features: q and k for the scores, q for read-outs)
-//   trf : transposed operand fragments, slot = (col / 16) * ceil(C/32) + row / 32
-//         (rows = features, contraction = positions: k and v for states, v for P.V)
-// Each thread moves 4 consecutive positions x one 16-byte feature piece, so the transposed
-// fragments get 4-element (8- or 16-byte) shared-memory stores.
-template <typename T, int C, bool ROW, bool TR>
-__device__ __forceinline__ void load_block(const T* __restrict__ g, int df, int valid,
-                                           T* rowf, T* trf, int tid, int nthreads) {
-  constexpr int EPP = Piece<T>::n;
-  constexpr int NKS_C = (C + 31) / 32;
-  typedef typename Quad<T>::type Q4;
-  const Q4 zero4 = {};
-  const int ppr = df / EPP;
-  const int nks_d = (df + 31) / 32;
-  for (int p = tid; p < (C / 4) * ppr; p += nthreads) {
-    const int tg = p / ppr, fp = p - tg * ppr;
-    const int r0 = 4 * tg, f0 = fp * EPP;
-    uint4 x[4];
+  // Branch-free: every lane issues its loads at a clamped, in-bounds address and zeroes what
+  // lies past `valid` (valid >= 1), so the compiler can count outstanding loads exactly.
+  __device__ __forceinline__ void fetch(const T* __restrict__ g, int valid, int tid) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) x[i] = load_piece<T>(g + (size_t)(r0 + i) * df + f0, r0 + i < valid);
-    if (ROW) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i;
-#pragma unroll
-        for (int h = 0; h < EPP / 4; ++h) {
-          const int col = f0 + 4 * h;
-          put_quad<T>(rowf, (r >> 4) * nks_d + (col >> 5), r & 15, col & 31, quad_of<T>(x[i], h));
-          if (df < 32) put_quad<T>(rowf, (r >> 4) * nks_d, r & 15, (col & 31) + 16, zero4);
-        }
-      }
+    for (int it = 0; it < ITERS; ++it) {
+      const int u = tid + it * NT;
+      const bool ok = (UNITS % NT == 0) || u < UNITS;
+      const int uc = ok ? u : 0;
+      const int r0 = 2 * (uc / PPR), f0 = (uc % PPR) * EPP;
+      const int ra = min(r0, valid - 1), rb = min(r0 + 1, valid - 1);
+      const uint4 a = *reinterpret_cast<const uint4*>(g + (size_t)ra * DF + f0);
+      const uint4 b = *reinterpret_cast<const uint4*>(g + (size_t)rb * DF + f0);
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      x[it][0] = (ok && r0 < valid) ? a : z;
+      x[it][1] = (ok && r0 + 1 < valid) ? b : z;
     }
-    if (TR) {
+  }
+
+  // row-major swizzled image; ws[it][i] (if given) scales row r0+i of unit it
+  template <bool TR, bool SCALE>
+  __device__ __forceinline__ void commit_image(unsigned char* img, int tid, const float (*ws)[2]) const {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int u = tid + it * NT;
+      if (u >= UNITS) break;
+      const int r0 = 2 * (u / PPR), f0 = (u % PPR) * EPP;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        put_piece<T, DF, TR>(img, r0 + i, f0, SCALE ? scale_piece<T>(x[it][i], ws[it][i]) : x[it][i]);
+    }
+  }
+
+  // fragment-order storage of the position-contracted operand (rows = features)
+  template <bool SCALE>
+  __device__ __forceinline__ void commit_frags(T* trf, int tid, const float (*ws)[2]) const {
+    constexpr int NKS_C = (C + 31) / 32;
+    typedef typename Pair<T>::type P2;
+    const P2 zero2 = {};
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int u = tid + it * NT;
+      if (u >= UNITS) break;
+      const int r0 = 2 * (u / PPR), f0 = (u % PPR) * EPP;
       const int k0 = r0 & 31, ks = r0 >> 5;
+      const float w0 = SCALE ? ws[it][0] : 1.f, w1 = SCALE ? ws[it][1] : 1.f;
 #pragma unroll
       for (int i = 0; i < EPP; ++i) {
         const int f = f0 + i;
-        Q4 q4;
-        q4[0] = elem_of<T>(x[0], i); q4[1] = elem_of<T>(x[1], i);
-        q4[2] = elem_of<T>(x[2], i); q4[3] = elem_of<T>(x[3], i);
-        put_quad<T>(trf, (f >> 4) * NKS_C + ks, f & 15, k0, q4);
-        if (C < 32) put_quad<T>(trf, (f >> 4) * NKS_C + ks, f & 15, k0 + 16, zero4);
+        P2 p2;
+        p2[0] = (T)(elemf<T>(x[it][0], i) * w0);
+        p2[1] = (T)(elemf<T>(x[it][1], i) * w1);
+        put_pair<T>(trf, (f >> 4) * NKS_C + ks, f & 15, k0, p2);
+        if (C < 32) put_pair<T>(trf, (f >> 4) * NKS_C + ks, f & 15, k0 + 16, zero2);
       }
     }
   }
-}
+};
 
-// Inclusive prefix sum of log_a over one chunk (run by one wave) into aloc[0..C-1];
-// positions past `valid` count as 0. Fixed summation order: bitwise reproducible.
+// lambda rows of one chunk (C*L contiguous floats) in registers: NF floats per thread, each
+// loaded at a clamped in-bounds index (branch-free) and zeroed past the chunk's valid rows.
+template <int C, int NT>
+struct LamRegs {
+  static constexpr int NF = (C * kLamCap + NT - 1) / NT;
+  float x[NF];
+
+  __device__ __forceinline__ void fetch(const float* __restrict__ g, int nvalid, int tid) {
+#pragma unroll
+    for (int it = 0; it < NF; ++it) {
+      const int i = tid + it * NT;
+      const float v = g[min(i, nvalid - 1)];
+      x[it] = i < nvalid ? v : 0.f;
+    }
+  }
+
+  __device__ __forceinline__ void commit(float* lam, int ntotal, int tid) const {
+#pragma unroll
+    for (int it = 0; it < NF; ++it) {
+      const int i = tid + it * NT;
+      if (i < ntotal) lam[i] = x[it];
+    }
+  }
+};
+
+// log_a of one chunk in every wave's registers (lane l holds positions E*l .. E*l+E-1), and
+// the chunk-local inclusive prefix sum A (same layout), computed by each wave on its own.
 template <int C>
-__device__ __forceinline__ void chunk_cumsum(const float* __restrict__ la, int valid,
-                                             float* aloc, int lane) {
-  constexpr int E = C > 64 ? C / 64 : 1;      // positions per lane
+struct DecayRegs {
+  static constexpr int E = C > 64 ? C / 64 : 1;
   float x[E];
-  float run = 0.f;
+  float a[E];
+
+  __device__ __forceinline__ void fetch(const float* __restrict__ la, int valid, int lane) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = lane * E + e;
-    run += (i < C && i < valid) ? la[i] : 0.f;
-    x[e] = run;
+    for (int e = 0; e < E; ++e) {
+      const int i = lane * E + e;
+      const float v = la[min(i, valid - 1)];
+      x[e] = (i < C && i < valid) ? v : 0.f;
+    }
   }
-  float tot = run;
+  // fixed summation order: bitwise reproducible
+  __device__ __forceinline__ void scan(int lane) {
+    float run = 0.f;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const float y = __shfl_up(tot, d, 64);
-    if (lane >= d) tot += y;
-  }
-  const float excl = tot - run;
+    for (int e = 0; e < E; ++e) { run += x[e]; a[e] = run; }
+    float tot = run;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = lane * E + e;
-    if (i < C) aloc[i] = excl + x[e];
+    for (int d = 1; d < 64; d <<= 1) {
+      const float y = __shfl_up(tot, d, 64);
+      if (lane >= d) tot += y;
+    }
+    const float excl = tot - run;
+#pragma unroll
+    for (int e = 0; e < E; ++e) a[e] += excl;
   }
-}
+  // A at chunk position r (all lanes of the wave must call it together)
+  __device__ __forceinline__ float at(int r) const {
+    if (E == 1) return __shfl(a[0], r, 64);
+    const float lo = __shfl(a[0], r / E, 64);
+    const float hi = __shfl(a[E - 1], r / E, 64);
+    return (r % E) ? hi : lo;
+  }
+  // wave 0: publish A, e^A, e^-A and whether the factorised decay is safe (|A| < 40)
+  __device__ __forceinline__ void publish(float* aloc, float* ea, float* eb, int* flag, int lane) const {
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = lane * E + e;
+      if (i < C) {
+        aloc[i] = a[e];
+        ea[i] = __expf(a[e]);
+        eb[i] = __expf(-a[e]);
+        amax = fmaxf(amax, fabsf(a[e]));
+      }
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
+    if (lane == 0) *flag = amax < 40.f ? 1 : 0;
+  }
+};
 
 // ----------------------------------------------------------------------------------------
-// per-wave building blocks
+// operand fragments from shared memory
 // ----------------------------------------------------------------------------------------
 
 template <typename T>
@@ -257,32 +391,80 @@ __device__ __forceinline__ Frag<T> lds_frag(const T* base, int slot, int lane) {
   return reinterpret_cast<const Frag<T>*>(base)[slot * 64 + lane];
 }
 
+template <typename T> __device__ __forceinline__ typename Quad<T>::type lds_quad(const unsigned char* p) {
+  return *reinterpret_cast<const typename Quad<T>::type*>(p);
+}
+
+// Row-major operand fragment (rows = positions rb*16.., contraction = features 32s..32s+31)
+template <typename T, int DF>
+__device__ __forceinline__ Frag<T> row_frag(const unsigned char* img, int rb, int s, int lane) {
+  typedef Img<T, DF, false> I;
+  typedef typename Quad<T>::type Q4;
+  const int r = 16 * rb + (lane & 15), g = lane >> 4;
+  const int q0 = 8 * s + g, q1 = q0 + 4;
+  const Q4 z = {};
+  const Q4 lo = lds_quad<T>(img + I::off(r, q0));
+  const Q4 hi = (q1 < I::NQ) ? lds_quad<T>(img + I::off(r, q1)) : z;
+  Frag<T> f;
+  if constexpr (sizeof(T) == 2) {
+    f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  } else {
+    f.lo = lo; f.hi = hi;
+  }
+  return f;
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Position-contracted operand fragment (rows = features fb*16.., contraction = positions
+// 32ks..32ks+31) from a row-major TR-swizzled bf16 image, by two transposing LDS reads:
+// in each 16-lane group the read returns to lane i, element b, element i%4 of the quad read
+// by lane 4b + i/4; so lane k of group g reads row 32ks + 16h + 4g + k/4, quad 4fb + k%4.
+template <int C, int DF>
+__device__ __forceinline__ Frag<bf16> tr_frag(const unsigned char* img, int fb, int ks, int lane) {
+  typedef Img<bf16, DF, true> I;
+  const int k = lane & 15, g = lane >> 4;
+  const int q = 4 * fb + (k & 3);
+  const int t0 = 32 * ks + 4 * g + (k >> 2);
+  const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(img + I::off(t0, q)));
+  s16x4 v1 = {0, 0, 0, 0};
+  if (C >= 32)
+    v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(img + I::off(t0 + 16, q)));
+  Frag<bf16> f;
+  f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+  return f;
+}
+
+// position-contracted operand: transposing read (bf16) or fragment-order slot (f32)
+template <typename T, int C, int DF>
+__device__ __forceinline__ Frag<T> col_frag(const unsigned char* base, int fb, int ks, int lane) {
+  if constexpr (TrNative<T>::value) {
+    return tr_frag<C, DF>(base, fb, ks, lane);
+  } else {
+    constexpr int NKS_C = (C + 31) / 32;
+    return lds_frag<T>(reinterpret_cast<const T*>(base), fb * NKS_C + ks, lane);
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// per-wave building blocks
+// ----------------------------------------------------------------------------------------
+
 // Decayed chunk state for the wave's 16 value columns, as 16x16 tiles F[dk block]:
-//   F = sum_{s in chunk} exp(gtot - A_s) k_s v_s^T   (gtot = A at the chunk's last position)
+//   F = sum_{s in chunk} exp(gtot - A_s) k_s v_s^T   (the decay is already applied to k~)
 template <typename T, int C, int DK>
-__device__ __forceinline__ void chunk_state(const T* ktf, const Frag<T> (&vfr)[(C + 31) / 32],
-                                            const float* aloc, float gtot, int lane,
-                                            f32x4 (&F)[DK / 16]) {
+__device__ __forceinline__ void chunk_state(const unsigned char* kt, const Frag<T> (&vfr)[(C + 31) / 32],
+                                            int lane, f32x4 (&F)[DK / 16]) {
   constexpr int NKS_C = (C + 31) / 32;
   constexpr int NDKB = DK / 16;
-  const int g = lane >> 4;
 #pragma unroll
   for (int b = 0; b < NDKB; ++b) F[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < NKS_C; ++ks) {
-    f32x4 wlo, whi;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int tlo = 32 * ks + 4 * g + e, thi = tlo + 16;
-      wlo[e] = tlo < C ? __expf(gtot - aloc[min(tlo, C - 1)]) : 0.f;
-      whi[e] = thi < C ? __expf(gtot - aloc[min(thi, C - 1)]) : 0.f;
-    }
-#pragma unroll
-    for (int b = 0; b < NDKB; ++b) {
-      f32x4 lo, hi;
-      frag_to_f32(lds_frag<T>(ktf, b * NKS_C + ks, lane), lo, hi);
-      mma(F[b], frag_from<T>(lo * wlo, hi * whi), vfr[ks]);
-    }
+    for (int b = 0; b < NDKB; ++b) mma(F[b], col_frag<T, C, DK>(kt, b, ks, lane), vfr[ks]);
   }
 }
 
@@ -295,12 +477,12 @@ __device__ __forceinline__ Frag<T> node_frag(const f32x4 (&N)[DK / 16], int s) {
 }
 
 // One Fenwick node read out by every query of the chunk (level-weighted, decayed):
-//   O[qb] += lambda[i, lev] * exp(aloc[i] + doff) * (N^T q_i)
-// doff = log decay from the node's last position to the chunk's first position (<= 0).
+//   O[qb] += lambda[i, lev] * exp(A_i) * edoff * (N^T q_i)
+// edoff = exp(log decay from the node's last position to the chunk's first position).
 template <typename T, int C, int DK>
-__device__ __forceinline__ void node_readout(const Frag<T> (&A)[(DK + 31) / 32], const T* qf,
-                                             const float* lam, int L, const float* aloc,
-                                             int lev, float doff, int lane, f32x4 (&O)[C / 16]) {
+__device__ __forceinline__ void node_readout(const Frag<T> (&A)[(DK + 31) / 32], const unsigned char* qimg,
+                                             const float* lam, int L, const float* ea,
+                                             int lev, float edoff, int lane, f32x4 (&O)[C / 16]) {
   constexpr int NQB = C / 16;
   constexpr int NKS_D = (DK + 31) / 32;
   const int j = lane & 15;
@@ -310,23 +492,25 @@ __device__ __forceinline__ void node_readout(const Frag<T> (&A)[(DK + 31) / 32],
 #pragma unroll
   for (int s = 0; s < NKS_D; ++s) {
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) mma(Y[qb], A[s], lds_frag<T>(qf, qb * NKS_D + s, lane));
+    for (int qb = 0; qb < NQB; ++qb) mma(Y[qb], A[s], row_frag<T, DK>(qimg, qb, s, lane));
   }
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
     const int qi = 16 * qb + j;
-    const float sc = lam[qi * L + lev] * __expf(aloc[qi] + doff);
-    O[qb] += sc * Y[qb];
+    O[qb] += (lam[qi * L + lev] * ea[qi] * edoff) * Y[qb];
   }
 }
 
 // Masked score unit (query block qb, key step ks): the two 16x16 score tiles of keys
 // 32ks..32ks+31 against queries 16qb..16qb+15, masked by
 //   lambda[i, bit_length(i ^ s)] * exp(A_i - A_s) for s <= i (chunk-local i, s), else 0,
-// returned as the P^T operand fragment of the value product.
+// returned as the P^T operand fragment of the value product. exp(A_i - A_s) is taken as
+// e^{A_i} e^{-A_s} when the chunk's |A| < 40 (`fact`), else directly.
 template <typename T, int C, int DK>
-__device__ __forceinline__ Frag<T> score_unit(const T* qf, const T* kf, const float* lam, int L,
-                                              const float* aloc, int qb, int ks, int lane) {
+__device__ __forceinline__ Frag<T> score_unit(const unsigned char* qimg, const unsigned char* kimg,
+                                              const float* lam, int L, const float* aloc,
+                                              const float* ea, const float* eb, bool fact,
+                                              int qb, int ks, int lane) {
   constexpr int NKS_D = (DK + 31) / 32;
   const int j = lane & 15, g = lane >> 4;
   const int kb0 = 2 * ks, kb1 = 2 * ks + 1;
@@ -334,21 +518,49 @@ __device__ __forceinline__ Frag<T> score_unit(const T* qf, const T* kf, const fl
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < NKS_D; ++s) {
-    const Frag<T> bq = lds_frag<T>(qf, qb * NKS_D + s, lane);
-    mma(s0, lds_frag<T>(kf, kb0 * NKS_D + s, lane), bq);
-    if (has1) mma(s1, lds_frag<T>(kf, kb1 * NKS_D + s, lane), bq);
+    const Frag<T> bq = row_frag<T, DK>(qimg, qb, s, lane);
+    mma(s0, row_frag<T, DK>(kimg, kb0, s, lane), bq);
+    if (has1) mma(s1, row_frag<T, DK>(kimg, kb1, s, lane), bq);
   }
   const int qi = 16 * qb + j;
-  const float aq = aloc[qi];
   const float* lrow = lam + qi * L;
-  f32x4 p0, p1;
+  const int key0 = 16 * kb0 + 4 * g;
+  f32x4 d0, d1;
+  if (fact) {
+    const float eq = ea[qi];
+    d0 = eq * *reinterpret_cast<const f32x4*>(eb + key0);
+    d1 = has1 ? eq * *reinterpret_cast<const f32x4*>(eb + key0 + 16) : f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
+    const float aq = aloc[qi];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int key0 = 16 * kb0 + 4 * g + r, key1 = key0 + 16;
-    const int l0 = min(bit_length((unsigned)(qi ^ key0)), L - 1);
-    const int l1 = min(bit_length((unsigned)(qi ^ key1)), L - 1);
-    p0[r] = key0 <= qi ? s0[r] * lrow[l0] * __expf(aq - aloc[key0]) : 0.f;
-    p1[r] = (has1 && key1 <= qi) ? s1[r] * lrow[l1] * __expf(aq - aloc[min(key1, C - 1)]) : 0.f;
+    for (int r = 0; r < 4; ++r) {
+      d0[r] = key0 + r <= qi ? __expf(aq - aloc[key0 + r]) : 0.f;
+      d1[r] = (has1 && key0 + 16 + r <= qi) ? __expf(aq - aloc[min(key0 + 16 + r, C - 1)]) : 0.f;
+    }
+  }
+  f32x4 p0, p1;
+  if (kb0 < qb) {
+    // whole tile below the diagonal: one level for the row
+    const float lv = lrow[min(4 + bit_length((unsigned)(kb0 ^ qb)), L - 1)];
+    p0 = (lv * s0) * d0;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = key0 + r;
+      p0[r] = key <= qi ? s0[r] * lrow[min(bit_length((unsigned)(qi ^ key)), L - 1)] * d0[r] : 0.f;
+    }
+  }
+  if (!has1) {
+    p1 = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else if (kb1 < qb) {
+    const float lv = lrow[min(4 + bit_length((unsigned)(kb1 ^ qb)), L - 1)];
+    p1 = (lv * s1) * d1;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = key0 + 16 + r;
+      p1[r] = key <= qi ? s1[r] * lrow[min(bit_length((unsigned)(qi ^ key)), L - 1)] * d1[r] : 0.f;
+    }
   }
   return frag_from<T>(p0, p1);
 }
@@ -365,8 +577,62 @@ template <> __device__ __forceinline__ void store_quad<float>(float* p, const f3
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 constexpr int num_units(int nqb) { return nqb <= 0 ? 0 : num_units(nqb - 1) + (nqb - 1) / 2 + 1; }
-// local Fenwick levels kept in registers per sweep: sweeps of up to 8 chunks (4 for dk=128)
-template <int DK> struct SweepCap { static constexpr int LMAX = DK >= 128 ? 2 : 3; };
+
+__device__ __forceinline__ void unit_decode(int un, int& qb, int& ks) {
+  qb = 0;
+  ks = un;
+  while (ks >= qb / 2 + 1) { ks -= qb / 2 + 1; ++qb; }
+}
+
+// Stages one chunk: q, k as row-major images (scores, read-outs), k~ = exp(g - A_s) k_s and v
+// as position-contracted operands (states, P.V), lambda rows, and (wave 0) A, e^A, e^-A.
+template <typename T, int C, int DK, int DV, int NT, bool WITH_Q>
+struct ChunkStage {
+  BlockRegs<T, C, DK, NT> qr, kr;
+  BlockRegs<T, C, DV, NT> vr;
+  LamRegs<C, NT> lr;
+  DecayRegs<C> ar;
+
+  __device__ __forceinline__ void fetch(const T* qg, const T* kg, const T* vg, const float* lamg,
+                                        const float* lag, int L, int valid, int tid, int lane) {
+    if (WITH_Q) {
+      qr.fetch(qg, valid, tid);
+      lr.fetch(lamg, valid * L, tid);
+    }
+    kr.fetch(kg, valid, tid);
+    vr.fetch(vg, valid, tid);
+    ar.fetch(lag, valid, lane);
+  }
+
+  __device__ __forceinline__ void commit(const ChunkSmem& S, unsigned char* smem, int L, int tid,
+                                         int lane, int w) {
+    ar.scan(lane);
+    const float g = ar.at(C - 1);
+    typedef BlockRegs<T, C, DK, NT> KR;
+    float ws[KR::ITERS][2];
+#pragma unroll
+    for (int it = 0; it < KR::ITERS; ++it) {
+      const int r0 = KR::row0(tid, it);
+      ws[it][0] = __expf(g - ar.at(r0));
+      ws[it][1] = __expf(g - ar.at(r0 + 1));
+    }
+    if (WITH_Q) {
+      qr.template commit_image<false, false>(smem + S.qimg, tid, nullptr);
+      kr.template commit_image<false, false>(smem + S.kimg, tid, nullptr);
+      lr.commit(reinterpret_cast<float*>(smem + S.lam), C * L, tid);
+    }
+    if constexpr (TrNative<T>::value) {
+      kr.template commit_image<true, true>(smem + S.kt, tid, ws);
+      vr.template commit_image<true, false>(smem + S.vt, tid, nullptr);
+    } else {
+      kr.template commit_frags<true>(reinterpret_cast<T*>(smem + S.kt), tid, ws);
+      vr.template commit_frags<false>(reinterpret_cast<T*>(smem + S.vt), tid, nullptr);
+    }
+    if (w == 0)
+      ar.publish(reinterpret_cast<float*>(smem + S.aloc), reinterpret_cast<float*>(smem + S.ea),
+                 reinterpret_cast<float*>(smem + S.eb), reinterpret_cast<int*>(smem + S.flag), lane);
+  }
+};
 
 // ----------------------------------------------------------------------------------------
 // kernels
@@ -376,54 +642,57 @@ struct Params {
   const void* q; const void* k; const void* v;
   const float* log_a; const float* lam;
   void* out;
-  int BH, T, DV, L;
+  int BH, T, L;
   int nchunks;      // ceil(T / C)
-  int sweep;        // R: consecutive chunks per workgroup (power of two)
+  int sweep;        // R: consecutive chunks per workgroup (power of two, <= kSweepCap)
   int m;            // log2(R)
   int nsweep;       // ceil(nchunks / R)
-  float* hbuf;      // [BH][nsweep-1][DV/16][DK/16][64] f32x4: sweep totals -> Fenwick nodes
-  float* gbuf;      // [BH][nsweep-1]: sweep log decays -> Fenwick node log decays
+  float* hbuf;      // [BH][nsweep-1][DV/16][DK/16][64] f32x4: sweep totals
+  float* gbuf;      // [BH][nsweep-1]: sweep log decays
+  float* gnode;     // [BH][nsweep-1]: Fenwick node log decays
   void* nodes;      // [BH][nsweep-1][DV/16][ceil(DK/32)][64] Frag<T>: nodes as read-out operands
-  int xcd_per;      // query grid: workgroups per XCD slice
+  int xcd_per;      // output grid: workgroups per XCD slice
+  int fen_lanes;    // Fenwick kernel: fragment lanes per workgroup slice (shared-memory pass)
 };
 
 // Sweep totals. Grid (nsweep-1, BH): only whole sweeps before the last one are needed.
 //   H = sum_{s in sweep} exp(A_end - A_s) k_s v_s^T,  G = A_end - A_{start-1}
-template <typename T, int C, int DK>
-__global__ __launch_bounds__(kMaxThreads) void lla_sweep_state_kernel(Params p) {
+template <typename T, int C, int DK, int DV>
+__global__ __launch_bounds__(4 * DV) void lla_sweep_state_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  constexpr int NDKB = DK / 16, NKS_C = (C + 31) / 32;
-  const int tid = threadIdx.x, nthreads = blockDim.x;
-  const int lane = tid & 63, w = tid >> 6;
+  constexpr int NT = 4 * DV, NDKB = DK / 16, NKS_C = (C + 31) / 32;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int sw = blockIdx.x, bh = blockIdx.y;
-  const int DV = p.DV, ns = p.nsweep - 1;
+  const int ns = p.nsweep - 1;
   const ChunkSmem S = chunk_smem<T>(C, DK, DV, p.L, false, false);
-  T* ktf = reinterpret_cast<T*>(smem + S.ktf);
-  T* vtf = reinterpret_cast<T*>(smem + S.vtf);
-  float* aloc = reinterpret_cast<float*>(smem + S.aloc);
 
   const size_t hoff = (size_t)bh * p.T;
   const T* kg = reinterpret_cast<const T*>(p.k) + hoff * DK;
   const T* vg = reinterpret_cast<const T*>(p.v) + hoff * DV;
   const float* lag = p.log_a + hoff;
 
+  ChunkStage<T, C, DK, DV, NT, false> st;
+  auto fetch = [&](int u) {
+    const int t0 = (sw * p.sweep + u) * C;
+    st.fetch(nullptr, kg + (size_t)t0 * DK, vg + (size_t)t0 * DV, nullptr, lag + t0, 0, C, tid, lane);
+  };
+  fetch(0);
+
   f32x4 H[NDKB];
 #pragma unroll
   for (int b = 0; b < NDKB; ++b) H[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   float G = 0.f;
   for (int u = 0; u < p.sweep; ++u) {
-    const int t0 = (sw * p.sweep + u) * C;
     if (u) __syncthreads();
-    load_block<T, C, false, true>(kg + (size_t)t0 * DK, DK, C, nullptr, ktf, tid, nthreads);
-    load_block<T, C, false, true>(vg + (size_t)t0 * DV, DV, C, nullptr, vtf, tid, nthreads);
-    if (w == 0) chunk_cumsum<C>(lag + t0, C, aloc, lane);
+    st.commit(S, smem, 0, tid, lane, w);
     __syncthreads();
-    const float gtot = aloc[C - 1];
+    fetch(u + 1 < p.sweep ? u + 1 : u);     // unconditional: re-reads this chunk at the end
+    const float gtot = reinterpret_cast<const float*>(smem + S.aloc)[C - 1];
     Frag<T> vfr[NKS_C];
 #pragma unroll
-    for (int ks = 0; ks < NKS_C; ++ks) vfr[ks] = lds_frag<T>(vtf, w * NKS_C + ks, lane);
+    for (int ks = 0; ks < NKS_C; ++ks) vfr[ks] = col_frag<T, C, DV>(smem + S.vt, w, ks, lane);
     f32x4 F[NDKB];
-    chunk_state<T, C, DK>(ktf, vfr, aloc, gtot, lane, F);
+    chunk_state<T, C, DK>(smem + S.kt, vfr, lane, F);
     const float d = __expf(gtot);
 #pragma unroll
     for (int b = 0; b < NDKB; ++b) H[b] = d * H[b] + F[b];
@@ -435,88 +704,105 @@ __global__ __launch_bounds__(kMaxThreads) void lla_sweep_state_kernel(Params p) 
   if (tid == 0) p.gbuf[(size_t)bh * ns + sw] = G;
 }
 
-// In-place Fenwick up-sweep over the ns = nsweep-1 sweep totals of a head: afterwards slot e
-// holds the node of the lowbit(e+1) sweeps ending at e, decayed to its last position, and
-// gbuf[e] its total log decay. Then every node is written as read-out fragments (Frag<T>).
-// Grid (ceil(DV/16 * ceil(DK/32) * 64 / blockDim), BH); thread = (value block, dk step, lane).
-template <typename T, int DK>
+// Fenwick up-sweep over the ns = nsweep-1 sweep totals of a head, in shared memory. Slot e
+// ends up holding the node of the lowbit(e+1) sweeps ending at e, decayed to its last
+// position (gnode[e]: its total log decay); every node is then written as read-out
+// fragments (Frag<T>). A workgroup owns lanes [l0, l0+nl) of one fragment (value block w,
+// key step s) for all ns nodes. Grid (DV/16 * ceil(DK/32) * 64/nl, BH).
+template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256) void lla_fenwick_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  float* gsh = reinterpret_cast<float*>(smem);
-  constexpr int NDKB = DK / 16, NKS_D = (DK + 31) / 32;
+  constexpr int NDVB = DV / 16, NDKB = DK / 16, NKS_D = (DK + 31) / 32;
   const int ns = p.nsweep - 1;
+  const int nl = p.fen_lanes, per_frag = 64 / nl;
   const int bh = blockIdx.y;
-  const int ndvb = p.DV / 16;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  const bool active = idx < ndvb * NKS_D * 64;
-  const int lane = idx & 63, s = (idx >> 6) % NKS_D, w = (idx >> 6) / NKS_D;
-  const int b0 = 2 * s, b1 = 2 * s + 1;
-  const bool has1 = b1 < NDKB;
+  const int frag = blockIdx.x / per_frag, l0 = (blockIdx.x % per_frag) * nl;
+  const int w = frag / NKS_D, s = frag % NKS_D;
+  const int b0 = 2 * s;
+  const bool has1 = b0 + 1 < NDKB;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int row = 2 * nl;                          // f32x4 per node in this slice
+  f32x4* sh = reinterpret_cast<f32x4*>(smem);      // [ns][2][nl]
+  float* gsh = reinterpret_cast<float*>(sh + (size_t)ns * row);
 
-  float* gb = p.gbuf + (size_t)bh * ns;
-  for (int i = threadIdx.x; i < ns; i += blockDim.x) gsh[i] = gb[i];
+  const f32x4* hb = reinterpret_cast<const f32x4*>(p.hbuf) + (size_t)bh * ns * NDVB * NDKB * 64;
+  for (int i = tid; i < ns * row; i += nt) {
+    const int e = i / row, r = i - e * row, half = r / nl, l = l0 + (r - half * nl);
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (half == 0 || has1) v = hb[(((size_t)e * NDVB + w) * NDKB + b0 + half) * 64 + l];
+    sh[i] = v;
+  }
+  const float* gb = p.gbuf + (size_t)bh * ns;
+  for (int i = tid; i < ns; i += nt) gsh[i] = gb[i];
   __syncthreads();
 
-  f32x4* hb = reinterpret_cast<f32x4*>(p.hbuf) + (size_t)bh * ns * ndvb * NDKB * 64;
-  auto tile = [&](int e, int b) -> f32x4* { return hb + (((size_t)e * ndvb + w) * NDKB + b) * 64 + lane; };
-
   for (int half = 1; half < ns; half <<= 1) {
-    if (active) {
-      for (int e = 2 * half - 1; e < ns; e += 2 * half) {
-        const float d = __expf(gsh[e]);     // decay across the right half (slot e as it is)
-        *tile(e, b0) = d * *tile(e - half, b0) + *tile(e, b0);
-        if (has1) *tile(e, b1) = d * *tile(e - half, b1) + *tile(e, b1);
-      }
+    const int first = 2 * half - 1, step = 2 * half;
+    const int nn = first < ns ? (ns - 1 - first) / step + 1 : 0;
+    for (int i = tid; i < nn * row; i += nt) {
+      const int k = i / row, r = i - k * row;
+      const int e = first + k * step;
+      const float d = __expf(gsh[e]);            // decay across the right half (slot e as it is)
+      sh[e * row + r] = d * sh[(e - half) * row + r] + sh[e * row + r];
     }
     __syncthreads();
-    for (int e = 2 * half - 1 + 2 * half * threadIdx.x; e < ns; e += 2 * half * blockDim.x)
+    for (int k = tid; k < nn; k += nt) {
+      const int e = first + k * step;
       gsh[e] += gsh[e - half];
+    }
     __syncthreads();
   }
-  if (active) {
-    Frag<T>* nd = reinterpret_cast<Frag<T>*>(p.nodes);
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    for (int e = 0; e < ns; ++e) {
-      const f32x4 lo = *tile(e, b0);
-      const f32x4 hi = has1 ? *tile(e, b1) : z;
-      nd[((((size_t)bh * ns + e) * ndvb + w) * NKS_D + s) * 64 + lane] = frag_from<T>(lo, hi);
-    }
+
+  Frag<T>* nd = reinterpret_cast<Frag<T>*>(p.nodes);
+  for (int i = tid; i < ns * nl; i += nt) {
+    const int e = i / nl, l = i - e * nl;
+    nd[((((size_t)bh * ns + e) * NDVB + w) * NKS_D + s) * 64 + l0 + l] =
+        frag_from<T>(sh[e * row + l], sh[e * row + nl + l]);
   }
   if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i < ns; i += blockDim.x) gb[i] = gsh[i];
+    for (int i = tid; i < ns; i += nt) p.gnode[(size_t)bh * ns + i] = gsh[i];
 }
 
-// The output kernel: one workgroup walks the R chunks of one sweep of one head.
+// The output kernel: one workgroup walks the R chunks of one sweep of one head; one wave per
+// 16 value columns. Global loads are issued branch-free so that waits count exactly:
+//   * the Fenwick nodes over earlier sweeps (up to XREG of them) are loaded into registers
+//     once, before the first chunk;
+//   * the inputs of chunk u+1 are loaded into registers right after chunk u is staged in
+//     shared memory (the current chunk again after the last one), so they are in flight while
+//     chunk u is computed, and nothing inside the chunk waits for them.
 // Workgroup ids are dealt round-robin to the 8 XCDs; consecutive sweeps of a head are mapped
 // to the same XCD so that the Fenwick nodes they share stay in one L2.
-// ALIAS: the masked scores reuse the key fragments' shared memory (needed when C=128 and
-// the head dims are 128); each wave then holds its score units in registers across a barrier.
-template <typename T, int C, int DK, bool ALIAS>
-__global__ __launch_bounds__(kMaxThreads) void lla_query_kernel(Params p) {
+// ALIAS: the masked scores reuse the key image's shared memory (C=128 with 128-wide heads);
+// each wave then holds its score units in registers across a barrier.
+template <typename T, int C, int DK, int DV, bool ALIAS>
+__global__ __launch_bounds__(4 * DV, 2) void lla_query_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  constexpr int NQB = C / 16, NKS_C = (C + 31) / 32, NKS_D = (DK + 31) / 32, NDKB = DK / 16;
+  constexpr int NT = 4 * DV, NW = DV / 16;
+  constexpr int NQB = C / 16, NKS_C = (C + 31) / 32, NKS_D = (DK + 31) / 32;
   constexpr int J = ilog2(C);
-  constexpr int LMAX = SweepCap<DK>::LMAX;
+  constexpr int LMAX = ilog2(kSweepCap);
   constexpr int NUNITS = num_units(NQB);
-  constexpr int UHOLD = ALIAS ? 4 : 1;
+  constexpr int UHOLD = ALIAS ? (NUNITS + NW - 1) / NW : 1;
+  constexpr int XREG = DK >= 128 ? 2 : 5;   // nodes over earlier sweeps held in registers
 
   const int total = p.nsweep * p.BH;
   const int lin = (blockIdx.x & 7) * p.xcd_per + (blockIdx.x >> 3);
   if (lin >= total) return;
   const int bh = lin / p.nsweep, sw = lin - bh * p.nsweep;
 
-  const int tid = threadIdx.x, nthreads = blockDim.x;
-  const int lane = tid & 63, w = tid >> 6, nw = nthreads >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
   const int j = lane & 15, g = lane >> 4;
-  const int DV = p.DV, L = p.L, ns = p.nsweep - 1;
+  const int L = p.L, ns = p.nsweep - 1;
   const ChunkSmem S = chunk_smem<T>(C, DK, DV, L, true, ALIAS);
-  T* qf = reinterpret_cast<T*>(smem + S.qf);
-  T* kf = reinterpret_cast<T*>(smem + S.kf);
+  const unsigned char* qimg = smem + S.qimg;
+  const unsigned char* kimg = smem + S.kimg;
   T* pf = reinterpret_cast<T*>(smem + S.pf);
-  T* ktf = reinterpret_cast<T*>(smem + S.ktf);
-  T* vtf = reinterpret_cast<T*>(smem + S.vtf);
-  float* lam = reinterpret_cast<float*>(smem + S.lam);
-  float* aloc = reinterpret_cast<float*>(smem + S.aloc);
+  const float* lam = reinterpret_cast<const float*>(smem + S.lam);
+  const float* aloc = reinterpret_cast<const float*>(smem + S.aloc);
+  const float* ea = reinterpret_cast<const float*>(smem + S.ea);
+  const float* eb = reinterpret_cast<const float*>(smem + S.eb);
+  const int* flag = reinterpret_cast<const int*>(smem + S.flag);
 
   const size_t hoff = (size_t)bh * p.T;
   const T* qg = reinterpret_cast<const T*>(p.q) + hoff * DK;
@@ -529,35 +815,72 @@ __global__ __launch_bounds__(kMaxThreads) void lla_query_kernel(Params p) {
   const int c0 = sw * p.sweep;
   const int nch = min(p.sweep, p.nchunks - c0);
 
-  f32x4 LN[LMAX][NDKB];   // local Fenwick nodes (this wave's value columns)
-  float LD[LMAX];         // log decay from each node's last position to the current chunk start
+  // nodes over earlier sweeps: one per set bit of sw, lowest first; node x ends at sweep
+  // ((sw >> jb) << jb) - 1 for the x-th set bit jb
+  const int next = __builtin_popcount((unsigned)sw);
+  const Frag<T>* nd = reinterpret_cast<const Frag<T>*>(p.nodes) +
+                      ((size_t)bh * (ns > 0 ? ns : 0) * NW + w) * NKS_D * 64 + lane;
+  const float* gn = p.gnode + (size_t)bh * (ns > 0 ? ns : 0);
+  auto node_index = [&](int x) {      // sweep index the x-th node ends at (clamped to 0)
+    unsigned m = (unsigned)sw;
+    for (int i = 0; i < x && m; ++i) m &= m - 1;
+    return m ? ((sw >> __builtin_ctz(m)) << __builtin_ctz(m)) - 1 : 0;
+  };
+  auto node_level = [&](int x) {
+    unsigned m = (unsigned)sw;
+    for (int i = 0; i < x && m; ++i) m &= m - 1;
+    return m ? J + 1 + p.m + __builtin_ctz(m) : 0;
+  };
+  auto load_node = [&](Frag<T> (&A)[NKS_D], int e) {
+#pragma unroll
+    for (int s = 0; s < NKS_D; ++s) A[s] = nd[(size_t)e * NW * NKS_D * 64 + s * 64];
+  };
+
+  Frag<T> X[XREG][NKS_D];
+  float XD[XREG];            // log decay across each node
+  if (ns > 0) {
+#pragma unroll
+    for (int x = 0; x < XREG; ++x) {
+      const int e = node_index(x);
+      load_node(X[x], e);
+      XD[x] = gn[e];
+    }
+  }
+  ChunkStage<T, C, DK, DV, NT, true> st;
+  auto prefetch = [&](int u) {
+    const int t0 = (c0 + u) * C;
+    const int valid = min(C, p.T - t0);
+    st.fetch(qg + (size_t)t0 * DK, kg + (size_t)t0 * DK, vg + (size_t)t0 * DV, lamg + (size_t)t0 * L,
+             lag + t0, L, valid, tid, lane);
+  };
+  prefetch(0);
+
+  Frag<T> LN[LMAX][NKS_D];   // Fenwick nodes inside the sweep (this wave's value columns)
+  float LD[LMAX];            // log decay from each node's last position to the current chunk start
 #pragma unroll
   for (int a = 0; a < LMAX; ++a) {
     LD[a] = 0.f;
 #pragma unroll
-    for (int b = 0; b < NDKB; ++b) LN[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < NKS_D; ++s) LN[a][s] = frag_from<T>(f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f});
   }
-  float gam = 0.f;        // log decay from the sweep's first position to the current chunk start
+  float gam = 0.f;           // log decay from the sweep's first position to the current chunk start
 
   for (int u = 0; u < nch; ++u) {
     const int t0 = (c0 + u) * C;
     const int valid = min(C, p.T - t0);
     if (u) __syncthreads();
-    load_block<T, C, true, false>(qg + (size_t)t0 * DK, DK, valid, qf, nullptr, tid, nthreads);
-    load_block<T, C, true, true>(kg + (size_t)t0 * DK, DK, valid, kf, ktf, tid, nthreads);
-    load_block<T, C, false, true>(vg + (size_t)t0 * DV, DV, valid, nullptr, vtf, tid, nthreads);
-    for (int i = tid; i < C * L; i += nthreads)
-      lam[i] = i < valid * L ? lamg[(size_t)t0 * L + i] : 0.f;
-    if (w == 0) chunk_cumsum<C>(lag + t0, valid, aloc, lane);
+    st.commit(S, smem, L, tid, lane, w);
     __syncthreads();
+    prefetch(u + 1 < nch ? u + 1 : u);     // unconditional: re-reads this chunk after the last
     const float gtot = aloc[C - 1];
+    const bool fact = *flag != 0;
 
     // masked scores -> P^T fragments
     if (!ALIAS) {
-      for (int un = w; un < NUNITS; un += nw) {
-        int qb = 0, ks = un;
-        while (ks >= qb / 2 + 1) { ks -= qb / 2 + 1; ++qb; }
-        const Frag<T> f = score_unit<T, C, DK>(qf, kf, lam, L, aloc, qb, ks, lane);
+      for (int un = w; un < NUNITS; un += NW) {
+        int qb, ks;
+        unit_decode(un, qb, ks);
+        const Frag<T> f = score_unit<T, C, DK>(qimg, kimg, lam, L, aloc, ea, eb, fact, qb, ks, lane);
         reinterpret_cast<Frag<T>*>(pf)[(qb * NKS_C + ks) * 64 + lane] = f;
       }
     } else {
@@ -565,12 +888,12 @@ __global__ __launch_bounds__(kMaxThreads) void lla_query_kernel(Params p) {
       int where[UHOLD];
 #pragma unroll
       for (int h = 0; h < UHOLD; ++h) {
-        const int un = w + h * nw;
+        const int un = w + h * NW;
         where[h] = -1;
         if (un < NUNITS) {
-          int qb = 0, ks = un;
-          while (ks >= qb / 2 + 1) { ks -= qb / 2 + 1; ++qb; }
-          held[h] = score_unit<T, C, DK>(qf, kf, lam, L, aloc, qb, ks, lane);
+          int qb, ks;
+          unit_decode(un, qb, ks);
+          held[h] = score_unit<T, C, DK>(qimg, kimg, lam, L, aloc, ea, eb, fact, qb, ks, lane);
           where[h] = qb * NKS_C + ks;
         }
       }
@@ -584,7 +907,7 @@ __global__ __launch_bounds__(kMaxThreads) void lla_query_kernel(Params p) {
     // intra-chunk values
     Frag<T> vfr[NKS_C];
 #pragma unroll
-    for (int ks = 0; ks < NKS_C; ++ks) vfr[ks] = lds_frag<T>(vtf, w * NKS_C + ks, lane);
+    for (int ks = 0; ks < NKS_C; ++ks) vfr[ks] = col_frag<T, C, DV>(smem + S.vt, w, ks, lane);
     f32x4 O[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -595,27 +918,24 @@ __global__ __launch_bounds__(kMaxThreads) void lla_query_kernel(Params p) {
 
     // Fenwick nodes inside the sweep (levels J+1 .. J+m)
 #pragma unroll
-    for (int a = 0; a < LMAX; ++a) {
-      if ((u >> a) & 1) {
-        Frag<T> A[NKS_D];
-#pragma unroll
-        for (int s = 0; s < NKS_D; ++s) A[s] = node_frag<T, DK>(LN[a], s);
-        node_readout<T, C, DK>(A, qf, lam, L, aloc, J + 1 + a, LD[a], lane, O);
-      }
-    }
-    // Fenwick nodes made of whole earlier sweeps (levels J+m+1 ..)
-    if (sw > 0) {
-      const Frag<T>* nd = reinterpret_cast<const Frag<T>*>(p.nodes);
+    for (int a = 0; a < LMAX; ++a)
+      if ((u >> a) & 1) node_readout<T, C, DK>(LN[a], qimg, lam, L, ea, J + 1 + a, __expf(LD[a]), lane, O);
+
+    // Fenwick nodes made of whole earlier sweeps (levels J+m+1 ..), lowest bit first
+    {
       float dext = 0.f;
-      for (int jb = 0; (sw >> jb) != 0; ++jb) {
-        if (!((sw >> jb) & 1)) continue;
-        const int e = ((sw >> jb) << jb) - 1;
-        Frag<T> A[NKS_D];
 #pragma unroll
-        for (int s = 0; s < NKS_D; ++s)
-          A[s] = nd[((((size_t)bh * ns + e) * (DV / 16) + w) * NKS_D + s) * 64 + lane];
-        node_readout<T, C, DK>(A, qf, lam, L, aloc, J + 1 + p.m + jb, gam + dext, lane, O);
-        dext += p.gbuf[(size_t)bh * ns + e];
+      for (int x = 0; x < XREG; ++x) {
+        if (x < next) {
+          node_readout<T, C, DK>(X[x], qimg, lam, L, ea, node_level(x), __expf(gam + dext), lane, O);
+          dext += XD[x];
+        }
+      }
+      for (int x = XREG; x < next; ++x) {    // beyond the register budget: load on demand
+        Frag<T> A[NKS_D];
+        load_node(A, node_index(x));
+        node_readout<T, C, DK>(A, qimg, lam, L, ea, node_level(x), __expf(gam + dext), lane, O);
+        dext += gn[node_index(x)];
       }
     }
     // store rows [0, valid)
@@ -627,8 +947,9 @@ __global__ __launch_bounds__(kMaxThreads) void lla_query_kernel(Params p) {
 
     // carry the chunk's state into the sweep's Fenwick nodes
     if (u + 1 < nch) {
+      constexpr int NDKB = DK / 16;
       f32x4 F[NDKB];
-      chunk_state<T, C, DK>(ktf, vfr, aloc, gtot, lane, F);
+      chunk_state<T, C, DK>(smem + S.kt, vfr, lane, F);
       const int cz = __builtin_ctz(u + 1);
 #pragma unroll
       for (int a = 0; a < LMAX; ++a) {
@@ -636,7 +957,12 @@ __global__ __launch_bounds__(kMaxThreads) void lla_query_kernel(Params p) {
         if (a < cz) {
           const float d = __expf(LD[a]);
 #pragma unroll
-          for (int b = 0; b < NDKB; ++b) F[b] += d * LN[a][b];
+          for (int s2 = 0; s2 < NKS_D; ++s2) {
+            f32x4 lo, hi;
+            frag_to_f32(LN[a][s2], lo, hi);
+            F[2 * s2] += d * lo;
+            if (2 * s2 + 1 < NDKB) F[2 * s2 + 1] += d * hi;
+          }
         }
       }
 #pragma unroll
@@ -644,7 +970,7 @@ __global__ __launch_bounds__(kMaxThreads) void lla_query_kernel(Params p) {
         if (a == cz) {
           LD[a] = 0.f;
 #pragma unroll
-          for (int b = 0; b < NDKB; ++b) LN[a][b] = F[b];
+          for (int s2 = 0; s2 < NKS_D; ++s2) LN[a][s2] = node_frag<T, DK>(F, s2);
         }
       }
     }

@@ -54,7 +54,7 @@ def test_defaults(L):
     assert L.loglinear_attn_default_sweep(4, 16, 8192, 64, 64, 64, 0) == 4
     assert L.loglinear_attn_default_sweep(1, 1, 64, 64, 64, 64, 0) == 1
     assert L.loglinear_attn_default_sweep(64, 64, 65536, 128, 128, 64, 0) == 4   # capped for dk=128
-    assert L.loglinear_attn_default_sweep(64, 64, 65536, 64, 64, 64, 0) == 8
+    assert L.loglinear_attn_default_sweep(64, 64, 65536, 64, 64, 64, 0) == 4
 
 
 def test_workspace_bytes(L):
@@ -64,8 +64,8 @@ def test_workspace_bytes(L):
     n = ws(4, 16, 8192, 64, 64, 64, 4, 0)
     ns = 8192 // 64 // 4 - 1
     per = 64 * ns
-    expect = per * 64 * 64 * 4 + per * 4 + per * 4 * 2 * 512 * 2
-    assert expect <= n <= expect + 3 * 256
+    expect = per * 64 * 64 * 4 + 2 * per * 4 + per * 4 * 2 * 512 * 2
+    assert expect <= n <= expect + 4 * 256
     assert ws(4, 16, 8192, 48, 64, 64, 4, 0) == 0           # invalid -> 0
     assert ws(1, 1, 1000, 64, 64, 64, 2, 0) > 0             # ragged T
 
@@ -96,7 +96,7 @@ def _call(L, a):
     (dict(chunk=24), _lib.LLA_ERR_UNSUPPORTED),
     (dict(sweep=3), _lib.LLA_ERR_UNSUPPORTED),
     (dict(sweep=16), _lib.LLA_ERR_UNSUPPORTED),
-    (dict(dk=128, dv=128, sweep=8), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(sweep=8), _lib.LLA_ERR_UNSUPPORTED),
     (dict(B=70000), _lib.LLA_ERR_UNSUPPORTED),
     (dict(q=None), _lib.LLA_ERR_INVALID_ARG),
     (dict(lam=None), _lib.LLA_ERR_INVALID_ARG),

@@ -44,7 +44,7 @@ def test_small_f32_workload_full():
     check_full(x, "f32", chunk=w.chunk)
 
 
-@pytest.mark.parametrize("chunk,sweep", [(16, 1), (16, 2), (16, 4), (16, 8), (32, 1), (32, 4), (64, 2), (128, 1)])
+@pytest.mark.parametrize("chunk,sweep", [(16, 1), (16, 2), (16, 4), (32, 1), (32, 4), (64, 2), (128, 1), (128, 2)])
 def test_small_f32_chunk_and_sweep_invariance(chunk, sweep):
     w = WORKLOADS["b1h2_t256_d16_f32"]
     x = generate(w, seed=0, log_a_mode="lowdecay")
@@ -65,8 +65,10 @@ SHAPES = [
     (1, 1, 1024, 64, 64, 64, 4),     # several sweeps
     (1, 2, 1000, 128, 128, 64, 4),   # d = 128, ragged
     (1, 1, 512, 128, 64, 128, 2),    # C = 128
-    (2, 2, 768, 16, 128, 32, 8),     # non power-of-two sweep count
-    (1, 1, 4160, 64, 64, 64, 8),     # 65 chunks: many sweeps + one extra chunk
+    (2, 2, 768, 16, 128, 32, 4),     # non power-of-two sweep count
+    (1, 1, 4160, 64, 64, 64, 4),     # 65 chunks: many sweeps + one extra chunk
+    (1, 2, 8192, 32, 32, 16, 1),     # 512 sweeps: Fenwick pass with narrow slices
+    (1, 1, 2048, 128, 128, 128, 2),  # C = 128, d = 128: aliased score storage
 ]
 
 
