@@ -7,7 +7,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "../../include/loglinear_attn.h"
+#include "loglinear_attn.h"
 #include "lla_dispatch.hpp"
 #include "lla_kernels.hpp"
 

@@ -661,7 +661,8 @@ template <typename T, int C, int DK, int DV>
 __global__ __launch_bounds__(4 * DV) void lla_sweep_state_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int NT = 4 * DV, NDKB = DK / 16, NKS_C = (C + 31) / 32;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index: uniform
   const int sw = blockIdx.x, bh = blockIdx.y;
   const int ns = p.nsweep - 1;
   const ChunkSmem S = chunk_smem<T>(C, DK, DV, p.L, false, false);
@@ -791,7 +792,8 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_query_kernel(Params p) {
   const int bh = lin / p.nsweep, sw = lin - bh * p.nsweep;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index: uniform
   const int j = lane & 15, g = lane >> 4;
   const int L = p.L, ns = p.nsweep - 1;
   const ChunkSmem S = chunk_smem<T>(C, DK, DV, L, true, ALIAS);
@@ -872,8 +874,8 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_query_kernel(Params p) {
     st.commit(S, smem, L, tid, lane, w);
     __syncthreads();
     prefetch(u + 1 < nch ? u + 1 : u);     // unconditional: re-reads this chunk after the last
-    const float gtot = aloc[C - 1];
-    const bool fact = *flag != 0;
+    const float gtot = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, aloc[C - 1])));
+    const bool fact = __builtin_amdgcn_readfirstlane(*flag) != 0;
 
     // masked scores -> P^T fragments
     if (!ALIAS) {
