@@ -3,11 +3,11 @@
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME]
 
-One step = one call of the C-ABI forward entry (sweep totals, Fenwick pass over sweeps,
-output kernel) over one batch of synthetic inputs already resident in HBM. Prints ONE
-JSON line: tokens/s (B*T per call), the roofline of the dominant kernel (the output
-kernel, timed live with the HIP events the library records around each of its kernels),
-and the CPU oracle timed on a bounded sample of the same workload.
+One step = one call of the C-ABI forward entry (a fill kernel clearing the ticket counter
+and node flags, then the fused forward kernel) over one batch of synthetic inputs already
+resident in HBM. Prints ONE JSON line: tokens/s (B*T per call), the roofline of the
+forward kernel (timed live with the HIP events the library records around its kernels on
+the launch stream), and the CPU oracle timed on a bounded sample of the same workload.
 
 Only one GPU is used; --gpus N with N > 1 exits with a message.
 """
@@ -99,8 +99,8 @@ def main(argv=None) -> int:
                     help="skip the cold-cache, copy-bandwidth and CPU legs (profiler runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device copies of MIB MiB (hardware-counter calibration)")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_query_kernel.json"),
-                    help="measured HBM traffic of the output kernel (from rocprofv3 counters)")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_fused_kernel.json"),
+                    help="measured HBM traffic of the forward kernel (from rocprofv3 counters)")
     a = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -142,7 +142,7 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream(dev)
 
     def new_events():
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         for e in evs:
             e.record(stream)        # creates the underlying hipEvent_t
         return evs
@@ -162,11 +162,10 @@ def main(argv=None) -> int:
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
 
-    stage = {"sweep_state": 0.0, "fenwick": 0.0, "output": 0.0}
+    stage = {"fill": 0.0, "forward": 0.0}
     for evs in evsets:
-        stage["sweep_state"] += evs[0].elapsed_time(evs[1])
-        stage["fenwick"] += evs[1].elapsed_time(evs[2])
-        stage["output"] += evs[2].elapsed_time(evs[3])
+        stage["fill"] += evs[0].elapsed_time(evs[1])
+        stage["forward"] += evs[1].elapsed_time(evs[2])
     stage = {k: v / a.steps for k, v in stage.items()}
 
     tokens = w.B * w.T
@@ -175,7 +174,7 @@ def main(argv=None) -> int:
     ms_per_step = elapsed / a.steps * 1e3
     value = tokens * a.steps / elapsed
 
-    t_out = stage["output"] * 1e-3
+    t_out = stage["forward"] * 1e-3
     achieved = byte_ht * ht / t_out / 1e9
     traffic = None
     if os.path.exists(a.traffic):
@@ -209,8 +208,8 @@ def main(argv=None) -> int:
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": "lla_query_kernel",
-            "kernel_ms": stage["output"],
+            "kernel": "lla_fused_kernel",
+            "kernel_ms": stage["forward"],
             "algorithmic_bytes_per_launch": byte_ht * ht,
         },
         "stages_ms": stage,

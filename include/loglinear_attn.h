@@ -29,16 +29,26 @@
  * lambda finite and >= 0 (the arithmetic does not depend on either sign, but
  * decay factors above 1 can overflow), q/k/v finite.
  *
- * Supported: B, H, T >= 0 (any product that is 0 is a no-op); dk, dv in
- * {16, 32, 64, 128}; chunk in {16, 32, 64, 128}; any T (a ragged last chunk is
- * masked). Output is bitwise deterministic for identical inputs and arguments.
+ * Supported: B, H, T >= 0 (any product that is 0 is a no-op); B*H <= 65535;
+ * dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64, 128}; any T up to 2^23
+ * (L <= 24; a ragged last chunk is masked). Output is bitwise deterministic for
+ * identical inputs and arguments.
+ *
+ * Execution: two kernels on `stream`: a fill kernel that clears the workspace's
+ * ticket counter and node flags, then one forward kernel in which each workgroup
+ * walks R consecutive chunks of one head (a "sweep"), publishes that sweep's Fenwick
+ * node in the workspace and reads the nodes of earlier sweeps of its head, waiting
+ * for them with bounded polls. Workgroups are ordered by an atomic ticket, so a
+ * workgroup only ever waits for workgroups that started before it. Should a wait
+ * nevertheless run out (a fault elsewhere), the affected outputs are written as NaN
+ * and the kernel still completes.
  *
  * Errors: every function validates its arguments on the host before it touches the
  * device and returns a status code (LLA_OK or a negative LLA_ERR_*); nothing is
  * printed, nothing aborts, no exception crosses the ABI. Launches are asynchronous
  * on `stream`; faults during kernel execution surface at the caller's next
  * synchronisation of that stream. Functions are thread safe; the library keeps no
- * state between calls.
+ * state between calls (per-call state lives in the workspace).
  */
 #ifndef LOGLINEAR_ATTN_H
 #define LOGLINEAR_ATTN_H
@@ -56,7 +66,7 @@ typedef struct ihipStream_t* lla_stream_t;
 enum lla_status {
   LLA_OK = 0,
   LLA_ERR_INVALID_ARG = -1,   /* null pointer, negative size, aliasing out, bad struct */
-  LLA_ERR_UNSUPPORTED = -2,   /* dk/dv/chunk outside the supported set, L > 32 */
+  LLA_ERR_UNSUPPORTED = -2,   /* dk/dv/chunk/sweep outside the supported set, L > 24, B*H > 65535 */
   LLA_ERR_HIP = -3,           /* a HIP runtime call or a kernel launch failed */
   LLA_ERR_NO_MEMORY = -4,     /* stream-ordered workspace allocation failed */
   LLA_ERR_WORKSPACE = -5      /* caller workspace smaller than loglinear_attn_workspace_bytes */
@@ -88,15 +98,18 @@ int loglinear_attn_fwd_f32(const float* q, const float* k, const float* v,
  * Extended entry: explicit dtype, chunk size, sweep length and workspace.
  *   chunk : 0 = library default, else one of 16, 32, 64, 128.
  *   sweep : 0 = library default, else the number of consecutive chunks one
- *           workgroup walks (1, 2, 4 or 8; 8 only when dk <= 64).
+ *           workgroup walks (1, 2 or 4).
  *   workspace / workspace_bytes : caller-owned device memory of at least
  *           loglinear_attn_workspace_bytes(...) bytes (256-byte aligned), or
- *           NULL/0 to let the library allocate stream-ordered on `stream`.
+ *           NULL/0 to let the library allocate stream-ordered on `stream`. The
+ *           workspace holds the ticket counter, node flags and nodes of one call:
+ *           two calls that may run concurrently (different streams) must not share
+ *           it; calls ordered on one stream may.
  *   stage_events : optional timing hooks; each non-NULL entry is a hipEvent_t the
- *           library records on `stream`: [0] before the first kernel, [1] after the
- *           sweep-total kernel, [2] after the Fenwick kernel, [3] after the output
- *           kernel ([1] and [2] are still recorded when a single sweep covers T and
- *           those kernels are skipped). The caller owns the events.
+ *           library records on `stream`: [0] before the fill kernel, [1] after it
+ *           (just before the forward kernel), [2] after the forward kernel; [3] is
+ *           not used. [0] and [1] are recorded back to back when a single sweep
+ *           covers T and no fill is needed. The caller owns the events.
  * The result does not depend on chunk or sweep beyond float rounding.
  */
 typedef struct lla_fwd_args {

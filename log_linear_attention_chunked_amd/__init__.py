@@ -108,9 +108,9 @@ def forward(q, k, v, log_a, lam, out=None, *, chunk: int = 0, sweep: int = 0,
     log_a: [B,H,T] float32; lam: [B,H,T,L] float32 with L = num_levels(T).
     Returns out [B,H,T,dv] in q's dtype. ``chunk``/``sweep`` 0 = library default;
     ``workspace``: optional uint8 device tensor of >= workspace_bytes(...) bytes.
-    ``stage_events``: optional 4 recorded ``torch.cuda.Event`` objects (or None) the
-    library records around its kernels (before, after sweep totals, after the Fenwick
-    pass, after the output kernel).
+    ``stage_events``: optional recorded ``torch.cuda.Event`` objects (up to 4, or None)
+    the library records around its kernels: before the fill kernel, before the forward
+    kernel, after the forward kernel (the fourth is not used).
     """
     import torch
     if out is None:

@@ -1,6 +1,6 @@
 // lla_api.hip — C ABI of the log-linear Mamba-2 forward pass: argument validation, plan
 // (chunk, sweep, workspace layout), and the stream-ordered launch sequence
-//   sweep totals -> Fenwick up-sweep over sweeps -> chunk walk with read-outs.
+//   clear ticket counter and node flags -> fused forward kernel.
 // The contract is documented in include/loglinear_attn.h.
 #include <hip/hip_runtime.h>
 
@@ -34,9 +34,18 @@ const KernelSet* kernel_set(int dtype, int C, int DK, int DV) {
 
 }  // namespace lla
 
+namespace lla {
+
+// Clears the workgroup ticket counter and the node flags ahead of a forward pass (a fill
+// kernel rather than a memset so that the sequence stays safe to capture in a graph).
+__global__ void lla_reset_kernel(int* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+}  // namespace lla
+
 namespace {
 
-using lla::ChunkSmem;
 using lla::KernelSet;
 using lla::Params;
 
@@ -45,13 +54,13 @@ inline int bit_len(unsigned x) { int n = 0; while (x) { ++n; x >>= 1; } return n
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr long kTargetWorkgroups = 2048;   // ~8 per CU on 256 CUs
-constexpr int kFenwickSmem = 64 * 1024;    // preferred shared memory of one Fenwick slice
+constexpr int kSpinLimit = 1 << 20;        // polls of a node flag (each ~1 us) before giving up
 
 struct Plan {
   int C, R, m, nchunks, nsweep, ns, L, esize, nw;
   long BH;
-  size_t ws_bytes, off_h, off_g, off_gn, off_nodes;
-  int smem_state, smem_query, smem_query_alias, fen_lanes, smem_fenwick;
+  size_t ws_bytes, off_sync, off_gnode, off_node32, off_nodeT, n_sync;
+  int smem;
 };
 
 int default_chunk(int dk, int dv) { return (dk <= 16 && dv <= 16) ? 16 : 64; }
@@ -61,11 +70,6 @@ int default_sweep(long BH, int T, int C) {
   int R = 1;
   while (R * 2 <= lla::kSweepCap && BH * ((nchunks + 2 * R - 1) / (2 * R)) >= kTargetWorkgroups) R *= 2;
   return R;
-}
-
-int smem_bytes(int dtype, int C, int dk, int dv, int L, bool with_q, bool alias) {
-  return dtype == LLA_DTYPE_BF16 ? lla::chunk_smem<lla::bf16>(C, dk, dv, L, with_q, alias).total
-                                 : lla::chunk_smem<float>(C, dk, dv, L, with_q, alias).total;
 }
 
 // Host-only part of the plan: sizes and layout; no device calls.
@@ -78,7 +82,7 @@ int make_plan(int B, int H, int T, int dk, int dv, int chunk, int sweep, int dty
     return LLA_ERR_UNSUPPORTED;
   const int C = chunk ? chunk : default_chunk(dk, dv);
   const long BH = (long)B * H;
-  if (BH > 65535) return LLA_ERR_UNSUPPORTED;       // grid y dimension of the sweep kernels
+  if (BH > 65535) return LLA_ERR_UNSUPPORTED;
   pl.C = C;
   pl.BH = BH;
   pl.L = T > 0 ? bit_len((unsigned)(T - 1)) + 1 : 0;
@@ -90,21 +94,18 @@ int make_plan(int B, int H, int T, int dk, int dv, int chunk, int sweep, int dty
   pl.m = bit_len((unsigned)pl.R) - 1;
   pl.nsweep = pl.nchunks > 0 ? (pl.nchunks + pl.R - 1) / pl.R : 0;
   pl.ns = pl.nsweep > 1 ? pl.nsweep - 1 : 0;
-  const size_t ns = (size_t)pl.ns;
+  if ((long)pl.nsweep * BH > 0x7fffffffL) return LLA_ERR_UNSUPPORTED;   // one workgroup per sweep
+  const size_t nodes = (size_t)BH * pl.ns * pl.nw;      // (head, node, wave) records
   size_t off = 0;
-  pl.off_h = off;     off = align256(off + (size_t)BH * ns * dk * dv * 4);
-  pl.off_g = off;     off = align256(off + (size_t)BH * ns * 4);
-  pl.off_gn = off;    off = align256(off + (size_t)BH * ns * 4);
-  pl.off_nodes = off; off = align256(off + (size_t)BH * ns * (dv / 16) * ((dk + 31) / 32) * 512 * pl.esize);
-  pl.ws_bytes = ns > 0 ? off : 0;
+  pl.n_sync = lla::kFlagBase + nodes;
+  pl.off_sync = off;   off = align256(off + pl.n_sync * 4);
+  pl.off_gnode = off;  off = align256(off + nodes * 4);
+  pl.off_node32 = off; off = align256(off + nodes * (dk / 16) * 64 * 16);
+  pl.off_nodeT = off;  off = align256(off + nodes * ((dk + 31) / 32) * 64 * 8 * pl.esize);
+  pl.ws_bytes = pl.ns > 0 ? off : 0;
   const int Lmem = pl.L > 0 ? pl.L : 1;
-  pl.smem_query = smem_bytes(dtype, C, dk, dv, Lmem, true, false);
-  pl.smem_query_alias = smem_bytes(dtype, C, dk, dv, Lmem, true, true);
-  pl.smem_state = smem_bytes(dtype, C, dk, dv, Lmem, false, false);
-  // Fenwick slice: the most fragment lanes whose nodes fit the preferred shared memory
-  pl.fen_lanes = 32;
-  while (pl.fen_lanes > 1 && ns * (2 * pl.fen_lanes * 16 + 4) > (size_t)kFenwickSmem) pl.fen_lanes /= 2;
-  pl.smem_fenwick = (int)align256(ns * (2 * pl.fen_lanes * 16 + 4) + 16);
+  pl.smem = dtype == LLA_DTYPE_BF16 ? lla::fused_smem_bytes<lla::bf16>(C, dk, dv, Lmem)
+                                    : lla::fused_smem_bytes<float>(C, dk, dv, Lmem);
   return LLA_OK;
 }
 
@@ -139,15 +140,7 @@ int launch(const lla_fwd_args& a, const Plan& pl, void* ws, hipStream_t stream) 
   if (hipGetDevice(&dev) != hipSuccess) return LLA_ERR_HIP;
   if (hipDeviceGetAttribute(&max_smem, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
     return LLA_ERR_HIP;
-
-  const void* qfn = ks->query;
-  int smem_q = pl.smem_query;
-  if (smem_q > max_smem) {
-    if (!ks->query_alias || pl.smem_query_alias > max_smem) return LLA_ERR_UNSUPPORTED;
-    qfn = ks->query_alias;
-    smem_q = pl.smem_query_alias;
-  }
-  if (pl.ns > 0 && (pl.smem_state > max_smem || pl.smem_fenwick > max_smem)) return LLA_ERR_UNSUPPORTED;
+  if (pl.smem > max_smem) return LLA_ERR_UNSUPPORTED;
 
   Params p;
   memset(&p, 0, sizeof(p));
@@ -155,16 +148,13 @@ int launch(const lla_fwd_args& a, const Plan& pl, void* ws, hipStream_t stream) 
   p.BH = (int)pl.BH; p.T = a.T; p.L = pl.L;
   p.nchunks = pl.nchunks; p.sweep = pl.R; p.m = pl.m; p.nsweep = pl.nsweep;
   if (ws) {
-    p.hbuf = reinterpret_cast<float*>((char*)ws + pl.off_h);
-    p.gbuf = reinterpret_cast<float*>((char*)ws + pl.off_g);
-    p.gnode = reinterpret_cast<float*>((char*)ws + pl.off_gn);
-    p.nodes = (char*)ws + pl.off_nodes;
+    p.sync = reinterpret_cast<int*>((char*)ws + pl.off_sync);
+    p.gnode = reinterpret_cast<float*>((char*)ws + pl.off_gnode);
+    p.node32 = reinterpret_cast<float*>((char*)ws + pl.off_node32);
+    p.nodeT = (char*)ws + pl.off_nodeT;
   }
-  const long total = (long)pl.nsweep * pl.BH;
-  p.xcd_per = (int)((total + 7) / 8);
-  p.fen_lanes = pl.fen_lanes;
+  p.spin_limit = kSpinLimit;
   void* args[] = {&p};
-  const dim3 block(64 * pl.nw);
   auto mark = [&](int i) {
     return a.stage_events[i] ? hipEventRecord(reinterpret_cast<hipEvent_t>(a.stage_events[i]), stream)
                              : hipSuccess;
@@ -172,23 +162,17 @@ int launch(const lla_fwd_args& a, const Plan& pl, void* ws, hipStream_t stream) 
 
   if (mark(0) != hipSuccess) return LLA_ERR_HIP;
   if (pl.ns > 0) {
-    if (set_smem(ks->state, pl.smem_state) != hipSuccess) return LLA_ERR_HIP;
-    if (hipLaunchKernel(ks->state, dim3(pl.ns, (unsigned)pl.BH), block, args, pl.smem_state, stream) != hipSuccess)
-      return LLA_ERR_HIP;
-    if (mark(1) != hipSuccess) return LLA_ERR_HIP;
-    const int slices = pl.nw * ((a.dk + 31) / 32) * (64 / pl.fen_lanes);
-    if (set_smem(ks->fenwick, pl.smem_fenwick) != hipSuccess) return LLA_ERR_HIP;
-    if (hipLaunchKernel(ks->fenwick, dim3(slices, (unsigned)pl.BH), dim3(256), args, pl.smem_fenwick,
-                        stream) != hipSuccess)
-      return LLA_ERR_HIP;
-    if (mark(2) != hipSuccess) return LLA_ERR_HIP;
-  } else if (mark(1) != hipSuccess || mark(2) != hipSuccess) {
-    return LLA_ERR_HIP;
+    const int n = (int)pl.n_sync;
+    const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
+    hipLaunchKernelGGL(lla::lla_reset_kernel, dim3(blocks), dim3(256), 0, stream, p.sync, n);
+    if (hipGetLastError() != hipSuccess) return LLA_ERR_HIP;
   }
-  if (set_smem(qfn, smem_q) != hipSuccess) return LLA_ERR_HIP;
-  if (hipLaunchKernel(qfn, dim3((unsigned)(8 * p.xcd_per)), block, args, smem_q, stream) != hipSuccess)
+  if (mark(1) != hipSuccess) return LLA_ERR_HIP;
+  if (set_smem(ks->fused, pl.smem) != hipSuccess) return LLA_ERR_HIP;
+  const unsigned grid = (unsigned)(pl.nsweep * pl.BH);
+  if (hipLaunchKernel(ks->fused, dim3(grid), dim3(64 * pl.nw), args, pl.smem, stream) != hipSuccess)
     return LLA_ERR_HIP;
-  if (mark(3) != hipSuccess) return LLA_ERR_HIP;
+  if (mark(2) != hipSuccess) return LLA_ERR_HIP;
   return LLA_OK;
 }
 

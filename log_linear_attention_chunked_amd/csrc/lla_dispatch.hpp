@@ -4,10 +4,7 @@
 namespace lla {
 
 struct KernelSet {
-  const void* state;         // lla_sweep_state_kernel<T, C, DK, DV>
-  const void* fenwick;       // lla_fenwick_kernel<T, DK, DV>
-  const void* query;         // lla_query_kernel<T, C, DK, DV, false>
-  const void* query_alias;   // lla_query_kernel<T, C, DK, DV, true>, or nullptr
+  const void* fused;         // lla_fused_kernel<T, C, DK, DV>
 };
 
 // dtype 0 = bf16, 1 = f32; C, DK, DV in {16, 32, 64, 128}; nullptr otherwise.

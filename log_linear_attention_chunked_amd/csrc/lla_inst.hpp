@@ -1,28 +1,14 @@
 // lla_inst.hpp — builds one (dtype, chunk) table of kernel instantiations.
 #pragma once
-#include <type_traits>
 
 #include "lla_dispatch.hpp"
 #include "lla_kernels.hpp"
 
 namespace lla {
 
-// The shared-memory-aliasing output kernel exists only where the plain one cannot fit:
-// bf16, C = 128, dk = dv = 128.
-template <typename TY, int C, int DK, int DV>
-const void* alias_kernel() {
-  if constexpr (std::is_same<TY, bf16>::value && C == 128 && DK == 128 && DV == 128)
-    return reinterpret_cast<const void*>(&lla_query_kernel<TY, C, DK, DV, true>);
-  else
-    return nullptr;
-}
-
 template <typename TY, int C, int DK, int DV>
 KernelSet make_set() {
-  return KernelSet{reinterpret_cast<const void*>(&lla_sweep_state_kernel<TY, C, DK, DV>),
-                   reinterpret_cast<const void*>(&lla_fenwick_kernel<TY, DK, DV>),
-                   reinterpret_cast<const void*>(&lla_query_kernel<TY, C, DK, DV, false>),
-                   alias_kernel<TY, C, DK, DV>()};
+  return KernelSet{reinterpret_cast<const void*>(&lla_fused_kernel<TY, C, DK, DV>)};
 }
 
 template <typename TY, int C, int DK>

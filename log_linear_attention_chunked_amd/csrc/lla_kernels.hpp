@@ -16,17 +16,18 @@
 //   lambda[t, J+1+j] * exp(A_t - A_end) * q_t^T N,   N = sum_{s in block} exp(A_end - A_s) k_s v_s^T
 // with A_end the prefix decay at the block's last position.
 //
-// Work split. A workgroup walks a "sweep" of R = 2^m consecutive chunks of one head.
-// Fenwick nodes inside the sweep are built on the fly in registers (carry merging as the
-// walk advances); nodes made of whole earlier sweeps come from a Fenwick tree over sweep
-// totals built by two small kernels beforehand:
-//   lla_sweep_state_kernel : per sweep, H = sum_s exp(A_sweep_end - A_s) k_s v_s^T and its
-//                            total log decay G (reads k, v, log_a).
-//   lla_fenwick_kernel     : in-place Fenwick up-sweep over the sweep totals of a head; emits
-//                            each node in bf16/f32 MFMA-operand order plus its log decay.
-//   lla_query_kernel       : per sweep, chunk by chunk: dense masked block on MFMA, decayed
-//                            chunk state on MFMA, level-fused read-out of the live Fenwick
-//                            nodes on MFMA, output store.
+// Work split. One kernel, one workgroup per "sweep" of R = 2^m consecutive chunks of one head
+// (lla_fused_kernel). Workgroups take a ticket from an atomic counter and map it sweep-major,
+// so every sweep they wait for belongs to a workgroup that started earlier.
+//   phase A: chunk states of the sweep (decayed k^T v on MFMA); the Fenwick nodes inside the
+//            sweep are kept in registers; the sweep total plus the nodes of earlier sweeps it
+//            absorbs (a Fenwick tree over sweeps) is published as this sweep's node.
+//   phase B: chunk by chunk: dense masked block on MFMA, read-out of the live Fenwick nodes
+//            (inside the sweep from registers, earlier sweeps from the published nodes),
+//            output store.
+// A node is published per wave (16 value columns): data stores, an agent-scope release fence,
+// then a flag; readers poll the flag (bounded: on timeout the outputs are set to NaN so that
+// a broken dependency can never hang the device) and take an agent-scope acquire fence.
 //
 // MFMA operand convention. All products use 16x16 output tiles. A K=32 operand fragment
 // gives lane (j = lane & 15, g = lane >> 4) eight values e = 0..7 at contraction index
@@ -91,6 +92,21 @@ __device__ __forceinline__ void frag_to_f32(const Frag<float>& f, f32x4& lo, f32
   lo = f.lo; hi = f.hi;
 }
 
+__device__ __forceinline__ Frag<bf16> frag_select_impl(bool c, const Frag<bf16>& a, const Frag<bf16>& b) {
+  Frag<bf16> r; r.v = c ? a.v : b.v; return r;
+}
+__device__ __forceinline__ Frag<float> frag_select_impl(bool c, const Frag<float>& a, const Frag<float>& b) {
+  Frag<float> r; r.lo = c ? a.lo : b.lo; r.hi = c ? a.hi : b.hi; return r;
+}
+template <typename T> __device__ __forceinline__ Frag<T> zero_frag() {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return frag_from<T>(z, z);
+}
+template <typename T>
+__device__ __forceinline__ Frag<T> frag_select(bool c, const Frag<T>& a, const Frag<T>& b) {
+  return frag_select_impl(c, a, b);
+}
+
 // 4 consecutive elements of a fragment (one half: e0 = 0 or 4)
 template <typename T> struct Quad;
 template <> struct Quad<bf16> { typedef bf16x4 type; };
@@ -130,10 +146,11 @@ struct ChunkSmem {
 };
 
 // Byte offsets of one chunk's shared memory (host and device agree). A fragment slot is one
-// operand fragment for all 64 lanes (64 x 8 elements).
+// operand fragment for all 64 lanes (64 x 8 elements). with_q: the query-side images (q, k,
+// masked scores, lambda); with_kt: the decayed-key operand of chunk states.
 template <typename T>
 __host__ __device__ inline ChunkSmem chunk_smem(int C, int DK, int DV, int L, bool with_q,
-                                                bool alias_p) {
+                                                bool with_kt) {
   const int es = (int)sizeof(T);
   const int slot = 64 * 8 * es;
   const int nqb = C / 16, nks_c = (C + 31) / 32;
@@ -141,20 +158,30 @@ __host__ __device__ inline ChunkSmem chunk_smem(int C, int DK, int DV, int L, bo
   ChunkSmem s;
   int off = 0;
   s.qimg = off; off += with_q ? C * DK * es : 0;
-  s.kimg = off;
-  const int kbytes = with_q ? C * DK * es : 0;
-  const int pbytes = with_q ? nqb * nks_c * slot : 0;
-  if (alias_p) { s.pf = off; off += (kbytes > pbytes ? kbytes : pbytes); }
-  else { off += kbytes; s.pf = off; off += pbytes; }
-  s.kt = off; off += trn ? C * DK * es : (DK / 16) * nks_c * slot;
-  s.vt = off; off += trn ? C * DV * es : (DV / 16) * nks_c * slot;
-  s.lam = off; off += with_q ? ((C * L * 4 + 15) & ~15) : 0;
+  s.kimg = off; off += with_q ? C * DK * es : 0;
+  s.pf = off;   off += with_q ? nqb * nks_c * slot : 0;
+  s.kt = off;   off += with_kt ? (trn ? C * DK * es : (DK / 16) * nks_c * slot) : 0;
+  s.vt = off;   off += trn ? C * DV * es : (DV / 16) * nks_c * slot;
+  s.lam = off;  off += with_q ? ((C * L * 4 + 15) & ~15) : 0;
   s.aloc = off; off += C * 4;
-  s.ea = off; off += C * 4;
-  s.eb = off; off += C * 4;
+  s.ea = off;   off += C * 4;
+  s.eb = off;   off += C * 4;
   s.flag = off; off += 16;
   s.total = (off + 255) & ~255;
   return s;
+}
+
+// Shared memory of the fused kernel: the phase A and phase B layouts overlap from offset 0;
+// the workgroup ticket sits after both.
+template <typename T>
+__host__ __device__ inline int fused_ticket_offset(int C, int DK, int DV, int L) {
+  const int a = chunk_smem<T>(C, DK, DV, L, false, true).total;
+  const int b = chunk_smem<T>(C, DK, DV, L, true, false).total;
+  return a > b ? a : b;
+}
+template <typename T>
+__host__ __device__ inline int fused_smem_bytes(int C, int DK, int DV, int L) {
+  return fused_ticket_offset<T>(C, DK, DV, L) + 16;
 }
 
 // ----------------------------------------------------------------------------------------
@@ -584,9 +611,10 @@ __device__ __forceinline__ void unit_decode(int un, int& qb, int& ks) {
   while (ks >= qb / 2 + 1) { ks -= qb / 2 + 1; ++qb; }
 }
 
-// Stages one chunk: q, k as row-major images (scores, read-outs), k~ = exp(g - A_s) k_s and v
-// as position-contracted operands (states, P.V), lambda rows, and (wave 0) A, e^A, e^-A.
-template <typename T, int C, int DK, int DV, int NT, bool WITH_Q>
+// Stages one chunk: v as the position-contracted operand (P.V, states) and log_a -> (wave 0)
+// A, e^A, e^-A; WITH_Q: q, k as row-major images (scores, read-outs) and lambda rows; KT:
+// k~ = exp(g - A_s) k_s as position-contracted operand (chunk states).
+template <typename T, int C, int DK, int DV, int NT, bool WITH_Q, bool KT>
 struct ChunkStage {
   BlockRegs<T, C, DK, NT> qr, kr;
   BlockRegs<T, C, DV, NT> vr;
@@ -607,27 +635,30 @@ struct ChunkStage {
   __device__ __forceinline__ void commit(const ChunkSmem& S, unsigned char* smem, int L, int tid,
                                          int lane, int w) {
     ar.scan(lane);
-    const float g = ar.at(C - 1);
-    typedef BlockRegs<T, C, DK, NT> KR;
-    float ws[KR::ITERS][2];
+    if (KT) {
+      const float g = ar.at(C - 1);
+      typedef BlockRegs<T, C, DK, NT> KR;
+      float ws[KR::ITERS][2];
 #pragma unroll
-    for (int it = 0; it < KR::ITERS; ++it) {
-      const int r0 = KR::row0(tid, it);
-      ws[it][0] = __expf(g - ar.at(r0));
-      ws[it][1] = __expf(g - ar.at(r0 + 1));
+      for (int it = 0; it < KR::ITERS; ++it) {
+        const int r0 = KR::row0(tid, it);
+        ws[it][0] = __expf(g - ar.at(r0));
+        ws[it][1] = __expf(g - ar.at(r0 + 1));
+      }
+      if constexpr (TrNative<T>::value)
+        kr.template commit_image<true, true>(smem + S.kt, tid, ws);
+      else
+        kr.template commit_frags<true>(reinterpret_cast<T*>(smem + S.kt), tid, ws);
     }
     if (WITH_Q) {
       qr.template commit_image<false, false>(smem + S.qimg, tid, nullptr);
       kr.template commit_image<false, false>(smem + S.kimg, tid, nullptr);
       lr.commit(reinterpret_cast<float*>(smem + S.lam), C * L, tid);
     }
-    if constexpr (TrNative<T>::value) {
-      kr.template commit_image<true, true>(smem + S.kt, tid, ws);
+    if constexpr (TrNative<T>::value)
       vr.template commit_image<true, false>(smem + S.vt, tid, nullptr);
-    } else {
-      kr.template commit_frags<true>(reinterpret_cast<T*>(smem + S.kt), tid, ws);
+    else
       vr.template commit_frags<false>(reinterpret_cast<T*>(smem + S.vt), tid, nullptr);
-    }
     if (w == 0)
       ar.publish(reinterpret_cast<float*>(smem + S.aloc), reinterpret_cast<float*>(smem + S.ea),
                  reinterpret_cast<float*>(smem + S.eb), reinterpret_cast<int*>(smem + S.flag), lane);
@@ -638,6 +669,79 @@ struct ChunkStage {
 // kernels
 // ----------------------------------------------------------------------------------------
 
+// Node records pass between workgroups of one launch, possibly on different XCDs (each XCD has
+// its own L2). Two schemes, chosen at compile time:
+//   kScopedNodeIO = false: plain loads and stores of node data, an agent-scope release fence
+//                          (L2 write-back) before the flag store and an agent-scope acquire
+//                          fence (L2 invalidate) after the flag is seen;
+//   kScopedNodeIO = true : node data is written and read with device-scope (sc1) buffer
+//                          accesses, which are coherent across XCDs without touching the rest
+//                          of L2; the flag is stored once those writes have completed.
+#ifndef LLA_SCOPED_NODE_IO
+#define LLA_SCOPED_NODE_IO 1
+#endif
+constexpr bool kScopedNodeIO = LLA_SCOPED_NODE_IO != 0;
+constexpr int kCpolDevice = 16;   // cache-policy immediate: sc1 (device scope)
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor over a wave-uniform base address (raw, unstrided).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t node_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+// 16-byte multiples (an f32x4 tile quad, a bf16 or f32 operand fragment), contiguous at byte_off
+template <typename V>
+__device__ __forceinline__ V node_ld(const void* base, int byte_off) {
+  static_assert(sizeof(V) % 16 == 0, "16-byte node accesses");
+  if constexpr (kScopedNodeIO) {
+    u32x4 r[sizeof(V) / 16];
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(V) / 16); ++i)
+      r[i] = __builtin_amdgcn_raw_buffer_load_b128(node_rsrc(base), byte_off + 16 * i, 0, kCpolDevice);
+    return __builtin_bit_cast(V, r);
+  } else {
+    return *reinterpret_cast<const V*>(reinterpret_cast<const char*>(base) + byte_off);
+  }
+}
+template <typename V>
+__device__ __forceinline__ void node_st(void* base, int byte_off, const V& x) {
+  static_assert(sizeof(V) % 16 == 0, "16-byte node accesses");
+  if constexpr (kScopedNodeIO) {
+    struct W { u32x4 r[sizeof(V) / 16]; };
+    const W wv = __builtin_bit_cast(W, x);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(V) / 16); ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(wv.r[i], node_rsrc(base), byte_off + 16 * i, 0, kCpolDevice);
+  } else {
+    *reinterpret_cast<V*>(reinterpret_cast<char*>(base) + byte_off) = x;
+  }
+}
+__device__ __forceinline__ float node_ld_f(const float* p) {
+  if constexpr (kScopedNodeIO) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+__device__ __forceinline__ void node_st_f(float* p, float x) {
+  if constexpr (kScopedNodeIO) __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = x;
+}
+// after a wave's node writes, before its flag store
+__device__ __forceinline__ void node_publish_fence() {
+  if constexpr (kScopedNodeIO) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);     // every outstanding access of this wave has completed
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  } else {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  }
+}
+// after the flags a wave waits for were seen set, before its node reads
+__device__ __forceinline__ void node_acquire_fence() {
+  if constexpr (kScopedNodeIO) __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+constexpr int kFlagBase = 64;   // ints ahead of the node flags (the ticket counter, alone in its line)
+
 struct Params {
   const void* q; const void* k; const void* v;
   const float* log_a; const float* lam;
@@ -647,164 +751,62 @@ struct Params {
   int sweep;        // R: consecutive chunks per workgroup (power of two, <= kSweepCap)
   int m;            // log2(R)
   int nsweep;       // ceil(nchunks / R)
-  float* hbuf;      // [BH][nsweep-1][DV/16][DK/16][64] f32x4: sweep totals
-  float* gbuf;      // [BH][nsweep-1]: sweep log decays
-  float* gnode;     // [BH][nsweep-1]: Fenwick node log decays
-  void* nodes;      // [BH][nsweep-1][DV/16][ceil(DK/32)][64] Frag<T>: nodes as read-out operands
-  int xcd_per;      // output grid: workgroups per XCD slice
-  int fen_lanes;    // Fenwick kernel: fragment lanes per workgroup slice (shared-memory pass)
+  int* sync;        // [0]: workgroup ticket counter; [kFlagBase + (bh*ns + e)*NW + w]: node flags
+  float* gnode;     // [BH][ns][NW]: log decay across node e (one copy per wave)
+  float* node32;    // [BH][ns][NW][DK/16][64] f32x4: node e as float32 accumulator tiles
+  void* nodeT;      // [BH][ns][NW][ceil(DK/32)][64] Frag<T>: node e as read-out operands
+  int spin_limit;   // polls of a node flag before the wait is abandoned
 };
 
-// Sweep totals. Grid (nsweep-1, BH): only whole sweeps before the last one are needed.
-//   H = sum_{s in sweep} exp(A_end - A_s) k_s v_s^T,  G = A_end - A_{start-1}
+// Node flags, data and decays are indexed by (head, node = sweep index e, wave).
+__device__ __forceinline__ size_t node_slot(int bh, int ns, int e, int nw, int w) {
+  return ((size_t)bh * ns + e) * nw + w;
+}
+
+// The forward pass. One workgroup per sweep of R chunks of one head, one wave per 16 value
+// columns; ns = nsweep - 1 sweeps per head publish a node (the last one has no reader).
+//
+// Node of sweep e: the Fenwick node over sweeps that ends at e, i.e. the lowbit(e+1) sweeps
+// (e - lowbit(e+1), e], decayed to the end of e:
+//   node(e) = H_e + sum_{i < ctz(e+1)} exp(gacc_i) node(e - 2^i),
+// H_e = sum_{s in sweep e} exp(A_end(e) - A_s) k_s v_s^T, gacc_i the log decay from the end of
+// node(e - 2^i) to the end of e. Sweep sw reads the nodes ending at ((sw >> j) << j) - 1 for
+// each set bit j of sw (level J + 1 + m + j); the first ctz(sw+1) of them are exactly the
+// children of its own node.
+//
+// Global loads are issued branch-free where possible, so that waits count exactly: the
+// inputs of the next chunk are loaded into registers right after the current chunk is staged
+// in shared memory, and the first chunk of phase B while the last chunk of phase A is
+// computed.
 template <typename T, int C, int DK, int DV>
-__global__ __launch_bounds__(4 * DV) void lla_sweep_state_kernel(Params p) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  constexpr int NT = 4 * DV, NDKB = DK / 16, NKS_C = (C + 31) / 32;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index: uniform
-  const int sw = blockIdx.x, bh = blockIdx.y;
-  const int ns = p.nsweep - 1;
-  const ChunkSmem S = chunk_smem<T>(C, DK, DV, p.L, false, false);
-
-  const size_t hoff = (size_t)bh * p.T;
-  const T* kg = reinterpret_cast<const T*>(p.k) + hoff * DK;
-  const T* vg = reinterpret_cast<const T*>(p.v) + hoff * DV;
-  const float* lag = p.log_a + hoff;
-
-  ChunkStage<T, C, DK, DV, NT, false> st;
-  auto fetch = [&](int u) {
-    const int t0 = (sw * p.sweep + u) * C;
-    st.fetch(nullptr, kg + (size_t)t0 * DK, vg + (size_t)t0 * DV, nullptr, lag + t0, 0, C, tid, lane);
-  };
-  fetch(0);
-
-  f32x4 H[NDKB];
-#pragma unroll
-  for (int b = 0; b < NDKB; ++b) H[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float G = 0.f;
-  for (int u = 0; u < p.sweep; ++u) {
-    if (u) __syncthreads();
-    st.commit(S, smem, 0, tid, lane, w);
-    __syncthreads();
-    fetch(u + 1 < p.sweep ? u + 1 : u);     // unconditional: re-reads this chunk at the end
-    const float gtot = reinterpret_cast<const float*>(smem + S.aloc)[C - 1];
-    Frag<T> vfr[NKS_C];
-#pragma unroll
-    for (int ks = 0; ks < NKS_C; ++ks) vfr[ks] = col_frag<T, C, DV>(smem + S.vt, w, ks, lane);
-    f32x4 F[NDKB];
-    chunk_state<T, C, DK>(smem + S.kt, vfr, lane, F);
-    const float d = __expf(gtot);
-#pragma unroll
-    for (int b = 0; b < NDKB; ++b) H[b] = d * H[b] + F[b];
-    G += gtot;
-  }
-  f32x4* hb = reinterpret_cast<f32x4*>(p.hbuf) + (((size_t)bh * ns + sw) * (DV / 16) + w) * NDKB * 64;
-#pragma unroll
-  for (int b = 0; b < NDKB; ++b) hb[b * 64 + lane] = H[b];
-  if (tid == 0) p.gbuf[(size_t)bh * ns + sw] = G;
-}
-
-// Fenwick up-sweep over the ns = nsweep-1 sweep totals of a head, in shared memory. Slot e
-// ends up holding the node of the lowbit(e+1) sweeps ending at e, decayed to its last
-// position (gnode[e]: its total log decay); every node is then written as read-out
-// fragments (Frag<T>). A workgroup owns lanes [l0, l0+nl) of one fragment (value block w,
-// key step s) for all ns nodes. Grid (DV/16 * ceil(DK/32) * 64/nl, BH).
-template <typename T, int DK, int DV>
-__global__ __launch_bounds__(256) void lla_fenwick_kernel(Params p) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  constexpr int NDVB = DV / 16, NDKB = DK / 16, NKS_D = (DK + 31) / 32;
-  const int ns = p.nsweep - 1;
-  const int nl = p.fen_lanes, per_frag = 64 / nl;
-  const int bh = blockIdx.y;
-  const int frag = blockIdx.x / per_frag, l0 = (blockIdx.x % per_frag) * nl;
-  const int w = frag / NKS_D, s = frag % NKS_D;
-  const int b0 = 2 * s;
-  const bool has1 = b0 + 1 < NDKB;
-  const int tid = threadIdx.x, nt = blockDim.x;
-  const int row = 2 * nl;                          // f32x4 per node in this slice
-  f32x4* sh = reinterpret_cast<f32x4*>(smem);      // [ns][2][nl]
-  float* gsh = reinterpret_cast<float*>(sh + (size_t)ns * row);
-
-  const f32x4* hb = reinterpret_cast<const f32x4*>(p.hbuf) + (size_t)bh * ns * NDVB * NDKB * 64;
-  for (int i = tid; i < ns * row; i += nt) {
-    const int e = i / row, r = i - e * row, half = r / nl, l = l0 + (r - half * nl);
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (half == 0 || has1) v = hb[(((size_t)e * NDVB + w) * NDKB + b0 + half) * 64 + l];
-    sh[i] = v;
-  }
-  const float* gb = p.gbuf + (size_t)bh * ns;
-  for (int i = tid; i < ns; i += nt) gsh[i] = gb[i];
-  __syncthreads();
-
-  for (int half = 1; half < ns; half <<= 1) {
-    const int first = 2 * half - 1, step = 2 * half;
-    const int nn = first < ns ? (ns - 1 - first) / step + 1 : 0;
-    for (int i = tid; i < nn * row; i += nt) {
-      const int k = i / row, r = i - k * row;
-      const int e = first + k * step;
-      const float d = __expf(gsh[e]);            // decay across the right half (slot e as it is)
-      sh[e * row + r] = d * sh[(e - half) * row + r] + sh[e * row + r];
-    }
-    __syncthreads();
-    for (int k = tid; k < nn; k += nt) {
-      const int e = first + k * step;
-      gsh[e] += gsh[e - half];
-    }
-    __syncthreads();
-  }
-
-  Frag<T>* nd = reinterpret_cast<Frag<T>*>(p.nodes);
-  for (int i = tid; i < ns * nl; i += nt) {
-    const int e = i / nl, l = i - e * nl;
-    nd[((((size_t)bh * ns + e) * NDVB + w) * NKS_D + s) * 64 + l0 + l] =
-        frag_from<T>(sh[e * row + l], sh[e * row + nl + l]);
-  }
-  if (blockIdx.x == 0)
-    for (int i = tid; i < ns; i += nt) p.gnode[(size_t)bh * ns + i] = gsh[i];
-}
-
-// The output kernel: one workgroup walks the R chunks of one sweep of one head; one wave per
-// 16 value columns. Global loads are issued branch-free so that waits count exactly:
-//   * the Fenwick nodes over earlier sweeps (up to XREG of them) are loaded into registers
-//     once, before the first chunk;
-//   * the inputs of chunk u+1 are loaded into registers right after chunk u is staged in
-//     shared memory (the current chunk again after the last one), so they are in flight while
-//     chunk u is computed, and nothing inside the chunk waits for them.
-// Workgroup ids are dealt round-robin to the 8 XCDs; consecutive sweeps of a head are mapped
-// to the same XCD so that the Fenwick nodes they share stay in one L2.
-// ALIAS: the masked scores reuse the key image's shared memory (C=128 with 128-wide heads);
-// each wave then holds its score units in registers across a barrier.
-template <typename T, int C, int DK, int DV, bool ALIAS>
-__global__ __launch_bounds__(4 * DV, 2) void lla_query_kernel(Params p) {
+__global__ __launch_bounds__(4 * DV, 2) void lla_fused_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int NT = 4 * DV, NW = DV / 16;
-  constexpr int NQB = C / 16, NKS_C = (C + 31) / 32, NKS_D = (DK + 31) / 32;
+  constexpr int NQB = C / 16, NKS_C = (C + 31) / 32, NKS_D = (DK + 31) / 32, NDKB = DK / 16;
   constexpr int J = ilog2(C);
   constexpr int LMAX = ilog2(kSweepCap);
+  constexpr int NSLOT = kSweepCap - 1;
   constexpr int NUNITS = num_units(NQB);
-  constexpr int UHOLD = ALIAS ? (NUNITS + NW - 1) / NW : 1;
   constexpr int XREG = DK >= 128 ? 2 : 5;   // nodes over earlier sweeps held in registers
-
-  const int total = p.nsweep * p.BH;
-  const int lin = (blockIdx.x & 7) * p.xcd_per + (blockIdx.x >> 3);
-  if (lin >= total) return;
-  const int bh = lin / p.nsweep, sw = lin - bh * p.nsweep;
+  static_assert(kSweepCap <= 4, "slot u of a sweep is the running total or chunk u alone only for R <= 4");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index: uniform
   const int j = lane & 15, g = lane >> 4;
   const int L = p.L, ns = p.nsweep - 1;
-  const ChunkSmem S = chunk_smem<T>(C, DK, DV, L, true, ALIAS);
-  const unsigned char* qimg = smem + S.qimg;
-  const unsigned char* kimg = smem + S.kimg;
-  T* pf = reinterpret_cast<T*>(smem + S.pf);
-  const float* lam = reinterpret_cast<const float*>(smem + S.lam);
-  const float* aloc = reinterpret_cast<const float*>(smem + S.aloc);
-  const float* ea = reinterpret_cast<const float*>(smem + S.ea);
-  const float* eb = reinterpret_cast<const float*>(smem + S.eb);
-  const int* flag = reinterpret_cast<const int*>(smem + S.flag);
+  const ChunkSmem SA = chunk_smem<T>(C, DK, DV, L, false, true);
+  const ChunkSmem SB = chunk_smem<T>(C, DK, DV, L, true, false);
+
+  // ticket -> (head, sweep), sweep-major
+  int t = blockIdx.x;
+  if (ns > 0) {
+    int* tk = reinterpret_cast<int*>(smem + fused_ticket_offset<T>(C, DK, DV, L));
+    if (tid == 0) *tk = __hip_atomic_fetch_add(p.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    t = __builtin_amdgcn_readfirstlane(*tk);
+  }
+  const int sw = t / p.BH, bh = t - sw * p.BH;
 
   const size_t hoff = (size_t)bh * p.T;
   const T* qg = reinterpret_cast<const T*>(p.q) + hoff * DK;
@@ -816,14 +818,9 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_query_kernel(Params p) {
 
   const int c0 = sw * p.sweep;
   const int nch = min(p.sweep, p.nchunks - c0);
-
-  // nodes over earlier sweeps: one per set bit of sw, lowest first; node x ends at sweep
-  // ((sw >> jb) << jb) - 1 for the x-th set bit jb
   const int next = __builtin_popcount((unsigned)sw);
-  const Frag<T>* nd = reinterpret_cast<const Frag<T>*>(p.nodes) +
-                      ((size_t)bh * (ns > 0 ? ns : 0) * NW + w) * NKS_D * 64 + lane;
-  const float* gn = p.gnode + (size_t)bh * (ns > 0 ? ns : 0);
-  auto node_index = [&](int x) {      // sweep index the x-th node ends at (clamped to 0)
+
+  auto node_index = [&](int x) {      // sweep index the x-th node of sw ends at (0 if none)
     unsigned m = (unsigned)sw;
     for (int i = 0; i < x && m; ++i) m &= m - 1;
     return m ? ((sw >> __builtin_ctz(m)) << __builtin_ctz(m)) - 1 : 0;
@@ -833,10 +830,113 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_query_kernel(Params p) {
     for (int i = 0; i < x && m; ++i) m &= m - 1;
     return m ? J + 1 + p.m + __builtin_ctz(m) : 0;
   };
+  const Frag<T>* ndT = reinterpret_cast<const Frag<T>*>(p.nodeT);
   auto load_node = [&](Frag<T> (&A)[NKS_D], int e) {
+    const Frag<T>* base = ndT + node_slot(bh, ns, e, NW, w) * NKS_D * 64;
 #pragma unroll
-    for (int s = 0; s < NKS_D; ++s) A[s] = nd[(size_t)e * NW * NKS_D * 64 + s * 64];
+    for (int s = 0; s < NKS_D; ++s) A[s] = node_ld<Frag<T>>(base, (s * 64 + lane) * (int)sizeof(Frag<T>));
   };
+
+  ChunkStage<T, C, DK, DV, NT, false, true> sa;
+  ChunkStage<T, C, DK, DV, NT, true, false> sb;
+  auto fetch_a = [&](int u) {
+    const int t0 = (c0 + u) * C;
+    const int valid = min(C, p.T - t0);
+    sa.fetch(nullptr, kg + (size_t)t0 * DK, vg + (size_t)t0 * DV, nullptr, lag + t0, 0, valid, tid, lane);
+  };
+  auto fetch_b = [&](int u) {
+    const int t0 = (c0 + u) * C;
+    const int valid = min(C, p.T - t0);
+    sb.fetch(qg + (size_t)t0 * DK, kg + (size_t)t0 * DK, vg + (size_t)t0 * DV, lamg + (size_t)t0 * L,
+             lag + t0, L, valid, tid, lane);
+  };
+
+  // ---------------- phase A: chunk states -> slots inside the sweep, sweep total ----------------
+  // Slot s (s < R-1) is the Fenwick node over the chunks of the sweep that ends at chunk s; for
+  // R <= 4 it is the running total when s+1 is a power of two and chunk s's own state otherwise.
+  Frag<T> SL[NSLOT][NKS_D];
+#pragma unroll
+  for (int s = 0; s < NSLOT; ++s)
+#pragma unroll
+    for (int s2 = 0; s2 < NKS_D; ++s2) SL[s][s2] = zero_frag<T>();
+  f32x4 H[NDKB];
+#pragma unroll
+  for (int b = 0; b < NDKB; ++b) H[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float G = 0.f;
+  auto body_a = [&](int u) {
+    const float gtot = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+        __builtin_bit_cast(int, reinterpret_cast<const float*>(smem + SA.aloc)[C - 1])));
+    Frag<T> vfr[NKS_C];
+#pragma unroll
+    for (int ks = 0; ks < NKS_C; ++ks) vfr[ks] = col_frag<T, C, DV>(smem + SA.vt, w, ks, lane);
+    f32x4 F[NDKB];
+    chunk_state<T, C, DK>(smem + SA.kt, vfr, lane, F);
+    const float d = __expf(gtot);
+#pragma unroll
+    for (int b = 0; b < NDKB; ++b) H[b] = d * H[b] + F[b];
+    G += gtot;
+    // value selects, not conditional stores: the slots must stay in registers
+#pragma unroll
+    for (int s = 0; s < NSLOT; ++s) {
+      const bool hit = u == s;
+      const bool whole = ((s + 1) & s) == 0;
+#pragma unroll
+      for (int s2 = 0; s2 < NKS_D; ++s2)
+        SL[s][s2] = frag_select<T>(hit, whole ? node_frag<T, DK>(H, s2) : node_frag<T, DK>(F, s2), SL[s][s2]);
+    }
+  };
+  fetch_a(0);
+  for (int u = 0; u + 1 < nch; ++u) {
+    if (u) __syncthreads();
+    sa.commit(SA, smem, L, tid, lane, w);
+    __syncthreads();
+    fetch_a(u + 1);
+    body_a(u);
+  }
+  if (nch > 1) __syncthreads();
+  sa.commit(SA, smem, L, tid, lane, w);
+  __syncthreads();
+  fetch_b(0);
+  body_a(nch - 1);
+
+  // ---------------- nodes of earlier sweeps: wait, absorb children, publish ----------------
+  bool bad = false;
+  for (int x = 0; x < next; ++x) {
+    const int* f = p.sync + kFlagBase + node_slot(bh, ns, node_index(x), NW, w);
+    int n = 0;
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+      if (++n > p.spin_limit) { bad = true; break; }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  if (next > 0) node_acquire_fence();
+
+  if (sw < ns) {
+    const int kc = __builtin_ctz((unsigned)(sw + 1));   // children: nodes x < kc of sw
+    const f32x4* n32 = reinterpret_cast<const f32x4*>(p.node32);
+    float gacc = G;
+    for (int x = 0; x < kc; ++x) {
+      const size_t e = node_slot(bh, ns, node_index(x), NW, w);
+      const float d = __expf(gacc);
+#pragma unroll
+      for (int b = 0; b < NDKB; ++b) H[b] += d * node_ld<f32x4>(n32 + e * NDKB * 64, (b * 64 + lane) * 16);
+      gacc += node_ld_f(p.gnode + e);
+    }
+    if (bad) {
+#pragma unroll
+      for (int b = 0; b < NDKB; ++b) H[b] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    }
+    const size_t me = node_slot(bh, ns, sw, NW, w);
+    f32x4* o32 = reinterpret_cast<f32x4*>(p.node32) + me * NDKB * 64;
+#pragma unroll
+    for (int b = 0; b < NDKB; ++b) node_st<f32x4>(o32, (b * 64 + lane) * 16, H[b]);
+    Frag<T>* oT = reinterpret_cast<Frag<T>*>(p.nodeT) + me * NKS_D * 64;
+#pragma unroll
+    for (int s = 0; s < NKS_D; ++s) node_st<Frag<T>>(oT, (s * 64 + lane) * (int)sizeof(Frag<T>), node_frag<T, DK>(H, s));
+    if (lane == 0) node_st_f(p.gnode + me, gacc);
+    node_publish_fence();
+    if (lane == 0) __hip_atomic_store(p.sync + kFlagBase + me, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   Frag<T> X[XREG][NKS_D];
   float XD[XREG];            // log decay across each node
@@ -845,71 +945,48 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_query_kernel(Params p) {
     for (int x = 0; x < XREG; ++x) {
       const int e = node_index(x);
       load_node(X[x], e);
-      XD[x] = gn[e];
+      XD[x] = node_ld_f(p.gnode + node_slot(bh, ns, e, NW, w));
     }
   }
-  ChunkStage<T, C, DK, DV, NT, true> st;
-  auto prefetch = [&](int u) {
-    const int t0 = (c0 + u) * C;
-    const int valid = min(C, p.T - t0);
-    st.fetch(qg + (size_t)t0 * DK, kg + (size_t)t0 * DK, vg + (size_t)t0 * DV, lamg + (size_t)t0 * L,
-             lag + t0, L, valid, tid, lane);
-  };
-  prefetch(0);
 
-  Frag<T> LN[LMAX][NKS_D];   // Fenwick nodes inside the sweep (this wave's value columns)
-  float LD[LMAX];            // log decay from each node's last position to the current chunk start
+  // ---------------- phase B: outputs, chunk by chunk ----------------
+  const unsigned char* qimg = smem + SB.qimg;
+  const unsigned char* kimg = smem + SB.kimg;
+  T* pf = reinterpret_cast<T*>(smem + SB.pf);
+  const float* lam = reinterpret_cast<const float*>(smem + SB.lam);
+  const float* aloc = reinterpret_cast<const float*>(smem + SB.aloc);
+  const float* ea = reinterpret_cast<const float*>(smem + SB.ea);
+  const float* eb = reinterpret_cast<const float*>(smem + SB.eb);
+  const int* flag = reinterpret_cast<const int*>(smem + SB.flag);
+
+  float SD[NSLOT];           // log decay from the end of slot s to the current chunk start
 #pragma unroll
-  for (int a = 0; a < LMAX; ++a) {
-    LD[a] = 0.f;
-#pragma unroll
-    for (int s = 0; s < NKS_D; ++s) LN[a][s] = frag_from<T>(f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f});
-  }
+  for (int s = 0; s < NSLOT; ++s) SD[s] = 0.f;
   float gam = 0.f;           // log decay from the sweep's first position to the current chunk start
 
   for (int u = 0; u < nch; ++u) {
     const int t0 = (c0 + u) * C;
     const int valid = min(C, p.T - t0);
-    if (u) __syncthreads();
-    st.commit(S, smem, L, tid, lane, w);
     __syncthreads();
-    prefetch(u + 1 < nch ? u + 1 : u);     // unconditional: re-reads this chunk after the last
+    sb.commit(SB, smem, L, tid, lane, w);
+    __syncthreads();
+    fetch_b(u + 1 < nch ? u + 1 : u);     // unconditional: re-reads this chunk after the last
     const float gtot = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, aloc[C - 1])));
     const bool fact = __builtin_amdgcn_readfirstlane(*flag) != 0;
 
     // masked scores -> P^T fragments
-    if (!ALIAS) {
-      for (int un = w; un < NUNITS; un += NW) {
-        int qb, ks;
-        unit_decode(un, qb, ks);
-        const Frag<T> f = score_unit<T, C, DK>(qimg, kimg, lam, L, aloc, ea, eb, fact, qb, ks, lane);
-        reinterpret_cast<Frag<T>*>(pf)[(qb * NKS_C + ks) * 64 + lane] = f;
-      }
-    } else {
-      Frag<T> held[UHOLD];
-      int where[UHOLD];
-#pragma unroll
-      for (int h = 0; h < UHOLD; ++h) {
-        const int un = w + h * NW;
-        where[h] = -1;
-        if (un < NUNITS) {
-          int qb, ks;
-          unit_decode(un, qb, ks);
-          held[h] = score_unit<T, C, DK>(qimg, kimg, lam, L, aloc, ea, eb, fact, qb, ks, lane);
-          where[h] = qb * NKS_C + ks;
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int h = 0; h < UHOLD; ++h)
-        if (where[h] >= 0) reinterpret_cast<Frag<T>*>(pf)[where[h] * 64 + lane] = held[h];
+    for (int un = w; un < NUNITS; un += NW) {
+      int qb, ks;
+      unit_decode(un, qb, ks);
+      const Frag<T> f = score_unit<T, C, DK>(qimg, kimg, lam, L, aloc, ea, eb, fact, qb, ks, lane);
+      reinterpret_cast<Frag<T>*>(pf)[(qb * NKS_C + ks) * 64 + lane] = f;
     }
     __syncthreads();
 
     // intra-chunk values
     Frag<T> vfr[NKS_C];
 #pragma unroll
-    for (int ks = 0; ks < NKS_C; ++ks) vfr[ks] = col_frag<T, C, DV>(smem + S.vt, w, ks, lane);
+    for (int ks = 0; ks < NKS_C; ++ks) vfr[ks] = col_frag<T, C, DV>(smem + SB.vt, w, ks, lane);
     f32x4 O[NQB];
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
@@ -918,10 +995,16 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_query_kernel(Params p) {
       for (int ks = 0; ks <= qb / 2; ++ks) mma(O[qb], vfr[ks], lds_frag<T>(pf, qb * NKS_C + ks, lane));
     }
 
-    // Fenwick nodes inside the sweep (levels J+1 .. J+m)
+    // Fenwick nodes inside the sweep (levels J+1 .. J+m): chunk u reads slot ((u>>a)<<a) - 1
+    // for each set bit a of u
 #pragma unroll
-    for (int a = 0; a < LMAX; ++a)
-      if ((u >> a) & 1) node_readout<T, C, DK>(LN[a], qimg, lam, L, ea, J + 1 + a, __expf(LD[a]), lane, O);
+    for (int s = 0; s < NSLOT; ++s) {
+#pragma unroll
+      for (int a = 0; a < LMAX; ++a) {
+        if (((u >> a) & 1) && ((u >> a) << a) - 1 == s)
+          node_readout<T, C, DK>(SL[s], qimg, lam, L, ea, J + 1 + a, __expf(SD[s]), lane, O);
+      }
+    }
 
     // Fenwick nodes made of whole earlier sweeps (levels J+m+1 ..), lowest bit first
     {
@@ -935,47 +1018,22 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_query_kernel(Params p) {
       }
       for (int x = XREG; x < next; ++x) {    // beyond the register budget: load on demand
         Frag<T> A[NKS_D];
-        load_node(A, node_index(x));
+        const int e = node_index(x);
+        load_node(A, e);
         node_readout<T, C, DK>(A, qimg, lam, L, ea, node_level(x), __expf(gam + dext), lane, O);
-        dext += gn[node_index(x)];
+        dext += node_ld_f(p.gnode + node_slot(bh, ns, e, NW, w));
       }
     }
-    // store rows [0, valid)
+    // store rows [0, valid); NaN if a node never arrived
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int qi = 16 * qb + j;
+      if (bad) O[qb] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
       if (qi < valid) store_quad<T>(og + (size_t)(t0 + qi) * DV + 16 * w + 4 * g, O[qb]);
     }
-
-    // carry the chunk's state into the sweep's Fenwick nodes
-    if (u + 1 < nch) {
-      constexpr int NDKB = DK / 16;
-      f32x4 F[NDKB];
-      chunk_state<T, C, DK>(smem + S.kt, vfr, lane, F);
-      const int cz = __builtin_ctz(u + 1);
 #pragma unroll
-      for (int a = 0; a < LMAX; ++a) {
-        LD[a] += gtot;
-        if (a < cz) {
-          const float d = __expf(LD[a]);
-#pragma unroll
-          for (int s2 = 0; s2 < NKS_D; ++s2) {
-            f32x4 lo, hi;
-            frag_to_f32(LN[a][s2], lo, hi);
-            F[2 * s2] += d * lo;
-            if (2 * s2 + 1 < NDKB) F[2 * s2 + 1] += d * hi;
-          }
-        }
-      }
-#pragma unroll
-      for (int a = 0; a < LMAX; ++a) {
-        if (a == cz) {
-          LD[a] = 0.f;
-#pragma unroll
-          for (int s2 = 0; s2 < NKS_D; ++s2) LN[a][s2] = node_frag<T, DK>(F, s2);
-        }
-      }
-    }
+    for (int s = 0; s < NSLOT; ++s)
+      if (s < u) SD[s] += gtot;
     gam += gtot;
   }
 }

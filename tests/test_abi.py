@@ -63,8 +63,8 @@ def test_workspace_bytes(L):
     assert ws(1, 1, 64, 64, 64, 64, 1, 0) == 0              # one chunk
     n = ws(4, 16, 8192, 64, 64, 64, 4, 0)
     ns = 8192 // 64 // 4 - 1
-    per = 64 * ns
-    expect = per * 64 * 64 * 4 + 2 * per * 4 + per * 4 * 2 * 512 * 2
+    per = 64 * ns                   # (head, node) pairs; each node is kept per wave (dv/16 = 4)
+    expect = per * 64 * 64 * 4 + per * 4 * 2 * 512 * 2 + 2 * per * 4 * 4 + 64 * 4
     assert expect <= n <= expect + 4 * 256
     assert ws(4, 16, 8192, 48, 64, 64, 4, 0) == 0           # invalid -> 0
     assert ws(1, 1, 1000, 64, 64, 64, 2, 0) > 0             # ragged T

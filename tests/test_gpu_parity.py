@@ -166,6 +166,57 @@ def test_caller_workspace_matches_library_workspace():
     assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("sweep", [1, 2, 4])
+def test_poisoned_workspace(dtype, sweep):
+    """Nodes pass between workgroups through the workspace: filled with 0xFF bytes (NaN data,
+    set flags) before every call, it must still give oracle parity, i.e. every node is read
+    only after its producer published it and the flags are cleared by the library."""
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    B, H, T = 2, 3, 3000
+    n = lla.workspace_bytes(B, H, T, 64, 64, 64, sweep, dtype)
+    assert n > 0
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    for seed in range(2):
+        x = generate(custom(B, H, T, 64, 64, dtype=dtype), seed=100 + seed, log_a_mode="lowdecay")
+        d = {k_: v_.cuda() for k_, v_ in x.items()}
+        ws.fill_(0xFF)
+        got = lla.forward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], chunk=64, sweep=sweep, workspace=ws)
+        torch.cuda.synchronize()
+        got = got.double().cpu().numpy()
+        want = O.bruteforce(x["q"], x["k"], x["v"], x["log_a"], x["lam"])
+        err = rel_l2(got, want)
+        print(f"poisoned workspace {dtype} sweep {sweep} seed {seed}: rel_l2={err:.3e}", flush=True)
+        assert np.all(np.isfinite(got))
+        assert err <= tol_for(dtype)
+
+
+def test_poisoned_workspace_headline_shape():
+    """The same at the benchmark's shape and launch configuration, three calls in a row."""
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    w = WORKLOADS["b4h16_t8192_d64_bf16"]
+    sweep = lla.default_sweep(w.B, w.H, w.T, w.dk, w.dv, w.chunk, w.dtype)
+    n = lla.workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.chunk, sweep, w.dtype)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    rows = sample_rows(w.T, w.chunk)
+    for seed in range(3):
+        x = generate(w, seed=200 + seed, log_a_mode="nodecay" if seed == 1 else None)
+        d = {k_: v_.cuda() for k_, v_ in x.items()}
+        ws.fill_(0xFF)
+        got = lla.forward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], chunk=w.chunk, sweep=sweep,
+                          workspace=ws)
+        torch.cuda.synchronize()
+        got = got.double().cpu().numpy()
+        assert np.all(np.isfinite(got))
+        for (b, h) in [(0, 0), (w.B - 1, w.H - 1), (1, 7)]:
+            want = O.bruteforce_rows(x["q"], x["k"], x["v"], x["log_a"], x["lam"], b, h, rows)
+            err = rel_l2(got[b, h, rows], want)
+            print(f"headline poisoned seed {seed} head ({b},{h}): rel_l2={err:.3e}", flush=True)
+            assert err <= tol_for(w.dtype)
+
+
 def test_plain_entry_points():
     import ctypes
     import torch
