@@ -36,10 +36,11 @@
  *
  * Execution: two kernels on `stream`: a fill kernel that clears the workspace's
  * ticket counter and node flags, then one forward kernel in which each workgroup
- * walks R consecutive chunks of one head (a "sweep"), publishes that sweep's Fenwick
- * node in the workspace and reads the nodes of earlier sweeps of its head, waiting
- * for them with bounded polls. Workgroups are ordered by an atomic ticket, so a
- * workgroup only ever waits for workgroups that started before it. Should a wait
+ * loads R consecutive chunks of one head (a "sweep") into shared memory, publishes
+ * that sweep's Fenwick node in the workspace and reads the nodes of earlier sweeps
+ * of its head, waiting for them with bounded polls. Workgroups are ordered by an
+ * atomic ticket, so a workgroup only ever waits for workgroups that started before
+ * it. Should a wait
  * nevertheless run out (a fault elsewhere), the affected outputs are written as NaN
  * and the kernel still completes.
  *
@@ -98,7 +99,8 @@ int loglinear_attn_fwd_f32(const float* q, const float* k, const float* v,
  * Extended entry: explicit dtype, chunk size, sweep length and workspace.
  *   chunk : 0 = library default, else one of 16, 32, 64, 128.
  *   sweep : 0 = library default, else the number of consecutive chunks one
- *           workgroup walks (1, 2 or 4).
+ *           workgroup holds in shared memory at once (1 or 2; LLA_ERR_UNSUPPORTED
+ *           when they do not fit the device's shared memory).
  *   workspace / workspace_bytes : caller-owned device memory of at least
  *           loglinear_attn_workspace_bytes(...) bytes (256-byte aligned), or
  *           NULL/0 to let the library allocate stream-ordered on `stream`. The

@@ -53,23 +53,31 @@ inline bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 
 inline int bit_len(unsigned x) { int n = 0; while (x) { ++n; x >>= 1; } return n; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-constexpr long kTargetWorkgroups = 2048;   // ~8 per CU on 256 CUs
 constexpr int kSpinLimit = 1 << 20;        // polls of a node flag (each ~1 us) before giving up
+constexpr int kLdsPerCU = 160 * 1024;      // gfx950 shared memory per compute unit
+constexpr long kMinWorkgroups = 512;       // below this, prefer one chunk per workgroup
 
 struct Plan {
   int C, R, m, nchunks, nsweep, ns, L, esize, nw;
   long BH;
-  size_t ws_bytes, off_sync, off_gnode, off_node32, off_nodeT, n_sync;
+  size_t ws_bytes, off_sync, off_gnode, off_nodeT, n_sync;
   int smem;
 };
 
 int default_chunk(int dk, int dv) { return (dk <= 16 && dv <= 16) ? 16 : 64; }
 
-int default_sweep(long BH, int T, int C) {
+int smem_bytes(int esize, int C, int dk, int dv, int R) {
+  return lla::smem_layout(esize, C, dk, dv, R).total;
+}
+
+// Two resident chunks when that keeps 8 waves per compute unit (2 per SIMD) within the
+// shared memory and leaves enough workgroups; one otherwise.
+int default_sweep(long BH, int T, int C, int dk, int dv, int esize) {
   const int nchunks = (T + C - 1) / C;
-  int R = 1;
-  while (R * 2 <= lla::kSweepCap && BH * ((nchunks + 2 * R - 1) / (2 * R)) >= kTargetWorkgroups) R *= 2;
-  return R;
+  const int nw = dv / 16;
+  const int wg_per_cu = nw >= 8 ? 1 : 8 / nw;
+  const bool fits = smem_bytes(esize, C, dk, dv, 2) * wg_per_cu <= kLdsPerCU;
+  return (fits && nchunks > 1 && BH * ((nchunks + 1) / 2) >= kMinWorkgroups) ? 2 : 1;
 }
 
 // Host-only part of the plan: sizes and layout; no device calls.
@@ -78,8 +86,7 @@ int make_plan(int B, int H, int T, int dk, int dv, int chunk, int sweep, int dty
   if (B < 0 || H < 0 || T < 0) return LLA_ERR_INVALID_ARG;
   if (!supported_dim(dk) || !supported_dim(dv)) return LLA_ERR_UNSUPPORTED;
   if (chunk != 0 && !supported_dim(chunk)) return LLA_ERR_UNSUPPORTED;
-  if (sweep != 0 && (sweep < 1 || sweep > lla::kSweepCap || (sweep & (sweep - 1))))
-    return LLA_ERR_UNSUPPORTED;
+  if (sweep != 0 && sweep != 1 && sweep != 2) return LLA_ERR_UNSUPPORTED;
   const int C = chunk ? chunk : default_chunk(dk, dv);
   const long BH = (long)B * H;
   if (BH > 65535) return LLA_ERR_UNSUPPORTED;
@@ -90,7 +97,7 @@ int make_plan(int B, int H, int T, int dk, int dv, int chunk, int sweep, int dty
   pl.esize = dtype == LLA_DTYPE_BF16 ? 2 : 4;
   pl.nw = dv / 16;
   pl.nchunks = (T + C - 1) / C;
-  pl.R = sweep ? sweep : default_sweep(BH, T, C);
+  pl.R = sweep ? sweep : default_sweep(BH, T, C, dk, dv, pl.esize);
   pl.m = bit_len((unsigned)pl.R) - 1;
   pl.nsweep = pl.nchunks > 0 ? (pl.nchunks + pl.R - 1) / pl.R : 0;
   pl.ns = pl.nsweep > 1 ? pl.nsweep - 1 : 0;
@@ -100,12 +107,9 @@ int make_plan(int B, int H, int T, int dk, int dv, int chunk, int sweep, int dty
   pl.n_sync = lla::kFlagBase + nodes;
   pl.off_sync = off;   off = align256(off + pl.n_sync * 4);
   pl.off_gnode = off;  off = align256(off + nodes * 4);
-  pl.off_node32 = off; off = align256(off + nodes * (dk / 16) * 64 * 16);
   pl.off_nodeT = off;  off = align256(off + nodes * ((dk + 31) / 32) * 64 * 8 * pl.esize);
   pl.ws_bytes = pl.ns > 0 ? off : 0;
-  const int Lmem = pl.L > 0 ? pl.L : 1;
-  pl.smem = dtype == LLA_DTYPE_BF16 ? lla::fused_smem_bytes<lla::bf16>(C, dk, dv, Lmem)
-                                    : lla::fused_smem_bytes<float>(C, dk, dv, Lmem);
+  pl.smem = smem_bytes(pl.esize, C, dk, dv, pl.R);
   return LLA_OK;
 }
 
@@ -150,7 +154,6 @@ int launch(const lla_fwd_args& a, const Plan& pl, void* ws, hipStream_t stream) 
   if (ws) {
     p.sync = reinterpret_cast<int*>((char*)ws + pl.off_sync);
     p.gnode = reinterpret_cast<float*>((char*)ws + pl.off_gnode);
-    p.node32 = reinterpret_cast<float*>((char*)ws + pl.off_node32);
     p.nodeT = (char*)ws + pl.off_nodeT;
   }
   p.spin_limit = kSpinLimit;
@@ -168,9 +171,10 @@ int launch(const lla_fwd_args& a, const Plan& pl, void* ws, hipStream_t stream) 
     if (hipGetLastError() != hipSuccess) return LLA_ERR_HIP;
   }
   if (mark(1) != hipSuccess) return LLA_ERR_HIP;
-  if (set_smem(ks->fused, pl.smem) != hipSuccess) return LLA_ERR_HIP;
+  const void* fn = ks->fwd[pl.R - 1];
+  if (set_smem(fn, pl.smem) != hipSuccess) return LLA_ERR_HIP;
   const unsigned grid = (unsigned)(pl.nsweep * pl.BH);
-  if (hipLaunchKernel(ks->fused, dim3(grid), dim3(64 * pl.nw), args, pl.smem, stream) != hipSuccess)
+  if (hipLaunchKernel(fn, dim3(grid), dim3(64 * pl.nw), args, pl.smem, stream) != hipSuccess)
     return LLA_ERR_HIP;
   if (mark(2) != hipSuccess) return LLA_ERR_HIP;
   return LLA_OK;
@@ -246,8 +250,8 @@ int loglinear_attn_default_sweep(int B, int H, int T, int dk, int dv, int chunk,
   (void)dtype;
   if (B < 0 || H < 0 || T < 0) return 0;
   const int C = chunk ? chunk : default_chunk(dk, dv);
-  if (!supported_dim(C)) return 0;
-  return default_sweep((long)B * H, T, C);
+  if (!supported_dim(C) || !supported_dim(dk) || !supported_dim(dv)) return 0;
+  return default_sweep((long)B * H, T, C, dk, dv, dtype == LLA_DTYPE_F32 ? 4 : 2);
 }
 
 const char* loglinear_attn_status_string(int status) {

@@ -4,7 +4,7 @@
 namespace lla {
 
 struct KernelSet {
-  const void* fused;         // lla_fused_kernel<T, C, DK, DV>
+  const void* fwd[2];        // lla_fwd_kernel<T, C, DK, DV, NB> for NB = 1, 2 resident chunks
 };
 
 // dtype 0 = bf16, 1 = f32; C, DK, DV in {16, 32, 64, 128}; nullptr otherwise.

@@ -8,7 +8,8 @@ namespace lla {
 
 template <typename TY, int C, int DK, int DV>
 KernelSet make_set() {
-  return KernelSet{reinterpret_cast<const void*>(&lla_fused_kernel<TY, C, DK, DV>)};
+  return KernelSet{{reinterpret_cast<const void*>(&lla_fwd_kernel<TY, C, DK, DV, 1>),
+                    reinterpret_cast<const void*>(&lla_fwd_kernel<TY, C, DK, DV, 2>)}};
 }
 
 template <typename TY, int C, int DK>

@@ -1,4 +1,4 @@
-// lla_kernels.hpp — gfx950 (CDNA4) kernels of the chunkwise log-linear Mamba-2 forward pass.
+// lla_kernels.hpp — gfx950 (CDNA4) forward kernel of chunkwise log-linear Mamba-2.
 //
 // Operation, per (b,h) and position t:
 //   o_t = sum_{s<=t} lambda[t, l(t,s)] * exp(A_t - A_s) * (q_t . k_s) * v_s,
@@ -16,26 +16,31 @@
 //   lambda[t, J+1+j] * exp(A_t - A_end) * q_t^T N,   N = sum_{s in block} exp(A_end - A_s) k_s v_s^T
 // with A_end the prefix decay at the block's last position.
 //
-// Work split. One kernel, one workgroup per "sweep" of R = 2^m consecutive chunks of one head
-// (lla_fused_kernel). Workgroups take a ticket from an atomic counter and map it sweep-major,
-// so every sweep they wait for belongs to a workgroup that started earlier.
-//   phase A: chunk states of the sweep (decayed k^T v on MFMA); the Fenwick nodes inside the
-//            sweep are kept in registers; the sweep total plus the nodes of earlier sweeps it
-//            absorbs (a Fenwick tree over sweeps) is published as this sweep's node.
-//   phase B: chunk by chunk: dense masked block on MFMA, read-out of the live Fenwick nodes
-//            (inside the sweep from registers, earlier sweeps from the published nodes),
-//            output store.
-// A node is published per wave (16 value columns): data stores, an agent-scope release fence,
-// then a flag; readers poll the flag (bounded: on timeout the outputs are set to NaN so that
-// a broken dependency can never hang the device) and take an agent-scope acquire fence.
+// Work split. One kernel, one workgroup per "sweep" of R consecutive chunks of one head (R = 1
+// or 2, all of them resident in shared memory at once), one wave per 16 value columns.
+// Workgroups take a ticket from an atomic counter and map it sweep-major, so every sweep
+// they wait for belongs to a workgroup that started earlier.
+//   load:    q, k, v of the sweep go straight from HBM into swizzled shared-memory images
+//            (global_load_lds), lambda and log_a through registers; one wait for all of it.
+//   phase A: chunk states k^T (w v) on MFMA (w: decay to the chunk end); the sweep total plus
+//            the nodes of earlier sweeps it absorbs (a Fenwick tree over sweeps) is published
+//            as this sweep's node; the state of chunk 0 is kept for chunk 1 (level J+1).
+//   phase B: per chunk: masked scores on MFMA -> P^T, P.V on MFMA, read-out of the live
+//            Fenwick nodes on MFMA (inside the sweep from registers, earlier sweeps from the
+//            published nodes), output store.
+// A node is published per wave (16 value columns) with device-scope stores, then a flag;
+// readers poll the flag (bounded: on timeout the outputs are set to NaN so that a broken
+// dependency can never hang the device) and read the node with device-scope loads.
 //
-// MFMA operand convention. All products use 16x16 output tiles. A K=32 operand fragment
-// gives lane (j = lane & 15, g = lane >> 4) eight values e = 0..7 at contraction index
-//   pi(g, e) = 4g + (e & 3) + 16 (e >> 2).
-// With this numbering the 16x16 accumulator layout (lane (j,g) holds rows 4g..4g+3 of
-// column j) of two vertically stacked tiles is exactly one operand fragment, so scores and
-// states produced by one MFMA feed the next one from registers. bf16 uses one
-// v_mfma_f32_16x16x32_bf16 per fragment, f32 eight v_mfma_f32_16x16x4_f32.
+// MFMA conventions. 16x16 output tiles; the accumulator gives lane (j = lane & 15,
+// g = lane >> 4) rows 4g..4g+3 of column j. A K=32 operand fragment gives lane (j, g) the
+// contraction indices 8g..8g+7 of its row/column j (bf16: one v_mfma_f32_16x16x32_bf16; f32:
+// eight v_mfma_f32_16x16x4_f32). Tiles whose rows are later used as a contraction index are
+// computed in pairs with permuted rows,
+//   tile 2s+h, row i  <->  index 32s + 8(i/4) + 4h + (i%4),
+// so that the two accumulators a lane holds are exactly its operand fragment for indices
+// 32s..32s+31: masked scores become P^T and chunk states become read-out operands without
+// leaving registers.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -47,8 +52,16 @@ typedef __bf16 bf16;
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kMaxThreads = 512;   // 8 waves: one per 16 output columns, dv <= 128
+constexpr int kLamCap = 24;       // lambda levels held per position (T <= 2^23)
+constexpr int kMaxSweep = 2;      // chunks resident per workgroup
+
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // ----------------------------------------------------------------------------------------
 // fragments and MFMA
@@ -92,248 +105,139 @@ __device__ __forceinline__ void frag_to_f32(const Frag<float>& f, f32x4& lo, f32
   lo = f.lo; hi = f.hi;
 }
 
-__device__ __forceinline__ Frag<bf16> frag_select_impl(bool c, const Frag<bf16>& a, const Frag<bf16>& b) {
-  Frag<bf16> r; r.v = c ? a.v : b.v; return r;
-}
-__device__ __forceinline__ Frag<float> frag_select_impl(bool c, const Frag<float>& a, const Frag<float>& b) {
-  Frag<float> r; r.lo = c ? a.lo : b.lo; r.hi = c ? a.hi : b.hi; return r;
-}
 template <typename T> __device__ __forceinline__ Frag<T> zero_frag() {
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   return frag_from<T>(z, z);
 }
-template <typename T>
-__device__ __forceinline__ Frag<T> frag_select(bool c, const Frag<T>& a, const Frag<T>& b) {
-  return frag_select_impl(c, a, b);
-}
-
-// 4 consecutive elements of a fragment (one half: e0 = 0 or 4)
-template <typename T> struct Quad;
-template <> struct Quad<bf16> { typedef bf16x4 type; };
-template <> struct Quad<float> { typedef f32x4 type; };
 
 __device__ __forceinline__ int bit_length(unsigned x) { return 32 - __clz((int)x); }
 
-
-constexpr int kLamCap = 24;       // lambda levels held per position (T <= 2^23)
-constexpr int kSweepCap = 4;      // chunks per sweep: Fenwick nodes inside a sweep in registers
-
-// bf16 operands contracted over positions (v, decayed k) are read with the gfx950 transposing
-// LDS read from a row-major image; f32 ones are stored in fragment order instead.
-template <typename T> struct TrNative { static constexpr bool value = sizeof(T) == 2; };
-
 // ----------------------------------------------------------------------------------------
-// shared-memory images of one chunk
+// shared-memory images
 // ----------------------------------------------------------------------------------------
-// A [C, DF] block is kept row-major in 4-element quads whose place inside a row is XOR-swizzled:
-//   TR = false: quad q of row r sits at q ^ (r mod 16). A fragment read takes one quad of
-//               16 consecutive rows per 16 lanes: 16 distinct bank groups.
-//   TR = true : quad q of row r sits at q ^ 4 (r mod 4). A transposing read takes 4 quads of
-//               4 consecutive rows per 16 lanes: 16 distinct bank groups.
-template <typename T, int DF, bool TR>
-struct Img {
-  static constexpr int NQ = DF / 4;                  // quads per row
-  static constexpr int QB = 4 * (int)sizeof(T);      // bytes per quad
-  static constexpr int ROWB = DF * (int)sizeof(T);   // bytes per row
-  __device__ __forceinline__ static int swz(int r) {
-    return TR ? ((4 * (r & 3)) & (NQ - 1)) : (r & (NQ - 1) & 15);
-  }
-  __device__ __forceinline__ static int off(int r, int q) { return r * ROWB + (q ^ swz(r)) * QB; }
-};
+// Every q, k, v image is row-major (row = position) in 16-byte vectors whose place in the
+// row is XOR-swizzled at 16-byte granularity, so that global_load_lds can write an image
+// directly (one 16-byte piece per lane). ES = element bytes, NV = vectors per row.
+//   row images (q, k): conflict-free operand-fragment reads (16 rows x one vector) and, for
+//                      bf16 k, conflict-free transposing reads of chunk states (4 rows x quads
+//                      2c+h, c = 0..3);
+//   value images (v):  bf16: conflict-free transposing reads (4 rows x 4 consecutive quads);
+//                      f32: read element-wise with the row swizzle.
+template <int ES, int NV>
+__host__ __device__ constexpr int swz_row(int r) {
+  return ES == 2 ? (NV == 2 ? (r >> 3) & 1
+                  : NV == 4 ? (r >> 2) & 3
+                  : NV == 8 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3))
+                            : (((r & 3) << 2) | ((r >> 2) & 3)))
+                 : (NV == 4 ? (r >> 2) & 3 : NV == 8 ? (r >> 1) & 7 : r & 15);
+}
+template <int ES, int NV>
+__host__ __device__ constexpr int swz_val(int r) {
+  return ES == 2 ? (2 * (r & 3)) & (NV - 1) : swz_row<ES, NV>(r);
+}
 
-struct ChunkSmem {
-  int qimg, kimg, pf, kt, vt, lam, aloc, ea, eb, flag, total;
-};
+// byte offset of element f (feature) of row r in an image with NV vectors per row
+template <int ES, int NV, bool VAL>
+__device__ __forceinline__ int elem_off(int r, int f) {
+  constexpr int EPV = 16 / ES;
+  const int x = VAL ? swz_val<ES, NV>(r) : swz_row<ES, NV>(r);
+  return r * NV * 16 + (((f / EPV) ^ x) << 4) + (f % EPV) * ES;
+}
 
-// Byte offsets of one chunk's shared memory (host and device agree). A fragment slot is one
-// operand fragment for all 64 lanes (64 x 8 elements). with_q: the query-side images (q, k,
-// masked scores, lambda); with_kt: the decayed-key operand of chunk states.
-template <typename T>
-__host__ __device__ inline ChunkSmem chunk_smem(int C, int DK, int DV, int L, bool with_q,
-                                                bool with_kt) {
-  const int es = (int)sizeof(T);
-  const int slot = 64 * 8 * es;
-  const int nqb = C / 16, nks_c = (C + 31) / 32;
-  const bool trn = es == 2;
-  ChunkSmem s;
+// Shared-memory layout of the forward kernel (host and device agree). Per resident chunk u:
+// q, k, v images, lambda rows (C x L floats, row stride L), A / e^A / e^-A / state weights,
+// a flag word, and the P^T fragments of its masked scores; then the workgroup ticket.
+struct Smem {
+  int q[kMaxSweep], k[kMaxSweep], v[kMaxSweep], lam[kMaxSweep], dec[kMaxSweep], flag[kMaxSweep],
+      pf[kMaxSweep], ticket, total;
+};
+__host__ __device__ inline Smem smem_layout(int es, int C, int DK, int DV, int NB) {
+  Smem s;
   int off = 0;
-  s.qimg = off; off += with_q ? C * DK * es : 0;
-  s.kimg = off; off += with_q ? C * DK * es : 0;
-  s.pf = off;   off += with_q ? nqb * nks_c * slot : 0;
-  s.kt = off;   off += with_kt ? (trn ? C * DK * es : (DK / 16) * nks_c * slot) : 0;
-  s.vt = off;   off += trn ? C * DV * es : (DV / 16) * nks_c * slot;
-  s.lam = off;  off += with_q ? ((C * L * 4 + 15) & ~15) : 0;
-  s.aloc = off; off += C * 4;
-  s.ea = off;   off += C * 4;
-  s.eb = off;   off += C * 4;
-  s.flag = off; off += 16;
+  const int nqb = C / 16, nks_c = cdiv(C, 32);
+  for (int u = 0; u < kMaxSweep; ++u) {
+    const bool on = u < NB;
+    s.q[u] = off;    off += on ? C * DK * es : 0;
+    s.k[u] = off;    off += on ? C * DK * es : 0;
+    s.v[u] = off;    off += on ? C * DV * es : 0;
+    s.lam[u] = off;  off += on ? C * kLamCap * 4 : 0;
+    s.dec[u] = off;  off += on ? 4 * C * 4 : 0;
+    s.flag[u] = off; off += on ? 16 : 0;
+    s.pf[u] = off;   off += on ? nqb * nks_c * 64 * 8 * es : 0;
+  }
+  s.ticket = off; off += 16;
   s.total = (off + 255) & ~255;
   return s;
 }
 
-// Shared memory of the fused kernel: the phase A and phase B layouts overlap from offset 0;
-// the workgroup ticket sits after both.
-template <typename T>
-__host__ __device__ inline int fused_ticket_offset(int C, int DK, int DV, int L) {
-  const int a = chunk_smem<T>(C, DK, DV, L, false, true).total;
-  const int b = chunk_smem<T>(C, DK, DV, L, true, false).total;
-  return a > b ? a : b;
-}
-template <typename T>
-__host__ __device__ inline int fused_smem_bytes(int C, int DK, int DV, int L) {
-  return fused_ticket_offset<T>(C, DK, DV, L) + 16;
-}
-
 // ----------------------------------------------------------------------------------------
-// global -> registers -> shared memory staging of one chunk
+// staging: HBM -> shared memory
 // ----------------------------------------------------------------------------------------
 
-template <typename T> struct Pair;
-template <> struct Pair<bf16> { typedef bf16 __attribute__((ext_vector_type(2))) type; };
-template <> struct Pair<float> { typedef float __attribute__((ext_vector_type(2))) type; };
-
-template <typename T>
-__device__ __forceinline__ uint4 load_piece(const T* p, bool valid) {
-  if (!valid) return make_uint4(0, 0, 0, 0);
-  return *reinterpret_cast<const uint4*>(p);
-}
-
-__device__ __forceinline__ unsigned word_of(const uint4& u, int i) {
-  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
-}
-
-// element i of a 16-byte piece, as float
-template <typename T> __device__ __forceinline__ float elemf(const uint4& u, int i);
-template <> __device__ __forceinline__ float elemf<bf16>(const uint4& u, int i) {
-  const unsigned w = word_of(u, i >> 1);
-  return __builtin_bit_cast(float, (i & 1) ? (w & 0xffff0000u) : (w << 16));
-}
-template <> __device__ __forceinline__ float elemf<float>(const uint4& u, int i) {
-  return __builtin_bit_cast(float, word_of(u, i));
-}
-
-// a 16-byte piece with every element multiplied by w (rounded back to T)
-template <typename T> __device__ __forceinline__ uint4 scale_piece(const uint4& u, float w);
-template <> __device__ __forceinline__ uint4 scale_piece<bf16>(const uint4& u, float w) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  bf16x8 r;
+// One [C, DF] block (row stride DF; rows past `valid` replaced by row valid-1) into an image,
+// by global_load_lds: slot p of the image (row p/NV, physical vector p%NV) receives logical
+// vector (p%NV) ^ swizzle(row) of that row. Wave w issues the 1 KB blocks i*NW + w; lanes
+// past the image end issue nothing.
+template <typename T, int C, int DF, int NW, bool VAL>
+__device__ __forceinline__ void dma_image(unsigned char* img, const T* __restrict__ g, int valid,
+                                          int w, int lane) {
+  constexpr int ES = (int)sizeof(T), NV = DF * ES / 16, SLOTS = C * NV;
+  constexpr int ITERS = cdiv(SLOTS, 64 * NW);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (bf16)(elemf<bf16>(u, i) * w);
-  const u32x4 x = __builtin_bit_cast(u32x4, r);
-  return make_uint4(x[0], x[1], x[2], x[3]);
-}
-template <> __device__ __forceinline__ uint4 scale_piece<float>(const uint4& u, float w) {
-  return make_uint4(__builtin_bit_cast(unsigned, elemf<float>(u, 0) * w),
-                    __builtin_bit_cast(unsigned, elemf<float>(u, 1) * w),
-                    __builtin_bit_cast(unsigned, elemf<float>(u, 2) * w),
-                    __builtin_bit_cast(unsigned, elemf<float>(u, 3) * w));
-}
-
-// Writes one 16-byte piece (features f0..f0+EPP-1 of row r) into a swizzled image.
-template <typename T, int DF, bool TR>
-__device__ __forceinline__ void put_piece(unsigned char* img, int r, int f0, const uint4& x) {
-  typedef Img<T, DF, TR> I;
-  if (sizeof(T) == 2) {
-    // two quads 2p, 2p+1 land on an aligned pair, swapped when the swizzle flips bit 0
-    const int q = f0 / 4;
-    const int phys = q ^ I::swz(r);
-    uint4 y = (phys & 1) ? make_uint4(x.z, x.w, x.x, x.y) : x;
-    *reinterpret_cast<uint4*>(img + r * I::ROWB + (phys & ~1) * I::QB) = y;
-  } else {
-    *reinterpret_cast<uint4*>(img + I::off(r, f0 / 4)) = x;
-  }
-}
-
-// Writes 2 consecutive contraction elements k0, k0+1 (k0 even) of fragment row/column rc of
-// fragment slot `slot` (fragment-order storage, f32 position-contracted operands).
-template <typename T>
-__device__ __forceinline__ void put_pair(T* base, int slot, int rc, int k0,
-                                         const typename Pair<T>::type& p2) {
-  const int hidx = k0 >> 2;
-  const int g = hidx & 3, e = (hidx >> 2) * 4 + (k0 & 3);
-  *reinterpret_cast<typename Pair<T>::type*>(base + ((size_t)slot * 64 + rc + 16 * g) * 8 + e) = p2;
-}
-
-// One [C, DF] block (row stride DF; rows past `valid` read as 0) in registers: units of 2
-// consecutive rows x one 16-byte piece, dealt round-robin to the NT threads.
-template <typename T, int C, int DF, int NT>
-struct BlockRegs {
-  static constexpr int EPP = 16 / (int)sizeof(T);
-  static constexpr int PPR = DF / EPP;
-  static constexpr int UNITS = (C / 2) * PPR;
-  static constexpr int ITERS = (UNITS + NT - 1) / NT;
-  uint4 x[ITERS][2];
-
-  __device__ __forceinline__ static int row0(int tid, int it) {
-    const int u = tid + it * NT;
-    return u < UNITS ? 2 * (u / PPR) : 0;
-  }
-
-  // Branch-free: every lane issues its loads at a clamped, in-bounds address and zeroes what
-  // lies past `valid` (valid >= 1), so the compiler can count outstanding loads exactly.
-  __device__ __forceinline__ void fetch(const T* __restrict__ g, int valid, int tid) {
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int u = tid + it * NT;
-      const bool ok = (UNITS % NT == 0) || u < UNITS;
-      const int uc = ok ? u : 0;
-      const int r0 = 2 * (uc / PPR), f0 = (uc % PPR) * EPP;
-      const int ra = min(r0, valid - 1), rb = min(r0 + 1, valid - 1);
-      const uint4 a = *reinterpret_cast<const uint4*>(g + (size_t)ra * DF + f0);
-      const uint4 b = *reinterpret_cast<const uint4*>(g + (size_t)rb * DF + f0);
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      x[it][0] = (ok && r0 < valid) ? a : z;
-      x[it][1] = (ok && r0 + 1 < valid) ? b : z;
+  for (int it = 0; it < ITERS; ++it) {
+    const int blk = it * NW + w;                       // 1 KB block of the image
+    const int p = blk * 64 + lane;
+    if (p < SLOTS) {
+      const int r = p / NV, pv = p % NV;
+      const int v = pv ^ (VAL ? swz_val<ES, NV>(r) : swz_row<ES, NV>(r));
+      const int rs = min(r, valid - 1);
+      const T* src = g + (size_t)rs * DF + v * (16 / ES);
+#if defined(__HIP_DEVICE_COMPILE__)
+      // (the host pass of hipcc does not know this gfx950 builtin; only device code uses it)
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(img + blk * 1024), 16, 0, 0);
+#else
+      (void)src;
+#endif
     }
   }
+}
 
-  // row-major swizzled image; ws[it][i] (if given) scales row r0+i of unit it
-  template <bool TR, bool SCALE>
-  __device__ __forceinline__ void commit_image(unsigned char* img, int tid, const float (*ws)[2]) const {
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int u = tid + it * NT;
-      if (u >= UNITS) break;
-      const int r0 = 2 * (u / PPR), f0 = (u % PPR) * EPP;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        put_piece<T, DF, TR>(img, r0 + i, f0, SCALE ? scale_piece<T>(x[it][i], ws[it][i]) : x[it][i]);
-    }
-  }
+// global_load_lds instructions wave w issues for one [C, DF] image
+template <typename T, int C, int DF, int NW>
+__host__ __device__ constexpr int dma_count(int w) {
+  constexpr int SLOTS = C * DF * (int)sizeof(T) / 16;
+  int n = 0;
+  for (int it = 0; it * NW + w < cdiv(SLOTS, 64); ++it) ++n;
+  return n;
+}
 
-  // fragment-order storage of the position-contracted operand (rows = features)
-  template <bool SCALE>
-  __device__ __forceinline__ void commit_frags(T* trf, int tid, const float (*ws)[2]) const {
-    constexpr int NKS_C = (C + 31) / 32;
-    typedef typename Pair<T>::type P2;
-    const P2 zero2 = {};
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const int u = tid + it * NT;
-      if (u >= UNITS) break;
-      const int r0 = 2 * (u / PPR), f0 = (u % PPR) * EPP;
-      const int k0 = r0 & 31, ks = r0 >> 5;
-      const float w0 = SCALE ? ws[it][0] : 1.f, w1 = SCALE ? ws[it][1] : 1.f;
-#pragma unroll
-      for (int i = 0; i < EPP; ++i) {
-        const int f = f0 + i;
-        P2 p2;
-        p2[0] = (T)(elemf<T>(x[it][0], i) * w0);
-        p2[1] = (T)(elemf<T>(x[it][1], i) * w1);
-        put_pair<T>(trf, (f >> 4) * NKS_C + ks, f & 15, k0, p2);
-        if (C < 32) put_pair<T>(trf, (f >> 4) * NKS_C + ks, f & 15, k0 + 16, zero2);
-      }
-    }
-  }
-};
+// s_waitcnt vmcnt(min(N, 63)) alone (expcnt and lgkmcnt left at their maxima); the counter
+// never exceeds 63, so the clamp only waits longer
+template <int N0>
+__device__ __forceinline__ void wait_vm() {
+  constexpr int N = N0 > 63 ? 63 : N0;
+  static_assert(N >= 0, "vmcnt");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Workgroup barrier for shared memory only: this wave's shared-memory accesses complete, then
+// s_barrier. (__syncthreads would also wait for every outstanding global access, including
+// copies still meant to be in flight.)
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // lambda rows of one chunk (C*L contiguous floats) in registers: NF floats per thread, each
-// loaded at a clamped in-bounds index (branch-free) and zeroed past the chunk's valid rows.
+// loaded at a clamped in-bounds index and zeroed past the chunk's valid rows.
 template <int C, int NT>
 struct LamRegs {
-  static constexpr int NF = (C * kLamCap + NT - 1) / NT;
+  static constexpr int NF = cdiv(C * kLamCap, NT);
   float x[NF];
-
   __device__ __forceinline__ void fetch(const float* __restrict__ g, int nvalid, int tid) {
 #pragma unroll
     for (int it = 0; it < NF; ++it) {
@@ -342,7 +246,6 @@ struct LamRegs {
       x[it] = i < nvalid ? v : 0.f;
     }
   }
-
   __device__ __forceinline__ void commit(float* lam, int ntotal, int tid) const {
 #pragma unroll
     for (int it = 0; it < NF; ++it) {
@@ -383,23 +286,22 @@ struct DecayRegs {
 #pragma unroll
     for (int e = 0; e < E; ++e) a[e] += excl;
   }
-  // A at chunk position r (all lanes of the wave must call it together)
-  __device__ __forceinline__ float at(int r) const {
-    if (E == 1) return __shfl(a[0], r, 64);
-    const float lo = __shfl(a[0], r / E, 64);
-    const float hi = __shfl(a[E - 1], r / E, 64);
-    return (r % E) ? hi : lo;
+  // total log decay of the chunk (all lanes of the wave must call it together)
+  __device__ __forceinline__ float total() const {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a[E - 1]), 63));
   }
-  // wave 0: publish A, e^A, e^-A and whether the factorised decay is safe (|A| < 40)
-  __device__ __forceinline__ void publish(float* aloc, float* ea, float* eb, int* flag, int lane) const {
+  // wave 0: publish A, e^A, e^-A, the state weights exp(g - A) and whether the factorised
+  // decay e^{A_i} e^{-A_s} is safe (|A| < 40)
+  __device__ __forceinline__ void publish(float* dec, int* flag, float g, int lane) const {
     float amax = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int i = lane * E + e;
       if (i < C) {
-        aloc[i] = a[e];
-        ea[i] = __expf(a[e]);
-        eb[i] = __expf(-a[e]);
+        dec[i] = a[e];
+        dec[C + i] = __expf(a[e]);
+        dec[2 * C + i] = __expf(-a[e]);
+        dec[3 * C + i] = __expf(g - a[e]);
         amax = fmaxf(amax, fabsf(a[e]));
       }
     }
@@ -413,105 +315,220 @@ struct DecayRegs {
 // operand fragments from shared memory
 // ----------------------------------------------------------------------------------------
 
-template <typename T>
-__device__ __forceinline__ Frag<T> lds_frag(const T* base, int slot, int lane) {
-  return reinterpret_cast<const Frag<T>*>(base)[slot * 64 + lane];
-}
-
-template <typename T> __device__ __forceinline__ typename Quad<T>::type lds_quad(const unsigned char* p) {
-  return *reinterpret_cast<const typename Quad<T>::type*>(p);
-}
-
-// Row-major operand fragment (rows = positions rb*16.., contraction = features 32s..32s+31)
+// Row operand: row r of a row image, contraction features 32s + 8g .. +7 (zero past DF).
 template <typename T, int DF>
-__device__ __forceinline__ Frag<T> row_frag(const unsigned char* img, int rb, int s, int lane) {
-  typedef Img<T, DF, false> I;
-  typedef typename Quad<T>::type Q4;
-  const int r = 16 * rb + (lane & 15), g = lane >> 4;
-  const int q0 = 8 * s + g, q1 = q0 + 4;
-  const Q4 z = {};
-  const Q4 lo = lds_quad<T>(img + I::off(r, q0));
-  const Q4 hi = (q1 < I::NQ) ? lds_quad<T>(img + I::off(r, q1)) : z;
+__device__ __forceinline__ Frag<T> row_frag(const unsigned char* img, int r, int s, int lane) {
+  constexpr int ES = (int)sizeof(T), NV = DF * ES / 16;
+  const int g = lane >> 4;
   Frag<T> f;
-  if constexpr (sizeof(T) == 2) {
-    f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  if constexpr (ES == 2) {
+    const int v = 4 * s + g;
+    const bool ok = NV >= 4 || v < NV;
+    const int x = swz_row<2, NV>(r);
+    u32x4 d = *reinterpret_cast<const u32x4*>(img + r * NV * 16 + (((ok ? v : 0) ^ x) << 4));
+    if (!ok) d = u32x4{0u, 0u, 0u, 0u};
+    f.v = __builtin_bit_cast(bf16x8, d);
   } else {
-    f.lo = lo; f.hi = hi;
+    const int v0 = 8 * s + 2 * g;
+    const bool ok = NV >= 8 || v0 < NV;
+    const int x = swz_row<4, NV>(r);
+    const int vv = ok ? v0 : 0;
+    f.lo = *reinterpret_cast<const f32x4*>(img + r * NV * 16 + ((vv ^ x) << 4));
+    f.hi = *reinterpret_cast<const f32x4*>(img + r * NV * 16 + (((vv + 1) ^ x) << 4));
+    if (!ok) { f.lo = f32x4{0.f, 0.f, 0.f, 0.f}; f.hi = f.lo; }
   }
   return f;
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+__device__ __forceinline__ s16x4 ds_read_tr(const unsigned char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+}
 
-// Position-contracted operand fragment (rows = features fb*16.., contraction = positions
-// 32ks..32ks+31) from a row-major TR-swizzled bf16 image, by two transposing LDS reads:
-// in each 16-lane group the read returns to lane i, element b, element i%4 of the quad read
-// by lane 4b + i/4; so lane k of group g reads row 32ks + 16h + 4g + k/4, quad 4fb + k%4.
-template <int C, int DF>
-__device__ __forceinline__ Frag<bf16> tr_frag(const unsigned char* img, int fb, int ks, int lane) {
-  typedef Img<bf16, DF, true> I;
+// Position-contracted operand: rows = 16 features, contraction = positions 32ks + 8g + e.
+// Output row i holds feature 16fsel + i of a value image (VAL), or feature
+// 32fsel + 8(i/4) + 4h + (i%4) of a key image (state tile (fsel, h)). bf16 by two transposing
+// reads: in each 16-lane group the read returns to lane i, element c, element i%4 of the quad
+// addressed by lane 4c + i/4, so lane k addresses position base + k/4 and the quad of output
+// rows 4(k%4)..4(k%4)+3. f32 element-wise. Positions >= C (C = 16) and features >= DF are 0.
+template <typename T, int C, int DF, bool VAL>
+__device__ __forceinline__ Frag<T> col_frag(const unsigned char* img, int fsel, int h, int ks,
+                                            int lane) {
+  constexpr int ES = (int)sizeof(T), NV = DF * ES / 16;
   const int k = lane & 15, g = lane >> 4;
-  const int q = 4 * fb + (k & 3);
-  const int t0 = 32 * ks + 4 * g + (k >> 2);
-  const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4*)(img + I::off(t0, q)));
-  s16x4 v1 = {0, 0, 0, 0};
-  if (C >= 32)
-    v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(img + I::off(t0 + 16, q)));
-  Frag<bf16> f;
-  f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+  const bool tok = C >= 32 || g < 2;
+  Frag<T> f;
+  if constexpr (ES == 2) {
+    const int qa = VAL ? 4 * fsel + (k & 3) : 8 * fsel + 2 * (k & 3) + h;    // addressed by k
+    const int qo = VAL ? 4 * fsel + (k >> 2) : 8 * fsel + 2 * (k >> 2) + h;  // of k's output rows
+    const bool qaok = qa < 2 * NV, qook = qo < 2 * NV;
+    const int t = tok ? 32 * ks + 8 * g + (k >> 2) : 0;
+    const int q = qaok ? qa : 0;
+    const int x0 = VAL ? swz_val<2, NV>(t) : swz_row<2, NV>(t);
+    const int x1 = VAL ? swz_val<2, NV>(t + 4) : swz_row<2, NV>(t + 4);
+    const s16x4 a = ds_read_tr(img + t * NV * 16 + (((q >> 1) ^ x0) << 4) + ((q & 1) << 3));
+    const s16x4 b = ds_read_tr(img + (t + 4) * NV * 16 + (((q >> 1) ^ x1) << 4) + ((q & 1) << 3));
+    f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+    if (!(tok && qook)) f = zero_frag<bf16>();
+  } else {
+    const int feat = VAL ? 16 * fsel + k : 32 * fsel + 8 * (k >> 2) + 4 * h + (k & 3);
+    const bool fok = feat < DF;
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = 32 * ks + 8 * g + i;
+      const bool ok = tok && fok && t < C;
+      const float val = *reinterpret_cast<const float*>(img + elem_off<4, NV, VAL>(ok ? t : 0, fok ? feat : 0));
+      e[i] = ok ? val : 0.f;
+    }
+    f.lo = f32x4{e[0], e[1], e[2], e[3]};
+    f.hi = f32x4{e[4], e[5], e[6], e[7]};
+  }
   return f;
 }
 
-// position-contracted operand: transposing read (bf16) or fragment-order slot (f32)
-template <typename T, int C, int DF>
-__device__ __forceinline__ Frag<T> col_frag(const unsigned char* base, int fb, int ks, int lane) {
-  if constexpr (TrNative<T>::value) {
-    return tr_frag<C, DF>(base, fb, ks, lane);
-  } else {
-    constexpr int NKS_C = (C + 31) / 32;
-    return lds_frag<T>(reinterpret_cast<const T*>(base), fb * NKS_C + ks, lane);
-  }
+// fragment multiplied element-wise by (w0, w1)
+__device__ __forceinline__ Frag<bf16> frag_scale(const Frag<bf16>& f, const f32x4& w0, const f32x4& w1) {
+  f32x4 lo, hi;
+  frag_to_f32(f, lo, hi);
+  return frag_from<bf16>(lo * w0, hi * w1);
 }
+__device__ __forceinline__ Frag<float> frag_scale(const Frag<float>& f, const f32x4& w0, const f32x4& w1) {
+  Frag<float> r; r.lo = f.lo * w0; r.hi = f.hi * w1; return r;
+}
+
+// Operand reads of one chunk's images. bf16: byte offsets per lane computed once for the
+// whole kernel (a row's swizzle depends only on its low 4 bits, so query blocks, key steps and
+// tile halves are immediate offsets; images differ only by their base). f32: the generic
+// element-wise reads above.
+template <typename T, int C, int DK, int DV> struct Reader;
+
+template <int C, int DK, int DV>
+struct Reader<bf16, C, DK, DV> {
+  static constexpr int NVK = DK / 8, NVV = DV / 8, RBK = NVK * 16, RBV = NVV * 16;
+  static constexpr int NKS_D = cdiv(DK, 32);
+  int oq[NKS_D];        // q row j, features 32s + 8g ..            (+ 16qb rows)
+  int ok[2][NKS_D];     // k row 8(j/4) + 4t + j%4 of score tile t  (+ 32ks rows)
+  int okt[2][NKS_D];    // k^T, state tile (s, .), read r: row 8g + k/4 + 4r, quad 8s + 2(k%4) (+ 32ks rows, + h quads)
+  int ovt;              // v^T, value block w: row 8g + k/4, quad 4w + k%4 (+ 32ks rows, + 4 rows for read 1)
+  bool fq;              // the lane's 8-feature vector exists (dk = 16: g < 2)
+  bool fkt;             // the lane's state-tile output rows exist (dk = 16: k/4 < 2)
+  bool tv;              // the lane group's positions exist (C = 16: g < 2)
+
+  __device__ __forceinline__ void init(int lane, int w) {
+    const int k = lane & 15, g = lane >> 4, b = k >> 2, c = k & 3;
+    fq = NVK >= 4 || g < 2;
+    fkt = NVK >= 4 || b < 2;
+    tv = C >= 32 || g < 2;
+#pragma unroll
+    for (int s = 0; s < NKS_D; ++s) {
+      const int v = fq ? 4 * s + g : 0;
+      oq[s] = k * RBK + ((v ^ swz_row<2, NVK>(k)) << 4);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int r = min(8 * b + 4 * t + c, C - 1);
+        ok[t][s] = r * RBK + ((v ^ swz_row<2, NVK>(r)) << 4);
+      }
+      const int vk = (4 * s + c < NVK) ? 4 * s + c : 0;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int row = tv ? 8 * g + b + 4 * r : 0;
+        okt[r][s] = row * RBK + ((vk ^ swz_row<2, NVK>(row)) << 4);
+      }
+    }
+    const int row = tv ? 8 * g + b : 0;
+    ovt = row * RBV + (((2 * w + (c >> 1)) ^ swz_val<2, NVV>(row)) << 4) + 8 * (c & 1);
+  }
+  __device__ __forceinline__ static Frag<bf16> frag16(const unsigned char* p, bool ok) {
+    u32x4 d = *reinterpret_cast<const u32x4*>(p);
+    if (!ok) d = u32x4{0u, 0u, 0u, 0u};
+    Frag<bf16> f;
+    f.v = __builtin_bit_cast(bf16x8, d);
+    return f;
+  }
+  __device__ __forceinline__ static Frag<bf16> frag_tr(const unsigned char* p0, const unsigned char* p1, bool ok) {
+    const s16x4 a = ds_read_tr(p0), b = ds_read_tr(p1);
+    Frag<bf16> f;
+    f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+    if (!ok) f = zero_frag<bf16>();
+    return f;
+  }
+  __device__ __forceinline__ Frag<bf16> q(const unsigned char* img, int qb, int s) const {
+    return frag16(img + oq[s] + 16 * qb * RBK, fq);
+  }
+  __device__ __forceinline__ Frag<bf16> k(const unsigned char* img, int t, int ks, int s) const {
+    return frag16(img + ok[t][s] + 32 * ks * RBK, fq);
+  }
+  __device__ __forceinline__ Frag<bf16> kt(const unsigned char* img, int s, int h, int ks) const {
+    return frag_tr(img + okt[0][s] + 32 * ks * RBK + 8 * h, img + okt[1][s] + 32 * ks * RBK + 8 * h, tv && fkt);
+  }
+  __device__ __forceinline__ Frag<bf16> vt(const unsigned char* img, int ks) const {
+    return frag_tr(img + ovt + 32 * ks * RBV, img + ovt + (32 * ks + 4) * RBV, tv);
+  }
+};
+
+template <int C, int DK, int DV>
+struct Reader<float, C, DK, DV> {
+  int lane, w;
+  __device__ __forceinline__ void init(int lane_, int w_) { lane = lane_; w = w_; }
+  __device__ __forceinline__ Frag<float> q(const unsigned char* img, int qb, int s) const {
+    return row_frag<float, DK>(img, 16 * qb + (lane & 15), s, lane);
+  }
+  __device__ __forceinline__ Frag<float> k(const unsigned char* img, int t, int ks, int s) const {
+    const int j = lane & 15;
+    return row_frag<float, DK>(img, min(32 * ks + 8 * (j >> 2) + 4 * t + (j & 3), C - 1), s, lane);
+  }
+  __device__ __forceinline__ Frag<float> kt(const unsigned char* img, int s, int h, int ks) const {
+    return col_frag<float, C, DK, false>(img, s, h, ks, lane);
+  }
+  __device__ __forceinline__ Frag<float> vt(const unsigned char* img, int ks) const {
+    return col_frag<float, C, DV, true>(img, w, 0, ks, lane);
+  }
+};
 
 // ----------------------------------------------------------------------------------------
 // per-wave building blocks
 // ----------------------------------------------------------------------------------------
 
-// Decayed chunk state for the wave's 16 value columns, as 16x16 tiles F[dk block]:
-//   F = sum_{s in chunk} exp(gtot - A_s) k_s v_s^T   (the decay is already applied to k~)
-template <typename T, int C, int DK>
-__device__ __forceinline__ void chunk_state(const unsigned char* kt, const Frag<T> (&vfr)[(C + 31) / 32],
-                                            int lane, f32x4 (&F)[DK / 16]) {
-  constexpr int NKS_C = (C + 31) / 32;
-  constexpr int NDKB = DK / 16;
+// Decayed chunk state for the wave's 16 value columns, as 2*ceil(DK/32) tiles with permuted
+// key-feature rows (tiles 2s, 2s+1 hold features 32s..32s+31):
+//   F = sum_{s in chunk} exp(g - A_s) k_s v_s^T   (weights applied to the value operand)
+template <typename T, int C, int DK, int DV>
+__device__ __forceinline__ void chunk_state(const Reader<T, C, DK, DV>& rd, const unsigned char* kimg,
+                                            const unsigned char* vimg, const float* wts, int lane,
+                                            f32x4 (&F)[2 * cdiv(DK, 32)]) {
+  constexpr int NKS_C = cdiv(C, 32), NKS_D = cdiv(DK, 32);
+  const int g = lane >> 4;
 #pragma unroll
-  for (int b = 0; b < NDKB; ++b) F[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < 2 * NKS_D; ++b) F[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < NKS_C; ++ks) {
+    const int p0 = min(32 * ks + 8 * g, C - 8);
+    const f32x4 w0 = *reinterpret_cast<const f32x4*>(wts + p0);
+    const f32x4 w1 = *reinterpret_cast<const f32x4*>(wts + p0 + 4);
+    const Frag<T> vf = frag_scale(rd.vt(vimg, ks), w0, w1);
 #pragma unroll
-    for (int b = 0; b < NDKB; ++b) mma(F[b], col_frag<T, C, DK>(kt, b, ks, lane), vfr[ks]);
+    for (int s = 0; s < NKS_D; ++s) {
+      mma(F[2 * s], rd.kt(kimg, s, 0, ks), vf);
+      mma(F[2 * s + 1], rd.kt(kimg, s, 1, ks), vf);
+    }
   }
 }
 
-// Read-out operand (rows = value columns, contraction = key features) of a state kept as
-// 16x16 accumulator tiles: tiles 2s and 2s+1 are exactly fragment s.
+// Read-out operand of a state kept as permuted tile pairs: tiles 2s, 2s+1 are fragment s.
 template <typename T, int DK>
-__device__ __forceinline__ Frag<T> node_frag(const f32x4 (&N)[DK / 16], int s) {
-  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  return frag_from<T>(N[2 * s], (2 * s + 1 < DK / 16) ? N[2 * s + 1] : z);
+__device__ __forceinline__ Frag<T> node_frag(const f32x4 (&N)[2 * cdiv(DK, 32)], int s) {
+  return frag_from<T>(N[2 * s], N[2 * s + 1]);
 }
 
 // One Fenwick node read out by every query of the chunk (level-weighted, decayed):
-//   O[qb] += lambda[i, lev] * exp(A_i) * edoff * (N^T q_i)
+//   O[qb] += lambda[i, lev] * e^{A_i} * edoff * (N^T q_i)
 // edoff = exp(log decay from the node's last position to the chunk's first position).
 template <typename T, int C, int DK>
-__device__ __forceinline__ void node_readout(const Frag<T> (&A)[(DK + 31) / 32], const unsigned char* qimg,
-                                             const float* lam, int L, const float* ea,
+__device__ __forceinline__ void node_readout(const Frag<T> (&A)[cdiv(DK, 32)],
+                                             const Frag<T> (&qf)[C / 16][cdiv(DK, 32)],
+                                             const float* lam, int LS, const float (&eaq)[C / 16],
                                              int lev, float edoff, int lane, f32x4 (&O)[C / 16]) {
-  constexpr int NQB = C / 16;
-  constexpr int NKS_D = (DK + 31) / 32;
+  constexpr int NQB = C / 16, NKS_D = cdiv(DK, 32);
   const int j = lane & 15;
   f32x4 Y[NQB];
 #pragma unroll
@@ -519,75 +536,68 @@ __device__ __forceinline__ void node_readout(const Frag<T> (&A)[(DK + 31) / 32],
 #pragma unroll
   for (int s = 0; s < NKS_D; ++s) {
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) mma(Y[qb], A[s], row_frag<T, DK>(qimg, qb, s, lane));
+    for (int qb = 0; qb < NQB; ++qb) mma(Y[qb], A[s], qf[qb][s]);
   }
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int qi = 16 * qb + j;
-    O[qb] += (lam[qi * L + lev] * ea[qi] * edoff) * Y[qb];
-  }
+  for (int qb = 0; qb < NQB; ++qb)
+    O[qb] += (lam[(16 * qb + j) * LS + lev] * eaq[qb] * edoff) * Y[qb];
 }
 
-// Masked score unit (query block qb, key step ks): the two 16x16 score tiles of keys
-// 32ks..32ks+31 against queries 16qb..16qb+15, masked by
-//   lambda[i, bit_length(i ^ s)] * exp(A_i - A_s) for s <= i (chunk-local i, s), else 0,
-// returned as the P^T operand fragment of the value product. exp(A_i - A_s) is taken as
-// e^{A_i} e^{-A_s} when the chunk's |A| < 40 (`fact`), else directly.
-template <typename T, int C, int DK>
-__device__ __forceinline__ Frag<T> score_unit(const unsigned char* qimg, const unsigned char* kimg,
-                                              const float* lam, int L, const float* aloc,
-                                              const float* ea, const float* eb, bool fact,
-                                              int qb, int ks, int lane) {
-  constexpr int NKS_D = (DK + 31) / 32;
+// Masked score unit (query block qb, key step ks) as the P^T operand fragment of the value
+// product: lane (j, g) element e = 4t + r holds key 32ks + 8g + e against query 16qb + j,
+//   lambda[i, bit_length(i ^ s)] * exp(A_i - A_s) * (q_i . k_s)  for s <= i, else 0
+// (chunk-local i, s). The two score tiles use permuted key rows (tile t, row i <-> key
+// 32ks + 8(i/4) + 4t + i%4). exp(A_i - A_s) is e^{A_i} e^{-A_s} when the chunk's |A| < 40
+// (`fact`), else taken directly. The key block 2ks + g/2 decides per lane: below the query
+// block one level for the row, equal per-element levels, above masked.
+template <typename T, int C, int DK, int DV>
+__device__ __forceinline__ Frag<T> score_unit(const Reader<T, C, DK, DV>& rd, const unsigned char* qimg,
+                                              const unsigned char* kimg, const float* lam, int LS,
+                                              const float* dec, bool fact, int qb, int ks, int lane) {
+  constexpr int NKS_D = cdiv(DK, 32);
   const int j = lane & 15, g = lane >> 4;
-  const int kb0 = 2 * ks, kb1 = 2 * ks + 1;
-  const bool has1 = kb1 <= qb;
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < NKS_D; ++s) {
-    const Frag<T> bq = row_frag<T, DK>(qimg, qb, s, lane);
-    mma(s0, row_frag<T, DK>(kimg, kb0, s, lane), bq);
-    if (has1) mma(s1, row_frag<T, DK>(kimg, kb1, s, lane), bq);
+    const Frag<T> qfr = rd.q(qimg, qb, s);
+    mma(s0, rd.k(kimg, 0, ks, s), qfr);
+    mma(s1, rd.k(kimg, 1, ks, s), qfr);
   }
   const int qi = 16 * qb + j;
-  const float* lrow = lam + qi * L;
-  const int key0 = 16 * kb0 + 4 * g;
+  const int kblk = 2 * ks + (g >> 1);
+  const int key0 = min(32 * ks + 8 * g, C - 8);      // keys key0 .. key0+7 (in range when used)
+  const float* lrow = lam + qi * LS;
   f32x4 d0, d1;
   if (fact) {
-    const float eq = ea[qi];
-    d0 = eq * *reinterpret_cast<const f32x4*>(eb + key0);
-    d1 = has1 ? eq * *reinterpret_cast<const f32x4*>(eb + key0 + 16) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const float eq = dec[C + qi];
+    d0 = eq * *reinterpret_cast<const f32x4*>(dec + 2 * C + key0);
+    d1 = eq * *reinterpret_cast<const f32x4*>(dec + 2 * C + key0 + 4);
   } else {
-    const float aq = aloc[qi];
+    const float aq = dec[qi];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      d0[r] = key0 + r <= qi ? __expf(aq - aloc[key0 + r]) : 0.f;
-      d1[r] = (has1 && key0 + 16 + r <= qi) ? __expf(aq - aloc[min(key0 + 16 + r, C - 1)]) : 0.f;
+      d0[r] = __expf(fminf(aq - dec[key0 + r], 0.f));
+      d1[r] = __expf(fminf(aq - dec[key0 + 4 + r], 0.f));
     }
   }
   f32x4 p0, p1;
-  if (kb0 < qb) {
-    // whole tile below the diagonal: one level for the row
-    const float lv = lrow[min(4 + bit_length((unsigned)(kb0 ^ qb)), L - 1)];
+  if (kblk < qb) {
+    const float lv = lrow[min(4 + bit_length((unsigned)(kblk ^ qb)), LS - 1)];
     p0 = (lv * s0) * d0;
-  } else {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = key0 + r;
-      p0[r] = key <= qi ? s0[r] * lrow[min(bit_length((unsigned)(qi ^ key)), L - 1)] * d0[r] : 0.f;
-    }
-  }
-  if (!has1) {
-    p1 = f32x4{0.f, 0.f, 0.f, 0.f};
-  } else if (kb1 < qb) {
-    const float lv = lrow[min(4 + bit_length((unsigned)(kb1 ^ qb)), L - 1)];
     p1 = (lv * s1) * d1;
-  } else {
+  } else if (kblk == qb) {
+    const int kl = 8 * (g & 1);                       // first key of the lane inside the 16-block
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int key = key0 + 16 + r;
-      p1[r] = key <= qi ? s1[r] * lrow[min(bit_length((unsigned)(qi ^ key)), L - 1)] * d1[r] : 0.f;
+      const int k0 = kl + r, k1 = kl + 4 + r;
+      const float l0 = lrow[min(bit_length((unsigned)(j ^ k0)), LS - 1)];
+      const float l1 = lrow[min(bit_length((unsigned)(j ^ k1)), LS - 1)];
+      p0[r] = k0 <= j ? s0[r] * l0 * d0[r] : 0.f;
+      p1[r] = k1 <= j ? s1[r] * l1 * d1[r] : 0.f;
     }
+  } else {
+    p0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    p1 = p0;
   }
   return frag_from<T>(p0, p1);
 }
@@ -602,143 +612,59 @@ template <> __device__ __forceinline__ void store_quad<float>(float* p, const f3
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
-constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+// Score units (qb, ks), ks <= qb/2: the ones holding a diagonal block (ks = qb/2, the most
+// work) first, one per wave, then the rest round-robin.
 constexpr int num_units(int nqb) { return nqb <= 0 ? 0 : num_units(nqb - 1) + (nqb - 1) / 2 + 1; }
-
-__device__ __forceinline__ void unit_decode(int un, int& qb, int& ks) {
-  qb = 0;
+__device__ __forceinline__ void unit_decode(int un, int nqb, int& qb, int& ks) {
+  if (un < nqb) { qb = un; ks = un / 2; return; }
+  un -= nqb;                                  // off-diagonal units: (qb, ks), ks < qb/2
+  qb = 2;
   ks = un;
-  while (ks >= qb / 2 + 1) { ks -= qb / 2 + 1; ++qb; }
+  while (ks >= qb / 2) { ks -= qb / 2; ++qb; }
 }
 
-// Stages one chunk: v as the position-contracted operand (P.V, states) and log_a -> (wave 0)
-// A, e^A, e^-A; WITH_Q: q, k as row-major images (scores, read-outs) and lambda rows; KT:
-// k~ = exp(g - A_s) k_s as position-contracted operand (chunk states).
-template <typename T, int C, int DK, int DV, int NT, bool WITH_Q, bool KT>
-struct ChunkStage {
-  BlockRegs<T, C, DK, NT> qr, kr;
-  BlockRegs<T, C, DV, NT> vr;
-  LamRegs<C, NT> lr;
-  DecayRegs<C> ar;
-
-  __device__ __forceinline__ void fetch(const T* qg, const T* kg, const T* vg, const float* lamg,
-                                        const float* lag, int L, int valid, int tid, int lane) {
-    if (WITH_Q) {
-      qr.fetch(qg, valid, tid);
-      lr.fetch(lamg, valid * L, tid);
-    }
-    kr.fetch(kg, valid, tid);
-    vr.fetch(vg, valid, tid);
-    ar.fetch(lag, valid, lane);
-  }
-
-  __device__ __forceinline__ void commit(const ChunkSmem& S, unsigned char* smem, int L, int tid,
-                                         int lane, int w) {
-    ar.scan(lane);
-    if (KT) {
-      const float g = ar.at(C - 1);
-      typedef BlockRegs<T, C, DK, NT> KR;
-      float ws[KR::ITERS][2];
-#pragma unroll
-      for (int it = 0; it < KR::ITERS; ++it) {
-        const int r0 = KR::row0(tid, it);
-        ws[it][0] = __expf(g - ar.at(r0));
-        ws[it][1] = __expf(g - ar.at(r0 + 1));
-      }
-      if constexpr (TrNative<T>::value)
-        kr.template commit_image<true, true>(smem + S.kt, tid, ws);
-      else
-        kr.template commit_frags<true>(reinterpret_cast<T*>(smem + S.kt), tid, ws);
-    }
-    if (WITH_Q) {
-      qr.template commit_image<false, false>(smem + S.qimg, tid, nullptr);
-      kr.template commit_image<false, false>(smem + S.kimg, tid, nullptr);
-      lr.commit(reinterpret_cast<float*>(smem + S.lam), C * L, tid);
-    }
-    if constexpr (TrNative<T>::value)
-      vr.template commit_image<true, false>(smem + S.vt, tid, nullptr);
-    else
-      vr.template commit_frags<false>(reinterpret_cast<T*>(smem + S.vt), tid, nullptr);
-    if (w == 0)
-      ar.publish(reinterpret_cast<float*>(smem + S.aloc), reinterpret_cast<float*>(smem + S.ea),
-                 reinterpret_cast<float*>(smem + S.eb), reinterpret_cast<int*>(smem + S.flag), lane);
-  }
-};
-
 // ----------------------------------------------------------------------------------------
-// kernels
+// node records between workgroups
 // ----------------------------------------------------------------------------------------
-
 // Node records pass between workgroups of one launch, possibly on different XCDs (each XCD has
-// its own L2). Two schemes, chosen at compile time:
-//   kScopedNodeIO = false: plain loads and stores of node data, an agent-scope release fence
-//                          (L2 write-back) before the flag store and an agent-scope acquire
-//                          fence (L2 invalidate) after the flag is seen;
-//   kScopedNodeIO = true : node data is written and read with device-scope (sc1) buffer
-//                          accesses, which are coherent across XCDs without touching the rest
-//                          of L2; the flag is stored once those writes have completed.
-#ifndef LLA_SCOPED_NODE_IO
-#define LLA_SCOPED_NODE_IO 1
-#endif
-constexpr bool kScopedNodeIO = LLA_SCOPED_NODE_IO != 0;
+// its own L2). A record is written once per launch, with device-scope (sc1) stores that write
+// through to memory; the wave then waits until its stores have completed and sets its flag
+// (device-scope atomic). Readers poll the flag with device-scope loads and then read the
+// record with ordinary, cacheable loads: no cache can hold an older copy, since nothing reads
+// a record before its flag is set and caches are invalidated between kernel launches, so
+// later readers of a node on the same XCD share its L2 lines.
 constexpr int kCpolDevice = 16;   // cache-policy immediate: sc1 (device scope)
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer descriptor over a wave-uniform base address (raw, unstrided).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t node_rsrc(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
 }
-// 16-byte multiples (an f32x4 tile quad, a bf16 or f32 operand fragment), contiguous at byte_off
-template <typename V>
-__device__ __forceinline__ V node_ld(const void* base, int byte_off) {
-  static_assert(sizeof(V) % 16 == 0, "16-byte node accesses");
-  if constexpr (kScopedNodeIO) {
-    u32x4 r[sizeof(V) / 16];
-#pragma unroll
-    for (int i = 0; i < (int)(sizeof(V) / 16); ++i)
-      r[i] = __builtin_amdgcn_raw_buffer_load_b128(node_rsrc(base), byte_off + 16 * i, 0, kCpolDevice);
-    return __builtin_bit_cast(V, r);
-  } else {
-    return *reinterpret_cast<const V*>(reinterpret_cast<const char*>(base) + byte_off);
-  }
-}
+// 16-byte multiples (a bf16 or f32 operand fragment), contiguous at byte_off
 template <typename V>
 __device__ __forceinline__ void node_st(void* base, int byte_off, const V& x) {
   static_assert(sizeof(V) % 16 == 0, "16-byte node accesses");
-  if constexpr (kScopedNodeIO) {
-    struct W { u32x4 r[sizeof(V) / 16]; };
-    const W wv = __builtin_bit_cast(W, x);
+  struct W { u32x4 r[sizeof(V) / 16]; };
+  const W wv = __builtin_bit_cast(W, x);
 #pragma unroll
-    for (int i = 0; i < (int)(sizeof(V) / 16); ++i)
-      __builtin_amdgcn_raw_buffer_store_b128(wv.r[i], node_rsrc(base), byte_off + 16 * i, 0, kCpolDevice);
-  } else {
-    *reinterpret_cast<V*>(reinterpret_cast<char*>(base) + byte_off) = x;
-  }
+  for (int i = 0; i < (int)(sizeof(V) / 16); ++i)
+    __builtin_amdgcn_raw_buffer_store_b128(wv.r[i], node_rsrc(base), byte_off + 16 * i, 0, kCpolDevice);
 }
+// node decays share cache lines between records: device-scope accesses only
 __device__ __forceinline__ float node_ld_f(const float* p) {
-  if constexpr (kScopedNodeIO) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else return *p;
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void node_st_f(float* p, float x) {
-  if constexpr (kScopedNodeIO) __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  else *p = x;
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// after a wave's node writes, before its flag store
+// after a wave's node writes, before its flag store: every access of the wave has completed
 __device__ __forceinline__ void node_publish_fence() {
-  if constexpr (kScopedNodeIO) {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);     // every outstanding access of this wave has completed
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  } else {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
-// after the flags a wave waits for were seen set, before its node reads
-__device__ __forceinline__ void node_acquire_fence() {
-  if constexpr (kScopedNodeIO) __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-}
+
+// ----------------------------------------------------------------------------------------
+// the kernel
+// ----------------------------------------------------------------------------------------
 
 constexpr int kFlagBase = 64;   // ints ahead of the node flags (the ticket counter, alone in its line)
 
@@ -748,12 +674,11 @@ struct Params {
   void* out;
   int BH, T, L;
   int nchunks;      // ceil(T / C)
-  int sweep;        // R: consecutive chunks per workgroup (power of two, <= kSweepCap)
+  int sweep;        // R: chunks per workgroup (the kernel's NB)
   int m;            // log2(R)
   int nsweep;       // ceil(nchunks / R)
   int* sync;        // [0]: workgroup ticket counter; [kFlagBase + (bh*ns + e)*NW + w]: node flags
   float* gnode;     // [BH][ns][NW]: log decay across node e (one copy per wave)
-  float* node32;    // [BH][ns][NW][DK/16][64] f32x4: node e as float32 accumulator tiles
   void* nodeT;      // [BH][ns][NW][ceil(DK/32)][64] Frag<T>: node e as read-out operands
   int spin_limit;   // polls of a node flag before the wait is abandoned
 };
@@ -763,7 +688,7 @@ __device__ __forceinline__ size_t node_slot(int bh, int ns, int e, int nw, int w
   return ((size_t)bh * ns + e) * nw + w;
 }
 
-// The forward pass. One workgroup per sweep of R chunks of one head, one wave per 16 value
+// The forward pass: one workgroup per sweep of NB chunks of one head, one wave per 16 value
 // columns; ns = nsweep - 1 sweeps per head publish a node (the last one has no reader).
 //
 // Node of sweep e: the Fenwick node over sweeps that ends at e, i.e. the lowbit(e+1) sweeps
@@ -773,35 +698,28 @@ __device__ __forceinline__ size_t node_slot(int bh, int ns, int e, int nw, int w
 // node(e - 2^i) to the end of e. Sweep sw reads the nodes ending at ((sw >> j) << j) - 1 for
 // each set bit j of sw (level J + 1 + m + j); the first ctz(sw+1) of them are exactly the
 // children of its own node.
-//
-// Global loads are issued branch-free where possible, so that waits count exactly: the
-// inputs of the next chunk are loaded into registers right after the current chunk is staged
-// in shared memory, and the first chunk of phase B while the last chunk of phase A is
-// computed.
-template <typename T, int C, int DK, int DV>
-__global__ __launch_bounds__(4 * DV, 2) void lla_fused_kernel(Params p) {
+template <typename T, int C, int DK, int DV, int NB>
+__global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int ES = (int)sizeof(T);
   constexpr int NT = 4 * DV, NW = DV / 16;
-  constexpr int NQB = C / 16, NKS_C = (C + 31) / 32, NKS_D = (DK + 31) / 32, NDKB = DK / 16;
+  constexpr int NQB = C / 16, NKS_C = cdiv(C, 32), NKS_D = cdiv(DK, 32), NTF = 2 * NKS_D;
   constexpr int J = ilog2(C);
-  constexpr int LMAX = ilog2(kSweepCap);
-  constexpr int NSLOT = kSweepCap - 1;
   constexpr int NUNITS = num_units(NQB);
   constexpr int XREG = DK >= 128 ? 2 : 5;   // nodes over earlier sweeps held in registers
-  static_assert(kSweepCap <= 4, "slot u of a sweep is the running total or chunk u alone only for R <= 4");
+  static_assert(NB >= 1 && NB <= kMaxSweep, "one or two resident chunks");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index: uniform
   const int j = lane & 15, g = lane >> 4;
   const int L = p.L, ns = p.nsweep - 1;
-  const ChunkSmem SA = chunk_smem<T>(C, DK, DV, L, false, true);
-  const ChunkSmem SB = chunk_smem<T>(C, DK, DV, L, true, false);
+  const Smem S = smem_layout(ES, C, DK, DV, NB);
 
   // ticket -> (head, sweep), sweep-major
   int t = blockIdx.x;
   if (ns > 0) {
-    int* tk = reinterpret_cast<int*>(smem + fused_ticket_offset<T>(C, DK, DV, L));
+    int* tk = reinterpret_cast<int*>(smem + S.ticket);
     if (tid == 0) *tk = __hip_atomic_fetch_add(p.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     t = __builtin_amdgcn_readfirstlane(*tk);
@@ -816,127 +734,211 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fused_kernel(Params p) {
   const float* lamg = p.lam + hoff * L;
   T* og = reinterpret_cast<T*>(p.out) + hoff * DV;
 
-  const int c0 = sw * p.sweep;
-  const int nch = min(p.sweep, p.nchunks - c0);
+  const int c0 = sw * NB;
+  const int nch = min(NB, p.nchunks - c0);
   const int next = __builtin_popcount((unsigned)sw);
 
-  auto node_index = [&](int x) {      // sweep index the x-th node of sw ends at (0 if none)
+  Reader<T, C, DK, DV> rd;
+  rd.init(lane, w);
+
+  // ---------------- load the sweep: every input read is issued here ----------------
+  // Registers first (log_a, lambda), then the k and v images (phase A), then the q images
+  // (phase B): global_load_lds completes in issue order, so waiting until no more than the
+  // q copies are outstanding means k and v have landed.
+  LamRegs<C, NT> lr[NB];
+  DecayRegs<C> ar[NB];
+  int t0s[NB], valids[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const int uc = u < nch ? u : 0;                 // a missing last chunk re-reads chunk 0
+    t0s[u] = (c0 + uc) * C;
+    valids[u] = min(C, p.T - t0s[u]);
+    ar[u].fetch(lag + t0s[u], valids[u], lane);
+    lr[u].fetch(lamg + (size_t)t0s[u] * L, valids[u] * L, tid);
+  }
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    dma_image<T, C, DK, NW, false>(smem + S.k[u], kg + (size_t)t0s[u] * DK, valids[u], w, lane);
+    dma_image<T, C, DV, NW, true>(smem + S.v[u], vg + (size_t)t0s[u] * DV, valids[u], w, lane);
+  }
+#pragma unroll
+  for (int u = 0; u < NB; ++u)
+    dma_image<T, C, DK, NW, false>(smem + S.q[u], qg + (size_t)t0s[u] * DK, valids[u], w, lane);
+  wait_vm<NB * dma_count<T, C, DK, NW>(NW - 1)>();   // this wave's k, v (and registers) landed
+  float gch[NB];                        // total log decay of each chunk
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    ar[u].scan(lane);
+    gch[u] = ar[u].total();
+    lr[u].commit(reinterpret_cast<float*>(smem + S.lam[u]), C * L, tid);
+    if (w == 0)
+      ar[u].publish(reinterpret_cast<float*>(smem + S.dec[u]), reinterpret_cast<int*>(smem + S.flag[u]),
+                    gch[u], lane);
+  }
+  lds_barrier();
+
+  // ---------------- phase A: chunk states, chunk 0's state, the sweep total ----------------
+  Frag<T> SL[NKS_D];              // state of chunk 0 (decayed to its end), level J+1 for chunk 1
+  f32x4 H[NTF];
+#pragma unroll
+  for (int b = 0; b < NTF; ++b) H[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float G = 0.f;
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    if (u < nch) {
+      f32x4 F[NTF];
+      chunk_state<T, C, DK, DV>(rd, smem + S.k[u], smem + S.v[u],
+                                reinterpret_cast<const float*>(smem + S.dec[u]) + 3 * C, lane, F);
+      const float d = __expf(gch[u]);
+#pragma unroll
+      for (int b = 0; b < NTF; ++b) H[b] = d * H[b] + F[b];
+      G += gch[u];
+      if (u == 0 && NB > 1) {
+#pragma unroll
+        for (int s = 0; s < NKS_D; ++s) SL[s] = node_frag<T, DK>(F, s);
+      }
+    }
+  }
+
+  // ---------------- Fenwick nodes over earlier sweeps ----------------
+  // The x-th node of sw (x-th set bit j of sw, lowest first) ends at sweep ((sw >> j) << j) - 1
+  // and has level J + 1 + m + j; the first XREG of them are tabulated once.
+  auto node_index_slow = [&](int x) {
     unsigned m = (unsigned)sw;
     for (int i = 0; i < x && m; ++i) m &= m - 1;
     return m ? ((sw >> __builtin_ctz(m)) << __builtin_ctz(m)) - 1 : 0;
   };
-  auto node_level = [&](int x) {
+  auto node_level_slow = [&](int x) {
     unsigned m = (unsigned)sw;
     for (int i = 0; i < x && m; ++i) m &= m - 1;
     return m ? J + 1 + p.m + __builtin_ctz(m) : 0;
   };
-  const Frag<T>* ndT = reinterpret_cast<const Frag<T>*>(p.nodeT);
-  auto load_node = [&](Frag<T> (&A)[NKS_D], int e) {
-    const Frag<T>* base = ndT + node_slot(bh, ns, e, NW, w) * NKS_D * 64;
+  int NE[XREG], NLV[XREG];
+  {
+    unsigned m = (unsigned)sw;
 #pragma unroll
-    for (int s = 0; s < NKS_D; ++s) A[s] = node_ld<Frag<T>>(base, (s * 64 + lane) * (int)sizeof(Frag<T>));
-  };
-
-  ChunkStage<T, C, DK, DV, NT, false, true> sa;
-  ChunkStage<T, C, DK, DV, NT, true, false> sb;
-  auto fetch_a = [&](int u) {
-    const int t0 = (c0 + u) * C;
-    const int valid = min(C, p.T - t0);
-    sa.fetch(nullptr, kg + (size_t)t0 * DK, vg + (size_t)t0 * DV, nullptr, lag + t0, 0, valid, tid, lane);
-  };
-  auto fetch_b = [&](int u) {
-    const int t0 = (c0 + u) * C;
-    const int valid = min(C, p.T - t0);
-    sb.fetch(qg + (size_t)t0 * DK, kg + (size_t)t0 * DK, vg + (size_t)t0 * DV, lamg + (size_t)t0 * L,
-             lag + t0, L, valid, tid, lane);
-  };
-
-  // ---------------- phase A: chunk states -> slots inside the sweep, sweep total ----------------
-  // Slot s (s < R-1) is the Fenwick node over the chunks of the sweep that ends at chunk s; for
-  // R <= 4 it is the running total when s+1 is a power of two and chunk s's own state otherwise.
-  Frag<T> SL[NSLOT][NKS_D];
-#pragma unroll
-  for (int s = 0; s < NSLOT; ++s)
-#pragma unroll
-    for (int s2 = 0; s2 < NKS_D; ++s2) SL[s][s2] = zero_frag<T>();
-  f32x4 H[NDKB];
-#pragma unroll
-  for (int b = 0; b < NDKB; ++b) H[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float G = 0.f;
-  auto body_a = [&](int u) {
-    const float gtot = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
-        __builtin_bit_cast(int, reinterpret_cast<const float*>(smem + SA.aloc)[C - 1])));
-    Frag<T> vfr[NKS_C];
-#pragma unroll
-    for (int ks = 0; ks < NKS_C; ++ks) vfr[ks] = col_frag<T, C, DV>(smem + SA.vt, w, ks, lane);
-    f32x4 F[NDKB];
-    chunk_state<T, C, DK>(smem + SA.kt, vfr, lane, F);
-    const float d = __expf(gtot);
-#pragma unroll
-    for (int b = 0; b < NDKB; ++b) H[b] = d * H[b] + F[b];
-    G += gtot;
-    // value selects, not conditional stores: the slots must stay in registers
-#pragma unroll
-    for (int s = 0; s < NSLOT; ++s) {
-      const bool hit = u == s;
-      const bool whole = ((s + 1) & s) == 0;
-#pragma unroll
-      for (int s2 = 0; s2 < NKS_D; ++s2)
-        SL[s][s2] = frag_select<T>(hit, whole ? node_frag<T, DK>(H, s2) : node_frag<T, DK>(F, s2), SL[s][s2]);
+    for (int x = 0; x < XREG; ++x) {
+      const int tz = m ? __builtin_ctz(m) : 0;
+      NE[x] = m ? ((sw >> tz) << tz) - 1 : 0;
+      NLV[x] = J + 1 + p.m + tz;
+      m &= m - 1;
     }
-  };
-  fetch_a(0);
-  for (int u = 0; u + 1 < nch; ++u) {
-    if (u) __syncthreads();
-    sa.commit(SA, smem, L, tid, lane, w);
-    __syncthreads();
-    fetch_a(u + 1);
-    body_a(u);
   }
-  if (nch > 1) __syncthreads();
-  sa.commit(SA, smem, L, tid, lane, w);
-  __syncthreads();
-  fetch_b(0);
-  body_a(nch - 1);
-
-  // ---------------- nodes of earlier sweeps: wait, absorb children, publish ----------------
+  auto node_index = [&](int x) { return x < XREG ? NE[x] : node_index_slow(x); };
+  auto node_level = [&](int x) { return x < XREG ? NLV[x] : node_level_slow(x); };
+  const Frag<T>* ndT = reinterpret_cast<const Frag<T>*>(p.nodeT);
+  auto node_base = [&](int e) { return ndT + node_slot(bh, ns, e, NW, w) * NKS_D * 64; };
+  auto flag_set = [&](int e) {
+    const int* f = p.sync + kFlagBase + node_slot(bh, ns, e, NW, w);
+    return __builtin_amdgcn_readfirstlane(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0;
+  };
   bool bad = false;
-  for (int x = 0; x < next; ++x) {
-    const int* f = p.sync + kFlagBase + node_slot(bh, ns, node_index(x), NW, w);
+  auto wait_node = [&](int e) {
     int n = 0;
-    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0) {
+    while (!flag_set(e)) {
       if (++n > p.spin_limit) { bad = true; break; }
       __builtin_amdgcn_s_sleep(2);
     }
-  }
-  if (next > 0) node_acquire_fence();
+  };
 
-  if (sw < ns) {
-    const int kc = __builtin_ctz((unsigned)(sw + 1));   // children: nodes x < kc of sw
-    const f32x4* n32 = reinterpret_cast<const f32x4*>(p.node32);
+  // Own node: the sweep total plus its children (the first kc nodes of sw), published right
+  // away when the children are already there, else after the intra-chunk work.
+  const int kc = sw < ns ? __builtin_ctz((unsigned)(sw + 1)) : 0;
+  bool published = sw >= ns;
+  auto publish = [&]() {
     float gacc = G;
     for (int x = 0; x < kc; ++x) {
-      const size_t e = node_slot(bh, ns, node_index(x), NW, w);
+      const int e = node_index(x);
+      const Frag<T>* nb = node_base(e);
       const float d = __expf(gacc);
 #pragma unroll
-      for (int b = 0; b < NDKB; ++b) H[b] += d * node_ld<f32x4>(n32 + e * NDKB * 64, (b * 64 + lane) * 16);
-      gacc += node_ld_f(p.gnode + e);
+      for (int s = 0; s < NKS_D; ++s) {
+        f32x4 lo, hi;
+        frag_to_f32(nb[s * 64 + lane], lo, hi);
+        H[2 * s] += d * lo;
+        H[2 * s + 1] += d * hi;
+      }
+      gacc += node_ld_f(p.gnode + node_slot(bh, ns, e, NW, w));
     }
     if (bad) {
 #pragma unroll
-      for (int b = 0; b < NDKB; ++b) H[b] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      for (int b = 0; b < NTF; ++b) H[b] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
     }
     const size_t me = node_slot(bh, ns, sw, NW, w);
-    f32x4* o32 = reinterpret_cast<f32x4*>(p.node32) + me * NDKB * 64;
-#pragma unroll
-    for (int b = 0; b < NDKB; ++b) node_st<f32x4>(o32, (b * 64 + lane) * 16, H[b]);
     Frag<T>* oT = reinterpret_cast<Frag<T>*>(p.nodeT) + me * NKS_D * 64;
 #pragma unroll
-    for (int s = 0; s < NKS_D; ++s) node_st<Frag<T>>(oT, (s * 64 + lane) * (int)sizeof(Frag<T>), node_frag<T, DK>(H, s));
+    for (int s = 0; s < NKS_D; ++s)
+      node_st<Frag<T>>(oT, (s * 64 + lane) * (int)sizeof(Frag<T>), node_frag<T, DK>(H, s));
     if (lane == 0) node_st_f(p.gnode + me, gacc);
     node_publish_fence();
     if (lane == 0) __hip_atomic_store(p.sync + kFlagBase + me, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  if (!published) {
+    bool ready = true;
+    for (int x = 0; x < kc; ++x) ready = ready && flag_set(node_index(x));
+    if (ready) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      publish();
+      published = true;
+    }
   }
+
+  wait_vm<0>();                         // this wave's q images landed
+  lds_barrier();
+
+  // ---------------- phase B, intra-sweep part: scores, P.V, the node inside the sweep ----------------
+  f32x4 O[NB][NQB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    if (u < nch) {
+      const unsigned char* qimg = smem + S.q[u];
+      const unsigned char* kimg = smem + S.k[u];
+      const float* lam = reinterpret_cast<const float*>(smem + S.lam[u]);
+      const float* dec = reinterpret_cast<const float*>(smem + S.dec[u]);
+      Frag<T>* pf = reinterpret_cast<Frag<T>*>(smem + S.pf[u]);
+      const bool fact = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(smem + S.flag[u])) != 0;
+
+      // masked scores -> P^T fragments (shared by all waves)
+      for (int un = w; un < NUNITS; un += NW) {
+        int qb, ks;
+        unit_decode(un, NQB, qb, ks);
+        pf[(qb * NKS_C + ks) * 64 + lane] = score_unit<T, C, DK, DV>(rd, qimg, kimg, lam, L, dec, fact, qb, ks, lane);
+      }
+      __syncthreads();
+
+      Frag<T> vfr[NKS_C];
+#pragma unroll
+      for (int ks = 0; ks < NKS_C; ++ks) vfr[ks] = rd.vt(smem + S.v[u], ks);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        O[u][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks <= qb / 2; ++ks) mma(O[u][qb], vfr[ks], pf[(qb * NKS_C + ks) * 64 + lane]);
+      }
+
+      // chunk 0 of the sweep, read by chunk 1 (level J+1; adjacent, so no decay in between)
+      if (NB > 1 && u == 1) {
+        Frag<T> qf[NQB][NKS_D];
+        float eaq[NQB];
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          eaq[qb] = dec[C + 16 * qb + j];
+#pragma unroll
+          for (int s = 0; s < NKS_D; ++s) qf[qb][s] = rd.q(qimg, qb, s);
+        }
+        node_readout<T, C, DK>(SL, qf, lam, L, eaq, J + 1, 1.f, lane, O[u]);
+      }
+    }
+  }
+
+  // ---------------- own node (if the children were late), nodes of earlier sweeps ----------------
+  if (!published) {
+    for (int x = 0; x < kc; ++x) wait_node(node_index(x));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    publish();
+  }
+  for (int x = kc; x < next; ++x) wait_node(node_index(x));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
   Frag<T> X[XREG][NKS_D];
   float XD[XREG];            // log decay across each node
@@ -944,97 +946,60 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fused_kernel(Params p) {
 #pragma unroll
     for (int x = 0; x < XREG; ++x) {
       const int e = node_index(x);
-      load_node(X[x], e);
+      const Frag<T>* nb = node_base(e);
+#pragma unroll
+      for (int s = 0; s < NKS_D; ++s) X[x][s] = nb[s * 64 + lane];
       XD[x] = node_ld_f(p.gnode + node_slot(bh, ns, e, NW, w));
     }
   }
 
-  // ---------------- phase B: outputs, chunk by chunk ----------------
-  const unsigned char* qimg = smem + SB.qimg;
-  const unsigned char* kimg = smem + SB.kimg;
-  T* pf = reinterpret_cast<T*>(smem + SB.pf);
-  const float* lam = reinterpret_cast<const float*>(smem + SB.lam);
-  const float* aloc = reinterpret_cast<const float*>(smem + SB.aloc);
-  const float* ea = reinterpret_cast<const float*>(smem + SB.ea);
-  const float* eb = reinterpret_cast<const float*>(smem + SB.eb);
-  const int* flag = reinterpret_cast<const int*>(smem + SB.flag);
-
-  float SD[NSLOT];           // log decay from the end of slot s to the current chunk start
-#pragma unroll
-  for (int s = 0; s < NSLOT; ++s) SD[s] = 0.f;
+  // ---------------- phase B, read-out of earlier sweeps and store ----------------
   float gam = 0.f;           // log decay from the sweep's first position to the current chunk start
-
-  for (int u = 0; u < nch; ++u) {
-    const int t0 = (c0 + u) * C;
-    const int valid = min(C, p.T - t0);
-    __syncthreads();
-    sb.commit(SB, smem, L, tid, lane, w);
-    __syncthreads();
-    fetch_b(u + 1 < nch ? u + 1 : u);     // unconditional: re-reads this chunk after the last
-    const float gtot = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, aloc[C - 1])));
-    const bool fact = __builtin_amdgcn_readfirstlane(*flag) != 0;
-
-    // masked scores -> P^T fragments
-    for (int un = w; un < NUNITS; un += NW) {
-      int qb, ks;
-      unit_decode(un, qb, ks);
-      const Frag<T> f = score_unit<T, C, DK>(qimg, kimg, lam, L, aloc, ea, eb, fact, qb, ks, lane);
-      reinterpret_cast<Frag<T>*>(pf)[(qb * NKS_C + ks) * 64 + lane] = f;
-    }
-    __syncthreads();
-
-    // intra-chunk values
-    Frag<T> vfr[NKS_C];
 #pragma unroll
-    for (int ks = 0; ks < NKS_C; ++ks) vfr[ks] = col_frag<T, C, DV>(smem + SB.vt, w, ks, lane);
-    f32x4 O[NQB];
+  for (int u = 0; u < NB; ++u) {
+    if (u < nch) {
+      const int t0 = (c0 + u) * C;
+      const int valid = min(C, p.T - t0);
+      const unsigned char* qimg = smem + S.q[u];
+      const float* lam = reinterpret_cast<const float*>(smem + S.lam[u]);
+      const float* dec = reinterpret_cast<const float*>(smem + S.dec[u]);
+      if (next > 0) {
+        Frag<T> qf[NQB][NKS_D];
+        float eaq[NQB];
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      O[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qb = 0; qb < NQB; ++qb) {
+          eaq[qb] = dec[C + 16 * qb + j];
 #pragma unroll
-      for (int ks = 0; ks <= qb / 2; ++ks) mma(O[qb], vfr[ks], lds_frag<T>(pf, qb * NKS_C + ks, lane));
-    }
-
-    // Fenwick nodes inside the sweep (levels J+1 .. J+m): chunk u reads slot ((u>>a)<<a) - 1
-    // for each set bit a of u
+          for (int s = 0; s < NKS_D; ++s) qf[qb][s] = rd.q(qimg, qb, s);
+        }
+        // Fenwick nodes made of whole earlier sweeps (levels J+m+1 ..), lowest bit first
+        float dext = 0.f;
 #pragma unroll
-    for (int s = 0; s < NSLOT; ++s) {
+        for (int x = 0; x < XREG; ++x) {
+          if (x < next) {
+            node_readout<T, C, DK>(X[x], qf, lam, L, eaq, node_level(x), __expf(gam + dext), lane, O[u]);
+            dext += XD[x];
+          }
+        }
+        for (int x = XREG; x < next; ++x) {    // beyond the register budget: load on demand
+          const int e = node_index(x);
+          const Frag<T>* nb = node_base(e);
+          Frag<T> A[NKS_D];
 #pragma unroll
-      for (int a = 0; a < LMAX; ++a) {
-        if (((u >> a) & 1) && ((u >> a) << a) - 1 == s)
-          node_readout<T, C, DK>(SL[s], qimg, lam, L, ea, J + 1 + a, __expf(SD[s]), lane, O);
-      }
-    }
-
-    // Fenwick nodes made of whole earlier sweeps (levels J+m+1 ..), lowest bit first
-    {
-      float dext = 0.f;
-#pragma unroll
-      for (int x = 0; x < XREG; ++x) {
-        if (x < next) {
-          node_readout<T, C, DK>(X[x], qimg, lam, L, ea, node_level(x), __expf(gam + dext), lane, O);
-          dext += XD[x];
+          for (int s = 0; s < NKS_D; ++s) A[s] = nb[s * 64 + lane];
+          node_readout<T, C, DK>(A, qf, lam, L, eaq, node_level(x), __expf(gam + dext), lane, O[u]);
+          dext += node_ld_f(p.gnode + node_slot(bh, ns, e, NW, w));
         }
       }
-      for (int x = XREG; x < next; ++x) {    // beyond the register budget: load on demand
-        Frag<T> A[NKS_D];
-        const int e = node_index(x);
-        load_node(A, e);
-        node_readout<T, C, DK>(A, qimg, lam, L, ea, node_level(x), __expf(gam + dext), lane, O);
-        dext += node_ld_f(p.gnode + node_slot(bh, ns, e, NW, w));
+      // store rows [0, valid); NaN if a node never arrived
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int qi = 16 * qb + j;
+        if (bad) O[u][qb] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        if (qi < valid) store_quad<T>(og + (size_t)(t0 + qi) * DV + 16 * w + 4 * g, O[u][qb]);
       }
+      gam += gch[u];
     }
-    // store rows [0, valid); NaN if a node never arrived
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const int qi = 16 * qb + j;
-      if (bad) O[qb] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-      if (qi < valid) store_quad<T>(og + (size_t)(t0 + qi) * DV + 16 * w + 4 * g, O[qb]);
-    }
-#pragma unroll
-    for (int s = 0; s < NSLOT; ++s)
-      if (s < u) SD[s] += gtot;
-    gam += gtot;
   }
 }
 

@@ -50,23 +50,31 @@ def test_status_strings(L):
 def test_defaults(L):
     assert L.loglinear_attn_default_chunk(16, 16, 256, 1) == 16
     assert L.loglinear_attn_default_chunk(64, 64, 8192, 0) == 64
-    # headline shape: 64 heads x 128 chunks -> sweeps of 4 chunks (2048 workgroups)
-    assert L.loglinear_attn_default_sweep(4, 16, 8192, 64, 64, 64, 0) == 4
-    assert L.loglinear_attn_default_sweep(1, 1, 64, 64, 64, 64, 0) == 1
-    assert L.loglinear_attn_default_sweep(64, 64, 65536, 128, 128, 64, 0) == 4   # capped for dk=128
-    assert L.loglinear_attn_default_sweep(64, 64, 65536, 64, 64, 64, 0) == 4
+    # headline shape: 64 heads x 128 chunks -> two resident chunks per workgroup
+    assert L.loglinear_attn_default_sweep(4, 16, 8192, 64, 64, 64, 0) == 2
+    assert L.loglinear_attn_default_sweep(1, 1, 64, 64, 64, 64, 0) == 1        # one chunk
+    assert L.loglinear_attn_default_sweep(1, 2, 2048, 64, 64, 64, 0) == 1      # too few workgroups
+    assert L.loglinear_attn_default_sweep(64, 64, 65536, 128, 128, 64, 0) == 2
+    assert L.loglinear_attn_default_sweep(64, 64, 65536, 128, 64, 64, 0) == 1  # shared memory
+    assert L.loglinear_attn_default_sweep(64, 64, 65536, 64, 64, 64, 1) == 1   # float32
 
 
 def test_workspace_bytes(L):
     ws = L.loglinear_attn_workspace_bytes
-    assert ws(1, 2, 256, 16, 16, 16, 16, 1) == 0           # one sweep covers T
+    assert ws(1, 2, 32, 16, 16, 16, 2, 1) == 0              # one sweep covers T
     assert ws(1, 1, 64, 64, 64, 64, 1, 0) == 0              # one chunk
-    n = ws(4, 16, 8192, 64, 64, 64, 4, 0)
-    ns = 8192 // 64 // 4 - 1
+    assert ws(1, 2, 256, 16, 16, 16, 16, 1) == 0            # unsupported sweep -> 0
+    n = ws(4, 16, 8192, 64, 64, 64, 2, 0)
+    ns = 8192 // 64 // 2 - 1
     per = 64 * ns                   # (head, node) pairs; each node is kept per wave (dv/16 = 4)
-    expect = per * 64 * 64 * 4 + per * 4 * 2 * 512 * 2 + 2 * per * 4 * 4 + 64 * 4
-    assert expect <= n <= expect + 4 * 256
-    assert ws(4, 16, 8192, 48, 64, 64, 4, 0) == 0           # invalid -> 0
+    expect = per * 4 * 2 * 512 * 2 + 2 * per * 4 * 4 + 64 * 4   # bf16 fragments, decays, flags
+    assert expect <= n <= expect + 3 * 256
+    # dk = 16: a record still holds one full fragment per wave (features 16..31 zero)
+    n16 = ws(1, 1, 4096, 16, 16, 64, 1, 0)
+    per16 = 4096 // 64 - 1
+    expect16 = per16 * 64 * 16 + 2 * per16 * 4 + 64 * 4
+    assert expect16 <= n16 <= expect16 + 3 * 256
+    assert ws(4, 16, 8192, 48, 64, 64, 2, 0) == 0           # invalid -> 0
     assert ws(1, 1, 1000, 64, 64, 64, 2, 0) > 0             # ragged T
 
 
@@ -95,6 +103,7 @@ def _call(L, a):
     (dict(dv=256), _lib.LLA_ERR_UNSUPPORTED),
     (dict(chunk=24), _lib.LLA_ERR_UNSUPPORTED),
     (dict(sweep=3), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(sweep=4), _lib.LLA_ERR_UNSUPPORTED),
     (dict(sweep=16), _lib.LLA_ERR_UNSUPPORTED),
     (dict(sweep=8), _lib.LLA_ERR_UNSUPPORTED),
     (dict(B=70000), _lib.LLA_ERR_UNSUPPORTED),
