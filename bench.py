@@ -93,7 +93,7 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--chunk", type=int, default=0, help="0: the workload's stated chunk size")
     ap.add_argument("--sweep", type=int, default=0, help="0: library default")
-    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-heads", type=int, default=12)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-only", action="store_true",
                     help="skip the cold-cache, copy-bandwidth and CPU legs (profiler runs)")
@@ -208,7 +208,7 @@ def main(argv=None) -> int:
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
-            "kernel": "lla_fused_kernel",
+            "kernel": "lla_fwd_kernel",
             "kernel_ms": stage["forward"],
             "algorithmic_bytes_per_launch": byte_ht * ht,
         },
