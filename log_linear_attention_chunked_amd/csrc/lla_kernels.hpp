@@ -46,6 +46,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace lla {
 
 typedef __bf16 bf16;
@@ -61,6 +63,17 @@ constexpr int kLamCap = 24;       // lambda levels held per position (T <= 2^23)
 constexpr int kMaxSweep = 2;      // chunks resident per workgroup
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
+// compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
 constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 // ----------------------------------------------------------------------------------------
@@ -741,65 +754,6 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   Reader<T, C, DK, DV> rd;
   rd.init(lane, w);
 
-  // ---------------- load the sweep: every input read is issued here ----------------
-  // Registers first (log_a, lambda), then the k and v images (phase A), then the q images
-  // (phase B): global_load_lds completes in issue order, so waiting until no more than the
-  // q copies are outstanding means k and v have landed.
-  LamRegs<C, NT> lr[NB];
-  DecayRegs<C> ar[NB];
-  int t0s[NB], valids[NB];
-#pragma unroll
-  for (int u = 0; u < NB; ++u) {
-    const int uc = u < nch ? u : 0;                 // a missing last chunk re-reads chunk 0
-    t0s[u] = (c0 + uc) * C;
-    valids[u] = min(C, p.T - t0s[u]);
-    ar[u].fetch(lag + t0s[u], valids[u], lane);
-    lr[u].fetch(lamg + (size_t)t0s[u] * L, valids[u] * L, tid);
-  }
-#pragma unroll
-  for (int u = 0; u < NB; ++u) {
-    dma_image<T, C, DK, NW, false>(smem + S.k[u], kg + (size_t)t0s[u] * DK, valids[u], w, lane);
-    dma_image<T, C, DV, NW, true>(smem + S.v[u], vg + (size_t)t0s[u] * DV, valids[u], w, lane);
-  }
-#pragma unroll
-  for (int u = 0; u < NB; ++u)
-    dma_image<T, C, DK, NW, false>(smem + S.q[u], qg + (size_t)t0s[u] * DK, valids[u], w, lane);
-  wait_vm<NB * dma_count<T, C, DK, NW>(NW - 1)>();   // this wave's k, v (and registers) landed
-  float gch[NB];                        // total log decay of each chunk
-#pragma unroll
-  for (int u = 0; u < NB; ++u) {
-    ar[u].scan(lane);
-    gch[u] = ar[u].total();
-    lr[u].commit(reinterpret_cast<float*>(smem + S.lam[u]), C * L, tid);
-    if (w == 0)
-      ar[u].publish(reinterpret_cast<float*>(smem + S.dec[u]), reinterpret_cast<int*>(smem + S.flag[u]),
-                    gch[u], lane);
-  }
-  lds_barrier();
-
-  // ---------------- phase A: chunk states, chunk 0's state, the sweep total ----------------
-  Frag<T> SL[NKS_D];              // state of chunk 0 (decayed to its end), level J+1 for chunk 1
-  f32x4 H[NTF];
-#pragma unroll
-  for (int b = 0; b < NTF; ++b) H[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float G = 0.f;
-#pragma unroll
-  for (int u = 0; u < NB; ++u) {
-    if (u < nch) {
-      f32x4 F[NTF];
-      chunk_state<T, C, DK, DV>(rd, smem + S.k[u], smem + S.v[u],
-                                reinterpret_cast<const float*>(smem + S.dec[u]) + 3 * C, lane, F);
-      const float d = __expf(gch[u]);
-#pragma unroll
-      for (int b = 0; b < NTF; ++b) H[b] = d * H[b] + F[b];
-      G += gch[u];
-      if (u == 0 && NB > 1) {
-#pragma unroll
-        for (int s = 0; s < NKS_D; ++s) SL[s] = node_frag<T, DK>(F, s);
-      }
-    }
-  }
-
   // ---------------- Fenwick nodes over earlier sweeps ----------------
   // The x-th node of sw (x-th set bit j of sw, lowest first) ends at sweep ((sw >> j) << j) - 1
   // and has level J + 1 + m + j; the first XREG of them are tabulated once.
@@ -832,23 +786,127 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
     const int* f = p.sync + kFlagBase + node_slot(bh, ns, e, NW, w);
     return __builtin_amdgcn_readfirstlane(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0;
   };
-  bool bad = false;
+  int bad = 0;                       // a flag never came: outputs become NaN (wave-uniform)
   auto wait_node = [&](int e) {
     int n = 0;
     while (!flag_set(e)) {
-      if (++n > p.spin_limit) { bad = true; break; }
+      if (++n > p.spin_limit) { bad = 1; break; }
       __builtin_amdgcn_s_sleep(2);
     }
   };
+  // node operands of the first XREG nodes in registers; bit x of `loaded` once X[x] is there
+  Frag<T> X[XREG][NKS_D];
+  float XD[XREG];            // log decay across each node
+  unsigned loaded = 0;
+  auto load_x = [&](auto xc) {
+    constexpr int x = decltype(xc)::value;
+    const Frag<T>* nb = node_base(NE[x]);
+#pragma unroll
+    for (int s = 0; s < NKS_D; ++s) X[x][s] = nb[s * 64 + lane];
+    XD[x] = node_ld_f(p.gnode + node_slot(bh, ns, NE[x], NW, w));
+    loaded |= 1u << x;
+  };
+
+
+  // ---------------- load the sweep: every input read is issued here ----------------
+  // Registers first (log_a, lambda), then the k and v images (phase A), then the q images
+  // (phase B): global_load_lds completes in issue order, so waiting until no more than the
+  // q copies are outstanding means k and v have landed.
+  // flags of the nodes over earlier sweeps, read along with the inputs (usually already set:
+  // those sweeps started long before)
+  int fl0[XREG];
+#pragma unroll
+  for (int x = 0; x < XREG; ++x)
+    fl0[x] = x < next ? __hip_atomic_load(p.sync + kFlagBase + node_slot(bh, ns, NE[x], NW, w),
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+  LamRegs<C, NT> lr[NB];
+  DecayRegs<C> ar[NB];
+  int t0s[NB], valids[NB];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const int uc = u < nch ? u : 0;                 // a missing last chunk re-reads chunk 0
+    t0s[u] = (c0 + uc) * C;
+    valids[u] = min(C, p.T - t0s[u]);
+    ar[u].fetch(lag + t0s[u], valids[u], lane);
+    lr[u].fetch(lamg + (size_t)t0s[u] * L, valids[u] * L, tid);
+  }
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    dma_image<T, C, DK, NW, false>(smem + S.k[u], kg + (size_t)t0s[u] * DK, valids[u], w, lane);
+    dma_image<T, C, DV, NW, true>(smem + S.v[u], vg + (size_t)t0s[u] * DV, valids[u], w, lane);
+  }
+#pragma unroll
+  for (int u = 0; u < NB; ++u)
+    dma_image<T, C, DK, NW, false>(smem + S.q[u], qg + (size_t)t0s[u] * DK, valids[u], w, lane);
+  wait_vm<NB * dma_count<T, C, DK, NW>(NW - 1)>();   // this wave's k, v (and registers) landed
+  float gch[NB];                        // total log decay of each chunk
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    ar[u].scan(lane);
+    gch[u] = ar[u].total();
+    lr[u].commit(reinterpret_cast<float*>(smem + S.lam[u]), C * L, tid);
+    if (w == 0)
+      ar[u].publish(reinterpret_cast<float*>(smem + S.dec[u]), reinterpret_cast<int*>(smem + S.flag[u]),
+                    gch[u], lane);
+  }
+  lds_barrier();
+
+  // published nodes over earlier sweeps: into registers now, their latency hides behind phase A
+  static_for<XREG>([&](auto xc) {
+    constexpr int x = decltype(xc)::value;
+    if (__builtin_amdgcn_readfirstlane(fl0[x]) != 0) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      load_x(xc);
+    }
+  });
+
+  // ---------------- phase A: chunk states, chunk 0's state, the sweep total ----------------
+  Frag<T> SL[NKS_D];              // state of chunk 0 (decayed to its end), level J+1 for chunk 1
+  f32x4 H[NTF];
+#pragma unroll
+  for (int b = 0; b < NTF; ++b) H[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float G = 0.f;
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    if (u < nch) {
+      f32x4 F[NTF];
+      chunk_state<T, C, DK, DV>(rd, smem + S.k[u], smem + S.v[u],
+                                reinterpret_cast<const float*>(smem + S.dec[u]) + 3 * C, lane, F);
+      const float d = __expf(gch[u]);
+#pragma unroll
+      for (int b = 0; b < NTF; ++b) H[b] = d * H[b] + F[b];
+      G += gch[u];
+      if (u == 0 && NB > 1) {
+#pragma unroll
+        for (int s = 0; s < NKS_D; ++s) SL[s] = node_frag<T, DK>(F, s);
+      }
+    }
+  }
 
   // Own node: the sweep total plus its children (the first kc nodes of sw), published right
-  // away when the children are already there, else after the intra-chunk work.
+  // away when the children are already in registers, else after the intra-chunk work.
   const int kc = sw < ns ? __builtin_ctz((unsigned)(sw + 1)) : 0;
   bool published = sw >= ns;
-  auto publish = [&]() {
+  auto publish = [&]() {            // children x < min(kc, XREG) are loaded
     float gacc = G;
-    for (int x = 0; x < kc; ++x) {
+    static_for<XREG>([&](auto xc) {
+      constexpr int x = decltype(xc)::value;
+      if (x < kc) {
+        const float d = __expf(gacc);
+#pragma unroll
+        for (int s = 0; s < NKS_D; ++s) {
+          f32x4 lo, hi;
+          frag_to_f32(X[x][s], lo, hi);
+          H[2 * s] += d * lo;
+          H[2 * s + 1] += d * hi;
+        }
+        gacc += XD[x];
+      }
+    });
+    for (int x = XREG; x < kc; ++x) {   // beyond the registers: wait and read on demand
       const int e = node_index(x);
+      wait_node(e);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
       const Frag<T>* nb = node_base(e);
       const float d = __expf(gacc);
 #pragma unroll
@@ -860,7 +918,7 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
       }
       gacc += node_ld_f(p.gnode + node_slot(bh, ns, e, NW, w));
     }
-    if (bad) {
+    if (__builtin_amdgcn_readfirstlane(bad)) {
 #pragma unroll
       for (int b = 0; b < NTF; ++b) H[b] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
     }
@@ -873,11 +931,9 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
     node_publish_fence();
     if (lane == 0) __hip_atomic_store(p.sync + kFlagBase + me, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  if (!published) {
-    bool ready = true;
-    for (int x = 0; x < kc; ++x) ready = ready && flag_set(node_index(x));
-    if (ready) {
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (!published && kc <= XREG) {
+    const unsigned need = (1u << kc) - 1u;
+    if ((loaded & need) == need) {
       publish();
       published = true;
     }
@@ -931,27 +987,27 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
     }
   }
 
-  // ---------------- own node (if the children were late), nodes of earlier sweeps ----------------
-  if (!published) {
-    for (int x = 0; x < kc; ++x) wait_node(node_index(x));
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    publish();
-  }
-  for (int x = kc; x < next; ++x) wait_node(node_index(x));
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-
-  Frag<T> X[XREG][NKS_D];
-  float XD[XREG];            // log decay across each node
-  if (ns > 0) {
-#pragma unroll
-    for (int x = 0; x < XREG; ++x) {
-      const int e = node_index(x);
-      const Frag<T>* nb = node_base(e);
-#pragma unroll
-      for (int s = 0; s < NKS_D; ++s) X[x][s] = nb[s * 64 + lane];
-      XD[x] = node_ld_f(p.gnode + node_slot(bh, ns, e, NW, w));
+  // ---------------- nodes that were not there yet; own node if it waited for them ----------------
+  // children first (later sweeps wait for this node), then the rest
+  static_for<XREG>([&](auto xc) {
+    constexpr int x = decltype(xc)::value;
+    if (x < kc && !((loaded >> x) & 1u)) {
+      wait_node(NE[x]);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      load_x(xc);
     }
-  }
+  });
+  if (!published) publish();
+  static_for<XREG>([&](auto xc) {
+    constexpr int x = decltype(xc)::value;
+    if (x < next && !((loaded >> x) & 1u)) {
+      wait_node(NE[x]);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      load_x(xc);
+    }
+  });
+  for (int x = XREG; x < next; ++x) wait_node(node_index(x));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
   // ---------------- phase B, read-out of earlier sweeps and store ----------------
   float gam = 0.f;           // log decay from the sweep's first position to the current chunk start
@@ -995,7 +1051,7 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         const int qi = 16 * qb + j;
-        if (bad) O[u][qb] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        if (__builtin_amdgcn_readfirstlane(bad)) O[u][qb] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
         if (qi < valid) store_quad<T>(og + (size_t)(t0 + qi) * DV + 16 * w + 4 * g, O[u][qb]);
       }
       gam += gch[u];
