@@ -187,27 +187,55 @@ __host__ __device__ inline Smem smem_layout(int es, int C, int DK, int DV, int N
 // staging: HBM -> shared memory
 // ----------------------------------------------------------------------------------------
 
-// One [C, DF] block (row stride DF; rows past `valid` replaced by row valid-1) into an image,
+// One [C, DF] block (row stride DF; rows past `valid` replaced by row valid-1) into an image
 // by global_load_lds: slot p of the image (row p/NV, physical vector p%NV) receives logical
 // vector (p%NV) ^ swizzle(row) of that row. Wave w issues the 1 KB blocks i*NW + w; lanes
 // past the image end issue nothing.
+// The per-lane part of the source offsets is computed once per kernel (the images of all
+// chunks share it); a ragged chunk (valid < C) takes the clamping path.
 template <typename T, int C, int DF, int NW, bool VAL>
-__device__ __forceinline__ void dma_image(unsigned char* img, const T* __restrict__ g, int valid,
-                                          int w, int lane) {
-  constexpr int ES = (int)sizeof(T), NV = DF * ES / 16, SLOTS = C * NV;
-  constexpr int ITERS = cdiv(SLOTS, 64 * NW);
+struct DmaPlan {
+  static constexpr int ES = (int)sizeof(T), NV = DF * ES / 16, SLOTS = C * NV;
+  static constexpr int ITERS = cdiv(SLOTS, 64 * NW);
+  int row[ITERS], col[ITERS];      // source row, element offset of the piece within the row
+  __device__ __forceinline__ void init(int w, int lane) {
 #pragma unroll
-  for (int it = 0; it < ITERS; ++it) {
-    const int blk = it * NW + w;                       // 1 KB block of the image
-    const int p = blk * 64 + lane;
-    if (p < SLOTS) {
-      const int r = p / NV, pv = p % NV;
-      const int v = pv ^ (VAL ? swz_val<ES, NV>(r) : swz_row<ES, NV>(r));
-      const int rs = min(r, valid - 1);
-      const T* src = g + (size_t)rs * DF + v * (16 / ES);
+    for (int it = 0; it < ITERS; ++it) {
+      const int p = (it * NW + w) * 64 + lane;
+      const int r = min(p / NV, C - 1), pv = p % NV;
+      row[it] = r;
+      col[it] = (pv ^ (VAL ? swz_val<ES, NV>(r) : swz_row<ES, NV>(r))) * (16 / ES);
+    }
+  }
+  __device__ __forceinline__ void issue(unsigned char* img, const T* __restrict__ g, int valid,
+                                        int w, int lane) const {
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      const int blk = it * NW + w;
+      if (blk * 64 + lane < SLOTS) {
+        const int r = valid == C ? row[it] : min(row[it], valid - 1);
+        const T* src = g + (size_t)(r * DF + col[it]);
 #if defined(__HIP_DEVICE_COMPILE__)
-      // (the host pass of hipcc does not know this gfx950 builtin; only device code uses it)
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(img + blk * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(src, (lds_void*)(img + blk * 1024), 16, 0, 0);
+#else
+        (void)src;
+#endif
+      }
+    }
+  }
+};
+
+// lambda rows of one chunk (n_total = C*L contiguous floats, n_valid of them real) by 4-byte
+// global_load_lds: float i lands at lam[i]; past the real ones the last is repeated (those
+// rows belong to positions past T, whose outputs are not stored).
+__device__ __forceinline__ void dma_lambda(float* lam, const float* __restrict__ g, int n_valid,
+                                           int n_total, int w, int nw, int lane) {
+  for (int blk = w; blk * 64 < n_total; blk += nw) {
+    const int i = blk * 64 + lane;
+    if (i < n_total) {
+      const float* src = g + min(i, n_valid - 1);
+#if defined(__HIP_DEVICE_COMPILE__)
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lam + blk * 64), 4, 0, 0);
 #else
       (void)src;
 #endif
@@ -215,7 +243,7 @@ __device__ __forceinline__ void dma_image(unsigned char* img, const T* __restric
   }
 }
 
-// global_load_lds instructions wave w issues for one [C, DF] image
+// global_load_lds instructions wave w issues for one [C, DF] image (DmaPlan::issue)
 template <typename T, int C, int DF, int NW>
 __host__ __device__ constexpr int dma_count(int w) {
   constexpr int SLOTS = C * DF * (int)sizeof(T) / 16;
@@ -244,29 +272,6 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
-
-// lambda rows of one chunk (C*L contiguous floats) in registers: NF floats per thread, each
-// loaded at a clamped in-bounds index and zeroed past the chunk's valid rows.
-template <int C, int NT>
-struct LamRegs {
-  static constexpr int NF = cdiv(C * kLamCap, NT);
-  float x[NF];
-  __device__ __forceinline__ void fetch(const float* __restrict__ g, int nvalid, int tid) {
-#pragma unroll
-    for (int it = 0; it < NF; ++it) {
-      const int i = tid + it * NT;
-      const float v = g[min(i, nvalid - 1)];
-      x[it] = i < nvalid ? v : 0.f;
-    }
-  }
-  __device__ __forceinline__ void commit(float* lam, int ntotal, int tid) const {
-#pragma unroll
-    for (int it = 0; it < NF; ++it) {
-      const int i = tid + it * NT;
-      if (i < ntotal) lam[i] = x[it];
-    }
-  }
-};
 
 // log_a of one chunk in every wave's registers (lane l holds positions E*l .. E*l+E-1), and
 // the chunk-local inclusive prefix sum A (same layout), computed by each wave on its own.
@@ -819,7 +824,6 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   for (int x = 0; x < XREG; ++x)
     fl0[x] = x < next ? __hip_atomic_load(p.sync + kFlagBase + node_slot(bh, ns, NE[x], NW, w),
                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-  LamRegs<C, NT> lr[NB];
   DecayRegs<C> ar[NB];
   int t0s[NB], valids[NB];
 #pragma unroll
@@ -828,23 +832,28 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
     t0s[u] = (c0 + uc) * C;
     valids[u] = min(C, p.T - t0s[u]);
     ar[u].fetch(lag + t0s[u], valids[u], lane);
-    lr[u].fetch(lamg + (size_t)t0s[u] * L, valids[u] * L, tid);
   }
-#pragma unroll
-  for (int u = 0; u < NB; ++u) {
-    dma_image<T, C, DK, NW, false>(smem + S.k[u], kg + (size_t)t0s[u] * DK, valids[u], w, lane);
-    dma_image<T, C, DV, NW, true>(smem + S.v[u], vg + (size_t)t0s[u] * DV, valids[u], w, lane);
-  }
+  DmaPlan<T, C, DK, NW, false> dk_plan;
+  DmaPlan<T, C, DV, NW, true> dv_plan;
+  dk_plan.init(w, lane);
+  dv_plan.init(w, lane);
 #pragma unroll
   for (int u = 0; u < NB; ++u)
-    dma_image<T, C, DK, NW, false>(smem + S.q[u], qg + (size_t)t0s[u] * DK, valids[u], w, lane);
+    dma_lambda(reinterpret_cast<float*>(smem + S.lam[u]), lamg + (size_t)t0s[u] * L, valids[u] * L, C * L,
+               w, NW, lane);
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    dk_plan.issue(smem + S.k[u], kg + (size_t)t0s[u] * DK, valids[u], w, lane);
+    dv_plan.issue(smem + S.v[u], vg + (size_t)t0s[u] * DV, valids[u], w, lane);
+  }
+#pragma unroll
+  for (int u = 0; u < NB; ++u) dk_plan.issue(smem + S.q[u], qg + (size_t)t0s[u] * DK, valids[u], w, lane);
   wait_vm<NB * dma_count<T, C, DK, NW>(NW - 1)>();   // this wave's k, v (and registers) landed
   float gch[NB];                        // total log decay of each chunk
 #pragma unroll
   for (int u = 0; u < NB; ++u) {
     ar[u].scan(lane);
     gch[u] = ar[u].total();
-    lr[u].commit(reinterpret_cast<float*>(smem + S.lam[u]), C * L, tid);
     if (w == 0)
       ar[u].publish(reinterpret_cast<float*>(smem + S.dec[u]), reinterpret_cast<int*>(smem + S.flag[u]),
                     gch[u], lane);
