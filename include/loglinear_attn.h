@@ -34,15 +34,14 @@
  * (L <= 24; a ragged last chunk is masked). Output is bitwise deterministic for
  * identical inputs and arguments.
  *
- * Execution: two kernels on `stream`: a fill kernel that clears the workspace's
- * ticket counter and node flags, then one forward kernel in which each workgroup
- * loads R consecutive chunks of one head (a "sweep") into shared memory, publishes
- * that sweep's Fenwick node in the workspace and reads the nodes of earlier sweeps
- * of its head, waiting for them with bounded polls. Workgroups are ordered by an
- * atomic ticket, so a workgroup only ever waits for workgroups that started before
- * it. Should a wait
- * nevertheless run out (a fault elsewhere), the affected outputs are written as NaN
- * and the kernel still completes.
+ * Execution: one forward kernel on `stream` (preceded by a fill kernel only when the
+ * library allocates the workspace itself) in which each workgroup loads R consecutive
+ * chunks of one head (a "sweep") into shared memory, publishes that sweep's Fenwick
+ * node in the workspace and reads the nodes of earlier sweeps of its head, waiting for
+ * them with bounded polls. Workgroups are ordered by an atomic ticket, so a workgroup
+ * only ever waits for workgroups that started before it. Should a wait nevertheless
+ * run out (a fault elsewhere, or a workspace that was not zero-filled), the affected
+ * outputs are written as NaN and the kernel still completes.
  *
  * Errors: every function validates its arguments on the host before it touches the
  * device and returns a status code (LLA_OK or a negative LLA_ERR_*); nothing is
@@ -103,15 +102,19 @@ int loglinear_attn_fwd_f32(const float* q, const float* k, const float* v,
  *           when they do not fit the device's shared memory).
  *   workspace / workspace_bytes : caller-owned device memory of at least
  *           loglinear_attn_workspace_bytes(...) bytes (256-byte aligned), or
- *           NULL/0 to let the library allocate stream-ordered on `stream`. The
- *           workspace holds the ticket counter, node flags and nodes of one call:
+ *           NULL/0 to let the library allocate (and zero) it stream-ordered on
+ *           `stream`. A caller workspace must be zero-filled once before its first
+ *           use (e.g. allocated zeroed); every call leaves it ready for the next one,
+ *           whatever the shapes, so it is never cleared again. It holds the ticket
+ *           counter (an epoch and a count), node flags and nodes of the running call:
  *           two calls that may run concurrently (different streams) must not share
- *           it; calls ordered on one stream may.
+ *           it; calls ordered on one stream may. Layout: the first
+ *           round_up_256(4 * (64 + B*H*(nsweep-1)*dv/16)) bytes are the counter and
+ *           flags, the only part that must start at zero.
  *   stage_events : optional timing hooks; each non-NULL entry is a hipEvent_t the
- *           library records on `stream`: [0] before the fill kernel, [1] after it
- *           (just before the forward kernel), [2] after the forward kernel; [3] is
- *           not used. [0] and [1] are recorded back to back when a single sweep
- *           covers T and no fill is needed. The caller owns the events.
+ *           library records on `stream`: [0] before the fill kernel (if any), [1]
+ *           just before the forward kernel, [2] after it; [3] is not used. The caller
+ *           owns the events.
  * The result does not depend on chunk or sweep beyond float rounding.
  */
 typedef struct lla_fwd_args {

