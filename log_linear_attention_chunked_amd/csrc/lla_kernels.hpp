@@ -212,7 +212,9 @@ struct DmaPlan {
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
       const int blk = it * NW + w;
-      if (blk * 64 + lane < SLOTS) {
+      // images made of whole 64-lane rounds issue unconditionally, so the compiler can count
+      // them when it places waits for earlier loads
+      if (SLOTS % (64 * NW) == 0 || blk * 64 + lane < SLOTS) {
         const int r = valid == C ? row[it] : min(row[it], valid - 1);
         const T* src = g + (size_t)(r * DF + col[it]);
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -832,9 +834,11 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
 
 
   // ---------------- load the sweep: every input read is issued here ----------------
-  // Registers first (log_a, lambda), then the k and v images (phase A), then the q images
-  // (phase B): global_load_lds completes in issue order, so waiting until no more than the
-  // q copies are outstanding means k and v have landed.
+  // log_a into registers first, then the k and v images (phase A), the lambda rows and the q
+  // images (phase B): global_load_lds completes in issue order, so waiting until no more than
+  // the q copies are outstanding means k, v and lambda have landed. The lambda copy has a
+  // run-time length, so it goes after the fixed-length k and v copies: the compiler then
+  // knows how many loads follow log_a and waits for log_a alone.
   // flags of the nodes over earlier sweeps, read along with the inputs (usually already set:
   // those sweeps started long before)
   int fl0[XREG];
@@ -857,17 +861,17 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   dk_plan.init(w, lane);
   dv_plan.init(w, lane);
 #pragma unroll
-  for (int u = 0; u < NB; ++u)
-    dma_lambda(reinterpret_cast<float*>(smem + S.lam[u]), lamg + (size_t)t0s[u] * L, valids[u] * L, C * L,
-               w, NW, lane);
-#pragma unroll
   for (int u = 0; u < NB; ++u) {
     dk_plan.issue(smem + S.k[u], kg + (size_t)t0s[u] * DK, valids[u], w, lane);
     dv_plan.issue(smem + S.v[u], vg + (size_t)t0s[u] * DV, valids[u], w, lane);
   }
 #pragma unroll
+  for (int u = 0; u < NB; ++u)
+    dma_lambda(reinterpret_cast<float*>(smem + S.lam[u]), lamg + (size_t)t0s[u] * L, valids[u] * L, C * L,
+               w, NW, lane);
+#pragma unroll
   for (int u = 0; u < NB; ++u) dk_plan.issue(smem + S.q[u], qg + (size_t)t0s[u] * DK, valids[u], w, lane);
-  wait_vm<NB * dma_count<T, C, DK, NW>(NW - 1)>();   // this wave's k, v (and registers) landed
+  wait_vm<NB * dma_count<T, C, DK, NW>(NW - 1)>();   // this wave's k, v, lambda landed
   float gch[NB];                        // total log decay of each chunk
 #pragma unroll
   for (int u = 0; u < NB; ++u) {
@@ -988,7 +992,7 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
         unit_decode(un, NQB, qb, ks);
         pf[(qb * NKS_C + ks) * 64 + lane] = score_unit<T, C, DK, DV>(rd, qimg, kimg, lam, L, dec, fact, qb, ks, lane);
       }
-      __syncthreads();
+      lds_barrier();
 
       Frag<T> vfr[NKS_C];
 #pragma unroll
@@ -1016,24 +1020,35 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   }
 
   // ---------------- nodes that were not there yet; own node if it waited for them ----------------
-  // children first (later sweeps wait for this node), then the rest
-  static_for<XREG>([&](auto xc) {
-    constexpr int x = decltype(xc)::value;
-    if (x < kc && !((loaded >> x) & 1u)) {
-      wait_node(NE[x]);
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      load_x(xc);
+  // Each round polls the flags of every node still missing at once and loads all that are
+  // published, until the nodes in `need` are there: first the children (later sweeps wait
+  // for this node), then the rest.
+  const int nreg = min(next, XREG);
+  auto gather = [&](unsigned need) {
+    int n = 0;
+    while (!bad && (loaded & need) != need) {
+      int fl[XREG];
+#pragma unroll
+      for (int x = 0; x < XREG; ++x)
+        fl[x] = (x < nreg && !((loaded >> x) & 1u))
+                    ? __hip_atomic_load(p.sync + kFlagBase + node_slot(bh, ns, NE[x], NW, w),
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                    : 0;
+      static_for<XREG>([&](auto xc) {
+        constexpr int x = decltype(xc)::value;
+        if (x < nreg && !((loaded >> x) & 1u) && __builtin_amdgcn_readfirstlane(fl[x]) == flagv) {
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          load_x(xc);
+        }
+      });
+      if ((loaded & need) == need) break;
+      if (++n > p.spin_limit) { bad = 1; break; }
+      __builtin_amdgcn_s_sleep(2);
     }
-  });
+  };
+  gather((1u << min(kc, XREG)) - 1u);
   if (!published) publish();
-  static_for<XREG>([&](auto xc) {
-    constexpr int x = decltype(xc)::value;
-    if (x < next && !((loaded >> x) & 1u)) {
-      wait_node(NE[x]);
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      load_x(xc);
-    }
-  });
+  gather((1u << nreg) - 1u);
   for (int x = XREG; x < next; ++x) wait_node(node_index(x));
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 
