@@ -227,11 +227,23 @@ struct DmaPlan {
   }
 };
 
-// lambda rows of one chunk (n_total = C*L contiguous floats, n_valid of them real) by 4-byte
-// global_load_lds: float i lands at lam[i]; past the real ones the last is repeated (those
-// rows belong to positions past T, whose outputs are not stored).
+// lambda rows of one chunk (n_total = C*L contiguous floats, a multiple of 4, n_valid of them
+// real) by global_load_lds: float i lands at lam[i]. A whole chunk with a 16-byte aligned source
+// moves in 16-byte pieces; otherwise 4-byte pieces, and past the real floats the last one is
+// repeated (those rows belong to positions past T, whose outputs are not stored).
 __device__ __forceinline__ void dma_lambda(float* lam, const float* __restrict__ g, int n_valid,
                                            int n_total, int w, int nw, int lane) {
+  if (n_valid == n_total && (reinterpret_cast<uintptr_t>(g) & 15) == 0) {
+    for (int blk = w; blk * 256 < n_total; blk += nw) {
+      const int i = (blk * 64 + lane) * 4;
+      if (i < n_total) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        __builtin_amdgcn_global_load_lds(g + i, (lds_void*)(lam + blk * 256), 16, 0, 0);
+#endif
+      }
+    }
+    return;
+  }
   for (int blk = w; blk * 64 < n_total; blk += nw) {
     const int i = blk * 64 + lane;
     if (i < n_total) {

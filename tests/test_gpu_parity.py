@@ -69,6 +69,7 @@ SHAPES = [
     (1, 1, 512, 128, 64, 128, 1),    # C = 128
     (2, 2, 768, 16, 128, 32, 2),     # dk = 16, dv = 128
     (1, 1, 4160, 64, 64, 64, 2),     # 65 chunks: many sweeps + a lone last chunk
+    (1, 3, 999, 64, 64, 64, 2),      # T*L odd: lambda rows of heads 1, 2 not 16-byte aligned
     (1, 2, 8192, 32, 32, 16, 1),     # 512 sweeps per head: deep Fenwick tree over sweeps
     (1, 1, 2048, 128, 128, 128, 1),  # C = 128, d = 128
 ]
