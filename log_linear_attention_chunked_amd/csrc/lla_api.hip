@@ -1,6 +1,7 @@
 // lla_api.hip — C ABI of the log-linear Mamba-2 forward pass: argument validation, plan
-// (chunk, sweep, workspace layout), and the stream-ordered launch sequence
-//   clear ticket counter and node flags -> fused forward kernel.
+// (chunk, sweep, workspace layout), and the stream-ordered launch sequence: the forward kernel,
+// preceded by a fill of the ticket counter and node flags only when the library allocates the
+// workspace itself.
 // The contract is documented in include/loglinear_attn.h.
 #include <hip/hip_runtime.h>
 
