@@ -35,6 +35,8 @@ Functions:
 * ``recurrent``         the O(log T)-state recurrent form: one state per level,
   merged like a carry when a lower level fills (study notes, section 3-6; zh
   lay summary, "drawer" merging). It shares no helper with ``bruteforce``.
+* ``recurrent_step``    one step of that form (the decoding step): the states
+  after t-1 and token t give the states after t and o_t.
 
 Readings taken where the pages are silent are listed in the design doc and repeated
 at the functions that depend on them: 0-based positions, the bucket of s == t is
@@ -48,7 +50,7 @@ import numpy as np
 
 __all__ = [
     "bit_length", "level", "num_levels", "level_matrix", "as_f64",
-    "bruteforce", "bruteforce_rows", "recurrent",
+    "bruteforce", "bruteforce_rows", "recurrent", "recurrent_step",
 ]
 
 
@@ -203,15 +205,34 @@ def _ctz(t: int) -> int:
     return (t & -t).bit_length() - 1
 
 
+def recurrent_step(S: np.ndarray, q_t, k_t, v_t, log_a_t: float, lam_t, t: int) -> np.ndarray:
+    """One step of the recurrent form for one head, in place on the level states.
+
+    ``S`` [Ls, dk, dv] holds the states after position t-1 (any contents for t = 0);
+    on return it holds them after position t, and the output o_t [dv] is returned.
+    With c = ctz(t) for t > 0: levels 0..c of t-1 are merged into level c+1 (the lower
+    drawers are full and spill into the next one, study notes section 3-6; zh lay
+    summary, "drawer" merging), levels 1..c empty, every state is multiplied by a_t;
+    then level 0 becomes k_t v_t^T (a_t is not in the decay of k_t) and
+    o_t = sum_l lambda[t, l] S_l^T q_t over the levels lam_t covers.
+    """
+    if t > 0:
+        c = _ctz(t)
+        merged = S[: c + 1].sum(axis=0)
+        S[1: c + 1] = 0.0
+        S[c + 1] = merged
+        S *= np.exp(log_a_t)
+    S[0] = np.outer(k_t, v_t)
+    n = len(lam_t)
+    return np.einsum("l,lkv,k->v", np.asarray(lam_t, dtype=np.float64), S[:n], q_t)
+
+
 def recurrent(q, k, v, log_a, lam) -> np.ndarray:
     """The recurrent (decoding) form: one dk x dv state per level.
 
     At step t the live states are level 0 = {t} and, for each set bit j of t,
     level j+1 holding the aligned block of 2^j positions just before the
-    blocks of the lower set bits. Going from t-1 to t with c = ctz(t): levels
-    0..c of t-1 are merged into level c+1 (the lower drawers are full and spill
-    into the next one), levels 1..c empty, every state is multiplied by a_t,
-    and level 0 is reset to k_t v_t^T. Then o_t = sum_l lambda[t,l] S_l^T q_t.
+    blocks of the lower set bits; ``recurrent_step`` moves from t-1 to t.
 
     Cost O(T L dk dv) per head: a second, independent algorithm for the same
     operator, used to cross-check ``bruteforce``.
@@ -226,13 +247,6 @@ def recurrent(q, k, v, log_a, lam) -> np.ndarray:
         for h in range(H):
             S = np.zeros((L + 1, dk, dv), dtype=np.float64)
             for t in range(T):
-                if t > 0:
-                    c = _ctz(t)
-                    merged = S[: c + 1].sum(axis=0)
-                    S[1: c + 1] = 0.0
-                    S[c + 1] = merged
-                    S *= np.exp(log_a[b, h, t])
-                S[0] = np.outer(k[b, h, t], v[b, h, t])
-                w = lam[b, h, t, :L]
-                out[b, h, t] = np.einsum("l,lkv,k->v", w, S[:L], q[b, h, t])
+                out[b, h, t] = recurrent_step(S, q[b, h, t], k[b, h, t], v[b, h, t],
+                                              log_a[b, h, t], lam[b, h, t, :L], t)
     return out

@@ -367,3 +367,50 @@ def test_planted_mistake_in_recurrent_carry(monkeypatch):
     bad = O.recurrent(*case)
     assert rel(good, O.bruteforce(*case)) <= 1e-12
     assert rel(bad, O.bruteforce(*case)) > 1e-6
+
+
+def test_planted_mistake_in_recurrent_step(monkeypatch):
+    # a_t also applied to the new level-0 state k_t v_t^T (the decay of k_s must start after s)
+    rng = np.random.default_rng(6)
+    case = rand_case(rng, 1, 1, 24, 3, 2)
+    good = O.recurrent(*case)
+
+    def wrong_step(S, q_t, k_t, v_t, log_a_t, lam_t, t):
+        if t > 0:
+            c = O._ctz(t)
+            merged = S[: c + 1].sum(axis=0)
+            S[1: c + 1] = 0.0
+            S[c + 1] = merged
+        S[0] = np.outer(k_t, v_t)
+        if t > 0:
+            S *= np.exp(log_a_t)
+        return np.einsum("l,lkv,k->v", np.asarray(lam_t, dtype=np.float64), S[:len(lam_t)], q_t)
+
+    monkeypatch.setattr(O, "recurrent_step", wrong_step)
+    bad = O.recurrent(*case)
+    assert rel(good, O.bruteforce(*case)) <= 1e-12
+    assert rel(bad, O.bruteforce(*case)) > 1e-6
+
+
+def test_recurrent_step_state_blocks():
+    # after step t the live states are exactly: level 0 = k_t v_t^T, and for each set bit j of t
+    # the decayed sum of k_s v_s^T over the aligned block of 2^j positions below the lower bits
+    rng = np.random.default_rng(7)
+    T, dk, dv = 45, 3, 2
+    q, k, v, la, lam = (np.asarray(x)[0, 0] for x in rand_case(rng, 1, 1, T, dk, dv))
+    L = O.num_levels(T)
+    S = np.zeros((L + 1, dk, dv))
+    A = np.cumsum(la)
+    for t in range(T):
+        O.recurrent_step(S, q[t], k[t], v[t], la[t], lam[t, :L], t)
+    t = T - 1
+    want = np.zeros_like(S)
+    want[0] = np.outer(k[t], v[t])
+    hi = t
+    for j in range(t.bit_length()):
+        if (t >> j) & 1:
+            lo = hi - (1 << j)
+            for s in range(lo, hi):
+                want[j + 1] += np.exp(A[t] - A[s]) * np.outer(k[s], v[s])
+            hi = lo
+    np.testing.assert_allclose(S, want, rtol=1e-12, atol=1e-12)
