@@ -154,6 +154,47 @@ int loglinear_attn_default_sweep(int B, int H, int T, int dk, int dv, int chunk,
 /* Static, NUL-terminated description of a status code. */
 const char* loglinear_attn_status_string(int status);
 
+/*
+ * loglinear_attn_decode_step — one decoding step: the same operator, one new token at position
+ * t for every (b, h), through the recurrent form with one dk x dv state per Fenwick level
+ * (study notes, sections 2-2 and 3-6; zh lay summary, "drawer" merging). With c = ctz(t) for
+ * t > 0, the level states 0..c after position t-1 merge into level c+1, every state is
+ * multiplied by a_t = exp(log_a_t), level 0 becomes k_t v_t^T, and
+ *     o_t = sum_l lambda[l] * S_l^T q_t  over the levels live after t
+ * (level 0 and level j+1 for each set bit j of t). Calling it for t = 0, 1, ..., T-1 on one
+ * cache gives the forward pass's outputs for those positions.
+ *
+ *   q, k   [B,H,dk]  v, out [B,H,dv]   bfloat16 (dtype LLA_DTYPE_BF16) or float32
+ *   log_a  [B,H]     lambda [B,H,Lc]  float32; lambda[.., l] = the token's weight of level l
+ *                                      (levels above bit_length(t) are not read)
+ *   state  [B,H,Lc,dk,dv] float32, log_scale [B,H,2,Lc] float32: the cache, owned by the
+ *          caller and updated in place. Level l >= 1, while live, is
+ *          state[b,h,l] * exp(log_scale[b,h,t&1,l]); level 0 (rank one) is kept as its
+ *          factors: (k, v) of the last even position in floats [0, dk+dv) of state[b,h,0],
+ *          of the last odd position in [dk+dv, 2(dk+dv)). Nothing is read before it was
+ *          written, so the cache needs no clearing before t = 0.
+ *   Lc     levels of the cache: at least bit_length(t) + 1 (LLA_ERR_INVALID_ARG otherwise),
+ *          at most 25 (positions below 2^24).
+ * Steps on one cache must run in order of t (on one stream); t is the same for all (b, h).
+ * Pointers are device pointers; out, state and log_scale must not overlap each other or the
+ * inputs. Returns LLA_OK or a negative LLA_ERR_* (B*H = 0 is a no-op).
+ */
+typedef struct lla_decode_args {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_a;
+  const float* lambda;
+  void* out;
+  float* state;
+  float* log_scale;
+  int B, H, dk, dv, Lc;
+  int dtype;                  /* enum lla_dtype */
+  long long t;
+} lla_decode_args;
+
+int loglinear_attn_decode_step(const lla_decode_args* args, lla_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,8 +16,8 @@ import ctypes
 from . import _lib
 from ._lib import LibraryNotBuilt  # noqa: F401
 
-__all__ = ["forward", "num_levels", "workspace_bytes", "default_chunk", "default_sweep",
-           "LLAError", "LibraryNotBuilt"]
+__all__ = ["forward", "decode_step", "new_decode_cache", "num_levels", "workspace_bytes",
+           "default_chunk", "default_sweep", "LLAError", "LibraryNotBuilt"]
 
 
 class LLAError(RuntimeError):
@@ -123,4 +123,53 @@ def forward(q, k, v, log_a, lam, out=None, *, chunk: int = 0, sweep: int = 0,
     st = _lib.lib().loglinear_attn_fwd_ex(ctypes.byref(a), ctypes.c_void_p(handle))
     if st != _lib.LLA_OK:
         raise LLAError(st)
+    return out
+
+
+def new_decode_cache(B, H, dk, dv, levels, device="cuda"):
+    """An empty decoding cache: (state [B,H,levels,dk,dv], log_scale [B,H,2,levels]), float32.
+    ``levels`` >= bit_length(t) + 1 for every position t it will see (<= 25)."""
+    import torch
+    state = torch.empty((B, H, levels, dk, dv), dtype=torch.float32, device=device)
+    log_scale = torch.empty((B, H, 2, levels), dtype=torch.float32, device=device)
+    return state, log_scale
+
+
+def decode_step(q, k, v, log_a, lam, state, log_scale, t: int, out=None, *, stream=None):
+    """One decoding step at position ``t`` (the same for every (b, h)); updates the cache.
+
+    q, k: [B,H,dk]; v: [B,H,dv] (bfloat16 or float32); log_a: [B,H] float32;
+    lam: [B,H,Lc] float32 (the token's level weights); state [B,H,Lc,dk,dv] and
+    log_scale [B,H,2,Lc] float32 (``new_decode_cache``). Returns out [B,H,dv] in q's dtype.
+    Steps on one cache must be issued for t = 0, 1, 2, ... in order.
+    """
+    import torch
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, dk]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    Lc = state.shape[2] if state.dim() == 5 else -1
+    _check(q, "q", q.dtype, (B, H, dk))
+    _check(k, "k", q.dtype, (B, H, dk))
+    _check(v, "v", q.dtype, (B, H, dv))
+    _check(log_a, "log_a", torch.float32, (B, H))
+    _check(lam, "lam", torch.float32, (B, H, Lc))
+    _check(state, "state", torch.float32, (B, H, Lc, dk, dv))
+    _check(log_scale, "log_scale", torch.float32, (B, H, 2, Lc))
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, (B, H, dv))
+    a = _lib.DecodeArgs()
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.log_a, a.lam, a.out = log_a.data_ptr(), lam.data_ptr(), out.data_ptr()
+    a.state, a.log_scale = state.data_ptr(), log_scale.data_ptr()
+    a.B, a.H, a.dk, a.dv, a.Lc = int(B), int(H), int(dk), int(dv), int(Lc)
+    a.dtype = _dtype_code(q.dtype)
+    a.t = int(t)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = _lib.lib().loglinear_attn_decode_step(ctypes.byref(a), ctypes.c_void_p(handle))
+    if st != _lib.LLA_OK:
+        raise LLAError(st, "loglinear_attn_decode_step")
     return out

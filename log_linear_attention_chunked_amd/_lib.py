@@ -35,6 +35,7 @@ EXPORTS = (
     "loglinear_attn_default_chunk",
     "loglinear_attn_default_sweep",
     "loglinear_attn_status_string",
+    "loglinear_attn_decode_step",
 )
 
 
@@ -65,6 +66,27 @@ class FwdArgs(ctypes.Structure):
     ]
 
 
+class DecodeArgs(ctypes.Structure):
+    """Mirror of ``lla_decode_args``."""
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("log_a", ctypes.c_void_p),
+        ("lam", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("state", ctypes.c_void_p),
+        ("log_scale", ctypes.c_void_p),
+        ("B", ctypes.c_int),
+        ("H", ctypes.c_int),
+        ("dk", ctypes.c_int),
+        ("dv", ctypes.c_int),
+        ("Lc", ctypes.c_int),
+        ("dtype", ctypes.c_int),
+        ("t", ctypes.c_longlong),
+    ]
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -87,6 +109,8 @@ def _declare(lib):
     lib.loglinear_attn_default_sweep.restype = i
     lib.loglinear_attn_status_string.argtypes = [i]
     lib.loglinear_attn_status_string.restype = ctypes.c_char_p
+    lib.loglinear_attn_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), vp]
+    lib.loglinear_attn_decode_step.restype = i
 
 
 def lib():

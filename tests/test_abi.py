@@ -144,3 +144,56 @@ def test_python_binding_requires_device_tensors():
     x = torch.zeros(1, 1, 8, 16)
     with pytest.raises(ValueError):
         lla.forward(x, x, x, torch.zeros(1, 1, 8), torch.zeros(1, 1, 8, 4))
+
+
+# ---------------------------------------------------------------------------------------
+# decoding step: host-side validation only (every case returns before any launch)
+# ---------------------------------------------------------------------------------------
+
+def _dargs(**kw):
+    a = _lib.DecodeArgs()
+    base = 1 << 40                 # fake, well-separated, aligned addresses: never dereferenced
+    a.q, a.k, a.v = base, base + (1 << 32), base + (2 << 32)
+    a.log_a, a.lam, a.out = base + (3 << 32), base + (4 << 32), base + (5 << 32)
+    a.state, a.log_scale = base + (6 << 32), base + (7 << 32)
+    a.B, a.H, a.dk, a.dv, a.Lc, a.dtype, a.t = 1, 2, 64, 64, 14, 0, 100
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(B=-1), _lib.LLA_ERR_INVALID_ARG),
+    (dict(t=-1), _lib.LLA_ERR_INVALID_ARG),
+    (dict(Lc=0), _lib.LLA_ERR_INVALID_ARG),
+    (dict(dk=48), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(dv=8), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(Lc=26), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(t=1 << 13, Lc=14), _lib.LLA_ERR_INVALID_ARG),     # needs bit_length(t)+1 = 15 levels
+    (dict(q=None), _lib.LLA_ERR_INVALID_ARG),
+    (dict(state=None), _lib.LLA_ERR_INVALID_ARG),
+    (dict(log_scale=None), _lib.LLA_ERR_INVALID_ARG),
+    (dict(q=(1 << 40) + 1), _lib.LLA_ERR_INVALID_ARG),     # misaligned bf16
+    (dict(state=(1 << 40) + (6 << 32) + 2), _lib.LLA_ERR_INVALID_ARG),
+    (dict(out=(1 << 40) + 64), _lib.LLA_ERR_INVALID_ARG),  # out overlaps q
+    (dict(state=(1 << 40) + (7 << 32) - 1024), _lib.LLA_ERR_INVALID_ARG),  # state overlaps log_scale
+])
+def test_decode_validation_codes(L, kw, code):
+    assert L.loglinear_attn_decode_step(ctypes.byref(_dargs(**kw)), None) == code
+
+
+def test_decode_levels_boundary(L):
+    # t = 2^13 - 1 needs 14 levels: accepted up to the launch, which a zero-head batch skips
+    assert L.loglinear_attn_decode_step(ctypes.byref(_dargs(B=0, t=(1 << 13) - 1, Lc=14)), None) == _lib.LLA_OK
+    assert L.loglinear_attn_decode_step(None, None) == _lib.LLA_ERR_INVALID_ARG
+
+
+def test_decode_binding_requires_device_tensors():
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    ensure_built()
+    x = torch.zeros(1, 1, 16)
+    with pytest.raises(ValueError):
+        lla.decode_step(x, x, x, torch.zeros(1, 1), torch.zeros(1, 1, 4),
+                        torch.zeros(1, 1, 4, 16, 16), torch.zeros(1, 1, 2, 4), 0)

@@ -1,0 +1,126 @@
+"""GPU parity of the decoding step: a cache advanced token by token through the C ABI
+against the fp64 CPU oracle on identical seeded inputs.
+
+Every output of a T-token run is compared with the O(T^2) definition (relative L2 over all
+outputs: 1e-4 for float32 inputs, 2e-2 for bfloat16 inputs), the cache itself with the
+oracle's recurrent states, and a cache full of NaN before t = 0 must change nothing.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.loglinear as O
+from lla_synth import custom, generate
+from tests._util import ensure_built, rel_l2, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    import torch
+    ensure_built()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_decode(x, levels=None, fill=None):
+    """Decode every position of x (forward-pass inputs [B,H,T,..]) on a fresh cache; returns
+    the outputs [B,H,T,dv] and the cache after the last step (all as numpy)."""
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    B, H, T, dk = x["q"].shape
+    dv = x["v"].shape[-1]
+    L = x["lam"].shape[-1]
+    Lc = levels or L
+    d = {k: v.cuda() for k, v in x.items()}
+    state, log_scale = lla.new_decode_cache(B, H, dk, dv, Lc)
+    if fill is not None:
+        state.fill_(fill)
+        log_scale.fill_(fill)
+    lam = torch.zeros((B, H, T, Lc), dtype=torch.float32, device="cuda")
+    lam[..., :L] = d["lam"]
+    outs = []
+    for t in range(T):
+        o = lla.decode_step(d["q"][:, :, t].contiguous(), d["k"][:, :, t].contiguous(),
+                            d["v"][:, :, t].contiguous(), d["log_a"][:, :, t].contiguous(),
+                            lam[:, :, t].contiguous(), state, log_scale, t)
+        outs.append(o)
+    torch.cuda.synchronize()
+    out = torch.stack(outs, dim=2).float().cpu().numpy().astype(np.float64)
+    return out, state.cpu().numpy().astype(np.float64), log_scale.cpu().numpy().astype(np.float64)
+
+
+CASES = [
+    # B, H, T, dk, dv, dtype
+    (2, 3, 300, 64, 64, "bf16"),
+    (1, 2, 200, 16, 32, "f32"),
+    (1, 1, 130, 128, 64, "bf16"),
+    (2, 1, 257, 32, 128, "f32"),
+    (1, 2, 64, 64, 16, "f32"),
+    (1, 1, 1, 16, 16, "f32"),          # a single token: level 0 only
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b{}h{}t{}dk{}dv{}_{}".format(*c))
+def test_decode_matches_oracle(case):
+    B, H, T, dk, dv, dtype = case
+    x = generate(custom(B, H, T, dk, dv, dtype=dtype), seed=T + dk + dv)
+    got, _, _ = run_decode(x)
+    want = O.bruteforce(x["q"], x["k"], x["v"], x["log_a"], x["lam"])
+    err = rel_l2(got, want)
+    print(f"decode {case}: rel_l2={err:.3e}", flush=True)
+    assert np.all(np.isfinite(got))
+    assert err <= tol_for(dtype), err
+
+
+def test_decode_cache_holds_the_level_states():
+    # after the last step, every live level (times its scale) equals the oracle's state
+    B, H, T, dk, dv = 1, 2, 77, 32, 16
+    x = generate(custom(B, H, T, dk, dv, dtype="f32"), seed=3)
+    _, state, log_scale = run_decode(x)
+    L = x["lam"].shape[-1]
+    xs = {k: O.as_f64(v) for k, v in x.items()}
+    t = T - 1
+    for h in range(H):
+        S = np.zeros((L + 1, dk, dv))
+        for s in range(T):
+            O.recurrent_step(S, xs["q"][0, h, s], xs["k"][0, h, s], xs["v"][0, h, s],
+                             xs["log_a"][0, h, s], xs["lam"][0, h, s, :L], s)
+        par = t & 1
+        k0 = state[0, h, 0].reshape(-1)[par * (dk + dv): par * (dk + dv) + dk]
+        v0 = state[0, h, 0].reshape(-1)[par * (dk + dv) + dk: (par + 1) * (dk + dv)]
+        assert rel_l2(np.outer(k0, v0), S[0]) <= 1e-6
+        for lev in range(1, L):
+            if (t >> (lev - 1)) & 1:
+                got = state[0, h, lev] * np.exp(log_scale[0, h, par, lev])
+                assert rel_l2(got, S[lev]) <= 1e-5, (h, lev)
+
+
+def test_decode_never_reads_an_unwritten_cache():
+    # NaN everywhere before t = 0: a level is read only after a step wrote it
+    x = generate(custom(1, 2, 150, 64, 32, dtype="bf16"), seed=9)
+    a, _, _ = run_decode(x)
+    b, _, _ = run_decode(x, fill=float("nan"))
+    assert np.all(np.isfinite(b))
+    assert np.array_equal(a, b)
+
+
+def test_decode_with_spare_levels():
+    # a cache with more levels than the positions need
+    x = generate(custom(1, 1, 100, 16, 16, dtype="f32"), seed=4)
+    got, _, _ = run_decode(x, levels=20)
+    want = O.bruteforce(x["q"], x["k"], x["v"], x["log_a"], x["lam"])
+    assert rel_l2(got, want) <= tol_for("f32")
+
+
+def test_decode_agrees_with_the_forward_pass():
+    # the token-by-token path and the chunked path give the same outputs (up to rounding)
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    x = generate(custom(2, 2, 320, 64, 64, dtype="f32"), seed=12)
+    got, _, _ = run_decode(x)
+    d = {k: v.cuda() for k, v in x.items()}
+    fwd = lla.forward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], chunk=64, sweep=2)
+    torch.cuda.synchronize()
+    assert rel_l2(got, fwd.cpu().numpy().astype(np.float64)) <= 1e-5
