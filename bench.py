@@ -50,6 +50,88 @@ def algorithmic_per_token(w, chunk: int) -> tuple[float, float]:
     return flop, byts
 
 
+def decode_measure(w, dev, stream, steps: int = 256, warmup: int = 32) -> dict:
+    """Decoding steps (``loglinear_attn_decode_step``) at the workload's head shape, for the
+    positions T-steps .. T-1 (decoding right after a prompt of ~T tokens).
+
+    The cache holds finite random states (every level the steps read is live data), so the
+    steps do exactly the work they do in use. Time per step = one launch each, back to back on
+    one stream, between two events. Bytes per step (what the step must move): per head the
+    live levels of t-1 (popcount(t-1) dk x dv fp32 states) read once, the merged level written,
+    the level-0 factors and the log-scales read and written, the token's q, k, v, log_a and
+    lambda read and its output written.
+    """
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    B, H, dk, dv = w.B, w.H, w.dk, w.dv
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    e = 2 if w.dtype == "bf16" else 4
+    Lc = max(w.L, 2)
+    g = torch.Generator(device="cpu").manual_seed(1)
+    state, log_scale = lla.new_decode_cache(B, H, dk, dv, Lc, device=dev)
+    state.copy_(0.1 * torch.randn(state.shape, generator=g))
+    log_scale.zero_()
+    q = torch.randn((B, H, dk), generator=g).to(dev, dt)
+    k = torch.randn((B, H, dk), generator=g).to(dev, dt)
+    v = torch.randn((B, H, dv), generator=g).to(dev, dt)
+    log_a = (-0.05 * torch.rand((B, H), generator=g)).to(dev)
+    lam = torch.rand((B, H, Lc), generator=g).to(dev)
+    out = torch.empty((B, H, dv), dtype=dt, device=dev)
+    t0 = max(w.T - steps, 1)
+    ts = list(range(t0, t0 + steps))
+    for t in ts[:warmup]:
+        lla.decode_step(q, k, v, log_a, lam, state, log_scale, t, out, stream=stream)
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for t in ts:
+        lla.decode_step(q, k, v, log_a, lam, state, log_scale, t, out, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_eager = e0.elapsed_time(e1) / steps
+    # the same steps captured once in a HIP graph and replayed: launches without the Python
+    # issue cost of each call (the eager loop above is bound by it)
+    ms = ms_eager
+    try:
+        gs = torch.cuda.Stream(dev)
+        gs.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gs):
+            with torch.cuda.graph(graph, stream=gs):
+                for t in ts:
+                    lla.decode_step(q, k, v, log_a, lam, state, log_scale, t, out, stream=gs)
+        stream.wait_stream(gs)
+        graph.replay()
+        torch.cuda.synchronize(dev)
+        reps = 5
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        ms = e0.elapsed_time(e1) / (reps * steps)
+    except Exception as exc:  # pragma: no cover - report the eager figure alone
+        print(f"decode graph capture failed ({exc}); reporting the eager loop", file=sys.stderr)
+    per_head = 0
+    for t in ts:
+        live = bin(t - 1).count("1")
+        per_head += (live + 1) * dk * dv * 4 + 4 * (dk + dv) * 4 + 4 * Lc * 4 \
+            + (2 * dk + 2 * dv) * e + 4 + 4 * Lc
+    byts = per_head * B * H / steps
+    achieved = byts / (ms * 1e-3) / 1e9
+    return {
+        "kernel": "lla_decode_kernel",
+        "config": {"B": B, "H": H, "dk": dk, "dv": dv, "levels": Lc, "positions": [ts[0], ts[-1]]},
+        "ms_per_step": ms,
+        "ms_per_step_eager_python": ms_eager,
+        "timing": "HIP graph of the steps, replayed" if ms != ms_eager else "eager loop",
+        "tokens_per_s": B / (ms * 1e-3),
+        "algorithmic_bytes_per_step": byts,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS},
+    }
+
+
 def cpu_baseline(w, x, heads: int) -> dict:
     """The fp64 oracle as it stands, on `heads` heads of the workload, scaled to tokens/s."""
     import oracle.loglinear as O
@@ -99,6 +181,7 @@ def main(argv=None) -> int:
                     help="skip the cold-cache, copy-bandwidth and CPU legs (profiler runs)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device copies of MIB MiB (hardware-counter calibration)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decoding-step measurement")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_fused_kernel.json"),
                     help="measured HBM traffic of the forward kernel (from rocprofv3 counters)")
     a = ap.parse_args(argv)
@@ -219,6 +302,9 @@ def main(argv=None) -> int:
         "algorithmic_flop_per_step": flop_ht * ht,
     }
 
+    if not a.no_decode:
+        res["decode"] = decode_measure(w, dev, stream)
+
     if not a.kernel_only:
         # cold caches: overwrite a 512 MiB buffer (outside the events) before each call
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -256,12 +342,12 @@ def main(argv=None) -> int:
 
 
 def _kernel_sha() -> str:
-    """Hash of the kernel sources, to tell whether recorded counters still apply."""
+    """Hash of the forward kernel's sources, to tell whether recorded counters still apply."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "log_linear_attention_chunked_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp")):
+        if f.endswith((".hip", ".hpp")) and f != "lla_decode.hip":
             h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
