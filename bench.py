@@ -77,8 +77,8 @@ def decode_measure(w, dev, stream, steps: int = 256, warmup: int = 32) -> dict:
     log_a = (-0.05 * torch.rand((B, H), generator=g)).to(dev)
     lam = torch.rand((B, H, Lc), generator=g).to(dev)
     out = torch.empty((B, H, dv), dtype=dt, device=dev)
-    t0 = max(w.T - steps, 1)
-    ts = list(range(t0, t0 + steps))
+    ts = list(range(max(w.T - steps, 1), w.T))     # positions the workload's cache covers
+    steps = len(ts)
     for t in ts[:warmup]:
         lla.decode_step(q, k, v, log_a, lam, state, log_scale, t, out, stream=stream)
     torch.cuda.synchronize(dev)

@@ -287,6 +287,27 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Inclusive prefix (sum or max) over the 64 lanes of a wave, by DPP: shifts by 1, 2, 4, 8
+// lanes inside each row of 16, then row 0's last lane into row 1 and row 2's into row 3, then
+// lane 31 into rows 2 and 3 (row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 =
+// 0x143). Lanes a step gives no source add the identity. A fixed order: bitwise reproducible.
+template <bool MAX>
+__device__ __forceinline__ float wave_scan(float x) {
+  const int id = __builtin_bit_cast(int, MAX ? -__builtin_inff() : 0.f);
+  auto step = [&](int y) {
+    const float v = __builtin_bit_cast(float, y);
+    x = MAX ? fmaxf(x, v) : x + v;
+  };
+  const int xi0 = __builtin_bit_cast(int, x);
+  step(__builtin_amdgcn_update_dpp(id, xi0, 0x111, 0xf, 0xf, false));
+  step(__builtin_amdgcn_update_dpp(id, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, false));
+  step(__builtin_amdgcn_update_dpp(id, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, false));
+  step(__builtin_amdgcn_update_dpp(id, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, false));
+  step(__builtin_amdgcn_update_dpp(id, __builtin_bit_cast(int, x), 0x142, 0xa, 0xf, false));
+  step(__builtin_amdgcn_update_dpp(id, __builtin_bit_cast(int, x), 0x143, 0xc, 0xf, false));
+  return x;
+}
+
 // log_a of one chunk in every wave's registers (lane l holds positions E*l .. E*l+E-1), and
 // the chunk-local inclusive prefix sum A (same layout), computed by each wave on its own.
 template <int C>
@@ -308,12 +329,8 @@ struct DecayRegs {
     float run = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) { run += x[e]; a[e] = run; }
-    float tot = run;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float y = __shfl_up(tot, d, 64);
-      if (lane >= d) tot += y;
-    }
+    (void)lane;
+    const float tot = wave_scan<false>(run);
     const float excl = tot - run;
 #pragma unroll
     for (int e = 0; e < E; ++e) a[e] += excl;
@@ -337,8 +354,7 @@ struct DecayRegs {
         amax = fmaxf(amax, fabsf(a[e]));
       }
     }
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d, 64));
+    amax = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_scan<true>(amax)), 63));
     if (lane == 0) *flag = amax < 40.f ? 1 : 0;
   }
 };
