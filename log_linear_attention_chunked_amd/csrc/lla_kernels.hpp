@@ -59,6 +59,39 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Copies from global into shared memory (global_load_lds: each lane's 4 or 16 bytes land at
+// M0 + lane * size), written as inline assembly. Through the builtin the compiler tracks them
+// as shared-memory stores of unknown extent and waits for every one of them (vmcnt 0) before
+// any later shared-memory read, which would hold phase A back until the q images arrive; it
+// adds no waits for these. Every read of copied data in this file is preceded by an explicit
+// wait_vm (copies complete in issue order) and, across waves, a barrier. The shared-memory
+// address, wave-uniform, is passed in M0.
+__device__ __forceinline__ unsigned lds_off(const void* p) {
+  return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(const lds_void*)p);
+}
+__device__ __forceinline__ void copy_lds16(const void* src, const void* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_off(dst)) : "memory");
+#else
+  (void)src; (void)dst;
+#endif
+}
+__device__ __forceinline__ void copy_lds4(const void* src, const void* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds_off(dst)) : "memory");
+#else
+  (void)src; (void)dst;
+#endif
+}
+// the same, device scope (sc1): node flags, coherent across XCDs like the flag polls
+__device__ __forceinline__ void copy_lds4_device(const void* src, const void* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("global_load_lds_dword %0, off sc1" ::"v"(src), "{m0}"(lds_off(dst)) : "memory");
+#else
+  (void)src; (void)dst;
+#endif
+}
+
 constexpr int kLamCap = 24;       // lambda levels held per position (T <= 2^23)
 constexpr int kMaxSweep = 2;      // chunks resident per workgroup
 
@@ -158,12 +191,15 @@ __device__ __forceinline__ int elem_off(int r, int f) {
 }
 
 // Shared-memory layout of the forward kernel (host and device agree). Per resident chunk u:
-// q, k, v images, lambda rows (C x L floats, row stride L), A / e^A / e^-A / state weights,
-// a flag word, and the P^T fragments of its masked scores; then the workgroup ticket.
+// q, k, v images, lambda rows (C x L floats, row stride L), A / e^A / e^-A / state weights (the
+// weights' slot first receives the chunk's log_a), a flag word and the chunk's total log decay,
+// and the P^T fragments of its masked scores; then copies of each wave's node flags, and the
+// workgroup ticket.
 struct Smem {
   int q[kMaxSweep], k[kMaxSweep], v[kMaxSweep], lam[kMaxSweep], dec[kMaxSweep], flag[kMaxSweep],
-      pf[kMaxSweep], ticket, total;
+      pf[kMaxSweep], flg, ticket, total;
 };
+constexpr int kFlagCopy = 8;      // node flags copied per wave (at least the register budget)
 __host__ __device__ inline Smem smem_layout(int es, int C, int DK, int DV, int NB) {
   Smem s;
   int off = 0;
@@ -178,6 +214,7 @@ __host__ __device__ inline Smem smem_layout(int es, int C, int DK, int DV, int N
     s.flag[u] = off; off += on ? 16 : 0;
     s.pf[u] = off;   off += on ? nqb * nks_c * 64 * 8 * es : 0;
   }
+  s.flg = off; off += 8 * kFlagCopy * 4;   // up to 8 waves
   s.ticket = off; off += 16;
   s.total = (off + 255) & ~255;
   return s;
@@ -217,11 +254,7 @@ struct DmaPlan {
       if (SLOTS % (64 * NW) == 0 || blk * 64 + lane < SLOTS) {
         const int r = valid == C ? row[it] : min(row[it], valid - 1);
         const T* src = g + (size_t)(r * DF + col[it]);
-#if defined(__HIP_DEVICE_COMPILE__)
-        __builtin_amdgcn_global_load_lds(src, (lds_void*)(img + blk * 1024), 16, 0, 0);
-#else
-        (void)src;
-#endif
+        copy_lds16(src, img + blk * 1024);
       }
     }
   }
@@ -237,9 +270,7 @@ __device__ __forceinline__ void dma_lambda(float* lam, const float* __restrict__
     for (int blk = w; blk * 256 < n_total; blk += nw) {
       const int i = (blk * 64 + lane) * 4;
       if (i < n_total) {
-#if defined(__HIP_DEVICE_COMPILE__)
-        __builtin_amdgcn_global_load_lds(g + i, (lds_void*)(lam + blk * 256), 16, 0, 0);
-#endif
+        copy_lds16(g + i, lam + blk * 256);
       }
     }
     return;
@@ -248,11 +279,7 @@ __device__ __forceinline__ void dma_lambda(float* lam, const float* __restrict__
     const int i = blk * 64 + lane;
     if (i < n_total) {
       const float* src = g + min(i, n_valid - 1);
-#if defined(__HIP_DEVICE_COMPILE__)
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lam + blk * 64), 4, 0, 0);
-#else
-      (void)src;
-#endif
+      copy_lds4(src, lam + blk * 64);
     }
   }
 }
@@ -316,12 +343,12 @@ struct DecayRegs {
   float x[E];
   float a[E];
 
-  __device__ __forceinline__ void fetch(const float* __restrict__ la, int valid, int lane) {
+  // from the chunk's log_a copied into shared memory (positions past `valid` count as 0)
+  __device__ __forceinline__ void fetch_lds(const float* la, int valid, int lane) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int i = lane * E + e;
-      const float v = la[min(i, valid - 1)];
-      x[e] = (i < C && i < valid) ? v : 0.f;
+      x[e] = (i < C && i < valid) ? la[i] : 0.f;
     }
   }
   // fixed summation order: bitwise reproducible
@@ -339,8 +366,9 @@ struct DecayRegs {
   __device__ __forceinline__ float total() const {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a[E - 1]), 63));
   }
-  // wave 0: publish A, e^A, e^-A, the state weights exp(g - A) and whether the factorised
-  // decay e^{A_i} e^{-A_s} is safe (|A| < 40)
+  // wave 0: publish A, e^A, e^-A, the state weights exp(g - A) (over the log_a copy: each lane
+  // reads its own positions before writing them), whether the factorised decay e^{A_i} e^{-A_s}
+  // is safe (|A| < 40), and the total g
   __device__ __forceinline__ void publish(float* dec, int* flag, float g, int lane) const {
     float amax = 0.f;
 #pragma unroll
@@ -355,7 +383,10 @@ struct DecayRegs {
       }
     }
     amax = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_scan<true>(amax)), 63));
-    if (lane == 0) *flag = amax < 40.f ? 1 : 0;
+    if (lane == 0) {
+      flag[0] = amax < 40.f ? 1 : 0;
+      flag[1] = __builtin_bit_cast(int, g);
+    }
   }
 };
 
@@ -756,6 +787,7 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   constexpr int NUNITS = num_units(NQB);
   constexpr int XREG = DK >= 128 ? 2 : 5;   // nodes over earlier sweeps held in registers
   static_assert(NB >= 1 && NB <= kMaxSweep, "one or two resident chunks");
+  static_assert(XREG <= kFlagCopy && NW <= 8, "node flag copies");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -862,27 +894,42 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
 
 
   // ---------------- load the sweep: every input read is issued here ----------------
-  // log_a into registers first, then the k and v images (phase A), the lambda rows and the q
-  // images (phase B): global_load_lds completes in issue order, so waiting until no more than
-  // the q copies are outstanding means k, v and lambda have landed. The lambda copy has a
-  // run-time length, so it goes after the fixed-length k and v copies: the compiler then
-  // knows how many loads follow log_a and waits for log_a alone.
-  // flags of the nodes over earlier sweeps, read along with the inputs (usually already set:
-  // those sweeps started long before)
-  int fl0[XREG];
-#pragma unroll
-  for (int x = 0; x < XREG; ++x)
-    fl0[x] = x < next ? __hip_atomic_load(p.sync + kFlagBase + node_slot(bh, ns, NE[x], NW, w),
-                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-  // (compared with flagv once the values are needed)
-  DecayRegs<C> ar[NB];
+  // Everything moves by global_load_lds straight into shared memory, in this order: each wave's
+  // node flags (device scope, like the flag polls: usually already set, those sweeps started long
+  // before), the chunks' log_a (wave 0), the k and v images (phase A), the lambda rows and the q
+  // images (phase B). The copies complete in issue order, so "no more than the copies issued
+  // after X outstanding" means X has landed. Nothing is loaded into registers before phase A:
+  // the compiler drains every outstanding copy before it uses a register loaded alongside them,
+  // which would hold phase A back until the q images arrive.
+  int* flc = reinterpret_cast<int*>(smem + S.flg) + w * kFlagCopy;
+  if (ns > 0 && lane < XREG) {
+    int e = NE[0];                      // lane x copies the flag of the x-th node (selects, not
+    static_for<XREG>([&](auto xc) {     // a dynamic register index)
+      constexpr int x = decltype(xc)::value;
+      if (lane == x) e = NE[x];
+    });
+    const int* src = p.sync + kFlagBase + node_slot(bh, ns, e, NW, w);
+    copy_lds4_device(src, flc);
+  }
   int t0s[NB], valids[NB];
 #pragma unroll
   for (int u = 0; u < NB; ++u) {
     const int uc = u < nch ? u : 0;                 // a missing last chunk re-reads chunk 0
     t0s[u] = (c0 + uc) * C;
     valids[u] = min(C, p.T - t0s[u]);
-    ar[u].fetch(lag + t0s[u], valids[u], lane);
+  }
+  if (w == 0) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      float* la = reinterpret_cast<float*>(smem + S.dec[u]) + 3 * C;
+#pragma unroll
+      for (int b = 0; b < cdiv(C, 64); ++b) {
+        if (b * 64 + lane < C) {
+          const float* src = lag + t0s[u] + min(b * 64 + lane, valids[u] - 1);
+          copy_lds4(src, la + b * 64);
+        }
+      }
+    }
   }
   DmaPlan<T, C, DK, NW, false> dk_plan;
   DmaPlan<T, C, DV, NW, true> dv_plan;
@@ -899,17 +946,27 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
                w, NW, lane);
 #pragma unroll
   for (int u = 0; u < NB; ++u) dk_plan.issue(smem + S.q[u], qg + (size_t)t0s[u] * DK, valids[u], w, lane);
-  wait_vm<NB * dma_count<T, C, DK, NW>(NW - 1)>();   // this wave's k, v, lambda landed
+  if (w == 0) {
+    // log_a landed (k, v and q copies of wave 0 follow it, lambda's at least none): scan, publish
+    wait_vm<NB * (2 * dma_count<T, C, DK, NW>(0) + dma_count<T, C, DV, NW>(0))>();
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      DecayRegs<C> ar;
+      float* dec = reinterpret_cast<float*>(smem + S.dec[u]);
+      ar.fetch_lds(dec + 3 * C, valids[u], lane);
+      ar.scan(lane);
+      ar.publish(dec, reinterpret_cast<int*>(smem + S.flag[u]), ar.total(), lane);
+    }
+  }
+  wait_vm<NB * dma_count<T, C, DK, NW>(NW - 1)>();   // this wave's flags, k, v, lambda landed
+  lds_barrier();
   float gch[NB];                        // total log decay of each chunk
 #pragma unroll
-  for (int u = 0; u < NB; ++u) {
-    ar[u].scan(lane);
-    gch[u] = ar[u].total();
-    if (w == 0)
-      ar[u].publish(reinterpret_cast<float*>(smem + S.dec[u]), reinterpret_cast<int*>(smem + S.flag[u]),
-                    gch[u], lane);
-  }
-  lds_barrier();
+  for (int u = 0; u < NB; ++u)
+    gch[u] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(smem + S.flag[u])[1]));
+  int fl0[XREG];
+#pragma unroll
+  for (int x = 0; x < XREG; ++x) fl0[x] = x < next ? flc[x] : 0;
 
   // published nodes over earlier sweeps: into registers now, their latency hides behind phase A
   static_for<XREG>([&](auto xc) {
