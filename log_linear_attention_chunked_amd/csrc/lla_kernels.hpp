@@ -66,8 +66,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 // adds no waits for these. Every read of copied data in this file is preceded by an explicit
 // wait_vm (copies complete in issue order) and, across waves, a barrier. The shared-memory
 // address, wave-uniform, is passed in M0.
+// a flat shared-memory address is the shared aperture's base plus the offset: its low 32 bits
 __device__ __forceinline__ unsigned lds_off(const void* p) {
-  return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(const lds_void*)p);
+  return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)p);
 }
 __device__ __forceinline__ void copy_lds16(const void* src, const void* dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
