@@ -67,6 +67,28 @@ __global__ __launch_bounds__(kCols * row_groups<DK>()) void lla_decode_kernel(Pa
   const T* vg = reinterpret_cast<const T*>(p.v) + (size_t)bh * dv;
   float* st = p.state + (size_t)bh * Lc * DK * dv;
   float* ls = p.lscale + (size_t)bh * 2 * Lc;
+
+  // The live levels of t-1 (which depend on t alone) are loaded first, together with the
+  // token's vectors: one memory round trip per step.
+  const long long tm = t - 1;
+  const int c = t > 0 ? __builtin_ctzll((unsigned long long)t) : 0;
+  const int top = t > 1 ? 64 - __builtin_clzll((unsigned long long)tm) : 0;   // bit_length(t-1)
+  float X[kMaxLevels - 1][RG];
+#pragma unroll
+  for (int l = 1; l < kMaxLevels; ++l) {
+    if (l <= top && ((tm >> (l - 1)) & 1)) {
+      const float* sl = st + ((size_t)l * DK + rg * RG) * dv + vc;
+#pragma unroll
+      for (int i = 0; i < RG; ++i) X[l - 1][i] = sl[(size_t)i * dv];
+    }
+  }
+  float F0[RG], vprev = 0.f;          // level 0 after t-1: rank one, factors of parity 1 - par
+  if (t > 0) {
+    const float* f0 = st + (size_t)(1 - par) * (DK + dv);
+    vprev = f0[DK + vc];
+#pragma unroll
+    for (int i = 0; i < RG; ++i) F0[i] = f0[rg * RG + i];
+  }
   if (tid < DK) {
     qs[tid] = to_f32<T>(qg[tid]);
     ks[tid] = to_f32<T>(kg[tid]);
@@ -81,25 +103,10 @@ __global__ __launch_bounds__(kCols * row_groups<DK>()) void lla_decode_kernel(Pa
 
   float part = 0.f;                          // this thread's rows of sum_l w_l S_l^T q
   if (t > 0) {
-    const long long tm = t - 1;
-    const int c = __builtin_ctzll((unsigned long long)t);
-    const int top = tm ? 64 - __builtin_clzll((unsigned long long)tm) : 0;   // bit_length(t-1)
-    // level 0 after t-1: rank one, factors of parity 1 - par
-    const float* f0 = st + (size_t)(1 - par) * (DK + dv);
-    const float vprev = f0[DK + vc];
     float M[RG];
 #pragma unroll
-    for (int i = 0; i < RG; ++i) M[i] = __expf(sig[0]) * f0[rg * RG + i] * vprev;
+    for (int i = 0; i < RG; ++i) M[i] = __expf(sig[0]) * F0[i] * vprev;
     // live levels 1..top of t-1; 1..c merge into c+1, the ones above c+1 are read out
-    float X[kMaxLevels - 1][RG];
-#pragma unroll
-    for (int l = 1; l < kMaxLevels; ++l) {
-      if (l <= top && ((tm >> (l - 1)) & 1)) {
-        const float* sl = st + ((size_t)l * DK + rg * RG) * dv + vc;
-#pragma unroll
-        for (int i = 0; i < RG; ++i) X[l - 1][i] = sl[(size_t)i * dv];
-      }
-    }
 #pragma unroll
     for (int l = 1; l < kMaxLevels; ++l) {
       if (l <= top && ((tm >> (l - 1)) & 1)) {
@@ -143,8 +150,8 @@ __global__ __launch_bounds__(kCols * row_groups<DK>()) void lla_decode_kernel(Pa
     if (tid < DK) st[(size_t)par * (DK + dv) + tid] = ks[tid];
     if (tid < Lc) {
       // log-scales after t: level 0 fresh, level c+1 just merged, the others decay by a_t
-      const int c = t > 0 ? __builtin_ctzll((unsigned long long)t) : -1;
-      ls[par * Lc + tid] = tid == 0 ? 0.f : tid == c + 1 ? la : sig[tid] + la;
+      const int cm = t > 0 ? c : -1;
+      ls[par * Lc + tid] = tid == 0 ? 0.f : tid == cm + 1 ? la : sig[tid] + la;
     }
   }
 }
