@@ -20,8 +20,10 @@
 // or 2, all of them resident in shared memory at once), one wave per 16 value columns.
 // Workgroups take a ticket from an atomic counter and map it sweep-major, so every sweep
 // they wait for belongs to a workgroup that started earlier.
-//   load:    q, k, v of the sweep go straight from HBM into swizzled shared-memory images
-//            (global_load_lds), lambda and log_a through registers; one wait for all of it.
+//   load:    node flags, log_a, k, v, lambda and q of the sweep go straight from HBM into
+//            shared memory (global_load_lds; q, k, v as swizzled images), in that order, with
+//            counted waits: wave 0 scans log_a once it lands, phase A starts once k and v
+//            have, while q is still arriving.
 //   phase A: chunk states k^T (w v) on MFMA (w: decay to the chunk end); the sweep total plus
 //            the nodes of earlier sweeps it absorbs (a Fenwick tree over sweeps) is published
 //            as this sweep's node; the state of chunk 0 is kept for chunk 1 (level J+1).
@@ -30,7 +32,7 @@
 //            published nodes), output store.
 // A node is published per wave (16 value columns) with device-scope stores, then a flag;
 // readers poll the flag (bounded: on timeout the outputs are set to NaN so that a broken
-// dependency can never hang the device) and read the node with device-scope loads.
+// dependency can never hang the device) and then read the node (see node_st below).
 //
 // MFMA conventions. 16x16 output tiles; the accumulator gives lane (j = lane & 15,
 // g = lane >> 4) rows 4g..4g+3 of column j. A K=32 operand fragment gives lane (j, g) the
@@ -336,8 +338,8 @@ __device__ __forceinline__ float wave_scan(float x) {
   return x;
 }
 
-// log_a of one chunk in every wave's registers (lane l holds positions E*l .. E*l+E-1), and
-// the chunk-local inclusive prefix sum A (same layout), computed by each wave on its own.
+// log_a of one chunk in a wave's registers (lane l holds positions E*l .. E*l+E-1), and the
+// chunk-local inclusive prefix sum A (same layout); wave 0 computes it for every chunk.
 template <int C>
 struct DecayRegs {
   static constexpr int E = C > 64 ? C / 64 : 1;
