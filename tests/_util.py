@@ -18,10 +18,11 @@ def ensure_built():
 
 def fits_smem(dtype: str, C: int, dk: int, dv: int, R: int) -> bool:
     """Whether R resident chunks fit the 160 KB of gfx950 shared memory (q, k, v images,
-    24 lambda levels, decays and flag, P^T fragments per chunk, plus the ticket)."""
+    24 lambda levels, decays and flag, P^T fragments per chunk, plus copies of up to 8 waves'
+    node flags and the ticket)."""
     es = 2 if dtype == "bf16" else 4
     per = C * (2 * dk + dv) * es + C * 24 * 4 + 16 * C + 16 + (C // 16) * ((C + 31) // 32) * 512 * es
-    return ((R * per + 16 + 255) & ~255) <= 160 * 1024
+    return ((R * per + 256 + 16 + 255) & ~255) <= 160 * 1024
 
 
 def rel_l2(got, want) -> float:
