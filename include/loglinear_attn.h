@@ -136,6 +136,42 @@ typedef struct lla_fwd_args {
 int loglinear_attn_fwd_ex(const lla_fwd_args* args, lla_stream_t stream);
 
 /*
+ * loglinear_attn_fwd_varlen — the forward pass over a variable-length batch: N independent
+ * sequences packed along the time axis. Sequence n of head h is rows
+ * [cu_seqlens[n], cu_seqlens[n+1]) of the packed tensors; its positions restart at 0, so its
+ * levels and decays are those of a batch of one sequence of length T_n (the operation above,
+ * per sequence). Layout: dense row-major [H, total_T, .]:
+ *   q, k [H, total_T, dk]   v, out [H, total_T, dv]   log_a [H, total_T]
+ *   lambda [H, total_T, L], L = loglinear_attn_num_levels(max_T) (a sequence reads levels
+ *   0 .. num_levels(T_n)-1 of its rows)
+ *   cu_seqlens: device int32 [N+1], cu_seqlens[0] = 0, nondecreasing, cu_seqlens[N] =
+ *   total_T, and no sequence longer than max_T (host value, sizes the grid and the
+ *   workspace). The device array is not checked; the kernel clamps each sequence into the
+ *   packed rows and to max_T, so a malformed array gives wrong outputs, never an access out
+ *   of bounds. Rows outside every sequence are left as they were.
+ * Chunk, sweep, workspace: as in loglinear_attn_fwd_ex, with the shapes of N x H heads of
+ * max_T tokens: the workspace needed is loglinear_attn_workspace_bytes(N, H, max_T, dk, dv,
+ * chunk, sweep, dtype).
+ */
+typedef struct lla_fwd_varlen_args {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_a;
+  const float* lambda;
+  void* out;
+  const int* cu_seqlens;      /* device */
+  int N, H, total_T, max_T, dk, dv;
+  int dtype;                  /* enum lla_dtype */
+  int chunk;
+  int sweep;
+  void* workspace;
+  size_t workspace_bytes;
+} lla_fwd_varlen_args;
+
+int loglinear_attn_fwd_varlen(const lla_fwd_varlen_args* args, lla_stream_t stream);
+
+/*
  * Bytes of workspace loglinear_attn_fwd_ex needs for these arguments (0 when
  * the sequence fits one sweep). chunk/sweep 0 mean the library defaults, as in
  * loglinear_attn_fwd_ex. Returns 0 as well for invalid arguments; the entry

@@ -16,7 +16,7 @@ import ctypes
 from . import _lib
 from ._lib import LibraryNotBuilt  # noqa: F401
 
-__all__ = ["forward", "decode_step", "new_decode_cache", "num_levels", "workspace_bytes",
+__all__ = ["forward", "forward_varlen", "decode_step", "new_decode_cache", "num_levels", "workspace_bytes",
            "default_chunk", "default_sweep", "LLAError", "LibraryNotBuilt"]
 
 
@@ -172,4 +172,51 @@ def decode_step(q, k, v, log_a, lam, state, log_scale, t: int, out=None, *, stre
     st = _lib.lib().loglinear_attn_decode_step(ctypes.byref(a), ctypes.c_void_p(handle))
     if st != _lib.LLA_OK:
         raise LLAError(st, "loglinear_attn_decode_step")
+    return out
+
+
+def forward_varlen(q, k, v, log_a, lam, cu_seqlens, max_T: int, out=None, *, chunk: int = 0,
+                   sweep: int = 0, workspace=None, stream=None):
+    """Forward pass over N sequences packed along time (variable-length batch).
+
+    q, k: [H, total_T, dk]; v: [H, total_T, dv] (bfloat16 or float32); log_a: [H, total_T]
+    float32; lam: [H, total_T, L] float32 with L = num_levels(max_T); cu_seqlens: int32
+    device tensor [N+1] of sequence boundaries (0 = cu_seqlens[0] <= ... <= cu_seqlens[N] =
+    total_T); max_T >= every sequence length. Each sequence's positions start at 0.
+    Returns out [H, total_T, dv] in q's dtype (rows outside every sequence are untouched).
+    """
+    import torch
+    if q.dim() != 3:
+        raise ValueError("q must be [H, total_T, dk]")
+    H, TT, dk = q.shape
+    dv = v.shape[-1]
+    L = num_levels(max_T) if max_T > 0 else 0
+    N = cu_seqlens.numel() - 1
+    _check(q, "q", q.dtype, (H, TT, dk))
+    _check(k, "k", q.dtype, (H, TT, dk))
+    _check(v, "v", q.dtype, (H, TT, dv))
+    _check(log_a, "log_a", torch.float32, (H, TT))
+    _check(lam, "lam", torch.float32, (H, TT, L))
+    _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
+    if out is None:
+        out = torch.empty((H, TT, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, (H, TT, dv))
+    a = _lib.VarlenArgs()
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.log_a, a.lam, a.out = log_a.data_ptr(), lam.data_ptr(), out.data_ptr()
+    a.cu_seqlens = cu_seqlens.data_ptr()
+    a.N, a.H, a.total_T, a.max_T, a.dk, a.dv = int(N), int(H), int(TT), int(max_T), int(dk), int(dv)
+    a.dtype = _dtype_code(q.dtype)
+    a.chunk, a.sweep = int(chunk), int(sweep)
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8, (workspace.numel(),))
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    else:
+        a.workspace, a.workspace_bytes = None, 0
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = _lib.lib().loglinear_attn_fwd_varlen(ctypes.byref(a), ctypes.c_void_p(handle))
+    if st != _lib.LLA_OK:
+        raise LLAError(st, "loglinear_attn_fwd_varlen")
     return out

@@ -36,6 +36,7 @@ EXPORTS = (
     "loglinear_attn_default_sweep",
     "loglinear_attn_status_string",
     "loglinear_attn_decode_step",
+    "loglinear_attn_fwd_varlen",
 )
 
 
@@ -63,6 +64,30 @@ class FwdArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("stage_events", ctypes.c_void_p * 4),
+    ]
+
+
+class VarlenArgs(ctypes.Structure):
+    """Mirror of ``lla_fwd_varlen_args``."""
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("log_a", ctypes.c_void_p),
+        ("lam", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("N", ctypes.c_int),
+        ("H", ctypes.c_int),
+        ("total_T", ctypes.c_int),
+        ("max_T", ctypes.c_int),
+        ("dk", ctypes.c_int),
+        ("dv", ctypes.c_int),
+        ("dtype", ctypes.c_int),
+        ("chunk", ctypes.c_int),
+        ("sweep", ctypes.c_int),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -111,6 +136,8 @@ def _declare(lib):
     lib.loglinear_attn_status_string.restype = ctypes.c_char_p
     lib.loglinear_attn_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), vp]
     lib.loglinear_attn_decode_step.restype = i
+    lib.loglinear_attn_fwd_varlen.argtypes = [ctypes.POINTER(VarlenArgs), vp]
+    lib.loglinear_attn_fwd_varlen.restype = i
 
 
 def lib():

@@ -137,7 +137,14 @@ hipError_t set_smem(const void* fn, int bytes) {
                        : hipSuccess;
 }
 
-int launch(const lla_fwd_args& a, const Plan& pl, void* ws, bool fresh_ws, hipStream_t stream) {
+// packed variable-length batch: N sequences of vH heads along T_packed rows
+struct Varlen {
+  const int* cu_seqlens;
+  int vH, T_packed;
+};
+
+int launch(const lla_fwd_args& a, const Plan& pl, void* ws, bool fresh_ws, hipStream_t stream,
+           const Varlen* vl = nullptr) {
   const KernelSet* ks = lla::kernel_set(a.dtype, pl.C, a.dk, a.dv);
   if (!ks) return LLA_ERR_UNSUPPORTED;
 
@@ -158,6 +165,11 @@ int launch(const lla_fwd_args& a, const Plan& pl, void* ws, bool fresh_ws, hipSt
     p.nodeT = (char*)ws + pl.off_nodeT;
   }
   p.spin_limit = kSpinLimit;
+  if (vl) {
+    p.T = vl->T_packed;
+    p.cu_seqlens = vl->cu_seqlens;
+    p.vH = vl->vH;
+  }
   void* args[] = {&p};
   auto mark = [&](int i) {
     return a.stage_events[i] ? hipEventRecord(reinterpret_cast<hipEvent_t>(a.stage_events[i]), stream)
@@ -181,13 +193,7 @@ int launch(const lla_fwd_args& a, const Plan& pl, void* ws, bool fresh_ws, hipSt
   return LLA_OK;
 }
 
-int forward(const lla_fwd_args& a, hipStream_t stream) {
-  Plan pl;
-  int st = make_plan(a.B, a.H, a.T, a.dk, a.dv, a.chunk, a.sweep, a.dtype, pl);
-  if (st != LLA_OK) return st;
-  if (pl.BH == 0 || a.T == 0) return LLA_OK;
-  st = validate_pointers(a, pl);
-  if (st != LLA_OK) return st;
+int run_forward(const lla_fwd_args& a, const Plan& pl, hipStream_t stream, const Varlen* vl) {
   void* ws = a.workspace;
   bool owned = false;
   if (pl.ws_bytes > 0) {
@@ -199,9 +205,43 @@ int forward(const lla_fwd_args& a, hipStream_t stream) {
       owned = true;
     }
   }
-  st = launch(a, pl, ws, owned, stream);
+  int st = launch(a, pl, ws, owned, stream, vl);
   if (owned && hipFreeAsync(ws, stream) != hipSuccess && st == LLA_OK) st = LLA_ERR_HIP;
   return st;
+}
+
+int forward_varlen(const lla_fwd_varlen_args& v, hipStream_t stream) {
+  if (v.N < 0 || v.H < 0 || v.total_T < 0 || v.max_T < 0) return LLA_ERR_INVALID_ARG;
+  if (v.dtype != LLA_DTYPE_BF16 && v.dtype != LLA_DTYPE_F32) return LLA_ERR_INVALID_ARG;
+  if (v.max_T > v.total_T) return LLA_ERR_INVALID_ARG;
+  // the plan of N x H heads of the longest length: chunk, sweep, grid and workspace
+  Plan pl;
+  int st = make_plan(v.N, v.H, v.max_T, v.dk, v.dv, v.chunk, v.sweep, v.dtype, pl);
+  if (st != LLA_OK) return st;
+  if (pl.BH == 0 || v.max_T == 0) return LLA_OK;
+  // tensors are [H, total_T, .]; lambda has L = num_levels(max_T) levels per row
+  lla_fwd_args a;
+  memset(&a, 0, sizeof(a));
+  a.q = v.q; a.k = v.k; a.v = v.v; a.log_a = v.log_a; a.lambda = v.lambda; a.out = v.out;
+  a.B = 1; a.H = v.H; a.T = v.total_T; a.dk = v.dk; a.dv = v.dv; a.dtype = v.dtype;
+  a.workspace = v.workspace; a.workspace_bytes = v.workspace_bytes;
+  Plan pp = pl;
+  pp.BH = v.H;                         // pointer extents: H heads of total_T rows
+  st = validate_pointers(a, pp);
+  if (st != LLA_OK) return st;
+  if (!v.cu_seqlens || ((uintptr_t)v.cu_seqlens & 3)) return LLA_ERR_INVALID_ARG;
+  const Varlen vl{v.cu_seqlens, v.H, v.total_T};
+  return run_forward(a, pl, stream, &vl);
+}
+
+int forward(const lla_fwd_args& a, hipStream_t stream) {
+  Plan pl;
+  int st = make_plan(a.B, a.H, a.T, a.dk, a.dv, a.chunk, a.sweep, a.dtype, pl);
+  if (st != LLA_OK) return st;
+  if (pl.BH == 0 || a.T == 0) return LLA_OK;
+  st = validate_pointers(a, pl);
+  if (st != LLA_OK) return st;
+  return run_forward(a, pl, stream, nullptr);
 }
 
 }  // namespace
@@ -211,6 +251,11 @@ extern "C" {
 int loglinear_attn_fwd_ex(const lla_fwd_args* args, lla_stream_t stream) {
   if (!args) return LLA_ERR_INVALID_ARG;
   return forward(*args, reinterpret_cast<hipStream_t>(stream));
+}
+
+int loglinear_attn_fwd_varlen(const lla_fwd_varlen_args* args, lla_stream_t stream) {
+  if (!args) return LLA_ERR_INVALID_ARG;
+  return forward_varlen(*args, reinterpret_cast<hipStream_t>(stream));
 }
 
 int loglinear_attn_fwd(const void* q, const void* k, const void* v, const float* log_a,

@@ -763,6 +763,11 @@ struct Params {
   float* gnode;     // [BH][ns][NW]: log decay across node e (one copy per wave)
   void* nodeT;      // [BH][ns][NW][ceil(DK/32)][64] Frag<T>: node e as read-out operands
   int spin_limit;   // polls of a node flag before the wait is abandoned
+  // Variable-length batches (cu_seqlens non-null): head index bh = n * vH + h is sequence n of
+  // head h, positions [cu_seqlens[n], cu_seqlens[n+1]) of the packed [vH, T, .] tensors (T is
+  // then the packed length); nchunks and nsweep are those of the longest sequence.
+  const int* cu_seqlens;
+  int vH;
 };
 
 // Node flags, data and decays are indexed by (head, node = sweep index e, wave).
@@ -827,7 +832,20 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   }
   const int sw = t / p.BH, bh = t - sw * p.BH;
 
-  const size_t hoff = (size_t)bh * p.T;
+  // this head's sequence: its length, first row in the tensors, chunk count
+  int Tn = p.T, nchunks = p.nchunks;
+  size_t hoff = (size_t)bh * p.T;
+  if (p.cu_seqlens) {
+    const int n = bh / p.vH, h = bh - n * p.vH;
+    // clamped into the packed rows and to the longest length the grid was sized for
+    const int s0 = min(max(p.cu_seqlens[n], 0), p.T);
+    const int s1 = min(max(p.cu_seqlens[n + 1], s0), min(s0 + p.nchunks * C, p.T));
+    Tn = s1 - s0;
+    nchunks = cdiv(Tn, C);
+    hoff = (size_t)h * p.T + s0;
+    if (sw * NB >= nchunks) return;   // shorter than the longest sequence: no such sweep, and
+  }                                   // no sweep of this head ever waits for one
+
   const T* qg = reinterpret_cast<const T*>(p.q) + hoff * DK;
   const T* kg = reinterpret_cast<const T*>(p.k) + hoff * DK;
   const T* vg = reinterpret_cast<const T*>(p.v) + hoff * DV;
@@ -836,7 +854,7 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   T* og = reinterpret_cast<T*>(p.out) + hoff * DV;
 
   const int c0 = sw * NB;
-  const int nch = min(NB, p.nchunks - c0);
+  const int nch = min(NB, nchunks - c0);
   const int next = __builtin_popcount((unsigned)sw);
 
   Reader<T, C, DK, DV> rd;
@@ -919,7 +937,7 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   for (int u = 0; u < NB; ++u) {
     const int uc = u < nch ? u : 0;                 // a missing last chunk re-reads chunk 0
     t0s[u] = (c0 + uc) * C;
-    valids[u] = min(C, p.T - t0s[u]);
+    valids[u] = min(C, Tn - t0s[u]);
   }
   if (w == 0) {
 #pragma unroll
@@ -1146,7 +1164,7 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   for (int u = 0; u < NB; ++u) {
     if (u < nch) {
       const int t0 = (c0 + u) * C;
-      const int valid = min(C, p.T - t0);
+      const int valid = min(C, Tn - t0);
       const unsigned char* qimg = smem + S.q[u];
       const float* lam = reinterpret_cast<const float*>(smem + S.lam[u]);
       const float* dec = reinterpret_cast<const float*>(smem + S.dec[u]);

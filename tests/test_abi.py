@@ -197,3 +197,41 @@ def test_decode_binding_requires_device_tensors():
     with pytest.raises(ValueError):
         lla.decode_step(x, x, x, torch.zeros(1, 1), torch.zeros(1, 1, 4),
                         torch.zeros(1, 1, 4, 16, 16), torch.zeros(1, 1, 2, 4), 0)
+
+
+# ---------------------------------------------------------------------------------------
+# variable-length forward: host-side validation only
+# ---------------------------------------------------------------------------------------
+
+def _vargs(**kw):
+    a = _lib.VarlenArgs()
+    base = 1 << 40                 # fake, well-separated, aligned addresses: never dereferenced
+    a.q, a.k, a.v = base, base + (1 << 32), base + (2 << 32)
+    a.log_a, a.lam, a.out = base + (3 << 32), base + (4 << 32), base + (5 << 32)
+    a.cu_seqlens = base + (6 << 32)
+    a.N, a.H, a.total_T, a.max_T, a.dk, a.dv = 3, 2, 700, 400, 64, 64
+    a.dtype, a.chunk, a.sweep = 0, 64, 1
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=-1), _lib.LLA_ERR_INVALID_ARG),
+    (dict(max_T=701), _lib.LLA_ERR_INVALID_ARG),        # longer than the packed rows
+    (dict(dtype=5), _lib.LLA_ERR_INVALID_ARG),
+    (dict(dk=24), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(cu_seqlens=None), _lib.LLA_ERR_INVALID_ARG),
+    (dict(cu_seqlens=(1 << 40) + (6 << 32) + 2), _lib.LLA_ERR_INVALID_ARG),
+    (dict(q=None), _lib.LLA_ERR_INVALID_ARG),
+    (dict(out=(1 << 40) + 1024), _lib.LLA_ERR_INVALID_ARG),   # out overlaps q
+    (dict(workspace=(1 << 44), workspace_bytes=64), _lib.LLA_ERR_WORKSPACE),
+])
+def test_varlen_validation_codes(L, kw, code):
+    assert L.loglinear_attn_fwd_varlen(ctypes.byref(_vargs(**kw)), None) == code
+
+
+@pytest.mark.parametrize("kw", [dict(N=0), dict(H=0), dict(max_T=0, total_T=0)])
+def test_varlen_empty_is_a_noop(L, kw):
+    assert L.loglinear_attn_fwd_varlen(ctypes.byref(_vargs(**kw)), None) == _lib.LLA_OK
+    assert L.loglinear_attn_fwd_varlen(None, None) == _lib.LLA_ERR_INVALID_ARG
