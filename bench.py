@@ -132,6 +132,61 @@ def decode_measure(w, dev, stream, steps: int = 256, warmup: int = 32) -> dict:
     }
 
 
+VARLEN_LENGTHS = [8192, 7000, 5000, 4096, 3000, 2500, 1500, 1000, 480]   # 32768 tokens per head
+
+
+def varlen_measure(dev, stream, steps: int = 20, warmup: int = 5) -> dict:
+    """The variable-length forward on 9 sequences of mixed lengths (longest 8192, 32768 tokens
+    per head, the headline's count) packed along time, H=16, d=64, bf16, C=64: time per call
+    between events (with a host copy of cu_seqlens, so one workgroup per sweep that exists;
+    and without it, where the grid is sized for 9 sequences of 8192 tokens), tokens/s, and
+    the roofline against the same algorithmic bytes per head-token as the dense forward
+    (lambda rows of num_levels(8192) levels)."""
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    from lla_synth import custom, generate
+    H, d, C = 16, 64, 64
+    total, mx = sum(VARLEN_LENGTHS), max(VARLEN_LENGTHS)
+    x = generate(custom(1, H, total, d, d, dtype="bf16"), seed=2)
+    L = lla.num_levels(mx)
+    q, k, v = (x[n][0].to(dev) for n in ("q", "k", "v"))
+    log_a = x["log_a"][0].to(dev)
+    lam = x["lam"][0, :, :, :L].contiguous().to(dev)
+    cu_host = torch.tensor([0] + list(__import__("itertools").accumulate(VARLEN_LENGTHS)), dtype=torch.int32)
+    cu = cu_host.to(dev)
+    sweep = lla.default_sweep(len(VARLEN_LENGTHS), H, mx, d, d, C, "bf16")
+    ws = torch.zeros(max(lla.workspace_bytes(len(VARLEN_LENGTHS), H, mx, d, d, C, sweep, "bf16"), 1),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(v)
+
+    def timed(host):
+        call = lambda: lla.forward_varlen(q, k, v, log_a, lam, cu, mx, out, chunk=C, sweep=sweep,
+                                          workspace=ws, stream=stream, cu_seqlens_host=host)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize(dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / steps
+
+    ms = timed(cu_host)
+    ms_bounds = timed(None)
+    byts = ((2 * d + 2 * d) * 2 + 4 * L + 4) * H * total
+    return {
+        "config": {"H": H, "dk": d, "dv": d, "chunk": C, "sweep": sweep, "lengths": VARLEN_LENGTHS},
+        "ms_per_call": ms,
+        "ms_per_call_without_host_copy": ms_bounds,
+        "tokens_per_s": total / (ms * 1e-3),
+        "algorithmic_bytes_per_call": byts,
+        "roofline": {"bound": "hbm", "achieved": byts / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+    }
+
+
 def cpu_baseline(w, x, heads: int) -> dict:
     """The fp64 oracle as it stands, on `heads` heads of the workload, scaled to tokens/s."""
     import oracle.loglinear as O
@@ -182,6 +237,7 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device copies of MIB MiB (hardware-counter calibration)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decoding-step measurement")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the variable-length measurement")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_fused_kernel.json"),
                     help="measured HBM traffic of the forward kernel (from rocprofv3 counters)")
     a = ap.parse_args(argv)
@@ -304,6 +360,8 @@ def main(argv=None) -> int:
 
     if not a.no_decode:
         res["decode"] = decode_measure(w, dev, stream)
+    if not a.no_varlen and not a.kernel_only:
+        res["varlen"] = varlen_measure(dev, stream)
 
     if not a.kernel_only:
         # cold caches: overwrite a 512 MiB buffer (outside the events) before each call

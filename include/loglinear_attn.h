@@ -145,10 +145,15 @@ int loglinear_attn_fwd_ex(const lla_fwd_args* args, lla_stream_t stream);
  *   lambda [H, total_T, L], L = loglinear_attn_num_levels(max_T) (a sequence reads levels
  *   0 .. num_levels(T_n)-1 of its rows)
  *   cu_seqlens: device int32 [N+1], cu_seqlens[0] = 0, nondecreasing, cu_seqlens[N] =
- *   total_T, and no sequence longer than max_T (host value, sizes the grid and the
- *   workspace). The device array is not checked; the kernel clamps each sequence into the
- *   packed rows and to max_T, so a malformed array gives wrong outputs, never an access out
- *   of bounds. Rows outside every sequence are left as they were.
+ *   total_T, and no sequence longer than max_T (host value, sizes the workspace). The device
+ *   array is not checked; the kernel clamps each sequence into the packed rows and to max_T,
+ *   so a malformed array gives wrong outputs, never an access out of bounds. Rows outside
+ *   every sequence are left as they were.
+ *   cu_seqlens_host: NULL, or a host copy of the same N+1 values, read before the call
+ *   returns; the launch then has exactly one workgroup per (sweep, sequence, head) that
+ *   exists. Without it the grid is sized for N x H heads of max_T tokens and the surplus
+ *   workgroups leave at once, which costs time when lengths vary a lot. The two copies must
+ *   hold the same values: where they do not, the kernel sees it and writes no output.
  * Chunk, sweep, workspace: as in loglinear_attn_fwd_ex, with the shapes of N x H heads of
  * max_T tokens: the workspace needed is loglinear_attn_workspace_bytes(N, H, max_T, dk, dv,
  * chunk, sweep, dtype).
@@ -161,6 +166,7 @@ typedef struct lla_fwd_varlen_args {
   const float* lambda;
   void* out;
   const int* cu_seqlens;      /* device */
+  const int* cu_seqlens_host; /* host copy, or NULL */
   int N, H, total_T, max_T, dk, dv;
   int dtype;                  /* enum lla_dtype */
   int chunk;

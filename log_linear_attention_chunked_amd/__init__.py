@@ -176,13 +176,15 @@ def decode_step(q, k, v, log_a, lam, state, log_scale, t: int, out=None, *, stre
 
 
 def forward_varlen(q, k, v, log_a, lam, cu_seqlens, max_T: int, out=None, *, chunk: int = 0,
-                   sweep: int = 0, workspace=None, stream=None):
+                   sweep: int = 0, workspace=None, stream=None, cu_seqlens_host=None):
     """Forward pass over N sequences packed along time (variable-length batch).
 
     q, k: [H, total_T, dk]; v: [H, total_T, dv] (bfloat16 or float32); log_a: [H, total_T]
     float32; lam: [H, total_T, L] float32 with L = num_levels(max_T); cu_seqlens: int32
     device tensor [N+1] of sequence boundaries (0 = cu_seqlens[0] <= ... <= cu_seqlens[N] =
     total_T); max_T >= every sequence length. Each sequence's positions start at 0.
+    cu_seqlens_host: optional host copy of the same values (CPU tensor or list): the launch then
+    has one workgroup per sweep that exists instead of one per sweep of max_T tokens.
     Returns out [H, total_T, dv] in q's dtype (rows outside every sequence are untouched).
     """
     import torch
@@ -205,6 +207,12 @@ def forward_varlen(q, k, v, log_a, lam, cu_seqlens, max_T: int, out=None, *, chu
     a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
     a.log_a, a.lam, a.out = log_a.data_ptr(), lam.data_ptr(), out.data_ptr()
     a.cu_seqlens = cu_seqlens.data_ptr()
+    host = None
+    if cu_seqlens_host is not None:
+        host = torch.as_tensor(cu_seqlens_host, dtype=torch.int32, device="cpu").contiguous()
+        if host.shape != (N + 1,):
+            raise ValueError(f"cu_seqlens_host must hold {N + 1} values, got {tuple(host.shape)}")
+    a.cu_seqlens_host = host.data_ptr() if host is not None else None
     a.N, a.H, a.total_T, a.max_T, a.dk, a.dv = int(N), int(H), int(TT), int(max_T), int(dk), int(dv)
     a.dtype = _dtype_code(q.dtype)
     a.chunk, a.sweep = int(chunk), int(sweep)

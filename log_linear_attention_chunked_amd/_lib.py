@@ -77,6 +77,7 @@ class VarlenArgs(ctypes.Structure):
         ("lam", ctypes.c_void_p),
         ("out", ctypes.c_void_p),
         ("cu_seqlens", ctypes.c_void_p),
+        ("cu_seqlens_host", ctypes.c_void_p),
         ("N", ctypes.c_int),
         ("H", ctypes.c_int),
         ("total_T", ctypes.c_int),

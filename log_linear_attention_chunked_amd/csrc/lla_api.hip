@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+
+#include <algorithm>
 #include <string.h>
 
 #include "loglinear_attn.h"
@@ -140,7 +142,8 @@ hipError_t set_smem(const void* fn, int bytes) {
 // packed variable-length batch: N sequences of vH heads along T_packed rows
 struct Varlen {
   const int* cu_seqlens;
-  int vH, T_packed;
+  int vN, vH, T_packed;
+  int tickets;      // workgroups that have a sweep (from a host copy of cu_seqlens), or 0
 };
 
 int launch(const lla_fwd_args& a, const Plan& pl, void* ws, bool fresh_ws, hipStream_t stream,
@@ -168,7 +171,9 @@ int launch(const lla_fwd_args& a, const Plan& pl, void* ws, bool fresh_ws, hipSt
   if (vl) {
     p.T = vl->T_packed;
     p.cu_seqlens = vl->cu_seqlens;
+    p.vN = vl->vN;
     p.vH = vl->vH;
+    p.vtotal = vl->tickets;
   }
   void* args[] = {&p};
   auto mark = [&](int i) {
@@ -184,9 +189,9 @@ int launch(const lla_fwd_args& a, const Plan& pl, void* ws, bool fresh_ws, hipSt
     if (hipGetLastError() != hipSuccess) return LLA_ERR_HIP;
   }
   if (mark(1) != hipSuccess) return LLA_ERR_HIP;
-  const void* fn = ks->fwd[pl.R - 1];
+  const void* fn = vl ? ks->fwd_varlen[pl.R - 1] : ks->fwd[pl.R - 1];
   if (set_smem(fn, pl.smem) != hipSuccess) return LLA_ERR_HIP;
-  const unsigned grid = (unsigned)(pl.nsweep * pl.BH);
+  const unsigned grid = (unsigned)(vl && vl->tickets ? vl->tickets : pl.nsweep * pl.BH);
   if (hipLaunchKernel(fn, dim3(grid), dim3(64 * pl.nw), args, pl.smem, stream) != hipSuccess)
     return LLA_ERR_HIP;
   if (mark(2) != hipSuccess) return LLA_ERR_HIP;
@@ -230,7 +235,21 @@ int forward_varlen(const lla_fwd_varlen_args& v, hipStream_t stream) {
   st = validate_pointers(a, pp);
   if (st != LLA_OK) return st;
   if (!v.cu_seqlens || ((uintptr_t)v.cu_seqlens & 3)) return LLA_ERR_INVALID_ARG;
-  const Varlen vl{v.cu_seqlens, v.H, v.total_T};
+  Varlen vl{v.cu_seqlens, v.N, v.H, v.total_T, 0};
+  if (v.cu_seqlens_host) {
+    // the workgroups that have a sweep, with the kernel's clamping of each sequence
+    long long sweeps = 0;
+    const long long span = (long long)pl.nchunks * pl.C;
+    for (int n = 0; n < v.N; ++n) {
+      const long long s0 = std::min<long long>(std::max(v.cu_seqlens_host[n], 0), v.total_T);
+      const long long s1 = std::min<long long>(std::max<long long>(v.cu_seqlens_host[n + 1], s0),
+                                               std::min<long long>(s0 + span, v.total_T));
+      const long long nch = (s1 - s0 + pl.C - 1) / pl.C;
+      sweeps += (nch + pl.R - 1) / pl.R;
+    }
+    if (sweeps == 0) return LLA_OK;
+    vl.tickets = (int)(sweeps * v.H);
+  }
   return run_forward(a, pl, stream, &vl);
 }
 

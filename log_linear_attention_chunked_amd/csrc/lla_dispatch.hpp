@@ -4,7 +4,8 @@
 namespace lla {
 
 struct KernelSet {
-  const void* fwd[2];        // lla_fwd_kernel<T, C, DK, DV, NB> for NB = 1, 2 resident chunks
+  const void* fwd[2];        // lla_fwd_kernel<T, C, DK, DV, NB, false> for NB = 1, 2 resident chunks
+  const void* fwd_varlen[2]; // lla_fwd_kernel<T, C, DK, DV, NB, true>: variable-length batches
 };
 
 // dtype 0 = bf16, 1 = f32; C, DK, DV in {16, 32, 64, 128}; nullptr otherwise.

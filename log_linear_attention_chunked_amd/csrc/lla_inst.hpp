@@ -8,8 +8,10 @@ namespace lla {
 
 template <typename TY, int C, int DK, int DV>
 KernelSet make_set() {
-  return KernelSet{{reinterpret_cast<const void*>(&lla_fwd_kernel<TY, C, DK, DV, 1>),
-                    reinterpret_cast<const void*>(&lla_fwd_kernel<TY, C, DK, DV, 2>)}};
+  return KernelSet{{reinterpret_cast<const void*>(&lla_fwd_kernel<TY, C, DK, DV, 1, false>),
+                    reinterpret_cast<const void*>(&lla_fwd_kernel<TY, C, DK, DV, 2, false>)},
+                   {reinterpret_cast<const void*>(&lla_fwd_kernel<TY, C, DK, DV, 1, true>),
+                    reinterpret_cast<const void*>(&lla_fwd_kernel<TY, C, DK, DV, 2, true>)}};
 }
 
 template <typename TY, int C, int DK>

@@ -765,14 +765,114 @@ struct Params {
   int spin_limit;   // polls of a node flag before the wait is abandoned
   // Variable-length batches (cu_seqlens non-null): head index bh = n * vH + h is sequence n of
   // head h, positions [cu_seqlens[n], cu_seqlens[n+1]) of the packed [vH, T, .] tensors (T is
-  // then the packed length); nchunks and nsweep are those of the longest sequence.
+  // then the packed length); nchunks and nsweep are those of the longest sequence. Tickets
+  // enumerate only the (sweep, sequence, head) that exist; vtotal is their number when the
+  // host knows it (the grid), else 0 (the grid is vN * vH * nsweep and the surplus leaves).
   const int* cu_seqlens;
-  int vH;
+  int vH, vN, vtotal;
 };
 
 // Node flags, data and decays are indexed by (head, node = sweep index e, wave).
 __device__ __forceinline__ size_t node_slot(int bh, int ns, int e, int nw, int w) {
   return ((size_t)bh * ns + e) * nw + w;
+}
+
+// Variable-length batch: length of sequence n, clamped into the packed rows and to the longest
+// length the grid was sized for (as the kernel reads it), and its number of sweeps.
+template <int C, int NB>
+__device__ __forceinline__ int varlen_sweeps(const Params& p, int n) {
+  const int s0 = min(max(p.cu_seqlens[n], 0), p.T);
+  const int s1 = min(max(p.cu_seqlens[n + 1], s0), min(s0 + p.nchunks * C, p.T));
+  return cdiv(cdiv(s1 - s0, C), NB);
+}
+
+// Sum over the 64 lanes of a wave (DPP inclusive scan, read from the last lane): all lanes call.
+__device__ __forceinline__ int wave_sum_int(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);
+  return __builtin_amdgcn_readlane(x, 63);
+}
+
+// Variable-length batch: this workgroup's ticket, mapped sweep-major onto the (sweep, sequence,
+// head) that exist. Tickets t in [P(s), P(s+1)) belong to sweep s, P(s) = H sum_n min(nsw_n, s);
+// within a sweep, sequences in order, heads fastest. Wave 0 works it out (one sequence per lane,
+// a binary search over s) and hands it to the other waves through `tk` (4 words). Returns false
+// when the workgroup has no ticket and must leave at once; else sets the sweep, the virtual head
+// and the value of a published flag in this launch.
+template <int C, int NB>
+__device__ bool varlen_ticket(const Params& p, unsigned* tk, int tid, int blk, bool counted,
+                              int& sw, int& bh, int& flagv) {
+  if (tid < 64) {
+    const int lane = tid;
+    const int N = p.vN, H = p.vH;
+    const int own = lane < N ? varlen_sweeps<C, NB>(p, lane) : 0;     // sequences 0..63
+    auto P = [&](int s) {             // H * sum_n min(nsw_n, s)
+      int acc = min(own, s);
+      for (int n = 64 + lane; n - lane < N; n += 64) acc += n < N ? min(varlen_sweeps<C, NB>(p, n), s) : 0;
+      return H * wave_sum_int(acc);
+    };
+    const int total = P(p.nsweep);
+    bool ok = p.vtotal ? p.vtotal == total : blk < total;   // surplus workgroups, or a host count
+    int t = blk;                                             // that disagrees: nothing is drawn
+    unsigned ep = 0;
+    if (ok && counted) {
+      unsigned lo = 0, hi = 0;
+      if (lane == 0) {
+        unsigned long long* ctr = reinterpret_cast<unsigned long long*>(p.sync);
+        const unsigned long long old = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lo = (unsigned)old;
+        hi = (unsigned)(old >> 32);
+        if (lo == (unsigned)total - 1u) {            // epochs skip 2^32 - 1 (flag value 0)
+          const unsigned nep = hi + 1u == 0xffffffffu ? 0u : hi + 1u;
+          __hip_atomic_store(ctr, (unsigned long long)nep << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      const unsigned cnt = __builtin_amdgcn_readlane(lo, 0);
+      ep = __builtin_amdgcn_readlane(hi, 0);
+      ok = cnt < (unsigned)total;                    // false: a workspace never zero-filled
+      t = (int)cnt;
+    }
+    int s = 0, n = 0, h = 0;
+    if (ok) {
+      int lo = 0, hi = p.nsweep;                     // the largest s with P(s) <= t
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (P(mid) <= t) lo = mid; else hi = mid;
+      }
+      s = lo;
+      const int r = t - P(s);
+      int i = r / H;
+      h = r - i * H;
+      for (int b = 0; b * 64 < N; ++b) {             // the i-th sequence that has sweep s
+        const int m = b * 64 + lane;
+        const bool act = m < N && (b == 0 ? own : varlen_sweeps<C, NB>(p, m)) > s;
+        const unsigned long long mask = __ballot(act);
+        const int cnt = __popcll(mask);
+        if (i < cnt) {
+          const int rank = __builtin_amdgcn_mbcnt_hi((unsigned)(mask >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((unsigned)mask, 0u));
+          n = b * 64 + __ffsll((long long)__ballot(act && rank == i)) - 1;
+          break;
+        }
+        i -= cnt;
+      }
+    }
+    if (lane == 0) {
+      tk[0] = ok;
+      tk[1] = ep + 1u;
+      tk[2] = (unsigned)s;
+      tk[3] = (unsigned)(n * H + h);
+    }
+  }
+  __syncthreads();
+  flagv = (int)__builtin_amdgcn_readfirstlane(tk[1]);
+  sw = (int)__builtin_amdgcn_readfirstlane(tk[2]);
+  bh = (int)__builtin_amdgcn_readfirstlane(tk[3]);
+  return __builtin_amdgcn_readfirstlane(tk[0]) != 0;
 }
 
 // The forward pass: one workgroup per sweep of NB chunks of one head, one wave per 16 value
@@ -784,8 +884,9 @@ __device__ __forceinline__ size_t node_slot(int bh, int ns, int e, int nw, int w
 // H_e = sum_{s in sweep e} exp(A_end(e) - A_s) k_s v_s^T, gacc_i the log decay from the end of
 // node(e - 2^i) to the end of e. Sweep sw reads the nodes ending at ((sw >> j) << j) - 1 for
 // each set bit j of sw (level J + 1 + m + j); the first ctz(sw+1) of them are exactly the
-// children of its own node.
-template <typename T, int C, int DK, int DV, int NB>
+// children of its own node. VL: a variable-length batch (p.cu_seqlens), a separate instance so
+// that the fixed-length kernel carries none of its code.
+template <typename T, int C, int DK, int DV, int NB, bool VL>
 __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   constexpr int ES = (int)sizeof(T);
@@ -810,7 +911,12 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   // for every later launch without being cleared again.
   int t = blockIdx.x;
   int flagv = 1;                      // value of a published flag in this launch
-  if (ns > 0) {
+  int vsw = 0, vbh = 0;               // variable-length batch: the ticket's sweep and head
+  if constexpr (VL) {
+    if (!varlen_ticket<C, NB>(p, reinterpret_cast<unsigned*>(smem + S.ticket), tid, blockIdx.x, ns > 0,
+                              vsw, vbh, flagv))
+      return;
+  } else if (ns > 0) {
     const unsigned total = (unsigned)p.BH * (unsigned)p.nsweep;
     unsigned* tk = reinterpret_cast<unsigned*>(smem + S.ticket);
     if (tid == 0) {
@@ -830,12 +936,12 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
     if (cnt >= total) return;         // a workspace that was never zero-filled: touch nothing
     t = (int)cnt;
   }
-  const int sw = t / p.BH, bh = t - sw * p.BH;
+  const int sw = VL ? vsw : t / p.BH, bh = VL ? vbh : t - (t / p.BH) * p.BH;
 
   // this head's sequence: its length, first row in the tensors, chunk count
   int Tn = p.T, nchunks = p.nchunks;
   size_t hoff = (size_t)bh * p.T;
-  if (p.cu_seqlens) {
+  if constexpr (VL) {
     const int n = bh / p.vH, h = bh - n * p.vH;
     // clamped into the packed rows and to the longest length the grid was sized for
     const int s0 = min(max(p.cu_seqlens[n], 0), p.T);
@@ -843,8 +949,7 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
     Tn = s1 - s0;
     nchunks = cdiv(Tn, C);
     hoff = (size_t)h * p.T + s0;
-    if (sw * NB >= nchunks) return;   // shorter than the longest sequence: no such sweep, and
-  }                                   // no sweep of this head ever waits for one
+  }
 
   const T* qg = reinterpret_cast<const T*>(p.q) + hoff * DK;
   const T* kg = reinterpret_cast<const T*>(p.k) + hoff * DK;

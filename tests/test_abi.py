@@ -235,3 +235,12 @@ def test_varlen_validation_codes(L, kw, code):
 def test_varlen_empty_is_a_noop(L, kw):
     assert L.loglinear_attn_fwd_varlen(ctypes.byref(_vargs(**kw)), None) == _lib.LLA_OK
     assert L.loglinear_attn_fwd_varlen(None, None) == _lib.LLA_ERR_INVALID_ARG
+
+
+def test_varlen_host_copy_of_empty_sequences_launches_nothing(L):
+    # a host copy whose sequences are all empty: nothing to compute, so no kernel is launched
+    # (the fake device addresses are never touched)
+    host = (ctypes.c_int * 4)(0, 0, 0, 0)
+    a = _vargs()
+    a.cu_seqlens_host = ctypes.cast(host, ctypes.c_void_p).value
+    assert L.loglinear_attn_fwd_varlen(ctypes.byref(a), None) == _lib.LLA_OK
