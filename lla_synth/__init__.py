@@ -35,7 +35,7 @@ from dataclasses import dataclass, replace
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "num_levels_for", "generate", "workload"]
+__all__ = ["Workload", "WORKLOADS", "num_levels_for", "generate", "workload", "grad_output"]
 
 
 def num_levels_for(T: int) -> int:
@@ -156,6 +156,14 @@ def generate(w: Workload, seed: int = 0, *, log_a_mode: str | None = None,
         raise ValueError(f"unknown dtype {w.dtype!r}")
     return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(),
                 log_a=log_a.contiguous(), lam=lam.contiguous())
+
+
+def grad_output(w: Workload, seed: int = 0):
+    """A seeded upstream gradient dO ``[B,H,T,dv]`` for the backward pass: standard normal
+    entries, in q/k/v's dtype (CPU tensor)."""
+    g = torch.Generator("cpu").manual_seed(int(seed) + 7919)
+    do = torch.randn((w.B, w.H, w.T, w.dv), generator=g, dtype=torch.float32)
+    return do.to(torch.bfloat16 if w.dtype == "bf16" else torch.float32).contiguous()
 
 
 def custom(B: int, H: int, T: int, dk: int, dv: int, dtype: str = "bf16",

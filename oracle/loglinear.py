@@ -37,6 +37,11 @@ Functions:
   lay summary, "drawer" merging). It shares no helper with ``bruteforce``.
 * ``recurrent_step``    one step of that form (the decoding step): the states
   after t-1 and token t give the states after t and o_t.
+* ``bruteforce_grad``   the gradients of ``sum(do * o)`` with respect to q, k, v,
+  log_a and lambda: the derivative of the definition above, written out on the
+  dense O(T^2) matrices (the pages name the backward pass, and the lambda
+  gradient in particular, as the hard part of training: study notes, sections
+  3-5 and 4-5, and the discussion's point on engineering cost).
 
 Readings taken where the pages are silent are listed in the design doc and repeated
 at the functions that depend on them: 0-based positions, the bucket of s == t is
@@ -50,7 +55,7 @@ import numpy as np
 
 __all__ = [
     "bit_length", "level", "num_levels", "level_matrix", "as_f64",
-    "bruteforce", "bruteforce_rows", "recurrent", "recurrent_step",
+    "bruteforce", "bruteforce_rows", "recurrent", "recurrent_step", "bruteforce_grad",
 ]
 
 
@@ -250,3 +255,56 @@ def recurrent(q, k, v, log_a, lam) -> np.ndarray:
                 out[b, h, t] = recurrent_step(S, q[b, h, t], k[b, h, t], v[b, h, t],
                                               log_a[b, h, t], lam[b, h, t, :L], t)
     return out
+
+
+# ----------------------------------------------------------------------------
+# Gradients of the definition (the backward pass)
+# ----------------------------------------------------------------------------
+
+def bruteforce_grad(q, k, v, log_a, lam, do):
+    """Gradients of ``sum(do * o)`` for ``o = bruteforce(q, k, v, log_a, lam)``, fp64.
+
+    Per head, with ``D[t,s] = exp(A_t - A_s)`` (s <= t, else 0), the level
+    weights ``Lam[t,s] = lam[t, l(t,s)]``, the mask ``M = Lam * D``, the scores
+    ``S = Q K^T`` and ``W = dO V^T`` (so that ``o = (M * S) V``):
+
+        dq = (M * W) K          dk = (M * W)^T Q          dv = (M * S)^T dO
+        dlam[t, l] = sum over s with l(t,s) = l of D[t,s] S[t,s] W[t,s]
+        dA_t = sum_s G[t,s] - sum_t' G[t',t],  G = M * S * W
+        dlog_a[r] = sum_{t >= r} dA_t          (A_t = sum_{r <= t} log_a[r])
+
+    ``dA_t`` collects A_t's two roles in the decay: it is the later end of
+    every pair (t, s) and the earlier end of every pair (t', t). Levels that no
+    pair of a row reaches get 0. Returns ``dict(dq, dk, dv, dlog_a, dlam)``
+    shaped like the inputs. Builds T x T matrices: meant for T up to a few
+    thousand.
+    """
+    q, k, v, log_a, lam, do = (as_f64(x) for x in (q, k, v, log_a, lam, do))
+    B, H, T, dk, dv = _check_shapes(q, k, v, log_a, lam)
+    if do.shape != (B, H, T, dv):
+        raise ValueError(f"do shape {do.shape} != {(B, H, T, dv)}")
+    L = lam.shape[3]
+    g = {"dq": np.zeros_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v),
+         "dlog_a": np.zeros_like(log_a), "dlam": np.zeros_like(lam)}
+    if T == 0:
+        return g
+    ts = np.arange(T)
+    vis = _causal(ts, ts)
+    lv = np.where(vis, _levels(ts, ts), 0)
+    for b in range(B):
+        for h in range(H):
+            A = _prefix_log_decay(log_a[b, h])
+            D = np.where(vis, np.exp(np.where(vis, _pair_log_decay(A, ts, ts), -np.inf)), 0.0)
+            M = _mask_block(lam[b, h], A, ts, ts)
+            S = _scores(q[b, h], k[b, h], ts, ts)
+            W = do[b, h] @ v[b, h].T
+            g["dq"][b, h] = (M * W) @ k[b, h]
+            g["dk"][b, h] = (M * W).T @ q[b, h]
+            g["dv"][b, h] = (M * S).T @ do[b, h]
+            U = D * S * W                      # the lambda-free part of G, zero above the diagonal
+            for lev in range(L):
+                g["dlam"][b, h, :, lev] = np.where(lv == lev, U, 0.0).sum(axis=1)
+            G = M * S * W
+            dA = G.sum(axis=1) - G.sum(axis=0)
+            g["dlog_a"][b, h] = np.cumsum(dA[::-1])[::-1]
+    return g

@@ -414,3 +414,88 @@ def test_recurrent_step_state_blocks():
                 want[j + 1] += np.exp(A[t] - A[s]) * np.outer(k[s], v[s])
             hi = lo
     np.testing.assert_allclose(S, want, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# the backward pass: gradients of sum(do * o)
+# ---------------------------------------------------------------------------
+
+def _tiny_grad_case(seed, B=1, H=1, T=11, dk=3, dv=2):
+    rng = np.random.default_rng(seed)
+    L = O.num_levels(T)
+    return dict(q=rng.normal(size=(B, H, T, dk)), k=rng.normal(size=(B, H, T, dk)),
+                v=rng.normal(size=(B, H, T, dv)), log_a=-rng.uniform(0.05, 0.6, size=(B, H, T)),
+                lam=rng.uniform(0.2, 1.5, size=(B, H, T, L))), rng.normal(size=(B, H, T, dv))
+
+
+def test_grad_matches_central_differences():
+    # every input element: d/dx sum(do * bruteforce(x)) by central differences of the
+    # forward definition, which is pinned on its own above
+    x, do = _tiny_grad_case(1)
+    g = O.bruteforce_grad(**x, do=do)
+    loss = lambda xx: float(np.sum(do * O.bruteforce(**xx)))
+    eps = 1e-6
+    for name, key in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("log_a", "dlog_a"), ("lam", "dlam")):
+        fd = np.zeros_like(x[name])
+        for idx in np.ndindex(x[name].shape):
+            xp = {n: a.copy() for n, a in x.items()}
+            xm = {n: a.copy() for n, a in x.items()}
+            xp[name][idx] += eps
+            xm[name][idx] -= eps
+            fd[idx] = (loss(xp) - loss(xm)) / (2 * eps)
+        err = np.abs(fd - g[key]).max() / max(np.abs(fd).max(), 1e-30)
+        assert err < 1e-7, (name, err)
+
+
+def test_grad_matches_autograd_of_a_dense_formula():
+    # CPU float64 autograd through the definition built pair by pair (a Python loop over
+    # (t, s), no helper of the oracle), at a size with several levels and two heads
+    import torch
+    x, do = _tiny_grad_case(2, B=1, H=2, T=37, dk=4, dv=3)
+    tx = {n: torch.tensor(a, dtype=torch.float64, requires_grad=True) for n, a in x.items()}
+    T = x["q"].shape[2]
+    A = torch.cumsum(tx["log_a"], dim=-1)
+    outs = []
+    for t in range(T):
+        acc = 0.0
+        for s in range(t + 1):
+            lev = (t ^ s).bit_length()
+            w = tx["lam"][..., t, lev] * torch.exp(A[..., t] - A[..., s])
+            qk = (tx["q"][..., t, :] * tx["k"][..., s, :]).sum(-1)
+            acc = acc + (w * qk)[..., None] * tx["v"][..., s, :]
+        outs.append(acc)
+    o = torch.stack(outs, dim=-2)
+    (o * torch.tensor(do)).sum().backward()
+    g = O.bruteforce_grad(**x, do=do)
+    for name, key in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("log_a", "dlog_a"), ("lam", "dlam")):
+        ref = tx[name].grad.numpy()
+        assert np.allclose(g[key], ref, rtol=1e-10, atol=1e-12), name
+
+
+def test_grad_structural_zeros():
+    # log_a[0] shifts every A_t alike, so no decay depends on it: its gradient is 0;
+    # lambda[t, l] for a level that t never reaches (l > 0 with bit l-1 of t clear) gets 0
+    x, do = _tiny_grad_case(3, B=2, H=1, T=70, dk=5, dv=4)
+    g = O.bruteforce_grad(**x, do=do)
+    scale = np.abs(g["dlog_a"]).max()
+    assert np.all(np.abs(g["dlog_a"][..., 0]) <= 1e-12 * scale)
+    T, L = 70, x["lam"].shape[-1]
+    for t in range(T):
+        for lev in range(1, L):
+            if not (t >> (lev - 1)) & 1:
+                assert np.all(g["dlam"][:, :, t, lev] == 0.0), (t, lev)
+    assert np.all(g["dlam"][..., 0] != 0.0)
+
+
+def test_grad_of_plain_causal_linear_attention():
+    # lambda = 1 on every level and no decay: o = causal (Q K^T) V, whose gradients are
+    # the textbook ones, written here with the lower-triangular mask
+    x, do = _tiny_grad_case(4, T=29, dk=3, dv=5)
+    x["lam"][:] = 1.0
+    x["log_a"][:] = 0.0
+    g = O.bruteforce_grad(**x, do=do)
+    q, k, v, d = x["q"][0, 0], x["k"][0, 0], x["v"][0, 0], do[0, 0]
+    Mc = np.tril(np.ones((29, 29)))
+    assert np.allclose(g["dq"][0, 0], (Mc * (d @ v.T)) @ k)
+    assert np.allclose(g["dk"][0, 0], (Mc * (d @ v.T)).T @ q)
+    assert np.allclose(g["dv"][0, 0], (Mc * (q @ k.T)).T @ d)
