@@ -405,7 +405,7 @@ def _kernel_sha() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "log_linear_attention_chunked_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp")) and f != "lla_decode.hip":
+        if f.endswith((".hip", ".hpp")) and f != "lla_decode.hip" and not f.startswith("lla_bwd"):
             h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 

@@ -237,6 +237,65 @@ typedef struct lla_decode_args {
 
 int loglinear_attn_decode_step(const lla_decode_args* args, lla_stream_t stream);
 
+/*
+ * loglinear_attn_bwd — the backward pass: gradients of sum(grad_out * o) with respect to every
+ * input of the forward operation above (the study notes name training speed and the gradient of
+ * the level weights as the hard part of the method, sections 3-5 and 4-5). Per head, with
+ * M[t,s] = lambda[t, l(t,s)] * exp(A_t - A_s) for s <= t, S[t,s] = q_t . k_s and
+ * W[t,s] = grad_out_t . v_s:
+ *   grad_q_t = sum_s M W k_s      grad_k_s = sum_t M W q_t      grad_v_s = sum_t M S grad_out_t
+ *   grad_lambda[t, l] = sum over the s with l(t,s) = l of exp(A_t - A_s) S W  (0 for a level no
+ *                       pair of row t reaches)
+ *   grad_log_a[r] = sum_{t >= r} (q_t . grad_q_t - k_t . grad_k_t)
+ *
+ *   q, k [B,H,T,dk]  v, grad_out [B,H,T,dv]  bfloat16 (LLA_DTYPE_BF16) or float32, all alike
+ *   log_a [B,H,T], lambda [B,H,T,L] float32, L = loglinear_attn_num_levels(T)
+ *   grad_q, grad_k [B,H,T,dk], grad_v [B,H,T,dv] in q's dtype; grad_log_a [B,H,T] and
+ *   grad_lambda [B,H,T,L] float32. All outputs are fully overwritten, never accumulated into.
+ *   chunk : 0 = library default (loglinear_attn_bwd_default_chunk), else 16, 32 or 64
+ *           (LLA_ERR_UNSUPPORTED when the gradient kernel's shared memory would exceed 160 KB).
+ *   workspace / workspace_bytes : caller device memory of at least
+ *           loglinear_attn_bwd_workspace_bytes(...) bytes (256-byte aligned; no clearing needed:
+ *           every byte read was written earlier in the same call), or NULL/0 to let the library
+ *           take it stream-ordered on `stream`. It holds the chunk-level Fenwick nodes, their
+ *           log decays, the per-level partial states of the target side and the per-position
+ *           dA of the running call, so calls that may run concurrently must not share it.
+ *   stage_events : optional hipEvent_t the library records on `stream`: [0] before the chunk
+ *           states, [1] before the gradient kernel, [2] after it, [3] after the grad_log_a scan.
+ * Pointers are device pointers; q, k, v, grad_out 16-byte aligned, the float arrays 4-byte
+ * aligned; no output may overlap an input or another output (LLA_ERR_INVALID_ARG). Supported
+ * shapes as for the forward pass (dk, dv in {16,32,64,128}, T < 2^23, B*H <= 65535).
+ * Asynchronous on `stream`, bitwise deterministic, returns LLA_OK or a negative LLA_ERR_*.
+ */
+typedef struct lla_bwd_args {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_a;
+  const float* lambda;
+  const void* grad_out;
+  void* grad_q;
+  void* grad_k;
+  void* grad_v;
+  float* grad_log_a;
+  float* grad_lambda;
+  int B, H, T, dk, dv;
+  int dtype;                  /* enum lla_dtype */
+  int chunk;
+  void* workspace;
+  size_t workspace_bytes;
+  void* stage_events[4];      /* hipEvent_t or NULL */
+} lla_bwd_args;
+
+int loglinear_attn_bwd(const lla_bwd_args* args, lla_stream_t stream);
+
+/* Bytes of workspace loglinear_attn_bwd needs (0 for invalid or unsupported arguments). */
+size_t loglinear_attn_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
+                                          int dtype);
+
+/* Chunk size loglinear_attn_bwd uses when chunk is 0 (0 for unsupported arguments). */
+int loglinear_attn_bwd_default_chunk(int dk, int dv, int dtype);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,7 +1,8 @@
 """Log-linear Mamba-2 attention forward pass on MI355X (gfx950), behind a C ABI.
 
-    from log_linear_attention_chunked_amd import forward
+    from log_linear_attention_chunked_amd import forward, backward
     out = forward(q, k, v, log_a, lam)          # device tensors, [B,H,T,d] layout
+    dq, dk, dv, dlog_a, dlam = backward(q, k, v, log_a, lam, dout)
 
 Computes, per head, o_t = sum_{s<=t} lam[t, l(t,s)] * prod_{r=s+1..t} a_r * (q_t.k_s) v_s
 with l(t,s) = bit_length(t XOR s) (Fenwick level) and a_r = exp(log_a[r]).
@@ -16,7 +17,7 @@ import ctypes
 from . import _lib
 from ._lib import LibraryNotBuilt  # noqa: F401
 
-__all__ = ["forward", "forward_varlen", "decode_step", "new_decode_cache", "num_levels", "workspace_bytes",
+__all__ = ["forward", "backward", "bwd_workspace_bytes", "bwd_default_chunk", "forward_varlen", "decode_step", "new_decode_cache", "num_levels", "workspace_bytes",
            "default_chunk", "default_sweep", "LLAError", "LibraryNotBuilt"]
 
 
@@ -227,4 +228,71 @@ def forward_varlen(q, k, v, log_a, lam, cu_seqlens, max_T: int, out=None, *, chu
     st = _lib.lib().loglinear_attn_fwd_varlen(ctypes.byref(a), ctypes.c_void_p(handle))
     if st != _lib.LLA_OK:
         raise LLAError(st, "loglinear_attn_fwd_varlen")
+    return out
+
+
+def bwd_workspace_bytes(B, H, T, dk, dv, chunk=0, dtype="bf16") -> int:
+    return int(_lib.lib().loglinear_attn_bwd_workspace_bytes(
+        int(B), int(H), int(T), int(dk), int(dv), int(chunk), _dtype_code(dtype)))
+
+
+def bwd_default_chunk(dk, dv, dtype="bf16") -> int:
+    return _lib.lib().loglinear_attn_bwd_default_chunk(int(dk), int(dv), _dtype_code(dtype))
+
+
+def backward(q, k, v, log_a, lam, dout, *, chunk: int = 0, workspace=None, stream=None,
+             stage_events=None, out=None):
+    """Backward pass: gradients of ``sum(dout * forward(q, k, v, log_a, lam))``.
+
+    Inputs as for ``forward`` plus ``dout`` [B,H,T,dv] in q's dtype. Returns
+    ``(dq, dk, dv, dlog_a, dlam)``: dq, dk [B,H,T,dk] and dv [B,H,T,dv] in q's dtype,
+    dlog_a [B,H,T] and dlam [B,H,T,L] float32. ``out``: optional tuple of those five
+    tensors to write into. ``chunk`` 0 = library default (16, 32 or 64); ``workspace``:
+    optional uint8 device tensor of >= bwd_workspace_bytes(...) bytes. ``stage_events``:
+    up to 4 ``torch.cuda.Event`` (or None) recorded before the chunk states, before and
+    after the gradient kernel, and after the log_a scan.
+    """
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, dk]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = num_levels(T) if T > 0 else 0
+    _check(q, "q", q.dtype, (B, H, T, dk))
+    _check(k, "k", q.dtype, (B, H, T, dk))
+    _check(v, "v", q.dtype, (B, H, T, dv))
+    _check(log_a, "log_a", torch.float32, (B, H, T))
+    _check(lam, "lam", torch.float32, (B, H, T, L))
+    _check(dout, "dout", q.dtype, (B, H, T, dv))
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+               torch.empty_like(log_a), torch.empty_like(lam))
+    gq, gk, gv, gla, glam = out
+    _check(gq, "dq", q.dtype, (B, H, T, dk))
+    _check(gk, "dk", q.dtype, (B, H, T, dk))
+    _check(gv, "dv", q.dtype, (B, H, T, dv))
+    _check(gla, "dlog_a", torch.float32, (B, H, T))
+    _check(glam, "dlam", torch.float32, (B, H, T, L))
+    a = _lib.BwdArgs()
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.log_a, a.lam, a.grad_out = log_a.data_ptr(), lam.data_ptr(), dout.data_ptr()
+    a.grad_q, a.grad_k, a.grad_v = gq.data_ptr(), gk.data_ptr(), gv.data_ptr()
+    a.grad_log_a, a.grad_lam = gla.data_ptr(), glam.data_ptr()
+    a.B, a.H, a.T, a.dk, a.dv = int(B), int(H), int(T), int(dk), int(dv)
+    a.dtype = _dtype_code(q.dtype)
+    a.chunk = int(chunk)
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8, (workspace.numel(),))
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    else:
+        a.workspace, a.workspace_bytes = None, 0
+    if stage_events is not None:
+        for i, ev in enumerate(stage_events):
+            a.stage_events[i] = ev.cuda_event if ev is not None else None
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = _lib.lib().loglinear_attn_bwd(ctypes.byref(a), ctypes.c_void_p(handle))
+    if st != _lib.LLA_OK:
+        raise LLAError(st, "loglinear_attn_bwd")
     return out

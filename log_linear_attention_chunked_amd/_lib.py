@@ -37,6 +37,9 @@ EXPORTS = (
     "loglinear_attn_status_string",
     "loglinear_attn_decode_step",
     "loglinear_attn_fwd_varlen",
+    "loglinear_attn_bwd",
+    "loglinear_attn_bwd_workspace_bytes",
+    "loglinear_attn_bwd_default_chunk",
 )
 
 
@@ -113,6 +116,33 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class BwdArgs(ctypes.Structure):
+    """Mirror of ``lla_bwd_args``."""
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("log_a", ctypes.c_void_p),
+        ("lam", ctypes.c_void_p),
+        ("grad_out", ctypes.c_void_p),
+        ("grad_q", ctypes.c_void_p),
+        ("grad_k", ctypes.c_void_p),
+        ("grad_v", ctypes.c_void_p),
+        ("grad_log_a", ctypes.c_void_p),
+        ("grad_lam", ctypes.c_void_p),
+        ("B", ctypes.c_int),
+        ("H", ctypes.c_int),
+        ("T", ctypes.c_int),
+        ("dk", ctypes.c_int),
+        ("dv", ctypes.c_int),
+        ("dtype", ctypes.c_int),
+        ("chunk", ctypes.c_int),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("stage_events", ctypes.c_void_p * 4),
+    ]
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -139,6 +169,12 @@ def _declare(lib):
     lib.loglinear_attn_decode_step.restype = i
     lib.loglinear_attn_fwd_varlen.argtypes = [ctypes.POINTER(VarlenArgs), vp]
     lib.loglinear_attn_fwd_varlen.restype = i
+    lib.loglinear_attn_bwd.argtypes = [ctypes.POINTER(BwdArgs), vp]
+    lib.loglinear_attn_bwd.restype = i
+    lib.loglinear_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.loglinear_attn_bwd_workspace_bytes.restype = sz
+    lib.loglinear_attn_bwd_default_chunk.argtypes = [i, i, i]
+    lib.loglinear_attn_bwd_default_chunk.restype = i
 
 
 def lib():

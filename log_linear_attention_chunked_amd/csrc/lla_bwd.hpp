@@ -1,0 +1,641 @@
+// lla_bwd.hpp — gfx950 backward pass of chunkwise log-linear Mamba-2 attention.
+//
+// Gradients of L = sum_t do_t . o_t for the forward operation
+//   o_t = sum_{s<=t} lambda[t, l(t,s)] * exp(A_t - A_s) * (q_t . k_s) * v_s,  l = bit_length(t ^ s).
+// ("Log-Linear Attention": the pages name training speed and the lambda gradient as the hard
+// part of the backward pass, study notes sections 3-5 and 4-5.) With M[t,s] the mask weight
+// lambda * exp(A_t - A_s), S = q.k and W[t,s] = do_t . v_s:
+//   dq_t = sum_s M W k_s        dk_s = sum_t M W q_t        dv_s = sum_t M S do_t
+//   dlambda[t, l] = sum_{s : l(t,s) = l} exp(A_t - A_s) S W
+//   dA_t = q_t . dq_t - k_t . dk_t,   dlog_a[r] = sum_{t >= r} dA_t
+// (A_t is the later end of every pair (t, s) and the earlier end of every pair (t', t); summing
+// M S W over either index gives the two dot products.)
+//
+// Chunk structure (chunk C = 2^J, N chunks, chunk levels j = 0 .. nl-1, nl = bit_length(N-1)).
+// For t in chunk c and s in an earlier chunk c', l(t,s) = J + 1 + j with j the highest bit of
+// c ^ c'. The query side is the forward pass's: target c reads, for each set bit j, the Fenwick
+// node (j, (c >> j) - 1) = sum_{s in block} exp(A_end - A_s) k_s v_s^T, decayed over the blocks
+// of c's lower set bits. The source side is its mirror image: source chunk c receives, for each
+// clear bit j, the right sibling block Y = (j, (c >> j) + 1) through
+//   RN(j, Y) = sum_{t in Y} lambda[t, J+1+j] exp(A_t - A_start(Y)) q_t do_t^T,
+// decayed over the right siblings of c's lower clear bits. lambda sits on the target here, so
+// RN cannot be built from the blocks below it like a forward node: each chunk contributes one
+// partial Z(c, j) per set bit j, and the partials are summed per block.
+//
+// Kernels, in stream order (bwd_gsum, bwd_tree and bwd_dloga, which do not depend on the element
+// type or the shapes, live in lla_bwd_api.hip):
+//   bwd_states  (chunk, head): F(c) = sum_s exp(g_c - A_s) k_s v_s^T (tree slot (0, c)),
+//               g_c, and Z(c, j) for the set bits j of c, on MFMA;
+//   bwd_gsum    (head): total log decay of every block (j, m), pairwise from the chunks;
+//   bwd_tree    (64 state elements, head): per block level i = 1 .. nl-1, the forward up-sweep
+//               node(i,m) = exp(G(i-1,2m+1)) node(i-1,2m) + node(i-1,2m+1) and, in place in the
+//               Z slots, the sums of the partials inside the odd blocks of every level j >= i;
+//   bwd_grads   (chunk, head): intra-chunk gradients on MFMA (masked S and W tiles, dlambda of
+//               the levels inside the chunk), node read-outs for dq and dlambda, the combined
+//               right-sibling state for dk and dv, dA;
+//   bwd_dloga   (head): dlog_a as the reverse prefix sum of dA.
+// Every sum runs in a fixed order: the gradients are bitwise deterministic.
+//
+// MFMA conventions as in the forward kernels: 16x16 output tiles, lane (j = lane & 15,
+// g = lane >> 4) holds rows 4g..4g+3 of column j; a K = 32 operand fragment gives lane (j, g)
+// the contraction indices 8g..8g+7 of its row j. Here every product is written
+// out[m][n] = sum_k A[m][k] Bt[n][k], with both operands read by row m (n) and index k.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lla_kernels.hpp"
+
+namespace lla {
+namespace bwd {
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* log_a;
+  const float* lam;
+  void* gq;
+  void* gk;
+  void* gv;
+  float* glog_a;
+  float* glam;
+  float* node;    // [BH][nslot][dk*dv]: forward Fenwick nodes over chunks, all block levels
+  float* gsum;    // [BH][nslot]: total log decay of each block
+  float* z;       // [BH][N][nl][dk*dv]: partials Z(c, j); after bwd_tree Z(start of Y, j) = RN(j, Y)
+  float* dA;      // [BH][T]
+  int BH, T, L, N, nl, nslot;
+};
+
+// slot of block (i, m) in the per-head tree: blocks of level i' < i come first
+__host__ __device__ inline int slot_of(int N, int i, int m) {
+  int o = 0;
+  for (int a = 0; a < i; ++a) o += (N + (1 << a) - 1) >> a;
+  return o + m;
+}
+
+// shared-memory layout of bwd_states / bwd_grads (host and device agree)
+struct BwdSmem {
+  int q, k, v, o, p1, p2, u, lam, al, ea, ws, dli, rs, total;
+};
+__host__ __device__ inline BwdSmem bwd_smem(int es, int C, int DK, int DV, bool grads) {
+  BwdSmem s{};
+  int off = 0;
+  auto take = [&](int bytes) { const int o = off; off += (bytes + 15) & ~15; return o; };
+  const int rk = DK + 16 / es, rv = DV + 16 / es, rc = C + 16 / es;
+  s.q = take(C * rk * es);
+  s.k = take(C * rk * es);
+  s.v = take(C * rv * es);
+  s.o = take(C * rv * es);
+  s.p1 = grads ? take(C * rc * es) : off;
+  s.p2 = grads ? take(C * rc * es) : off;
+  s.u = grads ? take(C * (C + 1) * 4) : off;
+  s.lam = take(C * kLamCap * 4);
+  s.al = take(C * 4);
+  s.ea = take(C * 4);
+  s.ws = take(C * 4);
+  s.dli = grads ? take(C * kLamCap * 4) : off;
+  s.rs = grads ? take(kLamCap * 12 + 16) : off;
+  s.total = (off + 255) & ~255;
+  return s;
+}
+
+template <int C>
+struct Waves {
+  static constexpr int NW = C >= 64 ? 4 : C / 16;   // waves per workgroup
+  static constexpr int RB = C / 16 / NW;             // 16-row blocks of positions per wave
+};
+
+// ----------------------------------------------------------------------------------------
+// fragments
+// ----------------------------------------------------------------------------------------
+
+template <typename T> __device__ __forceinline__ float to_f(T x) { return (float)x; }
+
+// X[r][k .. k+7] of a row-major shared-memory image with row stride RS (k a multiple of 8);
+// indices at or past K read as zero
+template <typename T, int K>
+__device__ __forceinline__ Frag<T> frag_row(const T* img, int RS, int r, int k) {
+  if (k >= K) return zero_frag<T>();
+  const T* p = img + r * RS + k;
+  if constexpr (sizeof(T) == 2) {
+    Frag<T> f;
+    f.v = *reinterpret_cast<const bf16x8*>(p);
+    return f;
+  } else {
+    Frag<T> f;
+    f.lo = *reinterpret_cast<const f32x4*>(p);
+    f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+    return f;
+  }
+}
+
+// X[k .. k+7][c] (a column of the image), each element times sc[k + e] when sc is given
+template <typename T, int K>
+__device__ __forceinline__ Frag<T> frag_col(const T* img, int RS, int k, int c,
+                                            const float* sc = nullptr) {
+  if (k >= K) return zero_frag<T>();
+  f32x4 lo, hi;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lo[e] = to_f(img[(k + e) * RS + c]);
+    hi[e] = to_f(img[(k + 4 + e) * RS + c]);
+  }
+  if (sc) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo[e] *= sc[k + e];
+      hi[e] *= sc[k + 4 + e];
+    }
+  }
+  return frag_from<T>(lo, hi);
+}
+
+// a row-major float state in global memory, g[r][k .. k+7] (row stride RS), as an operand
+template <typename T, int K>
+__device__ __forceinline__ Frag<T> frag_grow(const float* g, int RS, int r, int k) {
+  if (k >= K) return zero_frag<T>();
+  const float* p = g + (size_t)r * RS + k;
+  const f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
+  return frag_from<T>(lo, hi);
+}
+
+// sum over 16 lanes of the same group (lane & 15 varies): xor shuffles inside the group
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 8);
+  return x;
+}
+
+// kernel table of one (dtype, chunk, dk, dv)
+struct BwdKernels {
+  const void* states;   // bwd_states_kernel<T, C, DK, DV>
+  const void* grads;    // bwd_grads_kernel<T, C, DK, DV>
+};
+
+// per (dtype, chunk) tables, one instantiation unit each; nullptr outside {16,32,64,128}
+const BwdKernels* bwd_kernels_bf16_c16(int DK, int DV);
+const BwdKernels* bwd_kernels_bf16_c32(int DK, int DV);
+const BwdKernels* bwd_kernels_bf16_c64(int DK, int DV);
+const BwdKernels* bwd_kernels_f32_c16(int DK, int DV);
+const BwdKernels* bwd_kernels_f32_c32(int DK, int DV);
+const BwdKernels* bwd_kernels_f32_c64(int DK, int DV);
+
+// ----------------------------------------------------------------------------------------
+// shared staging of one chunk: q, k, v, do images, lambda rows, decays
+// ----------------------------------------------------------------------------------------
+
+template <typename T, int C, int DK, int DV>
+struct Chunk {
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int RK = DK + 16 / ES, RV = DV + 16 / ES;
+  T *q, *k, *v, *o;
+  float *lam, *al, *ea, *ws;
+  float g;   // total log decay of the chunk
+
+  __device__ void bind(unsigned char* sm, const BwdSmem& L) {
+    q = reinterpret_cast<T*>(sm + L.q);
+    k = reinterpret_cast<T*>(sm + L.k);
+    v = reinterpret_cast<T*>(sm + L.v);
+    o = reinterpret_cast<T*>(sm + L.o);
+    lam = reinterpret_cast<float*>(sm + L.lam);
+    al = reinterpret_cast<float*>(sm + L.al);
+    ea = reinterpret_cast<float*>(sm + L.ea);
+    ws = reinterpret_cast<float*>(sm + L.ws);
+  }
+
+  // rows [0, nv) from the head's tensors starting at row p0; rows past nv are zero
+  template <int D>
+  __device__ static void stage(T* img, const T* __restrict__ g, int nv, int tid, int nt) {
+    constexpr int EPV = 16 / ES, NV = D / EPV, RS = D + 16 / ES;
+    for (int idx = tid; idx < C * NV; idx += nt) {
+      const int r = idx / NV, c = (idx % NV) * EPV;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (r < nv) x = *reinterpret_cast<const u32x4*>(g + (size_t)r * D + c);
+      *reinterpret_cast<u32x4*>(img + r * RS + c) = x;
+    }
+  }
+
+  // everything of chunk c of head bh; ends with a barrier. A = chunk-local inclusive prefix of
+  // log_a, ea = exp(A), ws = exp(g - A) (decay from a position to the chunk's end).
+  __device__ void load(const BwdParams& p, int bh, int c, int nv, int tid, int nt) {
+    const size_t row0 = (size_t)bh * p.T + (size_t)c * C;
+    stage<DK>(q, reinterpret_cast<const T*>(p.q) + row0 * DK, nv, tid, nt);
+    stage<DK>(k, reinterpret_cast<const T*>(p.k) + row0 * DK, nv, tid, nt);
+    stage<DV>(v, reinterpret_cast<const T*>(p.v) + row0 * DV, nv, tid, nt);
+    stage<DV>(o, reinterpret_cast<const T*>(p.dout) + row0 * DV, nv, tid, nt);
+    // every level slot is written: rows past nv and levels past L read as zero weights
+    const float* lg = p.lam + row0 * p.L;
+    for (int i = tid; i < C * kLamCap; i += nt) {
+      const int r = i / kLamCap, l = i % kLamCap;
+      lam[i] = (r < nv && l < p.L) ? lg[r * p.L + l] : 0.f;
+    }
+    // chunk-local inclusive prefix of log_a by wave 0: each lane holds E consecutive rows
+    if (tid < 64) {
+      constexpr int E = C > 64 ? C / 64 : 1;
+      float x[E], run = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int r = tid * E + e;
+        x[e] = (r < C && r < nv) ? p.log_a[row0 + r] : 0.f;
+        run += x[e];
+        x[e] = run;
+      }
+      float incl = run;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_up(incl, d);
+        if (tid >= d) incl += y;
+      }
+      const float excl = incl - run;
+      const float tot = __shfl(incl, 63);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int r = tid * E + e;
+        if (r < C) {
+          const float a = excl + x[e];
+          al[r] = a;
+          ea[r] = __expf(a);
+          ws[r] = __expf(tot - a);
+        }
+      }
+    }
+    __syncthreads();
+    g = al[C - 1];
+  }
+};
+
+// ----------------------------------------------------------------------------------------
+// bwd_states: chunk state F(c) and the right-block partials Z(c, j)
+// ----------------------------------------------------------------------------------------
+
+// out[a][b] = sum_s X[s][a] * sc[s] * Y[s][b] over the chunk's positions (a < DA, b < DB),
+// stored row-major into dst (fp32); wave w takes 16-row blocks of a = w, w + NW, ...
+template <typename T, int C, int DA, int DB, int NW>
+__device__ __forceinline__ void outer_store(const T* X, int RX, const T* Y, int RY, const float* sc,
+                                            float* __restrict__ dst, int w, int lane) {
+  const int j = lane & 15, g = lane >> 4;
+  for (int ab = w; ab < DA / 16; ab += NW) {
+#pragma unroll
+    for (int bb = 0; bb < DB / 16; ++bb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s0 = 0; s0 < C; s0 += 32) {
+        const Frag<T> a = frag_col<T, C>(X, RX, s0 + 8 * g, ab * 16 + j);
+        const Frag<T> b = frag_col<T, C>(Y, RY, s0 + 8 * g, bb * 16 + j, sc);
+        mma(acc, a, b);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(size_t)(ab * 16 + 4 * g + r) * DB + bb * 16 + j] = acc[r];
+    }
+  }
+}
+
+template <typename T, int C, int DK, int DV>
+__global__ void __launch_bounds__(64 * Waves<C>::NW)
+bwd_states_kernel(BwdParams p) {
+  constexpr int NW = Waves<C>::NW, NT = 64 * NW, J = ilog2(C);
+  extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int nv = min(C, p.T - c * C);
+  const BwdSmem Lo = bwd_smem((int)sizeof(T), C, DK, DV, false);
+  Chunk<T, C, DK, DV> ch;
+  ch.bind(sm, Lo);
+  ch.load(p, bh, c, nv, tid, NT);
+  using CH = Chunk<T, C, DK, DV>;
+
+  const size_t SZ = (size_t)DK * DV;
+  // F(c): keys weighted by their decay to the chunk's end
+  outer_store<T, C, DK, DV, NW>(ch.k, CH::RK, ch.v, CH::RV, ch.ws,
+                                p.node + ((size_t)bh * p.nslot + c) * SZ, w, lane);
+  if (tid == 0) p.gsum[(size_t)bh * p.nslot + c] = ch.g;
+
+  // Z(c, j) for each set bit j of c: targets weighted by lambda of level J+1+j and exp(A)
+  float* sc = ch.ws;   // reused as the per-position weight once F is done
+  for (int jl = 0; jl < p.nl; ++jl) {
+    if (!((c >> jl) & 1)) continue;
+    __syncthreads();
+    for (int r = tid; r < C; r += NT) sc[r] = ch.lam[r * kLamCap + J + 1 + jl] * ch.ea[r];
+    __syncthreads();
+    outer_store<T, C, DK, DV, NW>(ch.q, CH::RK, ch.o, CH::RV, sc,
+                                  p.z + (((size_t)bh * p.N + c) * p.nl + jl) * SZ, w, lane);
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// bwd_grads: all gradients of one chunk
+// ----------------------------------------------------------------------------------------
+
+template <typename T, int C, int DK, int DV>
+__global__ void __launch_bounds__(64 * Waves<C>::NW)
+bwd_grads_kernel(BwdParams p) {
+  constexpr int NW = Waves<C>::NW, RB = Waves<C>::RB, NT = 64 * NW, J = ilog2(C);
+  constexpr int ES = (int)sizeof(T), RC = C + 16 / ES;
+  constexpr int NK = DK / 16, NV = DV / 16;
+  using CH = Chunk<T, C, DK, DV>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, jj = lane & 15, g4 = lane >> 4;
+  const int nv = min(C, p.T - c * C);
+  const BwdSmem Lo = bwd_smem(ES, C, DK, DV, true);
+  CH ch;
+  ch.bind(sm, Lo);
+  T* P1 = reinterpret_cast<T*>(sm + Lo.p1);     // M * W  [i][j]
+  T* P2 = reinterpret_cast<T*>(sm + Lo.p2);     // M * S  [i][j]
+  float* U = reinterpret_cast<float*>(sm + Lo.u);      // exp(A_i - A_j) S W  [i][j], stride C+1
+  float* dli = reinterpret_cast<float*>(sm + Lo.dli);  // dlambda of the levels J+1+j  [i][j]
+  ch.load(p, bh, c, nv, tid, NT);
+  const size_t SZ = (size_t)DK * DV;
+  const size_t row0 = (size_t)bh * p.T + (size_t)c * C;
+
+  // 1. masked score tiles: wave w takes 16-row blocks rb = w + NW*x of query positions i
+  for (int x = 0; x < RB; ++x) {
+    const int rb = w + NW * x;
+#pragma unroll
+    for (int cb = 0; cb < C / 16; ++cb) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f}, wv = {0.f, 0.f, 0.f, 0.f};
+      if (cb <= rb) {
+#pragma unroll
+        for (int a0 = 0; a0 < DK; a0 += 32)
+          mma(s, frag_row<T, DK>(ch.q, CH::RK, rb * 16 + jj, a0 + 8 * g4),
+              frag_row<T, DK>(ch.k, CH::RK, cb * 16 + jj, a0 + 8 * g4));
+#pragma unroll
+        for (int b0 = 0; b0 < DV; b0 += 32)
+          mma(wv, frag_row<T, DV>(ch.o, CH::RV, rb * 16 + jj, b0 + 8 * g4),
+              frag_row<T, DV>(ch.v, CH::RV, cb * 16 + jj, b0 + 8 * g4));
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = rb * 16 + 4 * g4 + r, j = cb * 16 + jj;
+        float p1 = 0.f, p2 = 0.f, u = 0.f;
+        if (j <= i) {
+          const float d = __expf(ch.al[i] - ch.al[j]);
+          const float m = ch.lam[i * kLamCap + bit_length((unsigned)(i ^ j))] * d;
+          p1 = m * wv[r];
+          p2 = m * s[r];
+          u = d * s[r] * wv[r];
+        }
+        P1[i * RC + j] = (T)p1;
+        P2[i * RC + j] = (T)p2;
+        U[i * (C + 1) + j] = u;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. intra-chunk products: dq = P1 K, dk = P1^T Q, dv = P2^T dO (rows: positions of block rb)
+  f32x4 aq[RB][NK], ak[RB][NK], av[RB][NV];
+  for (int x = 0; x < RB; ++x) {
+    const int rb = w + NW * x;
+#pragma unroll
+    for (int t = 0; t < NK; ++t) {
+      f32x4 zq = {0.f, 0.f, 0.f, 0.f}, zk = zq;
+#pragma unroll
+      for (int s0 = 0; s0 < C; s0 += 32) {
+        mma(zq, frag_row<T, C>(P1, RC, rb * 16 + jj, s0 + 8 * g4),
+            frag_col<T, C>(ch.k, CH::RK, s0 + 8 * g4, t * 16 + jj));
+        mma(zk, frag_col<T, C>(P1, RC, s0 + 8 * g4, rb * 16 + jj),
+            frag_col<T, C>(ch.q, CH::RK, s0 + 8 * g4, t * 16 + jj));
+      }
+      aq[x][t] = zq;
+      ak[x][t] = zk;
+    }
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {
+      f32x4 zv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s0 = 0; s0 < C; s0 += 32)
+        mma(zv, frag_col<T, C>(P2, RC, s0 + 8 * g4, rb * 16 + jj),
+            frag_col<T, C>(ch.o, CH::RV, s0 + 8 * g4, t * 16 + jj));
+      av[x][t] = zv;
+    }
+  }
+
+  const float* gs = p.gsum + (size_t)bh * p.nslot;
+
+  // 3. earlier chunks, query side: for each set bit j of c the node (j, (c>>j) - 1), decayed
+  //    over the nodes of the lower set bits; Y = dO node^T gives dq (weighted by lambda) and
+  //    dlambda (its row dot with q)
+  float dlow = 0.f;   // log decay from the end of the current node to the start of chunk c
+  for (int jl = 0; jl < p.nl; ++jl) {
+    if (!((c >> jl) & 1)) continue;
+    const int sl = slot_of(p.N, jl, (c >> jl) - 1);
+    const float* nd = p.node + ((size_t)bh * p.nslot + sl) * SZ;
+    const float dj = __expf(dlow);
+    for (int x = 0; x < RB; ++x) {
+      const int rb = w + NW * x;
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+      float scl[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = rb * 16 + 4 * g4 + r;
+        scl[r] = ch.lam[i * kLamCap + J + 1 + jl] * ch.ea[i] * dj;
+      }
+#pragma unroll
+      for (int t = 0; t < NK; ++t) {
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b0 = 0; b0 < DV; b0 += 32)
+          mma(y, frag_row<T, DV>(ch.o, CH::RV, rb * 16 + jj, b0 + 8 * g4),
+              frag_grow<T, DV>(nd, DV, t * 16 + jj, b0 + 8 * g4));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = rb * 16 + 4 * g4 + r;
+          aq[x][t][r] += scl[r] * y[r];
+          part[r] += y[r] * to_f(ch.q[i * CH::RK + t * 16 + jj]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float sum = sum16(part[r]);
+        const int i = rb * 16 + 4 * g4 + r;
+        if (jj == 0) dli[i * kLamCap + jl] = ch.ea[i] * dj * sum;
+      }
+    }
+    dlow += gs[sl];
+  }
+
+  // 4. later chunks, source side: U = sum over the clear bits j of c (right sibling present) of
+  //    RN(j, (c>>j) + 1), decayed over the right siblings of the lower clear bits;
+  //    dk += w_s (V U^T), dv += w_s (K U), w_s = exp(g - A_s).
+  //    Thread 0 lists the siblings (state offset, decay) in shared memory.
+  long long* rsoff = reinterpret_cast<long long*>(sm + Lo.rs);
+  float* rsdec = reinterpret_cast<float*>(sm + Lo.rs + kLamCap * 8);
+  int* rsn = reinterpret_cast<int*>(sm + Lo.rs + kLamCap * 12);
+  if (tid == 0) {
+    int nr = 0;
+    float dhigh = 0.f;
+    for (int jl = 0; jl < p.nl; ++jl) {
+      if ((c >> jl) & 1) continue;
+      const int ys = ((c >> jl) + 1) << jl;
+      if (ys >= p.N) break;   // every higher sibling starts further right
+      rsoff[nr] = (long long)((((size_t)bh * p.N + ys) * p.nl + jl) * SZ);
+      rsdec[nr] = __expf(dhigh);
+      ++nr;
+      dhigh += gs[slot_of(p.N, jl, (c >> jl) + 1)];
+    }
+    *rsn = nr;
+  }
+  __syncthreads();
+  const int nr = *rsn;
+  if (nr > 0) {
+    for (int x = 0; x < RB; ++x) {
+      const int rb = w + NW * x;
+      float wsr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wsr[r] = ch.ws[rb * 16 + 4 * g4 + r];
+      // dk[s][a] += w_s sum_b V[s][b] U[a][b]
+#pragma unroll
+      for (int t = 0; t < NK; ++t) {
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b0 = 0; b0 < DV; b0 += 32) {
+          const int kb = b0 + 8 * g4;
+          Frag<T> bu = zero_frag<T>();
+          if (kb < DV) {
+            f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
+            for (int n = 0; n < nr; ++n) {
+              const float* src = p.z + rsoff[n] + (size_t)(t * 16 + jj) * DV + kb;
+              const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+              const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+              const float dn = rsdec[n];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                lo[e] += dn * a[e];
+                hi[e] += dn * b[e];
+              }
+            }
+            bu = frag_from<T>(lo, hi);
+          }
+          mma(y, frag_row<T, DV>(ch.v, CH::RV, rb * 16 + jj, kb), bu);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ak[x][t][r] += wsr[r] * y[r];
+      }
+      // dv[s][b] += w_s sum_a K[s][a] U[a][b]
+#pragma unroll
+      for (int t = 0; t < NV; ++t) {
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int a0 = 0; a0 < DK; a0 += 32) {
+          const int ka = a0 + 8 * g4;
+          Frag<T> bu = zero_frag<T>();
+          if (ka < DK) {
+            f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
+            for (int n = 0; n < nr; ++n) {
+              const float* src = p.z + rsoff[n] + (size_t)ka * DV + t * 16 + jj;
+              const float dn = rsdec[n];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                lo[e] += dn * src[(size_t)e * DV];
+                hi[e] += dn * src[(size_t)(4 + e) * DV];
+              }
+            }
+            bu = frag_from<T>(lo, hi);
+          }
+          mma(y, frag_row<T, DK>(ch.k, CH::RK, rb * 16 + jj, ka), bu);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) av[x][t][r] += wsr[r] * y[r];
+      }
+    }
+  }
+
+  // 5. dA = q.dq - k.dk, and the stores
+  for (int x = 0; x < RB; ++x) {
+    const int rb = w + NW * x;
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < NK; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = rb * 16 + 4 * g4 + r, a = t * 16 + jj;
+        part[r] += aq[x][t][r] * to_f(ch.q[i * CH::RK + a]) - ak[x][t][r] * to_f(ch.k[i * CH::RK + a]);
+        if (i < nv) {
+          reinterpret_cast<T*>(p.gq)[(row0 + i) * DK + a] = (T)aq[x][t][r];
+          reinterpret_cast<T*>(p.gk)[(row0 + i) * DK + a] = (T)ak[x][t][r];
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = rb * 16 + 4 * g4 + r;
+        if (i < nv) reinterpret_cast<T*>(p.gv)[(row0 + i) * DV + t * 16 + jj] = (T)av[x][t][r];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float sum = sum16(part[r]);
+      const int i = rb * 16 + 4 * g4 + r;
+      if (jj == 0 && i < nv) p.dA[row0 + i] = sum;
+    }
+  }
+  __syncthreads();
+
+  // 6. dlambda rows: levels 0..J from the intra-chunk pairs, J+1+j from the node read-outs of
+  //    the set bits j of c, zero for every level no pair of the row reaches
+  for (int idx = tid; idx < nv * p.L; idx += NT) {
+    const int i = idx / p.L, l = idx % p.L;
+    float val = 0.f;
+    if (l == 0) {
+      val = U[i * (C + 1) + i];
+    } else if (l <= J) {
+      if ((i >> (l - 1)) & 1) {
+        const int j0 = (i >> l) << l, n = 1 << (l - 1);
+        for (int j = j0; j < j0 + n; ++j) val += U[i * (C + 1) + j];
+      }
+    } else {
+      const int jl = l - J - 1;
+      if (jl < p.nl && ((c >> jl) & 1)) val = dli[i * kLamCap + jl];
+    }
+    p.glam[(row0 + i) * p.L + l] = val;
+  }
+}
+
+}  // namespace bwd
+}  // namespace lla
+
+namespace lla {
+namespace bwd {
+
+template <typename TY, int C, int DK, int DV>
+BwdKernels make_bwd() {
+  return BwdKernels{reinterpret_cast<const void*>(&bwd_states_kernel<TY, C, DK, DV>),
+                    reinterpret_cast<const void*>(&bwd_grads_kernel<TY, C, DK, DV>)};
+}
+
+template <typename TY, int C, int DK_>
+void bwd_fill_row(BwdKernels (&r)[4]) {
+  r[0] = make_bwd<TY, C, DK_, 16>();
+  r[1] = make_bwd<TY, C, DK_, 32>();
+  r[2] = make_bwd<TY, C, DK_, 64>();
+  r[3] = make_bwd<TY, C, DK_, 128>();
+}
+
+template <typename TY, int C>
+const BwdKernels* bwd_table(int DK, int DV) {
+  static const struct Table {
+    BwdKernels t[4][4];
+    Table() {
+      bwd_fill_row<TY, C, 16>(t[0]);
+      bwd_fill_row<TY, C, 32>(t[1]);
+      bwd_fill_row<TY, C, 64>(t[2]);
+      bwd_fill_row<TY, C, 128>(t[3]);
+    }
+  } table;
+  const int di = DK == 16 ? 0 : DK == 32 ? 1 : DK == 64 ? 2 : DK == 128 ? 3 : -1;
+  const int vi = DV == 16 ? 0 : DV == 32 ? 1 : DV == 64 ? 2 : DV == 128 ? 3 : -1;
+  if (di < 0 || vi < 0) return nullptr;
+  return &table.t[di][vi];
+}
+
+}  // namespace bwd
+}  // namespace lla

@@ -1,0 +1,8 @@
+// Backward-pass kernel instantiations: f32 q/k/v/do and gradients, chunk size 32, all head dims.
+#include "lla_bwd.hpp"
+
+namespace lla {
+namespace bwd {
+const BwdKernels* bwd_kernels_f32_c32(int DK, int DV) { return bwd_table<float, 32>(DK, DV); }
+}  // namespace bwd
+}  // namespace lla

@@ -244,3 +244,65 @@ def test_varlen_host_copy_of_empty_sequences_launches_nothing(L):
     a = _vargs()
     a.cu_seqlens_host = ctypes.cast(host, ctypes.c_void_p).value
     assert L.loglinear_attn_fwd_varlen(ctypes.byref(a), None) == _lib.LLA_OK
+
+
+# ---- backward pass -------------------------------------------------------------------------
+
+def _bargs(**kw):
+    a = _lib.BwdArgs()
+    base = 1 << 40                 # fake, well-separated, aligned addresses: never dereferenced
+    names = ("q", "k", "v", "log_a", "lam", "grad_out", "grad_q", "grad_k", "grad_v",
+             "grad_log_a", "grad_lam")
+    for i, n in enumerate(names):
+        setattr(a, n, base + (i << 32))
+    a.B, a.H, a.T, a.dk, a.dv = 1, 2, 4096, 64, 64
+    a.dtype, a.chunk = 0, 64
+    a.workspace, a.workspace_bytes = None, 0
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), _lib.LLA_ERR_INVALID_ARG),
+    (dict(H=-1), _lib.LLA_ERR_INVALID_ARG),
+    (dict(dk=24), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(chunk=128), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(chunk=8), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(B=300, H=300), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(T=1 << 24), _lib.LLA_ERR_UNSUPPORTED),                     # 25 levels
+    (dict(dtype=1, dk=128, dv=128, chunk=64), _lib.LLA_ERR_UNSUPPORTED),  # shared memory
+    (dict(grad_out=None), _lib.LLA_ERR_INVALID_ARG),
+    (dict(grad_lam=None), _lib.LLA_ERR_INVALID_ARG),
+    (dict(grad_q=(1 << 40) + (6 << 32) + 8), _lib.LLA_ERR_INVALID_ARG),        # misaligned
+    (dict(grad_log_a=(1 << 40) + (9 << 32) + 2), _lib.LLA_ERR_INVALID_ARG),
+    (dict(grad_v=(1 << 40) + 4096), _lib.LLA_ERR_INVALID_ARG),                  # overlaps q
+    (dict(grad_k=(1 << 40) + (6 << 32) + 4096), _lib.LLA_ERR_INVALID_ARG),      # overlaps grad_q
+    (dict(workspace=(1 << 44), workspace_bytes=1024), _lib.LLA_ERR_WORKSPACE),
+    (dict(workspace=(1 << 44) + 16, workspace_bytes=1 << 34), _lib.LLA_ERR_INVALID_ARG),
+])
+def test_bwd_validation_codes(L, kw, code):
+    assert L.loglinear_attn_bwd(ctypes.byref(_bargs(**kw)), None) == code
+
+
+def test_bwd_null_struct_and_empty(L):
+    assert L.loglinear_attn_bwd(None, None) == _lib.LLA_ERR_INVALID_ARG
+    for kw in (dict(B=0), dict(T=0), dict(T=0, q=None)):
+        assert L.loglinear_attn_bwd(ctypes.byref(_bargs(**kw)), None) == _lib.LLA_OK
+
+
+def test_bwd_defaults_and_workspace(L):
+    assert L.loglinear_attn_bwd_default_chunk(16, 16, 1) == 16
+    assert L.loglinear_attn_bwd_default_chunk(64, 64, 0) == 64
+    assert L.loglinear_attn_bwd_default_chunk(128, 128, 0) == 64
+    assert L.loglinear_attn_bwd_default_chunk(128, 128, 1) == 32   # float32 images need less C
+    assert L.loglinear_attn_bwd_default_chunk(48, 64, 0) == 0
+    ws = L.loglinear_attn_bwd_workspace_bytes
+    # headline shape: N = 128 chunks, 7 chunk levels, 128 + 64 + ... + 2 = 254 tree slots per head
+    n = ws(4, 16, 8192, 64, 64, 64, 0)
+    sz = 64 * 64 * 4
+    expect = 64 * 254 * sz + 64 * 254 * 4 + 64 * 128 * 7 * sz + 64 * 8192 * 4
+    assert expect <= n <= expect + 4 * 256
+    # one chunk: only the per-position dA
+    assert ws(1, 2, 64, 64, 64, 64, 0) == 2 * 64 * 4
+    assert ws(1, 2, 64, 48, 64, 64, 0) == 0

@@ -1,0 +1,166 @@
+"""GPU parity of the backward pass: gradients from the C ABI (loglinear_attn_bwd) against the
+fp64 CPU oracle's gradients of the definition on identical seeded inputs and upstream gradient.
+
+Every gradient (dq, dk, dv, dlog_a, dlambda) is compared element by element through the
+relative L2 error over the whole tensor: 1e-4 for float32 inputs, 2e-2 for bfloat16 inputs
+with float32 accumulation. Cases cover several chunks and chunk levels with a ragged tail,
+dk != dv, the degenerate lengths (T = 1, T < C, T = C), one-hot lambda at every level with no
+decay (so that coarse levels are not hidden by decay), bitwise determinism, a caller workspace
+full of NaN bytes, and one head of the headline shape at full size.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.loglinear as O
+from lla_synth import custom, generate, grad_output, workload
+from tests._util import ensure_built, rel_l2, tol_for
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dq", "dk", "dv", "dlog_a", "dlam")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    import torch
+    ensure_built()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def run_bwd(x, do, **kw):
+    """Device backward pass on CPU inputs; returns the five gradients as float64 numpy."""
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    d = {k: v.cuda() for k, v in x.items()}
+    g = lla.backward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], do.cuda(), **kw)
+    torch.cuda.synchronize()
+    return {n: t.double().cpu().numpy() for n, t in zip(GRADS, g)}
+
+
+def check(w, x, do, label, **kw):
+    print(f"[bwd] {label} B={w.B} H={w.H} T={w.T} dk={w.dk} dv={w.dv} {w.dtype} {kw}", flush=True)
+    got = run_bwd(x, do, **kw)
+    want = O.bruteforce_grad(**x, do=do)
+    tol = tol_for(w.dtype)
+    errs = {n: rel_l2(got[n], want[n]) for n in GRADS}
+    for n in GRADS:
+        assert np.all(np.isfinite(got[n])), (label, n)
+        assert errs[n] <= tol, (label, n, errs)
+    return got
+
+
+CASES = [
+    # B, H, T, dk, dv, dtype, chunk
+    (1, 2, 256, 16, 16, "f32", 0),      # the small fp32 workload's shape, default chunk 16
+    (1, 2, 256, 16, 16, "f32", 32),
+    (1, 2, 200, 32, 16, "f32", 16),     # ragged, dk != dv
+    (2, 1, 333, 16, 32, "f32", 32),
+    (1, 2, 130, 64, 64, "f32", 64),
+    (1, 1, 100, 128, 16, "f32", 0),
+    (1, 2, 300, 64, 64, "bf16", 64),
+    (1, 2, 1000, 64, 64, "bf16", 0),
+    (2, 2, 600, 64, 128, "bf16", 0),
+    (1, 2, 520, 128, 32, "bf16", 32),
+    (1, 1, 1024, 128, 128, "bf16", 0),
+    (1, 2, 700, 32, 32, "bf16", 16),
+]
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv,dtype,chunk", CASES)
+def test_backward_matches_oracle(B, H, T, dk, dv, dtype, chunk):
+    w = custom(B, H, T, dk, dv, dtype)
+    x = generate(w, seed=T + dk)
+    do = grad_output(w, seed=T + dk)
+    check(w, x, do, "random", chunk=chunk)
+
+
+@pytest.mark.parametrize("T,chunk", [(1, 16), (5, 16), (16, 16), (17, 16), (64, 64), (63, 64), (65, 64)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_degenerate_lengths(T, chunk, dtype):
+    w = custom(1, 2, T, 32, 16, dtype)
+    x = generate(w, seed=3)
+    do = grad_output(w, seed=3)
+    check(w, x, do, "short", chunk=chunk)
+
+
+@pytest.mark.parametrize("level", list(range(10)))
+def test_backward_onehot_levels_no_decay(level):
+    # T = 512, C = 16: levels 0..4 inside a chunk, 5..9 across chunks (chunk levels 0..4)
+    w = custom(1, 2, 512, 16, 16, "f32")
+    x = generate(w, seed=11, log_a_mode="nodecay", lam_mode=f"onehot:{level}")
+    do = grad_output(w, seed=11)
+    check(w, x, do, f"onehot:{level}", chunk=16)
+
+
+@pytest.mark.parametrize("mode", ["nodecay", "lowdecay"])
+def test_backward_low_decay_bf16(mode):
+    w = custom(1, 2, 2048, 64, 64, "bf16")
+    x = generate(w, seed=5, log_a_mode=mode)
+    do = grad_output(w, seed=5)
+    check(w, x, do, mode, chunk=64)
+
+
+@pytest.mark.parametrize("level", [7, 9, 11])
+def test_backward_coarse_onehot_bf16(level):
+    w = custom(1, 1, 2048, 64, 64, "bf16")
+    x = generate(w, seed=6, log_a_mode="lowdecay", lam_mode=f"onehot:{level}")
+    do = grad_output(w, seed=6)
+    check(w, x, do, f"onehot:{level}", chunk=64)
+
+
+def test_backward_small_bf16_workload():
+    w = workload("b2h8_t2048_d64_bf16")
+    x = generate(w, seed=0)
+    do = grad_output(w, seed=0)
+    check(w, x, do, w.name, chunk=w.chunk)
+
+
+def test_backward_equal_lambda_is_mamba2_gradient():
+    # every level weight equal: the gradient of c_t x the Mamba-2 recurrence, here through the
+    # oracle's definition; also checks that dlambda splits the row total across levels
+    w = custom(1, 2, 400, 32, 32, "f32")
+    x = generate(w, seed=8, lam_mode="equal")
+    do = grad_output(w, seed=8)
+    got = check(w, x, do, "equal", chunk=32)
+    want = O.bruteforce_grad(**x, do=do)
+    assert rel_l2(got["dlam"].sum(-1), want["dlam"].sum(-1)) <= 1e-4
+
+
+def test_backward_deterministic_and_workspace_poison():
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    w = custom(2, 2, 1500, 64, 64, "bf16")
+    x = {k: v.cuda() for k, v in generate(w, seed=9).items()}
+    do = grad_output(w, seed=9).cuda()
+    print("[bwd] determinism / poisoned workspace", flush=True)
+    a = lla.backward(x["q"], x["k"], x["v"], x["log_a"], x["lam"], do)
+    nbytes = lla.bwd_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, 0, "bf16")
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    b = lla.backward(x["q"], x["k"], x["v"], x["log_a"], x["lam"], do, workspace=ws)
+    c = lla.backward(x["q"], x["k"], x["v"], x["log_a"], x["lam"], do, workspace=ws)
+    torch.cuda.synchronize()
+    for ta, tb, tc in zip(a, b, c):
+        assert torch.equal(ta, tb) and torch.equal(ta, tc)
+
+
+def test_backward_headline_shape_one_head():
+    # the headline shape (B=4, H=16, T=8192, d=64, bf16) at the launch configuration the
+    # benchmark times; the last head is compared with the oracle run on that head alone
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    w = workload("b4h16_t8192_d64_bf16")
+    x = generate(w, seed=0)
+    do = grad_output(w, seed=0)
+    print("[bwd] headline shape, head (3, 15)", flush=True)
+    d = {k: v.cuda() for k, v in x.items()}
+    g = lla.backward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], do.cuda())
+    torch.cuda.synchronize()
+    b, h = 3, 15
+    xs = {k: v[b:b + 1, h:h + 1] for k, v in x.items()}
+    want = O.bruteforce_grad(**xs, do=do[b:b + 1, h:h + 1])
+    for n, t in zip(GRADS, g):
+        got = t[b:b + 1, h:h + 1].double().cpu().numpy()
+        assert np.all(np.isfinite(t.float().cpu().numpy())), n
+        assert rel_l2(got, want[n]) <= 2e-2, (n, rel_l2(got, want[n]))
