@@ -132,6 +132,83 @@ def decode_measure(w, dev, stream, steps: int = 256, warmup: int = 32) -> dict:
     }
 
 
+def backward_algorithmic(w, chunk: int) -> tuple[float, float]:
+    """(FLOP, bytes) per head-token of the backward pass.
+
+    FLOP: the intra-chunk block's five products (scores and dO V^T, then dq, dk, dv),
+    2C(3dk + 2dv); the chunk state 2 dk dv; popcount(chunk index) target-side partials and as
+    many node read-outs for dq, 2 dk dv each, log2(T/C)/2 of each on average; the two read-outs
+    of the combined right-sibling state for dk and dv, 2 dk dv each. Bytes: q, k, v, dO read and
+    dq, dk, dv written once in the element type; log_a, lambda read and dlog_a, dlambda written
+    once in float32.
+    """
+    import math
+    e = 2 if w.dtype == "bf16" else 4
+    n = max(1, -(-w.T // chunk))
+    pbar = math.log2(n) / 2 if n > 1 else 0.0
+    flop = 2 * chunk * (3 * w.dk + 2 * w.dv) + 2 * w.dk * w.dv * (3 + 2 * pbar)
+    byts = (4 * w.dk + 3 * w.dv) * e + 8 * w.L + 8
+    return flop, byts
+
+
+def backward_measure(w, d, dev, stream, steps: int = 20, warmup: int = 5) -> dict:
+    """The backward pass (``loglinear_attn_bwd``) on the workload's inputs and a seeded upstream
+    gradient, with a caller workspace: time per call between events, per-stage times from the
+    events the library records (chunk states + block decays + tree, gradient kernel, dlog_a
+    scan), tokens/s and the roofline of the whole call against its algorithmic bytes."""
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    from lla_synth import grad_output
+    do = grad_output(w, seed=0).to(dev)
+    chunk = lla.bwd_default_chunk(w.dk, w.dv, w.dtype)
+    ws = torch.empty(max(lla.bwd_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, chunk, w.dtype), 1),
+                     dtype=torch.uint8, device=dev)
+    outs = (torch.empty_like(d["q"]), torch.empty_like(d["k"]), torch.empty_like(d["v"]),
+            torch.empty_like(d["log_a"]), torch.empty_like(d["lam"]))
+
+    def call(evs=None):
+        lla.backward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], do, chunk=chunk, workspace=ws,
+                     stream=stream, stage_events=evs, out=outs)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    stages = {"states_tree": 0.0, "grads": 0.0, "dloga": 0.0}
+    reps = 5
+    for _ in range(reps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for ev in evs:
+            ev.record(stream)
+        torch.cuda.synchronize(dev)
+        call(evs)
+        torch.cuda.synchronize(dev)
+        stages["states_tree"] += evs[0].elapsed_time(evs[1]) / reps
+        stages["grads"] += evs[1].elapsed_time(evs[2]) / reps
+        stages["dloga"] += evs[2].elapsed_time(evs[3]) / reps
+    flop_ht, byte_ht = backward_algorithmic(w, chunk)
+    ht = w.B * w.H * w.T
+    achieved = byte_ht * ht / (ms * 1e-3) / 1e9
+    peak_flops = (BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS) * 1e12
+    return {
+        "config": {"chunk": chunk, "workspace_bytes": ws.numel()},
+        "ms_per_call": ms,
+        "stages_ms": stages,
+        "tokens_per_s": w.B * w.T / (ms * 1e-3),
+        "algorithmic_bytes_per_call": byte_ht * ht,
+        "algorithmic_flop_per_call": flop_ht * ht,
+        "mfma_util_algorithmic": flop_ht * ht / (ms * 1e-3) / peak_flops,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "scope": "whole backward call"},
+    }
+
+
 VARLEN_LENGTHS = [8192, 7000, 5000, 4096, 3000, 2500, 1500, 1000, 480]   # 32768 tokens per head
 
 
@@ -238,6 +315,7 @@ def main(argv=None) -> int:
                     help="only run 5 device copies of MIB MiB (hardware-counter calibration)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decoding-step measurement")
     ap.add_argument("--no-varlen", action="store_true", help="skip the variable-length measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_fused_kernel.json"),
                     help="measured HBM traffic of the forward kernel (from rocprofv3 counters)")
     a = ap.parse_args(argv)
@@ -362,6 +440,8 @@ def main(argv=None) -> int:
         res["decode"] = decode_measure(w, dev, stream)
     if not a.no_varlen and not a.kernel_only:
         res["varlen"] = varlen_measure(dev, stream)
+    if not a.no_backward:
+        res["backward"] = backward_measure(w, d, dev, stream)
 
     if not a.kernel_only:
         # cold caches: overwrite a 512 MiB buffer (outside the events) before each call
