@@ -65,6 +65,7 @@ struct BwdParams {
   float* node;    // [BH][nslot][dk*dv]: forward Fenwick nodes over chunks, all block levels
   float* gsum;    // [BH][nslot]: total log decay of each block
   float* z;       // [BH][N][nl][dk*dv]: partials Z(c, j); after bwd_tree Z(start of Y, j) = RN(j, Y)
+  float* outs;    // [BH][nslot][dk*dv]: down-sweep; level 0 = the combined right-sibling state of each chunk
   float* dA;      // [BH][T]
   int BH, T, L, N, nl, nslot;
 };
@@ -78,8 +79,9 @@ __host__ __device__ inline int slot_of(int N, int i, int m) {
 
 // shared-memory layout of bwd_states / bwd_grads (host and device agree)
 struct BwdSmem {
-  int q, k, v, o, p1, p2, u, lam, al, ea, ws, dli, rs, total;
+  int q, k, v, o, p1, p2, lam, al, ea, ws, ust, nst, total;
 };
+
 __host__ __device__ inline BwdSmem bwd_smem(int es, int C, int DK, int DV, bool grads) {
   BwdSmem s{};
   int off = 0;
@@ -91,13 +93,14 @@ __host__ __device__ inline BwdSmem bwd_smem(int es, int C, int DK, int DV, bool 
   s.o = take(C * rv * es);
   s.p1 = grads ? take(C * rc * es) : off;
   s.p2 = grads ? take(C * rc * es) : off;
-  s.u = grads ? take(C * (C + 1) * 4) : off;
   s.lam = take(C * kLamCap * 4);
   s.al = take(C * 4);
   s.ea = take(C * 4);
   s.ws = take(C * 4);
-  s.dli = grads ? take(C * kLamCap * 4) : off;
-  s.rs = grads ? take(kLamCap * 12 + 16) : off;
+  // a [dk][dv] state image: first the combined right-sibling state, then (once the source-side
+  // products are done) one Fenwick node at a time
+  s.ust = grads ? take(DK * rv * es) : off;
+  s.nst = s.ust;
   s.total = (off + 255) & ~255;
   return s;
 }
@@ -133,22 +136,40 @@ __device__ __forceinline__ Frag<T> frag_row(const T* img, int RS, int r, int k) 
 }
 
 // X[k .. k+7][c] (a column of the image), each element times sc[k + e] when sc is given
+// (k a multiple of 8, the same in each 16-lane group; c = c0 + (lane & 15) with c0 a multiple of
+// 16). bf16: two transposing reads (ds_read_tr16_b64). In each 16-lane group such a read gives
+// lane i, as its element e, element i % 4 of the 4-element piece addressed by lane 4e + i / 4;
+// so lane L addresses row k + L / 4 (then k + 4 + L / 4), columns c0 + 4 (L % 4) .. + 3.
+// f32: element-wise reads.
 template <typename T, int K>
 __device__ __forceinline__ Frag<T> frag_col(const T* img, int RS, int k, int c,
                                             const float* sc = nullptr) {
-  if (k >= K) return zero_frag<T>();
+  const bool ok = k < K;
+  const int kk = ok ? k : 0;
   f32x4 lo, hi;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    lo[e] = to_f(img[(k + e) * RS + c]);
-    hi[e] = to_f(img[(k + 4 + e) * RS + c]);
-  }
-  if (sc) {
+  if constexpr (sizeof(T) == 2) {
+    const int L = c & 15, c0 = c - L;
+    const T* p = img + (kk + (L >> 2)) * RS + c0 + 4 * (L & 3);
+    const s16x4 a = ds_read_tr(reinterpret_cast<const unsigned char*>(p));
+    const s16x4 b = ds_read_tr(reinterpret_cast<const unsigned char*>(p + 4 * RS));
+    Frag<T> f;
+    f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+    if (!ok) return zero_frag<T>();
+    if (!sc) return f;
+    frag_to_f32(f, lo, hi);
+  } else {
+    if (!ok) return zero_frag<T>();
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      lo[e] *= sc[k + e];
-      hi[e] *= sc[k + 4 + e];
+      lo[e] = to_f(img[(k + e) * RS + c]);
+      hi[e] = to_f(img[(k + 4 + e) * RS + c]);
     }
+    if (!sc) return frag_from<T>(lo, hi);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lo[e] *= sc[k + e];
+    hi[e] *= sc[k + 4 + e];
   }
   return frag_from<T>(lo, hi);
 }
@@ -332,6 +353,19 @@ bwd_states_kernel(BwdParams p) {
 // bwd_grads: all gradients of one chunk
 // ----------------------------------------------------------------------------------------
 
+// a [DK][DV] float state in global memory into a shared image of element type T (row stride RV)
+template <typename T, int DK, int DV, int RV>
+__device__ __forceinline__ void stage_state(T* img, const float* __restrict__ g, int tid, int nt) {
+  constexpr int N4 = DK * DV / 4;
+  for (int idx = tid; idx < N4; idx += nt) {
+    const f32x4 x = reinterpret_cast<const f32x4*>(g)[idx];
+    const int a = (idx * 4) / DV, b = (idx * 4) % DV;
+    T* dst = img + a * RV + b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = (T)x[e];
+  }
+}
+
 template <typename T, int C, int DK, int DV>
 __global__ void __launch_bounds__(64 * Waves<C>::NW)
 bwd_grads_kernel(BwdParams p) {
@@ -348,13 +382,39 @@ bwd_grads_kernel(BwdParams p) {
   ch.bind(sm, Lo);
   T* P1 = reinterpret_cast<T*>(sm + Lo.p1);     // M * W  [i][j]
   T* P2 = reinterpret_cast<T*>(sm + Lo.p2);     // M * S  [i][j]
-  float* U = reinterpret_cast<float*>(sm + Lo.u);      // exp(A_i - A_j) S W  [i][j], stride C+1
-  float* dli = reinterpret_cast<float*>(sm + Lo.dli);  // dlambda of the levels J+1+j  [i][j]
-  ch.load(p, bh, c, nv, tid, NT);
+  T* Ust = reinterpret_cast<T*>(sm + Lo.ust);   // combined right-sibling state [a][b]
+  T* Nst = reinterpret_cast<T*>(sm + Lo.nst);   // one node [a][b] (the same region, after step 3)
   const size_t SZ = (size_t)DK * DV;
   const size_t row0 = (size_t)bh * p.T + (size_t)c * C;
+  // the combined right-sibling state, written by the down-sweep (zero for the last chunk);
+  // its loads are issued with the chunk's
+  const bool later = p.nl > 0;
+  if (later) stage_state<T, DK, DV, CH::RV>(Ust, p.outs + ((size_t)bh * p.nslot + c) * SZ, tid, NT);
+  // the first node of step 4 is prefetched into registers now (see step 4)
+  constexpr int NPF = DK * DV / 4 / NT;
+  constexpr bool PF = NPF >= 1 && NPF <= 4 && NPF * NT * 4 == DK * DV;
+  f32x4 pf[PF ? NPF : 1];
+  auto prefetch = [&](int jl) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(
+        p.node + ((size_t)bh * p.nslot + slot_of(p.N, jl, (c >> jl) - 1)) * SZ);
+#pragma unroll
+    for (int u = 0; u < (PF ? NPF : 1); ++u) pf[u] = src[tid + u * NT];
+  };
+  int first_set = 0;
+  while (first_set < p.nl && !((c >> first_set) & 1)) ++first_set;
+  if (PF && first_set < p.nl) prefetch(first_set);
+  ch.load(p, bh, c, nv, tid, NT);
 
-  // 1. masked score tiles: wave w takes 16-row blocks rb = w + NW*x of query positions i
+  // 1. masked score tiles: wave w takes 16-row blocks rb = w + NW*x of query positions i.
+  //    dlambda of the levels inside the chunk is summed per (row, level) in registers: in a tile
+  //    off the diagonal every pair has level 4 + bit_length(rb ^ cb); on it, bit_length(i ^ j).
+  float bins[RB][4][J + 1];
+  for (int x = 0; x < RB; ++x)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int l = 0; l <= J; ++l) bins[x][r][l] = 0.f;
+#pragma unroll
   for (int x = 0; x < RB; ++x) {
     const int rb = w + NW * x;
 #pragma unroll
@@ -370,20 +430,38 @@ bwd_grads_kernel(BwdParams p) {
           mma(wv, frag_row<T, DV>(ch.o, CH::RV, rb * 16 + jj, b0 + 8 * g4),
               frag_row<T, DV>(ch.v, CH::RV, cb * 16 + jj, b0 + 8 * g4));
       }
+      float u[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = rb * 16 + 4 * g4 + r, j = cb * 16 + jj;
-        float p1 = 0.f, p2 = 0.f, u = 0.f;
+        float p1 = 0.f, p2 = 0.f;
+        u[r] = 0.f;
         if (j <= i) {
           const float d = __expf(ch.al[i] - ch.al[j]);
           const float m = ch.lam[i * kLamCap + bit_length((unsigned)(i ^ j))] * d;
           p1 = m * wv[r];
           p2 = m * s[r];
-          u = d * s[r] * wv[r];
+          u[r] = d * s[r] * wv[r];
         }
         P1[i * RC + j] = (T)p1;
         P2[i * RC + j] = (T)p2;
-        U[i * (C + 1) + j] = u;
+      }
+      if (cb < rb) {
+        const int lv = 4 + bit_length((unsigned)(rb ^ cb));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float su = sum16(u[r]);
+#pragma unroll
+          for (int l = 5; l <= J; ++l)
+            if (l == lv) bins[x][r][l] += su;
+        }
+      } else if (cb == rb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int lv = bit_length((unsigned)((4 * g4 + r) ^ jj));
+#pragma unroll
+          for (int l = 0; l <= 4 && l <= J; ++l) bins[x][r][l] += sum16(lv == l ? u[r] : 0.f);
+        }
       }
     }
   }
@@ -391,6 +469,7 @@ bwd_grads_kernel(BwdParams p) {
 
   // 2. intra-chunk products: dq = P1 K, dk = P1^T Q, dv = P2^T dO (rows: positions of block rb)
   f32x4 aq[RB][NK], ak[RB][NK], av[RB][NV];
+#pragma unroll
   for (int x = 0; x < RB; ++x) {
     const int rb = w + NW * x;
 #pragma unroll
@@ -417,17 +496,67 @@ bwd_grads_kernel(BwdParams p) {
     }
   }
 
-  const float* gs = p.gsum + (size_t)bh * p.nslot;
+  // 3. later chunks, source side: dk += w_s (V U^T), dv += w_s (K U), w_s = exp(g - A_s),
+  //    U the combined right-sibling state staged at the start
+  if (later) {
+#pragma unroll
+    for (int x = 0; x < RB; ++x) {
+      const int rb = w + NW * x;
+      float wsr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wsr[r] = ch.ws[rb * 16 + 4 * g4 + r];
+#pragma unroll
+      for (int t = 0; t < NK; ++t) {
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b0 = 0; b0 < DV; b0 += 32)
+          mma(y, frag_row<T, DV>(ch.v, CH::RV, rb * 16 + jj, b0 + 8 * g4),
+              frag_row<T, DV>(Ust, CH::RV, t * 16 + jj, b0 + 8 * g4));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ak[x][t][r] += wsr[r] * y[r];
+      }
+#pragma unroll
+      for (int t = 0; t < NV; ++t) {
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int a0 = 0; a0 < DK; a0 += 32)
+          mma(y, frag_row<T, DK>(ch.k, CH::RK, rb * 16 + jj, a0 + 8 * g4),
+              frag_col<T, DK>(Ust, CH::RV, a0 + 8 * g4, t * 16 + jj));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) av[x][t][r] += wsr[r] * y[r];
+      }
+    }
+  }
 
-  // 3. earlier chunks, query side: for each set bit j of c the node (j, (c>>j) - 1), decayed
-  //    over the nodes of the lower set bits; Y = dO node^T gives dq (weighted by lambda) and
-  //    dlambda (its row dot with q)
+  // 4. earlier chunks, query side: for each set bit j of c the node (j, (c>>j) - 1), decayed
+  //    over the nodes of the lower set bits, staged into shared memory; Y = dO node^T gives dq
+  //    (weighted by lambda) and dlambda of level J+1+j (its row dot with q, written here).
+  //    When a node is at most 4 float4 per thread, the next node's loads are in flight in
+  //    registers while the current one is used (the first one's since the kernel started).
+  const float* gs = p.gsum + (size_t)bh * p.nslot;
   float dlow = 0.f;   // log decay from the end of the current node to the start of chunk c
-  for (int jl = 0; jl < p.nl; ++jl) {
+  for (int jl = first_set; jl < p.nl; ++jl) {
     if (!((c >> jl) & 1)) continue;
     const int sl = slot_of(p.N, jl, (c >> jl) - 1);
-    const float* nd = p.node + ((size_t)bh * p.nslot + sl) * SZ;
+    __syncthreads();   // the previous reads of the state image are done
+    if constexpr (PF) {
+#pragma unroll
+      for (int u = 0; u < NPF; ++u) {
+        const int idx = tid + u * NT;
+        const int a = (idx * 4) / DV, b = (idx * 4) % DV;
+        T* dst = Nst + a * CH::RV + b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e] = (T)pf[u][e];
+      }
+      int nx = jl + 1;
+      while (nx < p.nl && !((c >> nx) & 1)) ++nx;
+      if (nx < p.nl) prefetch(nx);
+    } else {
+      stage_state<T, DK, DV, CH::RV>(Nst, p.node + ((size_t)bh * p.nslot + sl) * SZ, tid, NT);
+    }
+    __syncthreads();
     const float dj = __expf(dlow);
+#pragma unroll
     for (int x = 0; x < RB; ++x) {
       const int rb = w + NW * x;
       float part[4] = {0.f, 0.f, 0.f, 0.f};
@@ -443,7 +572,7 @@ bwd_grads_kernel(BwdParams p) {
 #pragma unroll
         for (int b0 = 0; b0 < DV; b0 += 32)
           mma(y, frag_row<T, DV>(ch.o, CH::RV, rb * 16 + jj, b0 + 8 * g4),
-              frag_grow<T, DV>(nd, DV, t * 16 + jj, b0 + 8 * g4));
+              frag_row<T, DV>(Nst, CH::RV, t * 16 + jj, b0 + 8 * g4));
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = rb * 16 + 4 * g4 + r;
@@ -455,99 +584,14 @@ bwd_grads_kernel(BwdParams p) {
       for (int r = 0; r < 4; ++r) {
         const float sum = sum16(part[r]);
         const int i = rb * 16 + 4 * g4 + r;
-        if (jj == 0) dli[i * kLamCap + jl] = ch.ea[i] * dj * sum;
+        if (jj == r && i < nv) p.glam[(row0 + i) * p.L + J + 1 + jl] = ch.ea[i] * dj * sum;
       }
     }
     dlow += gs[sl];
   }
 
-  // 4. later chunks, source side: U = sum over the clear bits j of c (right sibling present) of
-  //    RN(j, (c>>j) + 1), decayed over the right siblings of the lower clear bits;
-  //    dk += w_s (V U^T), dv += w_s (K U), w_s = exp(g - A_s).
-  //    Thread 0 lists the siblings (state offset, decay) in shared memory.
-  long long* rsoff = reinterpret_cast<long long*>(sm + Lo.rs);
-  float* rsdec = reinterpret_cast<float*>(sm + Lo.rs + kLamCap * 8);
-  int* rsn = reinterpret_cast<int*>(sm + Lo.rs + kLamCap * 12);
-  if (tid == 0) {
-    int nr = 0;
-    float dhigh = 0.f;
-    for (int jl = 0; jl < p.nl; ++jl) {
-      if ((c >> jl) & 1) continue;
-      const int ys = ((c >> jl) + 1) << jl;
-      if (ys >= p.N) break;   // every higher sibling starts further right
-      rsoff[nr] = (long long)((((size_t)bh * p.N + ys) * p.nl + jl) * SZ);
-      rsdec[nr] = __expf(dhigh);
-      ++nr;
-      dhigh += gs[slot_of(p.N, jl, (c >> jl) + 1)];
-    }
-    *rsn = nr;
-  }
-  __syncthreads();
-  const int nr = *rsn;
-  if (nr > 0) {
-    for (int x = 0; x < RB; ++x) {
-      const int rb = w + NW * x;
-      float wsr[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) wsr[r] = ch.ws[rb * 16 + 4 * g4 + r];
-      // dk[s][a] += w_s sum_b V[s][b] U[a][b]
-#pragma unroll
-      for (int t = 0; t < NK; ++t) {
-        f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int b0 = 0; b0 < DV; b0 += 32) {
-          const int kb = b0 + 8 * g4;
-          Frag<T> bu = zero_frag<T>();
-          if (kb < DV) {
-            f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
-            for (int n = 0; n < nr; ++n) {
-              const float* src = p.z + rsoff[n] + (size_t)(t * 16 + jj) * DV + kb;
-              const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-              const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
-              const float dn = rsdec[n];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                lo[e] += dn * a[e];
-                hi[e] += dn * b[e];
-              }
-            }
-            bu = frag_from<T>(lo, hi);
-          }
-          mma(y, frag_row<T, DV>(ch.v, CH::RV, rb * 16 + jj, kb), bu);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ak[x][t][r] += wsr[r] * y[r];
-      }
-      // dv[s][b] += w_s sum_a K[s][a] U[a][b]
-#pragma unroll
-      for (int t = 0; t < NV; ++t) {
-        f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int a0 = 0; a0 < DK; a0 += 32) {
-          const int ka = a0 + 8 * g4;
-          Frag<T> bu = zero_frag<T>();
-          if (ka < DK) {
-            f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = lo;
-            for (int n = 0; n < nr; ++n) {
-              const float* src = p.z + rsoff[n] + (size_t)ka * DV + t * 16 + jj;
-              const float dn = rsdec[n];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                lo[e] += dn * src[(size_t)e * DV];
-                hi[e] += dn * src[(size_t)(4 + e) * DV];
-              }
-            }
-            bu = frag_from<T>(lo, hi);
-          }
-          mma(y, frag_row<T, DK>(ch.k, CH::RK, rb * 16 + jj, ka), bu);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) av[x][t][r] += wsr[r] * y[r];
-      }
-    }
-  }
-
   // 5. dA = q.dq - k.dk, and the stores
+#pragma unroll
   for (int x = 0; x < RB; ++x) {
     const int rb = w + NW * x;
     float part[4] = {0.f, 0.f, 0.f, 0.f};
@@ -575,28 +619,28 @@ bwd_grads_kernel(BwdParams p) {
     for (int r = 0; r < 4; ++r) {
       const float sum = sum16(part[r]);
       const int i = rb * 16 + 4 * g4 + r;
-      if (jj == 0 && i < nv) p.dA[row0 + i] = sum;
+      if (jj == r && i < nv) p.dA[row0 + i] = sum;
     }
-  }
-  __syncthreads();
 
-  // 6. dlambda rows: levels 0..J from the intra-chunk pairs, J+1+j from the node read-outs of
-  //    the set bits j of c, zero for every level no pair of the row reaches
-  for (int idx = tid; idx < nv * p.L; idx += NT) {
-    const int i = idx / p.L, l = idx % p.L;
-    float val = 0.f;
-    if (l == 0) {
-      val = U[i * (C + 1) + i];
-    } else if (l <= J) {
-      if ((i >> (l - 1)) & 1) {
-        const int j0 = (i >> l) << l, n = 1 << (l - 1);
-        for (int j = j0; j < j0 + n; ++j) val += U[i * (C + 1) + j];
+    // 6. dlambda of this block's rows: levels 0..J from the bins, zero for every level past J
+    //    that no node read-out of step 4 wrote (lane jj writes levels jj, jj + 16)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = rb * 16 + 4 * g4 + r;
+      if (i >= nv) continue;
+      for (int l = jj; l < p.L; l += 16) {
+        float val = 0.f;
+        if (l <= J) {
+#pragma unroll
+          for (int q = 0; q <= J; ++q)
+            if (q == l) val = bins[x][r][q];
+        } else {
+          const int jl = l - J - 1;
+          if (jl < p.nl && ((c >> jl) & 1)) continue;   // written in step 4
+        }
+        p.glam[(row0 + i) * p.L + l] = val;
       }
-    } else {
-      const int jl = l - J - 1;
-      if (jl < p.nl && ((c >> jl) & 1)) val = dli[i * kLamCap + jl];
     }
-    p.glam[(row0 + i) * p.L + l] = val;
   }
 }
 

@@ -31,32 +31,73 @@ __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdParams p) {
 }
 
 // ----------------------------------------------------------------------------------------
-// bwd_tree: forward up-sweep and right-block sums, 64 state elements per workgroup
+// bwd_tree: 64 state elements of one head per workgroup, 16 waves splitting the blocks of a level.
+//   up-sweep, levels i = 1 .. nl-1: node(i,m) = exp(G(i-1,2m+1)) node(i-1,2m) + node(i-1,2m+1);
+//     in the Z slots, the partial sums of every level j >= i whose odd block contains (i, m):
+//     Z(m<<i, j) += exp(G(i-1,2m)) Z((2m+1)<<(i-1), j), so that Z(start of Y, j) = RN(j, Y).
+//   down-sweep, levels i = nl-1 .. 0: Out(i, m) = what the chunks of block (i, m) receive from
+//     later blocks at levels >= i, decayed to the end of (i, m):
+//       left child with a right sibling Y: Out = exp(G(Y)) Out(parent) + RN(i, Y);
+//       otherwise: Out = Out(parent); the parent of the top level holds nothing.
+//     Out(0, c) is the combined right-sibling state of chunk c.
 // ----------------------------------------------------------------------------------------
 
-__global__ void __launch_bounds__(256) bwd_tree_kernel(BwdParams p, int SZ) {
+constexpr int kTreeWaves = 16;
+
+__global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, int SZ) {
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 64 + (threadIdx.x & 63), w = threadIdx.x >> 6;
   // the grid has exactly SZ / 64 columns of workgroups (SZ = dk*dv is a multiple of 64)
   const float* gs = p.gsum + (size_t)bh * p.nslot;
   float* nd = p.node + (size_t)bh * p.nslot * SZ + e;
   float* zz = p.z + (size_t)bh * p.N * p.nl * SZ + e;
+  float* ou = p.outs + (size_t)bh * p.nslot * SZ + e;
   for (int i = 1; i < p.nl; ++i) {
     const int nprev = (p.N + (1 << (i - 1)) - 1) >> (i - 1), nb = (p.N + (1 << i) - 1) >> i;
     const int o_prev = slot_of(p.N, i - 1, 0), o = slot_of(p.N, i, 0);
-    for (int m = w; m < nb; m += 4) {
+    for (int m = w; m < nb; m += kTreeWaves) {
       const bool right = 2 * m + 1 < nprev;
-      const float lhs = nd[(size_t)(o_prev + 2 * m) * SZ];
-      nd[(size_t)(o + m) * SZ] =
-          right ? __expf(gs[o_prev + 2 * m + 1]) * lhs + nd[(size_t)(o_prev + 2 * m + 1) * SZ] : lhs;
-      // partials of the levels j >= i whose odd block contains block (i, m)
-      const float dl = __expf(gs[o_prev + 2 * m]);
       const int c0 = m << i, c1 = (2 * m + 1) << (i - 1);
-      for (int j = i; j < p.nl; ++j) {
-        if (!((m >> (j - i)) & 1)) continue;
-        float* zl = zz + ((size_t)c0 * p.nl + j) * SZ;
-        if (right) *zl = *zl + dl * zz[((size_t)c1 * p.nl + j) * SZ];
+      // loads first (nothing stored below is read here), in groups of 4 partial levels
+      const float lhs = nd[(size_t)(o_prev + 2 * m) * SZ];
+      const float rhs = right ? nd[(size_t)(o_prev + 2 * m + 1) * SZ] : 0.f;
+      const float gr = right ? gs[o_prev + 2 * m + 1] : 0.f;
+      const float dl = __expf(gs[o_prev + 2 * m]);
+      nd[(size_t)(o + m) * SZ] = right ? __expf(gr) * lhs + rhs : lhs;
+      if (!right) continue;
+      for (int d0 = 0; i + d0 < p.nl; d0 += 4) {
+        float zl[4], zr[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int j = i + d0 + d;
+          zl[d] = zr[d] = 0.f;
+          if (j < p.nl && ((m >> (d0 + d)) & 1)) {
+            zl[d] = zz[((size_t)c0 * p.nl + j) * SZ];
+            zr[d] = zz[((size_t)c1 * p.nl + j) * SZ];
+          }
+        }
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int j = i + d0 + d;
+          if (j < p.nl && ((m >> (d0 + d)) & 1)) zz[((size_t)c0 * p.nl + j) * SZ] = zl[d] + dl * zr[d];
+        }
       }
+    }
+    __syncthreads();
+  }
+  for (int i = p.nl - 1; i >= 0; --i) {
+    const int nb = (p.N + (1 << i) - 1) >> i;
+    const int o = slot_of(p.N, i, 0);
+    const bool top = i + 1 >= p.nl;
+    const int op = top ? 0 : slot_of(p.N, i + 1, 0);
+    for (int m = w; m < nb; m += kTreeWaves) {
+      const float par = top ? 0.f : ou[(size_t)(op + (m >> 1)) * SZ];
+      float val = par;
+      if (!(m & 1) && m + 1 < nb) {
+        const float rn = zz[((size_t)(m + 1) * (1 << i) * p.nl + i) * SZ];
+        val = __expf(gs[o + m + 1]) * par + rn;
+      }
+      ou[(size_t)(o + m) * SZ] = val;
     }
     __syncthreads();
   }
@@ -111,7 +152,7 @@ constexpr int kLdsPerWorkgroup = 160 * 1024;
 struct BwdPlan {
   int C, N, nl, nslot, L, esize, smem_states, smem_grads;
   long BH;
-  size_t off_node, off_gsum, off_z, off_dA, ws_bytes;
+  size_t off_node, off_gsum, off_z, off_outs, off_dA, ws_bytes;
 };
 
 const BwdKernels* bwd_kernels(int dtype, int C, int DK, int DV) {
@@ -166,6 +207,7 @@ int make_bwd_plan(int B, int H, int T, int dk, int dv, int chunk, int dtype, Bwd
   pl.off_node = off; off = align256(off + (size_t)BH * pl.nslot * SZ * 4);
   pl.off_gsum = off; off = align256(off + (size_t)BH * pl.nslot * 4);
   pl.off_z = off;    off = align256(off + (size_t)BH * pl.N * pl.nl * SZ * 4);
+  pl.off_outs = off; off = align256(off + (size_t)BH * pl.nslot * SZ * 4);
   pl.off_dA = off;   off = align256(off + (size_t)BH * T * 4);
   pl.ws_bytes = off;
   pl.smem_states = lla::bwd::bwd_smem(pl.esize, C, dk, dv, false).total;
@@ -226,6 +268,7 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
   p.node = reinterpret_cast<float*>(w + pl.off_node);
   p.gsum = reinterpret_cast<float*>(w + pl.off_gsum);
   p.z = reinterpret_cast<float*>(w + pl.off_z);
+  p.outs = reinterpret_cast<float*>(w + pl.off_outs);
   p.dA = reinterpret_cast<float*>(w + pl.off_dA);
   p.BH = (int)pl.BH; p.T = a.T; p.L = pl.L; p.N = pl.N; p.nl = pl.nl; p.nslot = pl.nslot;
   void* args[] = {&p};
@@ -244,11 +287,11 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
     if (pl.nl > 1) {
       hipLaunchKernelGGL(lla::bwd::bwd_gsum_kernel, dim3((unsigned)pl.BH), dim3(256), 0, stream, p);
       if (hipGetLastError() != hipSuccess) return LLA_ERR_HIP;
-      const int SZ = a.dk * a.dv;   // a multiple of 64: the tree grid covers it exactly
-      hipLaunchKernelGGL(lla::bwd::bwd_tree_kernel, dim3((unsigned)(SZ / 64), (unsigned)pl.BH),
-                         dim3(256), 0, stream, p, SZ);
-      if (hipGetLastError() != hipSuccess) return LLA_ERR_HIP;
     }
+    const int SZ = a.dk * a.dv;   // a multiple of 64: the tree grid covers it exactly
+    hipLaunchKernelGGL(lla::bwd::bwd_tree_kernel, dim3((unsigned)(SZ / 64), (unsigned)pl.BH),
+                       dim3(64 * lla::bwd::kTreeWaves), 0, stream, p, SZ);
+    if (hipGetLastError() != hipSuccess) return LLA_ERR_HIP;
   }
   if (mark(1) != hipSuccess) return LLA_ERR_HIP;
   if (set_smem(ks->grads, pl.smem_grads) != hipSuccess) return LLA_ERR_HIP;
