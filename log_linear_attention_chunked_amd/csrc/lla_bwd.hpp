@@ -19,17 +19,17 @@
 // clear bit j, the right sibling block Y = (j, (c >> j) + 1) through
 //   RN(j, Y) = sum_{t in Y} lambda[t, J+1+j] exp(A_t - A_start(Y)) q_t do_t^T,
 // decayed over the right siblings of c's lower clear bits. lambda sits on the target here, so
-// RN cannot be built from the blocks below it like a forward node: each chunk contributes one
-// partial Z(c, j) per set bit j, and the partials are summed per block.
+// RN cannot be built from the blocks below it like a forward node: it is contracted from the
+// block's own q and do rows, level by level.
 //
 // Kernels, in stream order (bwd_gsum, bwd_tree and bwd_dloga, which do not depend on the element
 // type or the shapes, live in lla_bwd_api.hip):
-//   bwd_states  (chunk, head): F(c) = sum_s exp(g_c - A_s) k_s v_s^T (tree slot (0, c)),
-//               g_c, and Z(c, j) for the set bits j of c, on MFMA;
+//   bwd_states  (chunk, head): F(c) = sum_s exp(g_c - A_s) k_s v_s^T (tree slot (0, c)) and g_c;
+//   bwd_rn      (sub-block, head): the right blocks of level j split into sub-blocks of up to 8
+//               chunks; each sub-block's lambda-weighted, decayed q do^T on MFMA;
 //   bwd_gsum    (head): total log decay of every block (j, m), pairwise from the chunks;
-//   bwd_tree    (64 state elements, head): per block level i = 1 .. nl-1, the forward up-sweep
-//               node(i,m) = exp(G(i-1,2m+1)) node(i-1,2m) + node(i-1,2m+1) and, in place in the
-//               Z slots, the sums of the partials inside the odd blocks of every level j >= i;
+//   bwd_tree    (64 state elements, head): the forward up-sweep of the nodes, then a down-sweep
+//               that gives every chunk its combined right-sibling state;
 //   bwd_grads   (chunk, head): intra-chunk gradients on MFMA (masked S and W tiles, dlambda of
 //               the levels inside the chunk), node read-outs for dq and dlambda, the combined
 //               right-sibling state for dk and dv, dA;
@@ -64,11 +64,34 @@ struct BwdParams {
   float* glam;
   float* node;    // [BH][nslot][dk*dv]: forward Fenwick nodes over chunks, all block levels
   float* gsum;    // [BH][nslot]: total log decay of each block
-  float* z;       // [BH][N][nl][dk*dv]: partials Z(c, j); after bwd_tree Z(start of Y, j) = RN(j, Y)
+  float* rnp;     // [BH][items][dk*dv]: target-side block states, one per sub-block (see bwd_rn)
   float* outs;    // [BH][nslot][dk*dv]: down-sweep; level 0 = the combined right-sibling state of each chunk
   float* dA;      // [BH][T]
   int BH, T, L, N, nl, nslot;
+  int items;                  // sub-blocks per head over all levels
+  int rn_off[kLamCap + 1];    // first sub-block of each level
 };
+
+// Sub-blocks of the target side. At chunk level j the right blocks (2^j chunks) are split into
+// sub-blocks of 2^s chunks, s = min(j, kSubLog): sub-block sb (chunks sb << s ..) belongs to a
+// right block when bit j - s of sb is set. The k-th such sub-block of level j:
+constexpr int kSubLog = 3;
+__host__ __device__ inline int sub_log(int j) { return j < kSubLog ? j : kSubLog; }
+__host__ __device__ inline int sub_of_item(int j, int k) {
+  const int b = j - sub_log(j);
+  return ((k >> b) << (b + 1)) | (1 << b) | (k & ((1 << b) - 1));
+}
+__host__ __device__ inline int item_of_sub(int j, int sb) {
+  const int b = j - sub_log(j);
+  return ((sb >> (b + 1)) << b) | (sb & ((1 << b) - 1));
+}
+// sub-blocks of level j that hold at least one of the N chunks (bit j - s set in [0, ceil(N/2^s)))
+__host__ __device__ inline int items_of_level(int N, int j) {
+  const int s = sub_log(j), b = j - s;
+  const int M = (N + (1 << s) - 1) >> s;
+  const int rem = M & ((2 << b) - 1);
+  return ((M >> (b + 1)) << b) + (rem > (1 << b) ? rem - (1 << b) : 0);
+}
 
 // slot of block (i, m) in the per-head tree: blocks of level i' < i come first
 __host__ __device__ inline int slot_of(int N, int i, int m) {
@@ -196,6 +219,7 @@ __device__ __forceinline__ float sum16(float x) {
 // kernel table of one (dtype, chunk, dk, dv)
 struct BwdKernels {
   const void* states;   // bwd_states_kernel<T, C, DK, DV>
+  const void* rn;       // bwd_rn_kernel<T, C, DK, DV>
   const void* grads;    // bwd_grads_kernel<T, C, DK, DV>
 };
 
@@ -244,18 +268,21 @@ struct Chunk {
 
   // everything of chunk c of head bh; ends with a barrier. A = chunk-local inclusive prefix of
   // log_a, ea = exp(A), ws = exp(g - A) (decay from a position to the chunk's end).
+  // KV: k and v images; QO: q and do images; LAM: all lambda rows (else none)
+  template <bool KV = true, bool QO = true, bool LAM = true>
   __device__ void load(const BwdParams& p, int bh, int c, int nv, int tid, int nt) {
     const size_t row0 = (size_t)bh * p.T + (size_t)c * C;
-    stage<DK>(q, reinterpret_cast<const T*>(p.q) + row0 * DK, nv, tid, nt);
-    stage<DK>(k, reinterpret_cast<const T*>(p.k) + row0 * DK, nv, tid, nt);
-    stage<DV>(v, reinterpret_cast<const T*>(p.v) + row0 * DV, nv, tid, nt);
-    stage<DV>(o, reinterpret_cast<const T*>(p.dout) + row0 * DV, nv, tid, nt);
+    if (QO) stage<DK>(q, reinterpret_cast<const T*>(p.q) + row0 * DK, nv, tid, nt);
+    if (KV) stage<DK>(k, reinterpret_cast<const T*>(p.k) + row0 * DK, nv, tid, nt);
+    if (KV) stage<DV>(v, reinterpret_cast<const T*>(p.v) + row0 * DV, nv, tid, nt);
+    if (QO) stage<DV>(o, reinterpret_cast<const T*>(p.dout) + row0 * DV, nv, tid, nt);
     // every level slot is written: rows past nv and levels past L read as zero weights
     const float* lg = p.lam + row0 * p.L;
-    for (int i = tid; i < C * kLamCap; i += nt) {
-      const int r = i / kLamCap, l = i % kLamCap;
-      lam[i] = (r < nv && l < p.L) ? lg[r * p.L + l] : 0.f;
-    }
+    if (LAM)
+      for (int i = tid; i < C * kLamCap; i += nt) {
+        const int r = i / kLamCap, l = i % kLamCap;
+        lam[i] = (r < nv && l < p.L) ? lg[r * p.L + l] : 0.f;
+      }
     // chunk-local inclusive prefix of log_a by wave 0: each lane holds E consecutive rows
     if (tid < 64) {
       constexpr int E = C > 64 ? C / 64 : 1;
@@ -320,32 +347,82 @@ __device__ __forceinline__ void outer_store(const T* X, int RX, const T* Y, int 
 template <typename T, int C, int DK, int DV>
 __global__ void __launch_bounds__(64 * Waves<C>::NW)
 bwd_states_kernel(BwdParams p) {
-  constexpr int NW = Waves<C>::NW, NT = 64 * NW, J = ilog2(C);
+  constexpr int NW = Waves<C>::NW, NT = 64 * NW;
+  using CH = Chunk<T, C, DK, DV>;
   extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
   const int c = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int nv = min(C, p.T - c * C);
   const BwdSmem Lo = bwd_smem((int)sizeof(T), C, DK, DV, false);
-  Chunk<T, C, DK, DV> ch;
+  CH ch;
   ch.bind(sm, Lo);
-  ch.load(p, bh, c, nv, tid, NT);
-  using CH = Chunk<T, C, DK, DV>;
-
+  ch.template load<true, false, false>(p, bh, c, nv, tid, NT);
   const size_t SZ = (size_t)DK * DV;
   // F(c): keys weighted by their decay to the chunk's end
   outer_store<T, C, DK, DV, NW>(ch.k, CH::RK, ch.v, CH::RV, ch.ws,
                                 p.node + ((size_t)bh * p.nslot + c) * SZ, w, lane);
   if (tid == 0) p.gsum[(size_t)bh * p.nslot + c] = ch.g;
+}
 
-  // Z(c, j) for each set bit j of c: targets weighted by lambda of level J+1+j and exp(A)
-  float* sc = ch.ws;   // reused as the per-position weight once F is done
-  for (int jl = 0; jl < p.nl; ++jl) {
-    if (!((c >> jl) & 1)) continue;
+// ----------------------------------------------------------------------------------------
+// bwd_rn: one target-side sub-block state per workgroup,
+//   P(j, sb) = sum over the positions t of sub-block sb of lambda[t, J+1+j] exp(A_t - A_0) q_t do_t^T
+// with A_0 the prefix decay just before the sub-block, accumulated chunk by chunk on MFMA
+// ----------------------------------------------------------------------------------------
+
+template <typename T, int C, int DK, int DV>
+__global__ void __launch_bounds__(64 * Waves<C>::NW)
+bwd_rn_kernel(BwdParams p) {
+  constexpr int NW = Waves<C>::NW, NT = 64 * NW, J = ilog2(C);
+  constexpr int AB = cdiv(DK / 16, NW), NB = DV / 16;
+  using CH = Chunk<T, C, DK, DV>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
+  const int item = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, jj = lane & 15, g4 = lane >> 4;
+  int j = 0;
+  while (j + 1 < p.nl && p.rn_off[j + 1] <= item) ++j;
+  const int sb = sub_of_item(j, item - p.rn_off[j]);
+  const int c0 = sb << sub_log(j), c1 = min(c0 + (1 << sub_log(j)), p.N);
+  const BwdSmem Lo = bwd_smem((int)sizeof(T), C, DK, DV, false);
+  CH ch;
+  ch.bind(sm, Lo);
+  float* sc = ch.lam;   // per-position weights of the current chunk
+  f32x4 acc[AB][NB];
+#pragma unroll
+  for (int x = 0; x < AB; ++x)
+#pragma unroll
+    for (int y = 0; y < NB; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float eoff = 0.f;     // log decay from the sub-block's start to the current chunk's start
+  for (int c = c0; c < c1; ++c) {
+    const int nv = min(C, p.T - c * C);
+    if (c > c0) __syncthreads();   // the previous chunk's images are no longer read
+    ch.template load<false, true, false>(p, bh, c, nv, tid, NT);
+    const size_t row0 = (size_t)bh * p.T + (size_t)c * C;
+    for (int r = tid; r < C; r += NT)
+      sc[r] = r < nv ? p.lam[(row0 + r) * p.L + J + 1 + j] * __expf(eoff + ch.al[r]) : 0.f;
     __syncthreads();
-    for (int r = tid; r < C; r += NT) sc[r] = ch.lam[r * kLamCap + J + 1 + jl] * ch.ea[r];
-    __syncthreads();
-    outer_store<T, C, DK, DV, NW>(ch.q, CH::RK, ch.o, CH::RV, sc,
-                                  p.z + (((size_t)bh * p.N + c) * p.nl + jl) * SZ, w, lane);
+#pragma unroll
+    for (int x = 0; x < AB; ++x) {
+      const int ab = w + NW * x;
+      if (ab >= DK / 16) break;
+#pragma unroll
+      for (int y = 0; y < NB; ++y)
+#pragma unroll
+        for (int s0 = 0; s0 < C; s0 += 32)
+          mma(acc[x][y], frag_col<T, C>(ch.q, CH::RK, s0 + 8 * g4, ab * 16 + jj),
+              frag_col<T, C>(ch.o, CH::RV, s0 + 8 * g4, y * 16 + jj, sc));
+    }
+    eoff += ch.g;
+  }
+  float* dst = p.rnp + ((size_t)bh * p.items + item) * ((size_t)DK * DV);
+#pragma unroll
+  for (int x = 0; x < AB; ++x) {
+    const int ab = w + NW * x;
+    if (ab >= DK / 16) break;
+#pragma unroll
+    for (int y = 0; y < NB; ++y)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dst[(size_t)(ab * 16 + 4 * g4 + r) * DV + y * 16 + jj] = acc[x][y][r];
   }
 }
 
@@ -653,6 +730,7 @@ namespace bwd {
 template <typename TY, int C, int DK, int DV>
 BwdKernels make_bwd() {
   return BwdKernels{reinterpret_cast<const void*>(&bwd_states_kernel<TY, C, DK, DV>),
+                    reinterpret_cast<const void*>(&bwd_rn_kernel<TY, C, DK, DV>),
                     reinterpret_cast<const void*>(&bwd_grads_kernel<TY, C, DK, DV>)};
 }
 

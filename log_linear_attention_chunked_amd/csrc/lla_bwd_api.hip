@@ -1,6 +1,6 @@
 // lla_bwd_api.hip — C ABI of the backward pass: argument validation, plan (chunk, tree and
-// workspace layout) and the stream-ordered launch sequence bwd_states -> bwd_gsum -> bwd_tree
-// -> bwd_grads -> bwd_dloga. The contract is documented in include/loglinear_attn.h.
+// workspace layout) and the stream-ordered launch sequence bwd_states -> bwd_rn -> bwd_gsum ->
+// bwd_tree -> bwd_grads -> bwd_dloga. The contract is documented in include/loglinear_attn.h.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -32,12 +32,11 @@ __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdParams p) {
 
 // ----------------------------------------------------------------------------------------
 // bwd_tree: 64 state elements of one head per workgroup, 16 waves splitting the blocks of a level.
-//   up-sweep, levels i = 1 .. nl-1: node(i,m) = exp(G(i-1,2m+1)) node(i-1,2m) + node(i-1,2m+1);
-//     in the Z slots, the partial sums of every level j >= i whose odd block contains (i, m):
-//     Z(m<<i, j) += exp(G(i-1,2m)) Z((2m+1)<<(i-1), j), so that Z(start of Y, j) = RN(j, Y).
+//   up-sweep, levels i = 1 .. nl-1: node(i,m) = exp(G(i-1,2m+1)) node(i-1,2m) + node(i-1,2m+1).
 //   down-sweep, levels i = nl-1 .. 0: Out(i, m) = what the chunks of block (i, m) receive from
 //     later blocks at levels >= i, decayed to the end of (i, m):
-//       left child with a right sibling Y: Out = exp(G(Y)) Out(parent) + RN(i, Y);
+//       left child with a right sibling Y: Out = exp(G(Y)) Out(parent) + RN(i, Y), RN(i, Y) the
+//       sum of Y's sub-block states (bwd_rn), each decayed over the sub-blocks before it;
 //       otherwise: Out = Out(parent); the parent of the top level holds nothing.
 //     Out(0, c) is the combined right-sibling state of chunk c.
 // ----------------------------------------------------------------------------------------
@@ -50,38 +49,17 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
   // the grid has exactly SZ / 64 columns of workgroups (SZ = dk*dv is a multiple of 64)
   const float* gs = p.gsum + (size_t)bh * p.nslot;
   float* nd = p.node + (size_t)bh * p.nslot * SZ + e;
-  float* zz = p.z + (size_t)bh * p.N * p.nl * SZ + e;
+  const float* rp = p.rnp + (size_t)bh * p.items * SZ + e;
   float* ou = p.outs + (size_t)bh * p.nslot * SZ + e;
   for (int i = 1; i < p.nl; ++i) {
     const int nprev = (p.N + (1 << (i - 1)) - 1) >> (i - 1), nb = (p.N + (1 << i) - 1) >> i;
     const int o_prev = slot_of(p.N, i - 1, 0), o = slot_of(p.N, i, 0);
     for (int m = w; m < nb; m += kTreeWaves) {
       const bool right = 2 * m + 1 < nprev;
-      const int c0 = m << i, c1 = (2 * m + 1) << (i - 1);
-      // loads first (nothing stored below is read here), in groups of 4 partial levels
       const float lhs = nd[(size_t)(o_prev + 2 * m) * SZ];
       const float rhs = right ? nd[(size_t)(o_prev + 2 * m + 1) * SZ] : 0.f;
       const float gr = right ? gs[o_prev + 2 * m + 1] : 0.f;
-      const float dl = __expf(gs[o_prev + 2 * m]);
       nd[(size_t)(o + m) * SZ] = right ? __expf(gr) * lhs + rhs : lhs;
-      if (!right) continue;
-      for (int d0 = 0; i + d0 < p.nl; d0 += 4) {
-        float zl[4], zr[4];
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int j = i + d0 + d;
-          zl[d] = zr[d] = 0.f;
-          if (j < p.nl && ((m >> (d0 + d)) & 1)) {
-            zl[d] = zz[((size_t)c0 * p.nl + j) * SZ];
-            zr[d] = zz[((size_t)c1 * p.nl + j) * SZ];
-          }
-        }
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const int j = i + d0 + d;
-          if (j < p.nl && ((m >> (d0 + d)) & 1)) zz[((size_t)c0 * p.nl + j) * SZ] = zl[d] + dl * zr[d];
-        }
-      }
     }
     __syncthreads();
   }
@@ -90,11 +68,19 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
     const int o = slot_of(p.N, i, 0);
     const bool top = i + 1 >= p.nl;
     const int op = top ? 0 : slot_of(p.N, i + 1, 0);
+    const int s = sub_log(i), b = i - s, os = slot_of(p.N, s, 0);
+    const int nsub = (p.N + (1 << s) - 1) >> s;
     for (int m = w; m < nb; m += kTreeWaves) {
       const float par = top ? 0.f : ou[(size_t)(op + (m >> 1)) * SZ];
       float val = par;
       if (!(m & 1) && m + 1 < nb) {
-        const float rn = zz[((size_t)(m + 1) * (1 << i) * p.nl + i) * SZ];
+        const int sb0 = (m + 1) << b, sb1 = min((m + 2) << b, nsub);
+        float rn = 0.f, dec = 0.f;
+#pragma unroll 4
+        for (int sb = sb0; sb < sb1; ++sb) {
+          rn += __expf(dec) * rp[(size_t)(p.rn_off[i] + item_of_sub(i, sb)) * SZ];
+          dec += gs[os + sb];
+        }
         val = __expf(gs[o + m + 1]) * par + rn;
       }
       ou[(size_t)(o + m) * SZ] = val;
@@ -152,7 +138,8 @@ constexpr int kLdsPerWorkgroup = 160 * 1024;
 struct BwdPlan {
   int C, N, nl, nslot, L, esize, smem_states, smem_grads;
   long BH;
-  size_t off_node, off_gsum, off_z, off_outs, off_dA, ws_bytes;
+  int items, rn_off[lla::kLamCap + 1];
+  size_t off_node, off_gsum, off_rnp, off_outs, off_dA, ws_bytes;
 };
 
 const BwdKernels* bwd_kernels(int dtype, int C, int DK, int DV) {
@@ -206,7 +193,12 @@ int make_bwd_plan(int B, int H, int T, int dk, int dv, int chunk, int dtype, Bwd
   size_t off = 0;
   pl.off_node = off; off = align256(off + (size_t)BH * pl.nslot * SZ * 4);
   pl.off_gsum = off; off = align256(off + (size_t)BH * pl.nslot * 4);
-  pl.off_z = off;    off = align256(off + (size_t)BH * pl.N * pl.nl * SZ * 4);
+  pl.items = 0;
+  for (int j = 0; j <= lla::kLamCap; ++j) {
+    pl.rn_off[j] = pl.items;
+    if (j < pl.nl) pl.items += lla::bwd::items_of_level(pl.N, j);
+  }
+  pl.off_rnp = off;  off = align256(off + (size_t)BH * pl.items * SZ * 4);
   pl.off_outs = off; off = align256(off + (size_t)BH * pl.nslot * SZ * 4);
   pl.off_dA = off;   off = align256(off + (size_t)BH * T * 4);
   pl.ws_bytes = off;
@@ -267,7 +259,9 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
   char* w = static_cast<char*>(ws);
   p.node = reinterpret_cast<float*>(w + pl.off_node);
   p.gsum = reinterpret_cast<float*>(w + pl.off_gsum);
-  p.z = reinterpret_cast<float*>(w + pl.off_z);
+  p.rnp = reinterpret_cast<float*>(w + pl.off_rnp);
+  p.items = pl.items;
+  for (int j = 0; j <= lla::kLamCap; ++j) p.rn_off[j] = pl.rn_off[j];
   p.outs = reinterpret_cast<float*>(w + pl.off_outs);
   p.dA = reinterpret_cast<float*>(w + pl.off_dA);
   p.BH = (int)pl.BH; p.T = a.T; p.L = pl.L; p.N = pl.N; p.nl = pl.nl; p.nslot = pl.nslot;
@@ -283,6 +277,10 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
   if (pl.nl > 0) {
     if (set_smem(ks->states, pl.smem_states) != hipSuccess) return LLA_ERR_HIP;
     if (hipLaunchKernel(ks->states, chunks, dim3(NT), args, pl.smem_states, stream) != hipSuccess)
+      return LLA_ERR_HIP;
+    if (set_smem(ks->rn, pl.smem_states) != hipSuccess) return LLA_ERR_HIP;
+    if (hipLaunchKernel(ks->rn, dim3((unsigned)pl.items, (unsigned)pl.BH), dim3(NT), args,
+                        pl.smem_states, stream) != hipSuccess)
       return LLA_ERR_HIP;
     if (pl.nl > 1) {
       hipLaunchKernelGGL(lla::bwd::bwd_gsum_kernel, dim3((unsigned)pl.BH), dim3(256), 0, stream, p);

@@ -301,8 +301,9 @@ def test_bwd_defaults_and_workspace(L):
     # headline shape: N = 128 chunks, 7 chunk levels, 128 + 64 + ... + 2 = 254 tree slots per head
     n = ws(4, 16, 8192, 64, 64, 64, 0)
     sz = 64 * 64 * 4
-    # nodes, block decays, per-level partials, down-sweep states, per-position dA
-    expect = 64 * 254 * sz + 64 * 254 * 4 + 64 * 128 * 7 * sz + 64 * 254 * sz + 64 * 8192 * 4
+    # nodes, block decays, target-side sub-block states (64 + 32 + 16 + 4 x 8 = 144 per head),
+    # down-sweep states, per-position dA
+    expect = 64 * 254 * sz + 64 * 254 * 4 + 64 * 144 * sz + 64 * 254 * sz + 64 * 8192 * 4
     assert expect <= n <= expect + 4 * 256
     # one chunk: only the per-position dA
     assert ws(1, 2, 64, 64, 64, 64, 0) == 2 * 64 * 4
