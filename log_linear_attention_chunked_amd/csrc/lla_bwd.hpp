@@ -375,6 +375,9 @@ __global__ void __launch_bounds__(64 * Waves<C>::NW)
 bwd_rn_kernel(BwdParams p) {
   constexpr int NW = Waves<C>::NW, NT = 64 * NW, J = ilog2(C);
   constexpr int AB = cdiv(DK / 16, NW), NB = DV / 16;
+  constexpr int ES = (int)sizeof(T), EPV = 16 / ES;
+  constexpr int PQ = C * DK / EPV, PO = C * DV / EPV;        // 16-byte pieces of the q, do rows
+  constexpr int NQ = cdiv(PQ, NT), NO = cdiv(PO, NT);
   using CH = Chunk<T, C, DK, DV>;
   extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
   const int item = blockIdx.x, bh = blockIdx.y;
@@ -383,7 +386,7 @@ bwd_rn_kernel(BwdParams p) {
   while (j + 1 < p.nl && p.rn_off[j + 1] <= item) ++j;
   const int sb = sub_of_item(j, item - p.rn_off[j]);
   const int c0 = sb << sub_log(j), c1 = min(c0 + (1 << sub_log(j)), p.N);
-  const BwdSmem Lo = bwd_smem((int)sizeof(T), C, DK, DV, false);
+  const BwdSmem Lo = bwd_smem(ES, C, DK, DV, false);
   CH ch;
   ch.bind(sm, Lo);
   float* sc = ch.lam;   // per-position weights of the current chunk
@@ -392,15 +395,61 @@ bwd_rn_kernel(BwdParams p) {
   for (int x = 0; x < AB; ++x)
 #pragma unroll
     for (int y = 0; y < NB; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // the next chunk's q and do rows, log_a and lambda of level J+1+j, in registers: issued before
+  // the current chunk's products so that their latency hides behind them
+  u32x4 rq[NQ], ro[NO];
+  float rla = 0.f, rlm = 0.f;
+  auto fetch = [&](int c) {
+    const int nv = min(C, p.T - c * C);
+    const size_t row0 = (size_t)bh * p.T + (size_t)c * C;
+    const u32x4* gq = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(p.q) + row0 * DK);
+    const u32x4* go = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(p.dout) + row0 * DV);
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int idx = tid + u * NT;
+      rq[u] = (idx < PQ && idx / (DK / EPV) < nv) ? gq[idx] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+      const int idx = tid + u * NT;
+      ro[u] = (idx < PO && idx / (DV / EPV) < nv) ? go[idx] : u32x4{0u, 0u, 0u, 0u};
+    }
+    rla = lane < nv ? p.log_a[row0 + lane] : 0.f;
+    rlm = lane < nv ? p.lam[(row0 + lane) * p.L + J + 1 + j] : 0.f;
+  };
+  fetch(c0);
   float eoff = 0.f;     // log decay from the sub-block's start to the current chunk's start
   for (int c = c0; c < c1; ++c) {
-    const int nv = min(C, p.T - c * C);
-    if (c > c0) __syncthreads();   // the previous chunk's images are no longer read
-    ch.template load<false, true, false>(p, bh, c, nv, tid, NT);
-    const size_t row0 = (size_t)bh * p.T + (size_t)c * C;
-    for (int r = tid; r < C; r += NT)
-      sc[r] = r < nv ? p.lam[(row0 + r) * p.L + J + 1 + j] * __expf(eoff + ch.al[r]) : 0.f;
+    if (c > c0) __syncthreads();   // the previous chunk's images and weights are no longer read
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int idx = tid + u * NT;
+      if (idx < PQ) {
+        const int r = idx / (DK / EPV), f = (idx % (DK / EPV)) * EPV;
+        *reinterpret_cast<u32x4*>(ch.q + r * CH::RK + f) = rq[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+      const int idx = tid + u * NT;
+      if (idx < PO) {
+        const int r = idx / (DV / EPV), f = (idx % (DV / EPV)) * EPV;
+        *reinterpret_cast<u32x4*>(ch.o + r * CH::RV + f) = ro[u];
+      }
+    }
+    // every wave scans the chunk's log_a (C <= 64 positions, one per lane); wave 0 writes the
+    // weights lambda * exp(decay from the sub-block's start)
+    float incl = lane < C ? rla : 0.f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    if (w == 0 && lane < C) sc[lane] = rlm * __expf(eoff + incl);
+    eoff += __shfl(incl, C - 1);
     __syncthreads();
+    if (c + 1 < c1) fetch(c + 1);
 #pragma unroll
     for (int x = 0; x < AB; ++x) {
       const int ab = w + NW * x;
@@ -412,7 +461,6 @@ bwd_rn_kernel(BwdParams p) {
           mma(acc[x][y], frag_col<T, C>(ch.q, CH::RK, s0 + 8 * g4, ab * 16 + jj),
               frag_col<T, C>(ch.o, CH::RV, s0 + 8 * g4, y * 16 + jj, sc));
     }
-    eoff += ch.g;
   }
   float* dst = p.rnp + ((size_t)bh * p.items + item) * ((size_t)DK * DV);
 #pragma unroll

@@ -43,26 +43,41 @@ __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdParams p) {
 
 constexpr int kTreeWaves = 16;
 
+// LDS: every block value of the 64 elements, [slot][64] floats (up-sweep nodes, then the
+// down-sweep's values), when that fits; otherwise the up-sweep reads level i-1 back from the
+// node array and the down-sweep keeps every level in the outs array.
+template <bool LDS>
 __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, int SZ) {
-  const int bh = blockIdx.y;
-  const int e = blockIdx.x * 64 + (threadIdx.x & 63), w = threadIdx.x >> 6;
+  extern __shared__ __attribute__((aligned(16))) float tl[];
+  const int bh = blockIdx.y, lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 64 + lane, w = threadIdx.x >> 6;
   // the grid has exactly SZ / 64 columns of workgroups (SZ = dk*dv is a multiple of 64)
-  const float* gs = p.gsum + (size_t)bh * p.nslot;
-  float* nd = p.node + (size_t)bh * p.nslot * SZ + e;
-  const float* rp = p.rnp + (size_t)bh * p.items * SZ + e;
-  float* ou = p.outs + (size_t)bh * p.nslot * SZ + e;
+  const float* __restrict__ gs = p.gsum + (size_t)bh * p.nslot;
+  float* __restrict__ nd = p.node + (size_t)bh * p.nslot * SZ + e;
+  const float* __restrict__ rp = p.rnp + (size_t)bh * p.items * SZ + e;
+  float* __restrict__ ou = p.outs + (size_t)bh * p.nslot * SZ + e;
+  if (LDS) {
+    for (int m = w; m < p.N; m += kTreeWaves) tl[m * 64 + lane] = nd[(size_t)m * SZ];
+    __syncthreads();
+  }
   for (int i = 1; i < p.nl; ++i) {
     const int nprev = (p.N + (1 << (i - 1)) - 1) >> (i - 1), nb = (p.N + (1 << i) - 1) >> i;
     const int o_prev = slot_of(p.N, i - 1, 0), o = slot_of(p.N, i, 0);
     for (int m = w; m < nb; m += kTreeWaves) {
       const bool right = 2 * m + 1 < nprev;
-      const float lhs = nd[(size_t)(o_prev + 2 * m) * SZ];
-      const float rhs = right ? nd[(size_t)(o_prev + 2 * m + 1) * SZ] : 0.f;
-      const float gr = right ? gs[o_prev + 2 * m + 1] : 0.f;
-      nd[(size_t)(o + m) * SZ] = right ? __expf(gr) * lhs + rhs : lhs;
+      const int sl = o_prev + 2 * m;
+      const float lhs = LDS ? tl[sl * 64 + lane] : nd[(size_t)sl * SZ];
+      const float rhs = right ? (LDS ? tl[(sl + 1) * 64 + lane] : nd[(size_t)(sl + 1) * SZ]) : 0.f;
+      const float gr = right ? gs[sl + 1] : 0.f;
+      const float val = right ? __expf(gr) * lhs + rhs : lhs;
+      nd[(size_t)(o + m) * SZ] = val;
+      if (LDS) tl[(o + m) * 64 + lane] = val;
     }
     __syncthreads();
   }
+  // down-sweep; a wave takes KB of its blocks at a time and loads all their right-block states
+  // before it uses any of them
+  constexpr int KB = 8;
   for (int i = p.nl - 1; i >= 0; --i) {
     const int nb = (p.N + (1 << i) - 1) >> i;
     const int o = slot_of(p.N, i, 0);
@@ -70,20 +85,37 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
     const int op = top ? 0 : slot_of(p.N, i + 1, 0);
     const int s = sub_log(i), b = i - s, os = slot_of(p.N, s, 0);
     const int nsub = (p.N + (1 << s) - 1) >> s;
-    for (int m = w; m < nb; m += kTreeWaves) {
-      const float par = top ? 0.f : ou[(size_t)(op + (m >> 1)) * SZ];
-      float val = par;
-      if (!(m & 1) && m + 1 < nb) {
-        const int sb0 = (m + 1) << b, sb1 = min((m + 2) << b, nsub);
-        float rn = 0.f, dec = 0.f;
-#pragma unroll 4
-        for (int sb = sb0; sb < sb1; ++sb) {
-          rn += __expf(dec) * rp[(size_t)(p.rn_off[i] + item_of_sub(i, sb)) * SZ];
-          dec += gs[os + sb];
+    for (int m0 = w; m0 < nb; m0 += kTreeWaves * KB) {
+      float rn[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int m = m0 + u * kTreeWaves;
+        rn[u] = 0.f;
+        if (m < nb && !(m & 1) && m + 1 < nb) {
+          const int sb0 = (m + 1) << b, sb1 = min((m + 2) << b, nsub);
+          if (sb1 - sb0 == 1) {
+            rn[u] = rp[(size_t)(p.rn_off[i] + item_of_sub(i, sb0)) * SZ];
+          } else {
+            float dec = 0.f;
+            for (int sb = sb0; sb < sb1; ++sb) {
+              rn[u] += __expf(dec) * rp[(size_t)(p.rn_off[i] + item_of_sub(i, sb)) * SZ];
+              dec += gs[os + sb];
+            }
+          }
         }
-        val = __expf(gs[o + m + 1]) * par + rn;
       }
-      ou[(size_t)(o + m) * SZ] = val;
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int m = m0 + u * kTreeWaves;
+        if (m >= nb) break;
+        const int ps = op + (m >> 1);
+        const float par = top ? 0.f : (LDS ? tl[ps * 64 + lane] : ou[(size_t)ps * SZ]);
+        const float val = (!(m & 1) && m + 1 < nb) ? __expf(gs[o + m + 1]) * par + rn[u] : par;
+        // the level-i slots of tl held nodes that are no longer read: level i+1 was read above,
+        // and the up-sweep is over
+        if (LDS) tl[(o + m) * 64 + lane] = val;
+        if (!LDS || i == 0) ou[(size_t)(o + m) * SZ] = val;
+      }
     }
     __syncthreads();
   }
@@ -136,7 +168,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int kLdsPerWorkgroup = 160 * 1024;
 
 struct BwdPlan {
-  int C, N, nl, nslot, L, esize, smem_states, smem_grads;
+  int C, N, nl, nslot, L, esize, smem_states, smem_grads, tree_smem;
   long BH;
   int items, rn_off[lla::kLamCap + 1];
   size_t off_node, off_gsum, off_rnp, off_outs, off_dA, ws_bytes;
@@ -204,6 +236,8 @@ int make_bwd_plan(int B, int H, int T, int dk, int dv, int chunk, int dtype, Bwd
   pl.ws_bytes = off;
   pl.smem_states = lla::bwd::bwd_smem(pl.esize, C, dk, dv, false).total;
   pl.smem_grads = grads_smem(pl.esize, C, dk, dv);
+  // the tree kernel keeps its 64 elements' block values in shared memory when they fit
+  pl.tree_smem = (size_t)pl.nslot * 64 * 4 <= (size_t)kLdsPerWorkgroup ? pl.nslot * 64 * 4 : 0;
   if (pl.smem_grads > kLdsPerWorkgroup) return LLA_ERR_UNSUPPORTED;
   return LLA_OK;
 }
@@ -287,8 +321,14 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
       if (hipGetLastError() != hipSuccess) return LLA_ERR_HIP;
     }
     const int SZ = a.dk * a.dv;   // a multiple of 64: the tree grid covers it exactly
-    hipLaunchKernelGGL(lla::bwd::bwd_tree_kernel, dim3((unsigned)(SZ / 64), (unsigned)pl.BH),
-                       dim3(64 * lla::bwd::kTreeWaves), 0, stream, p, SZ);
+    const dim3 tgrid((unsigned)(SZ / 64), (unsigned)pl.BH), tblock(64 * lla::bwd::kTreeWaves);
+    if (pl.tree_smem > 0) {
+      const void* fn = reinterpret_cast<const void*>(&lla::bwd::bwd_tree_kernel<true>);
+      if (set_smem(fn, pl.tree_smem) != hipSuccess) return LLA_ERR_HIP;
+      hipLaunchKernelGGL(lla::bwd::bwd_tree_kernel<true>, tgrid, tblock, pl.tree_smem, stream, p, SZ);
+    } else {
+      hipLaunchKernelGGL(lla::bwd::bwd_tree_kernel<false>, tgrid, tblock, 0, stream, p, SZ);
+    }
     if (hipGetLastError() != hipSuccess) return LLA_ERR_HIP;
   }
   if (mark(1) != hipSuccess) return LLA_ERR_HIP;
