@@ -29,7 +29,9 @@
 //               chunks; each sub-block's lambda-weighted, decayed q do^T on MFMA;
 //   bwd_gsum    (head): total log decay of every block (j, m), pairwise from the chunks;
 //   bwd_tree    (64 state elements, head): the forward up-sweep of the nodes, then a down-sweep
-//               that gives every chunk its combined right-sibling state;
+//               that gives every chunk its combined right-sibling state; sums in fp32, and a copy
+//               in the element type of what the gradient kernel reads (it rounds its MFMA
+//               operands to that type in any case);
 //   bwd_grads   (chunk, head): intra-chunk gradients on MFMA (masked S and W tiles, dlambda of
 //               the levels inside the chunk), node read-outs for dq and dlambda, the combined
 //               right-sibling state for dk and dv, dA;
@@ -65,7 +67,11 @@ struct BwdParams {
   float* node;    // [BH][nslot][dk*dv]: forward Fenwick nodes over chunks, all block levels
   float* gsum;    // [BH][nslot]: total log decay of each block
   float* rnp;     // [BH][items][dk*dv]: target-side block states, one per sub-block (see bwd_rn)
-  float* outs;    // [BH][nslot][dk*dv]: down-sweep; level 0 = the combined right-sibling state of each chunk
+  float* outs;    // [BH][nslot][dk*dv]: down-sweep values (only when the tree cannot keep them on chip)
+  void* node_e;   // [BH][nslot][dk*dv] in the element type: the nodes as the gradient kernel reads them
+  void* u_e;      // [BH][N][dk*dv] in the element type: each chunk's combined right-sibling state
+  void* node_lo;  // bf16 only: node - bf16(node), so that hi + lo carries ~16 mantissa bits
+  void* u_lo;     // bf16 only: the same for the combined right-sibling states
   float* dA;      // [BH][T]
   int BH, T, L, N, nl, nslot;
   int items;                  // sub-blocks per head over all levels
@@ -102,7 +108,7 @@ __host__ __device__ inline int slot_of(int N, int i, int m) {
 
 // shared-memory layout of bwd_states / bwd_grads (host and device agree)
 struct BwdSmem {
-  int q, k, v, o, p1, p2, lam, al, ea, ws, ust, nst, total;
+  int q, k, v, o, p1, p2, lam, al, ea, ws, ust, nst, cg, total;
 };
 
 __host__ __device__ inline BwdSmem bwd_smem(int es, int C, int DK, int DV, bool grads) {
@@ -115,7 +121,8 @@ __host__ __device__ inline BwdSmem bwd_smem(int es, int C, int DK, int DV, bool 
   s.v = take(C * rv * es);
   s.o = take(C * rv * es);
   s.p1 = grads ? take(C * rc * es) : off;
-  s.p2 = grads ? take(C * rc * es) : off;
+  // P2, and (bf16) once the intra-chunk products are done, the low part of a [dk][dv] state image
+  s.p2 = grads ? take((es == 2 && DK * rv > C * rc ? DK * rv : C * rc) * es) : off;
   s.lam = take(C * kLamCap * 4);
   s.al = take(C * 4);
   s.ea = take(C * 4);
@@ -124,6 +131,7 @@ __host__ __device__ inline BwdSmem bwd_smem(int es, int C, int DK, int DV, bool 
   // products are done) one Fenwick node at a time
   s.ust = grads ? take(DK * rv * es) : off;
   s.nst = s.ust;
+  s.cg = grads ? take(4 * C * 4) : off;   // per-wave column sums of G = M S W
   s.total = (off + 255) & ~255;
   return s;
 }
@@ -195,6 +203,33 @@ __device__ __forceinline__ Frag<T> frag_col(const T* img, int RS, int k, int c,
     hi[e] *= sc[k + 4 + e];
   }
   return frag_from<T>(lo, hi);
+}
+
+// x * sc (a scaled column fragment) as hi + lo with hi = bf16(x sc), lo = bf16(x sc - hi), so
+// that a product with it keeps ~16 mantissa bits of the weights; fp32: lo = 0
+template <typename T, int K>
+__device__ __forceinline__ void frag_col_split(const T* img, int RS, int k, int c, const float* sc,
+                                               Frag<T>& hi, Frag<T>& lo) {
+  const Frag<T> f = frag_col<T, K>(img, RS, k, c, sc);
+  if constexpr (sizeof(T) == 2) {
+    // recompute the exact products in fp32 from the unscaled elements
+    const Frag<T> u = frag_col<T, K>(img, RS, k, c);
+    f32x4 ulo, uhi, hlo, hhi;
+    frag_to_f32(u, ulo, uhi);
+    frag_to_f32(f, hlo, hhi);
+    if (k < K) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ulo[e] = ulo[e] * sc[k + e] - hlo[e];
+        uhi[e] = uhi[e] * sc[k + 4 + e] - hhi[e];
+      }
+    }
+    hi = f;
+    lo = frag_from<T>(ulo, uhi);
+  } else {
+    hi = f;
+    lo = zero_frag<T>();
+  }
 }
 
 // a row-major float state in global memory, g[r][k .. k+7] (row stride RS), as an operand
@@ -335,8 +370,10 @@ __device__ __forceinline__ void outer_store(const T* X, int RX, const T* Y, int 
 #pragma unroll
       for (int s0 = 0; s0 < C; s0 += 32) {
         const Frag<T> a = frag_col<T, C>(X, RX, s0 + 8 * g, ab * 16 + j);
-        const Frag<T> b = frag_col<T, C>(Y, RY, s0 + 8 * g, bb * 16 + j, sc);
-        mma(acc, a, b);
+        Frag<T> bh, bl;
+        frag_col_split<T, C>(Y, RY, s0 + 8 * g, bb * 16 + j, sc, bh, bl);
+        mma(acc, a, bh);
+        if constexpr (sizeof(T) == 2) mma(acc, a, bl);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) dst[(size_t)(ab * 16 + 4 * g + r) * DB + bb * 16 + j] = acc[r];
@@ -457,9 +494,13 @@ bwd_rn_kernel(BwdParams p) {
 #pragma unroll
       for (int y = 0; y < NB; ++y)
 #pragma unroll
-        for (int s0 = 0; s0 < C; s0 += 32)
-          mma(acc[x][y], frag_col<T, C>(ch.q, CH::RK, s0 + 8 * g4, ab * 16 + jj),
-              frag_col<T, C>(ch.o, CH::RV, s0 + 8 * g4, y * 16 + jj, sc));
+        for (int s0 = 0; s0 < C; s0 += 32) {
+          const Frag<T> a = frag_col<T, C>(ch.q, CH::RK, s0 + 8 * g4, ab * 16 + jj);
+          Frag<T> bh, bl;
+          frag_col_split<T, C>(ch.o, CH::RV, s0 + 8 * g4, y * 16 + jj, sc, bh, bl);
+          mma(acc[x][y], a, bh);
+          if constexpr (sizeof(T) == 2) mma(acc[x][y], a, bl);
+        }
     }
   }
   float* dst = p.rnp + ((size_t)bh * p.items + item) * ((size_t)DK * DV);
@@ -478,21 +519,26 @@ bwd_rn_kernel(BwdParams p) {
 // bwd_grads: all gradients of one chunk
 // ----------------------------------------------------------------------------------------
 
-// a [DK][DV] float state in global memory into a shared image of element type T (row stride RV)
+// a [DK][DV] state stored in the element type T into a shared image (row stride RV), in 16-byte
+// pieces
 template <typename T, int DK, int DV, int RV>
-__device__ __forceinline__ void stage_state(T* img, const float* __restrict__ g, int tid, int nt) {
-  constexpr int N4 = DK * DV / 4;
-  for (int idx = tid; idx < N4; idx += nt) {
-    const f32x4 x = reinterpret_cast<const f32x4*>(g)[idx];
-    const int a = (idx * 4) / DV, b = (idx * 4) % DV;
-    T* dst = img + a * RV + b;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) dst[e] = (T)x[e];
+__device__ __forceinline__ void stage_state(T* img, const T* __restrict__ g, int tid, int nt) {
+  constexpr int EPV = 16 / (int)sizeof(T), NP = DK * DV / EPV;
+  for (int idx = tid; idx < NP; idx += nt) {
+    const int a = (idx * EPV) / DV, b = (idx * EPV) % DV;
+    *reinterpret_cast<u32x4*>(img + a * RV + b) = reinterpret_cast<const u32x4*>(g)[idx];
   }
 }
 
+// two waves per SIMD (at most 256 registers per lane, accumulation registers included) where two
+// workgroups' shared memory fits a compute unit (states up to 64 x 64); fewer would leave half
+// of it idle
+template <int DK, int DV>
+constexpr int grads_waves_per_eu() { return DK * DV <= 64 * 64 ? 2 : 1; }
+
 template <typename T, int C, int DK, int DV>
 __global__ void __launch_bounds__(64 * Waves<C>::NW)
+__attribute__((amdgpu_waves_per_eu(grads_waves_per_eu<DK, DV>())))
 bwd_grads_kernel(BwdParams p) {
   constexpr int NW = Waves<C>::NW, RB = Waves<C>::RB, NT = 64 * NW, J = ilog2(C);
   constexpr int ES = (int)sizeof(T), RC = C + 16 / ES;
@@ -514,17 +560,42 @@ bwd_grads_kernel(BwdParams p) {
   // the combined right-sibling state, written by the down-sweep (zero for the last chunk);
   // its loads are issued with the chunk's
   const bool later = p.nl > 0;
-  if (later) stage_state<T, DK, DV, CH::RV>(Ust, p.outs + ((size_t)bh * p.nslot + c) * SZ, tid, NT);
-  // the first node of step 4 is prefetched into registers now (see step 4)
-  constexpr int NPF = DK * DV / 4 / NT;
-  constexpr bool PF = NPF >= 1 && NPF <= 4 && NPF * NT * 4 == DK * DV;
-  f32x4 pf[PF ? NPF : 1];
+  // bf16: the cross-chunk states are read as hi + lo (two bf16 MFMAs per read-out), so that
+  // their rounding, shared by every position that reads a state, stays far below the inputs'
+  constexpr bool SPLIT = ES == 2;
+  T* Plo = P2;                                   // low part of the state image (after step 2)
+  const T* node_e = reinterpret_cast<const T*>(p.node_e) + (size_t)bh * p.nslot * SZ;
+  const T* node_lo = reinterpret_cast<const T*>(p.node_lo) + (size_t)bh * p.nslot * SZ;
+  const T* u_lo = reinterpret_cast<const T*>(p.u_lo) + ((size_t)bh * p.N + c) * SZ;
+  if (later)
+    stage_state<T, DK, DV, CH::RV>(Ust, reinterpret_cast<const T*>(p.u_e) + ((size_t)bh * p.N + c) * SZ, tid, NT);
+  // the first node of step 4 (and U's low part) are prefetched into registers now
+  constexpr int EPV = 16 / ES;
+  constexpr int NPF = DK * DV / EPV / NT;
+  constexpr bool PF = NPF >= 1 && NPF <= 4 && NPF * NT * EPV == DK * DV;
+  u32x4 pf[PF ? NPF : 1], pf2[PF && SPLIT ? NPF : 1];
   auto prefetch = [&](int jl) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(
-        p.node + ((size_t)bh * p.nslot + slot_of(p.N, jl, (c >> jl) - 1)) * SZ);
+    const size_t off = (size_t)slot_of(p.N, jl, (c >> jl) - 1) * SZ;
+    const u32x4* src = reinterpret_cast<const u32x4*>(node_e + off);
+    const u32x4* src2 = reinterpret_cast<const u32x4*>(node_lo + off);
 #pragma unroll
     for (int u = 0; u < (PF ? NPF : 1); ++u) pf[u] = src[tid + u * NT];
+    if constexpr (SPLIT)
+#pragma unroll
+      for (int u = 0; u < (PF ? NPF : 1); ++u) pf2[u] = src2[tid + u * NT];
   };
+  auto put = [&](T* img, const u32x4* r) {
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) {
+      const int idx = tid + u * NT;
+      const int a = (idx * EPV) / DV, b = (idx * EPV) % DV;
+      *reinterpret_cast<u32x4*>(img + a * CH::RV + b) = r[u];
+    }
+  };
+  u32x4 ulo[PF && SPLIT ? NPF : 1];
+  if (PF && SPLIT && later)
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) ulo[u] = reinterpret_cast<const u32x4*>(u_lo)[tid + u * NT];
   int first_set = 0;
   while (first_set < p.nl && !((c >> first_set) & 1)) ++first_set;
   if (PF && first_set < p.nl) prefetch(first_set);
@@ -533,6 +604,9 @@ bwd_grads_kernel(BwdParams p) {
   // 1. masked score tiles: wave w takes 16-row blocks rb = w + NW*x of query positions i.
   //    dlambda of the levels inside the chunk is summed per (row, level) in registers: in a tile
   //    off the diagonal every pair has level 4 + bit_length(rb ^ cb); on it, bit_length(i ^ j).
+  static_assert(RB == 1, "one 16-row block of positions per wave");
+  float* colp = reinterpret_cast<float*>(sm + Lo.cg);   // [wave][position]
+  float rowg[4] = {0.f, 0.f, 0.f, 0.f};   // per-lane partial row sums of G = P1 * S (fp32)
   float bins[RB][4][J + 1];
   for (int x = 0; x < RB; ++x)
 #pragma unroll
@@ -555,7 +629,7 @@ bwd_grads_kernel(BwdParams p) {
           mma(wv, frag_row<T, DV>(ch.o, CH::RV, rb * 16 + jj, b0 + 8 * g4),
               frag_row<T, DV>(ch.v, CH::RV, cb * 16 + jj, b0 + 8 * g4));
       }
-      float u[4];
+      float u[4], colg = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = rb * 16 + 4 * g4 + r, j = cb * 16 + jj;
@@ -570,7 +644,13 @@ bwd_grads_kernel(BwdParams p) {
         }
         P1[i * RC + j] = (T)p1;
         P2[i * RC + j] = (T)p2;
+        rowg[r] += p1 * s[r];
+        colg += p1 * s[r];
       }
+      // this wave's rows of column j: the four row groups of the lane's column
+      colg += __shfl_xor(colg, 16);
+      colg += __shfl_xor(colg, 32);
+      if (g4 == 0) colp[w * C + cb * 16 + jj] = colg;
       if (cb < rb) {
         const int lv = 4 + bit_length((unsigned)(rb ^ cb));
 #pragma unroll
@@ -622,7 +702,15 @@ bwd_grads_kernel(BwdParams p) {
   }
 
   // 3. later chunks, source side: dk += w_s (V U^T), dv += w_s (K U), w_s = exp(g - A_s),
-  //    U the combined right-sibling state staged at the start
+  //    U the combined right-sibling state staged at the start (its low part now, in P2's place);
+  //    pk collects k . (that part of dk)
+  float pk[4] = {0.f, 0.f, 0.f, 0.f};
+  if (SPLIT && later) {
+    __syncthreads();   // P2 is no longer read
+    if constexpr (PF) put(Plo, ulo);
+    else stage_state<T, DK, DV, CH::RV>(Plo, u_lo, tid, NT);
+    __syncthreads();
+  }
   if (later) {
 #pragma unroll
     for (int x = 0; x < RB; ++x) {
@@ -634,19 +722,26 @@ bwd_grads_kernel(BwdParams p) {
       for (int t = 0; t < NK; ++t) {
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int b0 = 0; b0 < DV; b0 += 32)
-          mma(y, frag_row<T, DV>(ch.v, CH::RV, rb * 16 + jj, b0 + 8 * g4),
-              frag_row<T, DV>(Ust, CH::RV, t * 16 + jj, b0 + 8 * g4));
+        for (int b0 = 0; b0 < DV; b0 += 32) {
+          const Frag<T> av_ = frag_row<T, DV>(ch.v, CH::RV, rb * 16 + jj, b0 + 8 * g4);
+          mma(y, av_, frag_row<T, DV>(Ust, CH::RV, t * 16 + jj, b0 + 8 * g4));
+          if constexpr (SPLIT) mma(y, av_, frag_row<T, DV>(Plo, CH::RV, t * 16 + jj, b0 + 8 * g4));
+        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ak[x][t][r] += wsr[r] * y[r];
+        for (int r = 0; r < 4; ++r) {
+          ak[x][t][r] += wsr[r] * y[r];
+          pk[r] += wsr[r] * y[r] * to_f(ch.k[(rb * 16 + 4 * g4 + r) * CH::RK + t * 16 + jj]);
+        }
       }
 #pragma unroll
       for (int t = 0; t < NV; ++t) {
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int a0 = 0; a0 < DK; a0 += 32)
-          mma(y, frag_row<T, DK>(ch.k, CH::RK, rb * 16 + jj, a0 + 8 * g4),
-              frag_col<T, DK>(Ust, CH::RV, a0 + 8 * g4, t * 16 + jj));
+        for (int a0 = 0; a0 < DK; a0 += 32) {
+          const Frag<T> ak_ = frag_row<T, DK>(ch.k, CH::RK, rb * 16 + jj, a0 + 8 * g4);
+          mma(y, ak_, frag_col<T, DK>(Ust, CH::RV, a0 + 8 * g4, t * 16 + jj));
+          if constexpr (SPLIT) mma(y, ak_, frag_col<T, DK>(Plo, CH::RV, a0 + 8 * g4, t * 16 + jj));
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) av[x][t][r] += wsr[r] * y[r];
       }
@@ -660,24 +755,20 @@ bwd_grads_kernel(BwdParams p) {
   //    registers while the current one is used (the first one's since the kernel started).
   const float* gs = p.gsum + (size_t)bh * p.nslot;
   float dlow = 0.f;   // log decay from the end of the current node to the start of chunk c
+  float dq_dot[4] = {0.f, 0.f, 0.f, 0.f};   // q . (this part of dq): sum over levels of lambda dlambda
   for (int jl = first_set; jl < p.nl; ++jl) {
     if (!((c >> jl) & 1)) continue;
     const int sl = slot_of(p.N, jl, (c >> jl) - 1);
     __syncthreads();   // the previous reads of the state image are done
     if constexpr (PF) {
-#pragma unroll
-      for (int u = 0; u < NPF; ++u) {
-        const int idx = tid + u * NT;
-        const int a = (idx * 4) / DV, b = (idx * 4) % DV;
-        T* dst = Nst + a * CH::RV + b;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[e] = (T)pf[u][e];
-      }
+      put(Nst, pf);
+      if constexpr (SPLIT) put(Plo, pf2);
       int nx = jl + 1;
       while (nx < p.nl && !((c >> nx) & 1)) ++nx;
       if (nx < p.nl) prefetch(nx);
     } else {
-      stage_state<T, DK, DV, CH::RV>(Nst, p.node + ((size_t)bh * p.nslot + sl) * SZ, tid, NT);
+      stage_state<T, DK, DV, CH::RV>(Nst, node_e + (size_t)sl * SZ, tid, NT);
+      if constexpr (SPLIT) stage_state<T, DK, DV, CH::RV>(Plo, node_lo + (size_t)sl * SZ, tid, NT);
     }
     __syncthreads();
     const float dj = __expf(dlow);
@@ -695,9 +786,11 @@ bwd_grads_kernel(BwdParams p) {
       for (int t = 0; t < NK; ++t) {
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int b0 = 0; b0 < DV; b0 += 32)
-          mma(y, frag_row<T, DV>(ch.o, CH::RV, rb * 16 + jj, b0 + 8 * g4),
-              frag_row<T, DV>(Nst, CH::RV, t * 16 + jj, b0 + 8 * g4));
+        for (int b0 = 0; b0 < DV; b0 += 32) {
+          const Frag<T> ao_ = frag_row<T, DV>(ch.o, CH::RV, rb * 16 + jj, b0 + 8 * g4);
+          mma(y, ao_, frag_row<T, DV>(Nst, CH::RV, t * 16 + jj, b0 + 8 * g4));
+          if constexpr (SPLIT) mma(y, ao_, frag_row<T, DV>(Plo, CH::RV, t * 16 + jj, b0 + 8 * g4));
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = rb * 16 + 4 * g4 + r;
@@ -709,23 +802,23 @@ bwd_grads_kernel(BwdParams p) {
       for (int r = 0; r < 4; ++r) {
         const float sum = sum16(part[r]);
         const int i = rb * 16 + 4 * g4 + r;
+        dq_dot[r] += scl[r] * sum;
         if (jj == r && i < nv) p.glam[(row0 + i) * p.L + J + 1 + jl] = ch.ea[i] * dj * sum;
       }
     }
     dlow += gs[sl];
   }
 
-  // 5. dA = q.dq - k.dk, and the stores
+  // 5. dA_t = q.dq - k.dk = (row sum - column sum of G inside the chunk, in fp32 from the score
+  //    tiles) + q . (dq from the nodes) - k . (dk from the later chunks); and the stores
 #pragma unroll
   for (int x = 0; x < RB; ++x) {
     const int rb = w + NW * x;
-    float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < NK; ++t) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = rb * 16 + 4 * g4 + r, a = t * 16 + jj;
-        part[r] += aq[x][t][r] * to_f(ch.q[i * CH::RK + a]) - ak[x][t][r] * to_f(ch.k[i * CH::RK + a]);
         if (i < nv) {
           reinterpret_cast<T*>(p.gq)[(row0 + i) * DK + a] = (T)aq[x][t][r];
           reinterpret_cast<T*>(p.gk)[(row0 + i) * DK + a] = (T)ak[x][t][r];
@@ -742,8 +835,10 @@ bwd_grads_kernel(BwdParams p) {
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float sum = sum16(part[r]);
       const int i = rb * 16 + 4 * g4 + r;
+      float colsum = 0.f;
+      for (int u = 0; u < NW; ++u) colsum += colp[u * C + i];
+      const float sum = sum16(rowg[r] - pk[r]) + dq_dot[r] - colsum;
       if (jj == r && i < nv) p.dA[row0 + i] = sum;
     }
 

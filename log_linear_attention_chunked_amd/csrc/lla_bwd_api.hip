@@ -46,7 +46,8 @@ constexpr int kTreeWaves = 16;
 // LDS: every block value of the 64 elements, [slot][64] floats (up-sweep nodes, then the
 // down-sweep's values), when that fits; otherwise the up-sweep reads level i-1 back from the
 // node array and the down-sweep keeps every level in the outs array.
-template <bool LDS>
+// E: the element type of the copies the gradient kernel reads (node_e, u_e)
+template <typename E, bool LDS>
 __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, int SZ) {
   extern __shared__ __attribute__((aligned(16))) float tl[];
   const int bh = blockIdx.y, lane = threadIdx.x & 63;
@@ -56,10 +57,23 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
   float* __restrict__ nd = p.node + (size_t)bh * p.nslot * SZ + e;
   const float* __restrict__ rp = p.rnp + (size_t)bh * p.items * SZ + e;
   float* __restrict__ ou = p.outs + (size_t)bh * p.nslot * SZ + e;
-  if (LDS) {
-    for (int m = w; m < p.N; m += kTreeWaves) tl[m * 64 + lane] = nd[(size_t)m * SZ];
-    __syncthreads();
+  E* __restrict__ ne = reinterpret_cast<E*>(p.node_e) + (size_t)bh * p.nslot * SZ + e;
+  E* __restrict__ ue = reinterpret_cast<E*>(p.u_e) + (size_t)bh * p.N * SZ + e;
+  // bf16 copies also keep their low parts, x - bf16(x)
+  constexpr bool SPLIT = sizeof(E) == 2;
+  E* __restrict__ nlo = reinterpret_cast<E*>(p.node_lo) + (size_t)bh * p.nslot * SZ + e;
+  E* __restrict__ ulo = reinterpret_cast<E*>(p.u_lo) + (size_t)bh * p.N * SZ + e;
+  auto put = [&](E* hi, E* lo, size_t at, float x) {
+    const E h = (E)x;
+    hi[at] = h;
+    if (SPLIT) lo[at] = (E)(x - (float)h);
+  };
+  for (int m = w; m < p.N; m += kTreeWaves) {
+    const float x = nd[(size_t)m * SZ];
+    put(ne, nlo, (size_t)m * SZ, x);
+    if (LDS) tl[m * 64 + lane] = x;
   }
+  __syncthreads();
   for (int i = 1; i < p.nl; ++i) {
     const int nprev = (p.N + (1 << (i - 1)) - 1) >> (i - 1), nb = (p.N + (1 << i) - 1) >> i;
     const int o_prev = slot_of(p.N, i - 1, 0), o = slot_of(p.N, i, 0);
@@ -70,8 +84,9 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
       const float rhs = right ? (LDS ? tl[(sl + 1) * 64 + lane] : nd[(size_t)(sl + 1) * SZ]) : 0.f;
       const float gr = right ? gs[sl + 1] : 0.f;
       const float val = right ? __expf(gr) * lhs + rhs : lhs;
-      nd[(size_t)(o + m) * SZ] = val;
+      put(ne, nlo, (size_t)(o + m) * SZ, val);
       if (LDS) tl[(o + m) * 64 + lane] = val;
+      else nd[(size_t)(o + m) * SZ] = val;
     }
     __syncthreads();
   }
@@ -114,7 +129,8 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
         // the level-i slots of tl held nodes that are no longer read: level i+1 was read above,
         // and the up-sweep is over
         if (LDS) tl[(o + m) * 64 + lane] = val;
-        if (!LDS || i == 0) ou[(size_t)(o + m) * SZ] = val;
+        else ou[(size_t)(o + m) * SZ] = val;
+        if (i == 0) put(ue, ulo, (size_t)m * SZ, val);
       }
     }
     __syncthreads();
@@ -171,7 +187,7 @@ struct BwdPlan {
   int C, N, nl, nslot, L, esize, smem_states, smem_grads, tree_smem;
   long BH;
   int items, rn_off[lla::kLamCap + 1];
-  size_t off_node, off_gsum, off_rnp, off_outs, off_dA, ws_bytes;
+  size_t off_node, off_gsum, off_rnp, off_outs, off_node_e, off_u_e, off_node_lo, off_u_lo, off_dA, ws_bytes;
 };
 
 const BwdKernels* bwd_kernels(int dtype, int C, int DK, int DV) {
@@ -231,13 +247,20 @@ int make_bwd_plan(int B, int H, int T, int dk, int dv, int chunk, int dtype, Bwd
     if (j < pl.nl) pl.items += lla::bwd::items_of_level(pl.N, j);
   }
   pl.off_rnp = off;  off = align256(off + (size_t)BH * pl.items * SZ * 4);
-  pl.off_outs = off; off = align256(off + (size_t)BH * pl.nslot * SZ * 4);
+  // the tree keeps its block values in shared memory when they fit: then the fp32 nodes above
+  // level 0 and the down-sweep's values never reach memory (the node region is still laid out
+  // per head with every slot; the outs region is not needed)
+  pl.tree_smem = (size_t)pl.nslot * 64 * 4 <= (size_t)kLdsPerWorkgroup ? pl.nslot * 64 * 4 : 0;
+  pl.off_outs = off; off = align256(off + (pl.tree_smem ? 0 : (size_t)BH * pl.nslot * SZ * 4));
+  pl.off_node_e = off; off = align256(off + (size_t)BH * pl.nslot * SZ * pl.esize);
+  pl.off_u_e = off;  off = align256(off + (pl.nl > 0 ? (size_t)BH * pl.N * SZ * pl.esize : 0));
+  const bool split = dtype == LLA_DTYPE_BF16;   // bf16 copies keep their low parts
+  pl.off_node_lo = off; off = align256(off + (split ? (size_t)BH * pl.nslot * SZ * pl.esize : 0));
+  pl.off_u_lo = off; off = align256(off + (split && pl.nl > 0 ? (size_t)BH * pl.N * SZ * pl.esize : 0));
   pl.off_dA = off;   off = align256(off + (size_t)BH * T * 4);
   pl.ws_bytes = off;
   pl.smem_states = lla::bwd::bwd_smem(pl.esize, C, dk, dv, false).total;
   pl.smem_grads = grads_smem(pl.esize, C, dk, dv);
-  // the tree kernel keeps its 64 elements' block values in shared memory when they fit
-  pl.tree_smem = (size_t)pl.nslot * 64 * 4 <= (size_t)kLdsPerWorkgroup ? pl.nslot * 64 * 4 : 0;
   if (pl.smem_grads > kLdsPerWorkgroup) return LLA_ERR_UNSUPPORTED;
   return LLA_OK;
 }
@@ -297,6 +320,10 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
   p.items = pl.items;
   for (int j = 0; j <= lla::kLamCap; ++j) p.rn_off[j] = pl.rn_off[j];
   p.outs = reinterpret_cast<float*>(w + pl.off_outs);
+  p.node_e = w + pl.off_node_e;
+  p.u_e = w + pl.off_u_e;
+  p.node_lo = w + pl.off_node_lo;
+  p.u_lo = w + pl.off_u_lo;
   p.dA = reinterpret_cast<float*>(w + pl.off_dA);
   p.BH = (int)pl.BH; p.T = a.T; p.L = pl.L; p.N = pl.N; p.nl = pl.nl; p.nslot = pl.nslot;
   void* args[] = {&p};
@@ -322,12 +349,19 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
     }
     const int SZ = a.dk * a.dv;   // a multiple of 64: the tree grid covers it exactly
     const dim3 tgrid((unsigned)(SZ / 64), (unsigned)pl.BH), tblock(64 * lla::bwd::kTreeWaves);
+    const bool bf = a.dtype == LLA_DTYPE_BF16;
     if (pl.tree_smem > 0) {
-      const void* fn = reinterpret_cast<const void*>(&lla::bwd::bwd_tree_kernel<true>);
+      const void* fn = bf ? reinterpret_cast<const void*>(&lla::bwd::bwd_tree_kernel<lla::bf16, true>)
+                          : reinterpret_cast<const void*>(&lla::bwd::bwd_tree_kernel<float, true>);
       if (set_smem(fn, pl.tree_smem) != hipSuccess) return LLA_ERR_HIP;
-      hipLaunchKernelGGL(lla::bwd::bwd_tree_kernel<true>, tgrid, tblock, pl.tree_smem, stream, p, SZ);
+      if (bf)
+        hipLaunchKernelGGL((lla::bwd::bwd_tree_kernel<lla::bf16, true>), tgrid, tblock, pl.tree_smem, stream, p, SZ);
+      else
+        hipLaunchKernelGGL((lla::bwd::bwd_tree_kernel<float, true>), tgrid, tblock, pl.tree_smem, stream, p, SZ);
+    } else if (bf) {
+      hipLaunchKernelGGL((lla::bwd::bwd_tree_kernel<lla::bf16, false>), tgrid, tblock, 0, stream, p, SZ);
     } else {
-      hipLaunchKernelGGL(lla::bwd::bwd_tree_kernel<false>, tgrid, tblock, 0, stream, p, SZ);
+      hipLaunchKernelGGL((lla::bwd::bwd_tree_kernel<float, false>), tgrid, tblock, 0, stream, p, SZ);
     }
     if (hipGetLastError() != hipSuccess) return LLA_ERR_HIP;
   }
