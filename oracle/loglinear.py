@@ -37,6 +37,8 @@ Functions:
   lay summary, "drawer" merging). It shares no helper with ``bruteforce``.
 * ``recurrent_step``    one step of that form (the decoding step): the states
   after t-1 and token t give the states after t and o_t.
+* ``bruteforce_grad_rows``  the same gradients for selected positions of one head (one row or
+  column of the pair matrices at a time), for sequences too long for the dense matrices.
 * ``bruteforce_grad``   the gradients of ``sum(do * o)`` with respect to q, k, v,
   log_a and lambda: the derivative of the definition above, written out on the
   dense O(T^2) matrices (the pages name the backward pass, and the lambda
@@ -56,6 +58,7 @@ import numpy as np
 __all__ = [
     "bit_length", "level", "num_levels", "level_matrix", "as_f64",
     "bruteforce", "bruteforce_rows", "recurrent", "recurrent_step", "bruteforce_grad",
+    "bruteforce_grad_rows",
 ]
 
 
@@ -308,3 +311,62 @@ def bruteforce_grad(q, k, v, log_a, lam, do):
             dA = G.sum(axis=1) - G.sum(axis=0)
             g["dlog_a"][b, h] = np.cumsum(dA[::-1])[::-1]
     return g
+
+
+def bruteforce_grad_rows(q, k, v, log_a, lam, do, b: int, h: int, rows, tail: int = 0):
+    """The gradients of ``bruteforce_grad`` for selected positions of head (b, h).
+
+    For each position p in ``rows``: dq[p] and dlam[p] from row p of the pair matrices
+    (targets t = p, sources s <= p), dk[p] and dv[p] from column p (sources s = p, targets
+    t >= p), and dA[p] = (row sum of G at p) - (column sum of G at p), G = M * S * W.
+    ``tail`` > 0 also returns dlog_a[r] = sum_{t >= r} dA_t for the last ``tail`` positions,
+    from dA at every one of them. Returns dict(rows, dq, dk, dv, dlam, dA, tail_start,
+    dlog_a_tail) as float64 arrays. Cost O(T (dk + dv)) per position.
+    """
+    qh, kh, vh, oh = (as_f64(x[b, h]) for x in (q, k, v, do))
+    la, lm = as_f64(log_a[b, h]), as_f64(lam[b, h])
+    T, L = qh.shape[0], lm.shape[1]
+    A = _prefix_log_decay(la)
+
+    def row(t):
+        ss = np.arange(0, t + 1)
+        ts = np.array([t])
+        lv = _levels(ts, ss)[0]
+        D = np.exp(_pair_log_decay(A, ts, ss)[0])
+        Sr = kh[ss] @ qh[t]
+        Wr = vh[ss] @ oh[t]
+        Mr = lm[t, lv] * D
+        dq = (Mr * Wr) @ kh[ss]
+        dl = np.zeros(L)
+        np.add.at(dl, lv, D * Sr * Wr)
+        return dq, dl, float(np.sum(Mr * Sr * Wr))
+
+    def col(s):
+        ts = np.arange(s, T)
+        ss = np.array([s])
+        lv = _levels(ts, ss)[:, 0]
+        D = np.exp(_pair_log_decay(A, ts, ss)[:, 0])
+        Sc = qh[ts] @ kh[s]
+        Wc = oh[ts] @ vh[s]
+        Mc = lm[ts, lv] * D
+        dk = (Mc * Wc) @ qh[ts]
+        dv = (Mc * Sc) @ oh[ts]
+        return dk, dv, float(np.sum(Mc * Sc * Wc))
+
+    rows = np.asarray(rows, dtype=np.int64)
+    out = {"rows": rows, "dq": [], "dk": [], "dv": [], "dlam": [], "dA": []}
+    for p in rows:
+        dq, dl, rs = row(int(p))
+        dk, dv, cs = col(int(p))
+        out["dq"].append(dq)
+        out["dlam"].append(dl)
+        out["dk"].append(dk)
+        out["dv"].append(dv)
+        out["dA"].append(rs - cs)
+    for key in ("dq", "dk", "dv", "dlam", "dA"):
+        out[key] = np.array(out[key])
+    out["tail_start"] = T - tail
+    if tail > 0:
+        dA = np.array([row(t)[2] - col(t)[2] for t in range(T - tail, T)])
+        out["dlog_a_tail"] = np.cumsum(dA[::-1])[::-1]
+    return out

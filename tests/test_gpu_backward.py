@@ -175,3 +175,44 @@ def test_backward_headline_shape_one_head():
         got = t[b:b + 1, h:h + 1].double().cpu().numpy()
         assert np.all(np.isfinite(t.float().cpu().numpy())), n
         assert rel_l2(got, want[n]) <= 2e-2, (n, rel_l2(got, want[n]))
+
+
+def _sample_rows(T, C, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(range(0, C // 2)) | set(range(T - C // 2, T)) | {C - 1, C, 2 * C - 1, 2 * C}
+    p = 1
+    while p < T:
+        rows |= {p - 1, p, p + 1}
+        p <<= 1
+    rows |= set(int(x) for x in rng.integers(0, T, 16))
+    return sorted(r for r in rows if 0 <= r < T)
+
+
+@pytest.mark.parametrize("name", ["b1h16_t32768_d128_bf16_knorm", "b1h8_t65536_d128_bf16_coarse"])
+def test_backward_long_workloads_sampled(name):
+    # the two long workloads at full size, in the launch configuration the library picks: for
+    # the last head, every gradient at sampled positions (the first and last half chunk, chunk
+    # edges, around powers of two, 16 uniform) and dlog_a over the last 64 positions, against
+    # the oracle computed position by position
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    w = workload(name)
+    x = generate(w, seed=0)
+    do = grad_output(w, seed=0)
+    print(f"[bwd] {name} full size", flush=True)
+    d = {k: v.cuda() for k, v in x.items()}
+    g = lla.backward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], do.cuda())
+    torch.cuda.synchronize()
+    got = {n: t for n, t in zip(GRADS, g)}
+    C = lla.bwd_default_chunk(w.dk, w.dv, w.dtype)
+    rows = _sample_rows(w.T, C, seed=1)
+    tail = 64
+    for h in (w.H - 1,):
+        ref = O.bruteforce_grad_rows(**x, do=do, b=0, h=h, rows=rows, tail=tail)
+        gh = {n: t[0, h].double().cpu().numpy() for n, t in got.items()}
+        for n in ("dq", "dk", "dv", "dlam"):
+            assert np.all(np.isfinite(gh[n])), (name, h, n)
+            err = rel_l2(gh[n][rows], ref[n])
+            assert err <= 2e-2, (name, h, n, err)
+        err = rel_l2(gh["dlog_a"][w.T - tail:], ref["dlog_a_tail"])
+        assert err <= 2e-2, (name, h, "dlog_a tail", err)

@@ -499,3 +499,19 @@ def test_grad_of_plain_causal_linear_attention():
     assert np.allclose(g["dq"][0, 0], (Mc * (d @ v.T)) @ k)
     assert np.allclose(g["dk"][0, 0], (Mc * (d @ v.T)).T @ q)
     assert np.allclose(g["dv"][0, 0], (Mc * (q @ k.T)).T @ d)
+
+
+def test_grad_rows_match_dense_gradients():
+    # the per-position form against the dense matrices, on rows spread over every level,
+    # a dlog_a tail, and a second head
+    x, do = _tiny_grad_case(5, B=2, H=2, T=70, dk=5, dv=4)
+    g = O.bruteforce_grad(**x, do=do)
+    rows = [0, 1, 2, 7, 8, 31, 32, 33, 63, 64, 69]
+    for b, h in ((0, 0), (1, 1)):
+        r = O.bruteforce_grad_rows(**x, do=do, b=b, h=h, rows=rows, tail=20)
+        for key in ("dq", "dk", "dv", "dlam"):
+            np.testing.assert_allclose(r[key], g[key][b, h][rows], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(r["dlog_a_tail"], g["dlog_a"][b, h][50:], rtol=1e-11, atol=1e-12)
+        # dA from the dense gradients: q . dq - k . dk
+        dA = np.einsum("td,td->t", x["q"][b, h], g["dq"][b, h]) - np.einsum("td,td->t", x["k"][b, h], g["dk"][b, h])
+        np.testing.assert_allclose(r["dA"], dA[rows], rtol=1e-10, atol=1e-12)
