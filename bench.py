@@ -112,6 +112,24 @@ def decode_measure(w, dev, stream, steps: int = 256, warmup: int = 32) -> dict:
         ms = e0.elapsed_time(e1) / (reps * steps)
     except Exception as exc:  # pragma: no cover - report the eager figure alone
         print(f"decode graph capture failed ({exc}); reporting the eager loop", file=sys.stderr)
+    # the hand-over from a prompt of the positions before the timed window (one call)
+    from lla_synth import generate
+    xp = generate(w.with_(T=ts[0]), seed=3)
+    kp, vp, lap = (xp[n].to(dev) for n in ("k", "v", "log_a"))
+    lla.decode_prefill(kp, vp, lap, state, log_scale, stream=stream)
+    torch.cuda.synchronize(dev)
+    reps_p = 5
+    e0.record(stream)
+    for _ in range(reps_p):
+        lla.decode_prefill(kp, vp, lap, state, log_scale, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_prefill = e0.elapsed_time(e1) / reps_p
+    P = ts[0] - 1
+    live = [l for l in range(1, Lc) if (P >> (l - 1)) & 1]
+    # k and v of every live level's block (each read once), log_a, the live states written
+    prefill_bytes = B * H * (sum(1 << (l - 1) for l in live) * (dk + dv) * e + ts[0] * 4
+                             + len(live) * dk * dv * 4)
     per_head = 0
     for t in ts:
         live = bin(t - 1).count("1")
@@ -126,6 +144,8 @@ def decode_measure(w, dev, stream, steps: int = 256, warmup: int = 32) -> dict:
         "ms_per_step_eager_python": ms_eager,
         "timing": "HIP graph of the steps, replayed" if ms != ms_eager else "eager loop",
         "tokens_per_s": B / (ms * 1e-3),
+        "prefill": {"prompt_tokens": ts[0], "ms": ms_prefill, "bytes": prefill_bytes,
+                    "gbs": prefill_bytes / (ms_prefill * 1e-3) / 1e9},
         "algorithmic_bytes_per_step": byts,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS},

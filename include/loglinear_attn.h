@@ -238,6 +238,34 @@ typedef struct lla_decode_args {
 int loglinear_attn_decode_step(const lla_decode_args* args, lla_stream_t stream);
 
 /*
+ * loglinear_attn_decode_prefill — hand-over from a prompt of T tokens to the decoding step: fills
+ * the cache so that loglinear_attn_decode_step can be called for t = T, T+1, ... and gives the
+ * outputs of the forward pass over the prompt followed by the decoded tokens. After position
+ * P = T - 1 the live levels are 0 (position P) and l = j + 1 for each set bit j of P, holding the
+ * aligned block of 2^j positions [(P >> l) << l, + 2^j), decayed to P (study notes, sections 2-2
+ * and 3-6): S_l = sum_{s in block} exp(A_P - A_s) k_s v_s^T.
+ *   k [B,H,T,dk], v [B,H,T,dv]: bfloat16 (LLA_DTYPE_BF16) or float32, 16-byte aligned;
+ *   log_a [B,H,T] float32.
+ *   state [B,H,Lc,dk,dv], log_scale [B,H,2,Lc]: the decoding cache (float32, owned by the caller,
+ *   layout as in loglinear_attn_decode_step); written: the live levels of P (unscaled), the
+ *   level-0 factors of parity P & 1 and the log-scale row of that parity; nothing else is read.
+ *   Lc >= bit_length(T) + 1 (the levels the step at t = T needs), <= 25.
+ * Returns LLA_OK or a negative LLA_ERR_*; B*H = 0 is a no-op. Asynchronous on `stream`,
+ * deterministic.
+ */
+typedef struct lla_prefill_args {
+  const void* k;
+  const void* v;
+  const float* log_a;
+  float* state;
+  float* log_scale;
+  int B, H, T, dk, dv, Lc;
+  int dtype;                  /* enum lla_dtype */
+} lla_prefill_args;
+
+int loglinear_attn_decode_prefill(const lla_prefill_args* args, lla_stream_t stream);
+
+/*
  * loglinear_attn_bwd — the backward pass: gradients of sum(grad_out * o) with respect to every
  * input of the forward operation above (the study notes name training speed and the gradient of
  * the level weights as the hard part of the method, sections 3-5 and 4-5). Per head, with

@@ -17,7 +17,7 @@ import ctypes
 from . import _lib
 from ._lib import LibraryNotBuilt  # noqa: F401
 
-__all__ = ["forward", "backward", "bwd_workspace_bytes", "bwd_default_chunk", "forward_varlen", "decode_step", "new_decode_cache", "num_levels", "workspace_bytes",
+__all__ = ["forward", "backward", "decode_prefill", "bwd_workspace_bytes", "bwd_default_chunk", "forward_varlen", "decode_step", "new_decode_cache", "num_levels", "workspace_bytes",
            "default_chunk", "default_sweep", "LLAError", "LibraryNotBuilt"]
 
 
@@ -133,6 +133,38 @@ def new_decode_cache(B, H, dk, dv, levels, device="cuda"):
     import torch
     state = torch.empty((B, H, levels, dk, dv), dtype=torch.float32, device=device)
     log_scale = torch.empty((B, H, 2, levels), dtype=torch.float32, device=device)
+    return state, log_scale
+
+
+def decode_prefill(k, v, log_a, state, log_scale, *, stream=None):
+    """Fill a decoding cache from a prompt: afterwards ``decode_step`` continues at t = T.
+
+    k: [B,H,T,dk], v: [B,H,T,dv] (bfloat16 or float32); log_a: [B,H,T] float32;
+    state [B,H,Lc,dk,dv] and log_scale [B,H,2,Lc] float32 (``new_decode_cache`` with
+    levels >= bit_length(T) + 1).
+    """
+    import torch
+    if k.dim() != 4:
+        raise ValueError("k must be [B, H, T, dk]")
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    Lc = state.shape[2] if state.dim() == 5 else -1
+    _check(k, "k", k.dtype, (B, H, T, dk))
+    _check(v, "v", k.dtype, (B, H, T, dv))
+    _check(log_a, "log_a", torch.float32, (B, H, T))
+    _check(state, "state", torch.float32, (B, H, Lc, dk, dv))
+    _check(log_scale, "log_scale", torch.float32, (B, H, 2, Lc))
+    a = _lib.PrefillArgs()
+    a.k, a.v, a.log_a = k.data_ptr(), v.data_ptr(), log_a.data_ptr()
+    a.state, a.log_scale = state.data_ptr(), log_scale.data_ptr()
+    a.B, a.H, a.T, a.dk, a.dv, a.Lc = int(B), int(H), int(T), int(dk), int(dv), int(Lc)
+    a.dtype = _dtype_code(k.dtype)
+    if stream is None:
+        stream = torch.cuda.current_stream(k.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = _lib.lib().loglinear_attn_decode_prefill(ctypes.byref(a), ctypes.c_void_p(handle))
+    if st != _lib.LLA_OK:
+        raise LLAError(st, "loglinear_attn_decode_prefill")
     return state, log_scale
 
 

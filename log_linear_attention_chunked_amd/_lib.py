@@ -40,6 +40,7 @@ EXPORTS = (
     "loglinear_attn_bwd",
     "loglinear_attn_bwd_workspace_bytes",
     "loglinear_attn_bwd_default_chunk",
+    "loglinear_attn_decode_prefill",
 )
 
 
@@ -143,6 +144,24 @@ class BwdArgs(ctypes.Structure):
     ]
 
 
+class PrefillArgs(ctypes.Structure):
+    """Mirror of ``lla_prefill_args``."""
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("log_a", ctypes.c_void_p),
+        ("state", ctypes.c_void_p),
+        ("log_scale", ctypes.c_void_p),
+        ("B", ctypes.c_int),
+        ("H", ctypes.c_int),
+        ("T", ctypes.c_int),
+        ("dk", ctypes.c_int),
+        ("dv", ctypes.c_int),
+        ("Lc", ctypes.c_int),
+        ("dtype", ctypes.c_int),
+    ]
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -175,6 +194,8 @@ def _declare(lib):
     lib.loglinear_attn_bwd_workspace_bytes.restype = sz
     lib.loglinear_attn_bwd_default_chunk.argtypes = [i, i, i]
     lib.loglinear_attn_bwd_default_chunk.restype = i
+    lib.loglinear_attn_decode_prefill.argtypes = [ctypes.POINTER(PrefillArgs), vp]
+    lib.loglinear_attn_decode_prefill.restype = i
 
 
 def lib():

@@ -312,3 +312,30 @@ def test_bwd_defaults_and_workspace(L):
     # one chunk: only the per-position dA
     assert ws(1, 2, 64, 64, 64, 64, 0) == 2 * 64 * 4
     assert ws(1, 2, 64, 48, 64, 64, 0) == 0
+
+
+def _pargs(**kw):
+    a = _lib.PrefillArgs()
+    base = 1 << 40
+    a.k, a.v, a.log_a = base, base + (1 << 32), base + (2 << 32)
+    a.state, a.log_scale = base + (3 << 32), base + (4 << 32)
+    a.B, a.H, a.T, a.dk, a.dv, a.Lc, a.dtype = 1, 2, 100, 64, 64, 8, 0
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), _lib.LLA_ERR_INVALID_ARG),
+    (dict(Lc=0), _lib.LLA_ERR_INVALID_ARG),
+    (dict(dtype=5), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(dk=48), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(Lc=26), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(T=128, Lc=8), _lib.LLA_ERR_INVALID_ARG),      # t = 128 needs bit_length(128) + 1 = 9 levels
+    (dict(k=None), _lib.LLA_ERR_INVALID_ARG),
+    (dict(v=(1 << 40) + (1 << 32) + 8), _lib.LLA_ERR_INVALID_ARG),       # misaligned
+    (dict(state=(1 << 40) + 4096), _lib.LLA_ERR_INVALID_ARG),            # overlaps k
+    (dict(B=0), _lib.LLA_OK),
+])
+def test_prefill_validation_codes(L, kw, code):
+    assert L.loglinear_attn_decode_prefill(ctypes.byref(_pargs(**kw)), None) == code

@@ -124,3 +124,44 @@ def test_decode_agrees_with_the_forward_pass():
     fwd = lla.forward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], chunk=64, sweep=2)
     torch.cuda.synchronize()
     assert rel_l2(got, fwd.cpu().numpy().astype(np.float64)) <= 1e-5
+
+
+PREFILL_CASES = [
+    # B, H, prompt T, decoded tokens, dk, dv, dtype
+    (2, 3, 300, 40, 64, 64, "bf16"),
+    (1, 2, 1000, 33, 16, 32, "f32"),
+    (1, 2, 1, 10, 64, 64, "f32"),
+    (1, 2, 64, 65, 32, 32, "f32"),
+    (1, 1, 4095, 20, 128, 128, "bf16"),
+    (1, 2, 2048, 12, 64, 16, "bf16"),
+]
+
+
+@pytest.mark.parametrize("B,H,T,K,dk,dv,dtype", PREFILL_CASES)
+def test_prefill_then_decode(B, H, T, K, dk, dv, dtype):
+    # the cache filled from a prompt of T tokens in one call, then K decoding steps: their
+    # outputs against the definition over the whole sequence
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    w = custom(B, H, T + K, dk, dv, dtype)
+    x = generate(w, seed=T + K)
+    print(f"[prefill] B={B} H={H} T={T} K={K} dk={dk} dv={dv} {dtype}", flush=True)
+    d = {k: v.cuda() for k, v in x.items()}
+    Lc = x["lam"].shape[-1]
+    state, log_scale = lla.new_decode_cache(B, H, dk, dv, Lc)
+    state.fill_(float("nan"))
+    log_scale.fill_(float("nan"))
+    lla.decode_prefill(d["k"][:, :, :T].contiguous(), d["v"][:, :, :T].contiguous(),
+                       d["log_a"][:, :, :T].contiguous(), state, log_scale)
+    outs = []
+    for t in range(T, T + K):
+        outs.append(lla.decode_step(d["q"][:, :, t].contiguous(), d["k"][:, :, t].contiguous(),
+                                    d["v"][:, :, t].contiguous(), d["log_a"][:, :, t].contiguous(),
+                                    d["lam"][:, :, t].contiguous(), state, log_scale, t))
+    torch.cuda.synchronize()
+    got = torch.stack(outs, dim=2).double().cpu().numpy()
+    rows = list(range(T, T + K))
+    want = np.stack([np.stack([O.bruteforce_rows(**x, b=b, h=h, rows=rows) for h in range(H)])
+                     for b in range(B)])
+    assert np.all(np.isfinite(got))
+    assert rel_l2(got, want) <= tol_for(dtype), rel_l2(got, want)
