@@ -500,12 +500,13 @@ def main(argv=None) -> int:
 
 
 def _kernel_sha() -> str:
-    """Hash of the forward kernel's sources, to tell whether recorded counters still apply."""
+    """Hash of the forward kernel's sources (its kernels, instantiations and launch code), to tell
+    whether recorded counters still apply."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "log_linear_attention_chunked_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp")) and f != "lla_decode.hip" and not f.startswith("lla_bwd"):
+        if f.endswith((".hip", ".hpp")) and f.startswith(("lla_api", "lla_dispatch", "lla_inst", "lla_kernels")):
             h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 

@@ -53,7 +53,12 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
   const int bh = blockIdx.y, lane = threadIdx.x & 63;
   const int e = blockIdx.x * 64 + lane, w = threadIdx.x >> 6;
   // the grid has exactly SZ / 64 columns of workgroups (SZ = dk*dv is a multiple of 64)
-  const float* __restrict__ gs = p.gsum + (size_t)bh * p.nslot;
+  const float* __restrict__ gsg = p.gsum + (size_t)bh * p.nslot;
+  // on chip, the block decays sit after the block values: no level waits on a decay load
+  float* gsl = tl + (size_t)p.nslot * 64;
+  if (LDS)
+    for (int i = threadIdx.x; i < p.nslot; i += blockDim.x) gsl[i] = gsg[i];
+  const float* gs = LDS ? gsl : gsg;
   float* __restrict__ nd = p.node + (size_t)bh * p.nslot * SZ + e;
   const float* __restrict__ rp = p.rnp + (size_t)bh * p.items * SZ + e;
   float* __restrict__ ou = p.outs + (size_t)bh * p.nslot * SZ + e;
@@ -250,7 +255,7 @@ int make_bwd_plan(int B, int H, int T, int dk, int dv, int chunk, int dtype, Bwd
   // the tree keeps its block values in shared memory when they fit: then the fp32 nodes above
   // level 0 and the down-sweep's values never reach memory (the node region is still laid out
   // per head with every slot; the outs region is not needed)
-  pl.tree_smem = (size_t)pl.nslot * 64 * 4 <= (size_t)kLdsPerWorkgroup ? pl.nslot * 64 * 4 : 0;
+  pl.tree_smem = (size_t)pl.nslot * 65 * 4 <= (size_t)kLdsPerWorkgroup ? pl.nslot * 65 * 4 : 0;
   pl.off_outs = off; off = align256(off + (pl.tree_smem ? 0 : (size_t)BH * pl.nslot * SZ * 4));
   pl.off_node_e = off; off = align256(off + (size_t)BH * pl.nslot * SZ * pl.esize);
   pl.off_u_e = off;  off = align256(off + (pl.nl > 0 ? (size_t)BH * pl.N * SZ * pl.esize : 0));
