@@ -59,6 +59,12 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
   if (LDS)
     for (int i = threadIdx.x; i < p.nslot; i += blockDim.x) gsl[i] = gsg[i];
   const float* gs = LDS ? gsl : gsg;
+  // on chip the waves exchange values through shared memory only: the barrier then waits for
+  // shared-memory accesses alone, and the loads issued ahead for the next level stay in flight
+  auto bar = [&]() {
+    if (LDS) lds_barrier();
+    else __syncthreads();
+  };
   float* __restrict__ nd = p.node + (size_t)bh * p.nslot * SZ + e;
   const float* __restrict__ rp = p.rnp + (size_t)bh * p.items * SZ + e;
   float* __restrict__ ou = p.outs + (size_t)bh * p.nslot * SZ + e;
@@ -78,7 +84,7 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
     put(ne, nlo, (size_t)m * SZ, x);
     if (LDS) tl[m * 64 + lane] = x;
   }
-  __syncthreads();
+  bar();
   for (int i = 1; i < p.nl; ++i) {
     const int nprev = (p.N + (1 << (i - 1)) - 1) >> (i - 1), nb = (p.N + (1 << i) - 1) >> i;
     const int o_prev = slot_of(p.N, i - 1, 0), o = slot_of(p.N, i, 0);
@@ -93,36 +99,52 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
       if (LDS) tl[(o + m) * 64 + lane] = val;
       else nd[(size_t)(o + m) * SZ] = val;
     }
-    __syncthreads();
+    bar();
   }
   // down-sweep; a wave takes KB of its blocks at a time and loads all their right-block states
-  // before it uses any of them
+  // before it uses any of them; the first KB of the next level are loaded while this level is
+  // worked on (they depend on nothing the sweep writes)
   constexpr int KB = 8;
+  auto fetch = [&](int i, int m0, float (&rn)[KB]) {
+    const int nb = (p.N + (1 << i) - 1) >> i;
+    const int s = sub_log(i), b = i - s, os = slot_of(p.N, s, 0);
+    const int nsub = (p.N + (1 << s) - 1) >> s;
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int m = m0 + u * kTreeWaves;
+      rn[u] = 0.f;
+      if (m < nb && !(m & 1) && m + 1 < nb) {
+        const int sb0 = (m + 1) << b, sb1 = min((m + 2) << b, nsub);
+        if (sb1 - sb0 == 1) {
+          rn[u] = rp[(size_t)(p.rn_off[i] + item_of_sub(i, sb0)) * SZ];
+        } else {
+          float dec = 0.f;
+          for (int sb = sb0; sb < sb1; ++sb) {
+            rn[u] += __expf(dec) * rp[(size_t)(p.rn_off[i] + item_of_sub(i, sb)) * SZ];
+            dec += gs[os + sb];
+          }
+        }
+      }
+    }
+  };
+  float rn_next[KB];
+  if (p.nl > 0) fetch(p.nl - 1, w, rn_next);
   for (int i = p.nl - 1; i >= 0; --i) {
+    float rn_first[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) rn_first[u] = rn_next[u];
+    if (i > 0) fetch(i - 1, w, rn_next);
     const int nb = (p.N + (1 << i) - 1) >> i;
     const int o = slot_of(p.N, i, 0);
     const bool top = i + 1 >= p.nl;
     const int op = top ? 0 : slot_of(p.N, i + 1, 0);
-    const int s = sub_log(i), b = i - s, os = slot_of(p.N, s, 0);
-    const int nsub = (p.N + (1 << s) - 1) >> s;
     for (int m0 = w; m0 < nb; m0 += kTreeWaves * KB) {
       float rn[KB];
+      if (m0 == w) {
 #pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const int m = m0 + u * kTreeWaves;
-        rn[u] = 0.f;
-        if (m < nb && !(m & 1) && m + 1 < nb) {
-          const int sb0 = (m + 1) << b, sb1 = min((m + 2) << b, nsub);
-          if (sb1 - sb0 == 1) {
-            rn[u] = rp[(size_t)(p.rn_off[i] + item_of_sub(i, sb0)) * SZ];
-          } else {
-            float dec = 0.f;
-            for (int sb = sb0; sb < sb1; ++sb) {
-              rn[u] += __expf(dec) * rp[(size_t)(p.rn_off[i] + item_of_sub(i, sb)) * SZ];
-              dec += gs[os + sb];
-            }
-          }
-        }
+        for (int u = 0; u < KB; ++u) rn[u] = rn_first[u];
+      } else {
+        fetch(i, m0, rn);
       }
 #pragma unroll
       for (int u = 0; u < KB; ++u) {
@@ -138,7 +160,7 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
         if (i == 0) put(ue, ulo, (size_t)m * SZ, val);
       }
     }
-    __syncthreads();
+    bar();
   }
 }
 
