@@ -809,30 +809,49 @@ bwd_grads_kernel(BwdParams p) {
     dlow += gs[sl];
   }
 
-  // 5. dA_t = q.dq - k.dk = (row sum - column sum of G inside the chunk, in fp32 from the score
-  //    tiles) + q . (dq from the nodes) - k . (dk from the later chunks); and the stores
+  // 5. the stores: dq, dk, dv go through the q, k, v images (no longer read) so that every
+  //    thread writes whole 16-byte pieces of rows; then dA_t = q.dq - k.dk = (row sum - column
+  //    sum of G inside the chunk, in fp32 from the score tiles) + q . (dq from the nodes)
+  //    - k . (dk from the later chunks)
+  __syncthreads();
 #pragma unroll
   for (int x = 0; x < RB; ++x) {
     const int rb = w + NW * x;
 #pragma unroll
-    for (int t = 0; t < NK; ++t) {
+    for (int t = 0; t < NK; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = rb * 16 + 4 * g4 + r, a = t * 16 + jj;
-        if (i < nv) {
-          reinterpret_cast<T*>(p.gq)[(row0 + i) * DK + a] = (T)aq[x][t][r];
-          reinterpret_cast<T*>(p.gk)[(row0 + i) * DK + a] = (T)ak[x][t][r];
-        }
+        ch.q[i * CH::RK + a] = (T)aq[x][t][r];
+        ch.k[i * CH::RK + a] = (T)ak[x][t][r];
+      }
+#pragma unroll
+    for (int t = 0; t < NV; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ch.v[(rb * 16 + 4 * g4 + r) * CH::RV + t * 16 + jj] = (T)av[x][t][r];
+  }
+  __syncthreads();
+  {
+    constexpr int EPV = 16 / ES;
+    for (int idx = tid; idx < C * (DK / EPV); idx += NT) {
+      const int r = idx / (DK / EPV), cc = (idx % (DK / EPV)) * EPV;
+      if (r < nv) {
+        *reinterpret_cast<u32x4*>(reinterpret_cast<T*>(p.gq) + (row0 + r) * DK + cc) =
+            *reinterpret_cast<const u32x4*>(ch.q + r * CH::RK + cc);
+        *reinterpret_cast<u32x4*>(reinterpret_cast<T*>(p.gk) + (row0 + r) * DK + cc) =
+            *reinterpret_cast<const u32x4*>(ch.k + r * CH::RK + cc);
       }
     }
-#pragma unroll
-    for (int t = 0; t < NV; ++t) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = rb * 16 + 4 * g4 + r;
-        if (i < nv) reinterpret_cast<T*>(p.gv)[(row0 + i) * DV + t * 16 + jj] = (T)av[x][t][r];
-      }
+    for (int idx = tid; idx < C * (DV / EPV); idx += NT) {
+      const int r = idx / (DV / EPV), cc = (idx % (DV / EPV)) * EPV;
+      if (r < nv)
+        *reinterpret_cast<u32x4*>(reinterpret_cast<T*>(p.gv) + (row0 + r) * DV + cc) =
+            *reinterpret_cast<const u32x4*>(ch.v + r * CH::RV + cc);
     }
+  }
+#pragma unroll
+  for (int x = 0; x < RB; ++x) {
+    const int rb = w + NW * x;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = rb * 16 + 4 * g4 + r;
