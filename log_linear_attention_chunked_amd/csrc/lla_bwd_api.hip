@@ -81,7 +81,8 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
   };
   for (int m = w; m < p.N; m += kTreeWaves) {
     const float x = nd[(size_t)m * SZ];
-    put(ne, nlo, (size_t)m * SZ, x);
+    // the gradient kernel reads node (j, (c >> j) - 1) for set bits j of c: even nodes only
+    if (!(m & 1)) put(ne, nlo, (size_t)m * SZ, x);
     if (LDS) tl[m * 64 + lane] = x;
   }
   bar();
@@ -95,7 +96,7 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
       const float rhs = right ? (LDS ? tl[(sl + 1) * 64 + lane] : nd[(size_t)(sl + 1) * SZ]) : 0.f;
       const float gr = right ? gs[sl + 1] : 0.f;
       const float val = right ? __expf(gr) * lhs + rhs : lhs;
-      put(ne, nlo, (size_t)(o + m) * SZ, val);
+      if (!(m & 1)) put(ne, nlo, (size_t)(o + m) * SZ, val);
       if (LDS) tl[(o + m) * 64 + lane] = val;
       else nd[(size_t)(o + m) * SZ] = val;
     }
