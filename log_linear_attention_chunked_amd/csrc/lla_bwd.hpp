@@ -545,7 +545,13 @@ bwd_grads_kernel(BwdParams p) {
   constexpr int NK = DK / 16, NV = DV / 16;
   using CH = Chunk<T, C, DK, DV>;
   extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
-  const int c = blockIdx.x, bh = blockIdx.y;
+  // workgroups go to the 8 XCDs in turn: with B*H a multiple of 8, XCD x gets heads x, x + 8, ...
+  // chunk after chunk, so the Fenwick nodes that consecutive chunks share stay in its L2
+  const int L = blockIdx.x;
+  const int q8 = L >> 3;
+  const bool xcd = (p.BH & 7) == 0;
+  const int c = xcd ? q8 % p.N : L % p.N;
+  const int bh = xcd ? ((q8 / p.N) << 3) + (L & 7) : L / p.N;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, jj = lane & 15, g4 = lane >> 4;
   const int nv = min(C, p.T - c * C);
   const BwdSmem Lo = bwd_smem(ES, C, DK, DV, true);

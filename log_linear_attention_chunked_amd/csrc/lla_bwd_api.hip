@@ -262,6 +262,7 @@ int make_bwd_plan(int B, int H, int T, int dk, int dv, int chunk, int dtype, Bwd
   pl.L = T > 0 ? bit_len((unsigned)(T - 1)) + 1 : 0;
   if (pl.L > lla::kLamCap) return LLA_ERR_UNSUPPORTED;
   pl.N = (T + C - 1) / C;
+  if ((long long)pl.N * BH > 0x7fffffffLL) return LLA_ERR_UNSUPPORTED;   // one workgroup per chunk
   pl.nl = pl.N > 1 ? bit_len((unsigned)(pl.N - 1)) : 0;
   pl.nslot = 0;
   for (int i = 0; i < (pl.nl > 0 ? pl.nl : 0); ++i) pl.nslot += (pl.N + (1 << i) - 1) >> i;
@@ -395,7 +396,9 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
   }
   if (mark(1) != hipSuccess) return LLA_ERR_HIP;
   if (set_smem(ks->grads, pl.smem_grads) != hipSuccess) return LLA_ERR_HIP;
-  if (hipLaunchKernel(ks->grads, chunks, dim3(NT), args, pl.smem_grads, stream) != hipSuccess)
+  // one-dimensional: the kernel maps workgroups to (chunk, head) so that each XCD keeps to its heads
+  if (hipLaunchKernel(ks->grads, dim3((unsigned)(pl.N * pl.BH)), dim3(NT), args, pl.smem_grads,
+                      stream) != hipSuccess)
     return LLA_ERR_HIP;
   if (mark(2) != hipSuccess) return LLA_ERR_HIP;
   hipLaunchKernelGGL(lla::bwd::bwd_dloga_kernel, dim3((unsigned)pl.BH), dim3(256), 0, stream, p);
