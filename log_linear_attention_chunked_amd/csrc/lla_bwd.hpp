@@ -417,7 +417,13 @@ bwd_rn_kernel(BwdParams p) {
   constexpr int NQ = cdiv(PQ, NT), NO = cdiv(PO, NT);
   using CH = Chunk<T, C, DK, DV>;
   extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
-  const int item = blockIdx.x, bh = blockIdx.y;
+  // one-dimensional grid in XCD order, as in bwd_grads: XCD x takes heads x, x + 8, ... (B*H a
+  // multiple of 8), every sub-block of a head in turn, so the q and dO rows a head reads once per
+  // level come from its L2 after the first time
+  const int Lw = blockIdx.x, q8 = Lw >> 3;
+  const bool xcd = (p.BH & 7) == 0;
+  const int item = xcd ? q8 % p.items : Lw % p.items;
+  const int bh = xcd ? ((q8 / p.items) << 3) + (Lw & 7) : Lw / p.items;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, jj = lane & 15, g4 = lane >> 4;
   int j = 0;
   while (j + 1 < p.nl && p.rn_off[j + 1] <= item) ++j;

@@ -275,6 +275,7 @@ int make_bwd_plan(int B, int H, int T, int dk, int dv, int chunk, int dtype, Bwd
     pl.rn_off[j] = pl.items;
     if (j < pl.nl) pl.items += lla::bwd::items_of_level(pl.N, j);
   }
+  if ((long long)pl.items * BH > 0x7fffffffLL) return LLA_ERR_UNSUPPORTED;   // one workgroup each
   pl.off_rnp = off;  off = align256(off + (size_t)BH * pl.items * SZ * 4);
   // the tree keeps its block values in shared memory when they fit: then the fp32 nodes above
   // level 0 and the down-sweep's values never reach memory (the node region is still laid out
@@ -369,7 +370,7 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
     if (hipLaunchKernel(ks->states, chunks, dim3(NT), args, pl.smem_states, stream) != hipSuccess)
       return LLA_ERR_HIP;
     if (set_smem(ks->rn, pl.smem_states) != hipSuccess) return LLA_ERR_HIP;
-    if (hipLaunchKernel(ks->rn, dim3((unsigned)pl.items, (unsigned)pl.BH), dim3(NT), args,
+    if (hipLaunchKernel(ks->rn, dim3((unsigned)((long long)pl.items * pl.BH)), dim3(NT), args,
                         pl.smem_states, stream) != hipSuccess)
       return LLA_ERR_HIP;
     if (pl.nl > 1) {
