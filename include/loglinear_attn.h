@@ -1,5 +1,6 @@
 /*
- * loglinear_attn.h — C ABI of the MI355X (gfx950) log-linear Mamba-2 forward pass.
+ * loglinear_attn.h — C ABI of the MI355X (gfx950) log-linear Mamba-2 attention: the forward pass,
+ * and further below its variable-length, decoding, prefill and backward entry points.
  *
  * Operation (per batch b and head h, every position t in [0, T)):
  *
