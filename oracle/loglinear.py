@@ -45,8 +45,8 @@ Functions:
   gradient in particular, as the hard part of training: study notes, sections
   3-5 and 4-5, and the discussion's point on engineering cost).
 
-Readings taken where the pages are silent are listed in the design doc and repeated
-at the functions that depend on them: 0-based positions, the bucket of s == t is
+Readings taken where the pages are silent, stated at the functions that depend on
+them: 0-based positions, the bucket of s == t is
 level 0 and is included (the sum runs over s <= t), ``a_s`` itself is not in
 the decay of k_s, no scale/normaliser/gate inside the operator.
 """
