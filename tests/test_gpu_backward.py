@@ -216,3 +216,26 @@ def test_backward_long_workloads_sampled(name):
             assert err <= 2e-2, (name, h, n, err)
         err = rel_l2(gh["dlog_a"][w.T - tail:], ref["dlog_a_tail"])
         assert err <= 2e-2, (name, h, "dlog_a tail", err)
+
+
+def test_backward_tree_in_workspace_sampled():
+    # 2048 chunks per head (T = 32768, C = 16): the tree's levels no longer fit shared memory at
+    # any width and stay in the workspace; sampled positions and a dlog_a tail, low decay so that
+    # the coarse levels carry weight
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    w = custom(1, 1, 32768, 16, 16, "bf16")
+    x = generate(w, seed=13, log_a_mode="lowdecay")
+    do = grad_output(w, seed=13)
+    print("[bwd] T=32768 C=16 tree in workspace", flush=True)
+    d = {k: v.cuda() for k, v in x.items()}
+    g = lla.backward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], do.cuda(), chunk=16)
+    torch.cuda.synchronize()
+    rows = _sample_rows(w.T, 16, seed=2)
+    ref = O.bruteforce_grad_rows(**x, do=do, b=0, h=0, rows=rows, tail=64)
+    gh = {n: t[0, 0].double().cpu().numpy() for n, t in zip(GRADS, g)}
+    for n in ("dq", "dk", "dv", "dlam"):
+        assert np.all(np.isfinite(gh[n])), n
+        err = rel_l2(gh[n][rows], ref[n])
+        assert err <= 2e-2, (n, err)
+    assert rel_l2(gh["dlog_a"][w.T - 64:], ref["dlog_a_tail"]) <= 2e-2
