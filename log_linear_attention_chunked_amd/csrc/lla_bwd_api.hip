@@ -47,19 +47,15 @@ constexpr int kTreeWaves = 16;
 // down-sweep's values), when that fits; otherwise the up-sweep reads level i-1 back from the
 // node array and the down-sweep keeps every level in the outs array.
 // E: the element type of the copies the gradient kernel reads (node_e, u_e)
-// EL: state elements per workgroup (64, 32 or 16); the 64 / EL lane groups of a wave work on
-// different blocks, so that fewer elements (less shared memory) still keep every lane busy
-template <typename E, bool LDS, int EL>
+template <typename E, bool LDS>
 __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, int SZ) {
   extern __shared__ __attribute__((aligned(16))) float tl[];
-  constexpr int S = 64 / EL, NG = kTreeWaves * S;   // lane groups per wave, per workgroup
   const int bh = blockIdx.y, lane = threadIdx.x & 63;
-  const int el = lane % EL, wg = (threadIdx.x >> 6) * S + lane / EL;
-  const int e = blockIdx.x * EL + el;
-  // the grid has exactly SZ / EL columns of workgroups (SZ = dk*dv is a multiple of 64)
+  const int e = blockIdx.x * 64 + lane, w = threadIdx.x >> 6;
+  // the grid has exactly SZ / 64 columns of workgroups (SZ = dk*dv is a multiple of 64)
   const float* __restrict__ gsg = p.gsum + (size_t)bh * p.nslot;
   // on chip, the block decays sit after the block values: no level waits on a decay load
-  float* gsl = tl + (size_t)p.nslot * EL;
+  float* gsl = tl + (size_t)p.nslot * 64;
   if (LDS)
     for (int i = threadIdx.x; i < p.nslot; i += blockDim.x) gsl[i] = gsg[i];
   const float* gs = LDS ? gsl : gsg;
@@ -83,25 +79,25 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
     hi[at] = h;
     if (SPLIT) lo[at] = (E)(x - (float)h);
   };
-  for (int m = wg; m < p.N; m += NG) {
+  for (int m = w; m < p.N; m += kTreeWaves) {
     const float x = nd[(size_t)m * SZ];
     // the gradient kernel reads node (j, (c >> j) - 1) for set bits j of c: even nodes only
     if (!(m & 1)) put(ne, nlo, (size_t)m * SZ, x);
-    if (LDS) tl[m * EL + el] = x;
+    if (LDS) tl[m * 64 + lane] = x;
   }
   bar();
   for (int i = 1; i < p.nl; ++i) {
     const int nprev = (p.N + (1 << (i - 1)) - 1) >> (i - 1), nb = (p.N + (1 << i) - 1) >> i;
     const int o_prev = slot_of(p.N, i - 1, 0), o = slot_of(p.N, i, 0);
-    for (int m = wg; m < nb; m += NG) {
+    for (int m = w; m < nb; m += kTreeWaves) {
       const bool right = 2 * m + 1 < nprev;
       const int sl = o_prev + 2 * m;
-      const float lhs = LDS ? tl[sl * EL + el] : nd[(size_t)sl * SZ];
-      const float rhs = right ? (LDS ? tl[(sl + 1) * EL + el] : nd[(size_t)(sl + 1) * SZ]) : 0.f;
+      const float lhs = LDS ? tl[sl * 64 + lane] : nd[(size_t)sl * SZ];
+      const float rhs = right ? (LDS ? tl[(sl + 1) * 64 + lane] : nd[(size_t)(sl + 1) * SZ]) : 0.f;
       const float gr = right ? gs[sl + 1] : 0.f;
       const float val = right ? __expf(gr) * lhs + rhs : lhs;
       if (!(m & 1)) put(ne, nlo, (size_t)(o + m) * SZ, val);
-      if (LDS) tl[(o + m) * EL + el] = val;
+      if (LDS) tl[(o + m) * 64 + lane] = val;
       else nd[(size_t)(o + m) * SZ] = val;
     }
     bar();
@@ -116,7 +112,7 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
     const int nsub = (p.N + (1 << s) - 1) >> s;
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
-      const int m = m0 + u * NG;
+      const int m = m0 + u * kTreeWaves;
       rn[u] = 0.f;
       if (m < nb && !(m & 1) && m + 1 < nb) {
         const int sb0 = (m + 1) << b, sb1 = min((m + 2) << b, nsub);
@@ -133,19 +129,19 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
     }
   };
   float rn_next[KB];
-  if (p.nl > 0) fetch(p.nl - 1, wg, rn_next);
+  if (p.nl > 0) fetch(p.nl - 1, w, rn_next);
   for (int i = p.nl - 1; i >= 0; --i) {
     float rn_first[KB];
 #pragma unroll
     for (int u = 0; u < KB; ++u) rn_first[u] = rn_next[u];
-    if (i > 0) fetch(i - 1, wg, rn_next);
+    if (i > 0) fetch(i - 1, w, rn_next);
     const int nb = (p.N + (1 << i) - 1) >> i;
     const int o = slot_of(p.N, i, 0);
     const bool top = i + 1 >= p.nl;
     const int op = top ? 0 : slot_of(p.N, i + 1, 0);
-    for (int m0 = wg; m0 < nb; m0 += NG * KB) {
+    for (int m0 = w; m0 < nb; m0 += kTreeWaves * KB) {
       float rn[KB];
-      if (m0 == wg) {
+      if (m0 == w) {
 #pragma unroll
         for (int u = 0; u < KB; ++u) rn[u] = rn_first[u];
       } else {
@@ -153,14 +149,14 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
       }
 #pragma unroll
       for (int u = 0; u < KB; ++u) {
-        const int m = m0 + u * NG;
+        const int m = m0 + u * kTreeWaves;
         if (m >= nb) break;
         const int ps = op + (m >> 1);
-        const float par = top ? 0.f : (LDS ? tl[ps * EL + el] : ou[(size_t)ps * SZ]);
+        const float par = top ? 0.f : (LDS ? tl[ps * 64 + lane] : ou[(size_t)ps * SZ]);
         const float val = (!(m & 1) && m + 1 < nb) ? __expf(gs[o + m + 1]) * par + rn[u] : par;
         // the level-i slots of tl held nodes that are no longer read: level i+1 was read above,
         // and the up-sweep is over
-        if (LDS) tl[(o + m) * EL + el] = val;
+        if (LDS) tl[(o + m) * 64 + lane] = val;
         else ou[(size_t)(o + m) * SZ] = val;
         if (i == 0) put(ue, ulo, (size_t)m * SZ, val);
       }
@@ -216,7 +212,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int kLdsPerWorkgroup = 160 * 1024;
 
 struct BwdPlan {
-  int C, N, nl, nslot, L, esize, smem_states, smem_grads, tree_smem, tree_el;
+  int C, N, nl, nslot, L, esize, smem_states, smem_grads, tree_smem;
   long BH;
   int items, rn_off[lla::kLamCap + 1];
   size_t off_node, off_gsum, off_rnp, off_outs, off_node_e, off_u_e, off_node_lo, off_u_lo, off_dA, ws_bytes;
@@ -284,14 +280,7 @@ int make_bwd_plan(int B, int H, int T, int dk, int dv, int chunk, int dtype, Bwd
   // the tree keeps its block values in shared memory when they fit: then the fp32 nodes above
   // level 0 and the down-sweep's values never reach memory (the node region is still laid out
   // per head with every slot; the outs region is not needed)
-  // (64 state elements per workgroup, or 32 or 16 when that is what it takes)
-  pl.tree_smem = 0;
-  pl.tree_el = 64;
-  for (int el = 64; el >= 16 && !pl.tree_smem; el /= 2)
-    if ((size_t)pl.nslot * (el + 1) * 4 <= (size_t)kLdsPerWorkgroup) {
-      pl.tree_smem = pl.nslot * (el + 1) * 4;
-      pl.tree_el = el;
-    }
+  pl.tree_smem = (size_t)pl.nslot * 65 * 4 <= (size_t)kLdsPerWorkgroup ? pl.nslot * 65 * 4 : 0;
   pl.off_outs = off; off = align256(off + (pl.tree_smem ? 0 : (size_t)BH * pl.nslot * SZ * 4));
   pl.off_node_e = off; off = align256(off + (size_t)BH * pl.nslot * SZ * pl.esize);
   pl.off_u_e = off;  off = align256(off + (pl.nl > 0 ? (size_t)BH * pl.N * SZ * pl.esize : 0));
@@ -389,28 +378,21 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
       if (hipGetLastError() != hipSuccess) return LLA_ERR_HIP;
     }
     const int SZ = a.dk * a.dv;   // a multiple of 64: the tree grid covers it exactly
+    const dim3 tgrid((unsigned)(SZ / 64), (unsigned)pl.BH), tblock(64 * lla::bwd::kTreeWaves);
     const bool bf = a.dtype == LLA_DTYPE_BF16;
-    const int el = pl.tree_smem > 0 ? pl.tree_el : 64;
-    const dim3 tgrid((unsigned)(SZ / el), (unsigned)pl.BH), tblock(64 * lla::bwd::kTreeWaves);
-    const void* fn = nullptr;
-    using namespace lla::bwd;
-    if (pl.tree_smem == 0)
-      fn = bf ? reinterpret_cast<const void*>(&bwd_tree_kernel<lla::bf16, false, 64>)
-              : reinterpret_cast<const void*>(&bwd_tree_kernel<float, false, 64>);
-    else if (el == 64)
-      fn = bf ? reinterpret_cast<const void*>(&bwd_tree_kernel<lla::bf16, true, 64>)
-              : reinterpret_cast<const void*>(&bwd_tree_kernel<float, true, 64>);
-    else if (el == 32)
-      fn = bf ? reinterpret_cast<const void*>(&bwd_tree_kernel<lla::bf16, true, 32>)
-              : reinterpret_cast<const void*>(&bwd_tree_kernel<float, true, 32>);
-    else
-      fn = bf ? reinterpret_cast<const void*>(&bwd_tree_kernel<lla::bf16, true, 16>)
-              : reinterpret_cast<const void*>(&bwd_tree_kernel<float, true, 16>);
-    if (pl.tree_smem > 0 && set_smem(fn, pl.tree_smem) != hipSuccess) return LLA_ERR_HIP;
-    int sz = SZ;
-    void* targs[] = {&p, &sz};
-    if (hipLaunchKernel(fn, tgrid, tblock, targs, pl.tree_smem, stream) != hipSuccess)
-      return LLA_ERR_HIP;
+    if (pl.tree_smem > 0) {
+      const void* fn = bf ? reinterpret_cast<const void*>(&lla::bwd::bwd_tree_kernel<lla::bf16, true>)
+                          : reinterpret_cast<const void*>(&lla::bwd::bwd_tree_kernel<float, true>);
+      if (set_smem(fn, pl.tree_smem) != hipSuccess) return LLA_ERR_HIP;
+      if (bf)
+        hipLaunchKernelGGL((lla::bwd::bwd_tree_kernel<lla::bf16, true>), tgrid, tblock, pl.tree_smem, stream, p, SZ);
+      else
+        hipLaunchKernelGGL((lla::bwd::bwd_tree_kernel<float, true>), tgrid, tblock, pl.tree_smem, stream, p, SZ);
+    } else if (bf) {
+      hipLaunchKernelGGL((lla::bwd::bwd_tree_kernel<lla::bf16, false>), tgrid, tblock, 0, stream, p, SZ);
+    } else {
+      hipLaunchKernelGGL((lla::bwd::bwd_tree_kernel<float, false>), tgrid, tblock, 0, stream, p, SZ);
+    }
     if (hipGetLastError() != hipSuccess) return LLA_ERR_HIP;
   }
   if (mark(1) != hipSuccess) return LLA_ERR_HIP;
