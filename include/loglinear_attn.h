@@ -32,8 +32,16 @@
  *
  * Supported: B, H, T >= 0 (any product that is 0 is a no-op); B*H <= 65535;
  * dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64, 128}; any T up to 2^23
- * (L <= 24; a ragged last chunk is masked). Output is bitwise deterministic for
- * identical inputs and arguments.
+ * (L <= 24; a ragged last chunk is masked), provided the chunks one workgroup holds fit the
+ * 160 KB of shared memory of a compute unit:
+ *   R * (C*(2*dk + dv)*e + 112*C + 16 + (C/16)*ceil(C/32)*512*e) + 272 <= 163840
+ * (R chunks per workgroup, e = element bytes). bfloat16 always fits at R = 1; float32 with
+ * chunk 128 and 2*dk + dv >= 192 fits at no R, and R = 2 does not fit for bfloat16 at chunk
+ * 128 with dk >= 64 or dv = 128, nor for float32 at chunk 128 or at chunk 64 with dk = 128 or
+ * dk = 64, dv = 128. Combinations that do not fit return LLA_ERR_UNSUPPORTED from the host-side
+ * checks, before any device call (and loglinear_attn_workspace_bytes returns 0 for them); the
+ * library's default chunk and sweep always fit. Output is bitwise deterministic for identical
+ * inputs and arguments.
  *
  * Execution: one forward kernel on `stream` (preceded by a fill kernel only when the
  * library allocates the workspace itself) in which each workgroup loads R consecutive
@@ -69,7 +77,8 @@ enum lla_status {
   LLA_ERR_INVALID_ARG = -1,   /* null pointer, negative size, aliasing out, bad struct */
   LLA_ERR_UNSUPPORTED = -2,   /* dk/dv/chunk/sweep outside the supported set, L > 24, B*H > 65535 */
   LLA_ERR_HIP = -3,           /* a HIP runtime call or a kernel launch failed */
-  LLA_ERR_NO_MEMORY = -4,     /* stream-ordered workspace allocation failed */
+  LLA_ERR_NO_MEMORY = -4,     /* stream-ordered workspace allocation failed (also forced, for
+                                 tests, by LLA_TEST_FAIL_ALLOC=1 in the environment) */
   LLA_ERR_WORKSPACE = -5      /* caller workspace smaller than loglinear_attn_workspace_bytes */
 };
 
@@ -111,7 +120,12 @@ int loglinear_attn_fwd_f32(const float* q, const float* k, const float* v,
  *           two calls that may run concurrently (different streams) must not share
  *           it; calls ordered on one stream may. Layout: the first
  *           round_up_256(4 * (64 + B*H*(nsweep-1)*dv/16)) bytes are the counter and
- *           flags, the only part that must start at zero.
+ *           flags, the only part that must start at zero. A workspace that was never
+ *           zero-filled gives undefined outputs, but never leaves `out` unwritten: where
+ *           the counter's count is at or past the number of workgroups every output row is
+ *           written as NaN (and stays so on every later call until the workspace is
+ *           zero-filled); where a node never comes, the rows that need it are NaN after a
+ *           bounded wait.
  *   stage_events : optional timing hooks; each non-NULL entry is a hipEvent_t the
  *           library records on `stream`: [0] before the fill kernel (if any), [1]
  *           just before the forward kernel, [2] after it; [3] is not used. The caller

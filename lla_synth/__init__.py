@@ -23,7 +23,9 @@ distributions follow the workloads' statements: per-token decays in
 Variants (parity stress cases; never timed) replace one drawn tensor after the
 draw so that every other tensor stays identical:
 
-* ``log_a_mode``: ``"nodecay"`` (all zero), ``"lowdecay"`` (``-1e-4 u``).
+* ``log_a_mode``: ``"nodecay"`` (all zero), ``"lowdecay"`` (``-1e-4 u``),
+  ``"strongdecay"`` (``-(0.5 + 2.5 u)``, i.e. per-token decays a = exp(-U(0.5, 3)), strong
+  Mamba-2-style gates: a chunk's local log decay then reaches well past -40).
 * ``lam_mode``: ``"onehot:<l>"``, ``"zero"``, ``"ones"``,
   ``"equal"`` (one weight per token shared by all levels).
 """
@@ -132,6 +134,8 @@ def generate(w: Workload, seed: int = 0, *, log_a_mode: str | None = None,
             log_a = torch.zeros_like(log_a)
         elif log_a_mode == "lowdecay":
             log_a = -1e-4 * u
+        elif log_a_mode == "strongdecay":
+            log_a = -(0.5 + 2.5 * u)
         else:
             raise ValueError(f"unknown log_a_mode {log_a_mode!r}")
     if lam_mode is not None:

@@ -12,6 +12,7 @@
 
 #include "loglinear_attn.h"
 #include "lla_dispatch.hpp"
+#include "lla_host.hpp"
 #include "lla_kernels.hpp"
 
 namespace lla {
@@ -57,7 +58,7 @@ inline int bit_len(unsigned x) { int n = 0; while (x) { ++n; x >>= 1; } return n
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int kSpinLimit = 1 << 20;        // polls of a node flag (each ~1 us) before giving up
-constexpr int kLdsPerCU = 160 * 1024;      // gfx950 shared memory per compute unit
+using lla::kLdsPerCU;
 constexpr long kMinWorkgroups = 512;       // below this, prefer one chunk per workgroup
 
 struct Plan {
@@ -113,6 +114,9 @@ int make_plan(int B, int H, int T, int dk, int dv, int chunk, int sweep, int dty
   pl.off_nodeT = off;  off = align256(off + nodes * ((dk + 31) / 32) * 64 * 8 * pl.esize);
   pl.ws_bytes = pl.ns > 0 ? off : 0;
   pl.smem = smem_bytes(pl.esize, C, dk, dv, pl.R);
+  // the sweep's images must fit one compute unit's shared memory (float32 at large chunk and
+  // head sizes does not)
+  if (pl.smem > kLdsPerCU) return LLA_ERR_UNSUPPORTED;
   return LLA_OK;
 }
 
@@ -206,7 +210,7 @@ int run_forward(const lla_fwd_args& a, const Plan& pl, hipStream_t stream, const
       if (a.workspace_bytes < pl.ws_bytes) return LLA_ERR_WORKSPACE;
       if ((uintptr_t)ws & 255) return LLA_ERR_INVALID_ARG;
     } else {
-      if (hipMallocAsync(&ws, pl.ws_bytes, stream) != hipSuccess) return LLA_ERR_NO_MEMORY;
+      if (lla::workspace_alloc(&ws, pl.ws_bytes, stream) != hipSuccess) return LLA_ERR_NO_MEMORY;
       owned = true;
     }
   }

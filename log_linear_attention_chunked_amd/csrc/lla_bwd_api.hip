@@ -8,6 +8,7 @@
 
 #include "loglinear_attn.h"
 #include "lla_bwd.hpp"
+#include "lla_host.hpp"
 
 namespace lla {
 namespace bwd {
@@ -421,7 +422,7 @@ int backward(const lla_bwd_args& a, hipStream_t stream) {
     if (a.workspace_bytes < pl.ws_bytes) return LLA_ERR_WORKSPACE;
     if ((uintptr_t)ws & 255) return LLA_ERR_INVALID_ARG;
   } else {
-    if (hipMallocAsync(&ws, pl.ws_bytes, stream) != hipSuccess) return LLA_ERR_NO_MEMORY;
+    if (lla::workspace_alloc(&ws, pl.ws_bytes, stream) != hipSuccess) return LLA_ERR_NO_MEMORY;
     owned = true;
   }
   st = launch_bwd(a, pl, ws, stream);

@@ -802,10 +802,11 @@ __device__ __forceinline__ int wave_sum_int(int x) {
 // within a sweep, sequences in order, heads fastest. Wave 0 works it out (one sequence per lane,
 // a binary search over s) and hands it to the other waves through `tk` (4 words). Returns false
 // when the workgroup has no ticket and must leave at once; else sets the sweep, the virtual head
-// and the value of a published flag in this launch.
+// and the value of a published flag in this launch, and `poisoned` when the counter was past the
+// ticket count (a workspace that was never zero-filled: the sweep's rows are then written as NaN).
 template <int C, int NB>
 __device__ bool varlen_ticket(const Params& p, unsigned* tk, int tid, int blk, bool counted,
-                              int& sw, int& bh, int& flagv) {
+                              int& sw, int& bh, int& flagv, bool& poisoned) {
   if (tid < 64) {
     const int lane = tid;
     const int N = p.vN, H = p.vH;
@@ -819,6 +820,7 @@ __device__ bool varlen_ticket(const Params& p, unsigned* tk, int tid, int blk, b
     bool ok = p.vtotal ? p.vtotal == total : blk < total;   // surplus workgroups, or a host count
     int t = blk;                                             // that disagrees: nothing is drawn
     unsigned ep = 0;
+    bool nan_rows = false;
     if (ok && counted) {
       unsigned lo = 0, hi = 0;
       if (lane == 0) {
@@ -833,8 +835,11 @@ __device__ bool varlen_ticket(const Params& p, unsigned* tk, int tid, int blk, b
       }
       const unsigned cnt = __builtin_amdgcn_readlane(lo, 0);
       ep = __builtin_amdgcn_readlane(hi, 0);
-      ok = cnt < (unsigned)total;                    // false: a workspace never zero-filled
-      t = (int)cnt;
+      // a count past the tickets: a workspace never zero-filled. The counts drawn then run over
+      // consecutive values, so (count - total) mod total meets every ticket once; that sweep's
+      // rows are written as NaN.
+      nan_rows = cnt >= (unsigned)total;
+      t = nan_rows ? (int)((cnt - (unsigned)total) % (unsigned)total) : (int)cnt;
     }
     int s = 0, n = 0, h = 0;
     if (ok) {
@@ -862,7 +867,7 @@ __device__ bool varlen_ticket(const Params& p, unsigned* tk, int tid, int blk, b
       }
     }
     if (lane == 0) {
-      tk[0] = ok;
+      tk[0] = ok ? (nan_rows ? 2u : 1u) : 0u;
       tk[1] = ep + 1u;
       tk[2] = (unsigned)s;
       tk[3] = (unsigned)(n * H + h);
@@ -872,7 +877,9 @@ __device__ bool varlen_ticket(const Params& p, unsigned* tk, int tid, int blk, b
   flagv = (int)__builtin_amdgcn_readfirstlane(tk[1]);
   sw = (int)__builtin_amdgcn_readfirstlane(tk[2]);
   bh = (int)__builtin_amdgcn_readfirstlane(tk[3]);
-  return __builtin_amdgcn_readfirstlane(tk[0]) != 0;
+  const unsigned st = __builtin_amdgcn_readfirstlane(tk[0]);
+  poisoned = st == 2u;
+  return st != 0u;
 }
 
 // The forward pass: one workgroup per sweep of NB chunks of one head, one wave per 16 value
@@ -912,9 +919,10 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   int t = blockIdx.x;
   int flagv = 1;                      // value of a published flag in this launch
   int vsw = 0, vbh = 0;               // variable-length batch: the ticket's sweep and head
+  bool poisoned = false;              // counter past the tickets: write the sweep's rows as NaN
   if constexpr (VL) {
     if (!varlen_ticket<C, NB>(p, reinterpret_cast<unsigned*>(smem + S.ticket), tid, blockIdx.x, ns > 0,
-                              vsw, vbh, flagv))
+                              vsw, vbh, flagv, poisoned))
       return;
   } else if (ns > 0) {
     const unsigned total = (unsigned)p.BH * (unsigned)p.nsweep;
@@ -933,8 +941,12 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
     __syncthreads();
     const unsigned cnt = __builtin_amdgcn_readfirstlane(tk[0]);
     flagv = (int)(__builtin_amdgcn_readfirstlane(tk[1]) + 1u);
-    if (cnt >= total) return;         // a workspace that was never zero-filled: touch nothing
-    t = (int)cnt;
+    // A count past the tickets: a workspace that was never zero-filled. The counts drawn are
+    // consecutive, so (count - total) mod total meets every ticket once; that sweep's rows are
+    // written as NaN (no node is read or published) and the workspace stays in that state until
+    // it is zero-filled again.
+    poisoned = cnt >= total;
+    t = poisoned ? (int)((cnt - total) % total) : (int)cnt;
   }
   const int sw = VL ? vsw : t / p.BH, bh = VL ? vbh : t - (t / p.BH) * p.BH;
 
@@ -961,6 +973,20 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   const int c0 = sw * NB;
   const int nch = min(NB, nchunks - c0);
   const int next = __builtin_popcount((unsigned)sw);
+
+  if (poisoned) {
+    const f32x4 nan4 = {__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    for (int u = 0; u < nch; ++u) {
+      const int t0 = (c0 + u) * C;
+      const int valid = min(C, Tn - t0);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        const int qi = 16 * qb + j;
+        if (qi < valid) store_quad<T>(og + (size_t)(t0 + qi) * DV + 16 * w + 4 * g, nan4);
+      }
+    }
+    return;
+  }
 
   Reader<T, C, DK, DV> rd;
   rd.init(lane, w);

@@ -25,6 +25,31 @@ def fits_smem(dtype: str, C: int, dk: int, dv: int, R: int) -> bool:
     return ((R * per + 256 + 16 + 255) & ~255) <= 160 * 1024
 
 
+def host_threads() -> int:
+    """Host cores this process may use (the GPU machine grants 16 per GPU), at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def per_head(fn, heads, workers: int | None = None) -> list:
+    """[fn(b, h) for (b, h) in heads], evaluated by a thread pool with single-threaded BLAS.
+
+    The oracle's work per head is numpy calls that release the GIL, so heads run in parallel
+    on the host cores; results come back in the order of ``heads``. Only the scheduling lives
+    here: what each call computes is the oracle's own code.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    heads = list(heads)
+    workers = workers or host_threads()
+    with threadpool_limits(1):
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            return list(ex.map(lambda bh: fn(*bh), heads))
+
+
 def rel_l2(got, want) -> float:
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)

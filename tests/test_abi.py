@@ -125,6 +125,42 @@ def test_null_struct(L):
     assert L.loglinear_attn_fwd_ex(None, None) == _lib.LLA_ERR_INVALID_ARG
 
 
+# float32 sweeps whose images exceed the 160 KB of shared memory of a compute unit: refused on
+# the host, before any device call, with no workspace size either
+FP32_TOO_BIG = [
+    # chunk, dk, dv, sweep
+    (128, 128, 128, 1), (128, 64, 64, 1), (128, 32, 128, 1), (128, 128, 16, 1),
+    (128, 16, 16, 2), (64, 128, 128, 2), (64, 128, 16, 2), (64, 64, 128, 2),
+]
+
+
+@pytest.mark.parametrize("C,dk,dv,R", FP32_TOO_BIG)
+def test_shared_memory_limits_are_host_checks(L, C, dk, dv, R):
+    assert _call(L, _args(dtype=1, chunk=C, dk=dk, dv=dv, sweep=R)) == _lib.LLA_ERR_UNSUPPORTED
+    assert L.loglinear_attn_workspace_bytes(1, 2, 4096, dk, dv, C, R, 1) == 0
+
+
+@pytest.mark.parametrize("C,dk,dv,R", [(128, 64, 32, 1), (128, 16, 128, 1), (64, 128, 128, 1),
+                                       (64, 64, 64, 2)])
+def test_shared_memory_limits_largest_fp32_that_fit(L, C, dk, dv, R):
+    assert L.loglinear_attn_workspace_bytes(1, 2, 4096, dk, dv, C, R, 1) > 0
+    # defaults never pick a sweep that does not fit
+    assert L.loglinear_attn_default_sweep(64, 64, 65536, dk, dv, C, 1) in (1, 2)
+
+
+def test_allocation_failure_returns_no_memory(L, monkeypatch):
+    # the library takes the workspace itself (none given) and the allocation fails: the
+    # documented status, before anything is launched
+    monkeypatch.setenv("LLA_TEST_FAIL_ALLOC", "1")
+    assert _call(L, _args()) == _lib.LLA_ERR_NO_MEMORY
+    assert L.loglinear_attn_bwd(ctypes.byref(_bargs()), None) == _lib.LLA_ERR_NO_MEMORY
+    # a caller workspace needs no allocation: validation still runs and reports its own codes
+    assert _call(L, _args(workspace=(1 << 44), workspace_bytes=1024)) == _lib.LLA_ERR_WORKSPACE
+    # one sweep covers the sequence: no workspace, so no allocation and nothing to fail (B = 0
+    # keeps the call a no-op on a machine without a device)
+    assert _call(L, _args(B=0)) == _lib.LLA_OK
+
+
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(T=0), dict(T=0, q=None, out=None)])
 def test_empty_is_a_noop(L, kw):
     assert _call(L, _args(**kw)) == _lib.LLA_OK
@@ -339,3 +375,4 @@ def _pargs(**kw):
 ])
 def test_prefill_validation_codes(L, kw, code):
     assert L.loglinear_attn_decode_prefill(ctypes.byref(_pargs(**kw)), None) == code
+

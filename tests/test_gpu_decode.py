@@ -74,6 +74,18 @@ def test_decode_matches_oracle(case):
     assert err <= tol_for(dtype), err
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_strong_decay(dtype):
+    # log_a = -U(0.5, 3): per-level log-scales reach far below -40 and are reset on rewrite
+    x = generate(custom(2, 2, 300, 64, 32, dtype=dtype), seed=17, log_a_mode="strongdecay")
+    got, _, _ = run_decode(x)
+    want = O.bruteforce(x["q"], x["k"], x["v"], x["log_a"], x["lam"])
+    err = rel_l2(got, want)
+    print(f"decode strong decay {dtype}: rel_l2={err:.3e}", flush=True)
+    assert np.all(np.isfinite(got))
+    assert err <= tol_for(dtype), err
+
+
 def test_decode_cache_holds_the_level_states():
     # after the last step, every live level (times its scale) equals the oracle's state
     B, H, T, dk, dv = 1, 2, 77, 32, 16
@@ -137,15 +149,18 @@ PREFILL_CASES = [
 ]
 
 
-@pytest.mark.parametrize("B,H,T,K,dk,dv,dtype", PREFILL_CASES)
-def test_prefill_then_decode(B, H, T, K, dk, dv, dtype):
+@pytest.mark.parametrize("B,H,T,K,dk,dv,dtype,mode", [c + (None,) for c in PREFILL_CASES] + [
+    (1, 2, 1000, 30, 64, 64, "bf16", "strongdecay"),
+    (1, 2, 777, 20, 32, 16, "f32", "strongdecay"),
+])
+def test_prefill_then_decode(B, H, T, K, dk, dv, dtype, mode):
     # the cache filled from a prompt of T tokens in one call, then K decoding steps: their
     # outputs against the definition over the whole sequence
     import torch
     import log_linear_attention_chunked_amd as lla
     w = custom(B, H, T + K, dk, dv, dtype)
-    x = generate(w, seed=T + K)
-    print(f"[prefill] B={B} H={H} T={T} K={K} dk={dk} dv={dv} {dtype}", flush=True)
+    x = generate(w, seed=T + K, log_a_mode=mode)
+    print(f"[prefill] B={B} H={H} T={T} K={K} dk={dk} dv={dv} {dtype} {mode}", flush=True)
     d = {k: v.cuda() for k, v in x.items()}
     Lc = x["lam"].shape[-1]
     state, log_scale = lla.new_decode_cache(B, H, dk, dv, Lc)

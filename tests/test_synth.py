@@ -68,6 +68,11 @@ def test_variants_keep_other_tensors():
     assert torch.all(nd["lam"].sum(-1) == 1) and torch.all(nd["lam"][..., 3] == 1)
     low = generate(w, 1, log_a_mode="lowdecay")
     assert low["log_a"].min() >= -1e-4
+    strong = generate(w, 1, log_a_mode="strongdecay")
+    assert strong["log_a"].max() <= -0.5 and strong["log_a"].min() >= -3.0
+    assert torch.equal(base["k"], strong["k"]) and torch.equal(base["lam"], strong["lam"])
+    # a 64-token chunk's local log decay then lies far past -40 (about -112 on average)
+    assert strong["log_a"].sum(-1).max() < -40
     eq = generate(w, 1, lam_mode="equal")
     assert torch.all(eq["lam"] == eq["lam"][..., :1])
     with pytest.raises(ValueError):
