@@ -79,7 +79,9 @@ enum lla_status {
   LLA_ERR_HIP = -3,           /* a HIP runtime call or a kernel launch failed */
   LLA_ERR_NO_MEMORY = -4,     /* stream-ordered workspace allocation failed (also forced, for
                                  tests, by LLA_TEST_FAIL_ALLOC=1 in the environment) */
-  LLA_ERR_WORKSPACE = -5      /* caller workspace smaller than loglinear_attn_workspace_bytes */
+  LLA_ERR_WORKSPACE = -5,     /* caller workspace smaller than loglinear_attn_workspace_bytes */
+  LLA_ERR_SCRATCH_LIMIT = -6  /* loglinear_attn_fwd_noalloc: the call needs more workspace than
+                                 its fixed scratch (loglinear_attn_noalloc_scratch_bytes) */
 };
 
 enum lla_dtype {
@@ -149,6 +151,29 @@ typedef struct lla_fwd_args {
 } lla_fwd_args;
 
 int loglinear_attn_fwd_ex(const lla_fwd_args* args, lla_stream_t stream);
+
+/*
+ * loglinear_attn_fwd_noalloc — loglinear_attn_fwd_ex that allocates nothing, for callers that
+ * cannot allocate device memory around the call: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. The workspace lives in a fixed scratch array in the
+ * library's device memory (loglinear_attn_noalloc_scratch_bytes() bytes, 64 MiB), one per
+ * device, held from the first call on that device until the process ends; no hipMalloc,
+ * hipFree or allocating library routine is called.
+ *   args : as for loglinear_attn_fwd_ex, except that workspace must be NULL and workspace_bytes
+ *          0 (LLA_ERR_INVALID_ARG otherwise). stage_events [1] and [2] are recorded around the
+ *          forward kernel as there; [0] is recorded first.
+ * Returns LLA_ERR_SCRATCH_LIMIT when loglinear_attn_workspace_bytes(...) for these arguments
+ * exceeds the scratch (checked on the host before any device call); otherwise as
+ * loglinear_attn_fwd_ex, with bitwise the same output.
+ * The first call on a device also zero-fills the scratch with a fill kernel on `stream`. Every
+ * call on a device shares that device's scratch and leaves it ready for the next call: calls on
+ * one device that may overlap in time (different streams, threads or processes sharing a
+ * context) race on it and must be serialised by the caller, e.g. by issuing them on one stream.
+ */
+int loglinear_attn_fwd_noalloc(const lla_fwd_args* args, lla_stream_t stream);
+
+/* Size in bytes of the fixed scratch of loglinear_attn_fwd_noalloc (per device). */
+size_t loglinear_attn_noalloc_scratch_bytes(void);
 
 /*
  * loglinear_attn_fwd_varlen — the forward pass over a variable-length batch: N independent

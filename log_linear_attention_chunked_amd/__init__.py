@@ -17,7 +17,7 @@ import ctypes
 from . import _lib
 from ._lib import LibraryNotBuilt  # noqa: F401
 
-__all__ = ["forward", "backward", "decode_prefill", "bwd_workspace_bytes", "bwd_default_chunk", "forward_varlen", "decode_step", "new_decode_cache", "num_levels", "workspace_bytes",
+__all__ = ["forward", "forward_noalloc", "noalloc_scratch_bytes", "backward", "decode_prefill", "bwd_workspace_bytes", "bwd_default_chunk", "forward_varlen", "decode_step", "new_decode_cache", "num_levels", "workspace_bytes",
            "default_chunk", "default_sweep", "LLAError", "LibraryNotBuilt"]
 
 
@@ -125,6 +125,29 @@ def forward(q, k, v, log_a, lam, out=None, *, chunk: int = 0, sweep: int = 0,
     if st != _lib.LLA_OK:
         raise LLAError(st)
     return out
+
+
+def forward_noalloc(q, k, v, log_a, lam, out, *, chunk: int = 0, sweep: int = 0, stream=None,
+                    stage_events=None):
+    """``forward`` through ``loglinear_attn_fwd_noalloc``: the library allocates nothing (its
+    workspace is a fixed per-device scratch of ``noalloc_scratch_bytes()`` bytes), and ``out``
+    must be given, so the call allocates no device memory at all. Same output as ``forward``,
+    bitwise. Calls on one device must not overlap in time (they share the scratch)."""
+    import torch
+    a = make_args(q, k, v, log_a, lam, out, chunk=chunk, sweep=sweep, workspace=None,
+                  stage_events=stage_events)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = _lib.lib().loglinear_attn_fwd_noalloc(ctypes.byref(a), ctypes.c_void_p(handle))
+    if st != _lib.LLA_OK:
+        raise LLAError(st, "loglinear_attn_fwd_noalloc")
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the fixed per-device scratch that ``forward_noalloc`` uses."""
+    return int(_lib.lib().loglinear_attn_noalloc_scratch_bytes())
 
 
 def new_decode_cache(B, H, dk, dv, levels, device="cuda"):

@@ -21,6 +21,7 @@ LLA_ERR_UNSUPPORTED = -2
 LLA_ERR_HIP = -3
 LLA_ERR_NO_MEMORY = -4
 LLA_ERR_WORKSPACE = -5
+LLA_ERR_SCRATCH_LIMIT = -6
 
 LLA_DTYPE_BF16 = 0
 LLA_DTYPE_F32 = 1
@@ -41,6 +42,8 @@ EXPORTS = (
     "loglinear_attn_bwd_workspace_bytes",
     "loglinear_attn_bwd_default_chunk",
     "loglinear_attn_decode_prefill",
+    "loglinear_attn_fwd_noalloc",
+    "loglinear_attn_noalloc_scratch_bytes",
 )
 
 
@@ -196,6 +199,10 @@ def _declare(lib):
     lib.loglinear_attn_bwd_default_chunk.restype = i
     lib.loglinear_attn_decode_prefill.argtypes = [ctypes.POINTER(PrefillArgs), vp]
     lib.loglinear_attn_decode_prefill.restype = i
+    lib.loglinear_attn_fwd_noalloc.argtypes = [ctypes.POINTER(FwdArgs), vp]
+    lib.loglinear_attn_fwd_noalloc.restype = i
+    lib.loglinear_attn_noalloc_scratch_bytes.argtypes = []
+    lib.loglinear_attn_noalloc_scratch_bytes.restype = sz
 
 
 def lib():

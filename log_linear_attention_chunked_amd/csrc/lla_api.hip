@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string.h>
 
 #include "loglinear_attn.h"
@@ -267,6 +268,56 @@ int forward(const lla_fwd_args& a, hipStream_t stream) {
   return run_forward(a, pl, stream, nullptr);
 }
 
+// ---- the entry point that allocates nothing: a fixed scratch array per device ----------------
+//
+// The forward kernel's workspace (ticket counter, node flags, node decays and node records) lives
+// in this static device array instead. Each device that runs the entry point holds its own copy
+// until the process ends. Its name is a host-side stand-in in host code: the device address is
+// taken once per device with hipGetSymbolAddress and only that address is ever passed on.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];          // device address of `scratch` on each device, once known
+
+// The scratch of the current device: its address is looked up on the first call on the device,
+// and the whole array is zero-filled then by a fill kernel on `stream` (the ticket counter and
+// flags must start at zero once; every call leaves them ready for the next one).
+int device_scratch(hipStream_t stream, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LLA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return LLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return LLA_ERR_HIP;
+    const int n = (int)(kScratchBytes / 4);
+    hipLaunchKernelGGL(lla::lla_reset_kernel, dim3(1024), dim3(256), 0, stream, static_cast<int*>(ptr), n);
+    if (hipGetLastError() != hipSuccess) return LLA_ERR_HIP;
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return LLA_OK;
+}
+
+int forward_noalloc(const lla_fwd_args& a, hipStream_t stream) {
+  if (a.workspace || a.workspace_bytes) return LLA_ERR_INVALID_ARG;   // the scratch replaces it
+  Plan pl;
+  int st = make_plan(a.B, a.H, a.T, a.dk, a.dv, a.chunk, a.sweep, a.dtype, pl);
+  if (st != LLA_OK) return st;
+  if (pl.ws_bytes > kScratchBytes) return LLA_ERR_SCRATCH_LIMIT;
+  if (pl.BH == 0 || a.T == 0) return LLA_OK;
+  st = validate_pointers(a, pl);
+  if (st != LLA_OK) return st;
+  void* ws = nullptr;
+  if (pl.ws_bytes > 0) {
+    st = device_scratch(stream, &ws);
+    if (st != LLA_OK) return st;
+  }
+  return launch(a, pl, ws, false, stream, nullptr);
+}
+
 }  // namespace
 
 extern "C" {
@@ -275,6 +326,13 @@ int loglinear_attn_fwd_ex(const lla_fwd_args* args, lla_stream_t stream) {
   if (!args) return LLA_ERR_INVALID_ARG;
   return forward(*args, reinterpret_cast<hipStream_t>(stream));
 }
+
+int loglinear_attn_fwd_noalloc(const lla_fwd_args* args, lla_stream_t stream) {
+  if (!args) return LLA_ERR_INVALID_ARG;
+  return forward_noalloc(*args, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t loglinear_attn_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int loglinear_attn_fwd_varlen(const lla_fwd_varlen_args* args, lla_stream_t stream) {
   if (!args) return LLA_ERR_INVALID_ARG;
@@ -331,6 +389,7 @@ const char* loglinear_attn_status_string(int status) {
     case LLA_ERR_HIP: return "HIP runtime call or kernel launch failed";
     case LLA_ERR_NO_MEMORY: return "workspace allocation failed";
     case LLA_ERR_WORKSPACE: return "caller workspace too small";
+    case LLA_ERR_SCRATCH_LIMIT: return "the call needs more workspace than the fixed scratch of loglinear_attn_fwd_noalloc";
     default: return "unknown status";
   }
 }

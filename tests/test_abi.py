@@ -376,3 +376,22 @@ def _pargs(**kw):
 def test_prefill_validation_codes(L, kw, code):
     assert L.loglinear_attn_decode_prefill(ctypes.byref(_pargs(**kw)), None) == code
 
+
+# ---- the forward entry point that allocates nothing ------------------------------------------
+
+def test_noalloc_scratch_limit_and_arguments(L):
+    scratch = L.loglinear_attn_noalloc_scratch_bytes()
+    assert scratch == 64 << 20
+    # the headline shape fits the scratch; the long d = 128 workloads do not
+    assert L.loglinear_attn_workspace_bytes(4, 16, 8192, 64, 64, 64, 2, 0) <= scratch
+    assert L.loglinear_attn_workspace_bytes(1, 16, 32768, 128, 128, 64, 0, 0) > scratch
+    big = _args(B=1, H=16, T=32768, dk=128, dv=128, chunk=64, sweep=0)
+    assert L.loglinear_attn_fwd_noalloc(ctypes.byref(big), None) == _lib.LLA_ERR_SCRATCH_LIMIT
+    assert _lib.status_string(_lib.LLA_ERR_SCRATCH_LIMIT) != "unknown status"
+    # a workspace argument is refused (the scratch replaces it); validation as in fwd_ex
+    ws = _args(workspace=(1 << 44), workspace_bytes=1 << 30)
+    assert L.loglinear_attn_fwd_noalloc(ctypes.byref(ws), None) == _lib.LLA_ERR_INVALID_ARG
+    assert L.loglinear_attn_fwd_noalloc(None, None) == _lib.LLA_ERR_INVALID_ARG
+    assert L.loglinear_attn_fwd_noalloc(ctypes.byref(_args(dk=48)), None) == _lib.LLA_ERR_UNSUPPORTED
+    assert L.loglinear_attn_fwd_noalloc(ctypes.byref(_args(q=None)), None) == _lib.LLA_ERR_INVALID_ARG
+    assert L.loglinear_attn_fwd_noalloc(ctypes.byref(_args(B=0)), None) == _lib.LLA_OK
