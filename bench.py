@@ -284,6 +284,94 @@ def varlen_measure(dev, stream, steps: int = 20, warmup: int = 5) -> dict:
     }
 
 
+def lambda_bf16_measure(w, d, chunk, sweep, ws, dev, stream, steps: int) -> dict:
+    """The same forward call with the level weights in bfloat16 (lambda_bf16 = 1, the same
+    values rounded once): forward-kernel time between the library's events, tokens/s, and the
+    roofline against the algorithmic bytes with 2L instead of 4L bytes of lambda per head-token."""
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    lam16 = d["lam"].to(torch.bfloat16).contiguous()
+    out = torch.empty_like(d["v"])
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in evs:
+        e.record(stream)
+    call = lambda ev=None: lla.forward(d["q"], d["k"], d["v"], d["log_a"], lam16, out, chunk=chunk,
+                                       sweep=sweep, workspace=ws, stream=stream,
+                                       stage_events=None if ev is None else [None] + ev)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize(dev)
+    ms = 0.0
+    for _ in range(steps):
+        call(evs)
+        torch.cuda.synchronize(dev)
+        ms += evs[0].elapsed_time(evs[1]) / steps
+    e = 2 if w.dtype == "bf16" else 4
+    byts = ((2 * w.dk + 2 * w.dv) * e + 2 * w.L + 4) * w.B * w.H * w.T
+    achieved = byts / (ms * 1e-3) / 1e9
+    return {"kernel_ms": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
+            "algorithmic_bytes_per_launch": byts,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS}}
+
+
+def tune(names, steps: int = 20, warmup: int = 3) -> list:
+    """Forward kernel time of every chunk size and sweep length that fits, per workload: the
+    measurement behind the library's default chunk and sweep (one JSON line per workload).
+
+    Each candidate runs with a caller workspace zero-filled once, timed between events over
+    `steps` back-to-back calls after `warmup` calls."""
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    from lla_synth import WORKLOADS, generate
+    from log_linear_attention_chunked_amd import _lib
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    rows = []
+    from lla_synth import custom
+    for name in names:
+        if name.startswith("shape:"):      # shape:B,H,T,dk,dv,dtype
+            B, H, T, dk, dv, dt = name.split(":", 1)[1].split(",")
+            w = custom(int(B), int(H), int(T), int(dk), int(dv), dtype=dt)
+            name = w.name
+        else:
+            w = WORKLOADS[name]
+        x = generate(w, seed=0)
+        d = {k: v.to(dev) for k, v in x.items()}
+        out = torch.empty_like(d["v"])
+        res = {}
+        for C in (16, 32, 64, 128):
+            for R in (1, 2):
+                n = lla.workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, C, R, w.dtype)
+                ws = torch.zeros(max(n, 1), dtype=torch.uint8, device=dev)
+                call = lambda: lla.forward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], out, chunk=C,
+                                           sweep=R, workspace=ws if n else None, stream=stream)
+                try:
+                    call()
+                except lla.LLAError as e:
+                    if e.status != _lib.LLA_ERR_UNSUPPORTED:
+                        raise
+                    continue                  # does not fit shared memory
+                for _ in range(warmup):
+                    call()
+                torch.cuda.synchronize(dev)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(steps):
+                    call()
+                e1.record(stream)
+                torch.cuda.synchronize(dev)
+                res[f"C{C}_R{R}"] = round(e0.elapsed_time(e1) / steps * 1e3, 2)
+                del ws
+        dc = lla.default_chunk(w.dk, w.dv, w.T, w.dtype)
+        ds = lla.default_sweep(w.B, w.H, w.T, w.dk, w.dv, dc, w.dtype)
+        best = min(res, key=res.get)
+        row = {"workload": name, "us_per_call": res, "best": best, "default": f"C{dc}_R{ds}"}
+        print(json.dumps(row), flush=True)
+        rows.append(row)
+    return rows
+
+
 def cpu_baseline(w, x, heads: int) -> dict:
     """The fp64 oracle as it stands, on `heads` heads of the workload, scaled to tokens/s."""
     import oracle.loglinear as O
@@ -336,6 +424,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-decode", action="store_true", help="skip the decoding-step measurement")
     ap.add_argument("--no-varlen", action="store_true", help="skip the variable-length measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
+    ap.add_argument("--tune", nargs="*", metavar="WORKLOAD", default=None,
+                    help="only time every chunk/sweep that fits, for these workloads (all if none; "
+                         "shape:B,H,T,dk,dv,dtype for another shape)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_fused_kernel.json"),
                     help="measured HBM traffic of the forward kernel (from rocprofv3 counters)")
     a = ap.parse_args(argv)
@@ -360,6 +451,9 @@ def main(argv=None) -> int:
     from lla_synth import WORKLOADS, generate
     from log_linear_attention_chunked_amd import _lib
 
+    if a.tune is not None:
+        tune(a.tune or list(WORKLOADS))
+        return 0
     if not os.path.exists(_lib.LIB_PATH):
         from log_linear_attention_chunked_amd.build import build
         build()
@@ -462,6 +556,8 @@ def main(argv=None) -> int:
         res["varlen"] = varlen_measure(dev, stream)
     if not a.no_backward:
         res["backward"] = backward_measure(w, d, dev, stream)
+    if not a.kernel_only:
+        res["lambda_bf16"] = lambda_bf16_measure(w, d, chunk, sweep, ws, dev, stream, a.steps)
 
     if not a.kernel_only:
         # cold caches: overwrite a 512 MiB buffer (outside the events) before each call

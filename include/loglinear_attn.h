@@ -132,6 +132,11 @@ int loglinear_attn_fwd_f32(const float* q, const float* k, const float* v,
  *           library records on `stream`: [0] before the fill kernel (if any), [1]
  *           just before the forward kernel, [2] after it; [3] is not used. The caller
  *           owns the events.
+ *   lambda_bf16 : 0 = lambda is float32 (4-byte aligned); 1 = lambda is bfloat16 (2-byte
+ *           aligned, same [B,H,T,L] layout), read exactly and widened to float32 inside the
+ *           kernel: the level weights then cost 2L instead of 4L bytes per head-token (the
+ *           study notes list the lambda parameterisation among the things to check, section
+ *           4-5). Any other value is LLA_ERR_INVALID_ARG.
  * The result does not depend on chunk or sweep beyond float rounding.
  */
 typedef struct lla_fwd_args {
@@ -139,7 +144,7 @@ typedef struct lla_fwd_args {
   const void* k;
   const void* v;
   const float* log_a;
-  const float* lambda;
+  const void* lambda;         /* float32, or bfloat16 when lambda_bf16 = 1 */
   void* out;
   int B, H, T, dk, dv;
   int dtype;                  /* enum lla_dtype */
@@ -148,6 +153,7 @@ typedef struct lla_fwd_args {
   void* workspace;
   size_t workspace_bytes;
   void* stage_events[4];      /* hipEvent_t or NULL */
+  int lambda_bf16;            /* 0: float32 lambda; 1: bfloat16 lambda */
 } lla_fwd_args;
 
 int loglinear_attn_fwd_ex(const lla_fwd_args* args, lla_stream_t stream);
@@ -203,7 +209,7 @@ typedef struct lla_fwd_varlen_args {
   const void* k;
   const void* v;
   const float* log_a;
-  const float* lambda;
+  const void* lambda;         /* float32, or bfloat16 when lambda_bf16 = 1 */
   void* out;
   const int* cu_seqlens;      /* device */
   const int* cu_seqlens_host; /* host copy, or NULL */
@@ -213,6 +219,7 @@ typedef struct lla_fwd_varlen_args {
   int sweep;
   void* workspace;
   size_t workspace_bytes;
+  int lambda_bf16;            /* as in lla_fwd_args */
 } lla_fwd_varlen_args;
 
 int loglinear_attn_fwd_varlen(const lla_fwd_varlen_args* args, lla_stream_t stream);
@@ -229,7 +236,16 @@ size_t loglinear_attn_workspace_bytes(int B, int H, int T, int dk, int dv,
 /* Number of lambda levels for T tokens: bit_length(T-1) + 1 (1 for T = 1, 0 for T <= 0). */
 int loglinear_attn_num_levels(int T);
 
-/* Chunk size and sweep length the library picks when both are left at 0. */
+/*
+ * Chunk size and sweep length the library picks when both are left at 0 (0 for invalid
+ * arguments), a rule fitted to forward-kernel times measured on MI355X over every chunk and sweep
+ * that fits, at 17 shapes:
+ *   chunk: 64; 128 for bfloat16 with dk = dv = 128 and T >= 65536; 32 for float32 with
+ *          dk, dv <= 16;
+ *   sweep: 2 for bfloat16 when the sequence has more than one chunk, two chunks fit the shared
+ *          memory and B*H*ceil(chunks/2) >= 128 workgroups result; 1 otherwise (always 1 for
+ *          float32).
+ */
 int loglinear_attn_default_chunk(int dk, int dv, int T, int dtype);
 int loglinear_attn_default_sweep(int B, int H, int T, int dk, int dv, int chunk, int dtype);
 
@@ -330,6 +346,8 @@ int loglinear_attn_decode_prefill(const lla_prefill_args* args, lla_stream_t str
  *           dA of the running call, so calls that may run concurrently must not share it.
  *   stage_events : optional hipEvent_t the library records on `stream`: [0] before the chunk
  *           states, [1] before the gradient kernel, [2] after it, [3] after the grad_log_a scan.
+ *   lambda_bf16 : 0 = lambda float32; 1 = lambda bfloat16 (2-byte aligned), read exactly as in
+ *           loglinear_attn_fwd_ex; grad_lambda is float32 either way.
  * Pointers are device pointers; q, k, v, grad_out 16-byte aligned, the float arrays 4-byte
  * aligned; no output may overlap an input or another output (LLA_ERR_INVALID_ARG). Supported
  * shapes as for the forward pass (dk, dv in {16,32,64,128}, T < 2^23, B*H <= 65535).
@@ -340,7 +358,7 @@ typedef struct lla_bwd_args {
   const void* k;
   const void* v;
   const float* log_a;
-  const float* lambda;
+  const void* lambda;         /* float32, or bfloat16 when lambda_bf16 = 1 */
   const void* grad_out;
   void* grad_q;
   void* grad_k;
@@ -353,6 +371,7 @@ typedef struct lla_bwd_args {
   void* workspace;
   size_t workspace_bytes;
   void* stage_events[4];      /* hipEvent_t or NULL */
+  int lambda_bf16;            /* 0: float32 lambda; 1: bfloat16 lambda (grad_lambda stays float32) */
 } lla_bwd_args;
 
 int loglinear_attn_bwd(const lla_bwd_args* args, lla_stream_t stream);

@@ -69,6 +69,13 @@ def _check(t, name, dtype, shape):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _check_lam(lam, shape):
+    """lambda: float32, or bfloat16 (the library widens it exactly)."""
+    import torch
+    _check(lam, "lam", torch.bfloat16 if getattr(lam, "dtype", None) == torch.bfloat16 else torch.float32,
+           shape)
+
+
 def make_args(q, k, v, log_a, lam, out, *, chunk=0, sweep=0, workspace=None,
               stage_events=None) -> _lib.FwdArgs:
     """Validate tensors and fill the C argument struct (no device work)."""
@@ -82,9 +89,10 @@ def make_args(q, k, v, log_a, lam, out, *, chunk=0, sweep=0, workspace=None,
     _check(k, "k", q.dtype, (B, H, T, dk))
     _check(v, "v", q.dtype, (B, H, T, dv))
     _check(log_a, "log_a", torch.float32, (B, H, T))
-    _check(lam, "lam", torch.float32, (B, H, T, L))
+    _check_lam(lam, (B, H, T, L))
     _check(out, "out", q.dtype, (B, H, T, dv))
     a = _lib.FwdArgs()
+    a.lambda_bf16 = int(lam.dtype == torch.bfloat16)
     a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
     a.log_a, a.lam, a.out = log_a.data_ptr(), lam.data_ptr(), out.data_ptr()
     a.B, a.H, a.T, a.dk, a.dv = int(B), int(H), int(T), int(dk), int(dv)
@@ -106,8 +114,8 @@ def forward(q, k, v, log_a, lam, out=None, *, chunk: int = 0, sweep: int = 0,
     """Forward pass on the current device and stream (or ``stream``).
 
     q, k: [B,H,T,dk]; v: [B,H,T,dv] (bfloat16 or float32, all the same);
-    log_a: [B,H,T] float32; lam: [B,H,T,L] float32 with L = num_levels(T).
-    Returns out [B,H,T,dv] in q's dtype. ``chunk``/``sweep`` 0 = library default;
+    log_a: [B,H,T] float32; lam: [B,H,T,L] float32 (or bfloat16: half the bytes, read
+    exactly) with L = num_levels(T). Returns out [B,H,T,dv] in q's dtype. ``chunk``/``sweep`` 0 = library default;
     ``workspace``: optional uint8 device tensor of >= workspace_bytes(...) bytes.
     ``stage_events``: optional recorded ``torch.cuda.Event`` objects (up to 4, or None)
     the library records around its kernels: before the fill kernel, before the forward
@@ -254,7 +262,7 @@ def forward_varlen(q, k, v, log_a, lam, cu_seqlens, max_T: int, out=None, *, chu
     _check(k, "k", q.dtype, (H, TT, dk))
     _check(v, "v", q.dtype, (H, TT, dv))
     _check(log_a, "log_a", torch.float32, (H, TT))
-    _check(lam, "lam", torch.float32, (H, TT, L))
+    _check_lam(lam, (H, TT, L))
     _check(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,))
     if out is None:
         out = torch.empty((H, TT, dv), dtype=q.dtype, device=q.device)
@@ -262,6 +270,7 @@ def forward_varlen(q, k, v, log_a, lam, cu_seqlens, max_T: int, out=None, *, chu
     a = _lib.VarlenArgs()
     a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
     a.log_a, a.lam, a.out = log_a.data_ptr(), lam.data_ptr(), out.data_ptr()
+    a.lambda_bf16 = int(lam.dtype == torch.bfloat16)
     a.cu_seqlens = cu_seqlens.data_ptr()
     host = None
     if cu_seqlens_host is not None:
@@ -317,11 +326,11 @@ def backward(q, k, v, log_a, lam, dout, *, chunk: int = 0, workspace=None, strea
     _check(k, "k", q.dtype, (B, H, T, dk))
     _check(v, "v", q.dtype, (B, H, T, dv))
     _check(log_a, "log_a", torch.float32, (B, H, T))
-    _check(lam, "lam", torch.float32, (B, H, T, L))
+    _check_lam(lam, (B, H, T, L))
     _check(dout, "dout", q.dtype, (B, H, T, dv))
     if out is None:
         out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
-               torch.empty_like(log_a), torch.empty_like(lam))
+               torch.empty_like(log_a), torch.empty(lam.shape, dtype=torch.float32, device=lam.device))
     gq, gk, gv, gla, glam = out
     _check(gq, "dq", q.dtype, (B, H, T, dk))
     _check(gk, "dk", q.dtype, (B, H, T, dk))
@@ -331,6 +340,7 @@ def backward(q, k, v, log_a, lam, dout, *, chunk: int = 0, workspace=None, strea
     a = _lib.BwdArgs()
     a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
     a.log_a, a.lam, a.grad_out = log_a.data_ptr(), lam.data_ptr(), dout.data_ptr()
+    a.lambda_bf16 = int(lam.dtype == torch.bfloat16)
     a.grad_q, a.grad_k, a.grad_v = gq.data_ptr(), gk.data_ptr(), gv.data_ptr()
     a.grad_log_a, a.grad_lam = gla.data_ptr(), glam.data_ptr()
     a.B, a.H, a.T, a.dk, a.dv = int(B), int(H), int(T), int(dk), int(dv)

@@ -71,6 +71,7 @@ class FwdArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("stage_events", ctypes.c_void_p * 4),
+        ("lambda_bf16", ctypes.c_int),
     ]
 
 
@@ -96,6 +97,7 @@ class VarlenArgs(ctypes.Structure):
         ("sweep", ctypes.c_int),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
+        ("lambda_bf16", ctypes.c_int),
     ]
 
 
@@ -144,6 +146,7 @@ class BwdArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("stage_events", ctypes.c_void_p * 4),
+        ("lambda_bf16", ctypes.c_int),
     ]
 
 

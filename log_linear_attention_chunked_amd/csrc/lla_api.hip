@@ -60,7 +60,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int kSpinLimit = 1 << 20;        // polls of a node flag (each ~1 us) before giving up
 using lla::kLdsPerCU;
-constexpr long kMinWorkgroups = 512;       // below this, prefer one chunk per workgroup
+constexpr long kMinWorkgroups = 128;       // below this, prefer one chunk per workgroup
 
 struct Plan {
   int C, R, m, nchunks, nsweep, ns, L, esize, nw;
@@ -69,20 +69,34 @@ struct Plan {
   int smem;
 };
 
-int default_chunk(int dk, int dv) { return (dk <= 16 && dv <= 16) ? 16 : 64; }
+// Default chunk size and sweep length, from forward-kernel times measured on MI355X over every
+// chunk/sweep that fits (bench.py --tune) for 17 shapes (B·H from 2 to 64, T from 256 to 131072,
+// d from 16 to 128, both dtypes):
+//   * what matters is the tokens a workgroup holds, C·R: 128 (chunk 64 with sweep 2, or chunk 128
+//     with sweep 1) was fastest or within 1.5% of it at every bfloat16 shape with enough
+//     workgroups, for every head size (d = 16: 22.9 µs against 44.7 at chunk 16, sweep 2);
+//   * chunk 128 beat chunk 64 with sweep 2 by 1-3% at dk = dv = 128 and T >= 65536 (1 x 8 x 65536:
+//     339 vs 347 µs; 1 x 32 x 65536: 1190 vs 1230; 1 x 2 x 131072: 221 vs 223), and tied below;
+//   * sweep 2 lost once fewer than 128 workgroups were left (1 x 2 x 2048: 15.4 vs 14.7 µs) and won
+//     above (2 x 8 x 2048, 256 workgroups: 17.6 vs 21.6);
+//   * float32 lost at sweep 2 (4 x 16 x 8192, d = 64: 417 vs 372 µs: the images of two chunks leave
+//     one workgroup of 4 waves per compute unit), and chunk 32 led at d = 16 (10.8 vs 11.8 µs at
+//     chunk 16).
+int default_chunk(int dk, int dv, int T, int esize) {
+  if (esize == 4) return (dk <= 16 && dv <= 16) ? 32 : 64;
+  if (dk == 128 && dv == 128 && T >= 65536) return 128;
+  return 64;
+}
 
 int smem_bytes(int esize, int C, int dk, int dv, int R) {
   return lla::smem_layout(esize, C, dk, dv, R).total;
 }
 
-// Two resident chunks when that keeps 8 waves per compute unit (2 per SIMD) within the
-// shared memory and leaves enough workgroups; one otherwise.
 int default_sweep(long BH, int T, int C, int dk, int dv, int esize) {
   const int nchunks = (T + C - 1) / C;
-  const int nw = dv / 16;
-  const int wg_per_cu = nw >= 8 ? 1 : 8 / nw;
-  const bool fits = smem_bytes(esize, C, dk, dv, 2) * wg_per_cu <= kLdsPerCU;
-  return (fits && nchunks > 1 && BH * ((nchunks + 1) / 2) >= kMinWorkgroups) ? 2 : 1;
+  if (nchunks <= 1 || esize == 4) return 1;
+  if (smem_bytes(esize, C, dk, dv, 2) > kLdsPerCU) return 1;
+  return BH * ((nchunks + 1) / 2) >= kMinWorkgroups ? 2 : 1;
 }
 
 // Host-only part of the plan: sizes and layout; no device calls.
@@ -92,7 +106,7 @@ int make_plan(int B, int H, int T, int dk, int dv, int chunk, int sweep, int dty
   if (!supported_dim(dk) || !supported_dim(dv)) return LLA_ERR_UNSUPPORTED;
   if (chunk != 0 && !supported_dim(chunk)) return LLA_ERR_UNSUPPORTED;
   if (sweep != 0 && sweep != 1 && sweep != 2) return LLA_ERR_UNSUPPORTED;
-  const int C = chunk ? chunk : default_chunk(dk, dv);
+  const int C = chunk ? chunk : default_chunk(dk, dv, T, dtype == LLA_DTYPE_F32 ? 4 : 2);
   const long BH = (long)B * H;
   if (BH > 65535) return LLA_ERR_UNSUPPORTED;
   pl.C = C;
@@ -130,9 +144,11 @@ int validate_pointers(const lla_fwd_args& a, const Plan& pl) {
   if (!a.q || !a.k || !a.v || !a.log_a || !a.lambda || !a.out) return LLA_ERR_INVALID_ARG;
   const size_t es = (size_t)pl.esize;
   const size_t nt = (size_t)pl.BH * a.T;
-  const size_t nq = nt * a.dk * es, nv = nt * a.dv * es, nla = nt * 4, nlam = nt * pl.L * 4;
+  if (a.lambda_bf16 != 0 && a.lambda_bf16 != 1) return LLA_ERR_INVALID_ARG;
+  const size_t lsz = a.lambda_bf16 ? 2 : 4;
+  const size_t nq = nt * a.dk * es, nv = nt * a.dv * es, nla = nt * 4, nlam = nt * pl.L * lsz;
   if (((uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.out) & 15) return LLA_ERR_INVALID_ARG;
-  if (((uintptr_t)a.log_a | (uintptr_t)a.lambda) & 3) return LLA_ERR_INVALID_ARG;
+  if (((uintptr_t)a.log_a & 3) || ((uintptr_t)a.lambda & (lsz - 1))) return LLA_ERR_INVALID_ARG;
   if (overlaps(a.out, nv, a.q, nq) || overlaps(a.out, nv, a.k, nq) || overlaps(a.out, nv, a.v, nv) ||
       overlaps(a.out, nv, a.log_a, nla) || overlaps(a.out, nv, a.lambda, nlam))
     return LLA_ERR_INVALID_ARG;
@@ -165,6 +181,7 @@ int launch(const lla_fwd_args& a, const Plan& pl, void* ws, bool fresh_ws, hipSt
   Params p;
   memset(&p, 0, sizeof(p));
   p.q = a.q; p.k = a.k; p.v = a.v; p.log_a = a.log_a; p.lam = a.lambda; p.out = a.out;
+  p.lam_bf16 = a.lambda_bf16;
   p.BH = (int)pl.BH; p.T = a.T; p.L = pl.L;
   p.nchunks = pl.nchunks; p.sweep = pl.R; p.m = pl.m; p.nsweep = pl.nsweep;
   if (ws) {
@@ -233,6 +250,7 @@ int forward_varlen(const lla_fwd_varlen_args& v, hipStream_t stream) {
   lla_fwd_args a;
   memset(&a, 0, sizeof(a));
   a.q = v.q; a.k = v.k; a.v = v.v; a.log_a = v.log_a; a.lambda = v.lambda; a.out = v.out;
+  a.lambda_bf16 = v.lambda_bf16;
   a.B = 1; a.H = v.H; a.T = v.total_T; a.dk = v.dk; a.dv = v.dv; a.dtype = v.dtype;
   a.workspace = v.workspace; a.workspace_bytes = v.workspace_bytes;
   Plan pp = pl;
@@ -369,14 +387,15 @@ size_t loglinear_attn_workspace_bytes(int B, int H, int T, int dk, int dv, int c
 int loglinear_attn_num_levels(int T) { return T > 0 ? bit_len((unsigned)(T - 1)) + 1 : 0; }
 
 int loglinear_attn_default_chunk(int dk, int dv, int T, int dtype) {
-  (void)T; (void)dtype;
-  return default_chunk(dk, dv);
+  if (!supported_dim(dk) || !supported_dim(dv) || T < 0) return 0;
+  if (dtype != LLA_DTYPE_BF16 && dtype != LLA_DTYPE_F32) return 0;
+  return default_chunk(dk, dv, T, dtype == LLA_DTYPE_F32 ? 4 : 2);
 }
 
 int loglinear_attn_default_sweep(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
-  (void)dtype;
   if (B < 0 || H < 0 || T < 0) return 0;
-  const int C = chunk ? chunk : default_chunk(dk, dv);
+  if (dtype != LLA_DTYPE_BF16 && dtype != LLA_DTYPE_F32) return 0;
+  const int C = chunk ? chunk : default_chunk(dk, dv, T, dtype == LLA_DTYPE_F32 ? 4 : 2);
   if (!supported_dim(C) || !supported_dim(dk) || !supported_dim(dv)) return 0;
   return default_sweep((long)B * H, T, C, dk, dv, dtype == LLA_DTYPE_F32 ? 4 : 2);
 }

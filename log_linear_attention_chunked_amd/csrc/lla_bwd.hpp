@@ -58,7 +58,8 @@ struct BwdParams {
   const void* v;
   const void* dout;
   const float* log_a;
-  const float* lam;
+  const void* lam;  // float32, or bfloat16 when lam_bf16
+  int lam_bf16;
   void* gq;
   void* gk;
   void* gv;
@@ -77,6 +78,15 @@ struct BwdParams {
   int items;                  // sub-blocks per head over all levels
   int rn_off[kLamCap + 1];    // first sub-block of each level
 };
+
+// lambda element i (float32, or bfloat16 widened exactly)
+__device__ __forceinline__ float lambda_at(const BwdParams& p, size_t i) {
+  if (p.lam_bf16) {
+    const unsigned short b = reinterpret_cast<const unsigned short*>(p.lam)[i];
+    return __builtin_bit_cast(float, (unsigned)b << 16);
+  }
+  return reinterpret_cast<const float*>(p.lam)[i];
+}
 
 // Sub-blocks of the target side. At chunk level j the right blocks (2^j chunks) are split into
 // sub-blocks of 2^s chunks, s = min(j, kSubLog): sub-block sb (chunks sb << s ..) belongs to a
@@ -312,11 +322,10 @@ struct Chunk {
     if (KV) stage<DV>(v, reinterpret_cast<const T*>(p.v) + row0 * DV, nv, tid, nt);
     if (QO) stage<DV>(o, reinterpret_cast<const T*>(p.dout) + row0 * DV, nv, tid, nt);
     // every level slot is written: rows past nv and levels past L read as zero weights
-    const float* lg = p.lam + row0 * p.L;
     if (LAM)
       for (int i = tid; i < C * kLamCap; i += nt) {
         const int r = i / kLamCap, l = i % kLamCap;
-        lam[i] = (r < nv && l < p.L) ? lg[r * p.L + l] : 0.f;
+        lam[i] = (r < nv && l < p.L) ? lambda_at(p, (row0 + r) * p.L + l) : 0.f;
       }
     // chunk-local inclusive prefix of log_a by wave 0: each lane holds E consecutive rows
     if (tid < 64) {
@@ -459,7 +468,7 @@ bwd_rn_kernel(BwdParams p) {
       ro[u] = (idx < PO && idx / (DV / EPV) < nv) ? go[idx] : u32x4{0u, 0u, 0u, 0u};
     }
     rla = lane < nv ? p.log_a[row0 + lane] : 0.f;
-    rlm = lane < nv ? p.lam[(row0 + lane) * p.L + J + 1 + j] : 0.f;
+    rlm = lane < nv ? lambda_at(p, (row0 + lane) * p.L + J + 1 + j) : 0.f;
   };
   fetch(c0);
   float eoff = 0.f;     // log decay from the sub-block's start to the current chunk's start

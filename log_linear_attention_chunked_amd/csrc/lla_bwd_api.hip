@@ -305,16 +305,18 @@ int validate(const lla_bwd_args& a, const BwdPlan& pl) {
   if (!a.q || !a.k || !a.v || !a.log_a || !a.lambda || !a.grad_out || !a.grad_q || !a.grad_k ||
       !a.grad_v || !a.grad_log_a || !a.grad_lambda)
     return LLA_ERR_INVALID_ARG;
+  if (a.lambda_bf16 != 0 && a.lambda_bf16 != 1) return LLA_ERR_INVALID_ARG;
   const size_t es = (size_t)pl.esize, nt = (size_t)pl.BH * a.T;
   const size_t nq = nt * a.dk * es, nv = nt * a.dv * es, nla = nt * 4, nlam = nt * pl.L * 4;
+  const size_t nlam_in = nt * pl.L * (a.lambda_bf16 ? 2 : 4);
   if (((uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.grad_out |
        (uintptr_t)a.grad_q | (uintptr_t)a.grad_k | (uintptr_t)a.grad_v) & 15)
     return LLA_ERR_INVALID_ARG;
-  if (((uintptr_t)a.log_a | (uintptr_t)a.lambda | (uintptr_t)a.grad_log_a |
-       (uintptr_t)a.grad_lambda) & 3)
+  if (((uintptr_t)a.log_a | (uintptr_t)a.grad_log_a | (uintptr_t)a.grad_lambda) & 3)
     return LLA_ERR_INVALID_ARG;
+  if ((uintptr_t)a.lambda & (a.lambda_bf16 ? 1 : 3)) return LLA_ERR_INVALID_ARG;
   const void* in[6] = {a.q, a.k, a.v, a.log_a, a.lambda, a.grad_out};
-  const size_t nin[6] = {nq, nq, nv, nla, nlam, nv};
+  const size_t nin[6] = {nq, nq, nv, nla, nlam_in, nv};
   const void* out[5] = {a.grad_q, a.grad_k, a.grad_v, a.grad_log_a, a.grad_lambda};
   const size_t nout[5] = {nq, nq, nv, nla, nlam};
   for (int o = 0; o < 5; ++o) {
@@ -343,6 +345,7 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
   BwdParams p;
   memset(&p, 0, sizeof(p));
   p.q = a.q; p.k = a.k; p.v = a.v; p.dout = a.grad_out; p.log_a = a.log_a; p.lam = a.lambda;
+  p.lam_bf16 = a.lambda_bf16;
   p.gq = a.grad_q; p.gk = a.grad_k; p.gv = a.grad_v; p.glog_a = a.grad_log_a; p.glam = a.grad_lambda;
   char* w = static_cast<char*>(ws);
   p.node = reinterpret_cast<float*>(w + pl.off_node);

@@ -86,6 +86,15 @@ __device__ __forceinline__ void copy_lds4(const void* src, const void* dst) {
   (void)src; (void)dst;
 #endif
 }
+// 2 bytes per lane, zero-extended into the lane's 4-byte slot at M0 + lane * 4 (bfloat16 lambda:
+// the slot then holds the bf16 bits in its low half)
+__device__ __forceinline__ void copy_lds2(const void* src, const void* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("global_load_lds_ushort %0, off" ::"v"(src), "{m0}"(lds_off(dst)) : "memory");
+#else
+  (void)src; (void)dst;
+#endif
+}
 // the same, device scope (sc1): node flags, coherent across XCDs like the flag polls
 __device__ __forceinline__ void copy_lds4_device(const void* src, const void* dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -284,6 +293,26 @@ __device__ __forceinline__ void dma_lambda(float* lam, const float* __restrict__
       const float* src = g + min(i, n_valid - 1);
       copy_lds4(src, lam + blk * 64);
     }
+  }
+}
+
+// bfloat16 lambda rows of one chunk (n_total = C*L elements, n_valid of them real): element i lands
+// zero-extended in the 4-byte slot lam[i] (past the real elements the last one is repeated), one
+// element per lane, so no alignment is assumed; lambda_widen turns the slots into floats once
+// they have landed.
+__device__ __forceinline__ void dma_lambda_bf16(float* lam, const unsigned short* __restrict__ g, int n_valid,
+                                                int n_total, int w, int nw, int lane) {
+  for (int blk = w; blk * 64 < n_total; blk += nw) {
+    const int i = blk * 64 + lane;
+    if (i < n_total) copy_lds2(g + min(i, n_valid - 1), lam + blk * 64);
+  }
+}
+// the elements wave w copied by dma_lambda_bf16 (after they landed): bf16 bits -> float
+__device__ __forceinline__ void lambda_widen(float* lam, int n_total, int w, int nw, int lane) {
+  unsigned* u = reinterpret_cast<unsigned*>(lam);
+  for (int blk = w; blk * 64 < n_total; blk += nw) {
+    const int i = blk * 64 + lane;
+    if (i < n_total) u[i] = u[i] << 16;
   }
 }
 
@@ -752,9 +781,10 @@ constexpr int kFlagBase = 64;   // ints ahead of the node flags (the ticket coun
 
 struct Params {
   const void* q; const void* k; const void* v;
-  const float* log_a; const float* lam;
+  const float* log_a; const void* lam;
   void* out;
   int BH, T, L;
+  int lam_bf16;     // lambda is bfloat16 (else float32)
   int nchunks;      // ceil(T / C)
   int sweep;        // R: chunks per workgroup (the kernel's NB)
   int m;            // log2(R)
@@ -967,7 +997,7 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
   const T* kg = reinterpret_cast<const T*>(p.k) + hoff * DK;
   const T* vg = reinterpret_cast<const T*>(p.v) + hoff * DV;
   const float* lag = p.log_a + hoff;
-  const float* lamg = p.lam + hoff * L;
+  const size_t lam_off = hoff * L;       // lambda element offset of this head's rows
   T* og = reinterpret_cast<T*>(p.out) + hoff * DV;
 
   const int c0 = sw * NB;
@@ -1092,10 +1122,16 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
     dk_plan.issue(smem + S.k[u], kg + (size_t)t0s[u] * DK, valids[u], w, lane);
     dv_plan.issue(smem + S.v[u], vg + (size_t)t0s[u] * DV, valids[u], w, lane);
   }
+  const bool lbf = p.lam_bf16 != 0;
 #pragma unroll
-  for (int u = 0; u < NB; ++u)
-    dma_lambda(reinterpret_cast<float*>(smem + S.lam[u]), lamg + (size_t)t0s[u] * L, valids[u] * L, C * L,
-               w, NW, lane);
+  for (int u = 0; u < NB; ++u) {
+    float* lam = reinterpret_cast<float*>(smem + S.lam[u]);
+    const size_t off = lam_off + (size_t)t0s[u] * L;
+    if (lbf)
+      dma_lambda_bf16(lam, reinterpret_cast<const unsigned short*>(p.lam) + off, valids[u] * L, C * L, w, NW, lane);
+    else
+      dma_lambda(lam, reinterpret_cast<const float*>(p.lam) + off, valids[u] * L, C * L, w, NW, lane);
+  }
 #pragma unroll
   for (int u = 0; u < NB; ++u) dk_plan.issue(smem + S.q[u], qg + (size_t)t0s[u] * DK, valids[u], w, lane);
   if (w == 0) {
@@ -1111,6 +1147,10 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
     }
   }
   wait_vm<NB * dma_count<T, C, DK, NW>(NW - 1)>();   // this wave's flags, k, v, lambda landed
+  if (lbf) {                  // the wave's own bf16 lambda copies -> floats; read after a barrier
+#pragma unroll
+    for (int u = 0; u < NB; ++u) lambda_widen(reinterpret_cast<float*>(smem + S.lam[u]), C * L, w, NW, lane);
+  }
   lds_barrier();
   float gch[NB];                        // total log decay of each chunk
 #pragma unroll

@@ -48,15 +48,24 @@ def test_status_strings(L):
 
 
 def test_defaults(L):
-    assert L.loglinear_attn_default_chunk(16, 16, 256, 1) == 16
+    # the measured rule (header): chunk 64, 128 for bf16 d = 128 at T >= 65536, 32 for small fp32
+    assert L.loglinear_attn_default_chunk(16, 16, 256, 1) == 32
+    assert L.loglinear_attn_default_chunk(16, 16, 4096, 0) == 64
     assert L.loglinear_attn_default_chunk(64, 64, 8192, 0) == 64
+    assert L.loglinear_attn_default_chunk(128, 128, 32768, 0) == 64
+    assert L.loglinear_attn_default_chunk(128, 128, 65536, 0) == 128
+    assert L.loglinear_attn_default_chunk(128, 128, 65536, 1) == 64
+    assert L.loglinear_attn_default_chunk(128, 64, 65536, 0) == 64
+    assert L.loglinear_attn_default_chunk(48, 64, 8192, 0) == 0
     # headline shape: 64 heads x 128 chunks -> two resident chunks per workgroup
     assert L.loglinear_attn_default_sweep(4, 16, 8192, 64, 64, 64, 0) == 2
+    assert L.loglinear_attn_default_sweep(2, 8, 2048, 64, 64, 64, 0) == 2      # 256 workgroups
     assert L.loglinear_attn_default_sweep(1, 1, 64, 64, 64, 64, 0) == 1        # one chunk
     assert L.loglinear_attn_default_sweep(1, 2, 2048, 64, 64, 64, 0) == 1      # too few workgroups
     assert L.loglinear_attn_default_sweep(64, 64, 65536, 128, 128, 64, 0) == 2
-    assert L.loglinear_attn_default_sweep(64, 64, 65536, 128, 64, 64, 0) == 1  # shared memory
+    assert L.loglinear_attn_default_sweep(1, 8, 65536, 128, 128, 0, 0) == 1   # chunk 128: shared memory
     assert L.loglinear_attn_default_sweep(64, 64, 65536, 64, 64, 64, 1) == 1   # float32
+    assert L.loglinear_attn_default_sweep(1, 16, 4096, 16, 16, 0, 0) == 2      # d = 16 at chunk 64
 
 
 def test_workspace_bytes(L):
@@ -146,6 +155,23 @@ def test_shared_memory_limits_largest_fp32_that_fit(L, C, dk, dv, R):
     assert L.loglinear_attn_workspace_bytes(1, 2, 4096, dk, dv, C, R, 1) > 0
     # defaults never pick a sweep that does not fit
     assert L.loglinear_attn_default_sweep(64, 64, 65536, dk, dv, C, 1) in (1, 2)
+
+
+def test_lambda_dtype_validation(L):
+    base = 1 << 40
+    lam = base + (4 << 32)
+    # bfloat16 lambda needs 2-byte alignment, float32 4-byte; other flag values are refused
+    assert _call(L, _args(lambda_bf16=2)) == _lib.LLA_ERR_INVALID_ARG
+    assert _call(L, _args(lambda_bf16=-1)) == _lib.LLA_ERR_INVALID_ARG
+    assert _call(L, _args(lambda_bf16=1, lam=lam + 1)) == _lib.LLA_ERR_INVALID_ARG
+    assert _call(L, _args(lambda_bf16=0, lam=lam + 2)) == _lib.LLA_ERR_INVALID_ARG
+    # out overlapping the (half as long) bf16 lambda is still caught
+    assert _call(L, _args(lambda_bf16=1, out=lam + 128)) == _lib.LLA_ERR_INVALID_ARG
+    assert L.loglinear_attn_bwd(ctypes.byref(_bargs(lambda_bf16=3)), None) == _lib.LLA_ERR_INVALID_ARG
+    assert L.loglinear_attn_bwd(ctypes.byref(_bargs(lambda_bf16=1, lam=lam + 1)), None) == _lib.LLA_ERR_INVALID_ARG
+    assert L.loglinear_attn_bwd(ctypes.byref(_bargs(lambda_bf16=0, lam=lam + 2)), None) == _lib.LLA_ERR_INVALID_ARG
+    # a 2-byte-aligned bf16 lambda passes validation (B = 0 keeps the call a no-op)
+    assert _call(L, _args(B=0, lambda_bf16=1, lam=lam + 2)) == _lib.LLA_OK
 
 
 def test_allocation_failure_returns_no_memory(L, monkeypatch):

@@ -46,6 +46,7 @@ def check(w, x, do, label, **kw):
     want = O.bruteforce_grad(**x, do=do)
     tol = tol_for(w.dtype)
     errs = {n: rel_l2(got[n], want[n]) for n in GRADS}
+    print(f"[bwd] {label}: " + ", ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
     for n in GRADS:
         assert np.all(np.isfinite(got[n])), (label, n)
         assert errs[n] <= tol, (label, n, errs)
