@@ -37,7 +37,8 @@ from dataclasses import dataclass, replace
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "num_levels_for", "generate", "workload", "grad_output"]
+__all__ = ["Workload", "WORKLOADS", "GDN_WORKLOADS", "num_levels_for", "generate", "generate_gdn",
+           "workload", "grad_output"]
 
 
 def num_levels_for(T: int) -> int:
@@ -160,6 +161,38 @@ def generate(w: Workload, seed: int = 0, *, log_a_mode: str | None = None,
         raise ValueError(f"unknown dtype {w.dtype!r}")
     return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(),
                 log_a=log_a.contiguous(), lam=lam.contiguous())
+
+
+# Log-linear Gated DeltaNet: the same shapes, keys L2-normalised per token (the delta rule's
+# transition I - beta k k^T is then a contraction for beta in (0, 1)), plus beta.
+GDN_WORKLOADS: dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("gdn_b1h2_t256_d16_f32", 1, 2, 256, 16, 16, "f32", 16, k_l2norm=True),
+        Workload("gdn_b2h8_t2048_d64_bf16", 2, 8, 2048, 64, 64, "bf16", 64, k_l2norm=True),
+        Workload("gdn_b4h16_t8192_d64_bf16", 4, 16, 8192, 64, 64, "bf16", 64, k_l2norm=True),
+        Workload("gdn_b1h8_t8192_d128_bf16", 1, 8, 8192, 128, 128, "bf16", 32, k_l2norm=True),
+    ]
+}
+
+
+def generate_gdn(w: Workload, seed: int = 0, *, log_a_mode: str | None = None,
+                 lam_mode: str | None = None, beta_mode: str | None = None) -> dict:
+    """Inputs of log-linear Gated DeltaNet: ``generate(w, seed, ...)`` (so q, k, v, log_a and
+    lambda are bit-identical to it) plus ``beta [B,H,T]`` float32 = sigmoid(N(0,1)), drawn from
+    a second generator seeded with ``seed + 104729``. ``beta_mode``: ``"zero"``, ``"ones"``
+    (parity stress cases)."""
+    x = generate(w, seed, log_a_mode=log_a_mode, lam_mode=lam_mode)
+    g = torch.Generator("cpu").manual_seed(int(seed) + 104729)
+    beta = torch.sigmoid(torch.randn((w.B, w.H, w.T), generator=g, dtype=torch.float32))
+    if beta_mode == "zero":
+        beta = torch.zeros_like(beta)
+    elif beta_mode == "ones":
+        beta = torch.ones_like(beta)
+    elif beta_mode is not None:
+        raise ValueError(f"unknown beta_mode {beta_mode!r}")
+    x["beta"] = beta.contiguous()
+    return x
 
 
 def grad_output(w: Workload, seed: int = 0):

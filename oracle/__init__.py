@@ -9,3 +9,4 @@ from .loglinear import (  # noqa: F401
     as_f64, bit_length, bruteforce, bruteforce_rows, level, level_matrix,
     num_levels, recurrent,
 )
+from .deltanet import gdn_attention, gdn_bruteforce, gdn_recurrent, gdn_recurrent_step  # noqa: F401
