@@ -383,6 +383,63 @@ size_t loglinear_attn_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, i
 /* Chunk size loglinear_attn_bwd uses when chunk is 0 (0 for unsupported arguments). */
 int loglinear_attn_bwd_default_chunk(int dk, int dv, int dtype);
 
+/*
+ * loglinear_attn_gdn_fwd — the forward pass of log-linear Gated DeltaNet: the Fenwick
+ * hierarchical mask applied to Gated DeltaNet's own attention matrix, so that every level state
+ * is carried by the delta-rule transition (study notes, section 3-5, where the model's temporal
+ * mask is composed with the hierarchical one keeping its transition; gist.science de technical
+ * summary, where every variant is O = (A * M)V with per-level recurrent states and the delta rule
+ * is combined with the hierarchical structure; zh technical summary, section 2.4). Per (b, h, t):
+ *
+ *   o_t = sum_{s <= t} lambda[t, l(t,s)] beta_s q_t^T A_t A_{t-1} ... A_{s+1} k_s v_s
+ *   A_r = a_r (I - beta_r k_r k_r^T),  a_r = exp(log_a[r]),  l(t, s) = bit_length(t XOR s)
+ *
+ * With every lambda equal this is Gated DeltaNet, S_t = a_t (I - beta_t k_t k_t^T) S_{t-1} +
+ * beta_t k_t v_t^T, o_t = S_t^T q_t. The delta rule's transition is a contraction only for
+ * ||k|| <= 1 and beta in [0, 2]: callers L2-normalise the keys (not checked).
+ *
+ *   q, k [B,H,T,dk], v, out [B,H,T,dv]: bfloat16 or float32 (dtype), naturally aligned
+ *   log_a, beta [B,H,T] float32; lambda [B,H,T,L] float32 (or bfloat16, lambda_bf16 = 1)
+ *   chunk : 0 = loglinear_attn_gdn_default_chunk(dk, dv, dtype), else 16, 32 or 64 when the
+ *           kernels' shared memory fits 160 KB (chunk 64 needs dk, dv <= 64).
+ *   workspace / workspace_bytes : caller device memory of at least
+ *           loglinear_attn_gdn_workspace_bytes(...) bytes (256-byte aligned, no clearing: every
+ *           byte read is written earlier in the call), or NULL/0 to let the library take it
+ *           stream-ordered on `stream`. Holds, in float32, the intra-chunk outputs, the query
+ *           rows carried to their chunk's start and the Fenwick tree over chunks (each node's
+ *           dk x dv state and dk x dk transition); calls that may run concurrently must not
+ *           share it.
+ *   stage_events : optional hipEvent_t recorded on `stream`: [0] before the per-chunk kernel,
+ *           [1] before the tree up-sweep, [2] before the query kernel, [3] after it.
+ * Every product is float32 on the vector units; the launches are gdn_chunk (one workgroup per
+ * chunk and head), one gdn_upsweep per tree level, and gdn_query. Asynchronous on `stream`,
+ * deterministic; returns LLA_OK or a negative LLA_ERR_*; B*H*T = 0 is a no-op.
+ */
+typedef struct lla_gdn_args {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_a;
+  const float* beta;
+  const void* lambda;         /* float32, or bfloat16 when lambda_bf16 = 1 */
+  void* out;
+  int B, H, T, dk, dv;
+  int dtype;                  /* enum lla_dtype */
+  int chunk;
+  void* workspace;
+  size_t workspace_bytes;
+  void* stage_events[4];      /* hipEvent_t or NULL */
+  int lambda_bf16;
+} lla_gdn_args;
+
+int loglinear_attn_gdn_fwd(const lla_gdn_args* args, lla_stream_t stream);
+
+/* Bytes of workspace loglinear_attn_gdn_fwd needs (0 for invalid or unsupported arguments). */
+size_t loglinear_attn_gdn_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype);
+
+/* Chunk loglinear_attn_gdn_fwd uses when chunk is 0: the largest of 64, 32, 16 that fits. */
+int loglinear_attn_gdn_default_chunk(int dk, int dv, int dtype);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,8 @@ import ctypes
 from . import _lib
 from ._lib import LibraryNotBuilt  # noqa: F401
 
-__all__ = ["forward", "forward_noalloc", "noalloc_scratch_bytes", "backward", "decode_prefill", "bwd_workspace_bytes", "bwd_default_chunk", "forward_varlen", "decode_step", "new_decode_cache", "num_levels", "workspace_bytes",
+__all__ = ["forward", "forward_noalloc", "noalloc_scratch_bytes", "gdn_forward", "gdn_workspace_bytes",
+           "gdn_default_chunk", "backward", "decode_prefill", "bwd_workspace_bytes", "bwd_default_chunk", "forward_varlen", "decode_step", "new_decode_cache", "num_levels", "workspace_bytes",
            "default_chunk", "default_sweep", "LLAError", "LibraryNotBuilt"]
 
 
@@ -156,6 +157,64 @@ def forward_noalloc(q, k, v, log_a, lam, out, *, chunk: int = 0, sweep: int = 0,
 def noalloc_scratch_bytes() -> int:
     """Bytes of the fixed per-device scratch that ``forward_noalloc`` uses."""
     return int(_lib.lib().loglinear_attn_noalloc_scratch_bytes())
+
+
+def gdn_workspace_bytes(B, H, T, dk, dv, chunk=0, dtype="bf16") -> int:
+    return int(_lib.lib().loglinear_attn_gdn_workspace_bytes(
+        int(B), int(H), int(T), int(dk), int(dv), int(chunk), _dtype_code(dtype)))
+
+
+def gdn_default_chunk(dk, dv, dtype="bf16") -> int:
+    return int(_lib.lib().loglinear_attn_gdn_default_chunk(int(dk), int(dv), _dtype_code(dtype)))
+
+
+def gdn_forward(q, k, v, log_a, beta, lam, out=None, *, chunk: int = 0, workspace=None,
+                stream=None, stage_events=None):
+    """Log-linear Gated DeltaNet forward (``loglinear_attn_gdn_fwd``) on the current stream.
+
+    q, k: [B,H,T,dk]; v: [B,H,T,dv] (bfloat16 or float32, all the same; keys L2-normalised by the
+    caller); log_a, beta: [B,H,T] float32; lam: [B,H,T,L] float32 or bfloat16, L = num_levels(T).
+    Returns out [B,H,T,dv] in q's dtype. ``chunk`` 0 = library default; ``workspace``: optional
+    uint8 device tensor of >= gdn_workspace_bytes(...) bytes; ``stage_events``: up to 4 recorded
+    ``torch.cuda.Event`` (before the chunk kernel, the up-sweep, the query kernel, after it).
+    """
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, dk]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = num_levels(T) if T > 0 else 0
+    _check(q, "q", q.dtype, (B, H, T, dk))
+    _check(k, "k", q.dtype, (B, H, T, dk))
+    _check(v, "v", q.dtype, (B, H, T, dv))
+    _check(log_a, "log_a", torch.float32, (B, H, T))
+    _check(beta, "beta", torch.float32, (B, H, T))
+    _check_lam(lam, (B, H, T, L))
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, (B, H, T, dv))
+    a = _lib.GdnArgs()
+    a.q, a.k, a.v = q.data_ptr(), k.data_ptr(), v.data_ptr()
+    a.log_a, a.beta, a.lam, a.out = log_a.data_ptr(), beta.data_ptr(), lam.data_ptr(), out.data_ptr()
+    a.lambda_bf16 = int(lam.dtype == torch.bfloat16)
+    a.B, a.H, a.T, a.dk, a.dv = int(B), int(H), int(T), int(dk), int(dv)
+    a.dtype = _dtype_code(q.dtype)
+    a.chunk = int(chunk)
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8, (workspace.numel(),))
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    else:
+        a.workspace, a.workspace_bytes = None, 0
+    if stage_events is not None:
+        for i, ev in enumerate(stage_events):
+            a.stage_events[i] = ev.cuda_event if ev is not None else None
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    st = _lib.lib().loglinear_attn_gdn_fwd(ctypes.byref(a), ctypes.c_void_p(handle))
+    if st != _lib.LLA_OK:
+        raise LLAError(st, "loglinear_attn_gdn_fwd")
+    return out
 
 
 def new_decode_cache(B, H, dk, dv, levels, device="cuda"):

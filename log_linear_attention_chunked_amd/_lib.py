@@ -44,6 +44,9 @@ EXPORTS = (
     "loglinear_attn_decode_prefill",
     "loglinear_attn_fwd_noalloc",
     "loglinear_attn_noalloc_scratch_bytes",
+    "loglinear_attn_gdn_fwd",
+    "loglinear_attn_gdn_workspace_bytes",
+    "loglinear_attn_gdn_default_chunk",
 )
 
 
@@ -168,6 +171,30 @@ class PrefillArgs(ctypes.Structure):
     ]
 
 
+class GdnArgs(ctypes.Structure):
+    """Mirror of ``lla_gdn_args``."""
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("log_a", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p),
+        ("lam", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("B", ctypes.c_int),
+        ("H", ctypes.c_int),
+        ("T", ctypes.c_int),
+        ("dk", ctypes.c_int),
+        ("dv", ctypes.c_int),
+        ("dtype", ctypes.c_int),
+        ("chunk", ctypes.c_int),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("stage_events", ctypes.c_void_p * 4),
+        ("lambda_bf16", ctypes.c_int),
+    ]
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -206,6 +233,12 @@ def _declare(lib):
     lib.loglinear_attn_fwd_noalloc.restype = i
     lib.loglinear_attn_noalloc_scratch_bytes.argtypes = []
     lib.loglinear_attn_noalloc_scratch_bytes.restype = sz
+    lib.loglinear_attn_gdn_fwd.argtypes = [ctypes.POINTER(GdnArgs), vp]
+    lib.loglinear_attn_gdn_fwd.restype = i
+    lib.loglinear_attn_gdn_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.loglinear_attn_gdn_workspace_bytes.restype = sz
+    lib.loglinear_attn_gdn_default_chunk.argtypes = [i, i, i]
+    lib.loglinear_attn_gdn_default_chunk.restype = i
 
 
 def lib():

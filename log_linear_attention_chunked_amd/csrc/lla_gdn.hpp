@@ -1,0 +1,440 @@
+// lla_gdn.hpp — gfx950 kernels of the chunkwise forward pass of log-linear Gated DeltaNet.
+//
+// Operation, per (b,h) and position t (Gated DeltaNet's attention matrix under the Fenwick
+// hierarchical mask; the model's own transition carries every level state — study notes,
+// section 3-5; gist.science de technical summary, "Kernidee" and "Anwendung auf bestehende
+// Modelle"; zh technical summary, section 2.4):
+//   o_t = sum_{s<=t} lambda[t, l(t,s)] beta_s q_t^T A_t ... A_{s+1} k_s v_s,
+//   A_r = a_r (I - beta_r k_r k_r^T),  a_r = exp(log_a[r]),  l(t,s) = bit_length(t ^ s).
+//
+// Chunk structure (chunk C = 2^J, local positions i, j; a_i = chunk-local inclusive prefix of
+// log_a, g = a_{C-1}, Gam[i,j] = exp(a_i - a_j)). With Tm = I + strict_lower(diag(beta)(K K^T *
+// Gam)) (the delta rule inside the chunk in its triangular, "UT" form):
+//   W = Tm^{-1} diag(beta e^a) K,  U = Tm^{-1} diag(beta) V
+//   intra-chunk:  O_intra = ((Lqk Tm^{-1} diag(beta)) * Lambda) V,  Lqk = (Q K^T * Gam) on j <= i
+//                 ((Lqk Tm^{-1} diag(beta))[i,j] = beta_j q_i^T A_i..A_{j+1} k_j, the attention
+//                 matrix inside the chunk);
+//   transport of a query to the chunk start: X0 = diag(e^a) Q - Lqk W
+//                 (row i is q_i^T A_i ... A_{c0}, c0 the chunk's first position);
+//   the chunk as a Fenwick leaf: its state N = Khat^T U and its transition Phi = e^g I - Khat^T W,
+//                 Khat = diag(e^{g-a}) K (the chunk's inputs, and A over the whole chunk).
+// Fenwick nodes over chunks (level j, block m of 2^j chunks): N(j,m) = Phi_R N_L + N_R and
+// Phi(j,m) = Phi_R Phi_L (children L = (j-1, 2m), R = (j-1, 2m+1)). Chunk c reads, for each set
+// bit j of c from the lowest, the node (j, (c >> j) - 1) at level J+1+j with X the query rows
+// carried to that node's end: O += lambda[:, J+1+j] * (X N), then X <- X Phi of that node.
+//
+// Kernels (stream order): gdn_chunk (one workgroup per chunk and head), gdn_upsweep (one launch
+// per tree level; workgroups over node, head and a 16-column panel), gdn_query (one workgroup
+// per chunk and head). Every product runs in float32 on the vector ALUs from shared memory; Tm^{-1}
+// is formed blockwise (16 x 16 diagonal blocks by forward substitution, then doubled); inputs may
+// be bfloat16 or float32, the output is in their type.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace lla {
+namespace gdn {
+
+typedef __bf16 bf16;
+constexpr int kNT = 256;          // threads per workgroup
+constexpr int kLamCapG = 24;      // lambda levels held per position (T <= 2^23)
+
+struct GdnParams {
+  const void* q; const void* k; const void* v;
+  const float* log_a; const float* beta; const void* lam;
+  void* out;
+  int lam_bf16;
+  int BH, T, L;
+  int nchunks;      // ceil(T / C)
+  int nslot;        // tree slots per head: sum over levels j of (nchunks >> j)
+  float* oi;        // [BH][nchunks*C][DV]: intra-chunk outputs
+  float* x0;        // [BH][nchunks*C][DK]: query rows carried to their chunk's start
+  float* node;      // [BH][nslot][DK][DV]: Fenwick node states
+  float* phi;       // [BH][nslot][DK][DK]: Fenwick node transitions
+  int level;        // up-sweep: the level being built (>= 1)
+  int off_prev;     // up-sweep: first slot of level-1
+  int off_cur;      // up-sweep: first slot of level
+  int ncur;         // up-sweep: nodes at level (nchunks >> level)
+};
+
+__device__ __forceinline__ int bit_length(unsigned x) { return 32 - __clz((int)x); }
+
+template <typename T> __device__ __forceinline__ float to_f(T x) { return (float)x; }
+
+__device__ __forceinline__ float lambda_at(const GdnParams& p, size_t i) {
+  if (p.lam_bf16) {
+    const unsigned short b = reinterpret_cast<const unsigned short*>(p.lam)[i];
+    return __builtin_bit_cast(float, (unsigned)b << 16);
+  }
+  return reinterpret_cast<const float*>(p.lam)[i];
+}
+
+// out(i, j) = sum_k A(i, k) B(k, j) for an M x N output over a K-long contraction, operands in
+// shared memory (float32): A(i, k) = TA ? A[k*lda + i] : A[i*lda + k], B(k, j) = TB ?
+// B[j*ldb + k] : B[k*ldb + j], times kscale[k] when kscale is given. Each thread computes 4 x 4
+// blocks of outputs (consecutive threads along a row of blocks) and hands every value to
+// epi(i, j, value).
+template <int M, int N, int K, bool TA, bool TB, typename Epi>
+__device__ __forceinline__ void gemm_f32(const float* A, int lda, const float* B, int ldb, int tid,
+                                         Epi&& epi, const float* kscale = nullptr) {
+  static_assert(M % 4 == 0 && N % 4 == 0, "4 x 4 blocks");
+  constexpr int BN = N / 4, NB = (M / 4) * BN;
+  for (int blk = tid; blk < NB; blk += kNT) {
+    const int i0 = (blk / BN) * 4, j0 = (blk % BN) * 4;
+    float acc[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+#pragma unroll 4
+    for (int k = 0; k < K; ++k) {
+      float a[4], b[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) a[r] = TA ? A[k * lda + i0 + r] : A[(i0 + r) * lda + k];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) b[c] = TB ? B[(j0 + c) * ldb + k] : B[k * ldb + j0 + c];
+      if (kscale) {
+        const float sk = kscale[k];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) b[c] *= sk;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] += a[r] * b[c];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) epi(i0 + r, j0 + c, acc[r][c]);
+  }
+}
+
+// Shared-memory bytes of the three kernels (host and device agree; the host refuses shapes past
+// 160 KB).
+__host__ __device__ constexpr int chunk_smem_bytes(int C, int DK, int DV) {
+  return 4 * (2 * C * (DK + 1) + C * (DV + 1) + 3 * C * (C + 1) + C * (DK + 1) + C * (DV + 1) +
+              C * kLamCapG + 3 * C);
+}
+__host__ __device__ constexpr int up_smem_bytes(int DK) { return 4 * (DK * (DK + 1) + DK * 17); }
+__host__ __device__ constexpr int query_smem_bytes(int C, int DK, int DV) {
+  return 4 * (2 * C * (DK + 1) + C * (DV + 1) + DK * ((DK > DV ? DK : DV) + 1) + C * kLamCapG);
+}
+
+// shared-memory layout of gdn_chunk (floats; row strides padded by one)
+template <int C, int DK, int DV>
+struct ChunkSmem {
+  static constexpr int SK = DK + 1, SV = DV + 1, SC = C + 1;
+  static constexpr int Q = 0, K = Q + C * SK, V = K + C * SK, M1 = V + C * SV, M2 = M1 + C * SC,
+                       Y = M2 + C * SC, W = Y + C * SC, U = W + C * SK, LAM = U + C * SV,
+                       AL = LAM + C * kLamCapG, BT = AL + C, BE = BT + C, TOTAL = BE + C;
+  static constexpr int BYTES = TOTAL * 4;
+  static_assert(BYTES == chunk_smem_bytes(C, DK, DV), "layout and size formula agree");
+};
+
+// gdn_chunk: per (chunk, head) the intra-chunk output, the query rows carried to the chunk's
+// start, and the chunk's Fenwick leaf (state and transition). Rows past T are zero inputs with
+// beta = 0 and log_a = 0 (A = I there), so they change nothing and their outputs are not stored.
+template <typename T, int C, int DK, int DV>
+__global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
+  static_assert(C <= 64, "one lane per position in the log_a scan");
+  using S = ChunkSmem<C, DK, DV>;
+  constexpr int SK = S::SK, SV = S::SV, SC = S::SC;
+  extern __shared__ float sm[];
+  float* Qs = sm + S::Q;  float* Ks = sm + S::K;  float* Vs = sm + S::V;
+  float* M1 = sm + S::M1; float* M2 = sm + S::M2; float* Ti = sm + S::Y;
+  float* Ws = sm + S::W;  float* Us = sm + S::U;  float* lam = sm + S::LAM;
+  float* al = sm + S::AL; float* bt = sm + S::BT; float* be = sm + S::BE;
+
+  const int tid = threadIdx.x;
+  const int c = blockIdx.x % p.nchunks, bh = blockIdx.x / p.nchunks;
+  const int t0 = c * C;
+  const int nv = min(C, p.T - t0);
+  const size_t row0 = (size_t)bh * p.T + t0;          // first input row of the chunk
+  const size_t wrow0 = ((size_t)bh * p.nchunks + c) * C;   // first workspace row of the chunk
+  const T* qg = reinterpret_cast<const T*>(p.q);
+  const T* kg = reinterpret_cast<const T*>(p.k);
+  const T* vg = reinterpret_cast<const T*>(p.v);
+
+  for (int i = tid; i < C * DK; i += kNT) {
+    const int r = i / DK, d = i % DK;
+    const bool ok = r < nv;
+    Qs[r * SK + d] = ok ? to_f(qg[(row0 + r) * DK + d]) : 0.f;
+    Ks[r * SK + d] = ok ? to_f(kg[(row0 + r) * DK + d]) : 0.f;
+  }
+  for (int i = tid; i < C * DV; i += kNT) {
+    const int r = i / DV, e = i % DV;
+    Vs[r * SV + e] = r < nv ? to_f(vg[(row0 + r) * DV + e]) : 0.f;
+  }
+  for (int i = tid; i < C * kLamCapG; i += kNT) {
+    const int r = i / kLamCapG, l = i % kLamCapG;
+    lam[i] = (r < nv && l < p.L) ? lambda_at(p, (row0 + r) * p.L + l) : 0.f;
+  }
+  if (tid < 64) {      // chunk-local inclusive prefix of log_a, one position per lane
+    float x = tid < nv ? p.log_a[row0 + tid] : 0.f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float y = __shfl_up(x, d);
+      if (tid >= d) x += y;
+    }
+    if (tid < C) {
+      const float b = tid < nv ? p.beta[row0 + tid] : 0.f;
+      al[tid] = x;
+      bt[tid] = b;
+      be[tid] = b * __expf(x);
+    }
+  }
+  for (int i = tid; i < C * C; i += kNT) Ti[(i / C) * SC + (i % C)] = 0.f;
+  __syncthreads();
+  const float g = al[C - 1];
+
+  // Tm = I + M1, M1 its strictly lower part; exp of a difference of prefixes, never above 1
+  gemm_f32<C, C, DK, false, true>(Ks, SK, Ks, SK, tid, [&](int i, int j, float x) {
+    M1[i * SC + j] = j < i ? bt[i] * x * __expf(al[i] - al[j]) : 0.f;
+  });
+  __syncthreads();
+
+  // Ti = Tm^{-1} (unit lower triangular): the 16 x 16 diagonal blocks by forward substitution,
+  // one column per thread; then blocks doubled, [A 0; B D]^{-1} = [A^{-1} 0; -D^{-1} B A^{-1}
+  // D^{-1}], with M2 as scratch for B A^{-1}
+  if (tid < C) {
+    const int b0 = (tid / 16) * 16, col = tid % 16;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float r = i == col ? 1.f : 0.f;
+      const float* mrow = M1 + (b0 + i) * SC + b0;
+#pragma unroll
+      for (int j = 0; j < i; ++j) r -= mrow[j] * x[j];
+      x[i] = r;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Ti[(b0 + i) * SC + b0 + col] = x[i];
+  }
+  __syncthreads();
+  auto merge = [&](auto nc) {
+    constexpr int n = decltype(nc)::value;
+    for (int p0 = 0; p0 < C; p0 += 2 * n) {
+      gemm_f32<n, n, n, false, false>(M1 + (p0 + n) * SC + p0, SC, Ti + p0 * SC + p0, SC, tid,
+                                      [&](int i, int j, float x) { M2[i * SC + j] = x; });
+      __syncthreads();
+      gemm_f32<n, n, n, false, false>(Ti + (p0 + n) * SC + p0 + n, SC, M2, SC, tid,
+                                      [&](int i, int j, float x) { Ti[(p0 + n + i) * SC + p0 + j] = -x; });
+      __syncthreads();
+    }
+  };
+  if constexpr (C > 16) merge(std::integral_constant<int, 16>{});
+  if constexpr (C > 32) merge(std::integral_constant<int, 32>{});
+
+  // W = Ti diag(beta e^a) K, U = Ti diag(beta) V; Lqk into M2 (its scratch use is over)
+  gemm_f32<C, DK, C, false, false>(Ti, SC, Ks, SK, tid, [&](int i, int d, float x) { Ws[i * SK + d] = x; }, be);
+  gemm_f32<C, DV, C, false, false>(Ti, SC, Vs, SV, tid, [&](int i, int e, float x) { Us[i * SV + e] = x; }, bt);
+  gemm_f32<C, C, DK, false, true>(Qs, SK, Ks, SK, tid, [&](int i, int j, float x) {
+    M2[i * SC + j] = j <= i ? x * __expf(al[i] - al[j]) : 0.f;
+  });
+  __syncthreads();
+
+  // X0 = diag(e^a) Q - Lqk W (to the workspace); M1 <- (Lqk Ti diag(beta)) * Lambda, the
+  // attention matrix inside the chunk under the level weights (Tm is no longer read)
+  float* x0g = p.x0 + wrow0 * DK;
+  gemm_f32<C, DK, C, false, false>(M2, SC, Ws, SK, tid, [&](int i, int d, float x) {
+    x0g[(size_t)i * DK + d] = __expf(al[i]) * Qs[i * SK + d] - x;
+  });
+  gemm_f32<C, C, C, false, false>(M2, SC, Ti, SC, tid, [&](int i, int j, float x) {
+    M1[i * SC + j] = j <= i ? x * bt[j] * lam[i * kLamCapG + bit_length((unsigned)(i ^ j))] : 0.f;
+  });
+  __syncthreads();
+
+  // O_intra = M1 V (to the workspace); Khat = diag(e^{g-a}) K into the q buffer (q is done)
+  float* oig = p.oi + wrow0 * DV;
+  gemm_f32<C, DV, C, false, false>(M1, SC, Vs, SV, tid, [&](int i, int e, float x) {
+    oig[(size_t)i * DV + e] = x;
+  });
+  for (int i = tid; i < C * DK; i += kNT) {
+    const int r = i / DK, d = i % DK;
+    Qs[r * SK + d] = __expf(g - al[r]) * Ks[r * SK + d];
+  }
+  __syncthreads();
+
+  // the chunk's leaf: N = Khat^T U, Phi = e^g I - Khat^T W
+  const size_t slot = (size_t)bh * p.nslot + c;
+  float* ng = p.node + slot * DK * DV;
+  float* pg = p.phi + slot * DK * DK;
+  gemm_f32<DK, DV, C, true, false>(Qs, SK, Us, SV, tid, [&](int d, int e, float x) {
+    ng[(size_t)d * DV + e] = x;
+  });
+  const float eg = __expf(g);
+  gemm_f32<DK, DK, C, true, false>(Qs, SK, Ws, SK, tid, [&](int d, int d2, float x) {
+    pg[(size_t)d * DK + d2] = (d == d2 ? eg : 0.f) - x;
+  });
+}
+
+// shared-memory layout of gdn_upsweep: the right child's transition and one 16-column panel
+template <int DK>
+struct UpSmem {
+  static constexpr int SP = DK + 1, PW = 16, SW = PW + 1;
+  static constexpr int PHI = 0, PAN = PHI + DK * SP, TOTAL = PAN + DK * SW;
+  static constexpr int BYTES = TOTAL * 4;
+  static_assert(BYTES == up_smem_bytes(DK), "layout and size formula agree");
+};
+
+// gdn_upsweep (level j >= 1): node (j, m) from its children L = (j-1, 2m), R = (j-1, 2m+1):
+//   [N | Phi](j, m) = Phi_R [N_L | Phi_L] + [N_R | 0]
+// one workgroup per (node, head, 16-column panel of [N | Phi]).
+template <int DK, int DV>
+__global__ __launch_bounds__(kNT) void gdn_upsweep_kernel(GdnParams p) {
+  using S = UpSmem<DK>;
+  constexpr int SP = S::SP, PW = S::PW, SW = S::SW, NPAN = (DV + DK) / PW;
+  extern __shared__ float sm[];
+  float* Pr = sm + S::PHI;
+  float* Pan = sm + S::PAN;
+  const int tid = threadIdx.x;
+  const int pan = blockIdx.x % NPAN;
+  const int rest = blockIdx.x / NPAN;
+  const int m = rest % p.ncur, bh = rest / p.ncur;
+  const size_t base = (size_t)bh * p.nslot;
+  const size_t sl = base + p.off_prev + 2 * m, sr = sl + 1, so = base + p.off_cur + m;
+  const bool isN = pan * PW < DV;                      // panel of N (else of Phi)
+  const int col0 = isN ? pan * PW : pan * PW - DV;
+  for (int i = tid; i < DK * DK; i += kNT) Pr[(i / DK) * SP + (i % DK)] = p.phi[sr * DK * DK + i];
+  for (int i = tid; i < DK * PW; i += kNT) {
+    const int r = i / PW, cc = i % PW;
+    Pan[r * SW + cc] = isN ? p.node[sl * DK * DV + (size_t)r * DV + col0 + cc]
+                           : p.phi[sl * DK * DK + (size_t)r * DK + col0 + cc];
+  }
+  __syncthreads();
+  if (isN) {
+    float* out = p.node + so * DK * DV;
+    const float* nr = p.node + sr * DK * DV;
+    gemm_f32<DK, PW, DK, false, false>(Pr, SP, Pan, SW, tid, [&](int r, int cc, float x) {
+      out[(size_t)r * DV + col0 + cc] = x + nr[(size_t)r * DV + col0 + cc];
+    });
+  } else {
+    float* out = p.phi + so * DK * DK;
+    gemm_f32<DK, PW, DK, false, false>(Pr, SP, Pan, SW, tid, [&](int r, int cc, float x) {
+      out[(size_t)r * DK + col0 + cc] = x;
+    });
+  }
+}
+
+// shared-memory layout of gdn_query: query rows (two copies, for X <- X Phi), outputs, one node
+// matrix at a time, lambda rows
+template <int C, int DK, int DV>
+struct QuerySmem {
+  static constexpr int SK = DK + 1, SV = DV + 1, MD = DK > DV ? DK : DV, SM = MD + 1;
+  static constexpr int X = 0, XN = X + C * SK, O = XN + C * SK, MAT = O + C * SV,
+                       LAM = MAT + DK * SM, TOTAL = LAM + C * kLamCapG;
+  static constexpr int BYTES = TOTAL * 4;
+  static_assert(BYTES == query_smem_bytes(C, DK, DV), "layout and size formula agree");
+};
+
+// gdn_query: per (chunk, head) the Fenwick nodes of the chunk's set bits, lowest first, read out
+// with the query rows carried to each node's end; plus the intra-chunk output; store.
+template <typename T, int C, int DK, int DV>
+__global__ __launch_bounds__(kNT) void gdn_query_kernel(GdnParams p) {
+  using S = QuerySmem<C, DK, DV>;
+  constexpr int SK = S::SK, SV = S::SV, SM = S::SM;
+  constexpr int J = C == 16 ? 4 : C == 32 ? 5 : 6;
+  extern __shared__ float sm[];
+  float* Xa = sm + S::X;
+  float* Xb = sm + S::XN;
+  float* Os = sm + S::O;
+  float* Ms = sm + S::MAT;
+  float* lam = sm + S::LAM;
+  const int tid = threadIdx.x;
+  const int c = blockIdx.x % p.nchunks, bh = blockIdx.x / p.nchunks;
+  const int t0 = c * C;
+  const int nv = min(C, p.T - t0);
+  const size_t row0 = (size_t)bh * p.T + t0;
+  const size_t wrow0 = ((size_t)bh * p.nchunks + c) * C;
+  for (int i = tid; i < C * DK; i += kNT) Xa[(i / DK) * SK + (i % DK)] = p.x0[wrow0 * DK + i];
+  for (int i = tid; i < C * DV; i += kNT) Os[(i / DV) * SV + (i % DV)] = p.oi[wrow0 * DV + i];
+  for (int i = tid; i < C * kLamCapG; i += kNT) {
+    const int r = i / kLamCapG, l = i % kLamCapG;
+    lam[i] = (r < nv && l < p.L) ? lambda_at(p, (row0 + r) * p.L + l) : 0.f;
+  }
+  __syncthreads();
+  int off = 0;                 // first slot of level j
+  for (int j = 0; (c >> j) != 0; ++j) {
+    const int cj = c >> j;
+    if (cj & 1) {
+      const size_t slot = (size_t)bh * p.nslot + off + (cj - 1);
+      for (int i = tid; i < DK * DV; i += kNT) Ms[(i / DV) * SM + (i % DV)] = p.node[slot * DK * DV + i];
+      __syncthreads();
+      const int lev = J + 1 + j;
+      gemm_f32<C, DV, DK, false, false>(Xa, SK, Ms, SM, tid, [&](int i, int e, float x) {
+        Os[i * SV + e] += lam[i * kLamCapG + lev] * x;
+      });
+      __syncthreads();
+      if ((c >> (j + 1)) != 0) {           // a higher node follows: X <- X Phi of this node
+        for (int i = tid; i < DK * DK; i += kNT) Ms[(i / DK) * SM + (i % DK)] = p.phi[slot * DK * DK + i];
+        __syncthreads();
+        gemm_f32<C, DK, DK, false, false>(Xa, SK, Ms, SM, tid, [&](int i, int d, float x) {
+          Xb[i * SK + d] = x;
+        });
+        __syncthreads();
+        float* tmp = Xa; Xa = Xb; Xb = tmp;
+      }
+    }
+    off += p.nchunks >> j;
+  }
+  T* og = reinterpret_cast<T*>(p.out);
+  for (int i = tid; i < C * DV; i += kNT) {
+    const int r = i / DV, e = i % DV;
+    if (r < nv) og[(row0 + r) * DV + e] = (T)Os[r * SV + e];
+  }
+}
+
+}  // namespace gdn
+}  // namespace lla
+
+namespace lla {
+namespace gdn {
+
+// per (dtype, chunk) tables of the chunk and query kernels, indexed by (dk, dv); entries whose
+// shared memory would exceed 160 KB are null
+struct GdnKernels {
+  const void* chunk;
+  const void* query;
+};
+const GdnKernels* kernels_bf16_c16(int DK, int DV);
+const GdnKernels* kernels_bf16_c32(int DK, int DV);
+const GdnKernels* kernels_bf16_c64(int DK, int DV);
+const GdnKernels* kernels_f32_c16(int DK, int DV);
+const GdnKernels* kernels_f32_c32(int DK, int DV);
+const GdnKernels* kernels_f32_c64(int DK, int DV);
+
+inline int dim_index(int x) { return x == 16 ? 0 : x == 32 ? 1 : x == 64 ? 2 : x == 128 ? 3 : -1; }
+
+// One (dtype, chunk) table: every (dk, dv) whose kernels fit shared memory.
+template <typename T, int C>
+struct GdnTable {
+  GdnKernels k[4][4];
+  template <int DK, int DV>
+  static constexpr bool fits() {
+    return chunk_smem_bytes(C, DK, DV) <= 160 * 1024 && query_smem_bytes(C, DK, DV) <= 160 * 1024;
+  }
+  template <int DK, int DV>
+  void set() {
+    if constexpr (fits<DK, DV>()) {
+      k[dim_index(DK)][dim_index(DV)] = {reinterpret_cast<const void*>(&gdn_chunk_kernel<T, C, DK, DV>),
+                                         reinterpret_cast<const void*>(&gdn_query_kernel<T, C, DK, DV>)};
+    } else {
+      k[dim_index(DK)][dim_index(DV)] = {nullptr, nullptr};
+    }
+  }
+  template <int DK>
+  void row() { set<DK, 16>(); set<DK, 32>(); set<DK, 64>(); set<DK, 128>(); }
+  GdnTable() { row<16>(); row<32>(); row<64>(); row<128>(); }
+  const GdnKernels* get(int DK, int DV) const {
+    const int a = dim_index(DK), b = dim_index(DV);
+    if (a < 0 || b < 0 || !k[a][b].chunk) return nullptr;
+    return &k[a][b];
+  }
+};
+
+}  // namespace gdn
+}  // namespace lla

@@ -1,0 +1,218 @@
+// lla_gdn_api.hip — C ABI of the log-linear Gated DeltaNet forward pass: argument validation,
+// plan (chunk, tree slots, workspace layout) and the stream-ordered launches gdn_chunk ->
+// gdn_upsweep (one per tree level) -> gdn_query. The contract is documented in
+// include/loglinear_attn.h.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "lla_gdn.hpp"
+#include "lla_host.hpp"
+#include "loglinear_attn.h"
+
+namespace {
+
+using lla::gdn::GdnKernels;
+using lla::gdn::GdnParams;
+
+inline bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+inline int bit_len(unsigned x) { int n = 0; while (x) { ++n; x >>= 1; } return n; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+const GdnKernels* gdn_kernels(int dtype, int C, int dk, int dv) {
+  using namespace lla::gdn;
+  if (dtype == LLA_DTYPE_BF16)
+    return C == 16 ? kernels_bf16_c16(dk, dv) : C == 32 ? kernels_bf16_c32(dk, dv) : C == 64 ? kernels_bf16_c64(dk, dv) : nullptr;
+  if (dtype == LLA_DTYPE_F32)
+    return C == 16 ? kernels_f32_c16(dk, dv) : C == 32 ? kernels_f32_c32(dk, dv) : C == 64 ? kernels_f32_c64(dk, dv) : nullptr;
+  return nullptr;
+}
+
+// the up-sweep kernel depends on (dk, dv) only
+template <int DK>
+const void* upsweep_for_dv(int dv) {
+  switch (dv) {
+    case 16: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep_kernel<DK, 16>);
+    case 32: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep_kernel<DK, 32>);
+    case 64: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep_kernel<DK, 64>);
+    case 128: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep_kernel<DK, 128>);
+  }
+  return nullptr;
+}
+const void* upsweep_kernel(int dk, int dv) {
+  switch (dk) {
+    case 16: return upsweep_for_dv<16>(dv);
+    case 32: return upsweep_for_dv<32>(dv);
+    case 64: return upsweep_for_dv<64>(dv);
+    case 128: return upsweep_for_dv<128>(dv);
+  }
+  return nullptr;
+}
+
+bool fits(int C, int dk, int dv) {
+  using namespace lla::gdn;
+  return chunk_smem_bytes(C, dk, dv) <= lla::kLdsPerCU && query_smem_bytes(C, dk, dv) <= lla::kLdsPerCU;
+}
+
+// the largest chunk of 64, 32, 16 whose kernels fit shared memory
+int default_chunk(int dk, int dv) {
+  for (int C : {64, 32, 16})
+    if (fits(C, dk, dv)) return C;
+  return 0;
+}
+
+struct GdnPlan {
+  int C, N, L, esize, nslot, top;   // top: highest tree level built (0 = leaves only)
+  long BH;
+  size_t off_oi, off_x0, off_node, off_phi, ws_bytes;
+};
+
+int make_plan(int B, int H, int T, int dk, int dv, int chunk, int dtype, GdnPlan& pl) {
+  if (dtype != LLA_DTYPE_BF16 && dtype != LLA_DTYPE_F32) return LLA_ERR_INVALID_ARG;
+  if (B < 0 || H < 0 || T < 0) return LLA_ERR_INVALID_ARG;
+  if (!supported_dim(dk) || !supported_dim(dv)) return LLA_ERR_UNSUPPORTED;
+  if (chunk != 0 && chunk != 16 && chunk != 32 && chunk != 64) return LLA_ERR_UNSUPPORTED;
+  const int C = chunk ? chunk : default_chunk(dk, dv);
+  if (C == 0 || !fits(C, dk, dv)) return LLA_ERR_UNSUPPORTED;
+  const long BH = (long)B * H;
+  if (BH > 65535) return LLA_ERR_UNSUPPORTED;
+  pl.C = C;
+  pl.BH = BH;
+  pl.L = T > 0 ? bit_len((unsigned)(T - 1)) + 1 : 0;
+  if (pl.L > lla::gdn::kLamCapG) return LLA_ERR_UNSUPPORTED;
+  pl.esize = dtype == LLA_DTYPE_BF16 ? 2 : 4;
+  pl.N = (T + C - 1) / C;
+  if ((long)pl.N * BH > 0x7fffffffL) return LLA_ERR_UNSUPPORTED;
+  // the highest chunk bit any chunk index has: levels 1..top are built, node (j, m) for m < N >> j
+  pl.top = pl.N > 1 ? bit_len((unsigned)(pl.N - 1)) - 1 : 0;
+  pl.nslot = 0;
+  for (int j = 0; j <= pl.top; ++j) pl.nslot += pl.N >> j;
+  const size_t rows = (size_t)BH * pl.N * C;
+  size_t off = 0;
+  pl.off_oi = off;   off = align256(off + rows * dv * 4);
+  pl.off_x0 = off;   off = align256(off + rows * dk * 4);
+  pl.off_node = off; off = align256(off + (size_t)BH * pl.nslot * dk * dv * 4);
+  pl.off_phi = off;  off = align256(off + (size_t)BH * pl.nslot * dk * dk * 4);
+  pl.ws_bytes = off;
+  return LLA_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+int validate(const lla_gdn_args& a, const GdnPlan& pl) {
+  if (!a.q || !a.k || !a.v || !a.log_a || !a.beta || !a.lambda || !a.out) return LLA_ERR_INVALID_ARG;
+  if (a.lambda_bf16 != 0 && a.lambda_bf16 != 1) return LLA_ERR_INVALID_ARG;
+  const size_t es = (size_t)pl.esize, nt = (size_t)pl.BH * a.T, ls = a.lambda_bf16 ? 2 : 4;
+  const size_t nq = nt * a.dk * es, nv = nt * a.dv * es, n4 = nt * 4, nl = nt * pl.L * ls;
+  if (((uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.out) & (es - 1)) return LLA_ERR_INVALID_ARG;
+  if (((uintptr_t)a.log_a | (uintptr_t)a.beta) & 3) return LLA_ERR_INVALID_ARG;
+  if ((uintptr_t)a.lambda & (ls - 1)) return LLA_ERR_INVALID_ARG;
+  if (overlaps(a.out, nv, a.q, nq) || overlaps(a.out, nv, a.k, nq) || overlaps(a.out, nv, a.v, nv) ||
+      overlaps(a.out, nv, a.log_a, n4) || overlaps(a.out, nv, a.beta, n4) || overlaps(a.out, nv, a.lambda, nl))
+    return LLA_ERR_INVALID_ARG;
+  return LLA_OK;
+}
+
+hipError_t set_smem(const void* fn, int bytes) {
+  return bytes > 65536 ? hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes)
+                       : hipSuccess;
+}
+
+int launch(const lla_gdn_args& a, const GdnPlan& pl, void* ws, hipStream_t stream) {
+  using namespace lla::gdn;
+  const GdnKernels* ks = gdn_kernels(a.dtype, pl.C, a.dk, a.dv);
+  const void* up = upsweep_kernel(a.dk, a.dv);
+  if (!ks || !up) return LLA_ERR_UNSUPPORTED;
+  GdnParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = a.q; p.k = a.k; p.v = a.v; p.log_a = a.log_a; p.beta = a.beta; p.lam = a.lambda; p.out = a.out;
+  p.lam_bf16 = a.lambda_bf16;
+  p.BH = (int)pl.BH; p.T = a.T; p.L = pl.L; p.nchunks = pl.N; p.nslot = pl.nslot;
+  p.oi = reinterpret_cast<float*>((char*)ws + pl.off_oi);
+  p.x0 = reinterpret_cast<float*>((char*)ws + pl.off_x0);
+  p.node = reinterpret_cast<float*>((char*)ws + pl.off_node);
+  p.phi = reinterpret_cast<float*>((char*)ws + pl.off_phi);
+  auto mark = [&](int i) {
+    return a.stage_events[i] ? hipEventRecord(reinterpret_cast<hipEvent_t>(a.stage_events[i]), stream)
+                             : hipSuccess;
+  };
+  const unsigned grid = (unsigned)(pl.N * pl.BH);
+  const int sc = chunk_smem_bytes(pl.C, a.dk, a.dv), sq = query_smem_bytes(pl.C, a.dk, a.dv);
+  const int su = up_smem_bytes(a.dk);
+  if (mark(0) != hipSuccess) return LLA_ERR_HIP;
+  {
+    void* args[] = {&p};
+    if (set_smem(ks->chunk, sc) != hipSuccess) return LLA_ERR_HIP;
+    if (hipLaunchKernel(ks->chunk, dim3(grid), dim3(kNT), args, sc, stream) != hipSuccess) return LLA_ERR_HIP;
+  }
+  if (mark(1) != hipSuccess) return LLA_ERR_HIP;
+  if (set_smem(up, su) != hipSuccess) return LLA_ERR_HIP;
+  int off_prev = 0;
+  for (int j = 1; j <= pl.top; ++j) {
+    GdnParams pj = p;
+    pj.level = j;
+    pj.off_prev = off_prev;
+    pj.off_cur = off_prev + (pl.N >> (j - 1));
+    pj.ncur = pl.N >> j;
+    off_prev = pj.off_cur;
+    void* args[] = {&pj};
+    const unsigned g = (unsigned)((long)pj.ncur * pl.BH * ((a.dv + a.dk) / 16));
+    if (hipLaunchKernel(up, dim3(g), dim3(kNT), args, su, stream) != hipSuccess) return LLA_ERR_HIP;
+  }
+  if (mark(2) != hipSuccess) return LLA_ERR_HIP;
+  {
+    void* args[] = {&p};
+    if (set_smem(ks->query, sq) != hipSuccess) return LLA_ERR_HIP;
+    if (hipLaunchKernel(ks->query, dim3(grid), dim3(kNT), args, sq, stream) != hipSuccess) return LLA_ERR_HIP;
+  }
+  if (mark(3) != hipSuccess) return LLA_ERR_HIP;
+  return LLA_OK;
+}
+
+int gdn_forward(const lla_gdn_args& a, hipStream_t stream) {
+  GdnPlan pl;
+  int st = make_plan(a.B, a.H, a.T, a.dk, a.dv, a.chunk, a.dtype, pl);
+  if (st != LLA_OK) return st;
+  if (pl.BH == 0 || a.T == 0) return LLA_OK;
+  st = validate(a, pl);
+  if (st != LLA_OK) return st;
+  void* ws = a.workspace;
+  bool owned = false;
+  if (ws) {
+    if (a.workspace_bytes < pl.ws_bytes) return LLA_ERR_WORKSPACE;
+    if ((uintptr_t)ws & 255) return LLA_ERR_INVALID_ARG;
+  } else {
+    if (lla::workspace_alloc(&ws, pl.ws_bytes, stream) != hipSuccess) return LLA_ERR_NO_MEMORY;
+    owned = true;
+  }
+  st = launch(a, pl, ws, stream);
+  if (owned && hipFreeAsync(ws, stream) != hipSuccess && st == LLA_OK) st = LLA_ERR_HIP;
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int loglinear_attn_gdn_fwd(const lla_gdn_args* args, lla_stream_t stream) {
+  if (!args) return LLA_ERR_INVALID_ARG;
+  return gdn_forward(*args, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t loglinear_attn_gdn_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
+  GdnPlan pl;
+  if (make_plan(B, H, T, dk, dv, chunk, dtype, pl) != LLA_OK) return 0;
+  return pl.ws_bytes;
+}
+
+int loglinear_attn_gdn_default_chunk(int dk, int dv, int dtype) {
+  if (!supported_dim(dk) || !supported_dim(dv)) return 0;
+  if (dtype != LLA_DTYPE_BF16 && dtype != LLA_DTYPE_F32) return 0;
+  return default_chunk(dk, dv);
+}
+
+}  // extern "C"

@@ -421,3 +421,61 @@ def test_noalloc_scratch_limit_and_arguments(L):
     assert L.loglinear_attn_fwd_noalloc(ctypes.byref(_args(dk=48)), None) == _lib.LLA_ERR_UNSUPPORTED
     assert L.loglinear_attn_fwd_noalloc(ctypes.byref(_args(q=None)), None) == _lib.LLA_ERR_INVALID_ARG
     assert L.loglinear_attn_fwd_noalloc(ctypes.byref(_args(B=0)), None) == _lib.LLA_OK
+
+
+# ---- log-linear Gated DeltaNet ------------------------------------------------------------------
+
+def _gargs(**kw):
+    a = _lib.GdnArgs()
+    base = 1 << 40                 # fake, well-separated, aligned addresses: never dereferenced
+    for i, n in enumerate(("q", "k", "v", "log_a", "beta", "lam", "out")):
+        setattr(a, n, base + (i << 32))
+    a.B, a.H, a.T, a.dk, a.dv = 1, 2, 4096, 64, 64
+    a.dtype, a.chunk = 0, 0
+    a.workspace, a.workspace_bytes = None, 0
+    for k_, v_ in kw.items():
+        setattr(a, k_, v_)
+    return a
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), _lib.LLA_ERR_INVALID_ARG),
+    (dict(T=-1), _lib.LLA_ERR_INVALID_ARG),
+    (dict(dk=48), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(chunk=128), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(chunk=8), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(dk=128, dv=128, chunk=64), _lib.LLA_ERR_UNSUPPORTED),     # shared memory
+    (dict(B=300, H=300), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(T=1 << 24), _lib.LLA_ERR_UNSUPPORTED),
+    (dict(beta=None), _lib.LLA_ERR_INVALID_ARG),
+    (dict(out=None), _lib.LLA_ERR_INVALID_ARG),
+    (dict(beta=(1 << 40) + (4 << 32) + 2), _lib.LLA_ERR_INVALID_ARG),   # misaligned
+    (dict(out=(1 << 40) + (4 << 32) + 64), _lib.LLA_ERR_INVALID_ARG),   # out overlaps beta
+    (dict(lambda_bf16=2), _lib.LLA_ERR_INVALID_ARG),
+    (dict(workspace=(1 << 44), workspace_bytes=1024), _lib.LLA_ERR_WORKSPACE),
+    (dict(workspace=(1 << 44) + 16, workspace_bytes=1 << 36), _lib.LLA_ERR_INVALID_ARG),
+])
+def test_gdn_validation_codes(L, kw, code):
+    assert L.loglinear_attn_gdn_fwd(ctypes.byref(_gargs(**kw)), None) == code
+
+
+def test_gdn_defaults_workspace_and_noop(L, monkeypatch):
+    assert L.loglinear_attn_gdn_fwd(None, None) == _lib.LLA_ERR_INVALID_ARG
+    for kw in (dict(B=0), dict(T=0), dict(T=0, q=None)):
+        assert L.loglinear_attn_gdn_fwd(ctypes.byref(_gargs(**kw)), None) == _lib.LLA_OK
+    assert L.loglinear_attn_gdn_default_chunk(64, 64, 0) == 64
+    assert L.loglinear_attn_gdn_default_chunk(128, 128, 0) == 32
+    assert L.loglinear_attn_gdn_default_chunk(128, 64, 1) == 32
+    assert L.loglinear_attn_gdn_default_chunk(16, 16, 1) == 64
+    assert L.loglinear_attn_gdn_default_chunk(48, 64, 0) == 0
+    ws = L.loglinear_attn_gdn_workspace_bytes
+    # B=4, H=16, T=8192, d=64, chunk 64: outputs and query rows in fp32; 128 chunks, whose
+    # indices have bits 0..6, so tree levels 0..6: 128 + 64 + ... + 2 = 254 slots of a 64 x 64
+    # state and a 64 x 64 transition per head
+    n = ws(4, 16, 8192, 64, 64, 0, 0)
+    expect = 64 * 8192 * (64 + 64) * 4 + 64 * 254 * (64 * 64 * 2) * 4
+    assert expect <= n <= expect + 4 * 256
+    assert ws(1, 1, 64, 64, 64, 64, 0) > 0          # one chunk: a leaf, no levels above it
+    assert ws(1, 1, 64, 64, 64, 128, 0) == 0         # unsupported -> 0
+    monkeypatch.setenv("LLA_TEST_FAIL_ALLOC", "1")
+    assert L.loglinear_attn_gdn_fwd(ctypes.byref(_gargs()), None) == _lib.LLA_ERR_NO_MEMORY
