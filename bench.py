@@ -372,6 +372,94 @@ def tune(names, steps: int = 20, warmup: int = 3) -> list:
     return rows
 
 
+def gdn_algorithmic(w, chunk: int) -> tuple[float, float]:
+    """(FLOP, bytes) per head-token of the chunkwise log-linear Gated DeltaNet forward.
+
+    FLOP (2 per multiply-add): per chunk, K K^T and Q K^T (C dk each per token), the blockwise
+    inverse of the C x C triangular matrix (~C^2/3 per token), W and U (C dk and C dv), the query
+    rows' transport X0 (C dk), the in-chunk attention matrix (C^2) and its product with V (C dv),
+    the leaf state and transition (dk dv and dk^2); then per Fenwick node read (log2(T/C)/2 on
+    average) X N (dk dv) and, for all but the last, X Phi (dk^2); the up-sweep is one level-j node
+    per 2^j chunks (below 1% here). Bytes: q, k, v, out in the element type, log_a and beta and
+    the L lambda levels in float32."""
+    import math
+    e = 2 if w.dtype == "bf16" else 4
+    C, dk, dv = chunk, w.dk, w.dv
+    n = max(1, -(-w.T // C))
+    pbar = math.log2(n) / 2 if n > 1 else 0.0
+    mac = (2 * C * dk + C * C / 3 + C * dk + C * dv + C * dk + C * C + C * dv + dk * dv + dk * dk
+           + pbar * dk * dv + max(pbar - 1, 0) * dk * dk)
+    byts = (2 * dk + 2 * dv) * e + 8 + 4 * w.L
+    return 2 * mac, byts
+
+
+def gdn_measure(dev, stream, steps: int = 10, warmup: int = 2) -> dict:
+    """Log-linear Gated DeltaNet (``loglinear_attn_gdn_fwd``) at the headline's shape (B=4, H=16,
+    T=8192, d=64, bf16, keys L2-normalised, beta = sigmoid(N(0,1))): time per call between events,
+    per-stage times from the library's events, tokens/s, and its roofline. Its products run in
+    float32 on the vector units, so the bound is the float32 rate (157.3 TFLOP/s); the HBM
+    fraction is reported beside it."""
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    from lla_synth import GDN_WORKLOADS, generate_gdn
+    w = GDN_WORKLOADS["gdn_b4h16_t8192_d64_bf16"]
+    x = generate_gdn(w, seed=0)
+    d = {k: v.to(dev) for k, v in x.items()}
+    chunk = lla.gdn_default_chunk(w.dk, w.dv, w.dtype)
+    ws = torch.empty(lla.gdn_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, chunk, w.dtype),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(d["v"])
+    call = lambda evs=None: lla.gdn_forward(d["q"], d["k"], d["v"], d["log_a"], d["beta"], d["lam"], out,
+                                            chunk=chunk, workspace=ws, stream=stream, stage_events=evs)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for ev in evs:
+        ev.record(stream)
+    torch.cuda.synchronize(dev)
+    call(evs)
+    torch.cuda.synchronize(dev)
+    stages = {"chunk": evs[0].elapsed_time(evs[1]), "upsweep": evs[1].elapsed_time(evs[2]),
+              "query": evs[2].elapsed_time(evs[3])}
+    flop_ht, byte_ht = gdn_algorithmic(w, chunk)
+    ht = w.B * w.H * w.T
+    tflops = flop_ht * ht / (ms * 1e-3) / 1e12
+    return {
+        "config": {"workload": w.name, "chunk": chunk, "workspace_bytes": ws.numel()},
+        "ms_per_call": ms,
+        "stages_ms": stages,
+        "tokens_per_s": w.B * w.T / (ms * 1e-3),
+        "algorithmic_flop_per_call": flop_ht * ht,
+        "algorithmic_bytes_per_call": byte_ht * ht,
+        "hbm_frac": byte_ht * ht / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"bound": "alu", "achieved": tflops, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / FP32_PEAK_TFLOPS, "scope": "whole call, float32 products"},
+    }
+
+
+def cpu_recurrent(w, x, heads: int) -> dict:
+    """The oracle's O(T log T) recurrent form (one dk x dv state per level, carry merges) on
+    `heads` heads of the workload, scaled to the whole call: the second CPU reference."""
+    import oracle.loglinear as O
+    heads = max(1, min(heads, w.H))
+    sl = slice(0, heads)
+    t = time.perf_counter()
+    O.recurrent(x["q"][:1, sl], x["k"][:1, sl], x["v"][:1, sl], x["log_a"][:1, sl], x["lam"][:1, sl])
+    dt = time.perf_counter() - t
+    full = dt * w.B * w.H / heads
+    return {"value": w.B * w.T / full, "unit": "tokens/s", "kind": "oracle (recurrent form)",
+            "sample": f"recurrent form on {heads} of {w.B * w.H} heads, {dt:.2f} s measured, scaled "
+                      f"x{w.B * w.H / heads:g}", "seconds_measured": dt}
+
+
 def cpu_baseline(w, x, heads: int) -> dict:
     """The fp64 oracle as it stands, on `heads` heads of the workload, scaled to tokens/s."""
     import oracle.loglinear as O
@@ -424,11 +512,12 @@ def main(argv=None) -> int:
     ap.add_argument("--no-decode", action="store_true", help="skip the decoding-step measurement")
     ap.add_argument("--no-varlen", action="store_true", help="skip the variable-length measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
+    ap.add_argument("--no-gdn", action="store_true", help="skip the log-linear Gated DeltaNet measurement")
     ap.add_argument("--tune", nargs="*", metavar="WORKLOAD", default=None,
                     help="only time every chunk/sweep that fits, for these workloads (all if none; "
                          "shape:B,H,T,dk,dv,dtype for another shape)")
-    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_fused_kernel.json"),
-                    help="measured HBM traffic of the forward kernel (from rocprofv3 counters)")
+    ap.add_argument("--counters", default=os.path.join(ROOT, "profiles", "fwd_counters.json"),
+                    help="forward-kernel counters per workload (rocprofv3: HBM traffic, MFMA busy cycles)")
     a = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -508,15 +597,18 @@ def main(argv=None) -> int:
 
     t_out = stage["forward"] * 1e-3
     achieved = byte_ht * ht / t_out / 1e9
-    traffic = None
-    if os.path.exists(a.traffic):
+    # counters recorded by rocprofv3 for this workload and launch configuration, used only while
+    # the forward kernel's sources are the ones they were taken from
+    traffic = mfma_busy = None
+    if os.path.exists(a.counters):
         try:
-            rec = json.load(open(a.traffic))
-            if (rec.get("workload") == w.name and rec.get("chunk") == chunk and rec.get("sweep") == sweep
+            rec = json.load(open(a.counters))["records"].get(w.name, {})
+            if (rec.get("chunk") == chunk and rec.get("sweep") == sweep
                     and rec.get("kernel_source_sha") == _kernel_sha()):
                 traffic = rec.get("hbm_bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
+                mfma_busy = rec.get("mfma_busy_frac")
+        except (OSError, ValueError, KeyError):
+            traffic = mfma_busy = None
     peak_flops = (BF16_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS) * 1e12
     res = {
         "metric": METRIC,
@@ -547,6 +639,7 @@ def main(argv=None) -> int:
         "stages_ms": stage,
         "path_hbm_frac": byte_ht * ht / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "mfma_util_algorithmic": flop_ht * ht / (ms_per_step * 1e-3) / peak_flops,
+        "mfma_busy_counter": mfma_busy,
         "algorithmic_flop_per_step": flop_ht * ht,
     }
 
@@ -558,6 +651,8 @@ def main(argv=None) -> int:
         res["backward"] = backward_measure(w, d, dev, stream)
     if not a.kernel_only:
         res["lambda_bf16"] = lambda_bf16_measure(w, d, chunk, sweep, ws, dev, stream, a.steps)
+    if not a.kernel_only and not a.no_gdn:
+        res["gated_deltanet"] = gdn_measure(dev, stream)
 
     if not a.kernel_only:
         # cold caches: overwrite a 512 MiB buffer (outside the events) before each call
@@ -589,6 +684,7 @@ def main(argv=None) -> int:
 
     if not a.kernel_only and not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, x, a.cpu_heads)
+        res["cpu_baseline"]["recurrent_form"] = cpu_recurrent(w, x, 8)
         res["gpu_over_cpu"] = value / res["cpu_baseline"]["value"]
 
     print(json.dumps(res), flush=True)
