@@ -273,7 +273,14 @@ const char* loglinear_attn_status_string(int status);
  *          written, so the cache needs no clearing before t = 0.
  *   Lc     levels of the cache: at least bit_length(t) + 1 (LLA_ERR_INVALID_ARG otherwise),
  *          at most 25 (positions below 2^24).
- * Steps on one cache must run in order of t (on one stream); t is the same for all (b, h).
+ * Steps on one cache must run in order of t (on one stream).
+ *   t_seq  NULL: every (b, h) is at position t. Else a device array of B int64 positions, one per
+ *          sequence (a batch of prompts of different lengths decoded together; the heads of a
+ *          sequence share its position), and t is the largest of them (it sizes the Lc check).
+ *          A negative entry means that sequence takes no step: its cache and its out rows are
+ *          left untouched (e.g. a finished request). An entry past t makes that sequence's out
+ *          rows NaN and leaves its cache untouched, so a wrong array never reaches past the
+ *          cache. 8-byte aligned; read on the device, never on the host.
  * Pointers are device pointers; out, state and log_scale must not overlap each other or the
  * inputs. Returns LLA_OK or a negative LLA_ERR_* (B*H = 0 is a no-op).
  */
@@ -289,6 +296,7 @@ typedef struct lla_decode_args {
   int B, H, dk, dv, Lc;
   int dtype;                  /* enum lla_dtype */
   long long t;
+  const long long* t_seq;     /* per-sequence positions [B] (device), or NULL */
 } lla_decode_args;
 
 int loglinear_attn_decode_step(const lla_decode_args* args, lla_stream_t stream);

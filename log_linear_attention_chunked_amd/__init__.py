@@ -258,13 +258,16 @@ def decode_prefill(k, v, log_a, state, log_scale, *, stream=None):
     return state, log_scale
 
 
-def decode_step(q, k, v, log_a, lam, state, log_scale, t: int, out=None, *, stream=None):
+def decode_step(q, k, v, log_a, lam, state, log_scale, t: int, out=None, *, stream=None,
+                t_seq=None):
     """One decoding step at position ``t`` (the same for every (b, h)); updates the cache.
 
     q, k: [B,H,dk]; v: [B,H,dv] (bfloat16 or float32); log_a: [B,H] float32;
     lam: [B,H,Lc] float32 (the token's level weights); state [B,H,Lc,dk,dv] and
     log_scale [B,H,2,Lc] float32 (``new_decode_cache``). Returns out [B,H,dv] in q's dtype.
     Steps on one cache must be issued for t = 0, 1, 2, ... in order.
+    ``t_seq``: optional int64 device tensor [B], one position per sequence (``t`` is then the
+    largest of them); a negative entry skips that sequence (cache and out rows untouched).
     """
     import torch
     if q.dim() != 3:
@@ -289,6 +292,11 @@ def decode_step(q, k, v, log_a, lam, state, log_scale, t: int, out=None, *, stre
     a.B, a.H, a.dk, a.dv, a.Lc = int(B), int(H), int(dk), int(dv), int(Lc)
     a.dtype = _dtype_code(q.dtype)
     a.t = int(t)
+    if t_seq is not None:
+        _check(t_seq, "t_seq", torch.int64, (B,))
+        a.t_seq = t_seq.data_ptr()
+    else:
+        a.t_seq = None
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)

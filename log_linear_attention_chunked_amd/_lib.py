@@ -122,6 +122,7 @@ class DecodeArgs(ctypes.Structure):
         ("Lc", ctypes.c_int),
         ("dtype", ctypes.c_int),
         ("t", ctypes.c_longlong),
+        ("t_seq", ctypes.c_void_p),
     ]
 
 

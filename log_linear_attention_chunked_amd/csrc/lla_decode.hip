@@ -43,8 +43,9 @@ struct Params {
   const float* log_a; const float* lam;
   void* out;
   float* state; float* lscale;
-  int dv, Lc;
-  long long t;
+  int dv, Lc, H;
+  long long t;                 // the position of every (b, h), or the largest one when t_seq is set
+  const long long* t_seq;      // per-sequence positions [B] (device), or null
 };
 
 // Row groups: thread (rg, col) owns rows rg*RG .. rg*RG+RG-1 of column 16*blockIdx.y + col.
@@ -58,7 +59,14 @@ __global__ __launch_bounds__(kCols * row_groups<DK>()) void lla_decode_kernel(Pa
   const int bh = blockIdx.x, cb = blockIdx.y;
   const int dv = p.dv, Lc = p.Lc;
   const int vc = cb * kCols + col;
-  const long long t = p.t;
+  // this sequence's position: a negative one takes no step (nothing is read or written); one past
+  // the largest the call declared (the cache was sized for) writes NaN and leaves the cache alone
+  const long long t = p.t_seq ? p.t_seq[bh / p.H] : p.t;
+  if (t < 0) return;
+  if (t > p.t) {
+    if (tid < kCols) reinterpret_cast<T*>(p.out)[(size_t)bh * dv + cb * kCols + tid] = from_f32<T>(__builtin_nanf(""));
+    return;
+  }
   const int par = (int)(t & 1);
 
   __shared__ float qs[DK], ks[DK], lam[kMaxLevels], sig[kMaxLevels], red[NRG][kCols];
@@ -199,6 +207,7 @@ extern "C" int loglinear_attn_decode_step(const lla_decode_args* a, lla_stream_t
   if (BH > 0x7fffffffLL) return LLA_ERR_UNSUPPORTED;
   if (!a->q || !a->k || !a->v || !a->log_a || !a->lambda || !a->out || !a->state || !a->log_scale)
     return LLA_ERR_INVALID_ARG;
+  if ((uintptr_t)a->t_seq % 8) return LLA_ERR_INVALID_ARG;
   const size_t es = a->dtype == LLA_DTYPE_BF16 ? 2 : 4;
   const void* eptr[] = {a->q, a->k, a->v, a->out};
   for (const void* x : eptr)
@@ -223,7 +232,8 @@ extern "C" int loglinear_attn_decode_step(const lla_decode_args* a, lla_stream_t
   memset(&p, 0, sizeof(p));
   p.q = a->q; p.k = a->k; p.v = a->v; p.log_a = a->log_a; p.lam = a->lambda; p.out = a->out;
   p.state = a->state; p.lscale = a->log_scale;
-  p.dv = a->dv; p.Lc = a->Lc; p.t = a->t;
+  p.dv = a->dv; p.Lc = a->Lc; p.t = a->t; p.H = a->H;
+  p.t_seq = a->t_seq;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const hipError_t e = a->dtype == LLA_DTYPE_BF16 ? launch<__hip_bfloat16>(p, (int)BH, a->dk, s)
                                                   : launch<float>(p, (int)BH, a->dk, s);

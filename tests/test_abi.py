@@ -240,6 +240,7 @@ def _dargs(**kw):
     (dict(state=(1 << 40) + (6 << 32) + 2), _lib.LLA_ERR_INVALID_ARG),
     (dict(out=(1 << 40) + 64), _lib.LLA_ERR_INVALID_ARG),  # out overlaps q
     (dict(state=(1 << 40) + (7 << 32) - 1024), _lib.LLA_ERR_INVALID_ARG),  # state overlaps log_scale
+    (dict(t_seq=(1 << 44) + 4), _lib.LLA_ERR_INVALID_ARG),                  # misaligned positions
 ])
 def test_decode_validation_codes(L, kw, code):
     assert L.loglinear_attn_decode_step(ctypes.byref(_dargs(**kw)), None) == code

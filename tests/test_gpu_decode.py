@@ -180,3 +180,65 @@ def test_prefill_then_decode(B, H, T, K, dk, dv, dtype, mode):
                      for b in range(B)])
     assert np.all(np.isfinite(got))
     assert rel_l2(got, want) <= tol_for(dtype), rel_l2(got, want)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_per_sequence_positions(dtype):
+    # three sequences decoded together at their own positions: sequence b starts at global step
+    # start[b] (skipped before that: negative position), so at step s it is at s - start[b];
+    # each sequence's outputs against the definition on that sequence alone, and the skipped
+    # steps leave its out rows and cache untouched
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    B, H, dk, dv = 3, 2, 32, 16
+    start = [0, 37, 100]
+    steps = 160
+    x = generate(custom(B, H, steps, dk, dv, dtype=dtype), seed=23)
+    d = {k: v.cuda() for k, v in x.items()}
+    Lc = x["lam"].shape[-1]
+    state, log_scale = lla.new_decode_cache(B, H, dk, dv, Lc)
+    state.fill_(float("nan"))
+    log_scale.fill_(float("nan"))
+    got = torch.full((B, H, steps, dv), 7.0, dtype=d["q"].dtype, device="cuda")
+    for s in range(steps):
+        pos = [s - st for st in start]
+        tq = torch.tensor(pos, dtype=torch.int64, device="cuda")
+        # sequence b at position p reads token p of its own stream
+        idx = [max(p, 0) for p in pos]
+        sel = lambda t: torch.stack([t[b, :, idx[b]] for b in range(B)]).contiguous()
+        out = torch.full((B, H, dv), 7.0, dtype=d["q"].dtype, device="cuda")
+        lla.decode_step(sel(d["q"]), sel(d["k"]), sel(d["v"]), sel(d["log_a"]), sel(d["lam"]),
+                        state, log_scale, max(pos), out, t_seq=tq)
+        for b in range(B):
+            if pos[b] >= 0:
+                got[b, :, pos[b]] = out[b]
+            else:
+                assert torch.all(out[b] == 7.0)      # a skipped sequence's out rows untouched
+    torch.cuda.synchronize()
+    got = got.double().cpu().numpy()
+    for b in range(B):
+        n = steps - start[b]
+        xb = {k_: v_[b:b + 1, :, :n] for k_, v_ in x.items()}
+        want = O.bruteforce(xb["q"], xb["k"], xb["v"], xb["log_a"], xb["lam"][..., :O.num_levels(n)])
+        err = rel_l2(got[b:b + 1, :, :n], want)
+        print(f"decode per-sequence positions {dtype} seq {b} ({n} tokens): rel_l2={err:.3e}", flush=True)
+        assert np.all(np.isfinite(got[b, :, :n]))
+        assert err <= tol_for(dtype), (b, err)
+
+
+def test_decode_position_past_the_declared_maximum_gives_nan():
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    B, H, dk, dv = 2, 1, 16, 16
+    x = generate(custom(B, H, 8, dk, dv, dtype="f32"), seed=2)
+    d = {k: v[:, :, 5].contiguous().cuda() for k, v in x.items()}
+    state, log_scale = lla.new_decode_cache(B, H, dk, dv, 5)
+    state.zero_()
+    log_scale.zero_()
+    before = state.clone()
+    tq = torch.tensor([5, 9], dtype=torch.int64, device="cuda")       # the second is past t = 5
+    lam = torch.rand((B, H, 5), dtype=torch.float32, device="cuda")
+    out = lla.decode_step(d["q"], d["k"], d["v"], d["log_a"], lam, state, log_scale, 5, t_seq=tq)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isnan(out[1])) and torch.all(torch.isfinite(out[0]))
+    assert torch.equal(state[1], before[1])
