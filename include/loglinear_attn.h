@@ -406,7 +406,7 @@ int loglinear_attn_bwd_default_chunk(int dk, int dv, int dtype);
  * beta_t k_t v_t^T, o_t = S_t^T q_t. The delta rule's transition is a contraction only for
  * ||k|| <= 1 and beta in [0, 2]: callers L2-normalise the keys (not checked).
  *
- *   q, k [B,H,T,dk], v, out [B,H,T,dv]: bfloat16 or float32 (dtype), naturally aligned
+ *   q, k [B,H,T,dk], v, out [B,H,T,dv]: bfloat16 or float32 (dtype), 16-byte aligned
  *   log_a, beta [B,H,T] float32; lambda [B,H,T,L] float32 (or bfloat16, lambda_bf16 = 1)
  *   chunk : 0 = loglinear_attn_gdn_default_chunk(dk, dv, dtype), else 16, 32 or 64 when the
  *           kernels' shared memory fits 160 KB (chunk 64 needs dk, dv <= 64).

@@ -25,7 +25,7 @@
 //
 // Kernels (stream order): gdn_chunk (one workgroup per chunk and head), gdn_upsweep (one launch
 // per tree level; workgroups over node, head and a 16-column panel), gdn_query (one workgroup
-// per chunk and head). Every product runs in float32 on the vector ALUs from shared memory; Tm^{-1}
+// per chunk and head). Every product runs in float32 on the matrix cores from shared memory; Tm^{-1}
 // is formed blockwise (16 x 16 diagonal blocks by forward substitution, then doubled); inputs may
 // be bfloat16 or float32, the output is in their type.
 #pragma once
@@ -74,44 +74,105 @@ __device__ __forceinline__ float lambda_at(const GdnParams& p, size_t i) {
 
 // out(i, j) = sum_k A(i, k) B(k, j) for an M x N output over a K-long contraction, operands in
 // shared memory (float32): A(i, k) = TA ? A[k*lda + i] : A[i*lda + k], B(k, j) = TB ?
-// B[j*ldb + k] : B[k*ldb + j], times kscale[k] when kscale is given. Each thread computes 4 x 4
-// blocks of outputs (consecutive threads along a row of blocks) and hands every value to
-// epi(i, j, value).
+// B[j*ldb + k] : B[k*ldb + j], times kscale[k] when kscale is given. On the matrix cores in
+// float32 (v_mfma_f32_16x16x4_f32): 16 x 16 output tiles dealt to the waves in turn; per step,
+// lane (j, g) (j = lane % 16, g = lane / 16) supplies A(16ti + j, k + g) and B(k + g, 16tj + j),
+// and the accumulator gives it rows 16ti + 4g .. +3 of column 16tj + j. Every output value is
+// handed once to epi(i, j, value).
 template <int M, int N, int K, bool TA, bool TB, typename Epi>
 __device__ __forceinline__ void gemm_f32(const float* A, int lda, const float* B, int ldb, int tid,
                                          Epi&& epi, const float* kscale = nullptr) {
-  static_assert(M % 4 == 0 && N % 4 == 0, "4 x 4 blocks");
-  constexpr int BN = N / 4, NB = (M / 4) * BN;
-  for (int blk = tid; blk < NB; blk += kNT) {
-    const int i0 = (blk / BN) * 4, j0 = (blk % BN) * 4;
-    float acc[4][4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+  static_assert(M % 16 == 0 && N % 16 == 0 && K % 4 == 0, "16 x 16 tiles, 4-deep steps");
+  constexpr int TN = N / 16, NTILE = (M / 16) * TN, NWAVE = kNT / 64;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int j = lane & 15, g = lane >> 4;
+  for (int tile = w; tile < NTILE; tile += NWAVE) {
+    const int i0 = (tile / TN) * 16, j0 = (tile % TN) * 16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-    for (int k = 0; k < K; ++k) {
-      float a[4], b[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] = TA ? A[k * lda + i0 + r] : A[(i0 + r) * lda + k];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) b[c] = TB ? B[(j0 + c) * ldb + k] : B[k * ldb + j0 + c];
-      if (kscale) {
-        const float sk = kscale[k];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) b[c] *= sk;
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] += a[r] * b[c];
+    for (int k = 0; k < K; k += 4) {
+      const int kk = k + g;
+      const float a = TA ? A[kk * lda + i0 + j] : A[(i0 + j) * lda + kk];
+      float b = TB ? B[(j0 + j) * ldb + kk] : B[kk * ldb + j0 + j];
+      if (kscale) b *= kscale[kk];
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) epi(i0 + r, j0 + c, acc[r][c]);
+    for (int r = 0; r < 4; ++r) epi(i0 + 4 * g + r, j0 + j, acc[r]);
   }
 }
+
+// An R x CC row-major block (source row stride src_ld elements) on its way into shared-memory
+// floats dst[r * ldd + c], rows at or past nv read as zeros: load() issues the thread's 16-byte
+// vector loads into registers, store() converts and writes them. Several blocks loaded before
+// any is stored cost one memory round trip together.
+template <typename T, int R, int CC>
+struct StagedBlock {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  static constexpr int EPV = 16 / (int)sizeof(T), VPR = CC / EPV, NVEC = R * VPR;
+  static constexpr int PER = (NVEC + kNT - 1) / kNT;
+  static_assert(CC % EPV == 0, "whole 16-byte vectors per row");
+  u32x4 buf[PER];
+
+  __device__ __forceinline__ void load(const T* src, size_t src_ld, int nv, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int v = tid + i * kNT, r = v / VPR;
+      buf[i] = u32x4{0u, 0u, 0u, 0u};
+      if (v < NVEC && r < nv) buf[i] = *reinterpret_cast<const u32x4*>(src + (size_t)r * src_ld + (v % VPR) * EPV);
+    }
+  }
+  __device__ __forceinline__ void store(float* dst, int ldd, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int v = tid + i * kNT;
+      if (v >= NVEC) break;
+      float* d = dst + (v / VPR) * ldd + (v % VPR) * EPV;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // the element is copied to a scalar first: a bit cast applied to the vector element
+        // itself compiles to a read of element 0 whatever e is
+        const unsigned word = buf[i][e];
+        if constexpr (sizeof(T) == 4) {
+          d[e] = __builtin_bit_cast(float, word);
+        } else {
+          d[2 * e] = __builtin_bit_cast(float, word << 16);
+          d[2 * e + 1] = __builtin_bit_cast(float, word & 0xffff0000u);
+        }
+      }
+    }
+  }
+};
+
+template <typename T, int R, int CC>
+__device__ __forceinline__ void stage_block(float* dst, int ldd, const T* src, size_t src_ld, int nv, int tid) {
+  StagedBlock<T, R, CC> b;
+  b.load(src, src_ld, nv, tid);
+  b.store(dst, ldd, tid);
+}
+
+// lambda rows of positions [row0, row0 + C) bound for lam[r * kLamCapG + l] (rows past nv and
+// levels past L are zero weights), loaded and stored like StagedBlock
+template <int C>
+struct StagedLambda {
+  static constexpr int PER = (C * kLamCapG + kNT - 1) / kNT;
+  float buf[PER];
+  __device__ __forceinline__ void load(const GdnParams& p, size_t row0, int nv, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * kNT, r = idx / kLamCapG, l = idx % kLamCapG;
+      buf[i] = (idx < C * kLamCapG && r < nv && l < p.L) ? lambda_at(p, (row0 + r) * p.L + l) : 0.f;
+    }
+  }
+  __device__ __forceinline__ void store(float* lam, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = tid + i * kNT;
+      if (idx < C * kLamCapG) lam[idx] = buf[i];
+    }
+  }
+};
 
 // Shared-memory bytes of the three kernels (host and device agree; the host refuses shapes past
 // 160 KB).
@@ -159,19 +220,18 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
   const T* kg = reinterpret_cast<const T*>(p.k);
   const T* vg = reinterpret_cast<const T*>(p.v);
 
-  for (int i = tid; i < C * DK; i += kNT) {
-    const int r = i / DK, d = i % DK;
-    const bool ok = r < nv;
-    Qs[r * SK + d] = ok ? to_f(qg[(row0 + r) * DK + d]) : 0.f;
-    Ks[r * SK + d] = ok ? to_f(kg[(row0 + r) * DK + d]) : 0.f;
-  }
-  for (int i = tid; i < C * DV; i += kNT) {
-    const int r = i / DV, e = i % DV;
-    Vs[r * SV + e] = r < nv ? to_f(vg[(row0 + r) * DV + e]) : 0.f;
-  }
-  for (int i = tid; i < C * kLamCapG; i += kNT) {
-    const int r = i / kLamCapG, l = i % kLamCapG;
-    lam[i] = (r < nv && l < p.L) ? lambda_at(p, (row0 + r) * p.L + l) : 0.f;
+  {
+    StagedBlock<T, C, DK> sq, sk;
+    StagedBlock<T, C, DV> sv;
+    StagedLambda<C> sl;
+    sq.load(qg + row0 * DK, DK, nv, tid);
+    sk.load(kg + row0 * DK, DK, nv, tid);
+    sv.load(vg + row0 * DV, DV, nv, tid);
+    sl.load(p, row0, nv, tid);
+    sq.store(Qs, SK, tid);
+    sk.store(Ks, SK, tid);
+    sv.store(Vs, SV, tid);
+    sl.store(lam, tid);
   }
   if (tid < 64) {      // chunk-local inclusive prefix of log_a, one position per lane
     float x = tid < nv ? p.log_a[row0 + tid] : 0.f;
@@ -299,11 +359,14 @@ __global__ __launch_bounds__(kNT) void gdn_upsweep_kernel(GdnParams p) {
   const size_t sl = base + p.off_prev + 2 * m, sr = sl + 1, so = base + p.off_cur + m;
   const bool isN = pan * PW < DV;                      // panel of N (else of Phi)
   const int col0 = isN ? pan * PW : pan * PW - DV;
-  for (int i = tid; i < DK * DK; i += kNT) Pr[(i / DK) * SP + (i % DK)] = p.phi[sr * DK * DK + i];
-  for (int i = tid; i < DK * PW; i += kNT) {
-    const int r = i / PW, cc = i % PW;
-    Pan[r * SW + cc] = isN ? p.node[sl * DK * DV + (size_t)r * DV + col0 + cc]
-                           : p.phi[sl * DK * DK + (size_t)r * DK + col0 + cc];
+  {
+    StagedBlock<float, DK, DK> sp;
+    StagedBlock<float, DK, PW> sc;
+    sp.load(p.phi + sr * DK * DK, DK, DK, tid);
+    if (isN) sc.load(p.node + sl * DK * DV + col0, DV, DK, tid);
+    else sc.load(p.phi + sl * DK * DK + col0, DK, DK, tid);
+    sp.store(Pr, SP, tid);
+    sc.store(Pan, SW, tid);
   }
   __syncthreads();
   if (isN) {
@@ -350,11 +413,16 @@ __global__ __launch_bounds__(kNT) void gdn_query_kernel(GdnParams p) {
   const int nv = min(C, p.T - t0);
   const size_t row0 = (size_t)bh * p.T + t0;
   const size_t wrow0 = ((size_t)bh * p.nchunks + c) * C;
-  for (int i = tid; i < C * DK; i += kNT) Xa[(i / DK) * SK + (i % DK)] = p.x0[wrow0 * DK + i];
-  for (int i = tid; i < C * DV; i += kNT) Os[(i / DV) * SV + (i % DV)] = p.oi[wrow0 * DV + i];
-  for (int i = tid; i < C * kLamCapG; i += kNT) {
-    const int r = i / kLamCapG, l = i % kLamCapG;
-    lam[i] = (r < nv && l < p.L) ? lambda_at(p, (row0 + r) * p.L + l) : 0.f;
+  {
+    StagedBlock<float, C, DK> sx;
+    StagedBlock<float, C, DV> so;
+    StagedLambda<C> sl;
+    sx.load(p.x0 + wrow0 * DK, DK, C, tid);
+    so.load(p.oi + wrow0 * DV, DV, C, tid);
+    sl.load(p, row0, nv, tid);
+    sx.store(Xa, SK, tid);
+    so.store(Os, SV, tid);
+    sl.store(lam, tid);
   }
   __syncthreads();
   int off = 0;                 // first slot of level j
@@ -362,7 +430,7 @@ __global__ __launch_bounds__(kNT) void gdn_query_kernel(GdnParams p) {
     const int cj = c >> j;
     if (cj & 1) {
       const size_t slot = (size_t)bh * p.nslot + off + (cj - 1);
-      for (int i = tid; i < DK * DV; i += kNT) Ms[(i / DV) * SM + (i % DV)] = p.node[slot * DK * DV + i];
+      stage_block<float, DK, DV>(Ms, SM, p.node + slot * DK * DV, DV, DK, tid);
       __syncthreads();
       const int lev = J + 1 + j;
       gemm_f32<C, DV, DK, false, false>(Xa, SK, Ms, SM, tid, [&](int i, int e, float x) {
@@ -370,7 +438,7 @@ __global__ __launch_bounds__(kNT) void gdn_query_kernel(GdnParams p) {
       });
       __syncthreads();
       if ((c >> (j + 1)) != 0) {           // a higher node follows: X <- X Phi of this node
-        for (int i = tid; i < DK * DK; i += kNT) Ms[(i / DK) * SM + (i % DK)] = p.phi[slot * DK * DK + i];
+        stage_block<float, DK, DK>(Ms, SM, p.phi + slot * DK * DK, DK, DK, tid);
         __syncthreads();
         gemm_f32<C, DK, DK, false, false>(Xa, SK, Ms, SM, tid, [&](int i, int d, float x) {
           Xb[i * SK + d] = x;

@@ -108,7 +108,7 @@ int validate(const lla_gdn_args& a, const GdnPlan& pl) {
   if (a.lambda_bf16 != 0 && a.lambda_bf16 != 1) return LLA_ERR_INVALID_ARG;
   const size_t es = (size_t)pl.esize, nt = (size_t)pl.BH * a.T, ls = a.lambda_bf16 ? 2 : 4;
   const size_t nq = nt * a.dk * es, nv = nt * a.dv * es, n4 = nt * 4, nl = nt * pl.L * ls;
-  if (((uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.out) & (es - 1)) return LLA_ERR_INVALID_ARG;
+  if (((uintptr_t)a.q | (uintptr_t)a.k | (uintptr_t)a.v | (uintptr_t)a.out) & 15) return LLA_ERR_INVALID_ARG;
   if (((uintptr_t)a.log_a | (uintptr_t)a.beta) & 3) return LLA_ERR_INVALID_ARG;
   if ((uintptr_t)a.lambda & (ls - 1)) return LLA_ERR_INVALID_ARG;
   if (overlaps(a.out, nv, a.q, nq) || overlaps(a.out, nv, a.k, nq) || overlaps(a.out, nv, a.v, nv) ||
