@@ -299,66 +299,123 @@ struct Chunk {
     ws = reinterpret_cast<float*>(sm + L.ws);
   }
 
-  // rows [0, nv) from the head's tensors starting at row p0; rows past nv are zero
-  template <int D>
-  __device__ static void stage(T* img, const T* __restrict__ g, int nv, int tid, int nt) {
-    constexpr int EPV = 16 / ES, NV = D / EPV, RS = D + 16 / ES;
-    for (int idx = tid; idx < C * NV; idx += nt) {
-      const int r = idx / NV, c = (idx % NV) * EPV;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (r < nv) x = *reinterpret_cast<const u32x4*>(g + (size_t)r * D + c);
-      *reinterpret_cast<u32x4*>(img + r * RS + c) = x;
+  // one image's rows [0, nv) in registers on their way into shared memory, in 16-byte pieces
+  // (rows past nv are written as zeros). Every load is unconditional, from a clamped row of the
+  // chunk (nv >= 1): with no load under a branch the compiler's counted waits stay exact, so a
+  // wait for these loads never drains loads issued after them.
+  template <int D, int NT>
+  struct Rows {
+    static constexpr int EPV = 16 / ES, NVR = D / EPV, RS = D + 16 / ES, NP = C * NVR;
+    static constexpr int PER = (NP + NT - 1) / NT;
+    u32x4 r[PER];
+    __device__ __forceinline__ void fetch(const T* g, int nv, int tid) {
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int idx = min(tid + u * NT, NP - 1), row = min(idx / NVR, nv - 1);
+        r[u] = *reinterpret_cast<const u32x4*>(g + (size_t)row * D + (idx % NVR) * EPV);
+      }
     }
-  }
+    __device__ __forceinline__ void put(T* img, int nv, int tid) const {
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int idx = tid + u * NT;
+        if (idx < NP)
+          *reinterpret_cast<u32x4*>(img + (idx / NVR) * RS + (idx % NVR) * EPV) =
+              idx / NVR < nv ? r[u] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
 
-  // everything of chunk c of head bh; ends with a barrier. A = chunk-local inclusive prefix of
-  // log_a, ea = exp(A), ws = exp(g - A) (decay from a position to the chunk's end).
+  // everything of chunk c of head bh: fetch() issues every global load into registers (raw words,
+  // unconditional, from clamped indices), put() writes the images, the lambda rows and (wave 0,
+  // after its chunk-local scan of log_a) the decays, without a barrier. Between the two a caller
+  // may issue loads of its own; the chunk then costs one memory round trip whatever else is in
+  // flight. A = chunk-local inclusive prefix of log_a, ea = exp(A), ws = exp(g - A) (decay from
+  // a position to the chunk's end).
   // KV: k and v images; QO: q and do images; LAM: all lambda rows (else none)
-  template <bool KV = true, bool QO = true, bool LAM = true>
-  __device__ void load(const BwdParams& p, int bh, int c, int nv, int tid, int nt) {
-    const size_t row0 = (size_t)bh * p.T + (size_t)c * C;
-    if (QO) stage<DK>(q, reinterpret_cast<const T*>(p.q) + row0 * DK, nv, tid, nt);
-    if (KV) stage<DK>(k, reinterpret_cast<const T*>(p.k) + row0 * DK, nv, tid, nt);
-    if (KV) stage<DV>(v, reinterpret_cast<const T*>(p.v) + row0 * DV, nv, tid, nt);
-    if (QO) stage<DV>(o, reinterpret_cast<const T*>(p.dout) + row0 * DV, nv, tid, nt);
-    // every level slot is written: rows past nv and levels past L read as zero weights
-    if (LAM)
-      for (int i = tid; i < C * kLamCap; i += nt) {
-        const int r = i / kLamCap, l = i % kLamCap;
-        lam[i] = (r < nv && l < p.L) ? lambda_at(p, (row0 + r) * p.L + l) : 0.f;
-      }
-    // chunk-local inclusive prefix of log_a by wave 0: each lane holds E consecutive rows
-    if (tid < 64) {
-      constexpr int E = C > 64 ? C / 64 : 1;
-      float x[E], run = 0.f;
+  template <int NT, bool KV = true, bool QO = true, bool LAM = true>
+  struct Staged {
+    static_assert(C <= 64, "one lane per position in the log_a scan");
+    static constexpr int PL = (C * kLamCap + NT - 1) / NT;
+    Rows<DK, NT> rq, rk;
+    Rows<DV, NT> rv, ro;
+    unsigned lm[LAM ? PL : 1];   // lambda: float32 bits, or bfloat16 bits in the low half
+    float la;
+    int nv, L, bf;
+
+    __device__ __forceinline__ void fetch(const BwdParams& p, int bh, int c, int nv_, int tid) {
+      nv = nv_;
+      L = p.L;
+      bf = p.lam_bf16;
+      const size_t row0 = (size_t)bh * p.T + (size_t)c * C;
+      // lambda first: its two kinds of loads sit in the two arms of a branch, and a wait the
+      // compiler puts at the start of one arm then has nothing else to drain
+      if (LAM) {
+        const size_t base = row0 * p.L;
+        if (bf) {
+          const unsigned short* lp = reinterpret_cast<const unsigned short*>(p.lam) + base;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int r = tid * E + e;
-        x[e] = (r < C && r < nv) ? p.log_a[row0 + r] : 0.f;
-        run += x[e];
-        x[e] = run;
-      }
-      float incl = run;
+          for (int u = 0; u < PL; ++u) {
+            const int i = min(tid + u * NT, C * kLamCap - 1);
+            lm[u] = lp[(size_t)min(i / kLamCap, nv - 1) * p.L + min(i % kLamCap, p.L - 1)];
+          }
+        } else {
+          const unsigned* lp = reinterpret_cast<const unsigned*>(p.lam) + base;
 #pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const float y = __shfl_up(incl, d);
-        if (tid >= d) incl += y;
+          for (int u = 0; u < PL; ++u) {
+            const int i = min(tid + u * NT, C * kLamCap - 1);
+            lm[u] = lp[(size_t)min(i / kLamCap, nv - 1) * p.L + min(i % kLamCap, p.L - 1)];
+          }
+        }
       }
-      const float excl = incl - run;
-      const float tot = __shfl(incl, 63);
+      la = p.log_a[row0 + min(tid, nv - 1)];
+      if (QO) rq.fetch(reinterpret_cast<const T*>(p.q) + row0 * DK, nv, tid);
+      if (KV) rk.fetch(reinterpret_cast<const T*>(p.k) + row0 * DK, nv, tid);
+      if (KV) rv.fetch(reinterpret_cast<const T*>(p.v) + row0 * DV, nv, tid);
+      if (QO) ro.fetch(reinterpret_cast<const T*>(p.dout) + row0 * DV, nv, tid);
+    }
+
+    __device__ __forceinline__ void put(Chunk& ch, int tid) const {
+      if (QO) rq.put(ch.q, nv, tid);
+      if (KV) rk.put(ch.k, nv, tid);
+      if (KV) rv.put(ch.v, nv, tid);
+      if (QO) ro.put(ch.o, nv, tid);
+      // every level slot is written: rows past nv and levels past L are zero weights
+      if (LAM)
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int r = tid * E + e;
-        if (r < C) {
-          const float a = excl + x[e];
-          al[r] = a;
-          ea[r] = __expf(a);
-          ws[r] = __expf(tot - a);
+        for (int u = 0; u < PL; ++u) {
+          const int i = tid + u * NT;
+          const float x = __builtin_bit_cast(float, bf ? lm[u] << 16 : lm[u]);
+          if (i < C * kLamCap) ch.lam[i] = (i / kLamCap < nv && i % kLamCap < L) ? x : 0.f;
+        }
+      if (tid < 64) {
+        float incl = (tid < C && tid < nv) ? la : 0.f;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const float y = __shfl_up(incl, d);
+          if (tid >= d) incl += y;
+        }
+        const float tot = __shfl(incl, 63);
+        if (tid < C) {
+          ch.al[tid] = incl;
+          ch.ea[tid] = __expf(incl);
+          ch.ws[tid] = __expf(tot - incl);
         }
       }
     }
+  };
+
+  // after put() and a barrier: the chunk's total log decay
+  __device__ __forceinline__ void finish() { g = al[C - 1]; }
+
+  // fetch, put, barrier
+  template <int NT, bool KV = true, bool QO = true, bool LAM = true>
+  __device__ void load(const BwdParams& p, int bh, int c, int nv, int tid) {
+    Staged<NT, KV, QO, LAM> st;
+    st.fetch(p, bh, c, nv, tid);
+    st.put(*this, tid);
     __syncthreads();
-    g = al[C - 1];
+    finish();
   }
 };
 
@@ -402,7 +459,7 @@ bwd_states_kernel(BwdParams p) {
   const BwdSmem Lo = bwd_smem((int)sizeof(T), C, DK, DV, false);
   CH ch;
   ch.bind(sm, Lo);
-  ch.template load<true, false, false>(p, bh, c, nv, tid, NT);
+  ch.template load<NT, true, false, false>(p, bh, c, nv, tid);
   const size_t SZ = (size_t)DK * DV;
   // F(c): keys weighted by their decay to the chunk's end
   outer_store<T, C, DK, DV, NW>(ch.k, CH::RK, ch.v, CH::RV, ch.ws,
@@ -534,14 +591,25 @@ bwd_rn_kernel(BwdParams p) {
 // bwd_grads: all gradients of one chunk
 // ----------------------------------------------------------------------------------------
 
-// a [DK][DV] state stored in the element type T into a shared image (row stride RV), in 16-byte
-// pieces
-template <typename T, int DK, int DV, int RV>
-__device__ __forceinline__ void stage_state(T* img, const T* __restrict__ g, int tid, int nt) {
-  constexpr int EPV = 16 / (int)sizeof(T), NP = DK * DV / EPV;
-  for (int idx = tid; idx < NP; idx += nt) {
+// one or two [DK][DV] states stored in the element type T into shared images (row stride RV), in
+// 16-byte pieces; every load is issued before any shared-memory write
+template <typename T, int DK, int DV, int RV, int NT, bool TWO = false>
+__device__ __forceinline__ void stage_state(T* img, const T* __restrict__ g, int tid, T* img2 = nullptr,
+                                            const T* __restrict__ g2 = nullptr) {
+  constexpr int EPV = 16 / (int)sizeof(T), NP = DK * DV / EPV, PER = (NP + NT - 1) / NT;
+  u32x4 r[PER], r2[TWO ? PER : 1];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int idx = tid + u * NT;
+    if (idx < NP) r[u] = reinterpret_cast<const u32x4*>(g)[idx];
+    if (TWO && idx < NP) r2[u] = reinterpret_cast<const u32x4*>(g2)[idx];
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int idx = tid + u * NT;
     const int a = (idx * EPV) / DV, b = (idx * EPV) % DV;
-    *reinterpret_cast<u32x4*>(img + a * RV + b) = reinterpret_cast<const u32x4*>(g)[idx];
+    if (idx < NP) *reinterpret_cast<u32x4*>(img + a * RV + b) = r[u];
+    if (TWO && idx < NP) *reinterpret_cast<u32x4*>(img2 + a * RV + b) = r2[u];
   }
 }
 
@@ -551,15 +619,14 @@ __device__ __forceinline__ void stage_state(T* img, const T* __restrict__ g, int
 template <int DK, int DV>
 constexpr int grads_waves_per_eu() { return DK * DV <= 64 * 64 ? 2 : 1; }
 
-template <typename T, int C, int DK, int DV>
-__global__ void __launch_bounds__(64 * Waves<C>::NW)
-__attribute__((amdgpu_waves_per_eu(grads_waves_per_eu<DK, DV>())))
-bwd_grads_kernel(BwdParams p) {
+// LATER: the head has more than one chunk (p.nl > 0), so there are later chunks and Fenwick
+// nodes; the body is compiled once for each case so that none of its loads sits under a branch
+template <typename T, int C, int DK, int DV, bool LATER>
+__device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm) {
   constexpr int NW = Waves<C>::NW, RB = Waves<C>::RB, NT = 64 * NW, J = ilog2(C);
   constexpr int ES = (int)sizeof(T), RC = C + 16 / ES;
   constexpr int NK = DK / 16, NV = DV / 16;
   using CH = Chunk<T, C, DK, DV>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
   // workgroups go to the 8 XCDs in turn: with B*H a multiple of 8, XCD x gets heads x, x + 8, ...
   // chunk after chunk, so the Fenwick nodes that consecutive chunks share stay in its L2
   const int L = blockIdx.x;
@@ -580,7 +647,7 @@ bwd_grads_kernel(BwdParams p) {
   const size_t row0 = (size_t)bh * p.T + (size_t)c * C;
   // the combined right-sibling state, written by the down-sweep (zero for the last chunk);
   // its loads are issued with the chunk's
-  const bool later = p.nl > 0;
+  constexpr bool later = LATER;
   // bf16: the cross-chunk states are read as hi + lo (two bf16 MFMAs per read-out), so that
   // their rounding, shared by every position that reads a state, stays far below the inputs'
   constexpr bool SPLIT = ES == 2;
@@ -588,15 +655,20 @@ bwd_grads_kernel(BwdParams p) {
   const T* node_e = reinterpret_cast<const T*>(p.node_e) + (size_t)bh * p.nslot * SZ;
   const T* node_lo = reinterpret_cast<const T*>(p.node_lo) + (size_t)bh * p.nslot * SZ;
   const T* u_lo = reinterpret_cast<const T*>(p.u_lo) + ((size_t)bh * p.N + c) * SZ;
-  if (later)
-    stage_state<T, DK, DV, CH::RV>(Ust, reinterpret_cast<const T*>(p.u_e) + ((size_t)bh * p.N + c) * SZ, tid, NT);
-  // the first node of step 4 (and U's low part) are prefetched into registers now
+  const T* u_e = reinterpret_cast<const T*>(p.u_e) + ((size_t)bh * p.N + c) * SZ;
+  // the chunk's loads are issued first, then the combined right-sibling state's and the first
+  // node of step 4 (prefetched into registers), and only then is anything written to shared
+  // memory: one memory round trip for all of it
+  typename CH::template Staged<NT> st;
+  st.fetch(p, bh, c, nv, tid);
   constexpr int EPV = 16 / ES;
   constexpr int NPF = DK * DV / EPV / NT;
   constexpr bool PF = NPF >= 1 && NPF <= 4 && NPF * NT * EPV == DK * DV;
   u32x4 pf[PF ? NPF : 1], pf2[PF && SPLIT ? NPF : 1];
+  // jl past the last set bit (nothing left to read) loads a valid slot that is never used
   auto prefetch = [&](int jl) {
-    const size_t off = (size_t)slot_of(p.N, jl, (c >> jl) - 1) * SZ;
+    if (jl >= p.nl) jl = 0;
+    const size_t off = (size_t)slot_of(p.N, jl, max((c >> jl) - 1, 0)) * SZ;
     const u32x4* src = reinterpret_cast<const u32x4*>(node_e + off);
     const u32x4* src2 = reinterpret_cast<const u32x4*>(node_lo + off);
 #pragma unroll
@@ -613,14 +685,23 @@ bwd_grads_kernel(BwdParams p) {
       *reinterpret_cast<u32x4*>(img + a * CH::RV + b) = r[u];
     }
   };
-  u32x4 ulo[PF && SPLIT ? NPF : 1];
+  u32x4 uhi[PF ? NPF : 1], ulo[PF && SPLIT ? NPF : 1];
+  if (PF && later)
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) uhi[u] = reinterpret_cast<const u32x4*>(u_e)[tid + u * NT];
   if (PF && SPLIT && later)
 #pragma unroll
     for (int u = 0; u < NPF; ++u) ulo[u] = reinterpret_cast<const u32x4*>(u_lo)[tid + u * NT];
   int first_set = 0;
   while (first_set < p.nl && !((c >> first_set) & 1)) ++first_set;
-  if (PF && first_set < p.nl) prefetch(first_set);
-  ch.load(p, bh, c, nv, tid, NT);
+  if (PF && later) prefetch(first_set);
+  st.put(ch, tid);
+  if (later) {
+    if constexpr (PF) put(Ust, uhi);
+    else stage_state<T, DK, DV, CH::RV, NT>(Ust, u_e, tid);
+  }
+  __syncthreads();
+  ch.finish();
 
   // 1. masked score tiles: wave w takes 16-row blocks rb = w + NW*x of query positions i.
   //    dlambda of the levels inside the chunk is summed per (row, level) in registers: in a tile
@@ -729,7 +810,7 @@ bwd_grads_kernel(BwdParams p) {
   if (SPLIT && later) {
     __syncthreads();   // P2 is no longer read
     if constexpr (PF) put(Plo, ulo);
-    else stage_state<T, DK, DV, CH::RV>(Plo, u_lo, tid, NT);
+    else stage_state<T, DK, DV, CH::RV, NT>(Plo, u_lo, tid);
     __syncthreads();
   }
   if (later) {
@@ -771,7 +852,8 @@ bwd_grads_kernel(BwdParams p) {
 
   // 4. earlier chunks, query side: for each set bit j of c the node (j, (c>>j) - 1), decayed
   //    over the nodes of the lower set bits, staged into shared memory; Y = dO node^T gives dq
-  //    (weighted by lambda) and dlambda of level J+1+j (its row dot with q, written here).
+  //    (weighted by lambda) and dlambda of level J+1+j (its row dot with q, parked in that
+  //    level's slot of the lambda rows, which nothing reads again, and stored in step 6).
   //    When a node is at most 4 float4 per thread, the next node's loads are in flight in
   //    registers while the current one is used (the first one's since the kernel started).
   const float* gs = p.gsum + (size_t)bh * p.nslot;
@@ -786,10 +868,9 @@ bwd_grads_kernel(BwdParams p) {
       if constexpr (SPLIT) put(Plo, pf2);
       int nx = jl + 1;
       while (nx < p.nl && !((c >> nx) & 1)) ++nx;
-      if (nx < p.nl) prefetch(nx);
+      prefetch(nx);
     } else {
-      stage_state<T, DK, DV, CH::RV>(Nst, node_e + (size_t)sl * SZ, tid, NT);
-      if constexpr (SPLIT) stage_state<T, DK, DV, CH::RV>(Plo, node_lo + (size_t)sl * SZ, tid, NT);
+      stage_state<T, DK, DV, CH::RV, NT, SPLIT>(Nst, node_e + (size_t)sl * SZ, tid, Plo, node_lo + (size_t)sl * SZ);
     }
     __syncthreads();
     const float dj = __expf(dlow);
@@ -824,7 +905,7 @@ bwd_grads_kernel(BwdParams p) {
         const float sum = sum16(part[r]);
         const int i = rb * 16 + 4 * g4 + r;
         dq_dot[r] += scl[r] * sum;
-        if (jj == r && i < nv) p.glam[(row0 + i) * p.L + J + 1 + jl] = ch.ea[i] * dj * sum;
+        if (jj == r) ch.lam[i * kLamCap + J + 1 + jl] = ch.ea[i] * dj * sum;
       }
     }
     dlow += gs[sl];
@@ -882,8 +963,9 @@ bwd_grads_kernel(BwdParams p) {
       if (jj == r && i < nv) p.dA[row0 + i] = sum;
     }
 
-    // 6. dlambda of this block's rows: levels 0..J from the bins, zero for every level past J
-    //    that no node read-out of step 4 wrote (lane jj writes levels jj, jj + 16)
+    // 6. dlambda of this block's rows: levels 0..J from the bins, the levels of step 4's node
+    //    read-outs from where it parked them, zero for every other level (lane jj writes levels
+    //    jj, jj + 16)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = rb * 16 + 4 * g4 + r;
@@ -896,12 +978,21 @@ bwd_grads_kernel(BwdParams p) {
             if (q == l) val = bins[x][r][q];
         } else {
           const int jl = l - J - 1;
-          if (jl < p.nl && ((c >> jl) & 1)) continue;   // written in step 4
+          if (jl < p.nl && ((c >> jl) & 1)) val = ch.lam[i * kLamCap + l];
         }
         p.glam[(row0 + i) * p.L + l] = val;
       }
     }
   }
+}
+
+template <typename T, int C, int DK, int DV>
+__global__ void __launch_bounds__(64 * Waves<C>::NW)
+__attribute__((amdgpu_waves_per_eu(grads_waves_per_eu<DK, DV>())))
+bwd_grads_kernel(BwdParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
+  if (p.nl > 0) grads_body<T, C, DK, DV, true>(p, sm);
+  else grads_body<T, C, DK, DV, false>(p, sm);
 }
 
 }  // namespace bwd
