@@ -22,16 +22,18 @@
 // RN cannot be built from the blocks below it like a forward node: it is contracted from the
 // block's own q and do rows, level by level.
 //
-// Kernels, in stream order (bwd_gsum, bwd_tree and bwd_dloga, which do not depend on the element
-// type or the shapes, live in lla_bwd_api.hip):
+// Kernels, in stream order (bwd_gsum, bwd_gtree / bwd_tree and bwd_dloga, which do not depend on
+// the chunk or the head dims, live in lla_bwd_api.hip):
 //   bwd_states  (chunk, head): F(c) = sum_s exp(g_c - A_s) k_s v_s^T (tree slot (0, c)) and g_c;
 //   bwd_rn      (sub-block, head): the right blocks of level j split into sub-blocks of up to 8
 //               chunks; each sub-block's lambda-weighted, decayed q do^T on MFMA;
 //   bwd_gsum    (head): total log decay of every block (j, m), pairwise from the chunks;
-//   bwd_tree    (64 state elements, head): the forward up-sweep of the nodes, then a down-sweep
-//               that gives every chunk its combined right-sibling state; sums in fp32, and a copy
-//               in the element type of what the gradient kernel reads (it rounds its MFMA
-//               operands to that type in any case);
+//   bwd_gtree   (64 state elements, head): the forward up-sweep of the nodes, then a down-sweep
+//               that gives every chunk its combined right-sibling state; each wave owns groups
+//               of 8 chunks (tree levels 0..3 in registers), the levels above go through shared
+//               memory; sums in fp32, and a copy in the element type of what the gradient kernel
+//               reads (it rounds its MFMA operands to that type in any case). bwd_tree does the
+//               same level by level through the workspace, for trees too large for bwd_gtree;
 //   bwd_grads   (chunk, head): intra-chunk gradients on MFMA (masked S and W tiles, dlambda of
 //               the levels inside the chunk), node read-outs for dq and dlambda, the combined
 //               right-sibling state for dk and dv, dA;

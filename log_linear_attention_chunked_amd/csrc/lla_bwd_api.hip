@@ -1,6 +1,7 @@
 // lla_bwd_api.hip — C ABI of the backward pass: argument validation, plan (chunk, tree and
 // workspace layout) and the stream-ordered launch sequence bwd_states -> bwd_rn -> bwd_gsum ->
-// bwd_tree -> bwd_grads -> bwd_dloga. The contract is documented in include/loglinear_attn.h.
+// bwd_gtree (or bwd_tree) -> bwd_grads -> bwd_dloga. The contract is documented in
+// include/loglinear_attn.h.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -44,28 +45,17 @@ __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdParams p) {
 
 constexpr int kTreeWaves = 16;
 
-// LDS: every block value of the 64 elements, [slot][64] floats (up-sweep nodes, then the
-// down-sweep's values), when that fits; otherwise the up-sweep reads level i-1 back from the
-// node array and the down-sweep keeps every level in the outs array.
+// For trees too large for bwd_gtree's shared memory: the up-sweep reads level i-1 back from
+// the node array and the down-sweep keeps every level in the outs array.
 // E: the element type of the copies the gradient kernel reads (node_e, u_e)
-template <typename E, bool LDS>
-__global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, int SZ) {
-  extern __shared__ __attribute__((aligned(16))) float tl[];
+// at most 64 registers per lane: two workgroups of 16 waves share a compute unit (8 waves per SIMD)
+template <typename E>
+__global__ void __launch_bounds__(64 * kTreeWaves) __attribute__((amdgpu_waves_per_eu(8)))
+bwd_tree_kernel(BwdParams p, int SZ) {
   const int bh = blockIdx.y, lane = threadIdx.x & 63;
   const int e = blockIdx.x * 64 + lane, w = threadIdx.x >> 6;
   // the grid has exactly SZ / 64 columns of workgroups (SZ = dk*dv is a multiple of 64)
-  const float* __restrict__ gsg = p.gsum + (size_t)bh * p.nslot;
-  // on chip, the block decays sit after the block values: no level waits on a decay load
-  float* gsl = tl + (size_t)p.nslot * 64;
-  if (LDS)
-    for (int i = threadIdx.x; i < p.nslot; i += blockDim.x) gsl[i] = gsg[i];
-  const float* gs = LDS ? gsl : gsg;
-  // on chip the waves exchange values through shared memory only: the barrier then waits for
-  // shared-memory accesses alone, and the loads issued ahead for the next level stay in flight
-  auto bar = [&]() {
-    if (LDS) lds_barrier();
-    else __syncthreads();
-  };
+  const float* __restrict__ gs = p.gsum + (size_t)bh * p.nslot;
   float* __restrict__ nd = p.node + (size_t)bh * p.nslot * SZ + e;
   const float* __restrict__ rp = p.rnp + (size_t)bh * p.items * SZ + e;
   float* __restrict__ ou = p.outs + (size_t)bh * p.nslot * SZ + e;
@@ -80,50 +70,91 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
     hi[at] = h;
     if (SPLIT) lo[at] = (E)(x - (float)h);
   };
-  for (int m = w; m < p.N; m += kTreeWaves) {
-    const float x = nd[(size_t)m * SZ];
-    // the gradient kernel reads node (j, (c >> j) - 1) for set bits j of c: even nodes only
-    if (!(m & 1)) put(ne, nlo, (size_t)m * SZ, x);
-    if (LDS) tl[m * 64 + lane] = x;
+  // level 0, KB chunks of a wave at a time: all their loads (unconditional, clamped to the last
+  // chunk) are issued before any value is used, so a batch costs one memory round trip
+  constexpr int KB = 8;
+  for (int m0 = w; m0 < p.N; m0 += kTreeWaves * KB) {
+    float x[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) x[u] = nd[(size_t)min(m0 + u * kTreeWaves, p.N - 1) * SZ];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int m = m0 + u * kTreeWaves;
+      if (m >= p.N) break;
+      // the gradient kernel reads node (j, (c >> j) - 1) for set bits j of c: even nodes only
+      if (!(m & 1)) put(ne, nlo, (size_t)m * SZ, x[u]);
+    }
   }
-  bar();
+  __syncthreads();
   for (int i = 1; i < p.nl; ++i) {
     const int nprev = (p.N + (1 << (i - 1)) - 1) >> (i - 1), nb = (p.N + (1 << i) - 1) >> i;
     const int o_prev = slot_of(p.N, i - 1, 0), o = slot_of(p.N, i, 0);
-    for (int m = w; m < nb; m += kTreeWaves) {
-      const bool right = 2 * m + 1 < nprev;
-      const int sl = o_prev + 2 * m;
-      const float lhs = LDS ? tl[sl * 64 + lane] : nd[(size_t)sl * SZ];
-      const float rhs = right ? (LDS ? tl[(sl + 1) * 64 + lane] : nd[(size_t)(sl + 1) * SZ]) : 0.f;
-      const float gr = right ? gs[sl + 1] : 0.f;
-      const float val = right ? __expf(gr) * lhs + rhs : lhs;
-      if (!(m & 1)) put(ne, nlo, (size_t)(o + m) * SZ, val);
-      if (LDS) tl[(o + m) * 64 + lane] = val;
-      else nd[(size_t)(o + m) * SZ] = val;
+    for (int m0 = w; m0 < nb; m0 += kTreeWaves * KB) {
+      // both children of KB blocks (clamped to valid slots of level i-1) before any is used
+      float lhs[KB], rhs[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int sl = o_prev + min(2 * (m0 + u * kTreeWaves), nprev - 1);
+        const int sr = o_prev + min(2 * (m0 + u * kTreeWaves) + 1, nprev - 1);
+        lhs[u] = nd[(size_t)sl * SZ];
+        rhs[u] = nd[(size_t)sr * SZ];
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int m = m0 + u * kTreeWaves;
+        if (m >= nb) break;
+        const bool right = 2 * m + 1 < nprev;
+        const float val = right ? __expf(gs[o_prev + 2 * m + 1]) * lhs[u] + rhs[u] : lhs[u];
+        if (!(m & 1)) put(ne, nlo, (size_t)(o + m) * SZ, val);
+        nd[(size_t)(o + m) * SZ] = val;
+      }
     }
-    bar();
+    __syncthreads();
   }
   // down-sweep; a wave takes KB of its blocks at a time and loads all their right-block states
   // before it uses any of them; the first KB of the next level are loaded while this level is
-  // worked on (they depend on nothing the sweep writes)
-  constexpr int KB = 8;
+  // worked on (they depend on nothing the sweep writes). Every load is unconditional from a
+  // clamped, valid item (a block with no right sibling multiplies it by zero), so the counted
+  // waits stay exact; a right block of several sub-blocks (levels past kSubLog) is summed KB
+  // sub-blocks at a time, their loads again issued together.
   auto fetch = [&](int i, int m0, float (&rn)[KB]) {
     const int nb = (p.N + (1 << i) - 1) >> i;
     const int s = sub_log(i), b = i - s, os = slot_of(p.N, s, 0);
     const int nsub = (p.N + (1 << s) - 1) >> s;
+    const int nit = items_of_level(p.N, i);
+    const float* rpl = rp + (size_t)p.rn_off[i] * SZ;
+    if (b == 0) {   // one sub-block per right block
+      float x[KB];
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int m = m0 + u * kTreeWaves;
+        // an odd block has no right sibling: every such lane reads item 0
+        x[u] = rpl[(m & 1) ? 0 : (size_t)min(item_of_sub(i, min(m + 1, nsub - 1)), nit - 1) * SZ];
+      }
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int m = m0 + u * kTreeWaves;
+        rn[u] = (m < nb && !(m & 1) && m + 1 < nb) ? x[u] : 0.f;
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < KB; ++u) {
       const int m = m0 + u * kTreeWaves;
       rn[u] = 0.f;
       if (m < nb && !(m & 1) && m + 1 < nb) {
         const int sb0 = (m + 1) << b, sb1 = min((m + 2) << b, nsub);
-        if (sb1 - sb0 == 1) {
-          rn[u] = rp[(size_t)(p.rn_off[i] + item_of_sub(i, sb0)) * SZ];
-        } else {
-          float dec = 0.f;
-          for (int sb = sb0; sb < sb1; ++sb) {
-            rn[u] += __expf(dec) * rp[(size_t)(p.rn_off[i] + item_of_sub(i, sb)) * SZ];
-            dec += gs[os + sb];
+        float dec = 0.f;
+        for (int t0 = sb0; t0 < sb1; t0 += KB) {
+          float x[KB];
+#pragma unroll
+          for (int e = 0; e < KB; ++e) x[e] = rpl[(size_t)item_of_sub(i, min(t0 + e, sb1 - 1)) * SZ];
+#pragma unroll
+          for (int e = 0; e < KB; ++e) {
+            if (t0 + e < sb1) {
+              rn[u] += __expf(dec) * x[e];
+              dec += gs[os + t0 + e];
+            }
           }
         }
       }
@@ -148,21 +179,253 @@ __global__ void __launch_bounds__(64 * kTreeWaves) bwd_tree_kernel(BwdParams p, 
       } else {
         fetch(i, m0, rn);
       }
+      // the parents' values (level i+1, clamped to its valid slots) before any is used
+      float par[KB];
+      const int npar = (p.N + (2 << i) - 1) >> (i + 1);
+#pragma unroll
+      for (int u = 0; u < KB; ++u) {
+        const int ps = op + min((m0 + u * kTreeWaves) >> 1, npar - 1);
+        par[u] = top ? 0.f : ou[(size_t)ps * SZ];
+      }
 #pragma unroll
       for (int u = 0; u < KB; ++u) {
         const int m = m0 + u * kTreeWaves;
         if (m >= nb) break;
-        const int ps = op + (m >> 1);
-        const float par = top ? 0.f : (LDS ? tl[ps * 64 + lane] : ou[(size_t)ps * SZ]);
-        const float val = (!(m & 1) && m + 1 < nb) ? __expf(gs[o + m + 1]) * par + rn[u] : par;
-        // the level-i slots of tl held nodes that are no longer read: level i+1 was read above,
-        // and the up-sweep is over
-        if (LDS) tl[(o + m) * 64 + lane] = val;
-        else ou[(size_t)(o + m) * SZ] = val;
+        const float val = (!(m & 1) && m + 1 < nb) ? __expf(gs[o + m + 1]) * par[u] + rn[u] : par[u];
+        ou[(size_t)(o + m) * SZ] = val;
         if (i == 0) put(ue, ulo, (size_t)m * SZ, val);
       }
     }
-    bar();
+    __syncthreads();
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// bwd_gtree: the same tree, with each wave owning groups of 8 consecutive chunks (bwd_rn's
+// sub-blocks). Levels 0..3 of a group (its chunks, pairs, quads and the group itself) are
+// combined in registers, up and down; only the levels above, over groups, go through shared
+// memory. A right block of several groups (level i >= 4) receives, from each of its groups g,
+// the contribution exp(decay from the block's start to g's start) * P(i, g) (P: bwd_rn's
+// sub-block state), written to shared memory by g's wave and summed in group order by the wave
+// that needs it. Every global load a workgroup makes (the groups' chunk states, their right
+// blocks' states, the contributions and the block decays) is issued before the first wait when
+// a wave owns one group, so the whole tree costs about one memory round trip.
+// Shared memory (floats): the block decays; per level i >= 3 (below nl) the block values (64
+// floats each, up-sweep values later overwritten by the down-sweep's); per level i >= 4 the
+// contributions, one per right-block group (item order of bwd_rn).
+// ----------------------------------------------------------------------------------------
+
+constexpr int kGrpLog = 3;            // 8 chunks per group
+static_assert(kGrpLog == kSubLog, "a group is one of bwd_rn's sub-blocks");
+constexpr int kGtCt = 6;              // levels >= 4 whose contributions a wave prefetches
+
+// a wave-uniform global address as the compiler's uniform value (both halves read from lane 0;
+// global address space): an access at it plus a lane offset then takes the scalar-base form
+// instead of a 64-bit address per lane
+template <typename P>
+__device__ __forceinline__ __attribute__((address_space(1))) P* uniform_ptr(P* ptr) {
+  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (__attribute__((address_space(1))) P*)(((uint64_t)hi << 32) | lo);
+}
+
+// first float of level i's block values (3 <= i <= nl) and of level i's contributions
+// (4 <= i <= nl; i = nl gives the total), after the nslot block decays
+__host__ __device__ inline int gtree_lv(int N, int nslot, int i) {
+  int off = (nslot + 63) & ~63;
+  for (int a = 3; a < i; ++a) off += ((N + (1 << a) - 1) >> a) * 64;
+  return off;
+}
+__host__ __device__ inline int gtree_ct(int N, int nl, int nslot, int i) {
+  int off = gtree_lv(N, nslot, nl > 3 ? nl : 3);
+  for (int a = 4; a < i; ++a) off += items_of_level(N, a) * 64;
+  return off;
+}
+__host__ __device__ inline int gtree_floats(int N, int nl, int nslot) {
+  return gtree_ct(N, nl, nslot, nl > 4 ? nl : 4);
+}
+
+template <typename E>
+__global__ void __launch_bounds__(64 * kTreeWaves) __attribute__((amdgpu_waves_per_eu(8)))
+bwd_gtree_kernel(BwdParams p, int SZ) {
+  extern __shared__ __attribute__((aligned(16))) float tl[];
+  // the wave index is uniform (read from lane 0), so every group and block index below is, and
+  // each access is a uniform base plus the lane's 4 (or 2) bytes
+  const int bh = blockIdx.y, lane = threadIdx.x & 63;
+  const unsigned ul = threadIdx.x & 63;   // the lane as an unsigned (zero-extended) offset
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int e0 = blockIdx.x * 64;
+  const int N = p.N, nl = p.nl, ng = (N + 7) >> kGrpLog;
+  const float* __restrict__ gsg = p.gsum + (size_t)bh * p.nslot;
+  float* gs = tl;                        // block decays first
+  const float* __restrict__ nd = p.node + (size_t)bh * p.nslot * SZ + e0;
+  const float* __restrict__ rp = p.rnp + (size_t)bh * p.items * SZ + e0;
+  E* __restrict__ ne = reinterpret_cast<E*>(p.node_e) + (size_t)bh * p.nslot * SZ + e0;
+  E* __restrict__ ue = reinterpret_cast<E*>(p.u_e) + (size_t)bh * N * SZ + e0;
+  constexpr bool SPLIT = sizeof(E) == 2;
+  E* __restrict__ nlo = reinterpret_cast<E*>(p.node_lo) + (size_t)bh * p.nslot * SZ + e0;
+  E* __restrict__ ulo = reinterpret_cast<E*>(p.u_lo) + (size_t)bh * N * SZ + e0;
+  auto put = [&](E* hi, E* lo, size_t at, float x) {
+    const E h = (E)x;
+    uniform_ptr(hi + at)[ul] = h;
+    if (SPLIT) uniform_ptr(lo + at)[ul] = (E)(x - (float)h);
+  };
+  // element `lane` of the state in slot i of a region
+  auto ld = [&](const float* base, int i) { return uniform_ptr(base + (size_t)i * SZ)[ul]; };
+  auto nb = [&](int i) { return (N + (1 << i) - 1) >> i; };
+  // item index of right block sb at level i, or item 0 (read, then multiplied by nothing) when
+  // there is none
+  auto item = [&](int i, int sb, bool ok) {
+    return ok ? p.rn_off[i] + item_of_sub(i, sb) : 0;
+  };
+
+  // one group's loads: its chunk states (zero past N), the right-block states of levels 0..3
+  // inside it, and its contributions to right blocks of levels 4 .. 3 + kGtCt
+  struct GLoads {
+    float x[8], r0[4], r1[2], r2, r3, ct[kGtCt];
+  };
+  auto load_group = [&](int g, GLoads& d) {
+    const int c0 = g << kGrpLog;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) d.x[k] = ld(nd, min(c0 + k, N - 1));
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int sb = c0 + 2 * h + 1;                       // level 0: chunk 2h+1 of the group
+      d.r0[h] = ld(rp, item(0, sb, 0 < nl && sb < N));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int sb = 4 * g + 2 * h + 1;
+      d.r1[h] = ld(rp, item(1, sb, 1 < nl && sb < nb(1)));
+    }
+    d.r2 = ld(rp, item(2, 2 * g + 1, 2 < nl && 2 * g + 1 < nb(2)));
+    d.r3 = ld(rp, item(3, g + 1, 3 < nl && !(g & 1) && g + 1 < ng));
+#pragma unroll
+    for (int u = 0; u < kGtCt; ++u) {
+      const int i = 4 + u;
+      d.ct[u] = ld(rp, item(i, g, i < nl && ((g >> (i - 3)) & 1)));
+    }
+  };
+
+  // the decays go to shared memory first (one value per thread for up to 1024 blocks, the rest,
+  // for larger trees, in a loop afterwards); the first group's loads are issued beside them
+  const float gv = gsg[min((int)threadIdx.x, p.nslot - 1)];
+  GLoads first;
+  if (w < ng) load_group(w, first);
+  if ((int)threadIdx.x < p.nslot) gs[threadIdx.x] = gv;
+  for (int i = threadIdx.x + 64 * kTreeWaves; i < p.nslot; i += 64 * kTreeWaves) gs[i] = gsg[i];
+  __syncthreads();
+  // decay of block m at level i (0 where the block does not exist: it then holds zeros)
+  auto G = [&](int i, int m) { return (i < nl && m < nb(i)) ? gs[slot_of(N, i, m)] : 0.f; };
+
+  // up-sweep inside a group, contributions, and the group's value at level 3
+  auto up_group = [&](int g, const GLoads& d) {
+    const int c0 = g << kGrpLog;
+    float x[8], y1[4], y2[2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = c0 + k < N ? d.x[k] : 0.f;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) y1[h] = __expf(G(0, c0 + 2 * h + 1)) * x[2 * h] + x[2 * h + 1];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) y2[h] = __expf(G(1, 4 * g + 2 * h + 1)) * y1[2 * h] + y1[2 * h + 1];
+    const float y3 = __expf(G(2, 2 * g + 1)) * y2[0] + y2[1];
+    // the gradient kernel reads node (j, (c >> j) - 1) for set bits j of c: even nodes only
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      if (0 < nl && c0 + 2 * h < N) put(ne, nlo, (size_t)(c0 + 2 * h) * SZ, x[2 * h]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (1 < nl && 4 * g + 2 * h < nb(1)) put(ne, nlo, (size_t)slot_of(N, 1, 4 * g + 2 * h) * SZ, y1[2 * h]);
+    if (2 < nl && 2 * g < nb(2)) put(ne, nlo, (size_t)slot_of(N, 2, 2 * g) * SZ, y2[0]);
+    if (3 < nl) {
+      if (!(g & 1)) put(ne, nlo, (size_t)slot_of(N, 3, g) * SZ, y3);
+      tl[gtree_lv(N, p.nslot, 3) + g * 64 + lane] = y3;
+    }
+  };
+  // contributions of a group to the right blocks above level 3 that hold it
+  auto contribute = [&](int g, const GLoads& d) {
+#pragma unroll
+    for (int u = 0; u < kGtCt; ++u) {
+      const int i = 4 + u;
+      if (i < nl && ((g >> (i - 3)) & 1)) {
+        float dec = 0.f;
+        for (int g2 = (g >> (i - 3)) << (i - 3); g2 < g; ++g2) dec += gs[slot_of(N, 3, g2)];
+        tl[gtree_ct(N, nl, p.nslot, i) + item_of_sub(i, g) * 64 + lane] = __expf(dec) * d.ct[u];
+      }
+    }
+  };
+  for (int g = w; g < ng; g += kTreeWaves) {
+    if (g == w) {
+      contribute(g, first);
+      up_group(g, first);
+    } else {
+      GLoads d;
+      load_group(g, d);
+      contribute(g, d);
+      up_group(g, d);
+    }
+  }
+  __syncthreads();
+
+  // levels >= 4, up: block values from the level below
+  for (int i = 4; i < nl; ++i) {
+    for (int m = w; m < nb(i); m += kTreeWaves) {
+      const float* lo = tl + gtree_lv(N, p.nslot, i - 1) + 2 * m * 64 + lane;
+      const bool right = 2 * m + 1 < nb(i - 1);
+      const float v = right ? __expf(G(i - 1, 2 * m + 1)) * lo[0] + lo[64] : lo[0];
+      tl[gtree_lv(N, p.nslot, i) + m * 64 + lane] = v;
+      if (!(m & 1)) put(ne, nlo, (size_t)slot_of(N, i, m) * SZ, v);
+    }
+    __syncthreads();
+  }
+  // levels >= 4, down (each block's value replaces its up-sweep value): what the block's
+  // chunks receive from later blocks at its level and above, decayed to the block's end
+  for (int i = nl - 1; i >= 4; --i) {
+    for (int m = w; m < nb(i); m += kTreeWaves) {
+      const float par = i + 1 < nl ? tl[gtree_lv(N, p.nslot, i + 1) + (m >> 1) * 64 + lane] : 0.f;
+      float v = par;
+      if (!(m & 1) && m + 1 < nb(i)) {
+        float rn = 0.f;
+        const int g0 = (m + 1) << (i - 3), g1 = min((m + 2) << (i - 3), ng);
+        const float* ct = tl + gtree_ct(N, nl, p.nslot, i) + lane;
+        for (int g2 = g0; g2 < g1; ++g2) rn += ct[item_of_sub(i, g2) * 64];
+        v = __expf(G(i, m + 1)) * par + rn;
+      }
+      tl[gtree_lv(N, p.nslot, i) + m * 64 + lane] = v;
+    }
+    __syncthreads();
+  }
+  // levels 3..0 of each group, down; the chunks' combined right-sibling states
+  auto down_group = [&](int g, const GLoads& d) {
+    const int c0 = g << kGrpLog;
+    const float par3 = 4 < nl ? tl[gtree_lv(N, p.nslot, 4) + (g >> 1) * 64 + lane] : 0.f;
+    const float d3 = (3 < nl && !(g & 1) && g + 1 < ng) ? __expf(G(3, g + 1)) * par3 + d.r3 : par3;
+    float d2[2], d1[4];
+    d2[0] = (2 < nl && 2 * g + 1 < nb(2)) ? __expf(G(2, 2 * g + 1)) * d3 + d.r2 : d3;
+    d2[1] = d3;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = 4 * g + 2 * h;
+      d1[2 * h] = (1 < nl && m + 1 < nb(1)) ? __expf(G(1, m + 1)) * d2[h] + d.r1[h] : d2[h];
+      d1[2 * h + 1] = d2[h];
+    }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int c = c0 + 2 * h;
+      const float d0 = (0 < nl && c + 1 < N) ? __expf(G(0, c + 1)) * d1[h] + d.r0[h] : d1[h];
+      if (c < N) put(ue, ulo, (size_t)c * SZ, d0);
+      if (c + 1 < N) put(ue, ulo, (size_t)(c + 1) * SZ, d1[h]);
+    }
+  };
+  for (int g = w; g < ng; g += kTreeWaves) {
+    if (g == w) {
+      down_group(g, first);
+    } else {
+      GLoads d;
+      load_group(g, d);
+      down_group(g, d);
+    }
   }
 }
 
@@ -213,7 +476,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int kLdsPerWorkgroup = 160 * 1024;
 
 struct BwdPlan {
-  int C, N, nl, nslot, L, esize, smem_states, smem_grads, tree_smem;
+  int C, N, nl, nslot, L, esize, smem_states, smem_grads;
+  int gtree_smem;   // > 0: the group tree (bwd_gtree) runs, with this much shared memory
   long BH;
   int items, rn_off[lla::kLamCap + 1];
   size_t off_node, off_gsum, off_rnp, off_outs, off_node_e, off_u_e, off_node_lo, off_u_lo, off_dA, ws_bytes;
@@ -281,8 +545,14 @@ int make_bwd_plan(int B, int H, int T, int dk, int dv, int chunk, int dtype, Bwd
   // the tree keeps its block values in shared memory when they fit: then the fp32 nodes above
   // level 0 and the down-sweep's values never reach memory (the node region is still laid out
   // per head with every slot; the outs region is not needed)
-  pl.tree_smem = (size_t)pl.nslot * 65 * 4 <= (size_t)kLdsPerWorkgroup ? pl.nslot * 65 * 4 : 0;
-  pl.off_outs = off; off = align256(off + (pl.tree_smem ? 0 : (size_t)BH * pl.nslot * SZ * 4));
+  // the group tree when its contributions are all prefetched (levels up to 3 + kGtCt) and its
+  // shared memory fits; otherwise the level-by-level tree
+  pl.gtree_smem = 0;
+  if (pl.nl > 0 && pl.nl <= 4 + lla::bwd::kGtCt) {
+    const size_t b = (size_t)lla::bwd::gtree_floats(pl.N, pl.nl, pl.nslot) * 4;
+    if (b <= (size_t)kLdsPerWorkgroup) pl.gtree_smem = (int)b;
+  }
+  pl.off_outs = off; off = align256(off + (pl.gtree_smem ? 0 : (size_t)BH * pl.nslot * SZ * 4));
   pl.off_node_e = off; off = align256(off + (size_t)BH * pl.nslot * SZ * pl.esize);
   pl.off_u_e = off;  off = align256(off + (pl.nl > 0 ? (size_t)BH * pl.N * SZ * pl.esize : 0));
   const bool split = dtype == LLA_DTYPE_BF16;   // bf16 copies keep their low parts
@@ -384,18 +654,18 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
     const int SZ = a.dk * a.dv;   // a multiple of 64: the tree grid covers it exactly
     const dim3 tgrid((unsigned)(SZ / 64), (unsigned)pl.BH), tblock(64 * lla::bwd::kTreeWaves);
     const bool bf = a.dtype == LLA_DTYPE_BF16;
-    if (pl.tree_smem > 0) {
-      const void* fn = bf ? reinterpret_cast<const void*>(&lla::bwd::bwd_tree_kernel<lla::bf16, true>)
-                          : reinterpret_cast<const void*>(&lla::bwd::bwd_tree_kernel<float, true>);
-      if (set_smem(fn, pl.tree_smem) != hipSuccess) return LLA_ERR_HIP;
+    if (pl.gtree_smem > 0) {
+      const void* fn = bf ? reinterpret_cast<const void*>(&lla::bwd::bwd_gtree_kernel<lla::bf16>)
+                          : reinterpret_cast<const void*>(&lla::bwd::bwd_gtree_kernel<float>);
+      if (set_smem(fn, pl.gtree_smem) != hipSuccess) return LLA_ERR_HIP;
       if (bf)
-        hipLaunchKernelGGL((lla::bwd::bwd_tree_kernel<lla::bf16, true>), tgrid, tblock, pl.tree_smem, stream, p, SZ);
+        hipLaunchKernelGGL((lla::bwd::bwd_gtree_kernel<lla::bf16>), tgrid, tblock, pl.gtree_smem, stream, p, SZ);
       else
-        hipLaunchKernelGGL((lla::bwd::bwd_tree_kernel<float, true>), tgrid, tblock, pl.tree_smem, stream, p, SZ);
+        hipLaunchKernelGGL((lla::bwd::bwd_gtree_kernel<float>), tgrid, tblock, pl.gtree_smem, stream, p, SZ);
     } else if (bf) {
-      hipLaunchKernelGGL((lla::bwd::bwd_tree_kernel<lla::bf16, false>), tgrid, tblock, 0, stream, p, SZ);
+      hipLaunchKernelGGL((lla::bwd::bwd_tree_kernel<lla::bf16>), tgrid, tblock, 0, stream, p, SZ);
     } else {
-      hipLaunchKernelGGL((lla::bwd::bwd_tree_kernel<float, false>), tgrid, tblock, 0, stream, p, SZ);
+      hipLaunchKernelGGL((lla::bwd::bwd_tree_kernel<float>), tgrid, tblock, 0, stream, p, SZ);
     }
     if (hipGetLastError() != hipSuccess) return LLA_ERR_HIP;
   }
