@@ -254,12 +254,21 @@ __device__ __forceinline__ Frag<T> frag_grow(const float* g, int RS, int r, int 
   return frag_from<T>(lo, hi);
 }
 
-// sum over 16 lanes of the same group (lane & 15 varies): xor shuffles inside the group
+// x from another lane of the same 16-lane row through a DPP move (the vector unit, not the
+// shared-memory permute that a generic shuffle compiles to): quad_perm patterns 0xB1 ([1,0,3,2])
+// and 0x4E ([2,3,0,1]); row_ror:4 = 0x124, row_ror:8 = 0x128
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// sum over the 16 lanes of a row (lane & 15 varies), in every lane: pairs, quads, then the
+// quads 4 and 8 lanes around the row
 __device__ __forceinline__ float sum16(float x) {
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x124>(x);
+  x += dpp_f<0x128>(x);
   return x;
 }
 
@@ -667,9 +676,10 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   constexpr int NPF = DK * DV / EPV / NT;
   constexpr bool PF = NPF >= 1 && NPF <= 4 && NPF * NT * EPV == DK * DV;
   u32x4 pf[PF ? NPF : 1], pf2[PF && SPLIT ? NPF : 1];
-  // jl past the last set bit (nothing left to read) loads a valid slot that is never used
-  auto prefetch = [&](int jl) {
-    if (jl >= p.nl) jl = 0;
+  // jl past the last set bit (nothing left to read) loads a valid slot that is never used: the
+  // node just read (cur, still in L2), or for chunk 0 (no node at all) slot 0
+  auto prefetch = [&](int jl, int cur) {
+    if (jl >= p.nl) jl = cur;
     const size_t off = (size_t)slot_of(p.N, jl, max((c >> jl) - 1, 0)) * SZ;
     const u32x4* src = reinterpret_cast<const u32x4*>(node_e + off);
     const u32x4* src2 = reinterpret_cast<const u32x4*>(node_lo + off);
@@ -696,7 +706,7 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
     for (int u = 0; u < NPF; ++u) ulo[u] = reinterpret_cast<const u32x4*>(u_lo)[tid + u * NT];
   int first_set = 0;
   while (first_set < p.nl && !((c >> first_set) & 1)) ++first_set;
-  if (PF && later) prefetch(first_set);
+  if (PF && later) prefetch(first_set, 0);
   st.put(ch, tid);
   if (later) {
     if constexpr (PF) put(Ust, uhi);
@@ -870,7 +880,7 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
       if constexpr (SPLIT) put(Plo, pf2);
       int nx = jl + 1;
       while (nx < p.nl && !((c >> nx) & 1)) ++nx;
-      prefetch(nx);
+      prefetch(nx, jl);
     } else {
       stage_state<T, DK, DV, CH::RV, NT, SPLIT>(Nst, node_e + (size_t)sl * SZ, tid, Plo, node_lo + (size_t)sl * SZ);
     }
