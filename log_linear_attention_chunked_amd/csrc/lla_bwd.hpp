@@ -276,6 +276,7 @@ __device__ __forceinline__ float sum16(float x) {
 struct BwdKernels {
   const void* states;   // bwd_states_kernel<T, C, DK, DV>
   const void* rn;       // bwd_rn_kernel<T, C, DK, DV>
+  const void* rng;      // bwd_rng_kernel<T, C, DK, DV> where its accumulators fit, else null
   const void* grads;    // bwd_grads_kernel<T, C, DK, DV>
 };
 
@@ -595,6 +596,260 @@ bwd_rn_kernel(BwdParams p) {
     for (int y = 0; y < NB; ++y)
 #pragma unroll
       for (int r = 0; r < 4; ++r) dst[(size_t)(ab * 16 + 4 * g4 + r) * DV + y * 16 + jj] = acc[x][y][r];
+  }
+}
+
+// ----------------------------------------------------------------------------------------
+// bwd_rng: the same sub-block states as bwd_rn, with one workgroup per group of 8 chunks (a
+// sub-block of every level >= 3) and head, chunk by chunk: the group's q and do rows are read
+// once, and every state its chunks belong to is accumulated at the same time. Slots 0..2: the
+// right blocks of levels 0, 1, 2 inside the group (a chunk takes part in level j when bit j of
+// its index is set; a block's state is stored when its last chunk is done and the slot starts
+// over); slots 3..: the group itself, for up to kRgHigh levels j >= 3 whose right blocks hold it
+// (bit j - 3 of the group index set), stored at the end; more such levels take another pass
+// over the group. The weights of a slot are lambda[t, J+1+j] exp(A_t - A_0), A_0 the prefix
+// decay just before the slot's block (the group's start for slots 3..).
+// ----------------------------------------------------------------------------------------
+
+// Tiles of a DK x DV product out[a][b] = sum_k A[k][a] B'[k][b] whose B' is a scaled (and, in
+// bf16, hi + lo split) operand: the waves split the b (column) dimension first, so that each
+// wave scales the columns it uses once per contraction step and reuses them for every a block
+// it holds (splitting a first would have every wave scale every column). Wave w holds YPW
+// column blocks y(w, ya) and, for each, APW row blocks ab(w, b) (possibly past DK / 16 when
+// there are more waves than tiles: such tiles are computed on zeros and not stored); tile
+// ya * APW + b of its accumulators.
+template <int DK, int DV, int NW>
+struct ScaledTiles {
+  static constexpr int NAT = DK / 16, NYT = DV / 16;
+  static constexpr bool BYCOL = NYT >= NW;                     // every wave its own columns
+  static constexpr int YPW = BYCOL ? NYT / NW : 1;
+  static constexpr int APW = BYCOL ? NAT : cdiv(NAT, NW / NYT);
+  static constexpr int TPW = YPW * APW;
+  __device__ static constexpr int y(int w, int ya) { return BYCOL ? w + NW * ya : w % NYT; }
+  __device__ static constexpr int ab(int w, int b) { return BYCOL ? b : w / NYT + (NW / NYT) * b; }
+  // the wave's tiles, row-major with row stride LD floats
+  template <int LD>
+  __device__ static void store(float* dst, const f32x4* acc, int w, int lane) {
+    const int jj = lane & 15, g4 = lane >> 4;
+#pragma unroll
+    for (int ya = 0; ya < YPW; ++ya)
+#pragma unroll
+      for (int b = 0; b < APW; ++b) {
+        const int a0 = ab(w, b);
+        if (a0 >= NAT) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          dst[(size_t)(a0 * 16 + 4 * g4 + r) * LD + y(w, ya) * 16 + jj] = acc[ya * APW + b][r];
+      }
+  }
+};
+
+// x (8 contraction elements as float, lo = first 4) times sc[0..7] as an MFMA operand pair
+// hi + lo: hi = x sc rounded to T, lo = the rounding error rounded to T (zero for float32)
+template <typename T>
+__device__ __forceinline__ void scale_split(const f32x4& ulo, const f32x4& uhi, const float* sc,
+                                            Frag<T>& hi, Frag<T>& lo) {
+  f32x4 xa, xb;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    xa[e] = ulo[e] * sc[e];
+    xb[e] = uhi[e] * sc[4 + e];
+  }
+  hi = frag_from<T>(xa, xb);
+  if constexpr (sizeof(T) == 2) {
+    f32x4 ha, hb;
+    frag_to_f32(hi, ha, hb);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xa[e] -= ha[e];
+      xb[e] -= hb[e];
+    }
+    lo = frag_from<T>(xa, xb);
+  } else {
+    lo = zero_frag<T>();
+  }
+}
+
+constexpr int kRgHigh = 4;
+
+// whether the 3 + kRgHigh accumulators of one wave fit its registers (at most 4 tiles each)
+template <int C, int DK, int DV>
+constexpr bool rng_fits() {
+  return ScaledTiles<DK, DV, Waves<C>::NW>::TPW <= 4;
+}
+
+template <typename T, int C, int DK, int DV>
+__global__ void __launch_bounds__(64 * Waves<C>::NW) __attribute__((amdgpu_waves_per_eu(2)))
+bwd_rng_kernel(BwdParams p) {
+  constexpr int NW = Waves<C>::NW, NT = 64 * NW, J = ilog2(C);
+  using TM = ScaledTiles<DK, DV, NW>;
+  constexpr int TPW = TM::TPW;
+  constexpr int ES = (int)sizeof(T), EPV = 16 / ES;
+  constexpr int PQ = C * DK / EPV, PO = C * DV / EPV;        // 16-byte pieces of the q, do rows
+  constexpr int NQ = cdiv(PQ, NT), NO = cdiv(PO, NT);
+  constexpr int NS = 3 + kRgHigh;                            // accumulator slots
+  static_assert(NS * C <= C * kLamCap, "slot weights fit the lambda rows");
+  using CH = Chunk<T, C, DK, DV>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
+  const int ng = (p.N + 7) >> 3;
+  // one-dimensional grid in XCD order, as in bwd_grads
+  const int Lw = blockIdx.x, q8 = Lw >> 3;
+  const bool xcd = (p.BH & 7) == 0;
+  const int g = xcd ? q8 % ng : Lw % ng;
+  const int bh = xcd ? ((q8 / ng) << 3) + (Lw & 7) : Lw / ng;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, jj = lane & 15, g4 = lane >> 4;
+  const int c0 = g << 3, c1 = min(c0 + 8, p.N);
+  const BwdSmem Lo = bwd_smem(ES, C, DK, DV, false);
+  CH ch;
+  ch.bind(sm, Lo);
+  float* scw = ch.lam;   // [slot][position] weights of the current chunk
+  const size_t SZ = (size_t)DK * DV;
+  float* rnp = p.rnp + (size_t)bh * p.items * SZ;
+
+  // the levels above 2 whose right blocks hold this group
+  int nh = 0;
+  for (int j = 3; j < p.nl; ++j) nh += (g >> (j - 3)) & 1;
+  const int npass = nh > kRgHigh ? cdiv(nh, kRgHigh) : 1;
+
+  for (int pass = 0; pass < npass; ++pass) {
+    // this pass's levels per slot (-1: unused): low slots in the first pass only
+    int lev[NS];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) lev[u] = (pass == 0 && u < p.nl) ? u : -1;
+#pragma unroll
+    for (int u = 3; u < NS; ++u) {   // the (pass * kRgHigh + u - 3)-th such level, if any
+      const int want = pass * kRgHigh + u - 3;
+      int k = 0, found = -1;
+      for (int j = 3; j < p.nl; ++j)
+        if ((g >> (j - 3)) & 1) {
+          if (k == want) found = j;
+          ++k;
+        }
+      lev[u] = found;
+    }
+    f32x4 acc[NS][TPW];
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) acc[u][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // the next chunk's q and do rows, log_a and the slots' lambda values, in registers (every
+    // load unconditional, from clamped valid indices)
+    u32x4 rq[NQ], ro[NO];
+    float rla = 0.f, rlm[NS];
+    auto fetch = [&](int c) {
+      const int nv = min(C, p.T - c * C);
+      const size_t row0 = (size_t)bh * p.T + (size_t)c * C;
+      const u32x4* gq = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(p.q) + row0 * DK);
+      const u32x4* go = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(p.dout) + row0 * DV);
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) {
+        const int idx = min(tid + u * NT, PQ - 1);
+        rq[u] = gq[min(idx / (DK / EPV), nv - 1) * (DK / EPV) + idx % (DK / EPV)];
+      }
+#pragma unroll
+      for (int u = 0; u < NO; ++u) {
+        const int idx = min(tid + u * NT, PO - 1);
+        ro[u] = go[min(idx / (DV / EPV), nv - 1) * (DV / EPV) + idx % (DV / EPV)];
+      }
+      const size_t r = row0 + min(lane, nv - 1);
+      rla = p.log_a[r];
+#pragma unroll
+      for (int u = 0; u < NS; ++u) rlm[u] = lambda_at(p, r * p.L + min(J + 1 + max(lev[u], 0), p.L - 1));
+    };
+    fetch(c0);
+    float eoff = 0.f;     // log decay from the group's start to the current chunk's start
+    float base[3] = {0.f, 0.f, 0.f};
+    for (int c = c0; c < c1; ++c) {
+      const int nv = min(C, p.T - c * C);
+      if (c > c0) __syncthreads();   // the previous chunk's images and weights are no longer read
+#pragma unroll
+      for (int u = 0; u < NQ; ++u) {
+        const int idx = tid + u * NT;
+        if (idx < PQ) {
+          const int r = idx / (DK / EPV), f = (idx % (DK / EPV)) * EPV;
+          *reinterpret_cast<u32x4*>(ch.q + r * CH::RK + f) = r < nv ? rq[u] : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NO; ++u) {
+        const int idx = tid + u * NT;
+        if (idx < PO) {
+          const int r = idx / (DV / EPV), f = (idx % (DV / EPV)) * EPV;
+          *reinterpret_cast<u32x4*>(ch.o + r * CH::RV + f) = r < nv ? ro[u] : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      // every wave scans the chunk's log_a (C <= 64 positions, one per lane); wave 0 writes the
+      // weights of the active slots
+      float incl = lane < nv ? rla : 0.f;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+      }
+      bool act[NS];
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        act[u] = lev[u] >= 0 && ((c >> u) & 1);
+        if (act[u] && !(c & ((1 << u) - 1))) base[u] = eoff;   // first chunk of its right block
+      }
+#pragma unroll
+      for (int u = 3; u < NS; ++u) act[u] = lev[u] >= 0;
+      if (w == 0 && lane < C) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u)
+          if (act[u]) scw[u * C + lane] = lane < nv ? rlm[u] * __expf(eoff - (u < 3 ? base[u] : 0.f) + incl) : 0.f;
+      }
+      eoff += __shfl(incl, C - 1);
+      __syncthreads();
+      if (c + 1 < c1) fetch(c + 1);
+      // the wave's tiles: do columns (the scaled operand) scaled and split once per slot and
+      // contraction step, then used against every q column block the wave holds
+#pragma unroll
+      for (int s0 = 0; s0 < C; s0 += 32) {
+        const int k = s0 + 8 * g4;
+        Frag<T> a[TM::APW];
+#pragma unroll
+        for (int b = 0; b < TM::APW; ++b) {
+          const int ab = TM::ab(w, b);
+          a[b] = ab < DK / 16 ? frag_col<T, C>(ch.q, CH::RK, k, ab * 16 + jj) : zero_frag<T>();
+        }
+#pragma unroll
+        for (int ya = 0; ya < TM::YPW; ++ya) {
+          const Frag<T> uo = frag_col<T, C>(ch.o, CH::RV, k, TM::y(w, ya) * 16 + jj);
+          f32x4 ulo, uhi;
+          frag_to_f32(uo, ulo, uhi);
+#pragma unroll
+          for (int u = 0; u < NS; ++u) {
+            if (!act[u]) continue;
+            // past C (chunk 16) the operands are zero; the weights are read in range
+            const float* sc = scw + u * C + (k < C ? k : 0);
+            Frag<T> bh_, bl_;
+            scale_split<T>(ulo, uhi, sc, bh_, bl_);
+#pragma unroll
+            for (int b = 0; b < TM::APW; ++b) {
+              mma(acc[u][ya * TM::APW + b], a[b], bh_);
+              if constexpr (sizeof(T) == 2) mma(acc[u][ya * TM::APW + b], a[b], bl_);
+            }
+          }
+        }
+      }
+      // store (and restart) each low slot whose right block ends with this chunk
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        if (!act[u] || (c + 1 < c1 && ((c + 1) >> u) & 1)) continue;
+        TM::template store<DV>(rnp + (size_t)(p.rn_off[u] + item_of_sub(u, c >> u)) * SZ, acc[u], w, lane);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i) acc[u][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    // the group's states of the levels above 2
+#pragma unroll
+    for (int u = 3; u < NS; ++u) {
+      if (lev[u] < 0) continue;
+      TM::template store<DV>(rnp + (size_t)(p.rn_off[lev[u]] + item_of_sub(lev[u], g)) * SZ, acc[u], w, lane);
+    }
+    if (pass + 1 < npass) __syncthreads();   // the images are rewritten by the next pass
   }
 }
 
@@ -1015,8 +1270,10 @@ namespace bwd {
 
 template <typename TY, int C, int DK, int DV>
 BwdKernels make_bwd() {
+  const void* rng = nullptr;
+  if constexpr (rng_fits<C, DK, DV>()) rng = reinterpret_cast<const void*>(&bwd_rng_kernel<TY, C, DK, DV>);
   return BwdKernels{reinterpret_cast<const void*>(&bwd_states_kernel<TY, C, DK, DV>),
-                    reinterpret_cast<const void*>(&bwd_rn_kernel<TY, C, DK, DV>),
+                    reinterpret_cast<const void*>(&bwd_rn_kernel<TY, C, DK, DV>), rng,
                     reinterpret_cast<const void*>(&bwd_grads_kernel<TY, C, DK, DV>)};
 }
 

@@ -643,10 +643,20 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
     if (set_smem(ks->states, pl.smem_states) != hipSuccess) return LLA_ERR_HIP;
     if (hipLaunchKernel(ks->states, chunks, dim3(NT), args, pl.smem_states, stream) != hipSuccess)
       return LLA_ERR_HIP;
-    if (set_smem(ks->rn, pl.smem_states) != hipSuccess) return LLA_ERR_HIP;
-    if (hipLaunchKernel(ks->rn, dim3((unsigned)((long long)pl.items * pl.BH)), dim3(NT), args,
-                        pl.smem_states, stream) != hipSuccess)
-      return LLA_ERR_HIP;
+    // the target-side sub-block states: one workgroup per group of 8 chunks where its
+    // accumulators fit, else one per sub-block and level
+    if (ks->rng) {
+      const long long ng = (pl.N + 7) / 8;
+      if (set_smem(ks->rng, pl.smem_states) != hipSuccess) return LLA_ERR_HIP;
+      if (hipLaunchKernel(ks->rng, dim3((unsigned)(ng * pl.BH)), dim3(NT), args, pl.smem_states,
+                          stream) != hipSuccess)
+        return LLA_ERR_HIP;
+    } else {
+      if (set_smem(ks->rn, pl.smem_states) != hipSuccess) return LLA_ERR_HIP;
+      if (hipLaunchKernel(ks->rn, dim3((unsigned)((long long)pl.items * pl.BH)), dim3(NT), args,
+                          pl.smem_states, stream) != hipSuccess)
+        return LLA_ERR_HIP;
+    }
     if (pl.nl > 1) {
       hipLaunchKernelGGL(lla::bwd::bwd_gsum_kernel, dim3((unsigned)pl.BH), dim3(256), 0, stream, p);
       if (hipGetLastError() != hipSuccess) return LLA_ERR_HIP;
