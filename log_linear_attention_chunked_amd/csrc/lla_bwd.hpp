@@ -431,186 +431,6 @@ struct Chunk {
   }
 };
 
-// ----------------------------------------------------------------------------------------
-// bwd_states: chunk state F(c) and the right-block partials Z(c, j)
-// ----------------------------------------------------------------------------------------
-
-// out[a][b] = sum_s X[s][a] * sc[s] * Y[s][b] over the chunk's positions (a < DA, b < DB),
-// stored row-major into dst (fp32); wave w takes 16-row blocks of a = w, w + NW, ...
-template <typename T, int C, int DA, int DB, int NW>
-__device__ __forceinline__ void outer_store(const T* X, int RX, const T* Y, int RY, const float* sc,
-                                            float* __restrict__ dst, int w, int lane) {
-  const int j = lane & 15, g = lane >> 4;
-  for (int ab = w; ab < DA / 16; ab += NW) {
-#pragma unroll
-    for (int bb = 0; bb < DB / 16; ++bb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s0 = 0; s0 < C; s0 += 32) {
-        const Frag<T> a = frag_col<T, C>(X, RX, s0 + 8 * g, ab * 16 + j);
-        Frag<T> bh, bl;
-        frag_col_split<T, C>(Y, RY, s0 + 8 * g, bb * 16 + j, sc, bh, bl);
-        mma(acc, a, bh);
-        if constexpr (sizeof(T) == 2) mma(acc, a, bl);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(size_t)(ab * 16 + 4 * g + r) * DB + bb * 16 + j] = acc[r];
-    }
-  }
-}
-
-template <typename T, int C, int DK, int DV>
-__global__ void __launch_bounds__(64 * Waves<C>::NW)
-bwd_states_kernel(BwdParams p) {
-  constexpr int NW = Waves<C>::NW, NT = 64 * NW;
-  using CH = Chunk<T, C, DK, DV>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
-  const int c = blockIdx.x, bh = blockIdx.y;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int nv = min(C, p.T - c * C);
-  const BwdSmem Lo = bwd_smem((int)sizeof(T), C, DK, DV, false);
-  CH ch;
-  ch.bind(sm, Lo);
-  ch.template load<NT, true, false, false>(p, bh, c, nv, tid);
-  const size_t SZ = (size_t)DK * DV;
-  // F(c): keys weighted by their decay to the chunk's end
-  outer_store<T, C, DK, DV, NW>(ch.k, CH::RK, ch.v, CH::RV, ch.ws,
-                                p.node + ((size_t)bh * p.nslot + c) * SZ, w, lane);
-  if (tid == 0) p.gsum[(size_t)bh * p.nslot + c] = ch.g;
-}
-
-// ----------------------------------------------------------------------------------------
-// bwd_rn: one target-side sub-block state per workgroup,
-//   P(j, sb) = sum over the positions t of sub-block sb of lambda[t, J+1+j] exp(A_t - A_0) q_t do_t^T
-// with A_0 the prefix decay just before the sub-block, accumulated chunk by chunk on MFMA
-// ----------------------------------------------------------------------------------------
-
-template <typename T, int C, int DK, int DV>
-__global__ void __launch_bounds__(64 * Waves<C>::NW)
-bwd_rn_kernel(BwdParams p) {
-  constexpr int NW = Waves<C>::NW, NT = 64 * NW, J = ilog2(C);
-  constexpr int AB = cdiv(DK / 16, NW), NB = DV / 16;
-  constexpr int ES = (int)sizeof(T), EPV = 16 / ES;
-  constexpr int PQ = C * DK / EPV, PO = C * DV / EPV;        // 16-byte pieces of the q, do rows
-  constexpr int NQ = cdiv(PQ, NT), NO = cdiv(PO, NT);
-  using CH = Chunk<T, C, DK, DV>;
-  extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
-  // one-dimensional grid in XCD order, as in bwd_grads: XCD x takes heads x, x + 8, ... (B*H a
-  // multiple of 8), every sub-block of a head in turn, so the q and dO rows a head reads once per
-  // level come from its L2 after the first time
-  const int Lw = blockIdx.x, q8 = Lw >> 3;
-  const bool xcd = (p.BH & 7) == 0;
-  const int item = xcd ? q8 % p.items : Lw % p.items;
-  const int bh = xcd ? ((q8 / p.items) << 3) + (Lw & 7) : Lw / p.items;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, jj = lane & 15, g4 = lane >> 4;
-  int j = 0;
-  while (j + 1 < p.nl && p.rn_off[j + 1] <= item) ++j;
-  const int sb = sub_of_item(j, item - p.rn_off[j]);
-  const int c0 = sb << sub_log(j), c1 = min(c0 + (1 << sub_log(j)), p.N);
-  const BwdSmem Lo = bwd_smem(ES, C, DK, DV, false);
-  CH ch;
-  ch.bind(sm, Lo);
-  float* sc = ch.lam;   // per-position weights of the current chunk
-  f32x4 acc[AB][NB];
-#pragma unroll
-  for (int x = 0; x < AB; ++x)
-#pragma unroll
-    for (int y = 0; y < NB; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // the next chunk's q and do rows, log_a and lambda of level J+1+j, in registers: issued before
-  // the current chunk's products so that their latency hides behind them
-  u32x4 rq[NQ], ro[NO];
-  float rla = 0.f, rlm = 0.f;
-  auto fetch = [&](int c) {
-    const int nv = min(C, p.T - c * C);
-    const size_t row0 = (size_t)bh * p.T + (size_t)c * C;
-    const u32x4* gq = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(p.q) + row0 * DK);
-    const u32x4* go = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(p.dout) + row0 * DV);
-#pragma unroll
-    for (int u = 0; u < NQ; ++u) {
-      const int idx = tid + u * NT;
-      rq[u] = (idx < PQ && idx / (DK / EPV) < nv) ? gq[idx] : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < NO; ++u) {
-      const int idx = tid + u * NT;
-      ro[u] = (idx < PO && idx / (DV / EPV) < nv) ? go[idx] : u32x4{0u, 0u, 0u, 0u};
-    }
-    rla = lane < nv ? p.log_a[row0 + lane] : 0.f;
-    rlm = lane < nv ? lambda_at(p, (row0 + lane) * p.L + J + 1 + j) : 0.f;
-  };
-  fetch(c0);
-  float eoff = 0.f;     // log decay from the sub-block's start to the current chunk's start
-  for (int c = c0; c < c1; ++c) {
-    if (c > c0) __syncthreads();   // the previous chunk's images and weights are no longer read
-#pragma unroll
-    for (int u = 0; u < NQ; ++u) {
-      const int idx = tid + u * NT;
-      if (idx < PQ) {
-        const int r = idx / (DK / EPV), f = (idx % (DK / EPV)) * EPV;
-        *reinterpret_cast<u32x4*>(ch.q + r * CH::RK + f) = rq[u];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < NO; ++u) {
-      const int idx = tid + u * NT;
-      if (idx < PO) {
-        const int r = idx / (DV / EPV), f = (idx % (DV / EPV)) * EPV;
-        *reinterpret_cast<u32x4*>(ch.o + r * CH::RV + f) = ro[u];
-      }
-    }
-    // every wave scans the chunk's log_a (C <= 64 positions, one per lane); wave 0 writes the
-    // weights lambda * exp(decay from the sub-block's start)
-    float incl = lane < C ? rla : 0.f;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float y = __shfl_up(incl, d);
-      if (lane >= d) incl += y;
-    }
-    if (w == 0 && lane < C) sc[lane] = rlm * __expf(eoff + incl);
-    eoff += __shfl(incl, C - 1);
-    __syncthreads();
-    if (c + 1 < c1) fetch(c + 1);
-#pragma unroll
-    for (int x = 0; x < AB; ++x) {
-      const int ab = w + NW * x;
-      if (ab >= DK / 16) break;
-#pragma unroll
-      for (int y = 0; y < NB; ++y)
-#pragma unroll
-        for (int s0 = 0; s0 < C; s0 += 32) {
-          const Frag<T> a = frag_col<T, C>(ch.q, CH::RK, s0 + 8 * g4, ab * 16 + jj);
-          Frag<T> bh, bl;
-          frag_col_split<T, C>(ch.o, CH::RV, s0 + 8 * g4, y * 16 + jj, sc, bh, bl);
-          mma(acc[x][y], a, bh);
-          if constexpr (sizeof(T) == 2) mma(acc[x][y], a, bl);
-        }
-    }
-  }
-  float* dst = p.rnp + ((size_t)bh * p.items + item) * ((size_t)DK * DV);
-#pragma unroll
-  for (int x = 0; x < AB; ++x) {
-    const int ab = w + NW * x;
-    if (ab >= DK / 16) break;
-#pragma unroll
-    for (int y = 0; y < NB; ++y)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(size_t)(ab * 16 + 4 * g4 + r) * DV + y * 16 + jj] = acc[x][y][r];
-  }
-}
-
-// ----------------------------------------------------------------------------------------
-// bwd_rng: the same sub-block states as bwd_rn, with one workgroup per group of 8 chunks (a
-// sub-block of every level >= 3) and head, chunk by chunk: the group's q and do rows are read
-// once, and every state its chunks belong to is accumulated at the same time. Slots 0..2: the
-// right blocks of levels 0, 1, 2 inside the group (a chunk takes part in level j when bit j of
-// its index is set; a block's state is stored when its last chunk is done and the slot starts
-// over); slots 3..: the group itself, for up to kRgHigh levels j >= 3 whose right blocks hold it
-// (bit j - 3 of the group index set), stored at the end; more such levels take another pass
-// over the group. The weights of a slot are lambda[t, J+1+j] exp(A_t - A_0), A_0 the prefix
-// decay just before the slot's block (the group's start for slots 3..).
-// ----------------------------------------------------------------------------------------
-
 // Tiles of a DK x DV product out[a][b] = sum_k A[k][a] B'[k][b] whose B' is a scaled (and, in
 // bf16, hi + lo split) operand: the waves split the b (column) dimension first, so that each
 // wave scales the columns it uses once per contraction step and reuses them for every a block
@@ -669,6 +489,197 @@ __device__ __forceinline__ void scale_split(const f32x4& ulo, const f32x4& uhi, 
     lo = zero_frag<T>();
   }
 }
+
+// ----------------------------------------------------------------------------------------
+// bwd_states: chunk state F(c) and the right-block partials Z(c, j)
+// ----------------------------------------------------------------------------------------
+
+// out[a][b] = sum_s X[s][a] * sc[s] * Y[s][b] over the chunk's positions (a < DA, b < DB),
+// stored row-major into dst (fp32); the waves split the tiles as ScaledTiles (the scaled
+// Y columns once per wave)
+template <typename T, int C, int DA, int DB, int NW>
+__device__ __forceinline__ void outer_store(const T* X, int RX, const T* Y, int RY, const float* sc,
+                                            float* __restrict__ dst, int w, int lane) {
+  using TM = ScaledTiles<DA, DB, NW>;
+  const int jj = lane & 15, g4 = lane >> 4;
+  f32x4 acc[TM::TPW];
+#pragma unroll
+  for (int i = 0; i < TM::TPW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s0 = 0; s0 < C; s0 += 32) {
+    const int k = s0 + 8 * g4;
+    Frag<T> a[TM::APW];
+#pragma unroll
+    for (int b = 0; b < TM::APW; ++b) {
+      const int ab = TM::ab(w, b);
+      a[b] = ab < DA / 16 ? frag_col<T, C>(X, RX, k, ab * 16 + jj) : zero_frag<T>();
+    }
+#pragma unroll
+    for (int ya = 0; ya < TM::YPW; ++ya) {
+      const Frag<T> uy = frag_col<T, C>(Y, RY, k, TM::y(w, ya) * 16 + jj);
+      f32x4 ulo, uhi;
+      frag_to_f32(uy, ulo, uhi);
+      Frag<T> bh, bl;
+      scale_split<T>(ulo, uhi, sc + (k < C ? k : 0), bh, bl);
+#pragma unroll
+      for (int b = 0; b < TM::APW; ++b) {
+        mma(acc[ya * TM::APW + b], a[b], bh);
+        if constexpr (sizeof(T) == 2) mma(acc[ya * TM::APW + b], a[b], bl);
+      }
+    }
+  }
+  TM::template store<DB>(dst, acc, w, lane);
+}
+
+template <typename T, int C, int DK, int DV>
+__global__ void __launch_bounds__(64 * Waves<C>::NW)
+bwd_states_kernel(BwdParams p) {
+  constexpr int NW = Waves<C>::NW, NT = 64 * NW;
+  using CH = Chunk<T, C, DK, DV>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int nv = min(C, p.T - c * C);
+  const BwdSmem Lo = bwd_smem((int)sizeof(T), C, DK, DV, false);
+  CH ch;
+  ch.bind(sm, Lo);
+  ch.template load<NT, true, false, false>(p, bh, c, nv, tid);
+  const size_t SZ = (size_t)DK * DV;
+  // F(c): keys weighted by their decay to the chunk's end
+  outer_store<T, C, DK, DV, NW>(ch.k, CH::RK, ch.v, CH::RV, ch.ws,
+                                p.node + ((size_t)bh * p.nslot + c) * SZ, w, lane);
+  if (tid == 0) p.gsum[(size_t)bh * p.nslot + c] = ch.g;
+}
+
+// ----------------------------------------------------------------------------------------
+// bwd_rn: one target-side sub-block state per workgroup,
+//   P(j, sb) = sum over the positions t of sub-block sb of lambda[t, J+1+j] exp(A_t - A_0) q_t do_t^T
+// with A_0 the prefix decay just before the sub-block, accumulated chunk by chunk on MFMA
+// ----------------------------------------------------------------------------------------
+
+template <typename T, int C, int DK, int DV>
+__global__ void __launch_bounds__(64 * Waves<C>::NW)
+bwd_rn_kernel(BwdParams p) {
+  constexpr int NW = Waves<C>::NW, NT = 64 * NW, J = ilog2(C);
+  using TM = ScaledTiles<DK, DV, NW>;
+  constexpr int ES = (int)sizeof(T), EPV = 16 / ES;
+  constexpr int PQ = C * DK / EPV, PO = C * DV / EPV;        // 16-byte pieces of the q, do rows
+  constexpr int NQ = cdiv(PQ, NT), NO = cdiv(PO, NT);
+  using CH = Chunk<T, C, DK, DV>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
+  // one-dimensional grid in XCD order, as in bwd_grads: XCD x takes heads x, x + 8, ... (B*H a
+  // multiple of 8), every sub-block of a head in turn, so the q and dO rows a head reads once per
+  // level come from its L2 after the first time
+  const int Lw = blockIdx.x, q8 = Lw >> 3;
+  const bool xcd = (p.BH & 7) == 0;
+  const int item = xcd ? q8 % p.items : Lw % p.items;
+  const int bh = xcd ? ((q8 / p.items) << 3) + (Lw & 7) : Lw / p.items;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, jj = lane & 15, g4 = lane >> 4;
+  int j = 0;
+  while (j + 1 < p.nl && p.rn_off[j + 1] <= item) ++j;
+  const int sb = sub_of_item(j, item - p.rn_off[j]);
+  const int c0 = sb << sub_log(j), c1 = min(c0 + (1 << sub_log(j)), p.N);
+  const BwdSmem Lo = bwd_smem(ES, C, DK, DV, false);
+  CH ch;
+  ch.bind(sm, Lo);
+  float* sc = ch.lam;   // per-position weights of the current chunk
+  f32x4 acc[TM::TPW];
+#pragma unroll
+  for (int i = 0; i < TM::TPW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // the next chunk's q and do rows, log_a and lambda of level J+1+j, in registers: issued before
+  // the current chunk's products so that their latency hides behind them
+  u32x4 rq[NQ], ro[NO];
+  float rla = 0.f, rlm = 0.f;
+  auto fetch = [&](int c) {
+    const int nv = min(C, p.T - c * C);
+    const size_t row0 = (size_t)bh * p.T + (size_t)c * C;
+    const u32x4* gq = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(p.q) + row0 * DK);
+    const u32x4* go = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(p.dout) + row0 * DV);
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int idx = tid + u * NT;
+      rq[u] = (idx < PQ && idx / (DK / EPV) < nv) ? gq[idx] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+      const int idx = tid + u * NT;
+      ro[u] = (idx < PO && idx / (DV / EPV) < nv) ? go[idx] : u32x4{0u, 0u, 0u, 0u};
+    }
+    rla = lane < nv ? p.log_a[row0 + lane] : 0.f;
+    rlm = lane < nv ? lambda_at(p, (row0 + lane) * p.L + J + 1 + j) : 0.f;
+  };
+  fetch(c0);
+  float eoff = 0.f;     // log decay from the sub-block's start to the current chunk's start
+  for (int c = c0; c < c1; ++c) {
+    if (c > c0) __syncthreads();   // the previous chunk's images and weights are no longer read
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int idx = tid + u * NT;
+      if (idx < PQ) {
+        const int r = idx / (DK / EPV), f = (idx % (DK / EPV)) * EPV;
+        *reinterpret_cast<u32x4*>(ch.q + r * CH::RK + f) = rq[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+      const int idx = tid + u * NT;
+      if (idx < PO) {
+        const int r = idx / (DV / EPV), f = (idx % (DV / EPV)) * EPV;
+        *reinterpret_cast<u32x4*>(ch.o + r * CH::RV + f) = ro[u];
+      }
+    }
+    // every wave scans the chunk's log_a (C <= 64 positions, one per lane); wave 0 writes the
+    // weights lambda * exp(decay from the sub-block's start)
+    float incl = lane < C ? rla : 0.f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const float y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    if (w == 0 && lane < C) sc[lane] = rlm * __expf(eoff + incl);
+    eoff += __shfl(incl, C - 1);
+    __syncthreads();
+    if (c + 1 < c1) fetch(c + 1);
+    // the wave's tiles: its do columns scaled and split once per contraction step
+#pragma unroll
+    for (int s0 = 0; s0 < C; s0 += 32) {
+      const int k = s0 + 8 * g4;
+      Frag<T> a[TM::APW];
+#pragma unroll
+      for (int b = 0; b < TM::APW; ++b) {
+        const int ab = TM::ab(w, b);
+        a[b] = ab < DK / 16 ? frag_col<T, C>(ch.q, CH::RK, k, ab * 16 + jj) : zero_frag<T>();
+      }
+#pragma unroll
+      for (int ya = 0; ya < TM::YPW; ++ya) {
+        const Frag<T> uo = frag_col<T, C>(ch.o, CH::RV, k, TM::y(w, ya) * 16 + jj);
+        f32x4 ulo, uhi;
+        frag_to_f32(uo, ulo, uhi);
+        Frag<T> bh_, bl_;
+        scale_split<T>(ulo, uhi, sc + (k < C ? k : 0), bh_, bl_);
+#pragma unroll
+        for (int b = 0; b < TM::APW; ++b) {
+          mma(acc[ya * TM::APW + b], a[b], bh_);
+          if constexpr (sizeof(T) == 2) mma(acc[ya * TM::APW + b], a[b], bl_);
+        }
+      }
+    }
+  }
+  TM::template store<DV>(p.rnp + ((size_t)bh * p.items + item) * ((size_t)DK * DV), acc, w, lane);
+}
+
+// ----------------------------------------------------------------------------------------
+// bwd_rng: the same sub-block states as bwd_rn, with one workgroup per group of 8 chunks (a
+// sub-block of every level >= 3) and head, chunk by chunk: the group's q and do rows are read
+// once, and every state its chunks belong to is accumulated at the same time. Slots 0..2: the
+// right blocks of levels 0, 1, 2 inside the group (a chunk takes part in level j when bit j of
+// its index is set; a block's state is stored when its last chunk is done and the slot starts
+// over); slots 3..: the group itself, for up to kRgHigh levels j >= 3 whose right blocks hold it
+// (bit j - 3 of the group index set), stored at the end; more such levels take another pass
+// over the group. The weights of a slot are lambda[t, J+1+j] exp(A_t - A_0), A_0 the prefix
+// decay just before the slot's block (the group's start for slots 3..).
+// ----------------------------------------------------------------------------------------
 
 constexpr int kRgHigh = 4;
 
