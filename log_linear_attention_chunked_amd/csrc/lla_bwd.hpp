@@ -120,7 +120,7 @@ __host__ __device__ inline int slot_of(int N, int i, int m) {
 
 // shared-memory layout of bwd_states / bwd_grads (host and device agree)
 struct BwdSmem {
-  int q, k, v, o, p1, p2, lam, al, ea, ws, ust, nst, cg, total;
+  int q, k, v, o, p1, p2, lam, al, ea, ws, ust, cg, dqd, total;
 };
 
 __host__ __device__ inline BwdSmem bwd_smem(int es, int C, int DK, int DV, bool grads) {
@@ -139,11 +139,10 @@ __host__ __device__ inline BwdSmem bwd_smem(int es, int C, int DK, int DV, bool 
   s.al = take(C * 4);
   s.ea = take(C * 4);
   s.ws = take(C * 4);
-  // a [dk][dv] state image: first the combined right-sibling state, then (once the source-side
-  // products are done) one Fenwick node at a time
+  // a [dk][dv] state image: the combined right-sibling state
   s.ust = grads ? take(DK * rv * es) : off;
-  s.nst = s.ust;
   s.cg = grads ? take(4 * C * 4) : off;   // per-wave column sums of G = M S W
+  s.dqd = grads ? take(C * 4) : off;       // q . (dq from the nodes), per position
   s.total = (off + 255) & ~255;
   return s;
 }
@@ -890,6 +889,39 @@ __device__ __forceinline__ void stage_state(T* img, const T* __restrict__ g, int
   }
 }
 
+// dq tiles (row block of the C positions, column block of DK) dealt to the NW = C / 16 waves by
+// column, so that a wave reads only the node rows of its own columns: WIDE (DK / 16 >= NW) gives
+// wave w the column blocks w, w + NW, ... and every row block; otherwise wave w has column block
+// w % NK and the row blocks congruent to w / NK modulo NW / NK. Tile index a * RBW + b.
+template <int C, int DK>
+struct DqTiles {
+  static constexpr int NW = Waves<C>::NW, NK = DK / 16;
+  static_assert(C / 16 == NW, "one 16-row block per wave");
+  static constexpr bool WIDE = NK >= NW;
+  static constexpr int TA = WIDE ? NK / NW : 1;     // column blocks per wave
+  static constexpr int RBW = WIDE ? NW : NK;        // row blocks per wave
+  __device__ static constexpr int t(int w, int a) { return WIDE ? w + NW * a : w % NK; }
+  __device__ static constexpr int rb(int w, int b) { return WIDE ? b : w / NK + (NW / NK) * b; }
+  __device__ static constexpr bool holds(int w, int R) { return WIDE || (R % (NW / NK)) == w / NK; }
+};
+
+// X[r][k .. k+7] of a row-major state in global memory (row stride RS elements, element type),
+// as an MFMA operand; the load is unconditional (from a clamped column when k >= K) and ok
+// tells the caller whether to use it or zeros
+template <typename T, int K>
+__device__ __forceinline__ Frag<T> frag_gload(const T* g, int RS, int r, int k, bool& ok) {
+  ok = K % 32 == 0 || k < K;   // steps of 32 over a multiple of 32 never pass K
+  const T* p = g + (size_t)r * RS + (ok ? k : K - 8);
+  Frag<T> f;
+  if constexpr (sizeof(T) == 2) {
+    f.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+  } else {
+    f.lo = *reinterpret_cast<const f32x4*>(p);
+    f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  return f;
+}
+
 // two waves per SIMD (at most 256 registers per lane, accumulation registers included) where two
 // workgroups' shared memory fits a compute unit (states up to 64 x 64); fewer would leave half
 // of it idle
@@ -919,7 +951,6 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   T* P1 = reinterpret_cast<T*>(sm + Lo.p1);     // M * W  [i][j]
   T* P2 = reinterpret_cast<T*>(sm + Lo.p2);     // M * S  [i][j]
   T* Ust = reinterpret_cast<T*>(sm + Lo.ust);   // combined right-sibling state [a][b]
-  T* Nst = reinterpret_cast<T*>(sm + Lo.nst);   // one node [a][b] (the same region, after step 3)
   const size_t SZ = (size_t)DK * DV;
   const size_t row0 = (size_t)bh * p.T + (size_t)c * C;
   // the combined right-sibling state, written by the down-sweep (zero for the last chunk);
@@ -941,9 +972,12 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   constexpr int EPV = 16 / ES;
   constexpr int NPF = DK * DV / EPV / NT;
   constexpr bool PF = NPF >= 1 && NPF <= 4 && NPF * NT * EPV == DK * DV;
-  u32x4 pf[PF ? NPF : 1], pf2[PF && SPLIT ? NPF : 1];
+  // step 4 by columns of dq when a node is too large for the staging's register prefetch
+  constexpr bool COLQ = !PF;
   // jl past the last set bit (nothing left to read) loads a valid slot that is never used: the
-  // node just read (cur, still in L2), or for chunk 0 (no node at all) slot 0
+  // node just read (cur, still in L2), or for chunk 0 slot 0.
+  // rows of dq: the whole node, every thread its share, on its way into shared memory
+  u32x4 pf[PF ? NPF : 1], pf2[PF && SPLIT ? NPF : 1];
   auto prefetch = [&](int jl, int cur) {
     if (jl >= p.nl) jl = cur;
     const size_t off = (size_t)slot_of(p.N, jl, max((c >> jl) - 1, 0)) * SZ;
@@ -955,6 +989,25 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
 #pragma unroll
       for (int u = 0; u < (PF ? NPF : 1); ++u) pf2[u] = src2[tid + u * NT];
   };
+  // columns of dq: the node rows this wave's dq columns need (hi and lo parts), straight into
+  // operand registers
+  using QT = DqTiles<C, DK>;
+  constexpr int NKS = DV >= 32 ? DV / 32 : 1;           // contraction steps over dv
+  constexpr int NBF = QT::TA * NKS;                      // operand fragments per node
+  auto load_node = [&](int jl, int cur, Frag<T>* hi, Frag<T>* lo, bool* ok) {
+    if (jl >= p.nl) jl = cur;
+    const size_t off = (size_t)slot_of(p.N, jl, max((c >> jl) - 1, 0)) * SZ;
+#pragma unroll
+    for (int a = 0; a < QT::TA; ++a)
+#pragma unroll
+      for (int kb = 0; kb < NKS; ++kb) {
+        const int r = QT::t(w, a) * 16 + jj, kk = kb * 32 + 8 * g4;
+        hi[a * NKS + kb] = frag_gload<T, DV>(node_e + off, DV, r, kk, ok[a * NKS + kb]);
+        if constexpr (SPLIT) lo[a * NKS + kb] = frag_gload<T, DV>(node_lo + off, DV, r, kk, ok[a * NKS + kb]);
+      }
+  };
+  Frag<T> bhi[NBF], blo[NBF];
+  bool bok[NBF];
   auto put = [&](T* img, const u32x4* r) {
 #pragma unroll
     for (int u = 0; u < NPF; ++u) {
@@ -972,7 +1025,11 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
     for (int u = 0; u < NPF; ++u) ulo[u] = reinterpret_cast<const u32x4*>(u_lo)[tid + u * NT];
   int first_set = 0;
   while (first_set < p.nl && !((c >> first_set) & 1)) ++first_set;
-  if (PF && later) prefetch(first_set, 0);
+  if constexpr (COLQ) {
+    if (later) load_node(first_set, 0, bhi, blo, bok);
+  } else {
+    if (later) prefetch(first_set, 0);
+  }
   st.put(ch, tid);
   if (later) {
     if constexpr (PF) put(Ust, uhi);
@@ -1049,25 +1106,41 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
         }
       }
     }
+    // dlambda of the levels inside the chunk, parked in the lambda rows' slots of those levels
+    // (this wave's rows; step 1 has read them) until step 6 stores them
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int l = 0; l <= J; ++l)
+        if (jj == l) ch.lam[(rb * 16 + 4 * g4 + r) * kLamCap + l] = bins[x][r][l];
   }
   __syncthreads();
 
-  // 2. intra-chunk products: dq = P1 K, dk = P1^T Q, dv = P2^T dO (rows: positions of block rb)
-  f32x4 aq[RB][NK], ak[RB][NK], av[RB][NV];
+  // 2. intra-chunk products: dq = P1 K (the wave's dq tiles: the rows of block rb, or by columns
+  //    as step 4 takes them), dk = P1^T Q, dv = P2^T dO (rows: positions of block rb)
+  f32x4 aq[NK], ak[RB][NK], av[RB][NV];
+#pragma unroll
+  for (int a = 0; a < (COLQ ? QT::TA : 1); ++a)
+#pragma unroll
+    for (int b = 0; b < (COLQ ? QT::RBW : NK); ++b) {
+      const int R = COLQ ? QT::rb(w, b) : w, t = COLQ ? QT::t(w, a) : b;
+      f32x4 zq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s0 = 0; s0 < C; s0 += 32)
+        mma(zq, frag_row<T, C>(P1, RC, R * 16 + jj, s0 + 8 * g4),
+            frag_col<T, C>(ch.k, CH::RK, s0 + 8 * g4, t * 16 + jj));
+      aq[COLQ ? a * QT::RBW + b : b] = zq;
+    }
 #pragma unroll
   for (int x = 0; x < RB; ++x) {
     const int rb = w + NW * x;
 #pragma unroll
     for (int t = 0; t < NK; ++t) {
-      f32x4 zq = {0.f, 0.f, 0.f, 0.f}, zk = zq;
+      f32x4 zk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s0 = 0; s0 < C; s0 += 32) {
-        mma(zq, frag_row<T, C>(P1, RC, rb * 16 + jj, s0 + 8 * g4),
-            frag_col<T, C>(ch.k, CH::RK, s0 + 8 * g4, t * 16 + jj));
+      for (int s0 = 0; s0 < C; s0 += 32)
         mma(zk, frag_col<T, C>(P1, RC, s0 + 8 * g4, rb * 16 + jj),
             frag_col<T, C>(ch.q, CH::RK, s0 + 8 * g4, t * 16 + jj));
-      }
-      aq[x][t] = zq;
       ak[x][t] = zk;
     }
 #pragma unroll
@@ -1129,32 +1202,34 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   }
 
   // 4. earlier chunks, query side: for each set bit j of c the node (j, (c>>j) - 1), decayed
-  //    over the nodes of the lower set bits, staged into shared memory; Y = dO node^T gives dq
-  //    (weighted by lambda) and dlambda of level J+1+j (its row dot with q, parked in that
-  //    level's slot of the lambda rows, which nothing reads again, and stored in step 6).
-  //    When a node is at most 4 float4 per thread, the next node's loads are in flight in
-  //    registers while the current one is used (the first one's since the kernel started).
+  //    over the nodes of the lower set bits; Y = dO node^T gives dq (weighted by lambda) and,
+  //    as its row dot with q, dlambda of level J+1+j (parked in that level's slot of the lambda
+  //    rows, which nothing reads again, and stored in step 6); q . (dq from the nodes) goes to
+  //    dqd for dA. Two ways, chosen by what measured faster:
+  //    - a node of at most 4 16-byte pieces per thread: staged into shared memory (the next
+  //      node's pieces in flight in registers meanwhile), every wave reading it whole for the
+  //      dq rows of its block;
+  //    - larger nodes, which the staging could not prefetch: by columns of dq, each wave loading
+  //      only the node rows of its own dq columns straight into operand registers, one node
+  //      ahead, with no barrier in the loop; the waves' dlambda shares are summed afterwards.
   const float* gs = p.gsum + (size_t)bh * p.nslot;
-  float dlow = 0.f;   // log decay from the end of the current node to the start of chunk c
-  float dq_dot[4] = {0.f, 0.f, 0.f, 0.f};   // q . (this part of dq): sum over levels of lambda dlambda
-  for (int jl = first_set; jl < p.nl; ++jl) {
-    if (!((c >> jl) & 1)) continue;
-    const int sl = slot_of(p.N, jl, (c >> jl) - 1);
-    __syncthreads();   // the previous reads of the state image are done
-    if constexpr (PF) {
+  float* dqd = reinterpret_cast<float*>(sm + Lo.dqd);
+  if constexpr (!COLQ) {
+    T* Nst = Ust;   // the state image, free once step 3 is done
+    float dlow = 0.f;   // log decay from the end of the current node to the start of chunk c
+    float dq_dot[4] = {0.f, 0.f, 0.f, 0.f};
+    const int rb = w;
+    for (int jl = first_set; jl < p.nl; ++jl) {
+      if (!((c >> jl) & 1)) continue;
+      const int sl = slot_of(p.N, jl, (c >> jl) - 1);
+      __syncthreads();   // the previous reads of the state image are done
       put(Nst, pf);
       if constexpr (SPLIT) put(Plo, pf2);
       int nx = jl + 1;
       while (nx < p.nl && !((c >> nx) & 1)) ++nx;
       prefetch(nx, jl);
-    } else {
-      stage_state<T, DK, DV, CH::RV, NT, SPLIT>(Nst, node_e + (size_t)sl * SZ, tid, Plo, node_lo + (size_t)sl * SZ);
-    }
-    __syncthreads();
-    const float dj = __expf(dlow);
-#pragma unroll
-    for (int x = 0; x < RB; ++x) {
-      const int rb = w + NW * x;
+      __syncthreads();
+      const float dj = __expf(dlow);
       float part[4] = {0.f, 0.f, 0.f, 0.f};
       float scl[4];
 #pragma unroll
@@ -1174,7 +1249,7 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = rb * 16 + 4 * g4 + r;
-          aq[x][t][r] += scl[r] * y[r];
+          aq[t][r] += scl[r] * y[r];
           part[r] += y[r] * to_f(ch.q[i * CH::RK + t * 16 + jj]);
         }
       }
@@ -1185,8 +1260,88 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
         dq_dot[r] += scl[r] * sum;
         if (jj == r) ch.lam[i * kLamCap + J + 1 + jl] = ch.ea[i] * dj * sum;
       }
+      dlow += gs[sl];
     }
-    dlow += gs[sl];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (jj == r) dqd[rb * 16 + 4 * g4 + r] = dq_dot[r];
+  } else {
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(sm + Lo.p1);   // [wave][node][position]
+    {
+      float dlow = 0.f;   // log decay from the end of the current node to the start of chunk c
+      int kn = 0;         // nodes done
+      Frag<T> nhi[NBF], nlo[NBF];
+      bool nok[NBF];
+      for (int jl = first_set; jl < p.nl; ++jl) {
+        if (!((c >> jl) & 1)) continue;
+        int nx = jl + 1;
+        while (nx < p.nl && !((c >> nx) & 1)) ++nx;
+        load_node(nx, jl, nhi, nlo, nok);
+        const float dj = __expf(dlow);
+#pragma unroll
+        for (int b = 0; b < QT::RBW; ++b) {
+          const int R = QT::rb(w, b);
+          float scl[4], part[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = R * 16 + 4 * g4 + r;
+            scl[r] = ch.lam[i * kLamCap + J + 1 + jl] * ch.ea[i] * dj;
+            part[r] = 0.f;
+          }
+#pragma unroll
+          for (int a = 0; a < QT::TA; ++a) {
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < NKS; ++kb) {
+              const Frag<T> ao_ = frag_row<T, DV>(ch.o, CH::RV, R * 16 + jj, kb * 32 + 8 * g4);
+              const int f = a * NKS + kb;
+              mma(y, ao_, bok[f] ? bhi[f] : zero_frag<T>());
+              if constexpr (SPLIT) mma(y, ao_, bok[f] ? blo[f] : zero_frag<T>());
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = R * 16 + 4 * g4 + r;
+              aq[a * QT::RBW + b][r] += scl[r] * y[r];
+              part[r] += y[r] * to_f(ch.q[i * CH::RK + QT::t(w, a) * 16 + jj]);
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float sum = sum16(part[r]);
+            if (jj == r) red[(w * p.nl + kn) * C + R * 16 + 4 * g4 + r] = sum;
+          }
+        }
+#pragma unroll
+        for (int f = 0; f < NBF; ++f) {
+          bhi[f] = nhi[f];
+          if constexpr (SPLIT) blo[f] = nlo[f];
+          bok[f] = nok[f];
+        }
+        dlow += gs[slot_of(p.N, jl, (c >> jl) - 1)];
+        ++kn;
+      }
+    }
+    // the waves' shares summed in wave order, one position per thread: dlambda of each node
+    // level (parked as above) and q . (dq from the nodes) for dA
+    __syncthreads();
+    if (tid < C) {
+      const int i = tid, R = i >> 4;
+      float dl = 0.f, acc = 0.f;
+      int kn = 0;
+      for (int jl = first_set; jl < p.nl; ++jl) {
+        if (!((c >> jl) & 1)) continue;
+        float sum = 0.f;
+        for (int u = 0; u < NW; ++u)
+          if (QT::holds(u, R)) sum += red[(u * p.nl + kn) * C + i];
+        const float e = ch.ea[i] * __expf(dl);
+        acc += ch.lam[i * kLamCap + J + 1 + jl] * e * sum;
+        ch.lam[i * kLamCap + J + 1 + jl] = e * sum;
+        dl += gs[slot_of(p.N, jl, (c >> jl) - 1)];
+        ++kn;
+      }
+      dqd[i] = acc;
+    }
   }
 
   // 5. the stores: dq, dk, dv go through the q, k, v images (no longer read) so that every
@@ -1195,6 +1350,15 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   //    - k . (dk from the later chunks)
   __syncthreads();
 #pragma unroll
+  for (int a = 0; a < (COLQ ? QT::TA : 1); ++a)
+#pragma unroll
+    for (int b = 0; b < (COLQ ? QT::RBW : NK); ++b) {
+      const int R = COLQ ? QT::rb(w, b) : w, t = COLQ ? QT::t(w, a) : b;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        ch.q[(R * 16 + 4 * g4 + r) * CH::RK + t * 16 + jj] = (T)aq[COLQ ? a * QT::RBW + b : b][r];
+    }
+#pragma unroll
   for (int x = 0; x < RB; ++x) {
     const int rb = w + NW * x;
 #pragma unroll
@@ -1202,7 +1366,6 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = rb * 16 + 4 * g4 + r, a = t * 16 + jj;
-        ch.q[i * CH::RK + a] = (T)aq[x][t][r];
         ch.k[i * CH::RK + a] = (T)ak[x][t][r];
       }
 #pragma unroll
@@ -1237,12 +1400,12 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
       const int i = rb * 16 + 4 * g4 + r;
       float colsum = 0.f;
       for (int u = 0; u < NW; ++u) colsum += colp[u * C + i];
-      const float sum = sum16(rowg[r] - pk[r]) + dq_dot[r] - colsum;
+      const float sum = sum16(rowg[r] - pk[r]) + dqd[i] - colsum;
       if (jj == r && i < nv) p.dA[row0 + i] = sum;
     }
 
-    // 6. dlambda of this block's rows: levels 0..J from the bins, the levels of step 4's node
-    //    read-outs from where it parked them, zero for every other level (lane jj writes levels
+    // 6. dlambda of this block's rows: levels 0..J and the levels of step 4's node read-outs
+    //    from where steps 1 and 4 parked them, zero for every other level (lane jj writes levels
     //    jj, jj + 16)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1251,9 +1414,7 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
       for (int l = jj; l < p.L; l += 16) {
         float val = 0.f;
         if (l <= J) {
-#pragma unroll
-          for (int q = 0; q <= J; ++q)
-            if (q == l) val = bins[x][r][q];
+          val = ch.lam[i * kLamCap + l];
         } else {
           const int jl = l - J - 1;
           if (jl < p.nl && ((c >> jl) & 1)) val = ch.lam[i * kLamCap + l];

@@ -563,6 +563,12 @@ int make_bwd_plan(int B, int H, int T, int dk, int dv, int chunk, int dtype, Bwd
   pl.smem_states = lla::bwd::bwd_smem(pl.esize, C, dk, dv, false).total;
   pl.smem_grads = grads_smem(pl.esize, C, dk, dv);
   if (pl.smem_grads > kLdsPerWorkgroup) return LLA_ERR_UNSUPPORTED;
+  {
+    // the gradient kernel's per-wave dlambda shares of the node levels, in its score images
+    const lla::bwd::BwdSmem g = lla::bwd::bwd_smem(pl.esize, C, dk, dv, true);
+    const int nw = C >= 64 ? 4 : C / 16;
+    if ((long long)nw * pl.nl * C * 4 > g.lam - g.p1) return LLA_ERR_UNSUPPORTED;
+  }
   return LLA_OK;
 }
 
