@@ -434,27 +434,26 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
 // ----------------------------------------------------------------------------------------
 
 __global__ void __launch_bounds__(256) bwd_dloga_kernel(BwdParams p) {
-  __shared__ float part[256];
-  const int bh = blockIdx.x, tid = threadIdx.x;
+  __shared__ float wtot[4];
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int per = (p.T + 255) / 256;
-  const int lo = tid * per, hi = min(p.T, lo + per);
+  const int lo = min(p.T, tid * per), hi = min(p.T, lo + per);
   const float* dA = p.dA + (size_t)bh * p.T;
   float* out = p.glog_a + (size_t)bh * p.T;
   float s = 0.f;
   for (int t = hi - 1; t >= lo; --t) s += dA[t];
-  part[tid] = s;
-  __syncthreads();
-  // suffix of the segment sums: threads above this one
-  if (tid == 0) {
-    float run = 0.f;
-    for (int u = 255; u >= 0; --u) {
-      const float x = part[u];
-      part[u] = run;
-      run += x;
-    }
+  // exclusive suffix of the segment sums over the threads above this one, in a fixed order:
+  // inside a wave by shuffles, across the 4 waves through shared memory
+  float incl = s;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const float y = __shfl_down(incl, d);
+    if (lane + d < 64) incl += y;
   }
+  if (lane == 0) wtot[w] = incl;
   __syncthreads();
-  float run = part[tid];
+  float run = incl - s;
+  for (int u = 3; u > w; --u) run += wtot[u];
   for (int t = hi - 1; t >= lo; --t) {
     run += dA[t];
     out[t] = run;
