@@ -261,6 +261,17 @@ __device__ __forceinline__ float dpp_f(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+// a wave-uniform global address as the compiler's uniform value (both halves read from lane 0;
+// global address space): an access at it plus a lane offset then takes the scalar-base form
+// instead of a 64-bit address per lane
+template <typename P>
+__device__ __forceinline__ __attribute__((address_space(1))) P* uniform_ptr(P* ptr) {
+  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (__attribute__((address_space(1))) P*)(((uint64_t)hi << 32) | lo);
+}
+
 // sum over the 16 lanes of a row (lane & 15 varies), in every lane: pairs, quads, then the
 // quads 4 and 8 lanes around the row
 __device__ __forceinline__ float sum16(float x) {
@@ -274,6 +285,7 @@ __device__ __forceinline__ float sum16(float x) {
 // kernel table of one (dtype, chunk, dk, dv)
 struct BwdKernels {
   const void* states;   // bwd_states_kernel<T, C, DK, DV>
+  const void* statesg;  // bwd_statesg_kernel<T, C, DK, DV> where its states fit, else null
   const void* rn;       // bwd_rn_kernel<T, C, DK, DV>
   const void* rng;      // bwd_rng_kernel<T, C, DK, DV> where its accumulators fit, else null
   const void* grads;    // bwd_grads_kernel<T, C, DK, DV>
@@ -548,6 +560,202 @@ bwd_states_kernel(BwdParams p) {
   outer_store<T, C, DK, DV, NW>(ch.k, CH::RK, ch.v, CH::RV, ch.ws,
                                 p.node + ((size_t)bh * p.nslot + c) * SZ, w, lane);
   if (tid == 0) p.gsum[(size_t)bh * p.nslot + c] = ch.g;
+}
+
+// ----------------------------------------------------------------------------------------
+// bwd_statesg: the chunk states by groups of 8 chunks (a sub-block of level 3) and head, with
+// the group's part of the forward nodes' up-sweep. Chunk by chunk, F(c) on MFMA; then in
+// registers node(1, m) = exp(G(0, 2m+1)) node(0, 2m) + node(0, 2m+1), and the same for levels
+// 2 and 3 (chunks past N are zero states with zero decay, so a block without its right half
+// keeps its left one; the block decays are formed as bwd_gsum forms them). Every even node of
+// levels 0..3 is written as the gradient kernel's MFMA operands (element type; bf16 as high and
+// low parts), the group itself (level 3) also in fp32 for the levels above it; g_c into the
+// block decays. Used with bwd_gtree, where its four states fit the registers.
+// ----------------------------------------------------------------------------------------
+
+template <typename T, int C, int DK, int DV>
+__global__ void __launch_bounds__(64 * Waves<C>::NW) __attribute__((amdgpu_waves_per_eu(2)))
+bwd_statesg_kernel(BwdParams p) {
+  constexpr int NW = Waves<C>::NW, NT = 64 * NW;
+  using TM = ScaledTiles<DK, DV, NW>;
+  constexpr int TPW = TM::TPW;
+  constexpr int ES = (int)sizeof(T), EPV = 16 / ES;
+  constexpr int PK = C * DK / EPV, PV = C * DV / EPV;        // 16-byte pieces of the k, v rows
+  constexpr int NKP = cdiv(PK, NT), NVP = cdiv(PV, NT);
+  constexpr bool SPLIT = ES == 2;
+  using CH = Chunk<T, C, DK, DV>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
+  const int ng = (p.N + 7) >> 3;
+  // one-dimensional grid in XCD order, as in bwd_grads
+  const int Lw = blockIdx.x, q8 = Lw >> 3;
+  const bool xcd = (p.BH & 7) == 0;
+  const int g = xcd ? q8 % ng : Lw % ng;
+  const int bh = xcd ? ((q8 / ng) << 3) + (Lw & 7) : Lw / ng;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, jj = lane & 15, g4 = lane >> 4;
+  const int c0 = g << 3, c1 = min(c0 + 8, p.N);
+  const BwdSmem Lo = bwd_smem(ES, C, DK, DV, false);
+  CH ch;
+  ch.bind(sm, Lo);
+  const size_t SZ = (size_t)DK * DV;
+  T* ne = reinterpret_cast<T*>(p.node_e) + (size_t)bh * p.nslot * SZ;
+  T* nlo = reinterpret_cast<T*>(p.node_lo) + (size_t)bh * p.nslot * SZ;
+  float* gsum = p.gsum + (size_t)bh * p.nslot;
+  auto nb = [&](int i) { return (p.N + (1 << i) - 1) >> i; };
+  // the wave's tiles of a state into slot s, as MFMA operands in the element type (a uniform
+  // base per tile and row step, the lane's offset added last)
+  const unsigned lofs = (unsigned)(4 * g4 * DV + jj);
+  auto put = [&](int s, const f32x4* X) {
+#pragma unroll
+    for (int ya = 0; ya < TM::YPW; ++ya)
+#pragma unroll
+      for (int b = 0; b < TM::APW; ++b) {
+        const int a0 = TM::ab(w, b);
+        if (a0 >= DK / 16) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const size_t at = (size_t)s * SZ + (size_t)(a0 * 16 + r) * DV + TM::y(w, ya) * 16;
+          const float x = X[ya * TM::APW + b][r];
+          const T hv = (T)x;
+          uniform_ptr(ne + at)[lofs] = hv;
+          if constexpr (SPLIT) uniform_ptr(nlo + at)[lofs] = (T)(x - (float)hv);
+        }
+      }
+  };
+
+  // the next chunk's k and v rows and log_a, in registers (unconditional, clamped)
+  u32x4 rk[NKP], rv[NVP];
+  float rla = 0.f;
+  auto fetch = [&](int c) {
+    const int nv = min(C, p.T - c * C);
+    const size_t row0 = (size_t)bh * p.T + (size_t)c * C;
+    const u32x4* gk = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(p.k) + row0 * DK);
+    const u32x4* gv = reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(p.v) + row0 * DV);
+#pragma unroll
+    for (int u = 0; u < NKP; ++u) {
+      const int idx = min(tid + u * NT, PK - 1);
+      rk[u] = gk[min(idx / (DK / EPV), nv - 1) * (DK / EPV) + idx % (DK / EPV)];
+    }
+#pragma unroll
+    for (int u = 0; u < NVP; ++u) {
+      const int idx = min(tid + u * NT, PV - 1);
+      rv[u] = gv[min(idx / (DV / EPV), nv - 1) * (DV / EPV) + idx % (DV / EPV)];
+    }
+    rla = p.log_a[row0 + min(lane, nv - 1)];
+  };
+  fetch(c0);
+  f32x4 F[TPW], K0[TPW], K1[TPW], K2[TPW];
+  float gl0 = 0.f, G1L = 0.f, G2L = 0.f;   // decays of the left chunk, pair and quad
+#pragma unroll 1
+  for (int l = 0; l < 8; ++l) {
+    const int c = c0 + l;
+    float gc = 0.f;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) F[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (c < c1) {
+      const int nv = min(C, p.T - c * C);
+      if (l > 0) __syncthreads();   // the previous chunk's images are no longer read
+#pragma unroll
+      for (int u = 0; u < NKP; ++u) {
+        const int idx = tid + u * NT;
+        if (idx < PK) {
+          const int r = idx / (DK / EPV), f = (idx % (DK / EPV)) * EPV;
+          *reinterpret_cast<u32x4*>(ch.k + r * CH::RK + f) = r < nv ? rk[u] : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NVP; ++u) {
+        const int idx = tid + u * NT;
+        if (idx < PV) {
+          const int r = idx / (DV / EPV), f = (idx % (DV / EPV)) * EPV;
+          *reinterpret_cast<u32x4*>(ch.v + r * CH::RV + f) = r < nv ? rv[u] : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      // every wave scans the chunk's log_a; wave 0 writes the weights exp(g_c - A_s)
+      float incl = lane < nv ? rla : 0.f;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const float y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+      }
+      gc = __shfl(incl, 63);
+      if (w == 0 && lane < C) ch.ws[lane] = __expf(gc - incl);
+      __syncthreads();
+      if (c + 1 < c1) fetch(c + 1);
+      // F(c) = k^T (ws * v), the wave's tiles
+#pragma unroll
+      for (int s0 = 0; s0 < C; s0 += 32) {
+        const int k = s0 + 8 * g4;
+        Frag<T> a[TM::APW];
+#pragma unroll
+        for (int b = 0; b < TM::APW; ++b) {
+          const int ab = TM::ab(w, b);
+          a[b] = ab < DK / 16 ? frag_col<T, C>(ch.k, CH::RK, k, ab * 16 + jj) : zero_frag<T>();
+        }
+#pragma unroll
+        for (int ya = 0; ya < TM::YPW; ++ya) {
+          const Frag<T> uy = frag_col<T, C>(ch.v, CH::RV, k, TM::y(w, ya) * 16 + jj);
+          f32x4 ulo, uhi;
+          frag_to_f32(uy, ulo, uhi);
+          Frag<T> bh_, bl_;
+          scale_split<T>(ulo, uhi, ch.ws + (k < C ? k : 0), bh_, bl_);
+#pragma unroll
+          for (int b = 0; b < TM::APW; ++b) {
+            mma(F[ya * TM::APW + b], a[b], bh_);
+            if constexpr (SPLIT) mma(F[ya * TM::APW + b], a[b], bl_);
+          }
+        }
+      }
+      if (tid == 0) gsum[c] = gc;
+    }
+    // the group's up-sweep (levels 0..3): even nodes out, the left halves kept
+    if (!(l & 1)) {
+      if (c < c1) put(c, F);
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) K0[i] = F[i];
+      gl0 = gc;
+      continue;
+    }
+    const float eg1 = __expf(gc);
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) F[i][r] = eg1 * K0[i][r] + F[i][r];   // node(1, c >> 1)
+    const float G1 = c < c1 ? gl0 + gc : gl0;
+    const int m1 = c >> 1;
+    if (!(l & 2)) {
+      if (1 < p.nl && m1 < nb(1)) put(slot_of(p.N, 1, m1), F);
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) K1[i] = F[i];
+      G1L = G1;
+      continue;
+    }
+    const bool right1 = (m1 < nb(1));   // the right pair holds at least one chunk
+    const float eg2 = __expf(right1 ? G1 : 0.f);
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) F[i][r] = eg2 * K1[i][r] + F[i][r];   // node(2, c >> 2)
+    const float G2 = right1 ? G1L + G1 : G1L;
+    const int m2 = c >> 2;
+    if (!(l & 4)) {
+      if (2 < p.nl && m2 < nb(2)) put(slot_of(p.N, 2, m2), F);
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) K2[i] = F[i];
+      G2L = G2;
+      continue;
+    }
+    const bool right2 = (m2 < nb(2));
+    const float eg3 = __expf(right2 ? G2 : 0.f);
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) F[i][r] = eg3 * K2[i][r] + F[i][r];   // the group: node(3, g)
+    if (3 < p.nl) {
+      if (!(g & 1)) put(slot_of(p.N, 3, g), F);
+      TM::template store<DV>(p.node + ((size_t)bh * p.nslot + slot_of(p.N, 3, g)) * SZ, F, w, lane);
+    }
+  }
+  (void)G2L;
 }
 
 // ----------------------------------------------------------------------------------------
@@ -1443,8 +1651,12 @@ namespace bwd {
 template <typename TY, int C, int DK, int DV>
 BwdKernels make_bwd() {
   const void* rng = nullptr;
-  if constexpr (rng_fits<C, DK, DV>()) rng = reinterpret_cast<const void*>(&bwd_rng_kernel<TY, C, DK, DV>);
-  return BwdKernels{reinterpret_cast<const void*>(&bwd_states_kernel<TY, C, DK, DV>),
+  const void* sg = nullptr;
+  if constexpr (rng_fits<C, DK, DV>()) {
+    rng = reinterpret_cast<const void*>(&bwd_rng_kernel<TY, C, DK, DV>);
+    sg = reinterpret_cast<const void*>(&bwd_statesg_kernel<TY, C, DK, DV>);
+  }
+  return BwdKernels{reinterpret_cast<const void*>(&bwd_states_kernel<TY, C, DK, DV>), sg,
                     reinterpret_cast<const void*>(&bwd_rn_kernel<TY, C, DK, DV>), rng,
                     reinterpret_cast<const void*>(&bwd_grads_kernel<TY, C, DK, DV>)};
 }

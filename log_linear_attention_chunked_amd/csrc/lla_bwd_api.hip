@@ -219,17 +219,6 @@ constexpr int kGrpLog = 3;            // 8 chunks per group
 static_assert(kGrpLog == kSubLog, "a group is one of bwd_rn's sub-blocks");
 constexpr int kGtCt = 6;              // levels >= 4 whose contributions a wave prefetches
 
-// a wave-uniform global address as the compiler's uniform value (both halves read from lane 0;
-// global address space): an access at it plus a lane offset then takes the scalar-base form
-// instead of a 64-bit address per lane
-template <typename P>
-__device__ __forceinline__ __attribute__((address_space(1))) P* uniform_ptr(P* ptr) {
-  const uint64_t a = reinterpret_cast<uint64_t>(ptr);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  return (__attribute__((address_space(1))) P*)(((uint64_t)hi << 32) | lo);
-}
-
 // first float of level i's block values (3 <= i <= nl) and of level i's contributions
 // (4 <= i <= nl; i = nl gives the total), after the nslot block decays
 __host__ __device__ inline int gtree_lv(int N, int nslot, int i) {
@@ -246,7 +235,9 @@ __host__ __device__ inline int gtree_floats(int N, int nl, int nslot) {
   return gtree_ct(N, nl, nslot, nl > 4 ? nl : 4);
 }
 
-template <typename E>
+// GROUPED: bwd_statesg has done levels 0..3 of every group (nodes written, the group in fp32 at
+// its level-3 slot); the tree then starts from the groups
+template <typename E, bool GROUPED>
 __global__ void __launch_bounds__(64 * kTreeWaves) __attribute__((amdgpu_waves_per_eu(8)))
 bwd_gtree_kernel(BwdParams p, int SZ) {
   extern __shared__ __attribute__((aligned(16))) float tl[];
@@ -287,8 +278,12 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
   };
   auto load_group = [&](int g, GLoads& d) {
     const int c0 = g << kGrpLog;
+    if constexpr (GROUPED) {
+      d.x[0] = ld(nd, 3 < nl ? slot_of(N, 3, g) : 0);
+    } else {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) d.x[k] = ld(nd, min(c0 + k, N - 1));
+      for (int k = 0; k < 8; ++k) d.x[k] = ld(nd, min(c0 + k, N - 1));
+    }
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const int sb = c0 + 2 * h + 1;                       // level 0: chunk 2h+1 of the group
@@ -321,6 +316,10 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
 
   // up-sweep inside a group, contributions, and the group's value at level 3
   auto up_group = [&](int g, const GLoads& d) {
+    if constexpr (GROUPED) {
+      if (3 < nl) tl[gtree_lv(N, p.nslot, 3) + g * 64 + lane] = d.x[0];
+      return;
+    }
     const int c0 = g << kGrpLog;
     float x[8], y1[4], y2[2];
 #pragma unroll
@@ -645,13 +644,23 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
 
   if (mark(0) != hipSuccess) return LLA_ERR_HIP;
   if (pl.nl > 0) {
-    if (set_smem(ks->states, pl.smem_states) != hipSuccess) return LLA_ERR_HIP;
-    if (hipLaunchKernel(ks->states, chunks, dim3(NT), args, pl.smem_states, stream) != hipSuccess)
-      return LLA_ERR_HIP;
+    // the chunk states: by groups of 8 chunks with the groups' part of the up-sweep when the
+    // group tree runs and the kernel exists for the shape, else one workgroup per chunk
+    const bool grouped = pl.gtree_smem > 0 && ks->statesg;
+    const long long ng = (pl.N + 7) / 8;
+    if (grouped) {
+      if (set_smem(ks->statesg, pl.smem_states) != hipSuccess) return LLA_ERR_HIP;
+      if (hipLaunchKernel(ks->statesg, dim3((unsigned)(ng * pl.BH)), dim3(NT), args, pl.smem_states,
+                          stream) != hipSuccess)
+        return LLA_ERR_HIP;
+    } else {
+      if (set_smem(ks->states, pl.smem_states) != hipSuccess) return LLA_ERR_HIP;
+      if (hipLaunchKernel(ks->states, chunks, dim3(NT), args, pl.smem_states, stream) != hipSuccess)
+        return LLA_ERR_HIP;
+    }
     // the target-side sub-block states: one workgroup per group of 8 chunks where its
     // accumulators fit, else one per sub-block and level
     if (ks->rng) {
-      const long long ng = (pl.N + 7) / 8;
       if (set_smem(ks->rng, pl.smem_states) != hipSuccess) return LLA_ERR_HIP;
       if (hipLaunchKernel(ks->rng, dim3((unsigned)(ng * pl.BH)), dim3(NT), args, pl.smem_states,
                           stream) != hipSuccess)
@@ -670,13 +679,14 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
     const dim3 tgrid((unsigned)(SZ / 64), (unsigned)pl.BH), tblock(64 * lla::bwd::kTreeWaves);
     const bool bf = a.dtype == LLA_DTYPE_BF16;
     if (pl.gtree_smem > 0) {
-      const void* fn = bf ? reinterpret_cast<const void*>(&lla::bwd::bwd_gtree_kernel<lla::bf16>)
-                          : reinterpret_cast<const void*>(&lla::bwd::bwd_gtree_kernel<float>);
+      using namespace lla::bwd;
+      const void* fn = grouped ? (bf ? reinterpret_cast<const void*>(&bwd_gtree_kernel<lla::bf16, true>)
+                                     : reinterpret_cast<const void*>(&bwd_gtree_kernel<float, true>))
+                               : (bf ? reinterpret_cast<const void*>(&bwd_gtree_kernel<lla::bf16, false>)
+                                     : reinterpret_cast<const void*>(&bwd_gtree_kernel<float, false>));
       if (set_smem(fn, pl.gtree_smem) != hipSuccess) return LLA_ERR_HIP;
-      if (bf)
-        hipLaunchKernelGGL((lla::bwd::bwd_gtree_kernel<lla::bf16>), tgrid, tblock, pl.gtree_smem, stream, p, SZ);
-      else
-        hipLaunchKernelGGL((lla::bwd::bwd_gtree_kernel<float>), tgrid, tblock, pl.gtree_smem, stream, p, SZ);
+      void* targs[] = {&p, const_cast<int*>(&SZ)};
+      if (hipLaunchKernel(fn, tgrid, tblock, targs, pl.gtree_smem, stream) != hipSuccess) return LLA_ERR_HIP;
     } else if (bf) {
       hipLaunchKernelGGL((lla::bwd::bwd_tree_kernel<lla::bf16>), tgrid, tblock, 0, stream, p, SZ);
     } else {
