@@ -272,6 +272,10 @@ __device__ __forceinline__ __attribute__((address_space(1))) P* uniform_ptr(P* p
   return (__attribute__((address_space(1))) P*)(((uint64_t)hi << 32) | lo);
 }
 
+// x from lane (lane ^ 4) of the same row: half_mirror (lane 7 - i of each 8) then quad_perm
+// [3,2,1,0] (lane i ^ 3)
+__device__ __forceinline__ float dpp_xor4(float x) { return dpp_f<0x1B>(dpp_f<0x141>(x)); }
+
 // sum over the 16 lanes of a row (lane & 15 varies), in every lane: pairs, quads, then the
 // quads 4 and 8 lanes around the row
 __device__ __forceinline__ float sum16(float x) {
@@ -1306,20 +1310,34 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
             if (l == lv) bins[x][r][l] += su;
         }
       } else if (cb == rb) {
+        // levels 0..4 lie inside this diagonal tile: with u_j the row's value at lane j, the
+        // partial sums P1_x = u_x + u_{x^1}, P2_x = P1_x + P1_{x^2}, P3_x = P2_x + P2_{x^4} give
+        // row i (= 4 g4 + r, local) its level sums at lane i: u_i, u_{i^1}, P1_{i^2}, P2_{i^4},
+        // P3_{i^8} (u is zero above the diagonal); that lane parks them in the lambda rows'
+        // slots of those levels (read already, by this wave only) until step 6 stores them
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int lv = bit_length((unsigned)((4 * g4 + r) ^ jj));
-#pragma unroll
-          for (int l = 0; l <= 4 && l <= J; ++l) bins[x][r][l] += sum16(lv == l ? u[r] : 0.f);
+          const float v = u[r];
+          const float p1 = v + dpp_f<0xB1>(v);
+          const float p2 = p1 + dpp_f<0x4E>(p1);
+          const float p3 = p2 + dpp_xor4(p2);
+          const float s1 = dpp_f<0xB1>(v), s2 = dpp_f<0x4E>(p1), s3 = dpp_xor4(p2), s4 = dpp_f<0x128>(p3);
+          if (jj == 4 * g4 + r) {
+            float* dl = ch.lam + (rb * 16 + jj) * kLamCap;
+            dl[0] = v;
+            dl[1] = s1;
+            dl[2] = s2;
+            dl[3] = s3;
+            dl[4] = s4;
+          }
         }
       }
     }
-    // dlambda of the levels inside the chunk, parked in the lambda rows' slots of those levels
-    // (this wave's rows; step 1 has read them) until step 6 stores them
+    // dlambda of the levels across the diagonal tiles (5..J), parked the same way
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int l = 0; l <= J; ++l)
+      for (int l = 5; l <= J; ++l)
         if (jj == l) ch.lam[(rb * 16 + 4 * g4 + r) * kLamCap + l] = bins[x][r][l];
   }
   __syncthreads();
