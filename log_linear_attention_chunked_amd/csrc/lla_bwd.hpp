@@ -79,7 +79,13 @@ struct BwdParams {
   int BH, T, L, N, nl, nslot;
   int items;                  // sub-blocks per head over all levels
   int rn_off[kLamCap + 1];    // first sub-block of each level
+  int lvl[kLamCap + 1];       // first tree slot of each level (slot_of(N, i, 0))
+  int gtlv[kLamCap + 1];      // bwd_gtree: first float of level i's block values (i >= 3)
+  int gtct[kLamCap + 1];      // bwd_gtree: first float of level i's contributions (i >= 4)
 };
+
+// slot of block (i, m) from the level offsets the host computed (no loop over the levels)
+__device__ __forceinline__ int slot_p(const BwdParams& p, int i, int m) { return p.lvl[i] + m; }
 
 // lambda element i (float32, or bfloat16 widened exactly)
 __device__ __forceinline__ float lambda_at(const BwdParams& p, size_t i) {
@@ -727,7 +733,7 @@ bwd_statesg_kernel(BwdParams p) {
     const float G1 = c < c1 ? gl0 + gc : gl0;
     const int m1 = c >> 1;
     if (!(l & 2)) {
-      if (1 < p.nl && m1 < nb(1)) put(slot_of(p.N, 1, m1), F);
+      if (1 < p.nl && m1 < nb(1)) put(slot_p(p, 1, m1), F);
 #pragma unroll
       for (int i = 0; i < TPW; ++i) K1[i] = F[i];
       G1L = G1;
@@ -742,7 +748,7 @@ bwd_statesg_kernel(BwdParams p) {
     const float G2 = right1 ? G1L + G1 : G1L;
     const int m2 = c >> 2;
     if (!(l & 4)) {
-      if (2 < p.nl && m2 < nb(2)) put(slot_of(p.N, 2, m2), F);
+      if (2 < p.nl && m2 < nb(2)) put(slot_p(p, 2, m2), F);
 #pragma unroll
       for (int i = 0; i < TPW; ++i) K2[i] = F[i];
       G2L = G2;
@@ -755,8 +761,8 @@ bwd_statesg_kernel(BwdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) F[i][r] = eg3 * K2[i][r] + F[i][r];   // the group: node(3, g)
     if (3 < p.nl) {
-      if (!(g & 1)) put(slot_of(p.N, 3, g), F);
-      TM::template store<DV>(p.node + ((size_t)bh * p.nslot + slot_of(p.N, 3, g)) * SZ, F, w, lane);
+      if (!(g & 1)) put(slot_p(p, 3, g), F);
+      TM::template store<DV>(p.node + ((size_t)bh * p.nslot + slot_p(p, 3, g)) * SZ, F, w, lane);
     }
   }
   (void)G2L;
@@ -1192,7 +1198,7 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   u32x4 pf[PF ? NPF : 1], pf2[PF && SPLIT ? NPF : 1];
   auto prefetch = [&](int jl, int cur) {
     if (jl >= p.nl) jl = cur;
-    const size_t off = (size_t)slot_of(p.N, jl, max((c >> jl) - 1, 0)) * SZ;
+    const size_t off = (size_t)slot_p(p, jl, max((c >> jl) - 1, 0)) * SZ;
     const u32x4* src = reinterpret_cast<const u32x4*>(node_e + off);
     const u32x4* src2 = reinterpret_cast<const u32x4*>(node_lo + off);
 #pragma unroll
@@ -1208,7 +1214,7 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   constexpr int NBF = QT::TA * NKS;                      // operand fragments per node
   auto load_node = [&](int jl, int cur, Frag<T>* hi, Frag<T>* lo, bool* ok) {
     if (jl >= p.nl) jl = cur;
-    const size_t off = (size_t)slot_of(p.N, jl, max((c >> jl) - 1, 0)) * SZ;
+    const size_t off = (size_t)slot_p(p, jl, max((c >> jl) - 1, 0)) * SZ;
 #pragma unroll
     for (int a = 0; a < QT::TA; ++a)
 #pragma unroll
@@ -1447,7 +1453,7 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
     const int rb = w;
     for (int jl = first_set; jl < p.nl; ++jl) {
       if (!((c >> jl) & 1)) continue;
-      const int sl = slot_of(p.N, jl, (c >> jl) - 1);
+      const int sl = slot_p(p, jl, (c >> jl) - 1);
       __syncthreads();   // the previous reads of the state image are done
       put(Nst, pf);
       if constexpr (SPLIT) put(Plo, pf2);
@@ -1544,7 +1550,7 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
           if constexpr (SPLIT) blo[f] = nlo[f];
           bok[f] = nok[f];
         }
-        dlow += gs[slot_of(p.N, jl, (c >> jl) - 1)];
+        dlow += gs[slot_p(p, jl, (c >> jl) - 1)];
         ++kn;
       }
     }
@@ -1563,7 +1569,7 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
         const float e = ch.ea[i] * __expf(dl);
         acc += ch.lam[i * kLamCap + J + 1 + jl] * e * sum;
         ch.lam[i * kLamCap + J + 1 + jl] = e * sum;
-        dl += gs[slot_of(p.N, jl, (c >> jl) - 1)];
+        dl += gs[slot_p(p, jl, (c >> jl) - 1)];
         ++kn;
       }
       dqd[i] = acc;

@@ -23,7 +23,7 @@ __global__ void __launch_bounds__(256) bwd_gsum_kernel(BwdParams p) {
   float* gs = p.gsum + (size_t)bh * p.nslot;
   for (int i = 1; i < p.nl; ++i) {
     const int nprev = (p.N + (1 << (i - 1)) - 1) >> (i - 1), nb = (p.N + (1 << i) - 1) >> i;
-    const int o_prev = slot_of(p.N, i - 1, 0), o = slot_of(p.N, i, 0);
+    const int o_prev = p.lvl[i - 1], o = p.lvl[i];
     for (int m = threadIdx.x; m < nb; m += blockDim.x) {
       const float l = gs[o_prev + 2 * m];
       gs[o + m] = 2 * m + 1 < nprev ? l + gs[o_prev + 2 * m + 1] : l;
@@ -88,7 +88,7 @@ bwd_tree_kernel(BwdParams p, int SZ) {
   __syncthreads();
   for (int i = 1; i < p.nl; ++i) {
     const int nprev = (p.N + (1 << (i - 1)) - 1) >> (i - 1), nb = (p.N + (1 << i) - 1) >> i;
-    const int o_prev = slot_of(p.N, i - 1, 0), o = slot_of(p.N, i, 0);
+    const int o_prev = p.lvl[i - 1], o = p.lvl[i];
     for (int m0 = w; m0 < nb; m0 += kTreeWaves * KB) {
       // both children of KB blocks (clamped to valid slots of level i-1) before any is used
       float lhs[KB], rhs[KB];
@@ -119,7 +119,7 @@ bwd_tree_kernel(BwdParams p, int SZ) {
   // sub-blocks at a time, their loads again issued together.
   auto fetch = [&](int i, int m0, float (&rn)[KB]) {
     const int nb = (p.N + (1 << i) - 1) >> i;
-    const int s = sub_log(i), b = i - s, os = slot_of(p.N, s, 0);
+    const int s = sub_log(i), b = i - s, os = p.lvl[s];
     const int nsub = (p.N + (1 << s) - 1) >> s;
     const int nit = items_of_level(p.N, i);
     const float* rpl = rp + (size_t)p.rn_off[i] * SZ;
@@ -168,9 +168,9 @@ bwd_tree_kernel(BwdParams p, int SZ) {
     for (int u = 0; u < KB; ++u) rn_first[u] = rn_next[u];
     if (i > 0) fetch(i - 1, w, rn_next);
     const int nb = (p.N + (1 << i) - 1) >> i;
-    const int o = slot_of(p.N, i, 0);
+    const int o = p.lvl[i];
     const bool top = i + 1 >= p.nl;
-    const int op = top ? 0 : slot_of(p.N, i + 1, 0);
+    const int op = top ? 0 : p.lvl[i + 1];
     for (int m0 = w; m0 < nb; m0 += kTreeWaves * KB) {
       float rn[KB];
       if (m0 == w) {
@@ -279,7 +279,7 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
   auto load_group = [&](int g, GLoads& d) {
     const int c0 = g << kGrpLog;
     if constexpr (GROUPED) {
-      d.x[0] = ld(nd, 3 < nl ? slot_of(N, 3, g) : 0);
+      d.x[0] = ld(nd, 3 < nl ? slot_p(p, 3, g) : 0);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) d.x[k] = ld(nd, min(c0 + k, N - 1));
@@ -312,12 +312,12 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
   for (int i = threadIdx.x + 64 * kTreeWaves; i < p.nslot; i += 64 * kTreeWaves) gs[i] = gsg[i];
   __syncthreads();
   // decay of block m at level i (0 where the block does not exist: it then holds zeros)
-  auto G = [&](int i, int m) { return (i < nl && m < nb(i)) ? gs[slot_of(N, i, m)] : 0.f; };
+  auto G = [&](int i, int m) { return (i < nl && m < nb(i)) ? gs[slot_p(p, i, m)] : 0.f; };
 
   // up-sweep inside a group, contributions, and the group's value at level 3
   auto up_group = [&](int g, const GLoads& d) {
     if constexpr (GROUPED) {
-      if (3 < nl) tl[gtree_lv(N, p.nslot, 3) + g * 64 + lane] = d.x[0];
+      if (3 < nl) tl[p.gtlv[3] + g * 64 + lane] = d.x[0];
       return;
     }
     const int c0 = g << kGrpLog;
@@ -335,11 +335,11 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
       if (0 < nl && c0 + 2 * h < N) put(ne, nlo, (size_t)(c0 + 2 * h) * SZ, x[2 * h]);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      if (1 < nl && 4 * g + 2 * h < nb(1)) put(ne, nlo, (size_t)slot_of(N, 1, 4 * g + 2 * h) * SZ, y1[2 * h]);
-    if (2 < nl && 2 * g < nb(2)) put(ne, nlo, (size_t)slot_of(N, 2, 2 * g) * SZ, y2[0]);
+      if (1 < nl && 4 * g + 2 * h < nb(1)) put(ne, nlo, (size_t)slot_p(p, 1, 4 * g + 2 * h) * SZ, y1[2 * h]);
+    if (2 < nl && 2 * g < nb(2)) put(ne, nlo, (size_t)slot_p(p, 2, 2 * g) * SZ, y2[0]);
     if (3 < nl) {
-      if (!(g & 1)) put(ne, nlo, (size_t)slot_of(N, 3, g) * SZ, y3);
-      tl[gtree_lv(N, p.nslot, 3) + g * 64 + lane] = y3;
+      if (!(g & 1)) put(ne, nlo, (size_t)slot_p(p, 3, g) * SZ, y3);
+      tl[p.gtlv[3] + g * 64 + lane] = y3;
     }
   };
   // contributions of a group to the right blocks above level 3 that hold it
@@ -349,8 +349,8 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
       const int i = 4 + u;
       if (i < nl && ((g >> (i - 3)) & 1)) {
         float dec = 0.f;
-        for (int g2 = (g >> (i - 3)) << (i - 3); g2 < g; ++g2) dec += gs[slot_of(N, 3, g2)];
-        tl[gtree_ct(N, nl, p.nslot, i) + item_of_sub(i, g) * 64 + lane] = __expf(dec) * d.ct[u];
+        for (int g2 = (g >> (i - 3)) << (i - 3); g2 < g; ++g2) dec += gs[slot_p(p, 3, g2)];
+        tl[p.gtct[i] + item_of_sub(i, g) * 64 + lane] = __expf(dec) * d.ct[u];
       }
     }
   };
@@ -370,11 +370,11 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
   // levels >= 4, up: block values from the level below
   for (int i = 4; i < nl; ++i) {
     for (int m = w; m < nb(i); m += kTreeWaves) {
-      const float* lo = tl + gtree_lv(N, p.nslot, i - 1) + 2 * m * 64 + lane;
+      const float* lo = tl + p.gtlv[i - 1] + 2 * m * 64 + lane;
       const bool right = 2 * m + 1 < nb(i - 1);
       const float v = right ? __expf(G(i - 1, 2 * m + 1)) * lo[0] + lo[64] : lo[0];
-      tl[gtree_lv(N, p.nslot, i) + m * 64 + lane] = v;
-      if (!(m & 1)) put(ne, nlo, (size_t)slot_of(N, i, m) * SZ, v);
+      tl[p.gtlv[i] + m * 64 + lane] = v;
+      if (!(m & 1)) put(ne, nlo, (size_t)slot_p(p, i, m) * SZ, v);
     }
     __syncthreads();
   }
@@ -382,23 +382,23 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
   // chunks receive from later blocks at its level and above, decayed to the block's end
   for (int i = nl - 1; i >= 4; --i) {
     for (int m = w; m < nb(i); m += kTreeWaves) {
-      const float par = i + 1 < nl ? tl[gtree_lv(N, p.nslot, i + 1) + (m >> 1) * 64 + lane] : 0.f;
+      const float par = i + 1 < nl ? tl[p.gtlv[i + 1] + (m >> 1) * 64 + lane] : 0.f;
       float v = par;
       if (!(m & 1) && m + 1 < nb(i)) {
         float rn = 0.f;
         const int g0 = (m + 1) << (i - 3), g1 = min((m + 2) << (i - 3), ng);
-        const float* ct = tl + gtree_ct(N, nl, p.nslot, i) + lane;
+        const float* ct = tl + p.gtct[i] + lane;
         for (int g2 = g0; g2 < g1; ++g2) rn += ct[item_of_sub(i, g2) * 64];
         v = __expf(G(i, m + 1)) * par + rn;
       }
-      tl[gtree_lv(N, p.nslot, i) + m * 64 + lane] = v;
+      tl[p.gtlv[i] + m * 64 + lane] = v;
     }
     __syncthreads();
   }
   // levels 3..0 of each group, down; the chunks' combined right-sibling states
   auto down_group = [&](int g, const GLoads& d) {
     const int c0 = g << kGrpLog;
-    const float par3 = 4 < nl ? tl[gtree_lv(N, p.nslot, 4) + (g >> 1) * 64 + lane] : 0.f;
+    const float par3 = 4 < nl ? tl[p.gtlv[4] + (g >> 1) * 64 + lane] : 0.f;
     const float d3 = (3 < nl && !(g & 1) && g + 1 < ng) ? __expf(G(3, g + 1)) * par3 + d.r3 : par3;
     float d2[2], d1[4];
     d2[0] = (2 < nl && 2 * g + 1 < nb(2)) ? __expf(G(2, 2 * g + 1)) * d3 + d.r2 : d3;
@@ -634,6 +634,11 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
   p.u_lo = w + pl.off_u_lo;
   p.dA = reinterpret_cast<float*>(w + pl.off_dA);
   p.BH = (int)pl.BH; p.T = a.T; p.L = pl.L; p.N = pl.N; p.nl = pl.nl; p.nslot = pl.nslot;
+  for (int i = 0; i <= lla::kLamCap; ++i) {
+    p.lvl[i] = i <= pl.nl ? lla::bwd::slot_of(pl.N, i, 0) : pl.nslot;
+    p.gtlv[i] = i >= 3 && i <= pl.nl ? lla::bwd::gtree_lv(pl.N, pl.nslot, i) : 0;
+    p.gtct[i] = i >= 4 && i <= pl.nl ? lla::bwd::gtree_ct(pl.N, pl.nl, pl.nslot, i) : 0;
+  }
   void* args[] = {&p};
   auto mark = [&](int i) {
     return a.stage_events[i] ? hipEventRecord(reinterpret_cast<hipEvent_t>(a.stage_events[i]), stream)
