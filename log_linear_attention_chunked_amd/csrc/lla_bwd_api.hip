@@ -429,20 +429,33 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
 }
 
 // ----------------------------------------------------------------------------------------
-// bwd_dloga: dlog_a[r] = sum_{t >= r} dA_t (one workgroup per head, fixed order)
+// bwd_dloga: dlog_a[r] = sum_{t >= r} dA_t (fixed order)
 // ----------------------------------------------------------------------------------------
 
+// one workgroup per segment of a head's positions (gridDim.x segments): the sum of every dA after
+// the segment by a block reduction, then the segment's own reverse prefix on top of it
 __global__ void __launch_bounds__(256) bwd_dloga_kernel(BwdParams p) {
   __shared__ float wtot[4];
-  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int per = (p.T + 255) / 256;
-  const int lo = min(p.T, tid * per), hi = min(p.T, lo + per);
+  const int bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int seglen = (p.T + gridDim.x - 1) / gridDim.x;
+  const int s0 = min(p.T, (int)blockIdx.x * seglen), s1 = min(p.T, s0 + seglen);
   const float* dA = p.dA + (size_t)bh * p.T;
   float* out = p.glog_a + (size_t)bh * p.T;
+  // the positions after the segment
+  float after = 0.f;
+  for (int t = s1 + tid; t < p.T; t += 256) after += dA[t];
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) after += __shfl_xor(after, d);
+  if (lane == 0) wtot[w] = after;
+  __syncthreads();
+  after = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+  __syncthreads();
+  // the segment: per-thread runs, their suffix over the threads above by wave shuffles and the
+  // waves above through shared memory, all in a fixed order
+  const int per = (s1 - s0 + 255) / 256;
+  const int lo = min(s1, s0 + tid * per), hi = min(s1, lo + per);
   float s = 0.f;
   for (int t = hi - 1; t >= lo; --t) s += dA[t];
-  // exclusive suffix of the segment sums over the threads above this one, in a fixed order:
-  // inside a wave by shuffles, across the 4 waves through shared memory
   float incl = s;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -451,7 +464,7 @@ __global__ void __launch_bounds__(256) bwd_dloga_kernel(BwdParams p) {
   }
   if (lane == 0) wtot[w] = incl;
   __syncthreads();
-  float run = incl - s;
+  float run = incl - s + after;
   for (int u = 3; u > w; --u) run += wtot[u];
   for (int t = hi - 1; t >= lo; --t) {
     run += dA[t];
@@ -706,7 +719,9 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
                       stream) != hipSuccess)
     return LLA_ERR_HIP;
   if (mark(2) != hipSuccess) return LLA_ERR_HIP;
-  hipLaunchKernelGGL(lla::bwd::bwd_dloga_kernel, dim3((unsigned)pl.BH), dim3(256), 0, stream, p);
+  // segments of about 1024 positions per head
+  hipLaunchKernelGGL(lla::bwd::bwd_dloga_kernel, dim3((unsigned)((a.T + 1023) / 1024), (unsigned)pl.BH),
+                     dim3(256), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return LLA_ERR_HIP;
   if (mark(3) != hipSuccess) return LLA_ERR_HIP;
   return LLA_OK;
