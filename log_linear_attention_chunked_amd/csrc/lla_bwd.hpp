@@ -80,8 +80,8 @@ struct BwdParams {
   int items;                  // sub-blocks per head over all levels
   int rn_off[kLamCap + 1];    // first sub-block of each level
   int lvl[kLamCap + 1];       // first tree slot of each level (slot_of(N, i, 0))
-  int gtlv[kLamCap + 1];      // bwd_gtree: first float of level i's block values (i >= 3)
-  int gtct[kLamCap + 1];      // bwd_gtree: first float of level i's contributions (i >= 4)
+  int gtlv[kLamCap + 1];      // bwd_gtree: first shared slot of level i's block values (i >= 3)
+  int gtct[kLamCap + 1];      // bwd_gtree: first shared slot of level i's contributions (i >= 4)
 };
 
 // slot of block (i, m) from the level offsets the host computed (no loop over the levels)

@@ -210,46 +210,56 @@ bwd_tree_kernel(BwdParams p, int SZ) {
 // that needs it. Every global load a workgroup makes (the groups' chunk states, their right
 // blocks' states, the contributions and the block decays) is issued before the first wait when
 // a wave owns one group, so the whole tree costs about one memory round trip.
-// Shared memory (floats): the block decays; per level i >= 3 (below nl) the block values (64
-// floats each, up-sweep values later overwritten by the down-sweep's); per level i >= 4 the
-// contributions, one per right-block group (item order of bwd_rn).
+// Shared memory: the block decays (floats); then slots of VE floats per lane: per level
+// i >= 3 (below nl) the block values (up-sweep values later overwritten by the down-sweep's); per
+// level i >= 4 the contributions, one per right-block group (item order of bwd_rn).
 // ----------------------------------------------------------------------------------------
 
 constexpr int kGrpLog = 3;            // 8 chunks per group
 static_assert(kGrpLog == kSubLog, "a group is one of bwd_rn's sub-blocks");
 constexpr int kGtCt = 6;              // levels >= 4 whose contributions a wave prefetches
+// Each lane holds VE (4, else 2 or 1 where the shared memory would not fit) consecutive state
+// elements: 16-byte loads, 8-byte bf16 stores and 16-byte shared-memory slots at VE = 4, where a
+// workgroup covers 256 elements and the scalar work of a group (its addresses, levels and
+// branches, the same for every element) is shared by four times the data.
 
-// first float of level i's block values (3 <= i <= nl) and of level i's contributions
-// (4 <= i <= nl; i = nl gives the total), after the nslot block decays
+// first slot of level i's block values (3 <= i <= nl) and of level i's contributions
+// (4 <= i <= nl; i = nl gives the total) in the value region, which follows the block decays
 __host__ __device__ inline int gtree_lv(int N, int nslot, int i) {
-  int off = (nslot + 63) & ~63;
-  for (int a = 3; a < i; ++a) off += ((N + (1 << a) - 1) >> a) * 64;
+  (void)nslot;
+  int off = 0;
+  for (int a = 3; a < i; ++a) off += (N + (1 << a) - 1) >> a;
   return off;
 }
 __host__ __device__ inline int gtree_ct(int N, int nl, int nslot, int i) {
   int off = gtree_lv(N, nslot, nl > 3 ? nl : 3);
-  for (int a = 4; a < i; ++a) off += items_of_level(N, a) * 64;
+  for (int a = 4; a < i; ++a) off += items_of_level(N, a);
   return off;
 }
-__host__ __device__ inline int gtree_floats(int N, int nl, int nslot) {
-  return gtree_ct(N, nl, nslot, nl > 4 ? nl : 4);
+// the decays, then every level's block values and contributions, VE * 64 floats per slot
+__host__ __device__ inline int gtree_floats(int N, int nl, int nslot, int VE) {
+  return ((nslot + 63) & ~63) + gtree_ct(N, nl, nslot, nl > 4 ? nl : 4) * VE * 64;
 }
 
 // GROUPED: bwd_statesg has done levels 0..3 of every group (nodes written, the group in fp32 at
 // its level-3 slot); the tree then starts from the groups
-template <typename E, bool GROUPED>
-__global__ void __launch_bounds__(64 * kTreeWaves) __attribute__((amdgpu_waves_per_eu(8)))
+template <typename E, bool GROUPED, int VE>
+__global__ void __launch_bounds__(64 * kTreeWaves) __attribute__((amdgpu_waves_per_eu(VE > 1 ? 4 : 8)))
 bwd_gtree_kernel(BwdParams p, int SZ) {
   extern __shared__ __attribute__((aligned(16))) float tl[];
+  constexpr int SW = 64 * VE;   // elements per workgroup (one shared-memory slot)
+  typedef float FV __attribute__((ext_vector_type(VE)));
+  typedef E EV __attribute__((ext_vector_type(VE)));
   // the wave index is uniform (read from lane 0), so every group and block index below is, and
-  // each access is a uniform base plus the lane's 4 (or 2) bytes
+  // each access is a uniform base plus the lane's bytes
   const int bh = blockIdx.y, lane = threadIdx.x & 63;
   const unsigned ul = threadIdx.x & 63;   // the lane as an unsigned (zero-extended) offset
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int e0 = blockIdx.x * 64;
+  const int e0 = blockIdx.x * SW;
   const int N = p.N, nl = p.nl, ng = (N + 7) >> kGrpLog;
   const float* __restrict__ gsg = p.gsum + (size_t)bh * p.nslot;
   float* gs = tl;                        // block decays first
+  float* tv = tl + ((p.nslot + 63) & ~63);   // then the block values, SW floats per slot
   const float* __restrict__ nd = p.node + (size_t)bh * p.nslot * SZ + e0;
   const float* __restrict__ rp = p.rnp + (size_t)bh * p.items * SZ + e0;
   E* __restrict__ ne = reinterpret_cast<E*>(p.node_e) + (size_t)bh * p.nslot * SZ + e0;
@@ -257,24 +267,34 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
   constexpr bool SPLIT = sizeof(E) == 2;
   E* __restrict__ nlo = reinterpret_cast<E*>(p.node_lo) + (size_t)bh * p.nslot * SZ + e0;
   E* __restrict__ ulo = reinterpret_cast<E*>(p.u_lo) + (size_t)bh * N * SZ + e0;
-  auto put = [&](E* hi, E* lo, size_t at, float x) {
-    const E h = (E)x;
-    uniform_ptr(hi + at)[ul] = h;
-    if (SPLIT) uniform_ptr(lo + at)[ul] = (E)(x - (float)h);
+  auto put = [&](E* hi, E* lo, size_t at, const FV& x) {
+    EV h, l;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) {
+      h[e] = (E)x[e];
+      l[e] = (E)(x[e] - (float)h[e]);
+    }
+    reinterpret_cast<__attribute__((address_space(1))) EV*>(uniform_ptr(hi + at))[ul] = h;
+    if (SPLIT) reinterpret_cast<__attribute__((address_space(1))) EV*>(uniform_ptr(lo + at))[ul] = l;
   };
-  // element `lane` of the state in slot i of a region
-  auto ld = [&](const float* base, int i) { return uniform_ptr(base + (size_t)i * SZ)[ul]; };
+  // the lane's elements of the state in slot i of a region
+  auto ld = [&](const float* base, int i) {
+    return reinterpret_cast<const __attribute__((address_space(1))) FV*>(uniform_ptr(base + (size_t)i * SZ))[ul];
+  };
+  // the lane's elements of block-value slot s (shared memory)
+  auto tvs = [&](int s) -> FV& { return *reinterpret_cast<FV*>(tv + s * SW + VE * lane); };
   auto nb = [&](int i) { return (N + (1 << i) - 1) >> i; };
   // item index of right block sb at level i, or item 0 (read, then multiplied by nothing) when
   // there is none
   auto item = [&](int i, int sb, bool ok) {
     return ok ? p.rn_off[i] + item_of_sub(i, sb) : 0;
   };
+  const FV zero = (FV)(0.f);
 
   // one group's loads: its chunk states (zero past N), the right-block states of levels 0..3
   // inside it, and its contributions to right blocks of levels 4 .. 3 + kGtCt
   struct GLoads {
-    float x[8], r0[4], r1[2], r2, r3, ct[kGtCt];
+    FV x[GROUPED ? 1 : 8], r0[4], r1[2], r2, r3, ct[kGtCt];
   };
   auto load_group = [&](int g, GLoads& d) {
     const int c0 = g << kGrpLog;
@@ -317,29 +337,30 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
   // up-sweep inside a group, contributions, and the group's value at level 3
   auto up_group = [&](int g, const GLoads& d) {
     if constexpr (GROUPED) {
-      if (3 < nl) tl[p.gtlv[3] + g * 64 + lane] = d.x[0];
+      if (3 < nl) tvs(p.gtlv[3] + g) = d.x[0];
       return;
-    }
-    const int c0 = g << kGrpLog;
-    float x[8], y1[4], y2[2];
+    } else {
+      const int c0 = g << kGrpLog;
+      FV x[8], y1[4], y2[2];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = c0 + k < N ? d.x[k] : 0.f;
+      for (int k = 0; k < 8; ++k) x[k] = c0 + k < N ? d.x[k] : zero;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) y1[h] = __expf(G(0, c0 + 2 * h + 1)) * x[2 * h] + x[2 * h + 1];
+      for (int h = 0; h < 4; ++h) y1[h] = __expf(G(0, c0 + 2 * h + 1)) * x[2 * h] + x[2 * h + 1];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) y2[h] = __expf(G(1, 4 * g + 2 * h + 1)) * y1[2 * h] + y1[2 * h + 1];
-    const float y3 = __expf(G(2, 2 * g + 1)) * y2[0] + y2[1];
-    // the gradient kernel reads node (j, (c >> j) - 1) for set bits j of c: even nodes only
+      for (int h = 0; h < 2; ++h) y2[h] = __expf(G(1, 4 * g + 2 * h + 1)) * y1[2 * h] + y1[2 * h + 1];
+      const FV y3 = __expf(G(2, 2 * g + 1)) * y2[0] + y2[1];
+      // the gradient kernel reads node (j, (c >> j) - 1) for set bits j of c: even nodes only
 #pragma unroll
-    for (int h = 0; h < 4; ++h)
-      if (0 < nl && c0 + 2 * h < N) put(ne, nlo, (size_t)(c0 + 2 * h) * SZ, x[2 * h]);
+      for (int h = 0; h < 4; ++h)
+        if (0 < nl && c0 + 2 * h < N) put(ne, nlo, (size_t)(c0 + 2 * h) * SZ, x[2 * h]);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      if (1 < nl && 4 * g + 2 * h < nb(1)) put(ne, nlo, (size_t)slot_p(p, 1, 4 * g + 2 * h) * SZ, y1[2 * h]);
-    if (2 < nl && 2 * g < nb(2)) put(ne, nlo, (size_t)slot_p(p, 2, 2 * g) * SZ, y2[0]);
-    if (3 < nl) {
-      if (!(g & 1)) put(ne, nlo, (size_t)slot_p(p, 3, g) * SZ, y3);
-      tl[p.gtlv[3] + g * 64 + lane] = y3;
+      for (int h = 0; h < 2; ++h)
+        if (1 < nl && 4 * g + 2 * h < nb(1)) put(ne, nlo, (size_t)slot_p(p, 1, 4 * g + 2 * h) * SZ, y1[2 * h]);
+      if (2 < nl && 2 * g < nb(2)) put(ne, nlo, (size_t)slot_p(p, 2, 2 * g) * SZ, y2[0]);
+      if (3 < nl) {
+        if (!(g & 1)) put(ne, nlo, (size_t)slot_p(p, 3, g) * SZ, y3);
+        tvs(p.gtlv[3] + g) = y3;
+      }
     }
   };
   // contributions of a group to the right blocks above level 3 that hold it
@@ -350,7 +371,7 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
       if (i < nl && ((g >> (i - 3)) & 1)) {
         float dec = 0.f;
         for (int g2 = (g >> (i - 3)) << (i - 3); g2 < g; ++g2) dec += gs[slot_p(p, 3, g2)];
-        tl[p.gtct[i] + item_of_sub(i, g) * 64 + lane] = __expf(dec) * d.ct[u];
+        tvs(p.gtct[i] + item_of_sub(i, g)) = __expf(dec) * d.ct[u];
       }
     }
   };
@@ -370,10 +391,10 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
   // levels >= 4, up: block values from the level below
   for (int i = 4; i < nl; ++i) {
     for (int m = w; m < nb(i); m += kTreeWaves) {
-      const float* lo = tl + p.gtlv[i - 1] + 2 * m * 64 + lane;
       const bool right = 2 * m + 1 < nb(i - 1);
-      const float v = right ? __expf(G(i - 1, 2 * m + 1)) * lo[0] + lo[64] : lo[0];
-      tl[p.gtlv[i] + m * 64 + lane] = v;
+      const FV l0 = tvs(p.gtlv[i - 1] + 2 * m);
+      const FV v = right ? __expf(G(i - 1, 2 * m + 1)) * l0 + tvs(p.gtlv[i - 1] + 2 * m + 1) : l0;
+      tvs(p.gtlv[i] + m) = v;
       if (!(m & 1)) put(ne, nlo, (size_t)slot_p(p, i, m) * SZ, v);
     }
     __syncthreads();
@@ -382,25 +403,24 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
   // chunks receive from later blocks at its level and above, decayed to the block's end
   for (int i = nl - 1; i >= 4; --i) {
     for (int m = w; m < nb(i); m += kTreeWaves) {
-      const float par = i + 1 < nl ? tl[p.gtlv[i + 1] + (m >> 1) * 64 + lane] : 0.f;
-      float v = par;
+      const FV par = i + 1 < nl ? tvs(p.gtlv[i + 1] + (m >> 1)) : zero;
+      FV v = par;
       if (!(m & 1) && m + 1 < nb(i)) {
-        float rn = 0.f;
+        FV rn = zero;
         const int g0 = (m + 1) << (i - 3), g1 = min((m + 2) << (i - 3), ng);
-        const float* ct = tl + p.gtct[i] + lane;
-        for (int g2 = g0; g2 < g1; ++g2) rn += ct[item_of_sub(i, g2) * 64];
+        for (int g2 = g0; g2 < g1; ++g2) rn += tvs(p.gtct[i] + item_of_sub(i, g2));
         v = __expf(G(i, m + 1)) * par + rn;
       }
-      tl[p.gtlv[i] + m * 64 + lane] = v;
+      tvs(p.gtlv[i] + m) = v;
     }
     __syncthreads();
   }
   // levels 3..0 of each group, down; the chunks' combined right-sibling states
   auto down_group = [&](int g, const GLoads& d) {
     const int c0 = g << kGrpLog;
-    const float par3 = 4 < nl ? tl[p.gtlv[4] + (g >> 1) * 64 + lane] : 0.f;
-    const float d3 = (3 < nl && !(g & 1) && g + 1 < ng) ? __expf(G(3, g + 1)) * par3 + d.r3 : par3;
-    float d2[2], d1[4];
+    const FV par3 = 4 < nl ? tvs(p.gtlv[4] + (g >> 1)) : zero;
+    const FV d3 = (3 < nl && !(g & 1) && g + 1 < ng) ? __expf(G(3, g + 1)) * par3 + d.r3 : par3;
+    FV d2[2], d1[4];
     d2[0] = (2 < nl && 2 * g + 1 < nb(2)) ? __expf(G(2, 2 * g + 1)) * d3 + d.r2 : d3;
     d2[1] = d3;
 #pragma unroll
@@ -412,7 +432,7 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const int c = c0 + 2 * h;
-      const float d0 = (0 < nl && c + 1 < N) ? __expf(G(0, c + 1)) * d1[h] + d.r0[h] : d1[h];
+      const FV d0 = (0 < nl && c + 1 < N) ? __expf(G(0, c + 1)) * d1[h] + d.r0[h] : d1[h];
       if (c < N) put(ue, ulo, (size_t)c * SZ, d0);
       if (c + 1 < N) put(ue, ulo, (size_t)(c + 1) * SZ, d1[h]);
     }
@@ -477,6 +497,23 @@ __global__ void __launch_bounds__(256) bwd_dloga_kernel(BwdParams p) {
 
 namespace {
 
+// the group tree's instance for an element type, a grouped start and VE elements per lane (at
+// most 2 without the grouped start, whose eight chunk states per group would not fit the
+// registers at 4)
+template <typename E, bool GROUPED>
+const void* gtree_fn_ve(int ve) {
+  using namespace lla::bwd;
+  if constexpr (GROUPED)
+    if (ve == 4) return reinterpret_cast<const void*>(&bwd_gtree_kernel<E, GROUPED, 4>);
+  if (ve == 2) return reinterpret_cast<const void*>(&bwd_gtree_kernel<E, GROUPED, 2>);
+  if (ve == 1) return reinterpret_cast<const void*>(&bwd_gtree_kernel<E, GROUPED, 1>);
+  return nullptr;
+}
+const void* gtree_fn(bool bf, bool grouped, int ve) {
+  if (bf) return grouped ? gtree_fn_ve<lla::bf16, true>(ve) : gtree_fn_ve<lla::bf16, false>(ve);
+  return grouped ? gtree_fn_ve<float, true>(ve) : gtree_fn_ve<float, false>(ve);
+}
+
 using lla::bwd::BwdKernels;
 using lla::bwd::BwdParams;
 
@@ -489,6 +526,7 @@ constexpr int kLdsPerWorkgroup = 160 * 1024;
 struct BwdPlan {
   int C, N, nl, nslot, L, esize, smem_states, smem_grads;
   int gtree_smem;   // > 0: the group tree (bwd_gtree) runs, with this much shared memory
+  int gtree_ve;     // and this many state elements per lane
   long BH;
   int items, rn_off[lla::kLamCap + 1];
   size_t off_node, off_gsum, off_rnp, off_outs, off_node_e, off_u_e, off_node_lo, off_u_lo, off_dA, ws_bytes;
@@ -559,9 +597,13 @@ int make_bwd_plan(int B, int H, int T, int dk, int dv, int chunk, int dtype, Bwd
   // the group tree when its contributions are all prefetched (levels up to 3 + kGtCt) and its
   // shared memory fits; otherwise the level-by-level tree
   pl.gtree_smem = 0;
-  if (pl.nl > 0 && pl.nl <= 4 + lla::bwd::kGtCt) {
-    const size_t b = (size_t)lla::bwd::gtree_floats(pl.N, pl.nl, pl.nslot) * 4;
-    if (b <= (size_t)kLdsPerWorkgroup) pl.gtree_smem = (int)b;
+  pl.gtree_ve = 0;
+  for (int ve = 4; ve >= 1 && pl.nl > 0 && pl.nl <= 4 + lla::bwd::kGtCt && !pl.gtree_smem; ve >>= 1) {
+    const size_t b = (size_t)lla::bwd::gtree_floats(pl.N, pl.nl, pl.nslot, ve) * 4;
+    if (b <= (size_t)kLdsPerWorkgroup) {
+      pl.gtree_smem = (int)b;
+      pl.gtree_ve = ve;
+    }
   }
   pl.off_outs = off; off = align256(off + (pl.gtree_smem ? 0 : (size_t)BH * pl.nslot * SZ * 4));
   pl.off_node_e = off; off = align256(off + (size_t)BH * pl.nslot * SZ * pl.esize);
@@ -693,18 +735,19 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
       hipLaunchKernelGGL(lla::bwd::bwd_gsum_kernel, dim3((unsigned)pl.BH), dim3(256), 0, stream, p);
       if (hipGetLastError() != hipSuccess) return LLA_ERR_HIP;
     }
-    const int SZ = a.dk * a.dv;   // a multiple of 64: the tree grid covers it exactly
+    const int SZ = a.dk * a.dv;   // a multiple of 256: the tree grids cover it exactly
     const dim3 tgrid((unsigned)(SZ / 64), (unsigned)pl.BH), tblock(64 * lla::bwd::kTreeWaves);
     const bool bf = a.dtype == LLA_DTYPE_BF16;
     if (pl.gtree_smem > 0) {
-      using namespace lla::bwd;
-      const void* fn = grouped ? (bf ? reinterpret_cast<const void*>(&bwd_gtree_kernel<lla::bf16, true>)
-                                     : reinterpret_cast<const void*>(&bwd_gtree_kernel<float, true>))
-                               : (bf ? reinterpret_cast<const void*>(&bwd_gtree_kernel<lla::bf16, false>)
-                                     : reinterpret_cast<const void*>(&bwd_gtree_kernel<float, false>));
+      // the shared memory planned for VE elements per lane covers any smaller VE
+      const int ve = grouped || pl.gtree_ve < 2 ? pl.gtree_ve : 2;
+      const void* fn = gtree_fn(bf, grouped, ve);
+      if (!fn) return LLA_ERR_UNSUPPORTED;
       if (set_smem(fn, pl.gtree_smem) != hipSuccess) return LLA_ERR_HIP;
       void* targs[] = {&p, const_cast<int*>(&SZ)};
-      if (hipLaunchKernel(fn, tgrid, tblock, targs, pl.gtree_smem, stream) != hipSuccess) return LLA_ERR_HIP;
+      if (hipLaunchKernel(fn, dim3((unsigned)(SZ / (64 * ve)), (unsigned)pl.BH), tblock, targs,
+                          pl.gtree_smem, stream) != hipSuccess)
+        return LLA_ERR_HIP;
     } else if (bf) {
       hipLaunchKernelGGL((lla::bwd::bwd_tree_kernel<lla::bf16>), tgrid, tblock, 0, stream, p, SZ);
     } else {
