@@ -259,6 +259,25 @@ __device__ __forceinline__ Frag<T> frag_grow(const float* g, int RS, int r, int 
   return frag_from<T>(lo, hi);
 }
 
+// lane l's value of x (a scalar read: every lane gets the same value)
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+// x summed over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48): exchanging the odd rows
+// of x with the even rows of a copy (v_permlane16_swap) leaves x[l] and x[l ^ 16] in the two
+// registers of every lane; the same with the wave's halves (v_permlane32_swap) for l ^ 32
+__device__ __forceinline__ float sum_rows(float x) {
+  const unsigned xi = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(xi, xi, false, false);
+  const unsigned a0 = r[0], a1 = r[1];   // copied out before the casts (element reads)
+  const float y = __builtin_bit_cast(float, a0) + __builtin_bit_cast(float, a1);
+  const unsigned yi = __builtin_bit_cast(unsigned, y);
+  const auto r2 = __builtin_amdgcn_permlane32_swap(yi, yi, false, false);
+  const unsigned b0 = r2[0], b1 = r2[1];
+  return __builtin_bit_cast(float, b0) + __builtin_bit_cast(float, b1);
+}
+
 // x from another lane of the same 16-lane row through a DPP move (the vector unit, not the
 // shared-memory permute that a generic shuffle compiles to): quad_perm patterns 0xB1 ([1,0,3,2])
 // and 0x4E ([2,3,0,1]); row_ror:4 = 0x124, row_ror:8 = 0x128
@@ -422,13 +441,8 @@ struct Chunk {
           if (i < C * kLamCap) ch.lam[i] = (i / kLamCap < nv && i % kLamCap < L) ? x : 0.f;
         }
       if (tid < 64) {
-        float incl = (tid < C && tid < nv) ? la : 0.f;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const float y = __shfl_up(incl, d);
-          if (tid >= d) incl += y;
-        }
-        const float tot = __shfl(incl, 63);
+        const float incl = wave_scan<false>((tid < C && tid < nv) ? la : 0.f);
+        const float tot = lane_f(incl, 63);
         if (tid < C) {
           ch.al[tid] = incl;
           ch.ea[tid] = __expf(incl);
@@ -681,13 +695,8 @@ bwd_statesg_kernel(BwdParams p) {
         }
       }
       // every wave scans the chunk's log_a; wave 0 writes the weights exp(g_c - A_s)
-      float incl = lane < nv ? rla : 0.f;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const float y = __shfl_up(incl, d);
-        if (lane >= d) incl += y;
-      }
-      gc = __shfl(incl, 63);
+      const float incl = wave_scan<false>(lane < nv ? rla : 0.f);
+      gc = lane_f(incl, 63);
       if (w == 0 && lane < C) ch.ws[lane] = __expf(gc - incl);
       __syncthreads();
       if (c + 1 < c1) fetch(c + 1);
@@ -848,14 +857,9 @@ bwd_rn_kernel(BwdParams p) {
     }
     // every wave scans the chunk's log_a (C <= 64 positions, one per lane); wave 0 writes the
     // weights lambda * exp(decay from the sub-block's start)
-    float incl = lane < C ? rla : 0.f;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float y = __shfl_up(incl, d);
-      if (lane >= d) incl += y;
-    }
+    const float incl = wave_scan<false>(lane < C ? rla : 0.f);
     if (w == 0 && lane < C) sc[lane] = rlm * __expf(eoff + incl);
-    eoff += __shfl(incl, C - 1);
+    eoff += lane_f(incl, C - 1);
     __syncthreads();
     if (c + 1 < c1) fetch(c + 1);
     // the wave's tiles: its do columns scaled and split once per contraction step
@@ -1009,12 +1013,7 @@ bwd_rng_kernel(BwdParams p) {
       }
       // every wave scans the chunk's log_a (C <= 64 positions, one per lane); wave 0 writes the
       // weights of the active slots
-      float incl = lane < nv ? rla : 0.f;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const float y = __shfl_up(incl, d);
-        if (lane >= d) incl += y;
-      }
+      const float incl = wave_scan<false>(lane < nv ? rla : 0.f);
       bool act[NS];
 #pragma unroll
       for (int u = 0; u < 3; ++u) {
@@ -1028,7 +1027,7 @@ bwd_rng_kernel(BwdParams p) {
         for (int u = 0; u < NS; ++u)
           if (act[u]) scw[u * C + lane] = lane < nv ? rlm[u] * __expf(eoff - (u < 3 ? base[u] : 0.f) + incl) : 0.f;
       }
-      eoff += __shfl(incl, C - 1);
+      eoff += lane_f(incl, C - 1);
       __syncthreads();
       if (c + 1 < c1) fetch(c + 1);
       // the wave's tiles: do columns (the scaled operand) scaled and split once per slot and
@@ -1303,8 +1302,7 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
         colg += p1 * s[r];
       }
       // this wave's rows of column j: the four row groups of the lane's column
-      colg += __shfl_xor(colg, 16);
-      colg += __shfl_xor(colg, 32);
+      colg = sum_rows(colg);
       if (g4 == 0) colp[w * C + cb * 16 + jj] = colg;
       if (cb < rb) {
         const int lv = 4 + bit_length((unsigned)(rb ^ cb));
