@@ -263,6 +263,7 @@ __device__ __forceinline__ Frag<T> frag_grow(const float* g, int RS, int r, int 
 __device__ __forceinline__ float lane_f(float x, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
+__device__ __forceinline__ int lane_i(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
 
 // x summed over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48): exchanging the odd rows
 // of x with the even rows of a copy (v_permlane16_swap) leaves x[l] and x[l ^ 16] in the two
@@ -309,6 +310,21 @@ __device__ __forceinline__ float sum16(float x) {
   x += dpp_f<0x124>(x);
   x += dpp_f<0x128>(x);
   return x;
+}
+
+// four row values x[0..3] (rows 0..3 of a lane's row group) each summed over the 16 lanes of the
+// row; lane j receives the sum of row j & 3. Two exchange steps halve the values a lane carries
+// (lanes j, j ^ 1 keep rows of opposite low bit; then j, j ^ 2 of opposite high bit), two
+// rotations add the lanes 4 and 8 apart: 11 vector instructions instead of four sums of 4 DPP
+// adds each
+__device__ __forceinline__ float sum16x4(const float (&x)[4], int jj) {
+  const bool b0 = jj & 1, b1 = jj & 2;
+  const float y0 = (b0 ? x[1] : x[0]) + dpp_f<0xB1>(b0 ? x[0] : x[1]);
+  const float y1 = (b0 ? x[3] : x[2]) + dpp_f<0xB1>(b0 ? x[2] : x[3]);
+  float z = (b1 ? y1 : y0) + dpp_f<0x4E>(b1 ? y0 : y1);
+  z += dpp_f<0x124>(z);
+  z += dpp_f<0x128>(z);
+  return z;
 }
 
 // kernel table of one (dtype, chunk, dk, dv)
@@ -1195,9 +1211,8 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   // node just read (cur, still in L2), or for chunk 0 slot 0.
   // rows of dq: the whole node, every thread its share, on its way into shared memory
   u32x4 pf[PF ? NPF : 1], pf2[PF && SPLIT ? NPF : 1];
-  auto prefetch = [&](int jl, int cur) {
-    if (jl >= p.nl) jl = cur;
-    const size_t off = (size_t)slot_p(p, jl, max((c >> jl) - 1, 0)) * SZ;
+  auto prefetch = [&](int sl) {
+    const size_t off = (size_t)sl * SZ;
     const u32x4* src = reinterpret_cast<const u32x4*>(node_e + off);
     const u32x4* src2 = reinterpret_cast<const u32x4*>(node_lo + off);
 #pragma unroll
@@ -1211,9 +1226,8 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   using QT = DqTiles<C, DK>;
   constexpr int NKS = DV >= 32 ? DV / 32 : 1;           // contraction steps over dv
   constexpr int NBF = QT::TA * NKS;                      // operand fragments per node
-  auto load_node = [&](int jl, int cur, Frag<T>* hi, Frag<T>* lo, bool* ok) {
-    if (jl >= p.nl) jl = cur;
-    const size_t off = (size_t)slot_p(p, jl, max((c >> jl) - 1, 0)) * SZ;
+  auto load_node = [&](int sl, Frag<T>* hi, Frag<T>* lo, bool* ok) {
+    const size_t off = (size_t)sl * SZ;
 #pragma unroll
     for (int a = 0; a < QT::TA; ++a)
 #pragma unroll
@@ -1240,12 +1254,34 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   if (PF && SPLIT && later)
 #pragma unroll
     for (int u = 0; u < NPF; ++u) ulo[u] = reinterpret_cast<const u32x4*>(u_lo)[tid + u * NT];
-  int first_set = 0;
-  while (first_set < p.nl && !((c >> first_set) & 1)) ++first_set;
+  // the nodes of step 4 are (j, (c >> j) - 1) for the set bits j of c (c < N <= 2^nl), lowest
+  // first. Lane l < nl holds node l's slot (slot 0 where bit l is clear) and its block decay
+  // (zero where clear), loaded with the rest; step 4 turns them into each node's decay to the
+  // chunk's start, so that its loop reads neither the kernel arguments nor memory for them
+  // (the row path only: the column path, short of registers, reads them in its loop)
+  const int first_set = c ? __builtin_ctz((unsigned)c) : p.nl;
+  int nslot_l = 0;
+  float gsl = 0.f;
+  auto node_table = [&]() {
+#pragma unroll
+    for (int l = 0; l < kLamCap; ++l)
+      if (lane == l && l < p.nl) nslot_l = slot_p(p, l, max((c >> l) - 1, 0));
+    gsl = later ? p.gsum[(size_t)bh * p.nslot + nslot_l] : 0.f;
+  };
+  if constexpr (!COLQ) node_table();
+  // the next set bit after jl, or nl past the last
+  auto next_set = [&](int jl) {
+    const int rest = c >> (jl + 1);
+    return rest ? jl + 1 + __builtin_ctz((unsigned)rest) : p.nl;
+  };
+  // node jl's slot, or (past the last node) node cur's, still in L2
+  auto slot_at = [&](int jl, int cur) { return lane_i(nslot_l, jl < p.nl ? jl : cur); };
+  // the first node's slot (slot 0 for chunk 0, which has none)
+  const int sl0 = first_set < p.nl ? slot_p(p, first_set, (c >> first_set) - 1) : 0;
   if constexpr (COLQ) {
-    if (later) load_node(first_set, 0, bhi, blo, bok);
+    if (later) load_node(sl0, bhi, blo, bok);
   } else {
-    if (later) prefetch(first_set, 0);
+    if (later) prefetch(sl0);
   }
   st.put(ch, tid);
   if (later) {
@@ -1442,30 +1478,34 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   //    - larger nodes, which the staging could not prefetch: by columns of dq, each wave loading
   //      only the node rows of its own dq columns straight into operand registers, one node
   //      ahead, with no barrier in the loop; the waves' dlambda shares are summed afterwards.
-  const float* gs = p.gsum + (size_t)bh * p.nslot;
   float* dqd = reinterpret_cast<float*>(sm + Lo.dqd);
   if constexpr (!COLQ) {
+    // decay factor from the end of node l to the start of chunk c: exp of the block decays of
+    // the nodes of the lower set bits (an exclusive prefix sum over the lanes)
+    const float gl = (lane < p.nl && ((c >> lane) & 1)) ? gsl : 0.f;
+    const float ej = __expf(wave_scan<false>(gl) - gl);
     T* Nst = Ust;   // the state image, free once step 3 is done
-    float dlow = 0.f;   // log decay from the end of the current node to the start of chunk c
-    float dq_dot[4] = {0.f, 0.f, 0.f, 0.f};
     const int rb = w;
-    for (int jl = first_set; jl < p.nl; ++jl) {
-      if (!((c >> jl) & 1)) continue;
-      const int sl = slot_p(p, jl, (c >> jl) - 1);
+    const int ro = jj & 3, io = rb * 16 + 4 * g4 + ro;   // the row whose sums this lane receives
+    float eai[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) eai[r] = ch.ea[rb * 16 + 4 * g4 + r];
+    const float eao = ro == 0 ? eai[0] : ro == 1 ? eai[1] : ro == 2 ? eai[2] : eai[3];
+    float dq_dot = 0.f;   // row io's q . (dq from the nodes)
+    for (int jl = first_set; jl < p.nl;) {
+      const int nx = next_set(jl);
       __syncthreads();   // the previous reads of the state image are done
       put(Nst, pf);
       if constexpr (SPLIT) put(Plo, pf2);
-      int nx = jl + 1;
-      while (nx < p.nl && !((c >> nx) & 1)) ++nx;
-      prefetch(nx, jl);
+      prefetch(slot_at(nx, jl));
       __syncthreads();
-      const float dj = __expf(dlow);
+      const float dj = lane_f(ej, jl);
       float part[4] = {0.f, 0.f, 0.f, 0.f};
       float scl[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = rb * 16 + 4 * g4 + r;
-        scl[r] = ch.lam[i * kLamCap + J + 1 + jl] * ch.ea[i] * dj;
+        scl[r] = ch.lam[i * kLamCap + J + 1 + jl] * eai[r] * dj;
       }
 #pragma unroll
       for (int t = 0; t < NK; ++t) {
@@ -1483,20 +1523,16 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
           part[r] += y[r] * to_f(ch.q[i * CH::RK + t * 16 + jj]);
         }
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float sum = sum16(part[r]);
-        const int i = rb * 16 + 4 * g4 + r;
-        dq_dot[r] += scl[r] * sum;
-        if (jj == r) ch.lam[i * kLamCap + J + 1 + jl] = ch.ea[i] * dj * sum;
-      }
-      dlow += gs[sl];
+      const float tot = sum16x4(part, jj);
+      const float so = ro == 0 ? scl[0] : ro == 1 ? scl[1] : ro == 2 ? scl[2] : scl[3];
+      dq_dot += so * tot;
+      if (jj < 4) ch.lam[io * kLamCap + J + 1 + jl] = eao * dj * tot;
+      jl = nx;
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      if (jj == r) dqd[rb * 16 + 4 * g4 + r] = dq_dot[r];
+    if (jj < 4) dqd[io] = dq_dot;
   } else {
     __syncthreads();
+    const float* gs = p.gsum + (size_t)bh * p.nslot;
     float* red = reinterpret_cast<float*>(sm + Lo.p1);   // [wave][node][position]
     {
       float dlow = 0.f;   // log decay from the end of the current node to the start of chunk c
@@ -1507,7 +1543,8 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
         if (!((c >> jl) & 1)) continue;
         int nx = jl + 1;
         while (nx < p.nl && !((c >> nx) & 1)) ++nx;
-        load_node(nx, jl, nhi, nlo, nok);
+        const int sl = slot_p(p, jl, (c >> jl) - 1);
+        load_node(nx < p.nl ? slot_p(p, nx, (c >> nx) - 1) : sl, nhi, nlo, nok);
         const float dj = __expf(dlow);
 #pragma unroll
         for (int b = 0; b < QT::RBW; ++b) {
@@ -1548,7 +1585,7 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
           if constexpr (SPLIT) blo[f] = nlo[f];
           bok[f] = nok[f];
         }
-        dlow += gs[slot_p(p, jl, (c >> jl) - 1)];
+        dlow += gs[sl];
         ++kn;
       }
     }
@@ -1559,8 +1596,7 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
       const int i = tid, R = i >> 4;
       float dl = 0.f, acc = 0.f;
       int kn = 0;
-      for (int jl = first_set; jl < p.nl; ++jl) {
-        if (!((c >> jl) & 1)) continue;
+      for (int jl = first_set; jl < p.nl; jl = next_set(jl)) {
         float sum = 0.f;
         for (int u = 0; u < NW; ++u)
           if (QT::holds(u, R)) sum += red[(u * p.nl + kn) * C + i];
