@@ -1297,12 +1297,11 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   static_assert(RB == 1, "one 16-row block of positions per wave");
   float* colp = reinterpret_cast<float*>(sm + Lo.cg);   // [wave][position]
   float rowg[4] = {0.f, 0.f, 0.f, 0.f};   // per-lane partial row sums of G = P1 * S (fp32)
-  float bins[RB][4][J + 1];
+  // dlambda of levels 5..J of row 4 g4 + (jj & 3) of the block (each lane's row of sum16x4)
+  float bins[RB][J + 1];
   for (int x = 0; x < RB; ++x)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int l = 0; l <= J; ++l) bins[x][r][l] = 0.f;
+    for (int l = 0; l <= J; ++l) bins[x][l] = 0.f;
 #pragma unroll
   for (int x = 0; x < RB; ++x) {
     const int rb = w + NW * x;
@@ -1342,13 +1341,10 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
       if (g4 == 0) colp[w * C + cb * 16 + jj] = colg;
       if (cb < rb) {
         const int lv = 4 + bit_length((unsigned)(rb ^ cb));
+        const float su = sum16x4(u, jj);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float su = sum16(u[r]);
-#pragma unroll
-          for (int l = 5; l <= J; ++l)
-            if (l == lv) bins[x][r][l] += su;
-        }
+        for (int l = 5; l <= J; ++l)
+          if (l == lv) bins[x][l] += su;
       } else if (cb == rb) {
         // levels 0..4 lie inside this diagonal tile: with u_j the row's value at lane j, the
         // partial sums P1_x = u_x + u_{x^1}, P2_x = P1_x + P1_{x^2}, P3_x = P2_x + P2_{x^4} give
@@ -1374,11 +1370,9 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
       }
     }
     // dlambda of the levels across the diagonal tiles (5..J), parked the same way
+    if (jj < 4)
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int l = 5; l <= J; ++l)
-        if (jj == l) ch.lam[(rb * 16 + 4 * g4 + r) * kLamCap + l] = bins[x][r][l];
+      for (int l = 5; l <= J; ++l) ch.lam[(rb * 16 + 4 * g4 + jj) * kLamCap + l] = bins[x][l];
   }
   __syncthreads();
 
@@ -1492,6 +1486,28 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
     for (int r = 0; r < 4; ++r) eai[r] = ch.ea[rb * 16 + 4 * g4 + r];
     const float eao = ro == 0 ? eai[0] : ro == 1 ? eai[1] : ro == 2 ? eai[2] : eai[3];
     float dq_dot = 0.f;   // row io's q . (dq from the nodes)
+    // bf16: the lane's q elements of the row dots below, read once, two per register (rows
+    // 4 g4 + 2h and + 2h + 1 of column t 16 + jj in qp[2t + h], low and high halves)
+    constexpr bool QREG = ES == 2;
+    uint32_t qp[QREG ? 2 * NK : 1];
+    if constexpr (QREG)
+#pragma unroll
+      for (int t = 0; t < NK; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int i = rb * 16 + 4 * g4 + 2 * h;
+          const uint32_t a = __builtin_bit_cast(uint16_t, ch.q[i * CH::RK + t * 16 + jj]);
+          const uint32_t b = __builtin_bit_cast(uint16_t, ch.q[(i + 1) * CH::RK + t * 16 + jj]);
+          qp[2 * t + h] = a | (b << 16);
+        }
+    auto qval = [&](int t, int r) {
+      if constexpr (QREG) {
+        const uint32_t v = qp[2 * t + (r >> 1)];
+        return __builtin_bit_cast(float, (r & 1) ? (v & 0xffff0000u) : (v << 16));
+      } else {
+        return to_f(ch.q[(rb * 16 + 4 * g4 + r) * CH::RK + t * 16 + jj]);
+      }
+    };
     for (int jl = first_set; jl < p.nl;) {
       const int nx = next_set(jl);
       __syncthreads();   // the previous reads of the state image are done
@@ -1518,9 +1534,8 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int i = rb * 16 + 4 * g4 + r;
           aq[t][r] += scl[r] * y[r];
-          part[r] += y[r] * to_f(ch.q[i * CH::RK + t * 16 + jj]);
+          part[r] += y[r] * qval(t, r);
         }
       }
       const float tot = sum16x4(part, jj);
@@ -1661,13 +1676,15 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
 #pragma unroll
   for (int x = 0; x < RB; ++x) {
     const int rb = w + NW * x;
+    {
+      float d[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = rb * 16 + 4 * g4 + r;
+      for (int r = 0; r < 4; ++r) d[r] = rowg[r] - pk[r];
+      const float rs = sum16x4(d, jj);   // row 4 g4 + (jj & 3)
+      const int i = rb * 16 + 4 * g4 + (jj & 3);
       float colsum = 0.f;
       for (int u = 0; u < NW; ++u) colsum += colp[u * C + i];
-      const float sum = sum16(rowg[r] - pk[r]) + dqd[i] - colsum;
-      if (jj == r && i < nv) p.dA[row0 + i] = sum;
+      if (jj < 4 && i < nv) p.dA[row0 + i] = rs + dqd[i] - colsum;
     }
 
     // 6. dlambda of this block's rows: levels 0..J and the levels of step 4's node read-outs
