@@ -75,6 +75,8 @@ struct BwdParams {
   void* u_e;      // [BH][N][dk*dv] in the element type: each chunk's combined right-sibling state
   void* node_lo;  // bf16 only: node - bf16(node), so that hi + lo carries ~16 mantissa bits
   void* u_lo;     // bf16 only: the same for the combined right-sibling states
+  float* ud;      // [BH][ceil(N/8)][dk*dv], in place of u_e when the gradient kernel forms U_c
+                  // itself: what each group of 8 chunks receives from the levels above 2
   float* dA;      // [BH][T]
   int BH, T, L, N, nl, nslot;
   int items;                  // sub-blocks per head over all levels
@@ -334,6 +336,7 @@ struct BwdKernels {
   const void* rn;       // bwd_rn_kernel<T, C, DK, DV>
   const void* rng;      // bwd_rng_kernel<T, C, DK, DV> where its accumulators fit, else null
   const void* grads;    // bwd_grads_kernel<T, C, DK, DV>
+  const void* grads_d;  // bwd_grads_kernel<T, C, DK, DV, true> on the staged path, else null
 };
 
 // per (dtype, chunk) tables, one instantiation unit each; nullptr outside {16,32,64,128}
@@ -1161,9 +1164,17 @@ __device__ __forceinline__ Frag<T> frag_gload(const T* g, int RS, int r, int k, 
 template <int DK, int DV>
 constexpr int grads_waves_per_eu() { return DK * DV <= 64 * 64 ? 2 : 1; }
 
+// whether the gradient kernel stages nodes through shared memory (each thread's share of a node
+// in 1..4 16-byte pieces), rather than reading them by columns of dq
+template <typename T, int C, int DK, int DV>
+constexpr bool grads_staged() {
+  constexpr int NPF = DK * DV / (16 / (int)sizeof(T)) / (64 * Waves<C>::NW);
+  return NPF >= 1 && NPF <= 4 && NPF * (64 * Waves<C>::NW) * (16 / (int)sizeof(T)) == DK * DV;
+}
+
 // LATER: the head has more than one chunk (p.nl > 0), so there are later chunks and Fenwick
 // nodes; the body is compiled once for each case so that none of its loads sits under a branch
-template <typename T, int C, int DK, int DV, bool LATER>
+template <typename T, int C, int DK, int DV, bool LATER, bool DM>
 __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm) {
   constexpr int NW = Waves<C>::NW, RB = Waves<C>::RB, NT = 64 * NW, J = ilog2(C);
   constexpr int ES = (int)sizeof(T), RC = C + 16 / ES;
@@ -1204,7 +1215,8 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   st.fetch(p, bh, c, nv, tid);
   constexpr int EPV = 16 / ES;
   constexpr int NPF = DK * DV / EPV / NT;
-  constexpr bool PF = NPF >= 1 && NPF <= 4 && NPF * NT * EPV == DK * DV;
+  constexpr bool PF = grads_staged<T, C, DK, DV>();
+  static_assert(PF == (NPF >= 1 && NPF <= 4 && NPF * NT * EPV == DK * DV), "staged path");
   // step 4 by columns of dq when a node is too large for the staging's register prefetch
   constexpr bool COLQ = !PF;
   // jl past the last set bit (nothing left to read) loads a valid slot that is never used: the
@@ -1248,12 +1260,46 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
     }
   };
   u32x4 uhi[PF ? NPF : 1], ulo[PF && SPLIT ? NPF : 1];
-  if (PF && later)
+  if (PF && later && !DM)
 #pragma unroll
     for (int u = 0; u < NPF; ++u) uhi[u] = reinterpret_cast<const u32x4*>(u_e)[tid + u * NT];
-  if (PF && SPLIT && later)
+  if (PF && SPLIT && later && !DM)
 #pragma unroll
     for (int u = 0; u < NPF; ++u) ulo[u] = reinterpret_cast<const u32x4*>(u_lo)[tid + u * NT];
+  // DM: U_c is formed here, in fp32, as the tree's down-sweep would: from what the chunk's group
+  // of 8 receives from the levels above 2 (ud) and, for each clear bit j < 3 of c, the right
+  // sibling block at level j inside the group (a target-side state of bwd_rng), decayed:
+  // U = D, then for j = 2, 1, 0 where that sibling exists, U = exp(G(sibling)) U + RN(sibling).
+  // Each thread forms the elements of its own 16-byte pieces; all of it is loaded with the rest.
+  constexpr int NF4 = DM ? NPF * EPV / 4 : 1;   // float4s of a state per thread
+  f32x4 udv[NF4], urn[3][NF4];
+  bool uin[3] = {false, false, false};
+  float ugs[3] = {0.f, 0.f, 0.f};
+  if constexpr (DM && LATER) {
+    static_assert(!DM || PF, "the gradient kernel forms U_c only on the staged path");
+    const float* dsrc = p.ud + ((size_t)bh * ((p.N + 7) >> 3) + (c >> 3)) * SZ;
+    const float* rsrc[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int m = c >> j;
+      uin[j] = j < p.nl && !(m & 1) && m + 1 < ((p.N + (1 << j) - 1) >> j);
+      const int it = uin[j] ? p.rn_off[j] + item_of_sub(j, m + 1) : 0;
+      rsrc[j] = p.rnp + ((size_t)bh * p.items + it) * SZ;
+      ugs[j] = p.gsum[(size_t)bh * p.nslot + (uin[j] ? slot_p(p, j, m + 1) : 0)];
+    }
+#pragma unroll
+    for (int u = 0; u < NPF; ++u)
+#pragma unroll
+      for (int q = 0; q < EPV / 4; ++q) {
+        const size_t at = (size_t)(tid + u * NT) * EPV + 4 * q;
+        udv[u * (EPV / 4) + q] = *reinterpret_cast<const f32x4*>(dsrc + at);
+        // only the blocks that exist (a uniform branch: every one of these loads is waited for
+        // before the first shared-memory write anyway)
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+          if (uin[j]) urn[j][u * (EPV / 4) + q] = *reinterpret_cast<const f32x4*>(rsrc[j] + at);
+      }
+  }
   // the nodes of step 4 are (j, (c >> j) - 1) for the set bits j of c (c < N <= 2^nl), lowest
   // first. Lane l < nl holds node l's slot (slot 0 where bit l is clear) and its block decay
   // (zero where clear), loaded with the rest; step 4 turns them into each node's decay to the
@@ -1282,6 +1328,40 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
     if (later) load_node(sl0, bhi, blo, bok);
   } else {
     if (later) prefetch(sl0);
+  }
+  if constexpr (DM && LATER) {
+    float ue[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) ue[j] = __expf(ugs[j]);
+#pragma unroll
+    for (int k = 0; k < NF4; ++k) {
+      f32x4 x = udv[k];
+#pragma unroll
+      for (int j = 2; j >= 0; --j)
+        if (uin[j]) x = ue[j] * x + urn[j][k];
+      udv[k] = x;
+    }
+    // hi = x rounded to T, lo = the rounding error rounded to T, packed as the copies would be
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const float x = udv[u * (EPV / 4) + e / 4][e % 4];
+        uint32_t hb, lb = 0;
+        if constexpr (SPLIT) {
+          const T h = (T)x;
+          hb = __builtin_bit_cast(uint16_t, h);
+          lb = __builtin_bit_cast(uint16_t, (T)(x - (float)h));
+          if (e & 1) { hw[e / 2] |= hb << 16; lw[e / 2] |= lb << 16; }
+          else { hw[e / 2] = hb; lw[e / 2] = lb; }
+        } else {
+          hw[e] = __builtin_bit_cast(uint32_t, x);
+        }
+      }
+      uhi[u] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+      if constexpr (SPLIT) ulo[u] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+    }
   }
   st.put(ch, tid);
   if (later) {
@@ -1708,13 +1788,15 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   }
 }
 
-template <typename T, int C, int DK, int DV>
+// DM: the gradient kernel forms each chunk's combined right-sibling state itself (from the
+// group's state in ud and the group's own target-side blocks); only on the staged node path
+template <typename T, int C, int DK, int DV, bool DM = false>
 __global__ void __launch_bounds__(64 * Waves<C>::NW)
 __attribute__((amdgpu_waves_per_eu(grads_waves_per_eu<DK, DV>())))
 bwd_grads_kernel(BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
-  if (p.nl > 0) grads_body<T, C, DK, DV, true>(p, sm);
-  else grads_body<T, C, DK, DV, false>(p, sm);
+  if (p.nl > 0) grads_body<T, C, DK, DV, true, DM>(p, sm);
+  else grads_body<T, C, DK, DV, false, false>(p, sm);
 }
 
 }  // namespace bwd
@@ -1727,13 +1809,16 @@ template <typename TY, int C, int DK, int DV>
 BwdKernels make_bwd() {
   const void* rng = nullptr;
   const void* sg = nullptr;
+  const void* gd = nullptr;
   if constexpr (rng_fits<C, DK, DV>()) {
     rng = reinterpret_cast<const void*>(&bwd_rng_kernel<TY, C, DK, DV>);
     sg = reinterpret_cast<const void*>(&bwd_statesg_kernel<TY, C, DK, DV>);
+    if constexpr (grads_staged<TY, C, DK, DV>())
+      gd = reinterpret_cast<const void*>(&bwd_grads_kernel<TY, C, DK, DV, true>);
   }
   return BwdKernels{reinterpret_cast<const void*>(&bwd_states_kernel<TY, C, DK, DV>), sg,
                     reinterpret_cast<const void*>(&bwd_rn_kernel<TY, C, DK, DV>), rng,
-                    reinterpret_cast<const void*>(&bwd_grads_kernel<TY, C, DK, DV>)};
+                    reinterpret_cast<const void*>(&bwd_grads_kernel<TY, C, DK, DV>), gd};
 }
 
 template <typename TY, int C, int DK_>

@@ -243,9 +243,13 @@ __host__ __device__ inline int gtree_floats(int N, int nl, int nslot, int VE) {
 
 // GROUPED: bwd_statesg has done levels 0..3 of every group (nodes written, the group in fp32 at
 // its level-3 slot); the tree then starts from the groups
-template <typename E, bool GROUPED, int VE>
+// DOUT (grouped only): the down-sweep stops at the groups and writes what each group receives
+// from the levels above 2, in fp32, to ud; the gradient kernel finishes it per chunk from the
+// group's target-side blocks of levels 0..2 (which this kernel then never reads)
+template <typename E, bool GROUPED, int VE, bool DOUT = false>
 __global__ void __launch_bounds__(64 * kTreeWaves) __attribute__((amdgpu_waves_per_eu(VE > 1 ? 4 : 8)))
 bwd_gtree_kernel(BwdParams p, int SZ) {
+  static_assert(GROUPED || !DOUT, "group states out only with the grouped start");
   extern __shared__ __attribute__((aligned(16))) float tl[];
   constexpr int SW = 64 * VE;   // elements per workgroup (one shared-memory slot)
   typedef float FV __attribute__((ext_vector_type(VE)));
@@ -304,17 +308,19 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) d.x[k] = ld(nd, min(c0 + k, N - 1));
     }
+    if constexpr (!DOUT) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const int sb = c0 + 2 * h + 1;                       // level 0: chunk 2h+1 of the group
-      d.r0[h] = ld(rp, item(0, sb, 0 < nl && sb < N));
-    }
+      for (int h = 0; h < 4; ++h) {
+        const int sb = c0 + 2 * h + 1;                     // level 0: chunk 2h+1 of the group
+        d.r0[h] = ld(rp, item(0, sb, 0 < nl && sb < N));
+      }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int sb = 4 * g + 2 * h + 1;
-      d.r1[h] = ld(rp, item(1, sb, 1 < nl && sb < nb(1)));
+      for (int h = 0; h < 2; ++h) {
+        const int sb = 4 * g + 2 * h + 1;
+        d.r1[h] = ld(rp, item(1, sb, 1 < nl && sb < nb(1)));
+      }
+      d.r2 = ld(rp, item(2, 2 * g + 1, 2 < nl && 2 * g + 1 < nb(2)));
     }
-    d.r2 = ld(rp, item(2, 2 * g + 1, 2 < nl && 2 * g + 1 < nb(2)));
     d.r3 = ld(rp, item(3, g + 1, 3 < nl && !(g & 1) && g + 1 < ng));
 #pragma unroll
     for (int u = 0; u < kGtCt; ++u) {
@@ -420,6 +426,11 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
     const int c0 = g << kGrpLog;
     const FV par3 = 4 < nl ? tvs(p.gtlv[4] + (g >> 1)) : zero;
     const FV d3 = (3 < nl && !(g & 1) && g + 1 < ng) ? __expf(G(3, g + 1)) * par3 + d.r3 : par3;
+    if constexpr (DOUT) {
+      reinterpret_cast<__attribute__((address_space(1))) FV*>(
+          uniform_ptr(p.ud + ((size_t)bh * ng + g) * SZ + e0))[ul] = d3;
+      return;
+    }
     FV d2[2], d1[4];
     d2[0] = (2 < nl && 2 * g + 1 < nb(2)) ? __expf(G(2, 2 * g + 1)) * d3 + d.r2 : d3;
     d2[1] = d3;
@@ -500,18 +511,23 @@ namespace {
 // the group tree's instance for an element type, a grouped start and VE elements per lane (at
 // most 2 without the grouped start, whose eight chunk states per group would not fit the
 // registers at 4)
-template <typename E, bool GROUPED>
+template <typename E, bool GROUPED, bool DOUT = false>
 const void* gtree_fn_ve(int ve) {
   using namespace lla::bwd;
   if constexpr (GROUPED)
-    if (ve == 4) return reinterpret_cast<const void*>(&bwd_gtree_kernel<E, GROUPED, 4>);
-  if (ve == 2) return reinterpret_cast<const void*>(&bwd_gtree_kernel<E, GROUPED, 2>);
-  if (ve == 1) return reinterpret_cast<const void*>(&bwd_gtree_kernel<E, GROUPED, 1>);
+    if (ve == 4) return reinterpret_cast<const void*>(&bwd_gtree_kernel<E, GROUPED, 4, DOUT>);
+  if (ve == 2) return reinterpret_cast<const void*>(&bwd_gtree_kernel<E, GROUPED, 2, DOUT>);
+  if (ve == 1) return reinterpret_cast<const void*>(&bwd_gtree_kernel<E, GROUPED, 1, DOUT>);
   return nullptr;
 }
-const void* gtree_fn(bool bf, bool grouped, int ve) {
-  if (bf) return grouped ? gtree_fn_ve<lla::bf16, true>(ve) : gtree_fn_ve<lla::bf16, false>(ve);
-  return grouped ? gtree_fn_ve<float, true>(ve) : gtree_fn_ve<float, false>(ve);
+// dout: the down-sweep stops at the groups (grouped only)
+const void* gtree_fn(bool bf, bool grouped, int ve, bool dout) {
+  if (bf) {
+    if (!grouped) return gtree_fn_ve<lla::bf16, false>(ve);
+    return dout ? gtree_fn_ve<lla::bf16, true, true>(ve) : gtree_fn_ve<lla::bf16, true>(ve);
+  }
+  if (!grouped) return gtree_fn_ve<float, false>(ve);
+  return dout ? gtree_fn_ve<float, true, true>(ve) : gtree_fn_ve<float, true>(ve);
 }
 
 using lla::bwd::BwdKernels;
@@ -687,6 +703,9 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
   p.u_e = w + pl.off_u_e;
   p.node_lo = w + pl.off_node_lo;
   p.u_lo = w + pl.off_u_lo;
+  // the group states when the gradient kernel forms U_c itself, in U's region (ceil(N/8) fp32
+  // states per head take no more room than N element-type ones for N >= 2)
+  p.ud = reinterpret_cast<float*>(w + pl.off_u_e);
   p.dA = reinterpret_cast<float*>(w + pl.off_dA);
   p.BH = (int)pl.BH; p.T = a.T; p.L = pl.L; p.N = pl.N; p.nl = pl.nl; p.nslot = pl.nslot;
   for (int i = 0; i <= lla::kLamCap; ++i) {
@@ -702,11 +721,15 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
   const int NT = 64 * (pl.C >= 64 ? 4 : pl.C / 16);
   const dim3 chunks((unsigned)pl.N, (unsigned)pl.BH);
 
+  // the chunk states: by groups of 8 chunks with the groups' part of the up-sweep when the
+  // group tree runs and the kernel exists for the shape, else one workgroup per chunk; with the
+  // grouped start and the staged gradient kernel, the tree hands over group states and the
+  // gradient kernel forms each chunk's combined right-sibling state
+  const bool grouped = pl.nl > 0 && pl.gtree_smem > 0 && ks->statesg;
+  const bool dmode = grouped && ks->grads_d;
+  const void* grads = dmode ? ks->grads_d : ks->grads;
   if (mark(0) != hipSuccess) return LLA_ERR_HIP;
   if (pl.nl > 0) {
-    // the chunk states: by groups of 8 chunks with the groups' part of the up-sweep when the
-    // group tree runs and the kernel exists for the shape, else one workgroup per chunk
-    const bool grouped = pl.gtree_smem > 0 && ks->statesg;
     const long long ng = (pl.N + 7) / 8;
     if (grouped) {
       if (set_smem(ks->statesg, pl.smem_states) != hipSuccess) return LLA_ERR_HIP;
@@ -741,7 +764,7 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
     if (pl.gtree_smem > 0) {
       // the shared memory planned for VE elements per lane covers any smaller VE
       const int ve = grouped || pl.gtree_ve < 2 ? pl.gtree_ve : 2;
-      const void* fn = gtree_fn(bf, grouped, ve);
+      const void* fn = gtree_fn(bf, grouped, ve, dmode);
       if (!fn) return LLA_ERR_UNSUPPORTED;
       if (set_smem(fn, pl.gtree_smem) != hipSuccess) return LLA_ERR_HIP;
       void* targs[] = {&p, const_cast<int*>(&SZ)};
@@ -756,9 +779,9 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
     if (hipGetLastError() != hipSuccess) return LLA_ERR_HIP;
   }
   if (mark(1) != hipSuccess) return LLA_ERR_HIP;
-  if (set_smem(ks->grads, pl.smem_grads) != hipSuccess) return LLA_ERR_HIP;
+  if (set_smem(grads, pl.smem_grads) != hipSuccess) return LLA_ERR_HIP;
   // one-dimensional: the kernel maps workgroups to (chunk, head) so that each XCD keeps to its heads
-  if (hipLaunchKernel(ks->grads, dim3((unsigned)(pl.N * pl.BH)), dim3(NT), args, pl.smem_grads,
+  if (hipLaunchKernel(grads, dim3((unsigned)(pl.N * pl.BH)), dim3(NT), args, pl.smem_grads,
                       stream) != hipSuccess)
     return LLA_ERR_HIP;
   if (mark(2) != hipSuccess) return LLA_ERR_HIP;
