@@ -379,16 +379,17 @@ def gdn_algorithmic(w, chunk: int) -> tuple[float, float]:
     inverse of the C x C triangular matrix (~C^2/3 per token), W and U (C dk and C dv), the query
     rows' transport X0 (C dk), the in-chunk attention matrix (C^2) and its product with V (C dv),
     the leaf state and transition (dk dv and dk^2); then per Fenwick node read (log2(T/C)/2 on
-    average) X N (dk dv) and, for all but the last, X Phi (dk^2); the up-sweep is one level-j node
-    per 2^j chunks (below 1% here). Bytes: q, k, v, out in the element type, log_a and beta and
-    the L lambda levels in float32."""
+    average) X N (dk dv) and, for all but the last, X Phi (dk^2); the up-sweep builds the n - 1
+    nodes above the n chunks of a head, each Phi_R [N_L | Phi_L] (dk^2 (dv + dk)), spread over the
+    head's T tokens. Bytes: q, k, v, out in the element type, log_a and beta and the L lambda
+    levels in float32."""
     import math
     e = 2 if w.dtype == "bf16" else 4
     C, dk, dv = chunk, w.dk, w.dv
     n = max(1, -(-w.T // C))
     pbar = math.log2(n) / 2 if n > 1 else 0.0
     mac = (2 * C * dk + C * C / 3 + C * dk + C * dv + C * dk + C * C + C * dv + dk * dv + dk * dk
-           + pbar * dk * dv + max(pbar - 1, 0) * dk * dk)
+           + pbar * dk * dv + max(pbar - 1, 0) * dk * dk + (n - 1) * dk * dk * (dv + dk) / w.T)
     byts = (2 * dk + 2 * dv) * e + 8 + 4 * w.L
     return 2 * mac, byts
 
@@ -397,7 +398,7 @@ def gdn_measure(dev, stream, steps: int = 10, warmup: int = 2) -> dict:
     """Log-linear Gated DeltaNet (``loglinear_attn_gdn_fwd``) at the headline's shape (B=4, H=16,
     T=8192, d=64, bf16, keys L2-normalised, beta = sigmoid(N(0,1))): time per call between events,
     per-stage times from the library's events, tokens/s, and its roofline. Its products run in
-    float32 on the vector units, so the bound is the float32 rate (157.3 TFLOP/s); the HBM
+    float32 on the matrix cores, so the bound is the float32 rate (157.3 TFLOP/s); the HBM
     fraction is reported beside it."""
     import torch
     import log_linear_attention_chunked_amd as lla

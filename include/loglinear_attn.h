@@ -419,7 +419,7 @@ int loglinear_attn_bwd_default_chunk(int dk, int dv, int dtype);
  *           share it.
  *   stage_events : optional hipEvent_t recorded on `stream`: [0] before the per-chunk kernel,
  *           [1] before the tree up-sweep, [2] before the query kernel, [3] after it.
- * Every product is float32 on the vector units; the launches are gdn_chunk (one workgroup per
+ * Every product is float32 on the matrix cores; the launches are gdn_chunk (one workgroup per
  * chunk and head), one gdn_upsweep per tree level, and gdn_query. Asynchronous on `stream`,
  * deterministic; returns LLA_OK or a negative LLA_ERR_*; B*H*T = 0 is a no-op.
  */
@@ -445,7 +445,8 @@ int loglinear_attn_gdn_fwd(const lla_gdn_args* args, lla_stream_t stream);
 /* Bytes of workspace loglinear_attn_gdn_fwd needs (0 for invalid or unsupported arguments). */
 size_t loglinear_attn_gdn_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype);
 
-/* Chunk loglinear_attn_gdn_fwd uses when chunk is 0: the largest of 64, 32, 16 that fits. */
+/* Chunk loglinear_attn_gdn_fwd uses when chunk is 0: 32 where it fits (every supported head
+ * size; measured fastest or tied with the best at every measured shape), else 16. */
 int loglinear_attn_gdn_default_chunk(int dk, int dv, int dtype);
 
 #ifdef __cplusplus

@@ -55,9 +55,15 @@ bool fits(int C, int dk, int dv) {
   return chunk_smem_bytes(C, dk, dv) <= lla::kLdsPerCU && query_smem_bytes(C, dk, dv) <= lla::kLdsPerCU;
 }
 
-// the largest chunk of 64, 32, 16 whose kernels fit shared memory
+// chunk 32 where it fits (every supported head size), else 16. Measured on MI355X (time per
+// call, chunks 64 / 32 / 16): 2.12 / 1.86 / 2.46 ms at B=4, H=16, T=8192, d=64 (bf16 and fp32
+// alike); 0.40 / 0.27 / 0.32 ms at d=16 and 0.95 / 0.58 / 0.71 ms at d=32 there; 0.146 / 0.143 /
+// 0.188 ms at B=2, H=8, T=2048, d=64; 2.26 / 1.95 / 2.59 ms at B=1, H=16, T=32768, d=64;
+// - / 1.33 / 1.96 ms at B=1, H=8, T=8192, d=128. At chunk 64 one workgroup of the chunk kernel
+// fills a compute unit's shared memory (140 KB at d=64); at 32 two fit, and the chunk kernel's
+// C^2 and C*d^2 work per chunk shrinks faster than the longer tree grows
 int default_chunk(int dk, int dv) {
-  for (int C : {64, 32, 16})
+  for (int C : {32, 16})
     if (fits(C, dk, dv)) return C;
   return 0;
 }

@@ -464,17 +464,22 @@ def test_gdn_defaults_workspace_and_noop(L, monkeypatch):
     assert L.loglinear_attn_gdn_fwd(None, None) == _lib.LLA_ERR_INVALID_ARG
     for kw in (dict(B=0), dict(T=0), dict(T=0, q=None)):
         assert L.loglinear_attn_gdn_fwd(ctypes.byref(_gargs(**kw)), None) == _lib.LLA_OK
-    assert L.loglinear_attn_gdn_default_chunk(64, 64, 0) == 64
+    # chunk 32 wherever it fits (every supported head size)
+    assert L.loglinear_attn_gdn_default_chunk(64, 64, 0) == 32
     assert L.loglinear_attn_gdn_default_chunk(128, 128, 0) == 32
     assert L.loglinear_attn_gdn_default_chunk(128, 64, 1) == 32
-    assert L.loglinear_attn_gdn_default_chunk(16, 16, 1) == 64
+    assert L.loglinear_attn_gdn_default_chunk(16, 16, 1) == 32
     assert L.loglinear_attn_gdn_default_chunk(48, 64, 0) == 0
     ws = L.loglinear_attn_gdn_workspace_bytes
     # B=4, H=16, T=8192, d=64, chunk 64: outputs and query rows in fp32; 128 chunks, whose
     # indices have bits 0..6, so tree levels 0..6: 128 + 64 + ... + 2 = 254 slots of a 64 x 64
     # state and a 64 x 64 transition per head
-    n = ws(4, 16, 8192, 64, 64, 0, 0)
+    n = ws(4, 16, 8192, 64, 64, 64, 0)
     expect = 64 * 8192 * (64 + 64) * 4 + 64 * 254 * (64 * 64 * 2) * 4
+    assert expect <= n <= expect + 4 * 256
+    # the default chunk 32: 256 chunks, levels 0..7, 256 + 128 + ... + 2 = 510 slots
+    n = ws(4, 16, 8192, 64, 64, 0, 0)
+    expect = 64 * 8192 * (64 + 64) * 4 + 64 * 510 * (64 * 64 * 2) * 4
     assert expect <= n <= expect + 4 * 256
     assert ws(1, 1, 64, 64, 64, 64, 0) > 0          # one chunk: a leaf, no levels above it
     assert ws(1, 1, 64, 64, 64, 128, 0) == 0         # unsupported -> 0
