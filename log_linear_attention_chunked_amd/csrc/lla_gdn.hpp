@@ -180,7 +180,13 @@ __host__ __device__ constexpr int chunk_smem_bytes(int C, int DK, int DV) {
   return 4 * (2 * C * (DK + 1) + C * (DV + 1) + 3 * C * (C + 1) + C * (DK + 1) + C * (DV + 1) +
               C * kLamCapG + 3 * C);
 }
-__host__ __device__ constexpr int up_smem_bytes(int DK) { return 4 * (DK * (DK + 1) + DK * 17); }
+// up-sweep panel width: the whole [N | Phi] row (WHOLE: one workgroup per node, the right
+// child's transition read once; for dk <= 64, at levels with enough nodes to fill the device) or
+// 16 columns (more, shorter workgroups, each reading the transition again)
+__host__ __device__ constexpr int up_panel(int DK, int DV, bool whole) { return whole ? DV + DK : 16; }
+__host__ __device__ constexpr int up_smem_bytes(int DK, int DV, bool whole) {
+  return 4 * (DK * (DK + 1) + DK * (up_panel(DK, DV, whole) + 1));
+}
 __host__ __device__ constexpr int query_smem_bytes(int C, int DK, int DV) {
   return 4 * (2 * C * (DK + 1) + C * (DV + 1) + DK * ((DK > DV ? DK : DV) + 1) + C * kLamCapG);
 }
@@ -332,21 +338,22 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
   });
 }
 
-// shared-memory layout of gdn_upsweep: the right child's transition and one 16-column panel
-template <int DK>
+// shared-memory layout of gdn_upsweep: the right child's transition and one panel of the left
+// child's [N | Phi]
+template <int DK, int DV, bool WHOLE>
 struct UpSmem {
-  static constexpr int SP = DK + 1, PW = 16, SW = PW + 1;
+  static constexpr int SP = DK + 1, PW = up_panel(DK, DV, WHOLE), SW = PW + 1;
   static constexpr int PHI = 0, PAN = PHI + DK * SP, TOTAL = PAN + DK * SW;
   static constexpr int BYTES = TOTAL * 4;
-  static_assert(BYTES == up_smem_bytes(DK), "layout and size formula agree");
+  static_assert(BYTES == up_smem_bytes(DK, DV, WHOLE), "layout and size formula agree");
 };
 
 // gdn_upsweep (level j >= 1): node (j, m) from its children L = (j-1, 2m), R = (j-1, 2m+1):
 //   [N | Phi](j, m) = Phi_R [N_L | Phi_L] + [N_R | 0]
-// one workgroup per (node, head, 16-column panel of [N | Phi]).
-template <int DK, int DV>
+// one workgroup per (node, head, panel of [N | Phi]); WHOLE: the panel is the whole row.
+template <int DK, int DV, bool WHOLE>
 __global__ __launch_bounds__(kNT) void gdn_upsweep_kernel(GdnParams p) {
-  using S = UpSmem<DK>;
+  using S = UpSmem<DK, DV, WHOLE>;
   constexpr int SP = S::SP, PW = S::PW, SW = S::SW, NPAN = (DV + DK) / PW;
   extern __shared__ float sm[];
   float* Pr = sm + S::PHI;
@@ -357,29 +364,52 @@ __global__ __launch_bounds__(kNT) void gdn_upsweep_kernel(GdnParams p) {
   const int m = rest % p.ncur, bh = rest / p.ncur;
   const size_t base = (size_t)bh * p.nslot;
   const size_t sl = base + p.off_prev + 2 * m, sr = sl + 1, so = base + p.off_cur + m;
-  const bool isN = pan * PW < DV;                      // panel of N (else of Phi)
-  const int col0 = isN ? pan * PW : pan * PW - DV;
-  {
-    StagedBlock<float, DK, DK> sp;
-    StagedBlock<float, DK, PW> sc;
-    sp.load(p.phi + sr * DK * DK, DK, DK, tid);
-    if (isN) sc.load(p.node + sl * DK * DV + col0, DV, DK, tid);
-    else sc.load(p.phi + sl * DK * DK + col0, DK, DK, tid);
-    sp.store(Pr, SP, tid);
-    sc.store(Pan, SW, tid);
-  }
-  __syncthreads();
-  if (isN) {
-    float* out = p.node + so * DK * DV;
-    const float* nr = p.node + sr * DK * DV;
-    gemm_f32<DK, PW, DK, false, false>(Pr, SP, Pan, SW, tid, [&](int r, int cc, float x) {
-      out[(size_t)r * DV + col0 + cc] = x + nr[(size_t)r * DV + col0 + cc];
+  const float* nr = p.node + sr * DK * DV;
+  if constexpr (WHOLE) {
+    {
+      StagedBlock<float, DK, DK> sp, sf;
+      StagedBlock<float, DK, DV> sn;
+      sp.load(p.phi + sr * DK * DK, DK, DK, tid);
+      sn.load(p.node + sl * DK * DV, DV, DK, tid);
+      sf.load(p.phi + sl * DK * DK, DK, DK, tid);
+      sp.store(Pr, SP, tid);
+      sn.store(Pan, SW, tid);
+      sf.store(Pan + DV, SW, tid);
+    }
+    __syncthreads();
+    float* on = p.node + so * DK * DV;
+    float* of = p.phi + so * DK * DK;
+    // the N columns, then the Phi columns (two products, each over its own output tiles)
+    gemm_f32<DK, DV, DK, false, false>(Pr, SP, Pan, SW, tid, [&](int r, int cc, float x) {
+      on[(size_t)r * DV + cc] = x + nr[(size_t)r * DV + cc];
+    });
+    gemm_f32<DK, DK, DK, false, false>(Pr, SP, Pan + DV, SW, tid, [&](int r, int cc, float x) {
+      of[(size_t)r * DK + cc] = x;
     });
   } else {
-    float* out = p.phi + so * DK * DK;
-    gemm_f32<DK, PW, DK, false, false>(Pr, SP, Pan, SW, tid, [&](int r, int cc, float x) {
-      out[(size_t)r * DK + col0 + cc] = x;
-    });
+    const bool isN = pan * PW < DV;                      // panel of N (else of Phi)
+    const int col0 = isN ? pan * PW : pan * PW - DV;
+    {
+      StagedBlock<float, DK, DK> sp;
+      StagedBlock<float, DK, PW> sc;
+      sp.load(p.phi + sr * DK * DK, DK, DK, tid);
+      if (isN) sc.load(p.node + sl * DK * DV + col0, DV, DK, tid);
+      else sc.load(p.phi + sl * DK * DK + col0, DK, DK, tid);
+      sp.store(Pr, SP, tid);
+      sc.store(Pan, SW, tid);
+    }
+    __syncthreads();
+    if (isN) {
+      float* out = p.node + so * DK * DV;
+      gemm_f32<DK, PW, DK, false, false>(Pr, SP, Pan, SW, tid, [&](int r, int cc, float x) {
+        out[(size_t)r * DV + col0 + cc] = x + nr[(size_t)r * DV + col0 + cc];
+      });
+    } else {
+      float* out = p.phi + so * DK * DK;
+      gemm_f32<DK, PW, DK, false, false>(Pr, SP, Pan, SW, tid, [&](int r, int cc, float x) {
+        out[(size_t)r * DK + col0 + cc] = x;
+      });
+    }
   }
 }
 

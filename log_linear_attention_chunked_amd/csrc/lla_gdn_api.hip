@@ -30,25 +30,29 @@ const GdnKernels* gdn_kernels(int dtype, int C, int dk, int dv) {
 }
 
 // the up-sweep kernel depends on (dk, dv) only
-template <int DK>
+template <int DK, bool WHOLE>
 const void* upsweep_for_dv(int dv) {
   switch (dv) {
-    case 16: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep_kernel<DK, 16>);
-    case 32: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep_kernel<DK, 32>);
-    case 64: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep_kernel<DK, 64>);
-    case 128: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep_kernel<DK, 128>);
+    case 16: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep_kernel<DK, 16, WHOLE>);
+    case 32: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep_kernel<DK, 32, WHOLE>);
+    case 64: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep_kernel<DK, 64, WHOLE>);
+    case 128: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep_kernel<DK, 128, WHOLE>);
   }
   return nullptr;
 }
-const void* upsweep_kernel(int dk, int dv) {
+// whole rows only for dk <= 64 (a 128 x 128 transition fills 66 KB of shared memory by itself)
+const void* upsweep_kernel(int dk, int dv, bool whole) {
   switch (dk) {
-    case 16: return upsweep_for_dv<16>(dv);
-    case 32: return upsweep_for_dv<32>(dv);
-    case 64: return upsweep_for_dv<64>(dv);
-    case 128: return upsweep_for_dv<128>(dv);
+    case 16: return whole ? upsweep_for_dv<16, true>(dv) : upsweep_for_dv<16, false>(dv);
+    case 32: return whole ? upsweep_for_dv<32, true>(dv) : upsweep_for_dv<32, false>(dv);
+    case 64: return whole ? upsweep_for_dv<64, true>(dv) : upsweep_for_dv<64, false>(dv);
+    case 128: return whole ? nullptr : upsweep_for_dv<128, false>(dv);
   }
   return nullptr;
 }
+// a level's nodes times heads from which one workgroup per node beats 16-column panels (at
+// fewer, the panels' extra workgroups fill the device better)
+constexpr long kUpWholeMin = 1024;
 
 bool fits(int C, int dk, int dv) {
   using namespace lla::gdn;
@@ -131,7 +135,8 @@ hipError_t set_smem(const void* fn, int bytes) {
 int launch(const lla_gdn_args& a, const GdnPlan& pl, void* ws, hipStream_t stream) {
   using namespace lla::gdn;
   const GdnKernels* ks = gdn_kernels(a.dtype, pl.C, a.dk, a.dv);
-  const void* up = upsweep_kernel(a.dk, a.dv);
+  const void* up = upsweep_kernel(a.dk, a.dv, false);
+  const void* upw = upsweep_kernel(a.dk, a.dv, true);   // null at dk = 128
   if (!ks || !up) return LLA_ERR_UNSUPPORTED;
   GdnParams p;
   memset(&p, 0, sizeof(p));
@@ -148,7 +153,7 @@ int launch(const lla_gdn_args& a, const GdnPlan& pl, void* ws, hipStream_t strea
   };
   const unsigned grid = (unsigned)(pl.N * pl.BH);
   const int sc = chunk_smem_bytes(pl.C, a.dk, a.dv), sq = query_smem_bytes(pl.C, a.dk, a.dv);
-  const int su = up_smem_bytes(a.dk);
+  const int su = up_smem_bytes(a.dk, a.dv, false), suw = up_smem_bytes(a.dk, a.dv, true);
   if (mark(0) != hipSuccess) return LLA_ERR_HIP;
   {
     void* args[] = {&p};
@@ -157,6 +162,7 @@ int launch(const lla_gdn_args& a, const GdnPlan& pl, void* ws, hipStream_t strea
   }
   if (mark(1) != hipSuccess) return LLA_ERR_HIP;
   if (set_smem(up, su) != hipSuccess) return LLA_ERR_HIP;
+  if (upw && set_smem(upw, suw) != hipSuccess) return LLA_ERR_HIP;
   int off_prev = 0;
   for (int j = 1; j <= pl.top; ++j) {
     GdnParams pj = p;
@@ -166,8 +172,10 @@ int launch(const lla_gdn_args& a, const GdnPlan& pl, void* ws, hipStream_t strea
     pj.ncur = pl.N >> j;
     off_prev = pj.off_cur;
     void* args[] = {&pj};
-    const unsigned g = (unsigned)((long)pj.ncur * pl.BH * ((a.dv + a.dk) / 16));
-    if (hipLaunchKernel(up, dim3(g), dim3(kNT), args, su, stream) != hipSuccess) return LLA_ERR_HIP;
+    const bool whole = upw && (long)pj.ncur * pl.BH >= kUpWholeMin;
+    const unsigned g = (unsigned)((long)pj.ncur * pl.BH * ((a.dv + a.dk) / up_panel(a.dk, a.dv, whole)));
+    if (hipLaunchKernel(whole ? upw : up, dim3(g), dim3(kNT), args, whole ? suw : su, stream) != hipSuccess)
+      return LLA_ERR_HIP;
   }
   if (mark(2) != hipSuccess) return LLA_ERR_HIP;
   {
