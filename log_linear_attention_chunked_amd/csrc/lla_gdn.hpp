@@ -443,6 +443,23 @@ __global__ __launch_bounds__(kNT) void gdn_query_kernel(GdnParams p) {
   const int nv = min(C, p.T - t0);
   const size_t row0 = (size_t)bh * p.T + t0;
   const size_t wrow0 = ((size_t)bh * p.nchunks + c) * C;
+  // slot of node (j, m) of this head: the levels below j come first
+  auto slot_of = [&](int j, int m) {
+    int off = 0;
+    for (int i = 0; i < j; ++i) off += p.nchunks >> i;
+    return (size_t)bh * p.nslot + off + m;
+  };
+  // the set bit of c after j (the next node), or -1
+  auto next_bit = [&](int j) {
+    const unsigned rest = (unsigned)c >> (j + 1);
+    return rest ? j + 1 + __builtin_ctz(rest) : -1;
+  };
+  // up to d = 64 the next node's state and transition travel in registers while the current one
+  // is read out (one memory round trip per node instead of two, none for the first)
+  constexpr bool PRE = DK <= 64;
+  StagedBlock<float, DK, PRE ? DV : 16> nb;
+  StagedBlock<float, DK, PRE ? DK : 16> fb;
+  int j = c ? __builtin_ctz((unsigned)c) : -1;
   {
     StagedBlock<float, C, DK> sx;
     StagedBlock<float, C, DV> so;
@@ -450,34 +467,46 @@ __global__ __launch_bounds__(kNT) void gdn_query_kernel(GdnParams p) {
     sx.load(p.x0 + wrow0 * DK, DK, C, tid);
     so.load(p.oi + wrow0 * DV, DV, C, tid);
     sl.load(p, row0, nv, tid);
+    if constexpr (PRE) {
+      if (j >= 0) {
+        const size_t slot = slot_of(j, (c >> j) - 1);
+        nb.load(p.node + slot * DK * DV, DV, DK, tid);
+        if (next_bit(j) >= 0) fb.load(p.phi + slot * DK * DK, DK, DK, tid);
+      }
+    }
     sx.store(Xa, SK, tid);
     so.store(Os, SV, tid);
     sl.store(lam, tid);
   }
   __syncthreads();
-  int off = 0;                 // first slot of level j
-  for (int j = 0; (c >> j) != 0; ++j) {
-    const int cj = c >> j;
-    if (cj & 1) {
-      const size_t slot = (size_t)bh * p.nslot + off + (cj - 1);
-      stage_block<float, DK, DV>(Ms, SM, p.node + slot * DK * DV, DV, DK, tid);
+  while (j >= 0) {
+    const size_t slot = slot_of(j, (c >> j) - 1);
+    const int jn = next_bit(j);
+    if constexpr (PRE) nb.store(Ms, SM, tid);
+    else stage_block<float, DK, DV>(Ms, SM, p.node + slot * DK * DV, DV, DK, tid);
+    __syncthreads();
+    const int lev = J + 1 + j;
+    gemm_f32<C, DV, DK, false, false>(Xa, SK, Ms, SM, tid, [&](int i, int e, float x) {
+      Os[i * SV + e] += lam[i * kLamCapG + lev] * x;
+    });
+    __syncthreads();
+    if (jn >= 0) {           // a higher node follows: X <- X Phi of this node
+      if constexpr (PRE) {
+        fb.store(Ms, SM, tid);
+        const size_t sn = slot_of(jn, (c >> jn) - 1);
+        nb.load(p.node + sn * DK * DV, DV, DK, tid);
+        if (next_bit(jn) >= 0) fb.load(p.phi + sn * DK * DK, DK, DK, tid);
+      } else {
+        stage_block<float, DK, DK>(Ms, SM, p.phi + slot * DK * DK, DK, DK, tid);
+      }
       __syncthreads();
-      const int lev = J + 1 + j;
-      gemm_f32<C, DV, DK, false, false>(Xa, SK, Ms, SM, tid, [&](int i, int e, float x) {
-        Os[i * SV + e] += lam[i * kLamCapG + lev] * x;
+      gemm_f32<C, DK, DK, false, false>(Xa, SK, Ms, SM, tid, [&](int i, int d, float x) {
+        Xb[i * SK + d] = x;
       });
       __syncthreads();
-      if ((c >> (j + 1)) != 0) {           // a higher node follows: X <- X Phi of this node
-        stage_block<float, DK, DK>(Ms, SM, p.phi + slot * DK * DK, DK, DK, tid);
-        __syncthreads();
-        gemm_f32<C, DK, DK, false, false>(Xa, SK, Ms, SM, tid, [&](int i, int d, float x) {
-          Xb[i * SK + d] = x;
-        });
-        __syncthreads();
-        float* tmp = Xa; Xa = Xb; Xb = tmp;
-      }
+      float* tmp = Xa; Xa = Xb; Xb = tmp;
     }
-    off += p.nchunks >> j;
+    j = jn;
   }
   T* og = reinterpret_cast<T*>(p.out);
   for (int i = tid; i < C * DV; i += kNT) {
