@@ -336,7 +336,7 @@ struct BwdKernels {
   const void* rn;       // bwd_rn_kernel<T, C, DK, DV>
   const void* rng;      // bwd_rng_kernel<T, C, DK, DV> where its accumulators fit, else null
   const void* grads;    // bwd_grads_kernel<T, C, DK, DV>
-  const void* grads_d;  // bwd_grads_kernel<T, C, DK, DV, true> on the staged path, else null
+  const void* grads_d;  // bwd_grads_kernel<T, C, DK, DV, true>: forms U_c from the tree's group states
 };
 
 // per (dtype, chunk) tables, one instantiation unit each; nullptr outside {16,32,64,128}
@@ -1271,14 +1271,14 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   // sibling block at level j inside the group (a target-side state of bwd_rng), decayed:
   // U = D, then for j = 2, 1, 0 where that sibling exists, U = exp(G(sibling)) U + RN(sibling).
   // Each thread forms the elements of its own 16-byte pieces; all of it is loaded with the rest.
-  constexpr int NF4 = DM ? NPF * EPV / 4 : 1;   // float4s of a state per thread
+  constexpr int NF4 = DM && PF ? NPF * EPV / 4 : 1;   // float4s of a state per thread
   f32x4 udv[NF4], urn[3][NF4];
   bool uin[3] = {false, false, false};
   float ugs[3] = {0.f, 0.f, 0.f};
+  const float* dsrc = p.ud;
+  const float* rsrc[3] = {p.rnp, p.rnp, p.rnp};
   if constexpr (DM && LATER) {
-    static_assert(!DM || PF, "the gradient kernel forms U_c only on the staged path");
-    const float* dsrc = p.ud + ((size_t)bh * ((p.N + 7) >> 3) + (c >> 3)) * SZ;
-    const float* rsrc[3];
+    dsrc = p.ud + ((size_t)bh * ((p.N + 7) >> 3) + (c >> 3)) * SZ;
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       const int m = c >> j;
@@ -1287,6 +1287,55 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
       rsrc[j] = p.rnp + ((size_t)bh * p.items + it) * SZ;
       ugs[j] = p.gsum[(size_t)bh * p.nslot + (uin[j] ? slot_p(p, j, m + 1) : 0)];
     }
+  }
+  // the column path (states too large to hold in registers at once): U_c's high or low parts
+  // formed in batches of UB 16-byte pieces per thread straight into a shared-memory image,
+  // each batch's loads issued together
+  auto form_u_img = [&](T* img, bool lo) {
+    constexpr int NP = DK * DV / EPV, PER = (NP + NT - 1) / NT, UB = 2, Q = EPV / 4;
+    float ue[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) ue[j] = __expf(ugs[j]);
+    for (int u0 = 0; u0 < PER; u0 += UB) {
+      f32x4 x[UB][Q], r[3][UB][Q];
+#pragma unroll
+      for (int b = 0; b < UB; ++b) {
+        const int idx = min(tid + (u0 + b) * NT, NP - 1);
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+          const size_t at = (size_t)idx * EPV + 4 * q;
+          x[b][q] = *reinterpret_cast<const f32x4*>(dsrc + at);
+#pragma unroll
+          for (int j = 0; j < 3; ++j)
+            if (uin[j]) r[j][b][q] = *reinterpret_cast<const f32x4*>(rsrc[j] + at);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < UB; ++b) {
+        const int idx = tid + (u0 + b) * NT;
+        if (u0 + b >= PER || idx >= NP) continue;
+        uint32_t wd[4];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          float v = x[b][e / 4][e % 4];
+#pragma unroll
+          for (int j = 2; j >= 0; --j)
+            if (uin[j]) v = ue[j] * v + r[j][b][e / 4][e % 4];
+          if constexpr (SPLIT) {
+            const T h = (T)v;
+            const uint32_t bits = __builtin_bit_cast(uint16_t, lo ? (T)(v - (float)h) : h);
+            if (e & 1) wd[e / 2] |= bits << 16;
+            else wd[e / 2] = bits;
+          } else {
+            wd[e] = __builtin_bit_cast(uint32_t, v);
+          }
+        }
+        const int a = (idx * EPV) / DV, bcol = (idx * EPV) % DV;
+        *reinterpret_cast<u32x4*>(img + a * CH::RV + bcol) = u32x4{wd[0], wd[1], wd[2], wd[3]};
+      }
+    }
+  };
+  if constexpr (DM && LATER && PF) {
 #pragma unroll
     for (int u = 0; u < NPF; ++u)
 #pragma unroll
@@ -1329,7 +1378,7 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   } else {
     if (later) prefetch(sl0);
   }
-  if constexpr (DM && LATER) {
+  if constexpr (DM && LATER && PF) {
     float ue[3];
 #pragma unroll
     for (int j = 0; j < 3; ++j) ue[j] = __expf(ugs[j]);
@@ -1366,6 +1415,7 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   st.put(ch, tid);
   if (later) {
     if constexpr (PF) put(Ust, uhi);
+    else if constexpr (DM) form_u_img(Ust, false);
     else stage_state<T, DK, DV, CH::RV, NT>(Ust, u_e, tid);
   }
   __syncthreads();
@@ -1501,6 +1551,7 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   if (SPLIT && later) {
     __syncthreads();   // P2 is no longer read
     if constexpr (PF) put(Plo, ulo);
+    else if constexpr (DM) form_u_img(Plo, true);
     else stage_state<T, DK, DV, CH::RV, NT>(Plo, u_lo, tid);
     __syncthreads();
   }
@@ -1789,7 +1840,7 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
 }
 
 // DM: the gradient kernel forms each chunk's combined right-sibling state itself (from the
-// group's state in ud and the group's own target-side blocks); only on the staged node path
+// group's state in ud and the group's own target-side blocks)
 template <typename T, int C, int DK, int DV, bool DM = false>
 __global__ void __launch_bounds__(64 * Waves<C>::NW)
 __attribute__((amdgpu_waves_per_eu(grads_waves_per_eu<DK, DV>())))
@@ -1813,9 +1864,8 @@ BwdKernels make_bwd() {
   if constexpr (rng_fits<C, DK, DV>()) {
     rng = reinterpret_cast<const void*>(&bwd_rng_kernel<TY, C, DK, DV>);
     sg = reinterpret_cast<const void*>(&bwd_statesg_kernel<TY, C, DK, DV>);
-    if constexpr (grads_staged<TY, C, DK, DV>())
-      gd = reinterpret_cast<const void*>(&bwd_grads_kernel<TY, C, DK, DV, true>);
   }
+  gd = reinterpret_cast<const void*>(&bwd_grads_kernel<TY, C, DK, DV, true>);
   return BwdKernels{reinterpret_cast<const void*>(&bwd_states_kernel<TY, C, DK, DV>), sg,
                     reinterpret_cast<const void*>(&bwd_rn_kernel<TY, C, DK, DV>), rng,
                     reinterpret_cast<const void*>(&bwd_grads_kernel<TY, C, DK, DV>), gd};

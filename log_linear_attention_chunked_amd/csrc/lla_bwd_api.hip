@@ -243,13 +243,12 @@ __host__ __device__ inline int gtree_floats(int N, int nl, int nslot, int VE) {
 
 // GROUPED: bwd_statesg has done levels 0..3 of every group (nodes written, the group in fp32 at
 // its level-3 slot); the tree then starts from the groups
-// DOUT (grouped only): the down-sweep stops at the groups and writes what each group receives
+// DOUT: the down-sweep stops at the groups and writes what each group receives
 // from the levels above 2, in fp32, to ud; the gradient kernel finishes it per chunk from the
 // group's target-side blocks of levels 0..2 (which this kernel then never reads)
 template <typename E, bool GROUPED, int VE, bool DOUT = false>
 __global__ void __launch_bounds__(64 * kTreeWaves) __attribute__((amdgpu_waves_per_eu(VE > 1 ? 4 : 8)))
 bwd_gtree_kernel(BwdParams p, int SZ) {
-  static_assert(GROUPED || !DOUT, "group states out only with the grouped start");
   extern __shared__ __attribute__((aligned(16))) float tl[];
   constexpr int SW = 64 * VE;   // elements per workgroup (one shared-memory slot)
   typedef float FV __attribute__((ext_vector_type(VE)));
@@ -523,10 +522,10 @@ const void* gtree_fn_ve(int ve) {
 // dout: the down-sweep stops at the groups (grouped only)
 const void* gtree_fn(bool bf, bool grouped, int ve, bool dout) {
   if (bf) {
-    if (!grouped) return gtree_fn_ve<lla::bf16, false>(ve);
+    if (!grouped) return dout ? gtree_fn_ve<lla::bf16, false, true>(ve) : gtree_fn_ve<lla::bf16, false>(ve);
     return dout ? gtree_fn_ve<lla::bf16, true, true>(ve) : gtree_fn_ve<lla::bf16, true>(ve);
   }
-  if (!grouped) return gtree_fn_ve<float, false>(ve);
+  if (!grouped) return dout ? gtree_fn_ve<float, false, true>(ve) : gtree_fn_ve<float, false>(ve);
   return dout ? gtree_fn_ve<float, true, true>(ve) : gtree_fn_ve<float, true>(ve);
 }
 
@@ -722,11 +721,11 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
   const dim3 chunks((unsigned)pl.N, (unsigned)pl.BH);
 
   // the chunk states: by groups of 8 chunks with the groups' part of the up-sweep when the
-  // group tree runs and the kernel exists for the shape, else one workgroup per chunk; with the
-  // grouped start and the staged gradient kernel, the tree hands over group states and the
-  // gradient kernel forms each chunk's combined right-sibling state
+  // group tree runs and the kernel exists for the shape, else one workgroup per chunk; whenever
+  // the group tree runs, it hands over group states and the gradient kernel forms each chunk's
+  // combined right-sibling state (the level-by-level tree still writes U_c)
   const bool grouped = pl.nl > 0 && pl.gtree_smem > 0 && ks->statesg;
-  const bool dmode = grouped && ks->grads_d;
+  const bool dmode = pl.nl > 0 && pl.gtree_smem > 0 && ks->grads_d;
   const void* grads = dmode ? ks->grads_d : ks->grads;
   if (mark(0) != hipSuccess) return LLA_ERR_HIP;
   if (pl.nl > 0) {
