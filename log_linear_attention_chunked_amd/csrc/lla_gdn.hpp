@@ -103,6 +103,56 @@ __device__ __forceinline__ void gemm_f32(const float* A, int lda, const float* B
   }
 }
 
+// Split-bf16 products (bfloat16 inputs): a float32 operand x is held as hi = bf16(x) and
+// lo = bf16(x - hi) (~16 mantissa bits), and a product as hi*hi + hi*lo + lo*hi on the bf16
+// matrix cores (v_mfma_f32_16x16x32_bf16, K = 32 per step), the dropped lo*lo term about 2^-16 of
+// it: float32-grade sums at a fraction of the float32 products' cost.
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4g __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4g lds_s16x4g;
+
+// A(i, k..k+7): row i of a row-major bf16 image, 8 consecutive contraction elements
+__device__ __forceinline__ bf16x8 frag_rows(const bf16* img, int ld, int i, int k) {
+  return *reinterpret_cast<const bf16x8*>(img + i * ld + k);
+}
+// B(k..k+7, n): column n of a row-major bf16 image over 8 consecutive rows, by two transposing
+// reads (ds_read_b64_tr_b16: lane L of a 16-lane group addresses row k + L/4, columns
+// n0 + 4 (L % 4) .. + 3, and receives column n0 + L of rows k .. k + 3)
+__device__ __forceinline__ bf16x8 frag_cols(const bf16* img, int ld, int k, int n) {
+  const int L = n & 15, n0 = n - L;
+  const bf16* q = img + (k + (L >> 2)) * ld + n0 + 4 * (L & 3);
+  const s16x4g a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4g*)q);
+  const s16x4g b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4g*)(q + 4 * ld));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// out(i, j) = sum_k A(i, k) B(k, j) over an M x N output and a K-long contraction, A and B
+// row-major in shared memory as high and low bf16 images (row strides lda, ldb elements, each a
+// multiple of 8); 16 x 16 tiles dealt to the waves in turn, the epilogue as gemm_f32's
+template <int M, int N, int K, typename Epi>
+__device__ __forceinline__ void gemm_bf3(const bf16* Ah, const bf16* Al, int lda, const bf16* Bh,
+                                         const bf16* Bl, int ldb, int tid, Epi&& epi) {
+  static_assert(M % 16 == 0 && N % 16 == 0 && K % 32 == 0, "16 x 16 tiles, 32-deep steps");
+  constexpr int TN = N / 16, NTILE = (M / 16) * TN, NWAVE = kNT / 64;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int j = lane & 15, g = lane >> 4;
+  for (int tile = w; tile < NTILE; tile += NWAVE) {
+    const int i0 = (tile / TN) * 16, j0 = (tile % TN) * 16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < K; k += 32) {
+      const bf16x8 ah = frag_rows(Ah, lda, i0 + j, k + 8 * g), al = frag_rows(Al, lda, i0 + j, k + 8 * g);
+      const bf16x8 bh = frag_cols(Bh, ldb, k + 8 * g, j0 + j), bl = frag_cols(Bl, ldb, k + 8 * g, j0 + j);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) epi(i0 + 4 * g + r, j0 + j, acc[r]);
+  }
+}
+
 // An R x CC row-major block (source row stride src_ld elements) on its way into shared-memory
 // floats dst[r * ldd + c], rows at or past nv read as zeros: load() issues the thread's 16-byte
 // vector loads into registers, store() converts and writes them. Several blocks loaded before
@@ -121,6 +171,30 @@ struct StagedBlock {
       const int v = tid + i * kNT, r = v / VPR;
       buf[i] = u32x4{0u, 0u, 0u, 0u};
       if (v < NVEC && r < nv) buf[i] = *reinterpret_cast<const u32x4*>(src + (size_t)r * src_ld + (v % VPR) * EPV);
+    }
+  }
+  // float32 blocks only: each element as high and low bf16 parts into two images
+  __device__ __forceinline__ void store_split(bf16* hi, bf16* lo, int ldd, int tid) const {
+    static_assert(sizeof(T) == 4, "float32 sources");
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int v = tid + i * kNT;
+      if (v >= NVEC) break;
+      const int at = (v / VPR) * ldd + (v % VPR) * EPV;
+      unsigned hw[2], lw[2];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned word = buf[i][e];
+        const float x = __builtin_bit_cast(float, word);
+        const bf16 h = (bf16)x;
+        const unsigned hb = __builtin_bit_cast(unsigned short, h);
+        const unsigned lb = __builtin_bit_cast(unsigned short, (bf16)(x - (float)h));
+        if (e & 1) { hw[e / 2] |= hb << 16; lw[e / 2] |= lb << 16; }
+        else { hw[e / 2] = hb; lw[e / 2] = lb; }
+      }
+      typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+      *reinterpret_cast<u32x2*>(hi + at) = u32x2{hw[0], hw[1]};
+      *reinterpret_cast<u32x2*>(lo + at) = u32x2{lw[0], lw[1]};
     }
   }
   __device__ __forceinline__ void store(float* dst, int ldd, int tid) const {
@@ -187,8 +261,18 @@ __host__ __device__ constexpr int up_panel(int DK, int DV, bool whole) { return 
 __host__ __device__ constexpr int up_smem_bytes(int DK, int DV, bool whole) {
   return 4 * (DK * (DK + 1) + DK * (up_panel(DK, DV, whole) + 1));
 }
-__host__ __device__ constexpr int query_smem_bytes(int C, int DK, int DV) {
+__host__ __device__ constexpr int query_smem_bytes_f32(int C, int DK, int DV) {
   return 4 * (2 * C * (DK + 1) + C * (DV + 1) + DK * ((DK > DV ? DK : DV) + 1) + C * kLamCapG);
+}
+// bfloat16 inputs: the query rows (two, each high and low parts) and the node matrix (high and
+// low parts) in bf16, rows padded by 8 elements; the outputs and lambda rows in fp32
+__host__ __device__ constexpr int query_smem_bytes_bf3(int C, int DK, int DV) {
+  return 2 * 4 * C * (DK + 8) + 4 * C * (DV + 1) + 2 * 2 * DK * ((DK > DV ? DK : DV) + 8) +
+         4 * C * kLamCapG;
+}
+__host__ __device__ constexpr int query_smem_bytes(int C, int DK, int DV) {
+  return query_smem_bytes_f32(C, DK, DV) > query_smem_bytes_bf3(C, DK, DV) ? query_smem_bytes_f32(C, DK, DV)
+                                                                           : query_smem_bytes_bf3(C, DK, DV);
 }
 
 // shared-memory layout of gdn_chunk (floats; row strides padded by one)
@@ -421,13 +505,130 @@ struct QuerySmem {
   static constexpr int X = 0, XN = X + C * SK, O = XN + C * SK, MAT = O + C * SV,
                        LAM = MAT + DK * SM, TOTAL = LAM + C * kLamCapG;
   static constexpr int BYTES = TOTAL * 4;
-  static_assert(BYTES == query_smem_bytes(C, DK, DV), "layout and size formula agree");
+  static_assert(BYTES == query_smem_bytes_f32(C, DK, DV), "layout and size formula agree");
 };
+
+// shared-memory layout of gdn_query's split-bf16 form (bytes): the query rows (two, high and
+// low parts), outputs (fp32), one node matrix (high and low parts), lambda rows (fp32)
+template <int C, int DK, int DV>
+struct QuerySmemB {
+  static constexpr int SX = DK + 8, SV = DV + 1, MD = DK > DV ? DK : DV, SMB = MD + 8;
+  static constexpr int XB = C * SX * 2, MB = DK * SMB * 2;
+  static constexpr int X = 0, O = X + 4 * XB, MH = O + C * SV * 4, ML = MH + MB, LAM = ML + MB,
+                       TOTAL = LAM + C * kLamCapG * 4;
+  static_assert(TOTAL == query_smem_bytes_bf3(C, DK, DV), "layout and size formula agree");
+  static_assert(XB % 16 == 0 && (C * SV * 4) % 16 == 0 && MB % 16 == 0, "16-byte aligned images");
+};
+
+// gdn_query for bfloat16 inputs (dk >= 32): the same read-outs, every product in split bf16
+// (gemm_bf3); the carried query rows are kept as high and low parts between nodes
+template <int C, int DK, int DV>
+__device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char* smb) {
+  using S = QuerySmemB<C, DK, DV>;
+  constexpr int SX = S::SX, SV = S::SV, SMB = S::SMB;
+  constexpr int J = C == 16 ? 4 : C == 32 ? 5 : 6;
+  bf16* xh[2] = {reinterpret_cast<bf16*>(smb + S::X), reinterpret_cast<bf16*>(smb + S::X + 2 * S::XB)};
+  bf16* xl[2] = {reinterpret_cast<bf16*>(smb + S::X + S::XB), reinterpret_cast<bf16*>(smb + S::X + 3 * S::XB)};
+  float* Os = reinterpret_cast<float*>(smb + S::O);
+  bf16* Mh = reinterpret_cast<bf16*>(smb + S::MH);
+  bf16* Ml = reinterpret_cast<bf16*>(smb + S::ML);
+  float* lam = reinterpret_cast<float*>(smb + S::LAM);
+  const int tid = threadIdx.x;
+  const int c = blockIdx.x % p.nchunks, bh = blockIdx.x / p.nchunks;
+  const int t0 = c * C;
+  const int nv = min(C, p.T - t0);
+  const size_t row0 = (size_t)bh * p.T + t0;
+  const size_t wrow0 = ((size_t)bh * p.nchunks + c) * C;
+  auto slot_of = [&](int j, int m) {
+    int off = 0;
+    for (int i = 0; i < j; ++i) off += p.nchunks >> i;
+    return (size_t)bh * p.nslot + off + m;
+  };
+  auto next_bit = [&](int j) {
+    const unsigned rest = (unsigned)c >> (j + 1);
+    return rest ? j + 1 + __builtin_ctz(rest) : -1;
+  };
+  // up to d = 64 the next node's state and transition travel in registers meanwhile
+  constexpr bool PRE = DK <= 64;
+  StagedBlock<float, DK, PRE ? DV : 16> nb;
+  StagedBlock<float, DK, PRE ? DK : 16> fb;
+  int j = c ? __builtin_ctz((unsigned)c) : -1;
+  {
+    StagedBlock<float, C, DK> sx;
+    StagedBlock<float, C, DV> so;
+    StagedLambda<C> sl;
+    sx.load(p.x0 + wrow0 * DK, DK, C, tid);
+    so.load(p.oi + wrow0 * DV, DV, C, tid);
+    sl.load(p, row0, nv, tid);
+    if constexpr (PRE) {
+      if (j >= 0) {
+        const size_t slot = slot_of(j, (c >> j) - 1);
+        nb.load(p.node + slot * DK * DV, DV, DK, tid);
+        if (next_bit(j) >= 0) fb.load(p.phi + slot * DK * DK, DK, DK, tid);
+      }
+    }
+    sx.store_split(xh[0], xl[0], SX, tid);
+    so.store(Os, SV, tid);
+    sl.store(lam, tid);
+  }
+  __syncthreads();
+  int a = 0;
+  while (j >= 0) {
+    const size_t slot = slot_of(j, (c >> j) - 1);
+    const int jn = next_bit(j);
+    if constexpr (PRE) {
+      nb.store_split(Mh, Ml, SMB, tid);
+    } else {
+      StagedBlock<float, DK, DV> b;
+      b.load(p.node + slot * DK * DV, DV, DK, tid);
+      b.store_split(Mh, Ml, SMB, tid);
+    }
+    __syncthreads();
+    const int lev = J + 1 + j;
+    gemm_bf3<C, DV, DK>(xh[a], xl[a], SX, Mh, Ml, SMB, tid, [&](int i, int e, float x) {
+      Os[i * SV + e] += lam[i * kLamCapG + lev] * x;
+    });
+    __syncthreads();
+    if (jn >= 0) {           // a higher node follows: X <- X Phi of this node
+      if constexpr (PRE) {
+        fb.store_split(Mh, Ml, SMB, tid);
+        const size_t sn = slot_of(jn, (c >> jn) - 1);
+        nb.load(p.node + sn * DK * DV, DV, DK, tid);
+        if (next_bit(jn) >= 0) fb.load(p.phi + sn * DK * DK, DK, DK, tid);
+      } else {
+        StagedBlock<float, DK, DK> b;
+        b.load(p.phi + slot * DK * DK, DK, DK, tid);
+        b.store_split(Mh, Ml, SMB, tid);
+      }
+      __syncthreads();
+      bf16* oh = xh[a ^ 1];
+      bf16* ol = xl[a ^ 1];
+      gemm_bf3<C, DK, DK>(xh[a], xl[a], SX, Mh, Ml, SMB, tid, [&](int i, int d, float x) {
+        const bf16 h = (bf16)x;
+        oh[i * SX + d] = h;
+        ol[i * SX + d] = (bf16)(x - (float)h);
+      });
+      __syncthreads();
+      a ^= 1;
+    }
+    j = jn;
+  }
+  bf16* og = reinterpret_cast<bf16*>(p.out);
+  for (int i = tid; i < C * DV; i += kNT) {
+    const int r = i / DV, e = i % DV;
+    if (r < nv) og[(row0 + r) * DV + e] = (bf16)Os[r * SV + e];
+  }
+}
 
 // gdn_query: per (chunk, head) the Fenwick nodes of the chunk's set bits, lowest first, read out
 // with the query rows carried to each node's end; plus the intra-chunk output; store.
 template <typename T, int C, int DK, int DV>
 __global__ __launch_bounds__(kNT) void gdn_query_kernel(GdnParams p) {
+  if constexpr (std::is_same<T, bf16>::value && DK >= 32) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smq[];
+    gdn_query_bf3<C, DK, DV>(p, smq);
+    return;
+  }
   using S = QuerySmem<C, DK, DV>;
   constexpr int SK = S::SK, SV = S::SV, SM = S::SM;
   constexpr int J = C == 16 ? 4 : C == 32 ? 5 : 6;
