@@ -397,9 +397,10 @@ def gdn_algorithmic(w, chunk: int) -> tuple[float, float]:
 def gdn_measure(dev, stream, steps: int = 10, warmup: int = 2) -> dict:
     """Log-linear Gated DeltaNet (``loglinear_attn_gdn_fwd``) at the headline's shape (B=4, H=16,
     T=8192, d=64, bf16, keys L2-normalised, beta = sigmoid(N(0,1))): time per call between events,
-    per-stage times from the library's events, tokens/s, and its roofline. Its products run in
-    float32 on the matrix cores, so the bound is the float32 rate (157.3 TFLOP/s); the HBM
-    fraction is reported beside it."""
+    per-stage times from the library's events, tokens/s, and its roofline. Its chunk and up-sweep
+    kernels multiply in float32 on the matrix cores (the query kernel in split bf16 for bf16
+    inputs), so the bound is the float32 rate (157.3 TFLOP/s); the HBM fraction is reported
+    beside it."""
     import torch
     import log_linear_attention_chunked_amd as lla
     from lla_synth import GDN_WORKLOADS, generate_gdn
@@ -442,7 +443,7 @@ def gdn_measure(dev, stream, steps: int = 10, warmup: int = 2) -> dict:
         "algorithmic_bytes_per_call": byte_ht * ht,
         "hbm_frac": byte_ht * ht / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "alu", "achieved": tflops, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / FP32_PEAK_TFLOPS, "scope": "whole call, float32 products"},
+                     "frac": tflops / FP32_PEAK_TFLOPS, "scope": "whole call, against the float32 rate (the chunk and up-sweep kernels multiply in float32; the query kernel in split bf16 for bf16 inputs)"},
     }
 
 
