@@ -24,10 +24,11 @@
 // carried to that node's end: O += lambda[:, J+1+j] * (X N), then X <- X Phi of that node.
 //
 // Kernels (stream order): gdn_chunk (one workgroup per chunk and head), gdn_upsweep (one launch
-// per tree level; workgroups over node, head and a 16-column panel), gdn_query (one workgroup
-// per chunk and head). Every product runs in float32 on the matrix cores from shared memory; Tm^{-1}
-// is formed blockwise (16 x 16 diagonal blocks by forward substitution, then doubled); inputs may
-// be bfloat16 or float32, the output is in their type.
+// per tree level; workgroups over node and head, or over node, head and a 16-column panel),
+// gdn_query (one workgroup per chunk and head). Products run on the matrix cores from shared
+// memory, in float32 — except gdn_query's for bfloat16 inputs, in split bf16 (high and low
+// parts, three bf16 products); Tm^{-1} is formed blockwise (16 x 16 diagonal blocks by forward
+// substitution, then doubled); inputs may be bfloat16 or float32, the output is in their type.
 #pragma once
 
 #include <hip/hip_runtime.h>
