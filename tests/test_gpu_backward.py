@@ -67,6 +67,10 @@ CASES = [
     (1, 2, 520, 128, 32, "bf16", 32),
     (1, 1, 1024, 128, 128, "bf16", 0),
     (1, 2, 700, 32, 32, "bf16", 16),
+    # d = 128 by columns of dq with a ragged last group of 8 chunks (21 and 22 chunks): the
+    # gradient kernel forms U_c from the tree's group states in batches
+    (1, 2, 1300, 128, 128, "bf16", 64),
+    (1, 1, 700, 128, 128, "f32", 0),
 ]
 
 
