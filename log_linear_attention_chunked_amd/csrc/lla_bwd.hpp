@@ -1270,7 +1270,8 @@ __device__ __forceinline__ void grads_body(const BwdParams& p, unsigned char* sm
   // of 8 receives from the levels above 2 (ud) and, for each clear bit j < 3 of c, the right
   // sibling block at level j inside the group (a target-side state of bwd_rng), decayed:
   // U = D, then for j = 2, 1, 0 where that sibling exists, U = exp(G(sibling)) U + RN(sibling).
-  // Each thread forms the elements of its own 16-byte pieces; all of it is loaded with the rest.
+  // Each thread forms the elements of its own 16-byte pieces: on the staged path with every
+  // load issued beside the prologue's others, on the column path in batches (form_u_img).
   constexpr int NF4 = DM && PF ? NPF * EPV / 4 : 1;   // float4s of a state per thread
   f32x4 udv[NF4], urn[3][NF4];
   bool uin[3] = {false, false, false};
