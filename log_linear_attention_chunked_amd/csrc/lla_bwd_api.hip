@@ -201,18 +201,20 @@ bwd_tree_kernel(BwdParams p, int SZ) {
 }
 
 // ----------------------------------------------------------------------------------------
-// bwd_gtree: the same tree, with each wave owning groups of 8 consecutive chunks (bwd_rn's
-// sub-blocks). Levels 0..3 of a group (its chunks, pairs, quads and the group itself) are
-// combined in registers, up and down; only the levels above, over groups, go through shared
-// memory. A right block of several groups (level i >= 4) receives, from each of its groups g,
-// the contribution exp(decay from the block's start to g's start) * P(i, g) (P: bwd_rn's
-// sub-block state), written to shared memory by g's wave and summed in group order by the wave
-// that needs it. Every global load a workgroup makes (the groups' chunk states, their right
-// blocks' states, the contributions and the block decays) is issued before the first wait when
-// a wave owns one group, so the whole tree costs about one memory round trip.
+// bwd_gtree: the same tree, with each wave owning a run of 2^wl consecutive groups of 8 chunks
+// (bwd_rn's sub-blocks; wl >= 1, the least that covers every group with the kTreeWaves waves).
+// Levels 0..3 of a group (its chunks, pairs, quads and the group itself) are combined in
+// registers, up and down; a pair of groups (level 4) is combined by its wave as it goes; only the
+// levels above go through shared memory. A right block of several groups (level i >= 4) receives,
+// from each of its groups g, the contribution exp(decay from the block's start to g's start) *
+// P(i, g) (P: bwd_rn's sub-block state); a wave sums the contributions of its groups per unit of
+// min(2^(i-3), 2^wl) groups (a unit lies inside one wave's run and one block) and the down-sweep
+// sums a block's units in order. Every global load a workgroup makes (the first group's chunk
+// states, right blocks' states and contributions, and the block decays) is issued before the
+// first wait.
 // Shared memory: the block decays (floats); then slots of VE floats per lane: per level
-// i >= 3 (below nl) the block values (up-sweep values later overwritten by the down-sweep's); per
-// level i >= 4 the contributions, one per right-block group (item order of bwd_rn).
+// i >= 4 (below nl) the block values (up-sweep values later overwritten by the down-sweep's); per
+// level i >= 4 the contributions, one per unit of a right block (in unit order).
 // ----------------------------------------------------------------------------------------
 
 constexpr int kGrpLog = 3;            // 8 chunks per group
@@ -223,22 +225,43 @@ constexpr int kGtCt = 6;              // levels >= 4 whose contributions a wave 
 // workgroup covers 256 elements and the scalar work of a group (its addresses, levels and
 // branches, the same for every element) is shared by four times the data.
 
-// first slot of level i's block values (3 <= i <= nl) and of level i's contributions
+// log2 of the groups a wave owns: at least 2 (a pair of groups), a power of two, and enough for
+// kTreeWaves waves to cover the ng groups
+__host__ __device__ inline int gtree_wave_log(int ng) {
+  int wl = 1;
+  while ((kTreeWaves << wl) < ng) ++wl;
+  return wl;
+}
+// log2 of the unit (in groups) over which a wave sums the level-i contributions, and the units
+// of right blocks at level i (unit t lies in block t >> (i - 3 - a), a right block when odd)
+__host__ __device__ inline int gtree_unit_log(int i, int wl) { return i - 3 < wl ? i - 3 : wl; }
+__host__ __device__ inline int gtree_units(int ng, int i, int wl) {
+  const int a = gtree_unit_log(i, wl), b = i - 3 - a;
+  const int M = (ng + (1 << a) - 1) >> a;
+  const int rem = M & ((2 << b) - 1);
+  return ((M >> (b + 1)) << b) + (rem > (1 << b) ? rem - (1 << b) : 0);
+}
+// the k-th unit of right blocks at level i: unit t (bit b of t set, b = i - 3 - a)
+__host__ __device__ inline int gtree_unit_item(int i, int wl, int t) {
+  const int b = i - 3 - gtree_unit_log(i, wl);
+  return ((t >> (b + 1)) << b) | (t & ((1 << b) - 1));
+}
+// first slot of level i's block values (4 <= i <= nl) and of level i's contributions
 // (4 <= i <= nl; i = nl gives the total) in the value region, which follows the block decays
-__host__ __device__ inline int gtree_lv(int N, int nslot, int i) {
-  (void)nslot;
+__host__ __device__ inline int gtree_lv(int N, int i) {
   int off = 0;
-  for (int a = 3; a < i; ++a) off += (N + (1 << a) - 1) >> a;
+  for (int a = 4; a < i; ++a) off += (N + (1 << a) - 1) >> a;
   return off;
 }
-__host__ __device__ inline int gtree_ct(int N, int nl, int nslot, int i) {
-  int off = gtree_lv(N, nslot, nl > 3 ? nl : 3);
-  for (int a = 4; a < i; ++a) off += items_of_level(N, a);
+__host__ __device__ inline int gtree_ct(int N, int nl, int i) {
+  const int ng = (N + 7) >> kGrpLog, wl = gtree_wave_log(ng);
+  int off = gtree_lv(N, nl > 4 ? nl : 4);
+  for (int a = 4; a < i; ++a) off += gtree_units(ng, a, wl);
   return off;
 }
 // the decays, then every level's block values and contributions, VE * 64 floats per slot
 __host__ __device__ inline int gtree_floats(int N, int nl, int nslot, int VE) {
-  return ((nslot + 63) & ~63) + gtree_ct(N, nl, nslot, nl > 4 ? nl : 4) * VE * 64;
+  return ((nslot + 63) & ~63) + gtree_ct(N, nl, nl > 4 ? nl : 4) * VE * 64;
 }
 
 // GROUPED: bwd_statesg has done levels 0..3 of every group (nodes written, the group in fp32 at
@@ -331,19 +354,21 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
   // the decays go to shared memory first (one value per thread for up to 1024 blocks, the rest,
   // for larger trees, in a loop afterwards); the first group's loads are issued beside them
   const float gv = gsg[min((int)threadIdx.x, p.nslot - 1)];
+  // this wave's groups [gb, ge)
+  const int wl = gtree_wave_log(ng);
+  const int gb = w << wl, ge = min(gb + (1 << wl), ng);
   GLoads first;
-  if (w < ng) load_group(w, first);
+  if (gb < ng) load_group(gb, first);
   if ((int)threadIdx.x < p.nslot) gs[threadIdx.x] = gv;
   for (int i = threadIdx.x + 64 * kTreeWaves; i < p.nslot; i += 64 * kTreeWaves) gs[i] = gsg[i];
   __syncthreads();
   // decay of block m at level i (0 where the block does not exist: it then holds zeros)
   auto G = [&](int i, int m) { return (i < nl && m < nb(i)) ? gs[slot_p(p, i, m)] : 0.f; };
 
-  // up-sweep inside a group, contributions, and the group's value at level 3
-  auto up_group = [&](int g, const GLoads& d) {
+  // up-sweep inside a group; returns the group's value at level 3
+  auto up_group = [&](int g, const GLoads& d) -> FV {
     if constexpr (GROUPED) {
-      if (3 < nl) tvs(p.gtlv[3] + g) = d.x[0];
-      return;
+      return d.x[0];
     } else {
       const int c0 = g << kGrpLog;
       FV x[8], y1[4], y2[2];
@@ -362,13 +387,22 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
       for (int h = 0; h < 2; ++h)
         if (1 < nl && 4 * g + 2 * h < nb(1)) put(ne, nlo, (size_t)slot_p(p, 1, 4 * g + 2 * h) * SZ, y1[2 * h]);
       if (2 < nl && 2 * g < nb(2)) put(ne, nlo, (size_t)slot_p(p, 2, 2 * g) * SZ, y2[0]);
-      if (3 < nl) {
-        if (!(g & 1)) put(ne, nlo, (size_t)slot_p(p, 3, g) * SZ, y3);
-        tvs(p.gtlv[3] + g) = y3;
-      }
+      if (3 < nl && !(g & 1)) put(ne, nlo, (size_t)slot_p(p, 3, g) * SZ, y3);
+      return y3;
     }
   };
-  // contributions of a group to the right blocks above level 3 that hold it
+  // the pair of groups g >> 1 (a level-4 block): the left group's value waits in the block's
+  // slot for its right sibling, which the same wave takes next
+  auto up_pair = [&](int g, const FV& y3) {
+    if (4 < nl) {
+      FV& v = tvs(p.gtlv[4] + (g >> 1));
+      if (!(g & 1)) v = y3;
+      else v = __expf(G(3, g)) * v + y3;
+      if (((g & 1) || g + 1 == ng) && !((g >> 1) & 1)) put(ne, nlo, (size_t)slot_p(p, 4, g >> 1) * SZ, v);
+    }
+  };
+  // contributions of a group to the right blocks above level 3 that hold it, summed over the
+  // groups of each unit (the unit's first group sets its slot, the others add, in group order)
   auto contribute = [&](int g, const GLoads& d) {
 #pragma unroll
     for (int u = 0; u < kGtCt; ++u) {
@@ -376,25 +410,29 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
       if (i < nl && ((g >> (i - 3)) & 1)) {
         float dec = 0.f;
         for (int g2 = (g >> (i - 3)) << (i - 3); g2 < g; ++g2) dec += gs[slot_p(p, 3, g2)];
-        tvs(p.gtct[i] + item_of_sub(i, g)) = __expf(dec) * d.ct[u];
+        const int a = gtree_unit_log(i, wl);
+        FV& c = tvs(p.gtct[i] + gtree_unit_item(i, wl, g >> a));
+        const FV t = __expf(dec) * d.ct[u];
+        if (g & ((1 << a) - 1)) c += t;
+        else c = t;
       }
     }
   };
-  for (int g = w; g < ng; g += kTreeWaves) {
-    if (g == w) {
+  for (int g = gb; g < ge; ++g) {
+    if (g == gb) {
       contribute(g, first);
-      up_group(g, first);
+      up_pair(g, up_group(g, first));
     } else {
       GLoads d;
       load_group(g, d);
       contribute(g, d);
-      up_group(g, d);
+      up_pair(g, up_group(g, d));
     }
   }
   __syncthreads();
 
-  // levels >= 4, up: block values from the level below
-  for (int i = 4; i < nl; ++i) {
+  // levels >= 5, up: block values from the level below
+  for (int i = 5; i < nl; ++i) {
     for (int m = w; m < nb(i); m += kTreeWaves) {
       const bool right = 2 * m + 1 < nb(i - 1);
       const FV l0 = tvs(p.gtlv[i - 1] + 2 * m);
@@ -412,8 +450,9 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
       FV v = par;
       if (!(m & 1) && m + 1 < nb(i)) {
         FV rn = zero;
-        const int g0 = (m + 1) << (i - 3), g1 = min((m + 2) << (i - 3), ng);
-        for (int g2 = g0; g2 < g1; ++g2) rn += tvs(p.gtct[i] + item_of_sub(i, g2));
+        const int a = gtree_unit_log(i, wl);
+        const int t0 = ((m + 1) << (i - 3)) >> a, t1 = (min((m + 2) << (i - 3), ng) + (1 << a) - 1) >> a;
+        for (int t = t0; t < t1; ++t) rn += tvs(p.gtct[i] + gtree_unit_item(i, wl, t));
         v = __expf(G(i, m + 1)) * par + rn;
       }
       tvs(p.gtlv[i] + m) = v;
@@ -447,8 +486,8 @@ bwd_gtree_kernel(BwdParams p, int SZ) {
       if (c + 1 < N) put(ue, ulo, (size_t)(c + 1) * SZ, d1[h]);
     }
   };
-  for (int g = w; g < ng; g += kTreeWaves) {
-    if (g == w) {
+  for (int g = gb; g < ge; ++g) {
+    if (g == gb) {
       down_group(g, first);
     } else {
       GLoads d;
@@ -709,8 +748,8 @@ int launch_bwd(const lla_bwd_args& a, const BwdPlan& pl, void* ws, hipStream_t s
   p.BH = (int)pl.BH; p.T = a.T; p.L = pl.L; p.N = pl.N; p.nl = pl.nl; p.nslot = pl.nslot;
   for (int i = 0; i <= lla::kLamCap; ++i) {
     p.lvl[i] = i <= pl.nl ? lla::bwd::slot_of(pl.N, i, 0) : pl.nslot;
-    p.gtlv[i] = i >= 3 && i <= pl.nl ? lla::bwd::gtree_lv(pl.N, pl.nslot, i) : 0;
-    p.gtct[i] = i >= 4 && i <= pl.nl ? lla::bwd::gtree_ct(pl.N, pl.nl, pl.nslot, i) : 0;
+    p.gtlv[i] = i >= 4 && i <= pl.nl ? lla::bwd::gtree_lv(pl.N, i) : 0;
+    p.gtct[i] = i >= 4 && i <= pl.nl ? lla::bwd::gtree_ct(pl.N, pl.nl, i) : 0;
   }
   void* args[] = {&p};
   auto mark = [&](int i) {
