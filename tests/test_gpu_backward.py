@@ -143,9 +143,9 @@ def test_backward_coarse_onehot_bf16(level):
 
 @pytest.mark.parametrize("T,dtype,mode", [(6000, "f32", "lowdecay"), (8192, "bf16", None)])
 def test_backward_many_chunks(T, dtype, mode):
-    # N = T/16 = 375 and 512 chunks, 9 chunk levels: the group tree with 4 and 2^2 groups per
-    # wave (a ragged last run at 47 groups); one-hot-free random lambda, low decay so that the
-    # coarse levels carry weight
+    # N = T/16 = 375 and 512 chunks, 9 chunk levels: the group tree with 4 groups per wave (a
+    # ragged last run at 47 groups); one-hot-free random lambda, low decay so that the coarse
+    # levels carry weight
     w = custom(1, 1, T, 16, 16, dtype)
     x = generate(w, seed=12, log_a_mode=mode)
     do = grad_output(w, seed=12)
