@@ -258,6 +258,23 @@ def test_backward_long_workloads_sampled(name):
     check_sampled(name, x, do, got, heads, rows)
 
 
+def test_backward_group_tree_1000_chunks_sampled():
+    # 1000 chunks per head (T = 16000, C = 16): the group tree at its largest tree, 125 groups in
+    # runs of 8 per wave (the last run 5 groups), units of 2, 4 and 8 groups summed per right
+    # block; sampled positions and a dlog_a tail, low decay so that the coarse levels carry weight
+    import torch
+    import log_linear_attention_chunked_amd as lla
+    w = custom(1, 2, 16000, 16, 16, "bf16")
+    x = generate(w, seed=14, log_a_mode="lowdecay")
+    do = grad_output(w, seed=14)
+    print("[bwd] T=16000 C=16 group tree, 1000 chunks", flush=True)
+    d = {k: v.cuda() for k, v in x.items()}
+    g = lla.backward(d["q"], d["k"], d["v"], d["log_a"], d["lam"], do.cuda(), chunk=16)
+    torch.cuda.synchronize()
+    got = {n: t for n, t in zip(GRADS, g)}
+    check_sampled("T=16000 C=16 group tree", x, do, got, [(0, 0), (0, 1)], _sample_rows(w.T, 16, seed=3))
+
+
 def test_backward_tree_in_workspace_sampled():
     # 2048 chunks per head (T = 32768, C = 16): the tree's levels no longer fit shared memory at
     # any width and stay in the workspace; sampled positions and a dlog_a tail, low decay so that
