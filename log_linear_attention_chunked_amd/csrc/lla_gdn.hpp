@@ -58,6 +58,7 @@ struct GdnParams {
   int level;        // up-sweep: the level being built (>= 1)
   int off_prev;     // up-sweep: first slot of level-1
   int off_cur;      // up-sweep: first slot of level
+  int off_next;     // up-sweep of two levels: first slot of level + 1
   int ncur;         // up-sweep: nodes at level (nchunks >> level)
 };
 
@@ -261,6 +262,10 @@ __host__ __device__ constexpr int chunk_smem_bytes(int C, int DK, int DV) {
 __host__ __device__ constexpr int up_panel(int DK, int DV, bool whole) { return whole ? DV + DK : 16; }
 __host__ __device__ constexpr int up_smem_bytes(int DK, int DV, bool whole) {
   return 4 * (DK * (DK + 1) + DK * (up_panel(DK, DV, whole) + 1));
+}
+// the two-level up-sweep: one transition and one whole [N | Phi] row block
+__host__ __device__ constexpr int up2_smem_bytes(int DK, int DV) {
+  return 4 * (DK * (DK + 1) + DK * (DV + DK + 1));
 }
 __host__ __device__ constexpr int query_smem_bytes_f32(int C, int DK, int DV) {
   return 4 * (2 * C * (DK + 1) + C * (DV + 1) + DK * ((DK > DV ? DK : DV) + 1) + C * kLamCapG);
@@ -495,6 +500,104 @@ __global__ __launch_bounds__(kNT) void gdn_upsweep_kernel(GdnParams p) {
         out[(size_t)r * DK + col0 + cc] = x;
       });
     }
+  }
+}
+
+// gdn_upsweep2 (levels j and j + 1 in one launch; dk <= 64): node (j + 1, m) as the fold of its
+// four grandchildren G0..G3 = (j - 1, 4m .. 4m + 3) in order, X <- Phi_G X + [N_G | 0] from
+// X = [N_G0 | Phi_G0] (the same products as the two levels' merges, associated from the left):
+// after G1, X is node (j, 2m), stored because the query reads the even nodes of every level;
+// after G3 it is node (j + 1, m), stored. The odd node (j, 2m + 1), read by nothing but its
+// parent, is never formed, and the level-j nodes are never read back. One workgroup per node
+// (j + 1, m) and head, plus, where level j has an odd node count, one that folds G0, G1 only
+// (level j's last node, which has no sibling). Each product's output tiles stay in the
+// registers until every wave has read X, then overwrite it in place.
+template <int DK, int DV>
+struct Up2Smem {
+  static constexpr int SP = DK + 1, NC = DV + DK, SW = NC + 1;
+  static constexpr int PHI = 0, X = PHI + DK * SP, TOTAL = X + DK * SW;
+  static constexpr int BYTES = TOTAL * 4;
+  static_assert(BYTES == up2_smem_bytes(DK, DV), "layout and size formula agree");
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kNT) void gdn_upsweep2_kernel(GdnParams p) {
+  using S = Up2Smem<DK, DV>;
+  constexpr int SP = S::SP, NC = S::NC, SW = S::SW;
+  constexpr int TN = NC / 16, NTILE = (DK / 16) * TN, NWAVE = kNT / 64;
+  constexpr int PERW = (NTILE + NWAVE - 1) / NWAVE;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  extern __shared__ float sm[];
+  float* A = sm + S::PHI;
+  float* X = sm + S::X;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int jl = lane & 15, g = lane >> 4;
+  const int npair = p.ncur >> 1, nwg = npair + (p.ncur & 1);
+  const int m = blockIdx.x % nwg, bh = blockIdx.x / nwg;
+  const int steps = m < npair ? 3 : 1;
+  const size_t base = (size_t)bh * p.nslot;
+  const size_t g0 = base + p.off_prev + 4 * m;
+  {
+    StagedBlock<float, DK, DV> sn;
+    StagedBlock<float, DK, DK> sf, sa;
+    sn.load(p.node + g0 * DK * DV, DV, DK, tid);
+    sf.load(p.phi + g0 * DK * DK, DK, DK, tid);
+    sa.load(p.phi + (g0 + 1) * DK * DK, DK, DK, tid);
+    sn.store(X, SW, tid);
+    sf.store(X + DV, SW, tid);
+    sa.store(A, SP, tid);
+  }
+  __syncthreads();
+  for (int s = 1; s <= steps; ++s) {
+    const size_t gs = g0 + s;
+    // N of G_s for the state columns and the next transition, in flight during the product
+    float nadd[PERW][4];
+#pragma unroll
+    for (int t = 0; t < PERW; ++t) {
+      const int tile = w + t * NWAVE;
+      const int i0 = (tile / TN) * 16, j0 = (tile % TN) * 16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        nadd[t][r] = (tile < NTILE && j0 < DV) ? p.node[gs * DK * DV + (size_t)(i0 + 4 * g + r) * DV + j0 + jl] : 0.f;
+    }
+    StagedBlock<float, DK, DK> nxt;
+    if (s < steps) nxt.load(p.phi + (gs + 1) * DK * DK, DK, DK, tid);
+    f32x4 acc[PERW];
+#pragma unroll
+    for (int t = 0; t < PERW; ++t) {
+      const int tile = w + t * NWAVE;
+      acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (tile < NTILE) {
+        const int i0 = (tile / TN) * 16, j0 = (tile % TN) * 16;
+#pragma unroll 4
+        for (int k = 0; k < DK; k += 4)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(i0 + jl) * SP + k + g], X[(k + g) * SW + j0 + jl],
+                                                        acc[t], 0, 0, 0);
+      }
+    }
+    __syncthreads();   // every wave has read A and X
+    const bool out = s != 2;
+    const size_t slot = s == 1 ? base + p.off_cur + 2 * m : base + p.off_next + m;
+#pragma unroll
+    for (int t = 0; t < PERW; ++t) {
+      const int tile = w + t * NWAVE;
+      if (tile < NTILE) {
+        const int i0 = (tile / TN) * 16, j0 = (tile % TN) * 16, col = j0 + jl;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = i0 + 4 * g + r;
+          const float x = acc[t][r] + nadd[t][r];
+          X[row * SW + col] = x;
+          if (out) {
+            if (j0 < DV) p.node[slot * DK * DV + (size_t)row * DV + col] = x;
+            else p.phi[slot * DK * DK + (size_t)row * DK + col - DV] = x;
+          }
+        }
+      }
+    }
+    if (s < steps) nxt.store(A, SP, tid);
+    __syncthreads();
   }
 }
 

@@ -53,6 +53,28 @@ const void* upsweep_kernel(int dk, int dv, bool whole) {
 // a level's nodes times heads from which one workgroup per node beats 16-column panels (at
 // fewer, the panels' extra workgroups fill the device better)
 constexpr long kUpWholeMin = 1024;
+// two levels in one launch (dk <= 64): the fold of four grandchildren per workgroup
+template <int DK>
+const void* upsweep2_for_dv(int dv) {
+  switch (dv) {
+    case 16: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep2_kernel<DK, 16>);
+    case 32: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep2_kernel<DK, 32>);
+    case 64: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep2_kernel<DK, 64>);
+    case 128: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep2_kernel<DK, 128>);
+  }
+  return nullptr;
+}
+const void* upsweep2_kernel(int dk, int dv) {
+  switch (dk) {
+    case 16: return upsweep2_for_dv<16>(dv);
+    case 32: return upsweep2_for_dv<32>(dv);
+    case 64: return upsweep2_for_dv<64>(dv);
+  }
+  return nullptr;
+}
+// workgroups (level j + 1 nodes, plus level j's unpaired last node, times heads) from which two
+// levels go in one launch
+constexpr long kUp2Min = 1;
 
 bool fits(int C, int dk, int dv) {
   using namespace lla::gdn;
@@ -137,6 +159,7 @@ int launch(const lla_gdn_args& a, const GdnPlan& pl, void* ws, hipStream_t strea
   const GdnKernels* ks = gdn_kernels(a.dtype, pl.C, a.dk, a.dv);
   const void* up = upsweep_kernel(a.dk, a.dv, false);
   const void* upw = upsweep_kernel(a.dk, a.dv, true);   // null at dk = 128
+  const void* up2 = upsweep2_kernel(a.dk, a.dv);        // null at dk = 128
   if (!ks || !up) return LLA_ERR_UNSUPPORTED;
   GdnParams p;
   memset(&p, 0, sizeof(p));
@@ -154,6 +177,7 @@ int launch(const lla_gdn_args& a, const GdnPlan& pl, void* ws, hipStream_t strea
   const unsigned grid = (unsigned)(pl.N * pl.BH);
   const int sc = chunk_smem_bytes(pl.C, a.dk, a.dv), sq = query_smem_bytes(pl.C, a.dk, a.dv);
   const int su = up_smem_bytes(a.dk, a.dv, false), suw = up_smem_bytes(a.dk, a.dv, true);
+  const int su2 = up2_smem_bytes(a.dk, a.dv);
   if (mark(0) != hipSuccess) return LLA_ERR_HIP;
   {
     void* args[] = {&p};
@@ -163,19 +187,29 @@ int launch(const lla_gdn_args& a, const GdnPlan& pl, void* ws, hipStream_t strea
   if (mark(1) != hipSuccess) return LLA_ERR_HIP;
   if (set_smem(up, su) != hipSuccess) return LLA_ERR_HIP;
   if (upw && set_smem(upw, suw) != hipSuccess) return LLA_ERR_HIP;
-  int off_prev = 0;
-  for (int j = 1; j <= pl.top; ++j) {
+  if (up2 && set_smem(up2, su2) != hipSuccess) return LLA_ERR_HIP;
+  int off_prev = 0;   // first slot of level j - 1
+  for (int j = 1; j <= pl.top;) {
     GdnParams pj = p;
     pj.level = j;
     pj.off_prev = off_prev;
     pj.off_cur = off_prev + (pl.N >> (j - 1));
+    pj.off_next = pj.off_cur + (pl.N >> j);
     pj.ncur = pl.N >> j;
-    off_prev = pj.off_cur;
     void* args[] = {&pj};
+    const long nwg2 = (long)((pj.ncur >> 1) + (pj.ncur & 1)) * pl.BH;
+    if (up2 && j + 1 <= pl.top && nwg2 >= kUp2Min) {
+      if (hipLaunchKernel(up2, dim3((unsigned)nwg2), dim3(kNT), args, su2, stream) != hipSuccess) return LLA_ERR_HIP;
+      off_prev = pj.off_next;   // the next launch builds level j + 2 from level j + 1
+      j += 2;
+      continue;
+    }
     const bool whole = upw && (long)pj.ncur * pl.BH >= kUpWholeMin;
     const unsigned g = (unsigned)((long)pj.ncur * pl.BH * ((a.dv + a.dk) / up_panel(a.dk, a.dv, whole)));
     if (hipLaunchKernel(whole ? upw : up, dim3(g), dim3(kNT), args, whole ? suw : su, stream) != hipSuccess)
       return LLA_ERR_HIP;
+    off_prev = pj.off_cur;
+    j += 1;
   }
   if (mark(2) != hipSuccess) return LLA_ERR_HIP;
   {
