@@ -419,9 +419,10 @@ int loglinear_attn_bwd_default_chunk(int dk, int dv, int dtype);
  *           share it.
  *   stage_events : optional hipEvent_t recorded on `stream`: [0] before the per-chunk kernel,
  *           [1] before the tree up-sweep, [2] before the query kernel, [3] after it.
- * Products run on the matrix cores in float32 (the query kernel's, for bfloat16 inputs, in split
- * bf16: high and low parts, three bf16 products each); the launches are gdn_chunk (one workgroup
- * per chunk and head), one gdn_upsweep per tree level, and gdn_query. Asynchronous on `stream`,
+ * Products run on the matrix cores in float32 (the query and up-sweep kernels', for bfloat16
+ * inputs with dk >= 32, in split bf16: high and low parts, three bf16 products each); the
+ * launches are gdn_chunk (one workgroup per chunk and head), the up-sweep (two tree levels per
+ * launch for dk <= 64, else one), and gdn_query. Asynchronous on `stream`,
  * deterministic; returns LLA_OK or a negative LLA_ERR_*; B*H*T = 0 is a no-op.
  */
 typedef struct lla_gdn_args {

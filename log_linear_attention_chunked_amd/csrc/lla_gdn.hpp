@@ -23,12 +23,15 @@
 // bit j of c from the lowest, the node (j, (c >> j) - 1) at level J+1+j with X the query rows
 // carried to that node's end: O += lambda[:, J+1+j] * (X N), then X <- X Phi of that node.
 //
-// Kernels (stream order): gdn_chunk (one workgroup per chunk and head), gdn_upsweep (one launch
-// per tree level; workgroups over node and head, or over node, head and a 16-column panel),
-// gdn_query (one workgroup per chunk and head). Products run on the matrix cores from shared
-// memory, in float32 — except gdn_query's for bfloat16 inputs, in split bf16 (high and low
-// parts, three bf16 products); Tm^{-1} is formed blockwise (16 x 16 diagonal blocks by forward
-// substitution, then doubled); inputs may be bfloat16 or float32, the output is in their type.
+// Kernels (stream order): gdn_chunk (one workgroup per chunk and head), the up-sweep (for
+// dk <= 64 gdn_upsweep2, two tree levels per launch, one workgroup per node of the upper level
+// and head; a last odd level, and every level at dk = 128, by gdn_upsweep, one launch per level
+// with workgroups over node and head or over node, head and a 16-column panel), gdn_query (one
+// workgroup per chunk and head). Products run on the matrix cores from shared memory, in
+// float32 — except, for bfloat16 inputs with dk >= 32, gdn_query's and gdn_upsweep2's, in split
+// bf16 (high and low parts, three bf16 products); Tm^{-1} is formed blockwise (16 x 16 diagonal
+// blocks by forward substitution, then doubled); inputs may be bfloat16 or float32, the output
+// is in their type.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -263,9 +266,10 @@ __host__ __device__ constexpr int up_panel(int DK, int DV, bool whole) { return 
 __host__ __device__ constexpr int up_smem_bytes(int DK, int DV, bool whole) {
   return 4 * (DK * (DK + 1) + DK * (up_panel(DK, DV, whole) + 1));
 }
-// the two-level up-sweep: one transition and one whole [N | Phi] row block
-__host__ __device__ constexpr int up2_smem_bytes(int DK, int DV) {
-  return 4 * (DK * (DK + 1) + DK * (DV + DK + 1));
+// the two-level up-sweep: one transition and one whole [N | Phi] row block, in float32 or (BF3)
+// as high and low bf16 images with rows padded by 8 elements
+__host__ __device__ constexpr int up2_smem_bytes(int DK, int DV, bool bf3) {
+  return bf3 ? 2 * 2 * (DK * (DK + 8) + DK * (DV + DK + 8)) : 4 * (DK * (DK + 1) + DK * (DV + DK + 1));
 }
 __host__ __device__ constexpr int query_smem_bytes_f32(int C, int DK, int DV) {
   return 4 * (2 * C * (DK + 1) + C * (DV + 1) + DK * ((DK > DV ? DK : DV) + 1) + C * kLamCapG);
@@ -511,25 +515,39 @@ __global__ __launch_bounds__(kNT) void gdn_upsweep_kernel(GdnParams p) {
 // parent, is never formed, and the level-j nodes are never read back. One workgroup per node
 // (j + 1, m) and head, plus, where level j has an odd node count, one that folds G0, G1 only
 // (level j's last node, which has no sibling). Each product's output tiles stay in the
-// registers until every wave has read X, then overwrite it in place.
-template <int DK, int DV>
+// registers until every wave has read X, then overwrite it in place. BF3 (bfloat16 inputs,
+// dk >= 32): Phi_G and X are held as high and low bf16 images and multiplied in split bf16 as in
+// gemm_bf3; the sums and every stored node stay float32.
+template <int DK, int DV, bool BF3>
 struct Up2Smem {
-  static constexpr int SP = DK + 1, NC = DV + DK, SW = NC + 1;
-  static constexpr int PHI = 0, X = PHI + DK * SP, TOTAL = X + DK * SW;
-  static constexpr int BYTES = TOTAL * 4;
-  static_assert(BYTES == up2_smem_bytes(DK, DV), "layout and size formula agree");
+  static constexpr int NC = DV + DK;
+  static constexpr int SP = BF3 ? DK + 8 : DK + 1, SW = BF3 ? NC + 8 : NC + 1;   // row strides
+  static constexpr int ABYTES = BF3 ? DK * SP * 2 : DK * SP * 4, XBYTES = BF3 ? DK * SW * 2 : DK * SW * 4;
+  // A (high), [A low], X (high), [X low]
+  static constexpr int A = 0, AL = A + ABYTES, X = AL + (BF3 ? ABYTES : 0), XL = X + XBYTES,
+                       TOTAL = XL + (BF3 ? XBYTES : 0);
+  static_assert(TOTAL == up2_smem_bytes(DK, DV, BF3), "layout and size formula agree");
+  static_assert(!BF3 || (ABYTES % 16 == 0 && XBYTES % 16 == 0), "16-byte aligned images");
 };
 
-template <int DK, int DV>
-__global__ __launch_bounds__(kNT) void gdn_upsweep2_kernel(GdnParams p) {
-  using S = Up2Smem<DK, DV>;
+template <int DK, int DV, bool BF3>
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(3))) void gdn_upsweep2_kernel(GdnParams p) {
+  static_assert(!BF3 || DK % 32 == 0, "32-deep split-bf16 steps");
+  using S = Up2Smem<DK, DV, BF3>;
   constexpr int SP = S::SP, NC = S::NC, SW = S::SW;
-  constexpr int TN = NC / 16, NTILE = (DK / 16) * TN, NWAVE = kNT / 64;
-  constexpr int PERW = (NTILE + NWAVE - 1) / NWAVE;
+  // wave w: row tile w % RT (its A fragments loaded once per step of the contraction) and
+  // column tiles w / RT + WPR * t, t < PERW (those past TN skipped)
+  constexpr int TN = NC / 16, RT = DK / 16, NWAVE = kNT / 64;
+  constexpr int WPR = NWAVE / RT, PERW = (TN + WPR - 1) / WPR;
+  static_assert(NWAVE % RT == 0, "whole row tiles per wave");
   typedef float f32x4 __attribute__((ext_vector_type(4)));
-  extern __shared__ float sm[];
-  float* A = sm + S::PHI;
-  float* X = sm + S::X;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smu[];
+  float* A = reinterpret_cast<float*>(smu + S::A);
+  float* X = reinterpret_cast<float*>(smu + S::X);
+  bf16* Ah = reinterpret_cast<bf16*>(smu + S::A);
+  bf16* Al = reinterpret_cast<bf16*>(smu + S::AL);
+  bf16* Xh = reinterpret_cast<bf16*>(smu + S::X);
+  bf16* Xl = reinterpret_cast<bf16*>(smu + S::XL);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int jl = lane & 15, g = lane >> 4;
@@ -538,15 +556,23 @@ __global__ __launch_bounds__(kNT) void gdn_upsweep2_kernel(GdnParams p) {
   const int steps = m < npair ? 3 : 1;
   const size_t base = (size_t)bh * p.nslot;
   const size_t g0 = base + p.off_prev + 4 * m;
+  const int i0 = (w % RT) * 16, c0 = w / RT;
+  auto col_tile = [&](int t) { return c0 + WPR * t; };
   {
     StagedBlock<float, DK, DV> sn;
     StagedBlock<float, DK, DK> sf, sa;
     sn.load(p.node + g0 * DK * DV, DV, DK, tid);
     sf.load(p.phi + g0 * DK * DK, DK, DK, tid);
     sa.load(p.phi + (g0 + 1) * DK * DK, DK, DK, tid);
-    sn.store(X, SW, tid);
-    sf.store(X + DV, SW, tid);
-    sa.store(A, SP, tid);
+    if constexpr (BF3) {
+      sn.store_split(Xh, Xl, SW, tid);
+      sf.store_split(Xh + DV, Xl + DV, SW, tid);
+      sa.store_split(Ah, Al, SP, tid);
+    } else {
+      sn.store(X, SW, tid);
+      sf.store(X + DV, SW, tid);
+      sa.store(A, SP, tid);
+    }
   }
   __syncthreads();
   for (int s = 1; s <= steps; ++s) {
@@ -555,25 +581,39 @@ __global__ __launch_bounds__(kNT) void gdn_upsweep2_kernel(GdnParams p) {
     float nadd[PERW][4];
 #pragma unroll
     for (int t = 0; t < PERW; ++t) {
-      const int tile = w + t * NWAVE;
-      const int i0 = (tile / TN) * 16, j0 = (tile % TN) * 16;
+      const int j0 = col_tile(t) * 16;
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        nadd[t][r] = (tile < NTILE && j0 < DV) ? p.node[gs * DK * DV + (size_t)(i0 + 4 * g + r) * DV + j0 + jl] : 0.f;
+        nadd[t][r] = j0 < DV ? p.node[gs * DK * DV + (size_t)(i0 + 4 * g + r) * DV + j0 + jl] : 0.f;
     }
     StagedBlock<float, DK, DK> nxt;
     if (s < steps) nxt.load(p.phi + (gs + 1) * DK * DK, DK, DK, tid);
     f32x4 acc[PERW];
 #pragma unroll
-    for (int t = 0; t < PERW; ++t) {
-      const int tile = w + t * NWAVE;
-      acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (tile < NTILE) {
-        const int i0 = (tile / TN) * 16, j0 = (tile % TN) * 16;
-#pragma unroll 4
-        for (int k = 0; k < DK; k += 4)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(i0 + jl) * SP + k + g], X[(k + g) * SW + j0 + jl],
-                                                        acc[t], 0, 0, 0);
+    for (int t = 0; t < PERW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (BF3) {
+#pragma unroll 1
+      for (int k = 0; k < DK; k += 32) {
+        const bf16x8 ah = frag_rows(Ah, SP, i0 + jl, k + 8 * g), al = frag_rows(Al, SP, i0 + jl, k + 8 * g);
+#pragma unroll
+        for (int t = 0; t < PERW; ++t) {
+          if (col_tile(t) < TN) {
+            const int j0 = col_tile(t) * 16;
+            const bf16x8 bh = frag_cols(Xh, SW, k + 8 * g, j0 + jl), bl = frag_cols(Xl, SW, k + 8 * g, j0 + jl);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[t], 0, 0, 0);
+          }
+        }
+      }
+    } else {
+#pragma unroll 1
+      for (int k = 0; k < DK; k += 4) {
+        const float a = A[(i0 + jl) * SP + k + g];
+#pragma unroll
+        for (int t = 0; t < PERW; ++t)
+          if (col_tile(t) < TN)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, X[(k + g) * SW + col_tile(t) * 16 + jl], acc[t], 0, 0, 0);
       }
     }
     __syncthreads();   // every wave has read A and X
@@ -581,14 +621,19 @@ __global__ __launch_bounds__(kNT) void gdn_upsweep2_kernel(GdnParams p) {
     const size_t slot = s == 1 ? base + p.off_cur + 2 * m : base + p.off_next + m;
 #pragma unroll
     for (int t = 0; t < PERW; ++t) {
-      const int tile = w + t * NWAVE;
-      if (tile < NTILE) {
-        const int i0 = (tile / TN) * 16, j0 = (tile % TN) * 16, col = j0 + jl;
+      if (col_tile(t) < TN) {
+        const int j0 = col_tile(t) * 16, col = j0 + jl;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = i0 + 4 * g + r;
           const float x = acc[t][r] + nadd[t][r];
-          X[row * SW + col] = x;
+          if constexpr (BF3) {
+            const bf16 h = (bf16)x;
+            Xh[row * SW + col] = h;
+            Xl[row * SW + col] = (bf16)(x - (float)h);
+          } else {
+            X[row * SW + col] = x;
+          }
           if (out) {
             if (j0 < DV) p.node[slot * DK * DV + (size_t)row * DV + col] = x;
             else p.phi[slot * DK * DK + (size_t)row * DK + col - DV] = x;
@@ -596,7 +641,10 @@ __global__ __launch_bounds__(kNT) void gdn_upsweep2_kernel(GdnParams p) {
         }
       }
     }
-    if (s < steps) nxt.store(A, SP, tid);
+    if (s < steps) {
+      if constexpr (BF3) nxt.store_split(Ah, Al, SP, tid);
+      else nxt.store(A, SP, tid);
+    }
     __syncthreads();
   }
 }

@@ -53,25 +53,27 @@ const void* upsweep_kernel(int dk, int dv, bool whole) {
 // a level's nodes times heads from which one workgroup per node beats 16-column panels (at
 // fewer, the panels' extra workgroups fill the device better)
 constexpr long kUpWholeMin = 1024;
-// two levels in one launch (dk <= 64): the fold of four grandchildren per workgroup
-template <int DK>
+// two levels in one launch (dk <= 64): the fold of four grandchildren per workgroup, its
+// products in split bf16 for bfloat16 inputs with dk >= 32 (as the query kernel's)
+template <int DK, bool BF3>
 const void* upsweep2_for_dv(int dv) {
   switch (dv) {
-    case 16: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep2_kernel<DK, 16>);
-    case 32: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep2_kernel<DK, 32>);
-    case 64: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep2_kernel<DK, 64>);
-    case 128: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep2_kernel<DK, 128>);
+    case 16: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep2_kernel<DK, 16, BF3>);
+    case 32: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep2_kernel<DK, 32, BF3>);
+    case 64: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep2_kernel<DK, 64, BF3>);
+    case 128: return reinterpret_cast<const void*>(&lla::gdn::gdn_upsweep2_kernel<DK, 128, BF3>);
   }
   return nullptr;
 }
-const void* upsweep2_kernel(int dk, int dv) {
+const void* upsweep2_kernel(int dk, int dv, bool bf3) {
   switch (dk) {
-    case 16: return upsweep2_for_dv<16>(dv);
-    case 32: return upsweep2_for_dv<32>(dv);
-    case 64: return upsweep2_for_dv<64>(dv);
+    case 16: return upsweep2_for_dv<16, false>(dv);
+    case 32: return bf3 ? upsweep2_for_dv<32, true>(dv) : upsweep2_for_dv<32, false>(dv);
+    case 64: return bf3 ? upsweep2_for_dv<64, true>(dv) : upsweep2_for_dv<64, false>(dv);
   }
   return nullptr;
 }
+inline bool up2_bf3(int dtype, int dk) { return dtype == LLA_DTYPE_BF16 && dk >= 32; }
 // workgroups (level j + 1 nodes, plus level j's unpaired last node, times heads) from which two
 // levels go in one launch
 constexpr long kUp2Min = 1;
@@ -159,7 +161,7 @@ int launch(const lla_gdn_args& a, const GdnPlan& pl, void* ws, hipStream_t strea
   const GdnKernels* ks = gdn_kernels(a.dtype, pl.C, a.dk, a.dv);
   const void* up = upsweep_kernel(a.dk, a.dv, false);
   const void* upw = upsweep_kernel(a.dk, a.dv, true);   // null at dk = 128
-  const void* up2 = upsweep2_kernel(a.dk, a.dv);        // null at dk = 128
+  const void* up2 = upsweep2_kernel(a.dk, a.dv, up2_bf3(a.dtype, a.dk));   // null at dk = 128
   if (!ks || !up) return LLA_ERR_UNSUPPORTED;
   GdnParams p;
   memset(&p, 0, sizeof(p));
@@ -177,7 +179,7 @@ int launch(const lla_gdn_args& a, const GdnPlan& pl, void* ws, hipStream_t strea
   const unsigned grid = (unsigned)(pl.N * pl.BH);
   const int sc = chunk_smem_bytes(pl.C, a.dk, a.dv), sq = query_smem_bytes(pl.C, a.dk, a.dv);
   const int su = up_smem_bytes(a.dk, a.dv, false), suw = up_smem_bytes(a.dk, a.dv, true);
-  const int su2 = up2_smem_bytes(a.dk, a.dv);
+  const int su2 = up2_smem_bytes(a.dk, a.dv, up2_bf3(a.dtype, a.dk));
   if (mark(0) != hipSuccess) return LLA_ERR_HIP;
   {
     void* args[] = {&p};
