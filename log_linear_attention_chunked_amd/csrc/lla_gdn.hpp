@@ -649,6 +649,21 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(3))) void g
   }
 }
 
+// gdn_query's (chunk, head) of this workgroup. Consecutive workgroups go to the 8 XCDs in turn,
+// each with its own L2; where the heads divide evenly, head h's chunks all run on XCD h % 8 (in
+// chunk order), so the nodes a head's chunks share are read through one L2.
+__device__ __forceinline__ void query_block(const GdnParams& p, int& c, int& bh) {
+  const int b = blockIdx.x;
+  if (p.BH % 8 == 0) {
+    const int k = b >> 3;
+    bh = (b & 7) + 8 * (k / p.nchunks);
+    c = k % p.nchunks;
+  } else {
+    c = b % p.nchunks;
+    bh = b / p.nchunks;
+  }
+}
+
 // shared-memory layout of gdn_query: query rows (two copies, for X <- X Phi), outputs, one node
 // matrix at a time, lambda rows
 template <int C, int DK, int DV>
@@ -686,7 +701,8 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
   bf16* Ml = reinterpret_cast<bf16*>(smb + S::ML);
   float* lam = reinterpret_cast<float*>(smb + S::LAM);
   const int tid = threadIdx.x;
-  const int c = blockIdx.x % p.nchunks, bh = blockIdx.x / p.nchunks;
+  int c, bh;
+  query_block(p, c, bh);
   const int t0 = c * C;
   const int nv = min(C, p.T - t0);
   const size_t row0 = (size_t)bh * p.T + t0;
@@ -791,7 +807,8 @@ __global__ __launch_bounds__(kNT) void gdn_query_kernel(GdnParams p) {
   float* Ms = sm + S::MAT;
   float* lam = sm + S::LAM;
   const int tid = threadIdx.x;
-  const int c = blockIdx.x % p.nchunks, bh = blockIdx.x / p.nchunks;
+  int c, bh;
+  query_block(p, c, bh);
   const int t0 = c * C;
   const int nv = min(C, p.T - t0);
   const size_t row0 = (size_t)bh * p.T + t0;
