@@ -415,8 +415,9 @@ int loglinear_attn_bwd_default_chunk(int dk, int dv, int dtype);
  *           byte read is written earlier in the call), or NULL/0 to let the library take it
  *           stream-ordered on `stream`. Holds, in float32, the intra-chunk outputs, the query
  *           rows carried to their chunk's start and the Fenwick tree over chunks (each node's
- *           dk x dv state and dk x dk transition); calls that may run concurrently must not
- *           share it.
+ *           dk x dv state and dk x dk transition; for bfloat16 inputs with 32 <= dk <= 64 each
+ *           node matrix as its high bf16 parts followed by its low parts, the same 4 bytes per
+ *           element); calls that may run concurrently must not share it.
  *   stage_events : optional hipEvent_t recorded on `stream`: [0] before the per-chunk kernel,
  *           [1] before the tree up-sweep, [2] before the query kernel, [3] after it.
  * Products run on the matrix cores in float32 (the query and up-sweep kernels', for bfloat16

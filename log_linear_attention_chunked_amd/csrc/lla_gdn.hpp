@@ -63,6 +63,7 @@ struct GdnParams {
   int off_cur;      // up-sweep: first slot of level
   int off_next;     // up-sweep of two levels: first slot of level + 1
   int ncur;         // up-sweep: nodes at level (nchunks >> level)
+  int two;          // gdn_upsweep2: 1 = levels level and level + 1; 0 = level's even nodes only
 };
 
 __device__ __forceinline__ int bit_length(unsigned x) { return 32 - __clz((int)x); }
@@ -75,6 +76,20 @@ __device__ __forceinline__ float lambda_at(const GdnParams& p, size_t i) {
     return __builtin_bit_cast(float, (unsigned)b << 16);
   }
   return reinterpret_cast<const float*>(p.lam)[i];
+}
+
+// Tree nodes in the workspace: float32 matrices, or, for bfloat16 inputs with 32 <= dk <= 64 (where
+// every product that reads them runs in split bf16), each slot's matrix as its high bf16 parts
+// followed by its low parts (the same 4 bytes per element), copied into the split-bf16 images
+// without conversion.
+template <typename T, int DK>
+constexpr bool nodes_split() { return std::is_same<T, bf16>::value && DK >= 32 && DK <= 64; }
+// element i of an n-element matrix stored at `at` as its high parts, then its low parts
+__device__ __forceinline__ void put_split(float* at, int n, int i, float x) {
+  bf16* h = reinterpret_cast<bf16*>(at);
+  const bf16 hi = (bf16)x;
+  h[i] = hi;
+  h[n + i] = (bf16)(x - (float)hi);
 }
 
 // out(i, j) = sum_k A(i, k) B(k, j) for an M x N output over a K-long contraction, operands in
@@ -200,6 +215,16 @@ struct StagedBlock {
       typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
       *reinterpret_cast<u32x2*>(hi + at) = u32x2{hw[0], hw[1]};
       *reinterpret_cast<u32x2*>(lo + at) = u32x2{lw[0], lw[1]};
+    }
+  }
+  // bf16 blocks only: the vectors as they are into a bf16 image (row stride ldd, a multiple of 8)
+  __device__ __forceinline__ void store_raw(bf16* dst, int ldd, int tid) const {
+    static_assert(sizeof(T) == 2, "bf16 sources");
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int v = tid + i * kNT;
+      if (v >= NVEC) break;
+      *reinterpret_cast<u32x4*>(dst + (v / VPR) * ldd + (v % VPR) * EPV) = buf[i];
     }
   }
   __device__ __forceinline__ void store(float* dst, int ldd, int tid) const {
@@ -423,12 +448,18 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
   const size_t slot = (size_t)bh * p.nslot + c;
   float* ng = p.node + slot * DK * DV;
   float* pg = p.phi + slot * DK * DK;
+  // split nodes: high and low parts straight from the accumulators (staging them through shared
+  // memory for 16-byte stores cost more in barriers than it saved)
+  constexpr bool NSPLIT = nodes_split<T, DK>();
   gemm_f32<DK, DV, C, true, false>(Qs, SK, Us, SV, tid, [&](int d, int e, float x) {
-    ng[(size_t)d * DV + e] = x;
+    if constexpr (NSPLIT) put_split(ng, DK * DV, d * DV + e, x);
+    else ng[(size_t)d * DV + e] = x;
   });
   const float eg = __expf(g);
   gemm_f32<DK, DK, C, true, false>(Qs, SK, Ws, SK, tid, [&](int d, int d2, float x) {
-    pg[(size_t)d * DK + d2] = (d == d2 ? eg : 0.f) - x;
+    const float y = (d == d2 ? eg : 0.f) - x;
+    if constexpr (NSPLIT) put_split(pg, DK * DK, d * DK + d2, y);
+    else pg[(size_t)d * DK + d2] = y;
   });
 }
 
@@ -516,8 +547,9 @@ __global__ __launch_bounds__(kNT) void gdn_upsweep_kernel(GdnParams p) {
 // (j + 1, m) and head, plus, where level j has an odd node count, one that folds G0, G1 only
 // (level j's last node, which has no sibling). Each product's output tiles stay in the
 // registers until every wave has read X, then overwrite it in place. BF3 (bfloat16 inputs,
-// dk >= 32): Phi_G and X are held as high and low bf16 images and multiplied in split bf16 as in
-// gemm_bf3; the sums and every stored node stay float32.
+// dk >= 32): the nodes are stored split (nodes_split), Phi_G and X are held as high and low bf16
+// images (copied in as stored) and multiplied in split bf16 as in gemm_bf3, N_G goes through the
+// images' state columns to be added in float32, and a stored node is copied out of the images.
 template <int DK, int DV, bool BF3>
 struct Up2Smem {
   static constexpr int NC = DV + DK;
@@ -551,43 +583,74 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(3))) void g
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int jl = lane & 15, g = lane >> 4;
-  const int npair = p.ncur >> 1, nwg = npair + (p.ncur & 1);
+  // two levels: one workgroup per node (j + 1, m) plus one for level j's unpaired last node;
+  // one level (the top one): its even nodes only (nothing reads the odd ones)
+  const int npair = p.two ? p.ncur >> 1 : 0;
+  const int nwg = p.two ? npair + (p.ncur & 1) : (p.ncur + 1) >> 1;
   const int m = blockIdx.x % nwg, bh = blockIdx.x / nwg;
   const int steps = m < npair ? 3 : 1;
   const size_t base = (size_t)bh * p.nslot;
   const size_t g0 = base + p.off_prev + 4 * m;
   const int i0 = (w % RT) * 16, c0 = w / RT;
   auto col_tile = [&](int t) { return c0 + WPR * t; };
-  {
+  // BF3: the nodes are stored as high and low bf16 parts, copied into the images as they are
+  auto hi_of = [](const float* at) { return reinterpret_cast<const bf16*>(at); };
+  if constexpr (BF3) {
+    StagedBlock<bf16, DK, DV> snh, snl;
+    StagedBlock<bf16, DK, DK> sfh, sfl, sah, sal;
+    snh.load(hi_of(p.node + g0 * DK * DV), DV, DK, tid);
+    snl.load(hi_of(p.node + g0 * DK * DV) + DK * DV, DV, DK, tid);
+    sfh.load(hi_of(p.phi + g0 * DK * DK), DK, DK, tid);
+    sfl.load(hi_of(p.phi + g0 * DK * DK) + DK * DK, DK, DK, tid);
+    sah.load(hi_of(p.phi + (g0 + 1) * DK * DK), DK, DK, tid);
+    sal.load(hi_of(p.phi + (g0 + 1) * DK * DK) + DK * DK, DK, DK, tid);
+    snh.store_raw(Xh, SW, tid);
+    snl.store_raw(Xl, SW, tid);
+    sfh.store_raw(Xh + DV, SW, tid);
+    sfl.store_raw(Xl + DV, SW, tid);
+    sah.store_raw(Ah, SP, tid);
+    sal.store_raw(Al, SP, tid);
+  } else {
     StagedBlock<float, DK, DV> sn;
     StagedBlock<float, DK, DK> sf, sa;
     sn.load(p.node + g0 * DK * DV, DV, DK, tid);
     sf.load(p.phi + g0 * DK * DK, DK, DK, tid);
     sa.load(p.phi + (g0 + 1) * DK * DK, DK, DK, tid);
-    if constexpr (BF3) {
-      sn.store_split(Xh, Xl, SW, tid);
-      sf.store_split(Xh + DV, Xl + DV, SW, tid);
-      sa.store_split(Ah, Al, SP, tid);
-    } else {
-      sn.store(X, SW, tid);
-      sf.store(X + DV, SW, tid);
-      sa.store(A, SP, tid);
-    }
+    sn.store(X, SW, tid);
+    sf.store(X + DV, SW, tid);
+    sa.store(A, SP, tid);
   }
   __syncthreads();
   for (int s = 1; s <= steps; ++s) {
     const size_t gs = g0 + s;
     // N of G_s for the state columns and the next transition, in flight during the product
-    float nadd[PERW][4];
+    // float32: the lane's elements of N_G directly; split: N_G's 16-byte vectors, which go
+    // through the images' state columns once the product has read them
+    float nadd[BF3 ? 1 : PERW][4];
+    if constexpr (!BF3) {
 #pragma unroll
-    for (int t = 0; t < PERW; ++t) {
-      const int j0 = col_tile(t) * 16;
+      for (int t = 0; t < PERW; ++t) {
+        const int j0 = col_tile(t) * 16;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        nadd[t][r] = j0 < DV ? p.node[gs * DK * DV + (size_t)(i0 + 4 * g + r) * DV + j0 + jl] : 0.f;
+        for (int r = 0; r < 4; ++r)
+          nadd[t][r] = j0 < DV ? p.node[gs * DK * DV + (size_t)(i0 + 4 * g + r) * DV + j0 + jl] : 0.f;
+      }
     }
-    StagedBlock<float, DK, DK> nxt;
-    if (s < steps) nxt.load(p.phi + (gs + 1) * DK * DK, DK, DK, tid);
+    StagedBlock<bf16, DK, BF3 ? DV : 16> nah, nal;
+    if constexpr (BF3) {
+      nah.load(hi_of(p.node + gs * DK * DV), DV, DK, tid);
+      nal.load(hi_of(p.node + gs * DK * DV) + DK * DV, DV, DK, tid);
+    }
+    StagedBlock<float, DK, BF3 ? 16 : DK> nxt;      // float32 transitions
+    StagedBlock<bf16, DK, BF3 ? DK : 16> nxh, nxl;   // split transitions
+    if (s < steps) {
+      if constexpr (BF3) {
+        nxh.load(hi_of(p.phi + (gs + 1) * DK * DK), DK, DK, tid);
+        nxl.load(hi_of(p.phi + (gs + 1) * DK * DK) + DK * DK, DK, DK, tid);
+      } else {
+        nxt.load(p.phi + (gs + 1) * DK * DK, DK, DK, tid);
+      }
+    }
     f32x4 acc[PERW];
 #pragma unroll
     for (int t = 0; t < PERW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -617,6 +680,17 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(3))) void g
       }
     }
     __syncthreads();   // every wave has read A and X
+    if constexpr (BF3) {
+      // N_G into the state columns of the images (read back below by the lane that owns each
+      // element), the next transition into A's
+      nah.store_raw(Xh, SW, tid);
+      nal.store_raw(Xl, SW, tid);
+      if (s < steps) {
+        nxh.store_raw(Ah, SP, tid);
+        nxl.store_raw(Al, SP, tid);
+      }
+      __syncthreads();
+    }
     const bool out = s != 2;
     const size_t slot = s == 1 ? base + p.off_cur + 2 * m : base + p.off_next + m;
 #pragma unroll
@@ -626,26 +700,43 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(3))) void g
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = i0 + 4 * g + r;
-          const float x = acc[t][r] + nadd[t][r];
           if constexpr (BF3) {
+            float x = acc[t][r];
+            if (j0 < DV) x += (float)Xh[row * SW + col] + (float)Xl[row * SW + col];
             const bf16 h = (bf16)x;
             Xh[row * SW + col] = h;
             Xl[row * SW + col] = (bf16)(x - (float)h);
           } else {
+            const float x = acc[t][r] + nadd[t][r];
             X[row * SW + col] = x;
-          }
-          if (out) {
-            if (j0 < DV) p.node[slot * DK * DV + (size_t)row * DV + col] = x;
-            else p.phi[slot * DK * DK + (size_t)row * DK + col - DV] = x;
+            if (out) {
+              if (j0 < DV) p.node[slot * DK * DV + (size_t)row * DV + col] = x;
+              else p.phi[slot * DK * DK + (size_t)row * DK + col - DV] = x;
+            }
           }
         }
       }
     }
-    if (s < steps) {
-      if constexpr (BF3) nxt.store_split(Ah, Al, SP, tid);
-      else nxt.store(A, SP, tid);
+    if constexpr (!BF3) {
+      if (s < steps) nxt.store(A, SP, tid);
     }
     __syncthreads();
+    if constexpr (BF3) {
+      // the stored node's high and low parts from the images, 16 bytes at a time (the next
+      // product only reads the images)
+      if (out) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        constexpr int VR = NC / 8;   // 16-byte vectors per image row
+        bf16* nh = reinterpret_cast<bf16*>(p.node + slot * DK * DV);
+        bf16* fh = reinterpret_cast<bf16*>(p.phi + slot * DK * DK);
+        for (int v = tid; v < 2 * DK * VR; v += kNT) {
+          const int part = v / (DK * VR), row = (v / VR) % DK, col = (v % VR) * 8;
+          const u32x4 x = *reinterpret_cast<const u32x4*>((part ? Xl : Xh) + row * SW + col);
+          if (col < DV) *reinterpret_cast<u32x4*>(nh + part * DK * DV + row * DV + col) = x;
+          else *reinterpret_cast<u32x4*>(fh + part * DK * DK + row * DK + col - DV) = x;
+        }
+      }
+    }
   }
 }
 
@@ -716,10 +807,21 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
     const unsigned rest = (unsigned)c >> (j + 1);
     return rest ? j + 1 + __builtin_ctz(rest) : -1;
   };
-  // up to d = 64 the next node's state and transition travel in registers meanwhile
+  // up to d = 64 the next node's state and transition travel in registers meanwhile, as the
+  // high and low bf16 parts the tree stores them in, copied into the images as they are
   constexpr bool PRE = DK <= 64;
-  StagedBlock<float, DK, PRE ? DV : 16> nb;
-  StagedBlock<float, DK, PRE ? DK : 16> fb;
+  static_assert(PRE == nodes_split<bf16, DK>(), "split nodes exactly where they are prefetched");
+  auto hi_of = [](const float* at) { return reinterpret_cast<const bf16*>(at); };
+  StagedBlock<bf16, DK, PRE ? DV : 16> nbh, nbl;
+  StagedBlock<bf16, DK, PRE ? DK : 16> fbh, fbl;
+  auto load_node = [&](size_t slot, bool phi) {
+    nbh.load(hi_of(p.node + slot * DK * DV), DV, DK, tid);
+    nbl.load(hi_of(p.node + slot * DK * DV) + DK * DV, DV, DK, tid);
+    if (phi) {
+      fbh.load(hi_of(p.phi + slot * DK * DK), DK, DK, tid);
+      fbl.load(hi_of(p.phi + slot * DK * DK) + DK * DK, DK, DK, tid);
+    }
+  };
   int j = c ? __builtin_ctz((unsigned)c) : -1;
   {
     StagedBlock<float, C, DK> sx;
@@ -729,11 +831,7 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
     so.load(p.oi + wrow0 * DV, DV, C, tid);
     sl.load(p, row0, nv, tid);
     if constexpr (PRE) {
-      if (j >= 0) {
-        const size_t slot = slot_of(j, (c >> j) - 1);
-        nb.load(p.node + slot * DK * DV, DV, DK, tid);
-        if (next_bit(j) >= 0) fb.load(p.phi + slot * DK * DK, DK, DK, tid);
-      }
+      if (j >= 0) load_node(slot_of(j, (c >> j) - 1), next_bit(j) >= 0);
     }
     sx.store_split(xh[0], xl[0], SX, tid);
     so.store(Os, SV, tid);
@@ -745,7 +843,8 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
     const size_t slot = slot_of(j, (c >> j) - 1);
     const int jn = next_bit(j);
     if constexpr (PRE) {
-      nb.store_split(Mh, Ml, SMB, tid);
+      nbh.store_raw(Mh, SMB, tid);
+      nbl.store_raw(Ml, SMB, tid);
     } else {
       StagedBlock<float, DK, DV> b;
       b.load(p.node + slot * DK * DV, DV, DK, tid);
@@ -759,10 +858,9 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
     __syncthreads();
     if (jn >= 0) {           // a higher node follows: X <- X Phi of this node
       if constexpr (PRE) {
-        fb.store_split(Mh, Ml, SMB, tid);
-        const size_t sn = slot_of(jn, (c >> jn) - 1);
-        nb.load(p.node + sn * DK * DV, DV, DK, tid);
-        if (next_bit(jn) >= 0) fb.load(p.phi + sn * DK * DK, DK, DK, tid);
+        fbh.store_raw(Mh, SMB, tid);
+        fbl.store_raw(Ml, SMB, tid);
+        load_node(slot_of(jn, (c >> jn) - 1), next_bit(jn) >= 0);
       } else {
         StagedBlock<float, DK, DK> b;
         b.load(p.phi + slot * DK * DK, DK, DK, tid);

@@ -74,9 +74,7 @@ const void* upsweep2_kernel(int dk, int dv, bool bf3) {
   return nullptr;
 }
 inline bool up2_bf3(int dtype, int dk) { return dtype == LLA_DTYPE_BF16 && dk >= 32; }
-// workgroups (level j + 1 nodes, plus level j's unpaired last node, times heads) from which two
-// levels go in one launch
-constexpr long kUp2Min = 1;
+
 
 bool fits(int C, int dk, int dv) {
   using namespace lla::gdn;
@@ -199,11 +197,15 @@ int launch(const lla_gdn_args& a, const GdnPlan& pl, void* ws, hipStream_t strea
     pj.off_next = pj.off_cur + (pl.N >> j);
     pj.ncur = pl.N >> j;
     void* args[] = {&pj};
-    const long nwg2 = (long)((pj.ncur >> 1) + (pj.ncur & 1)) * pl.BH;
-    if (up2 && j + 1 <= pl.top && nwg2 >= kUp2Min) {
-      if (hipLaunchKernel(up2, dim3((unsigned)nwg2), dim3(kNT), args, su2, stream) != hipSuccess) return LLA_ERR_HIP;
-      off_prev = pj.off_next;   // the next launch builds level j + 2 from level j + 1
-      j += 2;
+    if (up2) {
+      // for dk <= 64 every level goes through gdn_upsweep2 (its split-bf16 form reads and writes
+      // the nodes as high and low parts, which no other up-sweep kernel reads): two levels at a
+      // time, and a last odd level's even nodes on their own
+      pj.two = j + 1 <= pl.top ? 1 : 0;
+      const long nwg = pj.two ? (long)((pj.ncur >> 1) + (pj.ncur & 1)) * pl.BH : (long)((pj.ncur + 1) >> 1) * pl.BH;
+      if (hipLaunchKernel(up2, dim3((unsigned)nwg), dim3(kNT), args, su2, stream) != hipSuccess) return LLA_ERR_HIP;
+      off_prev = pj.two ? pj.off_next : pj.off_cur;
+      j += pj.two ? 2 : 1;
       continue;
     }
     const bool whole = upw && (long)pj.ncur * pl.BH >= kUpWholeMin;
