@@ -99,8 +99,8 @@ __device__ __forceinline__ void put_split(float* at, int n, int i, float x) {
 // lane (j, g) (j = lane % 16, g = lane / 16) supplies A(16ti + j, k + g) and B(k + g, 16tj + j),
 // and the accumulator gives it rows 16ti + 4g .. +3 of column 16tj + j. Every output value is
 // handed once to epi(i, j, value).
-template <int M, int N, int K, bool TA, bool TB, typename Epi>
-__device__ __forceinline__ void gemm_f32(const float* A, int lda, const float* B, int ldb, int tid,
+template <int M, int N, int K, bool TA, bool TB, typename AT, typename Epi>
+__device__ __forceinline__ void gemm_f32(const AT* A, int lda, const float* B, int ldb, int tid,
                                          Epi&& epi, const float* kscale = nullptr) {
   static_assert(M % 16 == 0 && N % 16 == 0 && K % 4 == 0, "16 x 16 tiles, 4-deep steps");
   constexpr int TN = N / 16, NTILE = (M / 16) * TN, NWAVE = kNT / 64;
@@ -113,7 +113,7 @@ __device__ __forceinline__ void gemm_f32(const float* A, int lda, const float* B
 #pragma unroll 4
     for (int k = 0; k < K; k += 4) {
       const int kk = k + g;
-      const float a = TA ? A[kk * lda + i0 + j] : A[(i0 + j) * lda + kk];
+      const float a = to_f(TA ? A[kk * lda + i0 + j] : A[(i0 + j) * lda + kk]);
       float b = TB ? B[(j0 + j) * ldb + kk] : B[kk * ldb + j0 + j];
       if (kscale) b *= kscale[kk];
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
@@ -256,33 +256,39 @@ __device__ __forceinline__ void stage_block(float* dst, int ldd, const T* src, s
   b.store(dst, ldd, tid);
 }
 
-// lambda rows of positions [row0, row0 + C) bound for lam[r * kLamCapG + l] (rows past nv and
-// levels past L are zero weights), loaded and stored like StagedBlock
-template <int C>
+// levels 0 .. LW - 1 of the lambda rows of positions [row0, row0 + C), bound for lam[r * LW + l]
+// (rows past nv and levels past L are zero weights), loaded and stored like StagedBlock
+template <int C, int LW = kLamCapG>
 struct StagedLambda {
-  static constexpr int PER = (C * kLamCapG + kNT - 1) / kNT;
+  static constexpr int PER = (C * LW + kNT - 1) / kNT;
   float buf[PER];
   __device__ __forceinline__ void load(const GdnParams& p, size_t row0, int nv, int tid) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int idx = tid + i * kNT, r = idx / kLamCapG, l = idx % kLamCapG;
-      buf[i] = (idx < C * kLamCapG && r < nv && l < p.L) ? lambda_at(p, (row0 + r) * p.L + l) : 0.f;
+      const int idx = tid + i * kNT, r = idx / LW, l = idx % LW;
+      buf[i] = (idx < C * LW && r < nv && l < p.L) ? lambda_at(p, (row0 + r) * p.L + l) : 0.f;
     }
   }
   __device__ __forceinline__ void store(float* lam, int tid) const {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int idx = tid + i * kNT;
-      if (idx < C * kLamCapG) lam[idx] = buf[i];
+      if (idx < C * LW) lam[idx] = buf[i];
     }
   }
 };
 
 // Shared-memory bytes of the three kernels (host and device agree; the host refuses shapes past
 // 160 KB).
-__host__ __device__ constexpr int chunk_smem_bytes(int C, int DK, int DV) {
-  return 4 * (2 * C * (DK + 1) + C * (DV + 1) + 3 * C * (C + 1) + C * (DK + 1) + C * (DV + 1) +
-              C * kLamCapG + 3 * C);
+// gdn_chunk reads the in-chunk lambda levels only (bit_length(i ^ j) <= log2 C)
+__host__ __device__ constexpr int chunk_lw(int C) { return C == 16 ? 5 : C == 32 ? 6 : 7; }
+// QB: bfloat16 inputs keep q as a bf16 image (rows padded by 8 elements; its values are exact in
+// bf16), and Khat then takes the float32 buffers of Lqk and Tm^{-1} (free by then) where they hold
+// it: at chunk 32 and d = 64, 57.6 -> 51.6 KB, three workgroups per compute unit instead of two
+__host__ __device__ constexpr bool chunk_qb(bool bf, int C, int DK) { return bf && 2 * (C + 1) >= DK + 1; }
+__host__ __device__ constexpr int chunk_smem_bytes(int C, int DK, int DV, bool bf = false) {
+  return 4 * ((chunk_qb(bf, C, DK) ? C * (DK + 8) / 2 : C * (DK + 1)) + C * (DK + 1) + C * (DV + 1) +
+              3 * C * (C + 1) + C * (DK + 1) + C * (DV + 1) + C * chunk_lw(C) + 3 * C);
 }
 // up-sweep panel width: the whole [N | Phi] row (WHOLE: one workgroup per node, the right
 // child's transition read once; for dk <= 64, at levels with enough nodes to fill the device) or
@@ -310,15 +316,18 @@ __host__ __device__ constexpr int query_smem_bytes(int C, int DK, int DV) {
                                                                            : query_smem_bytes_bf3(C, DK, DV);
 }
 
-// shared-memory layout of gdn_chunk (floats; row strides padded by one)
-template <int C, int DK, int DV>
+// shared-memory layout of gdn_chunk (floats; float32 row strides padded by one)
+template <int C, int DK, int DV, bool BF>
 struct ChunkSmem {
-  static constexpr int SK = DK + 1, SV = DV + 1, SC = C + 1;
-  static constexpr int Q = 0, K = Q + C * SK, V = K + C * SK, M1 = V + C * SV, M2 = M1 + C * SC,
-                       Y = M2 + C * SC, W = Y + C * SC, U = W + C * SK, LAM = U + C * SV,
-                       AL = LAM + C * kLamCapG, BT = AL + C, BE = BT + C, TOTAL = BE + C;
+  static constexpr bool QB = chunk_qb(BF, C, DK);
+  static constexpr int SK = DK + 1, SV = DV + 1, SC = C + 1, SQ = QB ? DK + 8 : SK, LW = chunk_lw(C);
+  static constexpr int Q = 0, K = Q + (QB ? C * SQ / 2 : C * SK), V = K + C * SK, M1 = V + C * SV,
+                       M2 = M1 + C * SC, Y = M2 + C * SC, W = Y + C * SC, U = W + C * SK,
+                       LAM = U + C * SV, AL = LAM + C * LW, BT = AL + C, BE = BT + C, TOTAL = BE + C;
+  static constexpr int KH = QB ? M2 : Q;   // Khat (float32, stride SK)
   static constexpr int BYTES = TOTAL * 4;
-  static_assert(BYTES == chunk_smem_bytes(C, DK, DV), "layout and size formula agree");
+  static_assert(BYTES == chunk_smem_bytes(C, DK, DV, BF), "layout and size formula agree");
+  static_assert(!QB || KH + C * SK <= W, "Khat fits the buffers of Lqk and Tm^{-1}");
 };
 
 // gdn_chunk: per (chunk, head) the intra-chunk output, the query rows carried to the chunk's
@@ -327,10 +336,14 @@ struct ChunkSmem {
 template <typename T, int C, int DK, int DV>
 __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
   static_assert(C <= 64, "one lane per position in the log_a scan");
-  using S = ChunkSmem<C, DK, DV>;
-  constexpr int SK = S::SK, SV = S::SV, SC = S::SC;
-  extern __shared__ float sm[];
-  float* Qs = sm + S::Q;  float* Ks = sm + S::K;  float* Vs = sm + S::V;
+  using S = ChunkSmem<C, DK, DV, std::is_same<T, bf16>::value>;
+  constexpr int SK = S::SK, SV = S::SV, SC = S::SC, SQ = S::SQ;
+  extern __shared__ __attribute__((aligned(16))) float sm[];
+  // q: a bf16 image (QB) or float32; Khat: float32, in q's buffer or (QB) those of Lqk and Tm^{-1}
+  typedef typename std::conditional<S::QB, bf16, float>::type QT;
+  QT* Qs = reinterpret_cast<QT*>(sm + S::Q);
+  float* Kh = sm + S::KH;
+  float* Ks = sm + S::K;  float* Vs = sm + S::V;
   float* M1 = sm + S::M1; float* M2 = sm + S::M2; float* Ti = sm + S::Y;
   float* Ws = sm + S::W;  float* Us = sm + S::U;  float* lam = sm + S::LAM;
   float* al = sm + S::AL; float* bt = sm + S::BT; float* be = sm + S::BE;
@@ -348,12 +361,13 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
   {
     StagedBlock<T, C, DK> sq, sk;
     StagedBlock<T, C, DV> sv;
-    StagedLambda<C> sl;
+    StagedLambda<C, S::LW> sl;
     sq.load(qg + row0 * DK, DK, nv, tid);
     sk.load(kg + row0 * DK, DK, nv, tid);
     sv.load(vg + row0 * DV, DV, nv, tid);
     sl.load(p, row0, nv, tid);
-    sq.store(Qs, SK, tid);
+    if constexpr (S::QB) sq.store_raw(Qs, SQ, tid);
+    else sq.store(Qs, SK, tid);
     sk.store(Ks, SK, tid);
     sv.store(Vs, SV, tid);
     sl.store(lam, tid);
@@ -417,7 +431,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
   // W = Ti diag(beta e^a) K, U = Ti diag(beta) V; Lqk into M2 (its scratch use is over)
   gemm_f32<C, DK, C, false, false>(Ti, SC, Ks, SK, tid, [&](int i, int d, float x) { Ws[i * SK + d] = x; }, be);
   gemm_f32<C, DV, C, false, false>(Ti, SC, Vs, SV, tid, [&](int i, int e, float x) { Us[i * SV + e] = x; }, bt);
-  gemm_f32<C, C, DK, false, true>(Qs, SK, Ks, SK, tid, [&](int i, int j, float x) {
+  gemm_f32<C, C, DK, false, true>(Qs, SQ, Ks, SK, tid, [&](int i, int j, float x) {
     M2[i * SC + j] = j <= i ? x * __expf(al[i] - al[j]) : 0.f;
   });
   __syncthreads();
@@ -426,21 +440,21 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
   // attention matrix inside the chunk under the level weights (Tm is no longer read)
   float* x0g = p.x0 + wrow0 * DK;
   gemm_f32<C, DK, C, false, false>(M2, SC, Ws, SK, tid, [&](int i, int d, float x) {
-    x0g[(size_t)i * DK + d] = __expf(al[i]) * Qs[i * SK + d] - x;
+    x0g[(size_t)i * DK + d] = __expf(al[i]) * to_f(Qs[i * SQ + d]) - x;
   });
   gemm_f32<C, C, C, false, false>(M2, SC, Ti, SC, tid, [&](int i, int j, float x) {
-    M1[i * SC + j] = j <= i ? x * bt[j] * lam[i * kLamCapG + bit_length((unsigned)(i ^ j))] : 0.f;
+    M1[i * SC + j] = j <= i ? x * bt[j] * lam[i * S::LW + bit_length((unsigned)(i ^ j))] : 0.f;
   });
   __syncthreads();
 
-  // O_intra = M1 V (to the workspace); Khat = diag(e^{g-a}) K into the q buffer (q is done)
+  // O_intra = M1 V (to the workspace); Khat = diag(e^{g-a}) K (q, Lqk and Tm^{-1} are done)
   float* oig = p.oi + wrow0 * DV;
   gemm_f32<C, DV, C, false, false>(M1, SC, Vs, SV, tid, [&](int i, int e, float x) {
     oig[(size_t)i * DV + e] = x;
   });
   for (int i = tid; i < C * DK; i += kNT) {
     const int r = i / DK, d = i % DK;
-    Qs[r * SK + d] = __expf(g - al[r]) * Ks[r * SK + d];
+    Kh[r * SK + d] = __expf(g - al[r]) * Ks[r * SK + d];
   }
   __syncthreads();
 
@@ -451,12 +465,12 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
   // split nodes: high and low parts straight from the accumulators (staging them through shared
   // memory for 16-byte stores cost more in barriers than it saved)
   constexpr bool NSPLIT = nodes_split<T, DK>();
-  gemm_f32<DK, DV, C, true, false>(Qs, SK, Us, SV, tid, [&](int d, int e, float x) {
+  gemm_f32<DK, DV, C, true, false>(Kh, SK, Us, SV, tid, [&](int d, int e, float x) {
     if constexpr (NSPLIT) put_split(ng, DK * DV, d * DV + e, x);
     else ng[(size_t)d * DV + e] = x;
   });
   const float eg = __expf(g);
-  gemm_f32<DK, DK, C, true, false>(Qs, SK, Ws, SK, tid, [&](int d, int d2, float x) {
+  gemm_f32<DK, DK, C, true, false>(Kh, SK, Ws, SK, tid, [&](int d, int d2, float x) {
     const float y = (d == d2 ? eg : 0.f) - x;
     if constexpr (NSPLIT) put_split(pg, DK * DK, d * DK + d2, y);
     else pg[(size_t)d * DK + d2] = y;
