@@ -173,6 +173,37 @@ __device__ __forceinline__ void gemm_bf3(const bf16* Ah, const bf16* Al, int lda
   }
 }
 
+// gemm_bf3 with the epilogue told the tile's place among the wave's (t < gemm_tiles_per_wave) and
+// the accumulator row r, so that a caller can keep the outputs in registers across products
+template <int M, int N>
+constexpr int gemm_tiles_per_wave() { return ((M / 16) * (N / 16) + kNT / 64 - 1) / (kNT / 64); }
+template <int M, int N, int K, typename Epi>
+__device__ __forceinline__ void gemm_bf3_t(const bf16* Ah, const bf16* Al, int lda, const bf16* Bh,
+                                           const bf16* Bl, int ldb, int tid, Epi&& epi) {
+  static_assert(M % 16 == 0 && N % 16 == 0 && K % 32 == 0, "16 x 16 tiles, 32-deep steps");
+  constexpr int TN = N / 16, NTILE = (M / 16) * TN, NWAVE = kNT / 64, PERW = gemm_tiles_per_wave<M, N>();
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int j = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < PERW; ++t) {
+    const int tile = w + t * NWAVE;
+    if (tile >= NTILE) break;
+    const int i0 = (tile / TN) * 16, j0 = (tile % TN) * 16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < K; k += 32) {
+      const bf16x8 ah = frag_rows(Ah, lda, i0 + j, k + 8 * g), al = frag_rows(Al, lda, i0 + j, k + 8 * g);
+      const bf16x8 bh = frag_cols(Bh, ldb, k + 8 * g, j0 + j), bl = frag_cols(Bl, ldb, k + 8 * g, j0 + j);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) epi(t, r, i0 + 4 * g + r, j0 + j, acc[r]);
+  }
+}
+
 // An R x CC row-major block (source row stride src_ld elements) on its way into shared-memory
 // floats dst[r * ldd + c], rows at or past nv read as zeros: load() issues the thread's 16-byte
 // vector loads into registers, store() converts and writes them. Several blocks loaded before
@@ -256,16 +287,17 @@ __device__ __forceinline__ void stage_block(float* dst, int ldd, const T* src, s
   b.store(dst, ldd, tid);
 }
 
-// levels 0 .. LW - 1 of the lambda rows of positions [row0, row0 + C), bound for lam[r * LW + l]
-// (rows past nv and levels past L are zero weights), loaded and stored like StagedBlock
-template <int C, int LW = kLamCapG>
+// levels L0 .. L0 + LW - 1 of the lambda rows of positions [row0, row0 + C), bound for
+// lam[r * LW + l - L0] (rows past nv and levels past L are zero weights), loaded and stored like
+// StagedBlock
+template <int C, int LW = kLamCapG, int L0 = 0>
 struct StagedLambda {
   static constexpr int PER = (C * LW + kNT - 1) / kNT;
   float buf[PER];
   __device__ __forceinline__ void load(const GdnParams& p, size_t row0, int nv, int tid) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const int idx = tid + i * kNT, r = idx / LW, l = idx % LW;
+      const int idx = tid + i * kNT, r = idx / LW, l = L0 + idx % LW;
       buf[i] = (idx < C * LW && r < nv && l < p.L) ? lambda_at(p, (row0 + r) * p.L + l) : 0.f;
     }
   }
@@ -305,12 +337,18 @@ __host__ __device__ constexpr int up2_smem_bytes(int DK, int DV, bool bf3) {
 __host__ __device__ constexpr int query_smem_bytes_f32(int C, int DK, int DV) {
   return 4 * (2 * C * (DK + 1) + C * (DV + 1) + DK * ((DK > DV ? DK : DV) + 1) + C * kLamCapG);
 }
-// bfloat16 inputs: the query rows (two, each high and low parts) and the node matrix (high and
-// low parts) in bf16, rows padded by 8 elements; the outputs and lambda rows in fp32
+// bfloat16 inputs (dk >= 32): the query rows (two, each high and low parts) and the node matrix
+// (high and low parts) in bf16, rows padded by 8 elements, and the lambda rows' levels above the
+// chunk in fp32 (the outputs stay in the registers): 39.2 KB at chunk 32, d = 64, four workgroups
+// per compute unit
+__host__ __device__ constexpr int query_jlev(int C) { return C == 16 ? 5 : C == 32 ? 6 : 7; }
 __host__ __device__ constexpr int query_smem_bytes_bf3(int C, int DK, int DV) {
-  return 2 * 4 * C * (DK + 8) + 4 * C * (DV + 1) + 2 * 2 * DK * ((DK > DV ? DK : DV) + 8) +
-         4 * C * kLamCapG;
+  return 2 * 4 * C * (DK + 8) + 2 * 2 * DK * ((DK > DV ? DK : DV) + 8) + 4 * C * (kLamCapG - query_jlev(C));
 }
+__host__ __device__ constexpr int query_smem_bytes(int C, int DK, int DV, bool bf) {
+  return bf && DK >= 32 ? query_smem_bytes_bf3(C, DK, DV) : query_smem_bytes_f32(C, DK, DV);
+}
+// the larger of the two (the shape checks, which do not depend on the input type)
 __host__ __device__ constexpr int query_smem_bytes(int C, int DK, int DV) {
   return query_smem_bytes_f32(C, DK, DV) > query_smem_bytes_bf3(C, DK, DV) ? query_smem_bytes_f32(C, DK, DV)
                                                                            : query_smem_bytes_bf3(C, DK, DV);
@@ -784,12 +822,12 @@ struct QuerySmem {
 // low parts), outputs (fp32), one node matrix (high and low parts), lambda rows (fp32)
 template <int C, int DK, int DV>
 struct QuerySmemB {
-  static constexpr int SX = DK + 8, SV = DV + 1, MD = DK > DV ? DK : DV, SMB = MD + 8;
+  static constexpr int SX = DK + 8, MD = DK > DV ? DK : DV, SMB = MD + 8;
+  static constexpr int J1 = query_jlev(C), LW = kLamCapG - J1;   // lambda levels J1 .. 23
   static constexpr int XB = C * SX * 2, MB = DK * SMB * 2;
-  static constexpr int X = 0, O = X + 4 * XB, MH = O + C * SV * 4, ML = MH + MB, LAM = ML + MB,
-                       TOTAL = LAM + C * kLamCapG * 4;
+  static constexpr int X = 0, MH = X + 4 * XB, ML = MH + MB, LAM = ML + MB, TOTAL = LAM + C * LW * 4;
   static_assert(TOTAL == query_smem_bytes_bf3(C, DK, DV), "layout and size formula agree");
-  static_assert(XB % 16 == 0 && (C * SV * 4) % 16 == 0 && MB % 16 == 0, "16-byte aligned images");
+  static_assert(XB % 16 == 0 && MB % 16 == 0, "16-byte aligned images");
 };
 
 // gdn_query for bfloat16 inputs (dk >= 32): the same read-outs, every product in split bf16
@@ -797,11 +835,10 @@ struct QuerySmemB {
 template <int C, int DK, int DV>
 __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char* smb) {
   using S = QuerySmemB<C, DK, DV>;
-  constexpr int SX = S::SX, SV = S::SV, SMB = S::SMB;
-  constexpr int J = C == 16 ? 4 : C == 32 ? 5 : 6;
+  constexpr int SX = S::SX, SMB = S::SMB, LW = S::LW;
+  constexpr int OPW = gemm_tiles_per_wave<C, DV>(), OTN = DV / 16, NOT = (C / 16) * OTN;
   bf16* xh[2] = {reinterpret_cast<bf16*>(smb + S::X), reinterpret_cast<bf16*>(smb + S::X + 2 * S::XB)};
   bf16* xl[2] = {reinterpret_cast<bf16*>(smb + S::X + S::XB), reinterpret_cast<bf16*>(smb + S::X + 3 * S::XB)};
-  float* Os = reinterpret_cast<float*>(smb + S::O);
   bf16* Mh = reinterpret_cast<bf16*>(smb + S::MH);
   bf16* Ml = reinterpret_cast<bf16*>(smb + S::ML);
   float* lam = reinterpret_cast<float*>(smb + S::LAM);
@@ -837,18 +874,26 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
     }
   };
   int j = c ? __builtin_ctz((unsigned)c) : -1;
+  // the outputs in the registers, in gemm_bf3_t's places: tile w + 4t of the C x DV output, row
+  // 4g + r of it, column (lane % 16); from the intra-chunk outputs
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, jl = lane & 15, g4 = 4 * (lane >> 4);
+  float oacc[OPW][4];
+#pragma unroll
+  for (int t = 0; t < OPW; ++t) {
+    const int tile = w + t * (kNT / 64), i0 = (tile / OTN) * 16, j0 = (tile % OTN) * 16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      oacc[t][r] = tile < NOT ? p.oi[(wrow0 + i0 + g4 + r) * DV + j0 + jl] : 0.f;
+  }
   {
     StagedBlock<float, C, DK> sx;
-    StagedBlock<float, C, DV> so;
-    StagedLambda<C> sl;
+    StagedLambda<C, LW, S::J1> sl;
     sx.load(p.x0 + wrow0 * DK, DK, C, tid);
-    so.load(p.oi + wrow0 * DV, DV, C, tid);
     sl.load(p, row0, nv, tid);
     if constexpr (PRE) {
       if (j >= 0) load_node(slot_of(j, (c >> j) - 1), next_bit(j) >= 0);
     }
     sx.store_split(xh[0], xl[0], SX, tid);
-    so.store(Os, SV, tid);
     sl.store(lam, tid);
   }
   __syncthreads();
@@ -865,9 +910,9 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
       b.store_split(Mh, Ml, SMB, tid);
     }
     __syncthreads();
-    const int lev = J + 1 + j;
-    gemm_bf3<C, DV, DK>(xh[a], xl[a], SX, Mh, Ml, SMB, tid, [&](int i, int e, float x) {
-      Os[i * SV + e] += lam[i * kLamCapG + lev] * x;
+    // level J + 1 + j, at j of the staged levels
+    gemm_bf3_t<C, DV, DK>(xh[a], xl[a], SX, Mh, Ml, SMB, tid, [&](int t, int r, int i, int e, float x) {
+      oacc[t][r] += lam[i * LW + j] * x;
     });
     __syncthreads();
     if (jn >= 0) {           // a higher node follows: X <- X Phi of this node
@@ -894,9 +939,12 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
     j = jn;
   }
   bf16* og = reinterpret_cast<bf16*>(p.out);
-  for (int i = tid; i < C * DV; i += kNT) {
-    const int r = i / DV, e = i % DV;
-    if (r < nv) og[(row0 + r) * DV + e] = (bf16)Os[r * SV + e];
+#pragma unroll
+  for (int t = 0; t < OPW; ++t) {
+    const int tile = w + t * (kNT / 64), i0 = (tile / OTN) * 16, j0 = (tile % OTN) * 16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (tile < NOT && i0 + g4 + r < nv) og[(row0 + i0 + g4 + r) * DV + j0 + jl] = (bf16)oacc[t][r];
   }
 }
 

@@ -176,7 +176,7 @@ int launch(const lla_gdn_args& a, const GdnPlan& pl, void* ws, hipStream_t strea
   };
   const unsigned grid = (unsigned)(pl.N * pl.BH);
   const int sc = chunk_smem_bytes(pl.C, a.dk, a.dv, a.dtype == LLA_DTYPE_BF16);
-  const int sq = query_smem_bytes(pl.C, a.dk, a.dv);
+  const int sq = query_smem_bytes(pl.C, a.dk, a.dv, a.dtype == LLA_DTYPE_BF16);
   const int su = up_smem_bytes(a.dk, a.dv, false), suw = up_smem_bytes(a.dk, a.dv, true);
   const int su2 = up2_smem_bytes(a.dk, a.dv, up2_bf3(a.dtype, a.dk));
   if (mark(0) != hipSuccess) return LLA_ERR_HIP;
