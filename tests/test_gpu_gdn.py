@@ -66,6 +66,11 @@ SHAPES = [
     (1, 1, 513, 128, 64, "f32", 32),
     (1, 2, 2048, 16, 16, "bf16", 16),    # 128 chunks: 7 tree levels
     (1, 1, 999, 32, 128, "bf16", 32),
+    # split-bf16 tree nodes: dk = 64 with dv = 128 (20 chunks, the two-level up-sweep's levels
+    # 1-2 and 3-4), and dk = 32 over 94 chunks (odd node counts at levels 1, 2 and 5, levels
+    # 1-2, 3-4 and 5-6 in pairs)
+    (1, 2, 640, 64, 128, "bf16", 32),
+    (2, 1, 1500, 32, 32, "bf16", 16),
 ]
 
 
