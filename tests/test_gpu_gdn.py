@@ -71,6 +71,8 @@ SHAPES = [
     # 1-2, 3-4 and 5-6 in pairs)
     (1, 2, 640, 64, 128, "bf16", 32),
     (2, 1, 1500, 32, 32, "bf16", 16),
+    # 33 chunks at chunk 32 (an odd count: the two-level up-sweep's unpaired last node at level 1)
+    (1, 2, 1050, 64, 64, "bf16", 32),
 ]
 
 
