@@ -99,8 +99,8 @@ __device__ __forceinline__ void put_split(float* at, int n, int i, float x) {
 // lane (j, g) (j = lane % 16, g = lane / 16) supplies A(16ti + j, k + g) and B(k + g, 16tj + j),
 // and the accumulator gives it rows 16ti + 4g .. +3 of column 16tj + j. Every output value is
 // handed once to epi(i, j, value).
-template <int M, int N, int K, bool TA, bool TB, typename AT, typename Epi>
-__device__ __forceinline__ void gemm_f32(const AT* A, int lda, const float* B, int ldb, int tid,
+template <int M, int N, int K, bool TA, bool TB, typename AT, typename BT, typename Epi>
+__device__ __forceinline__ void gemm_f32(const AT* A, int lda, const BT* B, int ldb, int tid,
                                          Epi&& epi, const float* kscale = nullptr) {
   static_assert(M % 16 == 0 && N % 16 == 0 && K % 4 == 0, "16 x 16 tiles, 4-deep steps");
   constexpr int TN = N / 16, NTILE = (M / 16) * TN, NWAVE = kNT / 64;
@@ -114,7 +114,7 @@ __device__ __forceinline__ void gemm_f32(const AT* A, int lda, const float* B, i
     for (int k = 0; k < K; k += 4) {
       const int kk = k + g;
       const float a = to_f(TA ? A[kk * lda + i0 + j] : A[(i0 + j) * lda + kk]);
-      float b = TB ? B[(j0 + j) * ldb + kk] : B[kk * ldb + j0 + j];
+      float b = to_f(TB ? B[(j0 + j) * ldb + kk] : B[kk * ldb + j0 + j]);
       if (kscale) b *= kscale[kk];
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
     }
@@ -168,6 +168,28 @@ __device__ __forceinline__ void gemm_bf3(const bf16* Ah, const bf16* Al, int lda
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) epi(i0 + 4 * g + r, j0 + j, acc[r]);
+  }
+}
+
+// out(i, j) = sum_k A(i, k) B(j, k) for operands whose values are bf16 (inputs): A and B row-major
+// bf16 images in shared memory, one v_mfma_f32_16x16x32_bf16 per 32-deep step (products exact,
+// sums in float32); tiles and epilogue as gemm_bf3's
+template <int M, int N, int K, typename Epi>
+__device__ __forceinline__ void gemm_bf1_nt(const bf16* A, int lda, const bf16* B, int ldb, int tid, Epi&& epi) {
+  static_assert(M % 16 == 0 && N % 16 == 0 && K % 32 == 0, "16 x 16 tiles, 32-deep steps");
+  constexpr int TN = N / 16, NTILE = (M / 16) * TN, NWAVE = kNT / 64;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int j = lane & 15, g = lane >> 4;
+  for (int tile = w; tile < NTILE; tile += NWAVE) {
+    const int i0 = (tile / TN) * 16, j0 = (tile % TN) * 16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < K; k += 32)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(frag_rows(A, lda, i0 + j, k + 8 * g),
+                                                    frag_rows(B, ldb, j0 + j, k + 8 * g), acc, 0, 0, 0);
 #pragma unroll
     for (int r = 0; r < 4; ++r) epi(i0 + 4 * g + r, j0 + j, acc[r]);
   }
@@ -314,12 +336,13 @@ struct StagedLambda {
 // 160 KB).
 // gdn_chunk reads the in-chunk lambda levels only (bit_length(i ^ j) <= log2 C)
 __host__ __device__ constexpr int chunk_lw(int C) { return C == 16 ? 5 : C == 32 ? 6 : 7; }
-// QB: bfloat16 inputs keep q as a bf16 image (rows padded by 8 elements; its values are exact in
-// bf16), and Khat then takes the float32 buffers of Lqk and Tm^{-1} (free by then) where they hold
-// it: at chunk 32 and d = 64, 57.6 -> 51.6 KB, three workgroups per compute unit instead of two
-__host__ __device__ constexpr bool chunk_qb(bool bf, int C, int DK) { return bf && 2 * (C + 1) >= DK + 1; }
+// QB: bfloat16 inputs keep q and k as bf16 images (rows padded by 8 elements; their values are
+// exact in bf16, and K K^T, Q K^T run on the bf16 matrix cores), and Khat then takes the float32
+// buffers of Lqk and Tm^{-1} (free by then) where they hold it: at chunk 32 and d = 64, 57.6 ->
+// 46.8 KB, three workgroups per compute unit instead of two
+__host__ __device__ constexpr bool chunk_qb(bool bf, int C, int DK) { return bf && 2 * (C + 1) >= DK + 1 && DK % 32 == 0; }
 __host__ __device__ constexpr int chunk_smem_bytes(int C, int DK, int DV, bool bf = false) {
-  return 4 * ((chunk_qb(bf, C, DK) ? C * (DK + 8) / 2 : C * (DK + 1)) + C * (DK + 1) + C * (DV + 1) +
+  return 4 * ((chunk_qb(bf, C, DK) ? C * (DK + 8) : 2 * C * (DK + 1)) + C * (DV + 1) +
               3 * C * (C + 1) + C * (DK + 1) + C * (DV + 1) + C * chunk_lw(C) + 3 * C);
 }
 // up-sweep panel width: the whole [N | Phi] row (WHOLE: one workgroup per node, the right
@@ -359,7 +382,7 @@ template <int C, int DK, int DV, bool BF>
 struct ChunkSmem {
   static constexpr bool QB = chunk_qb(BF, C, DK);
   static constexpr int SK = DK + 1, SV = DV + 1, SC = C + 1, SQ = QB ? DK + 8 : SK, LW = chunk_lw(C);
-  static constexpr int Q = 0, K = Q + (QB ? C * SQ / 2 : C * SK), V = K + C * SK, M1 = V + C * SV,
+  static constexpr int Q = 0, K = Q + (QB ? C * SQ / 2 : C * SK), V = K + (QB ? C * SQ / 2 : C * SK), M1 = V + C * SV,
                        M2 = M1 + C * SC, Y = M2 + C * SC, W = Y + C * SC, U = W + C * SK,
                        LAM = U + C * SV, AL = LAM + C * LW, BT = AL + C, BE = BT + C, TOTAL = BE + C;
   static constexpr int KH = QB ? M2 : Q;   // Khat (float32, stride SK)
@@ -377,11 +400,13 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
   using S = ChunkSmem<C, DK, DV, std::is_same<T, bf16>::value>;
   constexpr int SK = S::SK, SV = S::SV, SC = S::SC, SQ = S::SQ;
   extern __shared__ __attribute__((aligned(16))) float sm[];
-  // q: a bf16 image (QB) or float32; Khat: float32, in q's buffer or (QB) those of Lqk and Tm^{-1}
+  // q, k: bf16 images (QB) or float32 (row stride SQ); Khat: float32, in q's buffer or (QB) those
+  // of Lqk and Tm^{-1}
   typedef typename std::conditional<S::QB, bf16, float>::type QT;
   QT* Qs = reinterpret_cast<QT*>(sm + S::Q);
+  QT* Ks = reinterpret_cast<QT*>(sm + S::K);
   float* Kh = sm + S::KH;
-  float* Ks = sm + S::K;  float* Vs = sm + S::V;
+  float* Vs = sm + S::V;
   float* M1 = sm + S::M1; float* M2 = sm + S::M2; float* Ti = sm + S::Y;
   float* Ws = sm + S::W;  float* Us = sm + S::U;  float* lam = sm + S::LAM;
   float* al = sm + S::AL; float* bt = sm + S::BT; float* be = sm + S::BE;
@@ -404,9 +429,13 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
     sk.load(kg + row0 * DK, DK, nv, tid);
     sv.load(vg + row0 * DV, DV, nv, tid);
     sl.load(p, row0, nv, tid);
-    if constexpr (S::QB) sq.store_raw(Qs, SQ, tid);
-    else sq.store(Qs, SK, tid);
-    sk.store(Ks, SK, tid);
+    if constexpr (S::QB) {
+      sq.store_raw(Qs, SQ, tid);
+      sk.store_raw(Ks, SQ, tid);
+    } else {
+      sq.store(Qs, SK, tid);
+      sk.store(Ks, SK, tid);
+    }
     sv.store(Vs, SV, tid);
     sl.store(lam, tid);
   }
@@ -429,9 +458,9 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
   const float g = al[C - 1];
 
   // Tm = I + M1, M1 its strictly lower part; exp of a difference of prefixes, never above 1
-  gemm_f32<C, C, DK, false, true>(Ks, SK, Ks, SK, tid, [&](int i, int j, float x) {
-    M1[i * SC + j] = j < i ? bt[i] * x * __expf(al[i] - al[j]) : 0.f;
-  });
+  auto tm_lower = [&](int i, int j, float x) { M1[i * SC + j] = j < i ? bt[i] * x * __expf(al[i] - al[j]) : 0.f; };
+  if constexpr (S::QB) gemm_bf1_nt<C, C, DK>(Ks, SQ, Ks, SQ, tid, tm_lower);
+  else gemm_f32<C, C, DK, false, true>(Ks, SQ, Ks, SQ, tid, tm_lower);
   __syncthreads();
 
   // Ti = Tm^{-1} (unit lower triangular): the 16 x 16 diagonal blocks by forward substitution,
@@ -467,11 +496,11 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
   if constexpr (C > 32) merge(std::integral_constant<int, 32>{});
 
   // W = Ti diag(beta e^a) K, U = Ti diag(beta) V; Lqk into M2 (its scratch use is over)
-  gemm_f32<C, DK, C, false, false>(Ti, SC, Ks, SK, tid, [&](int i, int d, float x) { Ws[i * SK + d] = x; }, be);
+  gemm_f32<C, DK, C, false, false>(Ti, SC, Ks, SQ, tid, [&](int i, int d, float x) { Ws[i * SK + d] = x; }, be);
   gemm_f32<C, DV, C, false, false>(Ti, SC, Vs, SV, tid, [&](int i, int e, float x) { Us[i * SV + e] = x; }, bt);
-  gemm_f32<C, C, DK, false, true>(Qs, SQ, Ks, SK, tid, [&](int i, int j, float x) {
-    M2[i * SC + j] = j <= i ? x * __expf(al[i] - al[j]) : 0.f;
-  });
+  auto lqk = [&](int i, int j, float x) { M2[i * SC + j] = j <= i ? x * __expf(al[i] - al[j]) : 0.f; };
+  if constexpr (S::QB) gemm_bf1_nt<C, C, DK>(Qs, SQ, Ks, SQ, tid, lqk);
+  else gemm_f32<C, C, DK, false, true>(Qs, SQ, Ks, SQ, tid, lqk);
   __syncthreads();
 
   // X0 = diag(e^a) Q - Lqk W (to the workspace); M1 <- (Lqk Ti diag(beta)) * Lambda, the
@@ -492,7 +521,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
   });
   for (int i = tid; i < C * DK; i += kNT) {
     const int r = i / DK, d = i % DK;
-    Kh[r * SK + d] = __expf(g - al[r]) * Ks[r * SK + d];
+    Kh[r * SK + d] = __expf(g - al[r]) * to_f(Ks[r * SQ + d]);
   }
   __syncthreads();
 
