@@ -119,6 +119,39 @@ __host__ __device__ inline int items_of_level(int N, int j) {
   return ((M >> (b + 1)) << b) + (rem > (1 << b) ? rem - (1 << b) : 0);
 }
 
+// bwd_rn's processing order (the items' places in the workspace are unchanged): group by group
+// of 8 chunks, each group's items of levels 0..2 (its odd chunks, odd pairs, odd quad) and then
+// the levels >= 3 whose right blocks hold it, so that every read of a group's q and dO rows after
+// the first comes from L2. Position x of the order -> level j and sub-block sb: the group by a
+// binary search over the closed-form count of items before each group (every group but the
+// last is whole), then the item inside it.
+__host__ __device__ inline int rn_items_before(int nl, int g) {
+  int n = g * ((nl > 0 ? 4 : 0) + (nl > 1 ? 2 : 0) + (nl > 2 ? 1 : 0));
+  for (int j = 3; j < nl; ++j) {   // groups g' < g with bit j - 3 set
+    const int b = j - 3, rem = (g & ((2 << b) - 1)) - (1 << b);
+    n += ((g >> (b + 1)) << b) + (rem > 0 ? rem : 0);
+  }
+  return n;
+}
+__host__ __device__ inline void rn_item_at(int N, int nl, int x, int& j, int& sb) {
+  int lo = 0, hi = ((N + 7) >> 3) - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (rn_items_before(nl, mid) <= x) lo = mid;
+    else hi = mid - 1;
+  }
+  const int g = lo;
+  int r = x - rn_items_before(nl, g);
+  for (int h = 0; h < 4 && nl > 0; ++h)
+    if (8 * g + 2 * h + 1 < N && r-- == 0) { j = 0; sb = 8 * g + 2 * h + 1; return; }
+  for (int h = 0; h < 2 && nl > 1; ++h)
+    if (4 * g + 2 * h + 1 < ((N + 1) >> 1) && r-- == 0) { j = 1; sb = 4 * g + 2 * h + 1; return; }
+  if (nl > 2 && 2 * g + 1 < ((N + 3) >> 2) && r-- == 0) { j = 2; sb = 2 * g + 1; return; }
+  for (j = 3; j < nl; ++j)
+    if (((g >> (j - 3)) & 1) && r-- == 0) { sb = g; return; }
+  j = 0; sb = 0;   // not reached for x < items
+}
+
 // slot of block (i, m) in the per-head tree: blocks of level i' < i come first
 __host__ __device__ inline int slot_of(int N, int i, int m) {
   int o = 0;
@@ -813,16 +846,16 @@ bwd_rn_kernel(BwdParams p) {
   using CH = Chunk<T, C, DK, DV>;
   extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
   // one-dimensional grid in XCD order, as in bwd_grads: XCD x takes heads x, x + 8, ... (B*H a
-  // multiple of 8), every sub-block of a head in turn, so the q and dO rows a head reads once per
-  // level come from its L2 after the first time
+  // multiple of 8), a head's items in the group-major order of rn_item_at, so the q and dO rows
+  // of a group, read by up to 7 + (nl - 3) items, come from its L2 after the first time
   const int Lw = blockIdx.x, q8 = Lw >> 3;
   const bool xcd = (p.BH & 7) == 0;
-  const int item = xcd ? q8 % p.items : Lw % p.items;
+  const int x = xcd ? q8 % p.items : Lw % p.items;   // place in the group-major order
   const int bh = xcd ? ((q8 / p.items) << 3) + (Lw & 7) : Lw / p.items;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, jj = lane & 15, g4 = lane >> 4;
-  int j = 0;
-  while (j + 1 < p.nl && p.rn_off[j + 1] <= item) ++j;
-  const int sb = sub_of_item(j, item - p.rn_off[j]);
+  int j, sb;
+  rn_item_at(p.N, p.nl, x, j, sb);
+  const int item = p.rn_off[j] + item_of_sub(j, sb);
   const int c0 = sb << sub_log(j), c1 = min(c0 + (1 << sub_log(j)), p.N);
   const BwdSmem Lo = bwd_smem(ES, C, DK, DV, false);
   CH ch;
