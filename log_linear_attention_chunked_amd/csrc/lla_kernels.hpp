@@ -713,13 +713,26 @@ __device__ __forceinline__ Frag<T> score_unit(const Reader<T, C, DK, DV>& rd, co
   return frag_from<T>(p0, p1);
 }
 
+// Output rows are written once and never read in the launch: non-temporal stores, which keep
+// them from filling the L2 with dirty lines that the end of the launch must write back. The
+// streamed input copies keep the default policy (non-temporal copies measured slower).
 template <typename T> __device__ __forceinline__ void store_quad(T* p, const f32x4& v);
 template <> __device__ __forceinline__ void store_quad<bf16>(bf16* p, const f32x4& v) {
   bf16x4 b;
   b[0] = (bf16)v[0]; b[1] = (bf16)v[1]; b[2] = (bf16)v[2]; b[3] = (bf16)v[3];
-  *reinterpret_cast<bf16x4*>(p) = b;
+  __builtin_nontemporal_store(b, reinterpret_cast<bf16x4*>(p));
 }
 template <> __device__ __forceinline__ void store_quad<float>(float* p, const f32x4& v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+// four output values into shared memory (8 bytes as bf16, 16 as float)
+template <typename T> __device__ __forceinline__ void stage_quad(unsigned char* p, const f32x4& v);
+template <> __device__ __forceinline__ void stage_quad<bf16>(unsigned char* p, const f32x4& v) {
+  bf16x4 b;
+  b[0] = (bf16)v[0]; b[1] = (bf16)v[1]; b[2] = (bf16)v[2]; b[3] = (bf16)v[3];
+  *reinterpret_cast<bf16x4*>(p) = b;
+}
+template <> __device__ __forceinline__ void stage_quad<float>(unsigned char* p, const f32x4& v) {
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
@@ -1367,12 +1380,27 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
           dext += node_ld_f(p.gnode + node_slot(bh, ns, e, NW, w));
         }
       }
-      // store rows [0, valid); NaN if a node never arrived
+      // store rows [0, valid); NaN if a node never arrived. A wave holds 16 columns of every row,
+      // so the rows go through shared memory (the first chunk's k image onwards, unread since
+      // the second chunk's score barrier; 16-byte units XOR-swizzled by row) and leave as whole
+      // rows, each 16-byte piece by one lane: non-temporal stores of whole cache lines
+      unsigned char* stage = smem + S.k[0];
+      constexpr int RB = DV * ES, VR = RB / 16;   // row bytes, 16-byte units per row
+      if (u > 0 || NB == 1) lds_barrier();         // the stage is free (earlier rows copied out)
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         const int qi = 16 * qb + j;
         if (__builtin_amdgcn_readfirstlane(bad)) O[u][qb] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
-        if (qi < valid) store_quad<T>(og + (size_t)(t0 + qi) * DV + 16 * w + 4 * g, O[u][qb]);
+        const int cb = (16 * w + 4 * g) * ES;      // the lane's bytes in the row
+        stage_quad<T>(stage + qi * RB + (((cb >> 4) ^ (qi & (VR - 1))) << 4) + (cb & 15), O[u][qb]);
+      }
+      lds_barrier();
+      for (int v = tid; v < C * VR; v += NT) {
+        const int r = v / VR, c16 = v % VR;
+        if (r < valid) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * RB + ((c16 ^ (r & (VR - 1))) << 4));
+          __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(og + (size_t)(t0 + r) * DV) + c16 * 16));
+        }
       }
       gam += gch[u];
     }
