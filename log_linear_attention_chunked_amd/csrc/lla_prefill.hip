@@ -6,10 +6,14 @@
 // After position P the live levels are 0 (position P itself) and l = j + 1 for each set bit j of
 // P, holding the aligned block of 2^j positions [(P >> l) << l, + 2^j), decayed to P:
 //   S_l = sum_{s in block} exp(A_P - A_s) k_s v_s^T.
-// One workgroup per (head, level). Level 0 writes the rank-one factors (k_P, v_P) into the
-// cache's parity P & 1 and the log-scale row of that parity; a live level l >= 1 contracts its
-// block on MFMA in tiles of 64 positions taken from the block's end backwards, so every decay
-// weight exp(A_P - A_s) is built from sums of log_a <= 0 and never exceeds 1. The weighted
+// Workgroups over (head, item): item 0 writes the rank-one factors (k_P, v_P) of level 0 into the
+// cache's parity P & 1 and the log-scale row of that parity; every other item is a segment of
+// up to kSeg positions of a live level's block (the large blocks split so that no workgroup
+// walks a long block alone), contracted on MFMA in tiles of 64 positions taken from the
+// segment's end backwards, so every decay weight exp(A_P - A_s) is built from sums of
+// log_a <= 0 and never exceeds 1. A block of one segment is written to its level directly; the
+// segments of a longer block go to a scratch array and a second kernel adds them in segment
+// order (deterministic). The weighted
 // operand is split into bf16 hi + lo parts (bf16 inputs), as in the backward pass: the state is
 // read by every later step. The contract is documented in include/loglinear_attn.h.
 #include <hip/hip_runtime.h>
@@ -19,6 +23,7 @@
 
 #include "loglinear_attn.h"
 #include "lla_bwd.hpp"
+#include "lla_host.hpp"
 
 namespace lla {
 namespace prefill {
@@ -26,6 +31,7 @@ namespace prefill {
 constexpr int kTile = 64;          // positions per tile
 constexpr int kWaves = 4;
 constexpr int kMaxLevels = 25;     // as the decoding step's cache
+constexpr int kSeg = 256;          // positions per segment of a live level's block
 
 struct Params {
   const void* k;
@@ -33,8 +39,31 @@ struct Params {
   const float* log_a;
   float* state;     // [BH][Lc][dk][dv]
   float* lscale;    // [BH][2][Lc]
-  int T, Lc, dv;
+  float* scratch;   // [BH][nslot][dk][dv]: the segments of the blocks longer than kSeg
+  int T, Lc, dv, nslot;
 };
+
+// segments of level l's block (2^(l-1) positions)
+__host__ __device__ inline int seg_count(int l) { return l - 1 > 8 ? 1 << (l - 1 - 8) : 1; }
+static_assert(kSeg == 1 << 8, "segments of 2^8 positions");
+
+// item (>= 1) -> live level l, segment index, and the segment's scratch slot (-1: one segment,
+// written to the level itself); levels in increasing order, each with its segments
+__device__ inline void item_of(long long P, int item, int& l, int& seg, int& slot) {
+  int base = 1, sbase = 0;
+  for (l = 1; l < kMaxLevels; ++l) {
+    if (!((P >> (l - 1)) & 1)) continue;
+    const int ns = seg_count(l);
+    if (item < base + ns) {
+      seg = item - base;
+      slot = ns > 1 ? sbase + seg : -1;
+      return;
+    }
+    base += ns;
+    if (ns > 1) sbase += ns;
+  }
+  l = 0; seg = 0; slot = -1;   // not reached for items of the launch
+}
 
 template <typename T, int DK, int DV>
 __global__ void __launch_bounds__(64 * kWaves) prefill_kernel(Params p) {
@@ -44,16 +73,15 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_kernel(Params p) {
   __shared__ __attribute__((aligned(16))) T vs[kTile * RV];
   __shared__ float wt[kTile];
   __shared__ float red[NT];
-  const int bh = blockIdx.x, l = blockIdx.y;
+  const int bh = blockIdx.x, item = blockIdx.y;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, jj = lane & 15, g4 = lane >> 4;
   const long long P = (long long)p.T - 1;
   const size_t row0 = (size_t)bh * p.T;
   const T* kg = reinterpret_cast<const T*>(p.k) + row0 * DK;
   const T* vg = reinterpret_cast<const T*>(p.v) + row0 * DV;
   const float* lg = p.log_a + row0;
-  float* st = p.state + ((size_t)bh * p.Lc + l) * DK * DV;
   float* ls = p.lscale + ((size_t)bh * 2 + (P & 1)) * p.Lc;
-  if (l == 0) {
+  if (item == 0) {
     // level 0: the factors of position P at parity P & 1; every log-scale of that parity is 0
     // (live levels are stored unscaled, the others are never read)
     float* f0 = p.state + (size_t)bh * p.Lc * DK * DV + (size_t)(P & 1) * (DK + DV);
@@ -62,8 +90,13 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_kernel(Params p) {
     for (int i = tid; i < p.Lc; i += NT) ls[i] = 0.f;
     return;
   }
-  if (!((P >> (l - 1)) & 1)) return;   // level l is not live after P
-  const long long b0 = (P >> l) << l, n = 1LL << (l - 1), bend = b0 + n;   // block [b0, bend)
+  int l, seg, slot;
+  item_of(P, item, l, seg, slot);
+  float* st = slot < 0 ? p.state + ((size_t)bh * p.Lc + l) * DK * DV
+                       : p.scratch + ((size_t)bh * p.nslot + slot) * DK * DV;
+  // the segment [b0, bend) of the block [(P >> l) << l, + 2^(l-1))
+  const long long n = 1LL << (l - 1), sn = n < kSeg ? n : kSeg;
+  const long long b0 = ((P >> l) << l) + seg * sn, bend = b0 + sn;
 
   // R = sum of log_a over (end of the current tile, P]: first over [bend, P], in a fixed order
   float part = 0.f;
@@ -140,6 +173,28 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_kernel(Params p) {
   }
 }
 
+// the segments of every block longer than kSeg, added in segment order: one workgroup per (head,
+// such level), 16-byte pieces of the state per thread
+template <int DK, int DV>
+__global__ void __launch_bounds__(256) prefill_reduce_kernel(Params p) {
+  const int bh = blockIdx.x;
+  const long long P = (long long)p.T - 1;
+  int m = blockIdx.y, l = 1, sbase = 0;
+  for (; l < kMaxLevels; ++l) {          // the m-th live level with more than one segment
+    if (!((P >> (l - 1)) & 1) || seg_count(l) == 1) continue;
+    if (m-- == 0) break;
+    sbase += seg_count(l);
+  }
+  const int ns = seg_count(l);
+  const f32x4* src = reinterpret_cast<const f32x4*>(p.scratch + ((size_t)bh * p.nslot + sbase) * DK * DV);
+  f32x4* dst = reinterpret_cast<f32x4*>(p.state + ((size_t)bh * p.Lc + l) * DK * DV);
+  for (int i = threadIdx.x; i < DK * DV / 4; i += 256) {
+    f32x4 acc = src[i];
+    for (int s = 1; s < ns; ++s) acc += src[(size_t)s * (DK * DV / 4) + i];
+    dst[i] = acc;
+  }
+}
+
 template <typename T, int DK>
 const void* pick_dv(int dv) {
   switch (dv) {
@@ -158,6 +213,26 @@ const void* pick(int dk, int dv) {
     case 32: return pick_dv<T, 32>(dv);
     case 64: return pick_dv<T, 64>(dv);
     case 128: return pick_dv<T, 128>(dv);
+  }
+  return nullptr;
+}
+
+template <int DK>
+const void* pick_reduce_dv(int dv) {
+  switch (dv) {
+    case 16: return reinterpret_cast<const void*>(&prefill_reduce_kernel<DK, 16>);
+    case 32: return reinterpret_cast<const void*>(&prefill_reduce_kernel<DK, 32>);
+    case 64: return reinterpret_cast<const void*>(&prefill_reduce_kernel<DK, 64>);
+    case 128: return reinterpret_cast<const void*>(&prefill_reduce_kernel<DK, 128>);
+  }
+  return nullptr;
+}
+const void* pick_reduce(int dk, int dv) {
+  switch (dk) {
+    case 16: return pick_reduce_dv<16>(dv);
+    case 32: return pick_reduce_dv<32>(dv);
+    case 64: return pick_reduce_dv<64>(dv);
+    case 128: return pick_reduce_dv<128>(dv);
   }
   return nullptr;
 }
@@ -202,12 +277,34 @@ extern "C" int loglinear_attn_decode_prefill(const lla_prefill_args* a, lla_stre
   memset(&p, 0, sizeof(p));
   p.k = a->k; p.v = a->v; p.log_a = a->log_a; p.state = a->state; p.lscale = a->log_scale;
   p.T = a->T; p.Lc = a->Lc; p.dv = a->dv;
+  // items: level 0, then the segments of each live level; scratch slots for the blocks of more
+  // than one segment
+  const long long P = a->T - 1;
+  int items = 1, multi = 0;
+  for (int l = 1; l < kMaxLevels && (P >> (l - 1)); ++l) {
+    if (!((P >> (l - 1)) & 1)) continue;
+    items += seg_count(l);
+    if (seg_count(l) > 1) {
+      p.nslot += seg_count(l);
+      ++multi;
+    }
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* scratch = nullptr;
+  if (p.nslot > 0) {
+    if (lla::workspace_alloc(&scratch, (size_t)BH * p.nslot * a->dk * a->dv * 4, s) != hipSuccess)
+      return LLA_ERR_NO_MEMORY;
+    p.scratch = static_cast<float*>(scratch);
+  }
   void* args[] = {&p};
-  // one workgroup per (head, level); levels past bit_length(T - 1) are never live after T - 1
-  int levels = 1;
-  for (long long t = a->T - 1; t; t >>= 1) ++levels;
-  if (hipLaunchKernel(fn, dim3((unsigned)BH, (unsigned)levels), dim3(64 * kWaves), args, 0,
-                      reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
-    return LLA_ERR_HIP;
-  return LLA_OK;
+  int st = LLA_OK;
+  if (hipLaunchKernel(fn, dim3((unsigned)BH, (unsigned)items), dim3(64 * kWaves), args, 0, s) != hipSuccess)
+    st = LLA_ERR_HIP;
+  if (st == LLA_OK && multi > 0) {
+    const void* red = pick_reduce(a->dk, a->dv);
+    if (!red || hipLaunchKernel(red, dim3((unsigned)BH, (unsigned)multi), dim3(256), args, 0, s) != hipSuccess)
+      st = LLA_ERR_HIP;
+  }
+  if (scratch && hipFreeAsync(scratch, s) != hipSuccess && st == LLA_OK) st = LLA_ERR_HIP;
+  return st;
 }
