@@ -314,6 +314,9 @@ int loglinear_attn_decode_step(const lla_decode_args* args, lla_stream_t stream)
  *   layout as in loglinear_attn_decode_step); written: the live levels of P (unscaled), the
  *   level-0 factors of parity P & 1 and the log-scale row of that parity; nothing else is read.
  *   Lc >= bit_length(T) + 1 (the levels the step at t = T needs), <= 25.
+ * Blocks longer than 256 positions are contracted in segments of 256 whose partial states go
+ * to a scratch array the library allocates stream-ordered on `stream` (B*H*dk*dv*4 bytes per
+ * segment; LLA_ERR_NO_MEMORY if that fails) and are then added in segment order.
  * Returns LLA_OK or a negative LLA_ERR_*; B*H = 0 is a no-op. Asynchronous on `stream`,
  * deterministic.
  */
