@@ -185,6 +185,9 @@ def test_allocation_failure_returns_no_memory(L, monkeypatch):
     # one sweep covers the sequence: no workspace, so no allocation and nothing to fail (B = 0
     # keeps the call a no-op on a machine without a device)
     assert _call(L, _args(B=0)) == _lib.LLA_OK
+    # the prefill's scratch for blocks longer than 256 positions (T = 1000: the 512-position
+    # block of level 10 in two segments)
+    assert L.loglinear_attn_decode_prefill(ctypes.byref(_pargs(T=1000, Lc=11)), None) == _lib.LLA_ERR_NO_MEMORY
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(T=0), dict(T=0, q=None, out=None)])
