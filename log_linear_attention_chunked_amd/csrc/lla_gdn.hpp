@@ -25,13 +25,14 @@
 //
 // Kernels (stream order): gdn_chunk (one workgroup per chunk and head), the up-sweep (for
 // dk <= 64 gdn_upsweep2, two tree levels per launch, one workgroup per node of the upper level
-// and head; a last odd level, and every level at dk = 128, by gdn_upsweep, one launch per level
-// with workgroups over node and head or over node, head and a 16-column panel), gdn_query (one
-// workgroup per chunk and head). Products run on the matrix cores from shared memory, in
-// float32 — except, for bfloat16 inputs with dk >= 32, gdn_query's and gdn_upsweep2's, in split
-// bf16 (high and low parts, three bf16 products); Tm^{-1} is formed blockwise (16 x 16 diagonal
-// blocks by forward substitution, then doubled); inputs may be bfloat16 or float32, the output
-// is in their type.
+// and head, and a last odd level's even nodes on their own; at dk = 128 gdn_upsweep, one launch
+// per level with workgroups over node and head or over node, head and a 16-column panel),
+// gdn_query (one workgroup per chunk and head). Products run on the matrix cores from shared
+// memory, in float32 — except, for bfloat16 inputs, K K^T and Q K^T of gdn_chunk on bf16
+// operands (exact) and, with dk >= 32, gdn_query's and gdn_upsweep2's in split bf16 (high and
+// low parts, three bf16 products); Tm^{-1} is formed blockwise (16 x 16 diagonal blocks by
+// forward substitution, then doubled); inputs may be bfloat16 or float32, the output is in their
+// type.
 #pragma once
 
 #include <hip/hip_runtime.h>
