@@ -1381,12 +1381,16 @@ __global__ __launch_bounds__(4 * DV, 2) void lla_fwd_kernel(Params p) {
         }
       }
       // store rows [0, valid); NaN if a node never arrived. A wave holds 16 columns of every row,
-      // so the rows go through shared memory (the first chunk's k image onwards, unread since
-      // the second chunk's score barrier; 16-byte units XOR-swizzled by row) and leave as whole
-      // rows, each 16-byte piece by one lane: non-temporal stores of whole cache lines
+      // so the rows go through shared memory (the first chunk's k image onwards, 16-byte units
+      // XOR-swizzled by row) and leave as whole rows, each 16-byte piece by one lane:
+      // non-temporal stores of whole cache lines. The stage is free once every wave is past the
+      // second chunk's score barrier (the first chunk's k and v images are read before it) and,
+      // for the second chunk, once the first chunk's rows are copied out; a sweep of one chunk
+      // has no second score barrier, so it takes a barrier of its own (its stage may reach into
+      // the v image that P.V reads when dv > dk)
       unsigned char* stage = smem + S.k[0];
       constexpr int RB = DV * ES, VR = RB / 16;   // row bytes, 16-byte units per row
-      if (u > 0 || NB == 1) lds_barrier();         // the stage is free (earlier rows copied out)
+      if (u > 0 || nch < 2) lds_barrier();
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         const int qi = 16 * qb + j;

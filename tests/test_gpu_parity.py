@@ -87,6 +87,9 @@ SHAPES = [
     (1, 3, 999, 64, 64, 64, 2),      # T*L odd: lambda rows of heads 1, 2 not 16-byte aligned
     (1, 2, 8192, 32, 32, 16, 1),     # 512 sweeps per head: deep Fenwick tree over sweeps
     (1, 1, 2048, 128, 128, 128, 1),  # C = 128, d = 128
+    # dv > dk with a lone last chunk (the output rows' staging reaches into its v image)
+    (1, 2, 300, 32, 64, 64, 2),
+    (2, 1, 600, 16, 128, 32, 2),
 ]
 
 
