@@ -196,6 +196,32 @@ __device__ __forceinline__ void gemm_bf1_nt(const bf16* A, int lda, const bf16* 
   }
 }
 
+// out(i, j) = sum_k A(k, i) B(k, j): A an exact-bf16 row-major image read transposed (its columns
+// by the transposing reads), B as high and low bf16 images, row-major; A has no low part, so a
+// 32-deep step is two v_mfma_f32_16x16x32_bf16 (A hi + A lo). Tiles and epilogue as gemm_bf3's.
+template <int M, int N, int K, typename Epi>
+__device__ __forceinline__ void gemm_bf2_tn(const bf16* A, int lda, const bf16* Bh, const bf16* Bl, int ldb,
+                                            int tid, Epi&& epi) {
+  static_assert(M % 16 == 0 && N % 16 == 0 && K % 32 == 0, "16 x 16 tiles, 32-deep steps");
+  constexpr int TN = N / 16, NTILE = (M / 16) * TN, NWAVE = kNT / 64;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int j = lane & 15, g = lane >> 4;
+  for (int tile = w; tile < NTILE; tile += NWAVE) {
+    const int i0 = (tile / TN) * 16, j0 = (tile % TN) * 16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < K; k += 32) {
+      const bf16x8 a = frag_cols(A, lda, k + 8 * g, i0 + j);
+      const bf16x8 bh = frag_cols(Bh, ldb, k + 8 * g, j0 + j), bl = frag_cols(Bl, ldb, k + 8 * g, j0 + j);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) epi(i0 + 4 * g + r, j0 + j, acc[r]);
+  }
+}
+
 // gemm_bf3 with the epilogue told the tile's place among the wave's (t < gemm_tiles_per_wave) and
 // the accumulator row r, so that a caller can keep the outputs in registers across products
 template <int M, int N>
@@ -342,9 +368,17 @@ __host__ __device__ constexpr int chunk_lw(int C) { return C == 16 ? 5 : C == 32
 // buffers of Lqk and Tm^{-1} (free by then) where they hold it: at chunk 32 and d = 64, 57.6 ->
 // 46.8 KB, three workgroups per compute unit instead of two
 __host__ __device__ constexpr bool chunk_qb(bool bf, int C, int DK) { return bf && 2 * (C + 1) >= DK + 1 && DK % 32 == 0; }
+// LB (QB with chunks of 32 or 64): the leaf's products run on the bf16 matrix cores. Since
+// Khat = diag(e^{g-a}) K, the row scale moves onto U and W (U' = diag(e^{g-a}) U, W'' likewise),
+// K^T stays exact in bf16, U' and W'' are held as high and low bf16 images (rows padded by 8), and
+// each 32-deep step is K^T hi + K^T lo: two v_mfma_f32_16x16x32_bf16 instead of eight float32 steps.
+// U' takes U's buffer (grown to C (dv + 8) floats), W'' the buffers of q (low parts) and Lqk
+// (high parts), free by then.
+__host__ __device__ constexpr bool chunk_lb(bool bf, int C, int DK) { return chunk_qb(bf, C, DK) && C % 32 == 0; }
 __host__ __device__ constexpr int chunk_smem_bytes(int C, int DK, int DV, bool bf = false) {
   return 4 * ((chunk_qb(bf, C, DK) ? C * (DK + 8) : 2 * C * (DK + 1)) + C * (DV + 1) +
-              3 * C * (C + 1) + C * (DK + 1) + C * (DV + 1) + C * chunk_lw(C) + 3 * C);
+              3 * C * (C + 1) + C * (DK + 1) + (chunk_lb(bf, C, DK) ? C * (DV + 8) : C * (DV + 1)) +
+              C * chunk_lw(C) + 3 * C);
 }
 // up-sweep panel width: the whole [N | Phi] row (WHOLE: one workgroup per node, the right
 // child's transition read once; for dk <= 64, at levels with enough nodes to fill the device) or
@@ -381,15 +415,20 @@ __host__ __device__ constexpr int query_smem_bytes(int C, int DK, int DV) {
 // shared-memory layout of gdn_chunk (floats; float32 row strides padded by one)
 template <int C, int DK, int DV, bool BF>
 struct ChunkSmem {
-  static constexpr bool QB = chunk_qb(BF, C, DK);
+  static constexpr bool QB = chunk_qb(BF, C, DK), LB = chunk_lb(BF, C, DK);
   static constexpr int SK = DK + 1, SV = DV + 1, SC = C + 1, SQ = QB ? DK + 8 : SK, LW = chunk_lw(C);
+  static constexpr int SU = LB ? DV + 8 : SV, SW = DK + 8;   // U or U' (bf16 images), W'' images
   static constexpr int Q = 0, K = Q + (QB ? C * SQ / 2 : C * SK), V = K + (QB ? C * SQ / 2 : C * SK), M1 = V + C * SV,
                        M2 = M1 + C * SC, Y = M2 + C * SC, W = Y + C * SC, U = W + C * SK,
-                       LAM = U + C * SV, AL = LAM + C * LW, BT = AL + C, BE = BT + C, TOTAL = BE + C;
-  static constexpr int KH = QB ? M2 : Q;   // Khat (float32, stride SK)
+                       LAM = U + C * SU, AL = LAM + C * LW, BT = AL + C, BE = BT + C, TOTAL = BE + C;
+  static constexpr int KH = QB ? M2 : Q;   // Khat (float32, stride SK), where the leaf needs it (!LB)
   static constexpr int BYTES = TOTAL * 4;
   static_assert(BYTES == chunk_smem_bytes(C, DK, DV, BF), "layout and size formula agree");
-  static_assert(!QB || KH + C * SK <= W, "Khat fits the buffers of Lqk and Tm^{-1}");
+  static_assert(LB || !QB || KH + C * SK <= W, "Khat fits the buffers of Lqk and Tm^{-1}");
+  static_assert(!LB || (2 * C * SW <= 2 * 4 * C * SC && C * SW == 2 * (K - Q)),
+                "W'' high parts fit the buffers of Lqk and Tm^{-1}, its low parts q's");
+  static_assert(K % 2 == 0 && M2 % 2 == 0 && U % 2 == 0 && (C * SU) % 4 == 0,
+                "bf16 images start on 8-byte boundaries (transposing reads)");
 };
 
 // gdn_chunk: per (chunk, head) the intra-chunk output, the query rows carried to the chunk's
@@ -498,7 +537,17 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
 
   // W = Ti diag(beta e^a) K, U = Ti diag(beta) V; Lqk into M2 (its scratch use is over)
   gemm_f32<C, DK, C, false, false>(Ti, SC, Ks, SQ, tid, [&](int i, int d, float x) { Ws[i * SK + d] = x; }, be);
-  gemm_f32<C, DV, C, false, false>(Ti, SC, Vs, SV, tid, [&](int i, int e, float x) { Us[i * SV + e] = x; }, bt);
+  if constexpr (S::LB) {   // U' = diag(e^{g-a}) U as high and low bf16 images
+    bf16* Uh = reinterpret_cast<bf16*>(Us);
+    gemm_f32<C, DV, C, false, false>(Ti, SC, Vs, SV, tid, [&](int i, int e, float x) {
+      const float y = __expf(g - al[i]) * x;
+      const bf16 h = (bf16)y;
+      Uh[i * S::SU + e] = h;
+      Uh[C * S::SU + i * S::SU + e] = (bf16)(y - (float)h);
+    }, bt);
+  } else {
+    gemm_f32<C, DV, C, false, false>(Ti, SC, Vs, SV, tid, [&](int i, int e, float x) { Us[i * SV + e] = x; }, bt);
+  }
   auto lqk = [&](int i, int j, float x) { M2[i * SC + j] = j <= i ? x * __expf(al[i] - al[j]) : 0.f; };
   if constexpr (S::QB) gemm_bf1_nt<C, C, DK>(Qs, SQ, Ks, SQ, tid, lqk);
   else gemm_f32<C, C, DK, false, true>(Qs, SQ, Ks, SQ, tid, lqk);
@@ -515,14 +564,24 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
   });
   __syncthreads();
 
-  // O_intra = M1 V (to the workspace); Khat = diag(e^{g-a}) K (q, Lqk and Tm^{-1} are done)
+  // O_intra = M1 V (to the workspace); Khat = diag(e^{g-a}) K, or (LB) W'' = diag(e^{g-a}) W as
+  // high and low bf16 images (q, Lqk and Tm^{-1} are done)
   float* oig = p.oi + wrow0 * DV;
   gemm_f32<C, DV, C, false, false>(M1, SC, Vs, SV, tid, [&](int i, int e, float x) {
     oig[(size_t)i * DV + e] = x;
   });
+  bf16* Wh = reinterpret_cast<bf16*>(sm + S::M2);
+  bf16* Wl = reinterpret_cast<bf16*>(sm + S::Q);
   for (int i = tid; i < C * DK; i += kNT) {
     const int r = i / DK, d = i % DK;
-    Kh[r * SK + d] = __expf(g - al[r]) * to_f(Ks[r * SQ + d]);
+    if constexpr (S::LB) {
+      const float y = __expf(g - al[r]) * Ws[r * SK + d];
+      const bf16 h = (bf16)y;
+      Wh[r * S::SW + d] = h;
+      Wl[r * S::SW + d] = (bf16)(y - (float)h);
+    } else {
+      Kh[r * SK + d] = __expf(g - al[r]) * to_f(Ks[r * SQ + d]);
+    }
   }
   __syncthreads();
 
@@ -533,16 +592,25 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
   // split nodes: high and low parts straight from the accumulators (staging them through shared
   // memory for 16-byte stores cost more in barriers than it saved)
   constexpr bool NSPLIT = nodes_split<T, DK>();
-  gemm_f32<DK, DV, C, true, false>(Kh, SK, Us, SV, tid, [&](int d, int e, float x) {
+  auto put_n = [&](int d, int e, float x) {
     if constexpr (NSPLIT) put_split(ng, DK * DV, d * DV + e, x);
     else ng[(size_t)d * DV + e] = x;
-  });
+  };
   const float eg = __expf(g);
-  gemm_f32<DK, DK, C, true, false>(Kh, SK, Ws, SK, tid, [&](int d, int d2, float x) {
+  auto put_phi = [&](int d, int d2, float x) {
     const float y = (d == d2 ? eg : 0.f) - x;
     if constexpr (NSPLIT) put_split(pg, DK * DK, d * DK + d2, y);
     else pg[(size_t)d * DK + d2] = y;
-  });
+  };
+  if constexpr (S::LB) {   // N = K^T U', Phi = e^g I - K^T W''
+    const bf16* Kb = reinterpret_cast<const bf16*>(Ks);
+    const bf16* Uh = reinterpret_cast<const bf16*>(Us);
+    gemm_bf2_tn<DK, DV, C>(Kb, SQ, Uh, Uh + C * S::SU, S::SU, tid, put_n);
+    gemm_bf2_tn<DK, DK, C>(Kb, SQ, Wh, Wl, S::SW, tid, put_phi);
+  } else {
+    gemm_f32<DK, DV, C, true, false>(Kh, SK, Us, SV, tid, put_n);
+    gemm_f32<DK, DK, C, true, false>(Kh, SK, Ws, SK, tid, put_phi);
+  }
 }
 
 // shared-memory layout of gdn_upsweep: the right child's transition and one panel of the left
