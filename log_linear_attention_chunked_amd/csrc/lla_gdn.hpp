@@ -222,6 +222,32 @@ __device__ __forceinline__ void gemm_bf2_tn(const bf16* A, int lda, const bf16* 
   }
 }
 
+// out(i, j) = sum_k A(i, k) B(k, j): A row-major as high and low bf16 images, B an exact-bf16
+// row-major image; two v_mfma_f32_16x16x32_bf16 per 32-deep step (A hi + A lo against B), tiles
+// and epilogue as gemm_bf3's
+template <int M, int N, int K, typename Epi>
+__device__ __forceinline__ void gemm_bf2_nn(const bf16* Ah, const bf16* Al, int lda, const bf16* B, int ldb,
+                                            int tid, Epi&& epi) {
+  static_assert(M % 16 == 0 && N % 16 == 0 && K % 32 == 0, "16 x 16 tiles, 32-deep steps");
+  constexpr int TN = N / 16, NTILE = (M / 16) * TN, NWAVE = kNT / 64;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int j = lane & 15, g = lane >> 4;
+  for (int tile = w; tile < NTILE; tile += NWAVE) {
+    const int i0 = (tile / TN) * 16, j0 = (tile % TN) * 16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < K; k += 32) {
+      const bf16x8 ah = frag_rows(Ah, lda, i0 + j, k + 8 * g), al = frag_rows(Al, lda, i0 + j, k + 8 * g);
+      const bf16x8 b = frag_cols(B, ldb, k + 8 * g, j0 + j);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, b, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, b, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) epi(i0 + 4 * g + r, j0 + j, acc[r]);
+  }
+}
+
 // gemm_bf3 with the epilogue told the tile's place among the wave's (t < gemm_tiles_per_wave) and
 // the accumulator row r, so that a caller can keep the outputs in registers across products
 template <int M, int N>
@@ -373,12 +399,14 @@ __host__ __device__ constexpr bool chunk_qb(bool bf, int C, int DK) { return bf 
 // K^T stays exact in bf16, U' and W'' are held as high and low bf16 images (rows padded by 8), and
 // each 32-deep step is K^T hi + K^T lo: two v_mfma_f32_16x16x32_bf16 instead of eight float32 steps.
 // U' takes U's buffer (grown to C (dv + 8) floats), W'' the buffers of q (low parts) and Lqk
-// (high parts), free by then.
+// (high parts), free by then. v is then kept as a bf16 image too, and the in-chunk attention
+// matrix as high and low bf16 images (its product with v: two bf16 steps per 32, v exact).
 __host__ __device__ constexpr bool chunk_lb(bool bf, int C, int DK) { return chunk_qb(bf, C, DK) && C % 32 == 0; }
 __host__ __device__ constexpr int chunk_smem_bytes(int C, int DK, int DV, bool bf = false) {
-  return 4 * ((chunk_qb(bf, C, DK) ? C * (DK + 8) : 2 * C * (DK + 1)) + C * (DV + 1) +
-              3 * C * (C + 1) + C * (DK + 1) + (chunk_lb(bf, C, DK) ? C * (DV + 8) : C * (DV + 1)) +
-              C * chunk_lw(C) + 3 * C);
+  return 4 * ((chunk_qb(bf, C, DK) ? C * (DK + 8) : 2 * C * (DK + 1)) +
+              (chunk_lb(bf, C, DK) ? C * (DV + 8) / 2 + C * (C + 8) + 2 * C * (C + 1)
+                                   : C * (DV + 1) + 3 * C * (C + 1)) +
+              C * (DK + 1) + (chunk_lb(bf, C, DK) ? C * (DV + 8) : C * (DV + 1)) + C * chunk_lw(C) + 3 * C);
 }
 // up-sweep panel width: the whole [N | Phi] row (WHOLE: one workgroup per node, the right
 // child's transition read once; for dk <= 64, at levels with enough nodes to fill the device) or
@@ -418,8 +446,9 @@ struct ChunkSmem {
   static constexpr bool QB = chunk_qb(BF, C, DK), LB = chunk_lb(BF, C, DK);
   static constexpr int SK = DK + 1, SV = DV + 1, SC = C + 1, SQ = QB ? DK + 8 : SK, LW = chunk_lw(C);
   static constexpr int SU = LB ? DV + 8 : SV, SW = DK + 8;   // U or U' (bf16 images), W'' images
-  static constexpr int Q = 0, K = Q + (QB ? C * SQ / 2 : C * SK), V = K + (QB ? C * SQ / 2 : C * SK), M1 = V + C * SV,
-                       M2 = M1 + C * SC, Y = M2 + C * SC, W = Y + C * SC, U = W + C * SK,
+  static constexpr int SVB = DV + 8, SM = C + 8;   // (LB) v's bf16 image, the attention matrix's images
+  static constexpr int Q = 0, K = Q + (QB ? C * SQ / 2 : C * SK), V = K + (QB ? C * SQ / 2 : C * SK),
+                       M1 = V + (LB ? C * SVB / 2 : C * SV), M2 = M1 + (LB ? C * SM : C * SC), Y = M2 + C * SC, W = Y + C * SC, U = W + C * SK,
                        LAM = U + C * SU, AL = LAM + C * LW, BT = AL + C, BE = BT + C, TOTAL = BE + C;
   static constexpr int KH = QB ? M2 : Q;   // Khat (float32, stride SK), where the leaf needs it (!LB)
   static constexpr int BYTES = TOTAL * 4;
@@ -429,6 +458,8 @@ struct ChunkSmem {
                 "W'' high parts fit the buffers of Lqk and Tm^{-1}, its low parts q's");
   static_assert(K % 2 == 0 && M2 % 2 == 0 && U % 2 == 0 && (C * SU) % 4 == 0,
                 "bf16 images start on 8-byte boundaries (transposing reads)");
+  static_assert(!LB || (V % 4 == 0 && M1 % 4 == 0 && (C * SM) % 8 == 0),
+                "v's image and the attention matrix's start on 16-byte boundaries");
 };
 
 // gdn_chunk: per (chunk, head) the intra-chunk output, the query rows carried to the chunk's
@@ -476,7 +507,8 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
       sq.store(Qs, SK, tid);
       sk.store(Ks, SK, tid);
     }
-    sv.store(Vs, SV, tid);
+    if constexpr (S::LB) sv.store_raw(reinterpret_cast<bf16*>(Vs), S::SVB, tid);
+    else sv.store(Vs, SV, tid);
     sl.store(lam, tid);
   }
   if (tid < 64) {      // chunk-local inclusive prefix of log_a, one position per lane
@@ -539,7 +571,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
   gemm_f32<C, DK, C, false, false>(Ti, SC, Ks, SQ, tid, [&](int i, int d, float x) { Ws[i * SK + d] = x; }, be);
   if constexpr (S::LB) {   // U' = diag(e^{g-a}) U as high and low bf16 images
     bf16* Uh = reinterpret_cast<bf16*>(Us);
-    gemm_f32<C, DV, C, false, false>(Ti, SC, Vs, SV, tid, [&](int i, int e, float x) {
+    gemm_f32<C, DV, C, false, false>(Ti, SC, reinterpret_cast<const bf16*>(Vs), S::SVB, tid, [&](int i, int e, float x) {
       const float y = __expf(g - al[i]) * x;
       const bf16 h = (bf16)y;
       Uh[i * S::SU + e] = h;
@@ -560,16 +592,28 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
     x0g[(size_t)i * DK + d] = __expf(al[i]) * to_f(Qs[i * SQ + d]) - x;
   });
   gemm_f32<C, C, C, false, false>(M2, SC, Ti, SC, tid, [&](int i, int j, float x) {
-    M1[i * SC + j] = j <= i ? x * bt[j] * lam[i * S::LW + bit_length((unsigned)(i ^ j))] : 0.f;
+    const float y = j <= i ? x * bt[j] * lam[i * S::LW + bit_length((unsigned)(i ^ j))] : 0.f;
+    if constexpr (S::LB) {   // high and low bf16 images
+      bf16* Mh = reinterpret_cast<bf16*>(M1);
+      const bf16 h = (bf16)y;
+      Mh[i * S::SM + j] = h;
+      Mh[C * S::SM + i * S::SM + j] = (bf16)(y - (float)h);
+    } else {
+      M1[i * SC + j] = y;
+    }
   });
   __syncthreads();
 
   // O_intra = M1 V (to the workspace); Khat = diag(e^{g-a}) K, or (LB) W'' = diag(e^{g-a}) W as
   // high and low bf16 images (q, Lqk and Tm^{-1} are done)
   float* oig = p.oi + wrow0 * DV;
-  gemm_f32<C, DV, C, false, false>(M1, SC, Vs, SV, tid, [&](int i, int e, float x) {
-    oig[(size_t)i * DV + e] = x;
-  });
+  auto put_oi = [&](int i, int e, float x) { oig[(size_t)i * DV + e] = x; };
+  if constexpr (S::LB) {
+    const bf16* Mh = reinterpret_cast<const bf16*>(M1);
+    gemm_bf2_nn<C, DV, C>(Mh, Mh + C * S::SM, S::SM, reinterpret_cast<const bf16*>(Vs), S::SVB, tid, put_oi);
+  } else {
+    gemm_f32<C, DV, C, false, false>(M1, SC, Vs, SV, tid, put_oi);
+  }
   bf16* Wh = reinterpret_cast<bf16*>(sm + S::M2);
   bf16* Wl = reinterpret_cast<bf16*>(sm + S::Q);
   for (int i = tid; i < C * DK; i += kNT) {
