@@ -1080,13 +1080,27 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
     }
     j = jn;
   }
-  bf16* og = reinterpret_cast<bf16*>(p.out);
+  // the outputs leave as whole rows: staged through the query rows' images (every read of them
+  // ended at the last barrier) and written with 16-byte non-temporal stores, so that no partly
+  // written line is left in L2 to be merged (rows past T are not stored)
+  constexpr int SO = DV + 8, VR = DV / 8;   // staged row stride (bf16 elements), 16-byte pieces a row
+  static_assert(C * SO * 2 <= 4 * S::XB && DV % 8 == 0, "staged outputs fit the query rows' images");
+  bf16* st = reinterpret_cast<bf16*>(smb + S::X);
 #pragma unroll
   for (int t = 0; t < OPW; ++t) {
     const int tile = w + t * (kNT / 64), i0 = (tile / OTN) * 16, j0 = (tile % OTN) * 16;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      if (tile < NOT && i0 + g4 + r < nv) og[(row0 + i0 + g4 + r) * DV + j0 + jl] = (bf16)oacc[t][r];
+      if (tile < NOT) st[(i0 + g4 + r) * SO + j0 + jl] = (bf16)oacc[t][r];
+  }
+  __syncthreads();
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  bf16* og = reinterpret_cast<bf16*>(p.out);
+  for (int v = tid; v < C * VR; v += kNT) {
+    const int r = v / VR, c8 = (v % VR) * 8;
+    if (r < nv)
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(st + r * SO + c8),
+                                  reinterpret_cast<u32x4*>(og + (row0 + r) * DV + c8));
   }
 }
 
