@@ -443,7 +443,7 @@ def gdn_measure(dev, stream, steps: int = 10, warmup: int = 2) -> dict:
         "algorithmic_bytes_per_call": byte_ht * ht,
         "hbm_frac": byte_ht * ht / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "alu", "achieved": tflops, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / FP32_PEAK_TFLOPS, "scope": "whole call, against the float32 rate (the chunk kernel multiplies in float32; the up-sweep and query kernels in split bf16 for bf16 inputs with dk >= 32)"},
+                     "frac": tflops / FP32_PEAK_TFLOPS, "scope": "whole call, against the float32 rate (for bf16 inputs with dk >= 32 the up-sweep and query kernels multiply in split bf16, the chunk kernel its leaf products and the attention matrix times v; its other products in float32)"},
     }
 
 
