@@ -147,10 +147,30 @@ __device__ __forceinline__ bf16x8 frag_cols(const bf16* img, int ld, int k, int 
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// Node images 64 elements wide (128-byte rows, no padding) with their 32-byte windows permuted
+// per row: window w of row r sits at w ^ swz_win(r). A transposing read takes 32-byte pieces of
+// rows k + {0..3} + 8g; the permutation (row bits 1 and 3) sends the even and the odd ones of
+// every 8 rows that one pass serves to 4 different windows, so they meet no bank twice (padded
+// 144-byte rows gave those rows overlapping banks).
+__device__ __forceinline__ int swz_win(int r) { return ((r >> 1) & 1) | (((r >> 3) & 1) << 1); }
+__device__ __forceinline__ int swz_col(int r, int col) { return col ^ (swz_win(r) << 4); }
+__device__ __forceinline__ bf16x8 frag_cols_sw(const bf16* img, int k, int n) {
+  constexpr int ld = 64;
+  const int L = n & 15, n0 = n - L, r = k + (L >> 2), col = n0 + 4 * (L & 3);
+  const s16x4g a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4g*)(img + r * ld + swz_col(r, col)));
+  const s16x4g b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4g*)(img + (r + 4) * ld + swz_col(r + 4, col)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+template <bool SW>
+__device__ __forceinline__ bf16x8 frag_cols_b(const bf16* img, int ld, int k, int n) {
+  if constexpr (SW) return frag_cols_sw(img, k, n);
+  else return frag_cols(img, ld, k, n);
+}
+
 // out(i, j) = sum_k A(i, k) B(k, j) over an M x N output and a K-long contraction, A and B
 // row-major in shared memory as high and low bf16 images (row strides lda, ldb elements, each a
 // multiple of 8); 16 x 16 tiles dealt to the waves in turn, the epilogue as gemm_f32's
-template <int M, int N, int K, typename Epi>
+template <int M, int N, int K, bool SWB = false, typename Epi>
 __device__ __forceinline__ void gemm_bf3(const bf16* Ah, const bf16* Al, int lda, const bf16* Bh,
                                          const bf16* Bl, int ldb, int tid, Epi&& epi) {
   static_assert(M % 16 == 0 && N % 16 == 0 && K % 32 == 0, "16 x 16 tiles, 32-deep steps");
@@ -164,7 +184,7 @@ __device__ __forceinline__ void gemm_bf3(const bf16* Ah, const bf16* Al, int lda
 #pragma unroll
     for (int k = 0; k < K; k += 32) {
       const bf16x8 ah = frag_rows(Ah, lda, i0 + j, k + 8 * g), al = frag_rows(Al, lda, i0 + j, k + 8 * g);
-      const bf16x8 bh = frag_cols(Bh, ldb, k + 8 * g, j0 + j), bl = frag_cols(Bl, ldb, k + 8 * g, j0 + j);
+      const bf16x8 bh = frag_cols_b<SWB>(Bh, ldb, k + 8 * g, j0 + j), bl = frag_cols_b<SWB>(Bl, ldb, k + 8 * g, j0 + j);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
@@ -252,7 +272,7 @@ __device__ __forceinline__ void gemm_bf2_nn(const bf16* Ah, const bf16* Al, int 
 // the accumulator row r, so that a caller can keep the outputs in registers across products
 template <int M, int N>
 constexpr int gemm_tiles_per_wave() { return ((M / 16) * (N / 16) + kNT / 64 - 1) / (kNT / 64); }
-template <int M, int N, int K, typename Epi>
+template <int M, int N, int K, bool SWB = false, typename Epi>
 __device__ __forceinline__ void gemm_bf3_t(const bf16* Ah, const bf16* Al, int lda, const bf16* Bh,
                                            const bf16* Bl, int ldb, int tid, Epi&& epi) {
   static_assert(M % 16 == 0 && N % 16 == 0 && K % 32 == 0, "16 x 16 tiles, 32-deep steps");
@@ -269,7 +289,7 @@ __device__ __forceinline__ void gemm_bf3_t(const bf16* Ah, const bf16* Al, int l
 #pragma unroll
     for (int k = 0; k < K; k += 32) {
       const bf16x8 ah = frag_rows(Ah, lda, i0 + j, k + 8 * g), al = frag_rows(Al, lda, i0 + j, k + 8 * g);
-      const bf16x8 bh = frag_cols(Bh, ldb, k + 8 * g, j0 + j), bl = frag_cols(Bl, ldb, k + 8 * g, j0 + j);
+      const bf16x8 bh = frag_cols_b<SWB>(Bh, ldb, k + 8 * g, j0 + j), bl = frag_cols_b<SWB>(Bl, ldb, k + 8 * g, j0 + j);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
@@ -331,6 +351,18 @@ struct StagedBlock {
       const int v = tid + i * kNT;
       if (v >= NVEC) break;
       *reinterpret_cast<u32x4*>(dst + (v / VPR) * ldd + (v % VPR) * EPV) = buf[i];
+    }
+  }
+  // bf16 blocks only: into a 64-wide node image with the 32-byte windows permuted per row
+  // (swz_col)
+  __device__ __forceinline__ void store_raw_sw(bf16* dst, int tid) const {
+    static_assert(sizeof(T) == 2 && CC <= 64, "bf16 sources, rows within the 64-wide image");
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int v = tid + i * kNT;
+      if (v >= NVEC) break;
+      const int r = v / VPR;
+      *reinterpret_cast<u32x4*>(dst + r * 64 + swz_col(r, (v % VPR) * EPV)) = buf[i];
     }
   }
   __device__ __forceinline__ void store(float* dst, int ldd, int tid) const {
@@ -428,8 +460,12 @@ __host__ __device__ constexpr int query_smem_bytes_f32(int C, int DK, int DV) {
 // chunk in fp32 (the outputs stay in the registers): 39.2 KB at chunk 32, d = 64, four workgroups
 // per compute unit
 __host__ __device__ constexpr int query_jlev(int C) { return C == 16 ? 5 : C == 32 ? 6 : 7; }
+// node images 64 wide are unpadded (their windows permuted per row instead)
+__host__ __device__ constexpr int query_node_ld(int DK, int DV) {
+  return (DK > DV ? DK : DV) == 64 ? 64 : (DK > DV ? DK : DV) + 8;
+}
 __host__ __device__ constexpr int query_smem_bytes_bf3(int C, int DK, int DV) {
-  return 2 * 4 * C * (DK + 8) + 2 * 2 * DK * ((DK > DV ? DK : DV) + 8) + 4 * C * (kLamCapG - query_jlev(C));
+  return 2 * 4 * C * (DK + 8) + 2 * 2 * DK * query_node_ld(DK, DV) + 4 * C * (kLamCapG - query_jlev(C));
 }
 __host__ __device__ constexpr int query_smem_bytes(int C, int DK, int DV, bool bf) {
   return bf && DK >= 32 ? query_smem_bytes_bf3(C, DK, DV) : query_smem_bytes_f32(C, DK, DV);
@@ -964,7 +1000,8 @@ struct QuerySmem {
 // low parts), outputs (fp32), one node matrix (high and low parts), lambda rows (fp32)
 template <int C, int DK, int DV>
 struct QuerySmemB {
-  static constexpr int SX = DK + 8, MD = DK > DV ? DK : DV, SMB = MD + 8;
+  static constexpr int SX = DK + 8, MD = DK > DV ? DK : DV, SMB = query_node_ld(DK, DV);
+  static constexpr bool SW = MD == 64;   // node images with permuted windows (swz_col)
   static constexpr int J1 = query_jlev(C), LW = kLamCapG - J1;   // lambda levels J1 .. 23
   static constexpr int XB = C * SX * 2, MB = DK * SMB * 2;
   static constexpr int X = 0, MH = X + 4 * XB, ML = MH + MB, LAM = ML + MB, TOTAL = LAM + C * LW * 4;
@@ -1043,7 +1080,10 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
   while (j >= 0) {
     const size_t slot = slot_of(j, (c >> j) - 1);
     const int jn = next_bit(j);
-    if constexpr (PRE) {
+    if constexpr (S::SW) {
+      nbh.store_raw_sw(Mh, tid);
+      nbl.store_raw_sw(Ml, tid);
+    } else if constexpr (PRE) {
       nbh.store_raw(Mh, SMB, tid);
       nbl.store_raw(Ml, SMB, tid);
     } else {
@@ -1053,12 +1093,16 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
     }
     __syncthreads();
     // level J + 1 + j, at j of the staged levels
-    gemm_bf3_t<C, DV, DK>(xh[a], xl[a], SX, Mh, Ml, SMB, tid, [&](int t, int r, int i, int e, float x) {
+    gemm_bf3_t<C, DV, DK, S::SW>(xh[a], xl[a], SX, Mh, Ml, SMB, tid, [&](int t, int r, int i, int e, float x) {
       oacc[t][r] += lam[i * LW + j] * x;
     });
     __syncthreads();
     if (jn >= 0) {           // a higher node follows: X <- X Phi of this node
-      if constexpr (PRE) {
+      if constexpr (S::SW) {
+        fbh.store_raw_sw(Mh, tid);
+        fbl.store_raw_sw(Ml, tid);
+        load_node(slot_of(jn, (c >> jn) - 1), next_bit(jn) >= 0);
+      } else if constexpr (PRE) {
         fbh.store_raw(Mh, SMB, tid);
         fbl.store_raw(Ml, SMB, tid);
         load_node(slot_of(jn, (c >> jn) - 1), next_bit(jn) >= 0);
@@ -1070,7 +1114,7 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
       __syncthreads();
       bf16* oh = xh[a ^ 1];
       bf16* ol = xl[a ^ 1];
-      gemm_bf3<C, DK, DK>(xh[a], xl[a], SX, Mh, Ml, SMB, tid, [&](int i, int d, float x) {
+      gemm_bf3<C, DK, DK, S::SW>(xh[a], xl[a], SX, Mh, Ml, SMB, tid, [&](int i, int d, float x) {
         const bf16 h = (bf16)x;
         oh[i * SX + d] = h;
         ol[i * SX + d] = (bf16)(x - (float)h);

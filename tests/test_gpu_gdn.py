@@ -73,6 +73,9 @@ SHAPES = [
     (2, 1, 1500, 32, 32, "bf16", 16),
     # 33 chunks at chunk 32 (an odd count: the two-level up-sweep's unpaired last node at level 1)
     (1, 2, 1050, 64, 64, "bf16", 32),
+    # dk = 32, dv = 64: the query kernel's 64-wide node images with permuted windows hold a
+    # 32 x 32 transition (27 chunks, a ragged tail)
+    (2, 1, 850, 32, 64, "bf16", 32),
 ]
 
 
