@@ -423,8 +423,11 @@ int loglinear_attn_bwd_default_chunk(int dk, int dv, int dtype);
  *           element); calls that may run concurrently must not share it.
  *   stage_events : optional hipEvent_t recorded on `stream`: [0] before the per-chunk kernel,
  *           [1] before the tree up-sweep, [2] before the query kernel, [3] after it.
- * Products run on the matrix cores in float32 (the query and up-sweep kernels', for bfloat16
- * inputs with dk >= 32, in split bf16: high and low parts, three bf16 products each); the
+ * Products run on the matrix cores in float32, except for bfloat16 inputs with dk >= 32: there
+ * the query and up-sweep kernels' run in split bf16 (high and low parts, three bf16 products
+ * each), and, at chunk 32 or 64 where q and k fit as bf16 images, the per-chunk kernel's leaf
+ * state and transition and its attention matrix times v take the high and low parts of one
+ * operand against the other, exact in bf16 (two bf16 products each); the
  * launches are gdn_chunk (one workgroup per chunk and head), the up-sweep (two tree levels per
  * launch for dk <= 64, else one), and gdn_query. Asynchronous on `stream`,
  * deterministic; returns LLA_OK or a negative LLA_ERR_*; B*H*T = 0 is a no-op.
