@@ -465,7 +465,7 @@ __host__ __device__ constexpr int query_node_ld(int DK, int DV) {
   return (DK > DV ? DK : DV) == 64 ? 64 : (DK > DV ? DK : DV) + 8;
 }
 __host__ __device__ constexpr int query_smem_bytes_bf3(int C, int DK, int DV) {
-  return 2 * 4 * C * (DK + 8) + 2 * 2 * DK * query_node_ld(DK, DV) + 4 * C * (kLamCapG - query_jlev(C));
+  return 2 * 2 * C * (DK + 8) + 2 * 2 * DK * query_node_ld(DK, DV) + 4 * C * (kLamCapG - query_jlev(C));
 }
 __host__ __device__ constexpr int query_smem_bytes(int C, int DK, int DV, bool bf) {
   return bf && DK >= 32 ? query_smem_bytes_bf3(C, DK, DV) : query_smem_bytes_f32(C, DK, DV);
@@ -1004,7 +1004,7 @@ struct QuerySmemB {
   static constexpr bool SW = MD == 64;   // node images with permuted windows (swz_col)
   static constexpr int J1 = query_jlev(C), LW = kLamCapG - J1;   // lambda levels J1 .. 23
   static constexpr int XB = C * SX * 2, MB = DK * SMB * 2;
-  static constexpr int X = 0, MH = X + 4 * XB, ML = MH + MB, LAM = ML + MB, TOTAL = LAM + C * LW * 4;
+  static constexpr int X = 0, MH = X + 2 * XB, ML = MH + MB, LAM = ML + MB, TOTAL = LAM + C * LW * 4;
   static_assert(TOTAL == query_smem_bytes_bf3(C, DK, DV), "layout and size formula agree");
   static_assert(XB % 16 == 0 && MB % 16 == 0, "16-byte aligned images");
 };
@@ -1016,8 +1016,10 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
   using S = QuerySmemB<C, DK, DV>;
   constexpr int SX = S::SX, SMB = S::SMB, LW = S::LW;
   constexpr int OPW = gemm_tiles_per_wave<C, DV>(), OTN = DV / 16, NOT = (C / 16) * OTN;
-  bf16* xh[2] = {reinterpret_cast<bf16*>(smb + S::X), reinterpret_cast<bf16*>(smb + S::X + 2 * S::XB)};
-  bf16* xl[2] = {reinterpret_cast<bf16*>(smb + S::X + S::XB), reinterpret_cast<bf16*>(smb + S::X + 3 * S::XB)};
+  // the carried query rows, updated in place (each wave's new tiles wait in its registers until
+  // every wave has read the old rows)
+  bf16* xh = reinterpret_cast<bf16*>(smb + S::X);
+  bf16* xl = reinterpret_cast<bf16*>(smb + S::X + S::XB);
   bf16* Mh = reinterpret_cast<bf16*>(smb + S::MH);
   bf16* Ml = reinterpret_cast<bf16*>(smb + S::ML);
   float* lam = reinterpret_cast<float*>(smb + S::LAM);
@@ -1072,11 +1074,12 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
     if constexpr (PRE) {
       if (j >= 0) load_node(slot_of(j, (c >> j) - 1), next_bit(j) >= 0);
     }
-    sx.store_split(xh[0], xl[0], SX, tid);
+    sx.store_split(xh, xl, SX, tid);
     sl.store(lam, tid);
   }
   __syncthreads();
-  int a = 0;
+  constexpr int XPW = gemm_tiles_per_wave<C, DK>(), XTN = DK / 16, NXT = (C / 16) * XTN;
+  float xt[XPW][4];
   while (j >= 0) {
     const size_t slot = slot_of(j, (c >> j) - 1);
     const int jn = next_bit(j);
@@ -1093,7 +1096,7 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
     }
     __syncthreads();
     // level J + 1 + j, at j of the staged levels
-    gemm_bf3_t<C, DV, DK, S::SW>(xh[a], xl[a], SX, Mh, Ml, SMB, tid, [&](int t, int r, int i, int e, float x) {
+    gemm_bf3_t<C, DV, DK, S::SW>(xh, xl, SX, Mh, Ml, SMB, tid, [&](int t, int r, int i, int e, float x) {
       oacc[t][r] += lam[i * LW + j] * x;
     });
     __syncthreads();
@@ -1112,15 +1115,22 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
         b.store_split(Mh, Ml, SMB, tid);
       }
       __syncthreads();
-      bf16* oh = xh[a ^ 1];
-      bf16* ol = xl[a ^ 1];
-      gemm_bf3<C, DK, DK, S::SW>(xh[a], xl[a], SX, Mh, Ml, SMB, tid, [&](int i, int d, float x) {
-        const bf16 h = (bf16)x;
-        oh[i * SX + d] = h;
-        ol[i * SX + d] = (bf16)(x - (float)h);
-      });
+      gemm_bf3_t<C, DK, DK, S::SW>(xh, xl, SX, Mh, Ml, SMB, tid,
+                                   [&](int t, int r, int i, int d, float x) { xt[t][r] = x; });
       __syncthreads();
-      a ^= 1;
+      // every read of the old rows and of the transition is done: the new rows go in place (the
+      // next node's state joins them in this phase, and the loop's barrier follows)
+#pragma unroll
+      for (int t = 0; t < XPW; ++t) {
+        const int tile = w + t * (kNT / 64), i0 = (tile / XTN) * 16, d0 = (tile % XTN) * 16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (tile < NXT) {
+            const bf16 h = (bf16)xt[t][r];
+            xh[(i0 + g4 + r) * SX + d0 + jl] = h;
+            xl[(i0 + g4 + r) * SX + d0 + jl] = (bf16)(xt[t][r] - (float)h);
+          }
+      }
     }
     j = jn;
   }
@@ -1128,7 +1138,7 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
   // ended at the last barrier) and written with 16-byte non-temporal stores, so that no partly
   // written line is left in L2 to be merged (rows past T are not stored)
   constexpr int SO = DV + 8, VR = DV / 8;   // staged row stride (bf16 elements), 16-byte pieces a row
-  static_assert(C * SO * 2 <= 4 * S::XB && DV % 8 == 0, "staged outputs fit the query rows' images");
+  static_assert(C * SO * 2 <= S::LAM && DV % 8 == 0, "staged outputs fit the query rows' and nodes' images");
   bf16* st = reinterpret_cast<bf16*>(smb + S::X);
 #pragma unroll
   for (int t = 0; t < OPW; ++t) {
@@ -1150,8 +1160,16 @@ __device__ __forceinline__ void gdn_query_bf3(const GdnParams& p, unsigned char*
 
 // gdn_query: per (chunk, head) the Fenwick nodes of the chunk's set bits, lowest first, read out
 // with the query rows carried to each node's end; plus the intra-chunk output; store.
+// the split-bf16 query kernel up to chunk 32 and dk, dv = 64, where five workgroups' shared memory
+// fits a compute unit (27 KB at chunk 32, d = 64), has its registers held to five waves per SIMD
+// (at chunk 64 the bound would spill, and the shared memory allows four anyway)
 template <typename T, int C, int DK, int DV>
-__global__ __launch_bounds__(kNT) void gdn_query_kernel(GdnParams p) {
+constexpr int query_min_waves() {
+  return std::is_same<T, bf16>::value && C <= 32 && DK >= 32 && DK <= 64 && DV <= 64 &&
+                 5 * query_smem_bytes_bf3(C, DK, DV) <= 160 * 1024 ? 5 : 1;
+}
+template <typename T, int C, int DK, int DV>
+__global__ __launch_bounds__(kNT, (query_min_waves<T, C, DK, DV>())) void gdn_query_kernel(GdnParams p) {
   if constexpr (std::is_same<T, bf16>::value && DK >= 32) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smq[];
     gdn_query_bf3<C, DK, DV>(p, smq);
