@@ -622,10 +622,12 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
   __syncthreads();
 
   // X0 = diag(e^a) Q - Lqk W (to the workspace); M1 <- (Lqk Ti diag(beta)) * Lambda, the
-  // attention matrix inside the chunk under the level weights (Tm is no longer read)
+  // attention matrix inside the chunk under the level weights (Tm is no longer read). X0 and the
+  // intra-chunk outputs are read only by the query kernel, after the up-sweep: stored
+  // non-temporally, they leave the caches to the leaves the up-sweep reads next
   float* x0g = p.x0 + wrow0 * DK;
   gemm_f32<C, DK, C, false, false>(M2, SC, Ws, SK, tid, [&](int i, int d, float x) {
-    x0g[(size_t)i * DK + d] = __expf(al[i]) * to_f(Qs[i * SQ + d]) - x;
+    __builtin_nontemporal_store(__expf(al[i]) * to_f(Qs[i * SQ + d]) - x, &x0g[(size_t)i * DK + d]);
   });
   gemm_f32<C, C, C, false, false>(M2, SC, Ti, SC, tid, [&](int i, int j, float x) {
     const float y = j <= i ? x * bt[j] * lam[i * S::LW + bit_length((unsigned)(i ^ j))] : 0.f;
@@ -643,7 +645,7 @@ __global__ __launch_bounds__(kNT) void gdn_chunk_kernel(GdnParams p) {
   // O_intra = M1 V (to the workspace); Khat = diag(e^{g-a}) K, or (LB) W'' = diag(e^{g-a}) W as
   // high and low bf16 images (q, Lqk and Tm^{-1} are done)
   float* oig = p.oi + wrow0 * DV;
-  auto put_oi = [&](int i, int e, float x) { oig[(size_t)i * DV + e] = x; };
+  auto put_oi = [&](int i, int e, float x) { __builtin_nontemporal_store(x, &oig[(size_t)i * DV + e]); };
   if constexpr (S::LB) {
     const bf16* Mh = reinterpret_cast<const bf16*>(M1);
     gemm_bf2_nn<C, DV, C>(Mh, Mh + C * S::SM, S::SM, reinterpret_cast<const bf16*>(Vs), S::SVB, tid, put_oi);
